@@ -1,0 +1,216 @@
+"""Seeded synthetic inputs for the KDA operator, shared by the tests, the bench
+and the smoke check.  This module holds none of the operator's arithmetic:
+only random draws, the input normalisation the workloads prescribe, and bf16
+rounding of inputs.
+
+Distributions (the same for every workload, "config" gate):
+  q, k  ~ N(0, 1), L2-normalised per (token, head) over d_k; q is then scaled
+          by d_k**-0.5 (so the operator itself runs with scale = 1).
+  v     ~ N(0, 1)
+  g     = -5 * sigmoid(N(0, 1))        [T, H, d_k] fp32, natural-log decay
+  beta  = sigmoid(N(0, 1))             [T, H] fp32
+  S0    ~ N(0, 0.01), read as variance 0.01 (std 0.1), when a workload has one.
+Normalisation is done in fp32 with no epsilon; bf16 workloads round q, k, v
+to bf16 (round-to-nearest-even) afterwards, and every consumer sees exactly
+those rounded values.
+
+Stress gates: "slow" g = -5*sigmoid(N(0,1) - 6) (mean g ~ -0.02, long memory);
+"min" g = -5 everywhere (the bound); "zero" g = 0 (no decay).
+
+Seeding: every tensor block is drawn from its own PCG64 stream,
+SeedSequence([20261203, workload_id, seq, block, tensor_id, seed]), with
+blocks of 4096 tokens inside each sequence, so any block can be regenerated
+alone and generation parallelises over threads.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+ROOT_SEED = 20261203
+BLOCK = 4096
+_TID = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "s0": 5, "lengths": 6}
+
+
+def _rng(wid, seq, block, tensor, seed):
+    return np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence([ROOT_SEED, wid, seq, block, _TID[tensor], seed])))
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> nearest bf16 (ties to even), returned as fp32 values."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of fp32 values that are already bf16-exact (uint16 array)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _sigmoid(x):
+    return (1.0 / (1.0 + np.exp(-x.astype(np.float32)))).astype(np.float32)
+
+
+def _l2n(x):
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32), dtype=np.float32)
+    return (x / n).astype(np.float32)
+
+
+@dataclass
+class Workload:
+    """A synthetic KDA problem.  Arrays are host numpy fp32 (bf16-exact where
+    ``dtype == 'bf16'``)."""
+    name: str
+    seqlens: list
+    H: int
+    dk: int
+    dv: int
+    dtype: str                      # "f32" or "bf16": dtype of q, k, v
+    q: np.ndarray = None
+    k: np.ndarray = None
+    v: np.ndarray = None
+    g: np.ndarray = None
+    beta: np.ndarray = None
+    s0: np.ndarray = None           # [N, H, dk, dv] or None
+    checkpoint_every: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def cu_seqlens(self):
+        return np.concatenate([[0], np.cumsum(self.seqlens)]).astype(np.int64)
+
+    @property
+    def total_tokens(self):
+        return int(sum(self.seqlens))
+
+
+def _gen_block(wid, seed, s, b, T0, Tb, H, dk, dv, dtype, gate, out):
+    rq = _rng(wid, s, b, "q", seed)
+    rk = _rng(wid, s, b, "k", seed)
+    rv = _rng(wid, s, b, "v", seed)
+    rg = _rng(wid, s, b, "g", seed)
+    rb = _rng(wid, s, b, "beta", seed)
+    q = _l2n(rq.standard_normal((Tb, H, dk), dtype=np.float32)) * np.float32(dk ** -0.5)
+    k = _l2n(rk.standard_normal((Tb, H, dk), dtype=np.float32))
+    v = rv.standard_normal((Tb, H, dv), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    x = rg.standard_normal((Tb, H, dk), dtype=np.float32)
+    if gate == "config":
+        g = np.float32(-5.0) * _sigmoid(x)
+    elif gate == "slow":
+        g = np.float32(-5.0) * _sigmoid(x - np.float32(6.0))
+    elif gate == "min":
+        g = np.full((Tb, H, dk), -5.0, dtype=np.float32)
+    elif gate == "zero":
+        g = np.zeros((Tb, H, dk), dtype=np.float32)
+    else:
+        raise ValueError(gate)
+    beta = _sigmoid(rb.standard_normal((Tb, H), dtype=np.float32))
+    out["q"][T0:T0 + Tb] = q
+    out["k"][T0:T0 + Tb] = k
+    out["v"][T0:T0 + Tb] = v
+    out["g"][T0:T0 + Tb] = g
+    out["beta"][T0:T0 + Tb] = beta
+
+
+def make_prefill(seqlens, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.0, gate="config",
+                 checkpoint_every=0, wid=100, name=None, threads=None) -> Workload:
+    seqlens = [int(x) for x in seqlens]
+    T = sum(seqlens)
+    out = {n: np.empty((T, H, d), dtype=np.float32) for n, d in (("q", dk), ("k", dk), ("v", dv), ("g", dk))}
+    out["beta"] = np.empty((T, H), dtype=np.float32)
+    jobs = []
+    off = 0
+    for s, L in enumerate(seqlens):
+        for b in range(0, max(1, math.ceil(L / BLOCK))):
+            Tb = min(BLOCK, L - b * BLOCK)
+            if Tb > 0:
+                jobs.append((wid, seed, s, b, off + b * BLOCK, Tb, H, dk, dv, dtype, gate, out))
+        off += L
+    nt = threads or min(16, max(1, len(os.sched_getaffinity(0))))
+    if len(jobs) > 1 and nt > 1:
+        with ThreadPoolExecutor(nt) as ex:
+            list(ex.map(lambda j: _gen_block(*j), jobs))
+    else:
+        for j in jobs:
+            _gen_block(*j)
+    s0 = None
+    if s0_std > 0:
+        s0 = np.empty((len(seqlens), H, dk, dv), dtype=np.float32)
+        for s in range(len(seqlens)):
+            s0[s] = _rng(wid, s, 0, "s0", seed).standard_normal((H, dk, dv), dtype=np.float32) * np.float32(s0_std)
+    return Workload(name or f"prefill_H{H}_d{dk}", seqlens, H, dk, dv, dtype, out["q"], out["k"], out["v"],
+                    out["g"], out["beta"], s0, checkpoint_every, {"gate": gate, "seed": seed})
+
+
+def make_decode(N, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.1, gate="config", wid=103,
+                name=None, threads=None) -> Workload:
+    """N independent sequences, one new token each; the state is [N, H, dk, dv]."""
+    w = make_prefill([1] * N, H, dk, dv, dtype, seed, 0.0, gate, 0, wid, name or f"decode_N{N}_H{H}", threads)
+    # one independent state per sequence, drawn in parallel blocks of sequences
+    s0 = np.empty((N, H, dk, dv), dtype=np.float32)
+
+    def fill(s):
+        s0[s] = _rng(wid, s, 0, "s0", seed).standard_normal((H, dk, dv), dtype=np.float32) * np.float32(s0_std)
+    nt = threads or min(16, max(1, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(nt) as ex:
+        list(ex.map(fill, range(N)))
+    w.s0 = s0
+    return w
+
+
+def config4_lengths(n=64, lo=512, hi=131072, step=512):
+    """64 lengths, log-uniform on [lo, hi], rounded to the nearest multiple of
+    `step` inside [lo, hi].  The total is whatever the draw gives (about 1.5M
+    expected); it is reported, not rescaled."""
+    r = _rng(4, 0, 0, "lengths", 0)
+    x = np.exp(r.uniform(math.log(lo), math.log(hi), size=n))
+    L = np.clip(np.rint(x / step) * step, lo, hi).astype(np.int64)
+    return [int(v) for v in L]
+
+
+# The five workloads the operator is measured and checked on.
+CONFIGS = {
+    0: dict(name="tiny_f32_T256_H2_d64", kind="prefill", seqlens=[256], H=2, dk=64, dv=64, dtype="f32",
+            s0_std=0.0, checkpoint_every=0),
+    1: dict(name="prefill_T4096_H32_d128", kind="prefill", seqlens=[4096], H=32, dk=128, dv=128, dtype="bf16",
+            s0_std=0.0, checkpoint_every=0),
+    2: dict(name="prefill_T65536_H96_d128", kind="prefill", seqlens=[65536], H=96, dk=128, dv=128,
+            dtype="bf16", s0_std=0.1, checkpoint_every=0),
+    3: dict(name="decode_N256_H96_d128", kind="decode", N=256, H=96, dk=128, dv=128, dtype="bf16", s0_std=0.1),
+    4: dict(name="varlen64_H32_d128_ckpt512", kind="prefill", seqlens=None, H=32, dk=128, dv=128, dtype="bf16",
+            s0_std=0.1, checkpoint_every=512),
+}
+
+
+def make_config(cid: int, seed: int = 0, gate: str = "config", threads=None) -> Workload:
+    c = dict(CONFIGS[cid])
+    if c["kind"] == "decode":
+        return make_decode(c["N"], c["H"], c["dk"], c["dv"], c["dtype"], seed, c["s0_std"], gate, wid=cid,
+                           name=c["name"], threads=threads)
+    seqlens = c["seqlens"] if c["seqlens"] is not None else config4_lengths()
+    return make_prefill(seqlens, c["H"], c["dk"], c["dv"], c["dtype"], seed, c["s0_std"], gate,
+                        c["checkpoint_every"], wid=cid, name=c["name"], threads=threads)
+
+
+def rel_max_err(x, ref) -> float:
+    """max |x - ref| / RMS(ref) over the whole tensor, in fp64; inf if x has a
+    non-finite value."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        return float("inf")
+    rms = math.sqrt(float(np.mean(ref * ref))) if ref.size else 0.0
+    if ref.size == 0:
+        return 0.0
+    d = float(np.max(np.abs(x - ref)))
+    return d / rms if rms > 0 else (0.0 if d == 0 else float("inf"))
