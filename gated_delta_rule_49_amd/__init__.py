@@ -1,0 +1,202 @@
+"""gated_delta_rule_49_amd -- Python binding of libkda, an MI355X (gfx950)
+implementation of the Kimi Delta Attention (KDA) operator.
+
+This module only marshals arguments: it takes torch tensors for device memory
+and the current HIP stream, and calls the C ABI declared in ``include/kda.h``
+(same names: ``kda_chunk_fwd``, ``kda_decode_step``,
+``kda_chunk_fwd_workspace_bytes``, ``kda_status_str``, ``kda_abi_version``).
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback of any kind -- if ``libkda.so`` is missing or fails to load, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_DEVICE = range(5)
+KDA_F32, KDA_BF16 = 0, 1
+
+
+class KdaFwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+        ("initial_state", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
+        ("checkpoint_every", ctypes.c_int32), ("checkpoints", ctypes.c_void_p), ("o", ctypes.c_void_p),
+    ]
+
+
+class KdaDecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+        ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("state", ctypes.c_void_p),
+        ("state_indices", ctypes.c_void_p), ("o", ctypes.c_void_p),
+    ]
+
+
+EXPORTED = ["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_status_str",
+            "kda_abi_version"]
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load libkda.so (once).  Raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; "
+                                   "g.build()'` (hipcc, gfx950) first")
+            L = ctypes.CDLL(LIB_PATH)
+            L.kda_chunk_fwd.argtypes = [ctypes.POINTER(KdaFwdArgs), ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]
+            L.kda_chunk_fwd.restype = ctypes.c_int
+            L.kda_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(KdaFwdArgs)]
+            L.kda_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+            L.kda_decode_step.argtypes = [ctypes.POINTER(KdaDecodeArgs), ctypes.c_void_p]
+            L.kda_decode_step.restype = ctypes.c_int
+            L.kda_status_str.argtypes = [ctypes.c_int]
+            L.kda_status_str.restype = ctypes.c_char_p
+            L.kda_abi_version.argtypes = []
+            L.kda_abi_version.restype = ctypes.c_uint32
+            _lib = L
+    return _lib
+
+
+def kda_status_str(status: int) -> str:
+    return lib().kda_status_str(int(status)).decode()
+
+
+def kda_abi_version() -> int:
+    return int(lib().kda_abi_version())
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status):
+        super().__init__(kda_status_str(status))
+        self.status = status
+
+
+def _check(status):
+    if status != KDA_OK:
+        raise KdaError(status)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final_state, checkpoint_every,
+                  checkpoints, o):
+    T, H, dk = q.shape
+    a = KdaFwdArgs()
+    a.struct_size = ctypes.sizeof(KdaFwdArgs)
+    a.num_seqs = int(cu_host.numel() - 1)
+    a.total_tokens = int(T)
+    a.num_heads = int(H)
+    a.dk = int(dk)
+    a.dv = int(v.shape[2])
+    a.chunk_size = 64
+    a.in_dtype = _dtype_code(q)
+    a.scale = float(scale)
+    a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
+    a.cu_seqlens = _ptr(cu_dev)
+    a.cu_seqlens_host = cu_host.data_ptr()
+    a.initial_state = _ptr(initial_state)
+    a.final_state = _ptr(final_state)
+    a.checkpoint_every = int(checkpoint_every)
+    a.checkpoints = _ptr(checkpoints)
+    a.o = _ptr(o)
+    return a
+
+
+def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, output_final_state=True,
+                  checkpoint_every=0, stream=None):
+    """Chunked KDA prefill (packed varlen).
+
+    q, k: [T, H, dk]; v: [T, H, dv] (bf16 or fp32, CUDA, contiguous); g: [T, H, dk] fp32;
+    beta: [T, H] fp32; cu_seqlens: int sequence offsets [N+1] (list / CPU or CUDA tensor,
+    None = one sequence); initial_state: fp32 [N, H, dk, dv] or None.
+    Returns (o [T,H,dv] fp32, final_state [N,H,dk,dv] fp32 or None, checkpoints or None).
+    """
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    if cu_seqlens is None:
+        cu_host = torch.tensor([0, T], dtype=torch.int32)
+    elif isinstance(cu_seqlens, torch.Tensor):
+        cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+    else:
+        cu_host = torch.tensor(list(cu_seqlens), dtype=torch.int32)
+    cu_dev = cu_host.to(dev)
+    N = cu_host.numel() - 1
+    o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
+    ck = None
+    if checkpoint_every:
+        M = int(((cu_host[1:] - cu_host[:-1]) // checkpoint_every).sum())
+        ck = torch.empty((M, H, dk, dv), dtype=torch.float32, device=dev)
+    a = make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, sf, checkpoint_every, ck, o)
+    L = lib()
+    ws_bytes = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a))
+    if ws_bytes == 0 and N > 0:
+        # invalid arguments: let the entry point report the precise status
+        _check(L.kda_chunk_fwd(ctypes.byref(a), None, 0, _stream(stream)))
+    ws = torch.empty(max(int(ws_bytes), 256), dtype=torch.uint8, device=dev)
+    _check(L.kda_chunk_fwd(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                           _stream(stream)))
+    return o, sf, ck
+
+
+def make_decode_args(q, k, v, g, beta, state, o, scale):
+    N, H, dk = q.shape
+    a = KdaDecodeArgs()
+    a.struct_size = ctypes.sizeof(KdaDecodeArgs)
+    a.num_seqs = int(N)
+    a.num_heads = int(H)
+    a.dk = int(dk)
+    a.dv = int(v.shape[2])
+    a.in_dtype = _dtype_code(q)
+    a.scale = float(scale)
+    a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
+    a.state = _ptr(state)
+    a.state_indices = None
+    a.o = _ptr(o)
+    return a
+
+
+def kda_decode_step(q, k, v, g, beta, state, scale=1.0, out=None, stream=None):
+    """One decode token per sequence; `state` [N,H,dk,dv] fp32 is updated in place.
+    Returns o [N, H, dv] fp32."""
+    N, H, dk = q.shape
+    o = out if out is not None else torch.empty((N, H, v.shape[2]), dtype=torch.float32, device=q.device)
+    a = make_decode_args(q, k, v, g, beta, state, o, scale)
+    _check(lib().kda_decode_step(ctypes.byref(a), _stream(stream)))
+    return o

@@ -1,0 +1,125 @@
+// kda_api.hip -- the C ABI of libkda (declared in include/kda.h).
+//
+// Host-side argument validation (pure host code: it runs before any launch
+// and touches no device memory), workspace sizing, and kernel dispatch.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "kda.h"
+
+extern "C" hipError_t kda_launch_decode(int dk, int in_bf16, int N, int H, const void *q, const void *k,
+                                        const void *v, const float *g, const float *beta, float *state,
+                                        float *o, float scale, hipStream_t stream);
+extern "C" size_t kda_chunk_workspace_layout(int N, size_t *order_off, size_t *base_off);
+extern "C" hipError_t kda_launch_chunk(int dk, int in_bf16, int N, int H, const void *q, const void *k,
+                                       const void *v, const float *g, const float *beta, const int32_t *cu,
+                                       const float *s0, float *sf, int every, float *ckpt, float *o,
+                                       float scale, void *workspace, hipStream_t stream);
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kda_status check_dims(int dk, int dv, kda_dtype dt) {
+    if (dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARGUMENT;
+    if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+// Validation shared by kda_chunk_fwd and the workspace query.
+kda_status validate_fwd(const kda_fwd_args *a) {
+    if (!a) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->struct_size != sizeof(kda_fwd_args)) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->num_seqs < 0 || a->total_tokens < 0 || a->num_heads <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    const kda_status d = check_dims(a->dk, a->dv, a->in_dtype);
+    if (d != KDA_OK) return d;
+    if (a->chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+    if (a->checkpoint_every < 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->checkpoint_every > 0 && a->checkpoint_every % a->chunk_size != 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!a->cu_seqlens_host) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->num_seqs > 0 && !a->cu_seqlens) return KDA_ERR_INVALID_ARGUMENT;
+    const int32_t *cu = a->cu_seqlens_host;
+    if (cu[0] != 0) return KDA_ERR_INVALID_ARGUMENT;
+    for (int n = 0; n < a->num_seqs; ++n)
+        if (cu[n + 1] < cu[n]) return KDA_ERR_INVALID_ARGUMENT;
+    if (cu[a->num_seqs] != a->total_tokens) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->total_tokens > 0) {
+        if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->g) ||
+            !aligned16(a->beta) || !aligned16(a->o))
+            return KDA_ERR_INVALID_ARGUMENT;
+        if ((const void *)a->o == a->q || (const void *)a->o == a->k || (const void *)a->o == a->v ||
+            (const void *)a->o == a->g || (const void *)a->o == a->beta)
+            return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if ((a->initial_state && !aligned16(a->initial_state)) || (a->final_state && !aligned16(a->final_state)))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (a->checkpoint_every > 0) {
+        int64_t m = 0;
+        for (int n = 0; n < a->num_seqs; ++n) m += (cu[n + 1] - cu[n]) / a->checkpoint_every;
+        if (m > 0 && (!a->checkpoints || !aligned16(a->checkpoints))) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if (!(a->scale == a->scale)) return KDA_ERR_INVALID_ARGUMENT;  // NaN scale
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_status_str(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+        case KDA_ERR_DEVICE: return "KDA_ERR_DEVICE";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+size_t kda_chunk_fwd_workspace_bytes(const kda_fwd_args *a) {
+    if (validate_fwd(a) != KDA_OK) return 0;
+    return kda_chunk_workspace_layout(a->num_seqs, nullptr, nullptr);
+}
+
+kda_status kda_chunk_fwd(const kda_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
+    const kda_status st = validate_fwd(a);
+    if (st != KDA_OK) return st;
+    const size_t need = kda_chunk_workspace_layout(a->num_seqs, nullptr, nullptr);
+    if (a->num_seqs > 0) {
+        if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if (a->num_seqs == 0) return KDA_OK;
+    const hipError_t e = kda_launch_chunk(a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->q, a->k,
+                                          a->v, a->g, a->beta, a->cu_seqlens, a->initial_state, a->final_state,
+                                          a->checkpoint_every, a->checkpoints, a->o, a->scale, workspace,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+kda_status kda_decode_step(const kda_decode_args *a, void *stream) {
+    if (!a || a->struct_size != sizeof(kda_decode_args)) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->num_seqs < 0 || a->num_heads <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    const kda_status d = check_dims(a->dk, a->dv, a->in_dtype);
+    if (d != KDA_OK) return d;
+    if (a->state_indices) return KDA_ERR_UNSUPPORTED;
+    if (!(a->scale == a->scale)) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->num_seqs == 0) return KDA_OK;
+    if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->state || !a->o) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(a->state) || !aligned16(a->o) || !aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) ||
+        !aligned16(a->g) || !aligned16(a->beta))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if ((void *)a->o == (void *)a->state) return KDA_ERR_INVALID_ARGUMENT;
+    const hipError_t e = kda_launch_decode(a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->q, a->k,
+                                           a->v, a->g, a->beta, a->state, a->o, a->scale,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,722 @@
+// kda_chunk.hip -- chunked KDA prefill over packed variable-length sequences (gfx950).
+//
+// Operator: per (sequence, head), tokens in order,
+//     S <- Diag(exp(g_t)) S ;  u_t = beta_t (v_t - S^T k_t) ;  S <- S + k_t u_t^T ;  o_t = scale S^T q_t
+// (the gated delta rule with a per-channel forget gate: "Attention->K3 course,
+// Day 21", quiz Q9 and answer D19; skillsmp K3 skill card, quick facts).
+//
+// Chunk-recurrent form (chunk C = 64, the entering state S, G_r = log-decay
+// summed over the chunk up to row r, Gamma = exp(G)):
+//     A_kk[r,i] = beta_r sum_c k_rc k_ic e^{G_rc - G_ic}   (i <  r)
+//     A_qk[r,i] =        sum_c q_rc k_ic e^{G_rc - G_ic}   (i <= r)
+//     T   = (I + A_kk)^{-1} Diag(beta)
+//     U   = T (V - (Gamma*K) S)                        delta-rule residuals of the chunk
+//     O   = scale [ (Gamma*Q) S + A_qk U ]
+//     S  <- Diag(Gamma_last) S + (e^{G_last - G} * K)^T U
+// ("parallel inside a chunk, recurrent across chunks": scripod show notes,
+// chapter 2.1; the bounded log-decay g >= -5 from the K3 skill card's quick
+// facts is what lets the pairwise decay factor be split per 16-row sub-chunk,
+// e^{G_r - G_i} = e^{G_r - G_ref} e^{G_ref - G_i}, with both factors inside fp32
+// range because 16 * 5 = 80 < 88, so every Gram tile is a dense MFMA product).
+//
+// Design (one workgroup per (sequence, head), NW = d_v/16 waves):
+//   * Decay factors come from exp(g) and running products inside each 16-row
+//     sub-chunk (E_start: from the sub-chunk start, E_end: to its end), never
+//     from exponentials of long sums.
+//   * Gram tiles A_kk, A_qk: 10 lower 16x16 tiles each, as MFMA products of
+//     Ks_a = k * E_start (rows of sub-chunk a) with Kn^(a)_b = k * e^{G_ref(a) - G}
+//     (rows of sub-chunk b <= a); operands in hi+lo bf16 (3 MFMA passes).
+//   * T: the four 16x16 diagonal inverses by forward substitution (one wave),
+//     then the off-diagonal blocks by fp32-MFMA block products (32x32 blocked
+//     inverse), in fp32.
+//   * The recurrence is separable over value columns, so wave w owns value
+//     columns [16w, 16w+16): it keeps its d_k x 16 slice of S in registers (fp32)
+//     for the whole sequence and runs U, O and the state update for its slice
+//     with no inter-wave traffic; the d_v-independent operands (T, A_qk,
+//     Gamma*K, Gamma*Q, e^{G_last-G}*K) are shared through LDS.
+//   * Precision (bf16 inputs): every product that feeds the outputs is formed
+//     from hi+lo bf16 operand pairs except V - (Gamma*K) S, which uses single bf16
+//     operands; accumulation is fp32; o and S are fp32.  The fp32 path uses fp32
+//     MFMA throughout.
+#include "kda_common.h"
+
+namespace kda {
+
+constexpr int CH = 64;    // chunk size (tokens)
+constexpr int SUB = 16;   // sub-chunk size (rows of one MFMA tile)
+constexpr int TP = 20;    // row pitch (floats) of the fp32 16x16 tiles used by the inverse
+constexpr int TSZ = 16 * TP;
+
+// ---- fragment-major LDS operand layout ---------------------------------------
+// A matrix with R rows and K contraction columns is stored in blocks of 16 rows
+// x 32 columns; inside a block, the 8 values lane l feeds to one MFMA K-step
+// are contiguous (16 B as bf16, 32 B as fp32) so a fragment is one wide read.
+// Column k of a block maps to (lane group q, slot e):
+//     k%32 <  16 : q = (k%16)/4, e = k%4          k%32 >= 16 : q = (k%16)/4, e = 4 + k%4
+// which is also the row order of a pair of 16x16 MFMA output tiles, so an
+// output pair can be fed back as an operand straight from registers.
+__device__ __forceinline__ int frag_slot(int rr, int q, int kb) { return 16 * q + (rr ^ ((2 * q + 8 * kb) & 15)); }
+
+template <int KB>
+__device__ __forceinline__ int fofs(int r, int k) {
+    const int rb = r >> 4, rr = r & 15, kb = k >> 5, kk = k & 31;
+    const int q = (kk & 15) >> 2, e = (kk & 3) | ((kk >> 4) << 2);
+    return ((rb * KB + kb) * 64 + frag_slot(rr, q, kb)) * 8 + e;
+}
+template <int KB>
+__device__ __forceinline__ int fbase(int rb, int kb, int lane) {
+    return ((rb * KB + kb) * 64 + frag_slot(lane & 15, lane >> 4, kb)) * 8;
+}
+// 64x64 lower-block-triangular matrices (T, A_qk): only blocks (rb, kb <= rb/2) exist.
+__device__ __forceinline__ int tri_block(int rb, int kb) { return rb < 2 ? rb : 2 + 2 * (rb - 2) + kb; }
+__device__ __forceinline__ int tofs(int r, int k) {
+    const int rb = r >> 4, rr = r & 15, kb = k >> 5, kk = k & 31;
+    const int q = (kk & 15) >> 2, e = (kk & 3) | ((kk >> 4) << 2);
+    return (tri_block(rb, kb) * 64 + frag_slot(rr, q, kb)) * 8 + e;
+}
+__device__ __forceinline__ int tbase(int rb, int kb, int lane) {
+    return (tri_block(rb, kb) * 64 + frag_slot(lane & 15, lane >> 4, kb)) * 8;
+}
+
+// ---- precision policies -------------------------------------------------------
+template <bool F32P> struct Frag;
+template <> struct Frag<false> { bf16x8_t hi, lo; };
+template <> struct Frag<true> { float v[8]; };
+
+// Matrix storage: "HL" = value carried at ~16 bits (bf16 hi + lo planes, or fp32),
+// "H" = single precision carrier (one bf16 plane, or fp32).
+template <bool F32P> struct Mat;
+template <> struct Mat<false> {
+    static constexpr int ES = 2;  // element bytes per plane
+    template <int N> __device__ static void put_hl(char *base, int plane_bytes, int off, const float (&x)[N]) {
+        __bf16 *hi = reinterpret_cast<__bf16 *>(base) + off;
+        __bf16 *lo = reinterpret_cast<__bf16 *>(base + plane_bytes) + off;
+        if constexpr (N == 2) {
+            __bf16 h0, l0, h1, l1;
+            split_hl(x[0], h0, l0);
+            split_hl(x[1], h1, l1);
+            *reinterpret_cast<uint32_t *>(hi) = (uint32_t)bf16_raw(h0) | ((uint32_t)bf16_raw(h1) << 16);
+            *reinterpret_cast<uint32_t *>(lo) = (uint32_t)bf16_raw(l0) | ((uint32_t)bf16_raw(l1) << 16);
+        } else if constexpr (N == 4) {
+            __bf16 h[4], l[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) split_hl(x[i], h[i], l[i]);
+            uint2 H, L;
+            H.x = (uint32_t)bf16_raw(h[0]) | ((uint32_t)bf16_raw(h[1]) << 16);
+            H.y = (uint32_t)bf16_raw(h[2]) | ((uint32_t)bf16_raw(h[3]) << 16);
+            L.x = (uint32_t)bf16_raw(l[0]) | ((uint32_t)bf16_raw(l[1]) << 16);
+            L.y = (uint32_t)bf16_raw(l[2]) | ((uint32_t)bf16_raw(l[3]) << 16);
+            *reinterpret_cast<uint2 *>(hi) = H;
+            *reinterpret_cast<uint2 *>(lo) = L;
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; ++i) split_hl(x[i], hi[i], lo[i]);
+        }
+    }
+    __device__ static void put_hl1(char *base, int plane_bytes, int off, float x) {
+        __bf16 h, l;
+        split_hl(x, h, l);
+        reinterpret_cast<__bf16 *>(base)[off] = h;
+        reinterpret_cast<__bf16 *>(base + plane_bytes)[off] = l;
+    }
+    __device__ static void put_h2(char *base, int off, float x0, float x1) {
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<__bf16 *>(base) + off) =
+            (uint32_t)bf16_raw(to_bf16(x0)) | ((uint32_t)bf16_raw(to_bf16(x1)) << 16);
+    }
+    template <bool LO> __device__ static Frag<false> get(const char *base, int plane_bytes, int off) {
+        Frag<false> f;
+        f.hi = *reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(base) + off);
+        if constexpr (LO) f.lo = *reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(base + plane_bytes) + off);
+        return f;
+    }
+    // Operand fragment from two 16x16 output tiles covering contraction rows
+    // [32s, 32s+16) and [32s+16, 32s+32) (hi only, or hi+lo).
+    template <bool LO> __device__ static Frag<false> from_tiles(const f32x4_t &t0, const f32x4_t &t1) {
+        Frag<false> f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (LO) {
+                __bf16 h, l;
+                split_hl(t0[e], h, l); f.hi[e] = h; f.lo[e] = l;
+                split_hl(t1[e], h, l); f.hi[4 + e] = h; f.lo[4 + e] = l;
+            } else {
+                f.hi[e] = to_bf16(t0[e]);
+                f.hi[4 + e] = to_bf16(t1[e]);
+            }
+        }
+        return f;
+    }
+};
+template <> struct Mat<true> {
+    static constexpr int ES = 4;
+    template <int N> __device__ static void put_hl(char *base, int, int off, const float (&x)[N]) {
+        float *p = reinterpret_cast<float *>(base) + off;
+        if constexpr (N == 2) *reinterpret_cast<float2 *>(p) = make_float2(x[0], x[1]);
+        else if constexpr (N == 4) *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+        else {
+#pragma unroll
+            for (int i = 0; i < N; ++i) p[i] = x[i];
+        }
+    }
+    __device__ static void put_hl1(char *base, int, int off, float x) { reinterpret_cast<float *>(base)[off] = x; }
+    __device__ static void put_h2(char *base, int off, float x0, float x1) {
+        *reinterpret_cast<float2 *>(reinterpret_cast<float *>(base) + off) = make_float2(x0, x1);
+    }
+    template <bool LO> __device__ static Frag<true> get(const char *base, int, int off) {
+        Frag<true> f;
+        const float4 a = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + off);
+        const float4 b = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + off + 4);
+        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+        return f;
+    }
+    template <bool LO> __device__ static Frag<true> from_tiles(const f32x4_t &t0, const f32x4_t &t1) {
+        Frag<true> f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { f.v[e] = t0[e]; f.v[4 + e] = t1[e]; }
+        return f;
+    }
+};
+
+// acc += A * B over one 32-wide K-step.  bf16: hi*hi (+ lo*hi) (+ hi*lo).
+template <bool ALO, bool BLO>
+__device__ __forceinline__ void mma(f32x4_t &acc, const Frag<false> &a, const Frag<false> &b) {
+    if constexpr (ALO) acc = mfma_bf16(a.lo, b.hi, acc);
+    if constexpr (BLO) acc = mfma_bf16(a.hi, b.lo, acc);
+    acc = mfma_bf16(a.hi, b.hi, acc);
+}
+template <bool ALO, bool BLO>
+__device__ __forceinline__ void mma(f32x4_t &acc, const Frag<true> &a, const Frag<true> &b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = mfma_f32(a.v[e], b.v[e], acc);
+}
+
+// ---- fp32 16x16 tile products for the triangular inverse ------------------------
+// Tiles are row-major [16][TP] fp32 in LDS.  In instruction kk lane l feeds
+// k = 4*(l/16) + kk, which matches the row order of an output tile held in
+// registers (element kk of lane l is row 4*(l/16) + kk).
+__device__ __forceinline__ void tmm_ll(f32x4_t &acc, const float *A, const float *B, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(A[r * TP + 4 * q + kk], B[(4 * q + kk) * TP + r], acc);
+}
+__device__ __forceinline__ void tmm_lr(f32x4_t &acc, const float *A, const f32x4_t &R, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(A[r * TP + 4 * q + kk], R[kk], acc);
+}
+__device__ __forceinline__ void tile_store(float *Tl, const f32x4_t &v, int lane) {
+    const int c = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Tl[(4 * q + e) * TP + c] = v[e];
+}
+
+__host__ __device__ constexpr int vidx(int a, int b) { return a * (a + 1) / 2 + b; }
+
+// ---- LDS map -------------------------------------------------------------------
+template <int DK, bool F32P>
+struct Lds {
+    static constexpr int ES = Mat<F32P>::ES;
+    // Gram phase (region G)
+    static constexpr int KQS_PLANE = 64 * DK * ES;             // Ks, later Qs
+    static constexpr int KN_PLANE = 160 * DK * ES;             // Kn^(a)_b, 10 row blocks
+    static constexpr int KQS = 0;
+    static constexpr int KN = KQS + 64 * DK * 4;
+    static constexpr int G_END = KN + 160 * DK * 4;
+    // scan operands (region X, aliases G)
+    static constexpr int GK = 0;                               // Gamma*K   [64][DK]   single carrier
+    static constexpr int QT_PLANE = 64 * DK * ES;              // Gamma*Q   [64][DK]   hl
+    static constexpr int QT = GK + 64 * DK * ES;
+    static constexpr int KHT_PLANE = DK * 64 * ES;             // (e^{G_last-G}*K)^T [DK][64]  hl
+    static constexpr int KHT = QT + 64 * DK * 4;
+    static constexpr int X_END = KHT + DK * 64 * 4;
+    static_assert(X_END <= G_END, "scan operands must fit in the Gram region");
+    // region Y: T and A_qk, 6 blocks each, hl
+    static constexpr int TRI_PLANE = 6 * 64 * 8 * ES;
+    static constexpr int TM = G_END;
+    static constexpr int AQK = TM + 6 * 64 * 8 * 4;
+    // region Z: 14 fp32 16x16 tiles for the inverse (L/M tiles 0..9, X tiles 10..13)
+    static constexpr int Z = AQK + 6 * 64 * 8 * 4;
+    static constexpr int XCHG = Z;                             // [8][DK] fp32 half-products, aliases Z
+    static constexpr int Z_END = Z + 14 * TSZ * 4;
+    static_assert(8 * DK * 4 <= 14 * TSZ * 4, "exchange buffer must fit in Z");
+    static constexpr int BETA = Z_END;                         // [64] fp32
+    static constexpr int GC = BETA + 64 * 4;                   // [DK] fp32
+    static constexpr int TOTAL = GC + DK * 4;
+};
+
+struct ChunkParams {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const int32_t *cu_seqlens;
+    const int32_t *order;          // sequences, longest first
+    const int64_t *ckpt_base;      // per sequence: index of its first checkpoint
+    const float *s0;
+    float *sf;
+    float *ckpt;
+    float *o;
+    int H;
+    int every;
+    float scale;
+};
+
+template <int DK, bool F32P, typename IN_T>
+__global__ void __launch_bounds__(DK * 4)
+chunk_fwd_kernel(const ChunkParams p) {
+    constexpr int DV = DK;
+    constexpr int NW = DV / 16;          // waves; wave w owns value columns [16w, 16w+16)
+    constexpr int NT = NW * 64;
+    constexpr int KB = DK / 32;          // K-steps over d_k
+    constexpr int KT = DK / 16;          // 16-row tiles over d_k
+    constexpr int NCP = DK / 2;          // channel pairs
+    using L = Lds<DK, F32P>;
+    using M = Mat<F32P>;
+    using F = Frag<F32P>;
+    static_assert(NT / NCP == 8, "8 row groups of 8 rows");
+
+    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+    float *zt = reinterpret_cast<float *>(smem + L::Z);
+    float *s_beta = reinterpret_cast<float *>(smem + L::BETA);
+    float *s_gc = reinterpret_cast<float *>(smem + L::GC);
+    float *s_xchg = reinterpret_cast<float *>(smem + L::XCHG);
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    const int h = blockIdx.x % p.H;
+    const int n = p.order[blockIdx.x / p.H];
+    const int seq_start = p.cu_seqlens[n];
+    const int seq_len = p.cu_seqlens[n + 1] - seq_start;
+    const int H = p.H;
+
+    // Elementwise role: channel pair cp (channels 2cp, 2cp+1), rows [8 rg, 8 rg + 8).
+    const int cp = tid % NCP, rg = tid / NCP;
+    const int c0 = 2 * cp;
+    const int sa = rg >> 1, hf = rg & 1;   // sub-chunk and half of this row group
+
+    // Scan role: value columns [j0, j0 + 16).
+    const int j0 = 16 * wave;
+
+    // Zero the structurally-zero tiles of T and A_qk (upper tiles (0,1) and (2,3)).
+    for (int idx = tid; idx < 2 * 16 * 16; idx += NT) {
+        const int t = idx >> 8, rr = (idx >> 4) & 15, cc = idx & 15;
+        const int r = t == 0 ? rr : 32 + rr, c = t == 0 ? 16 + cc : 48 + cc;
+        M::put_hl1(smem + L::TM, L::TRI_PLANE, tofs(r, c), 0.f);
+        M::put_hl1(smem + L::AQK, L::TRI_PLANE, tofs(r, c), 0.f);
+    }
+
+    // State slice in registers: Sr[ct][e] = S[16 ct + 4 lq + e][j0 + lr].
+    f32x4_t Sr[KT];
+    const size_t st_off = ((size_t)n * H + h) * DK * DV;
+#pragma unroll
+    for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            Sr[ct][e] = p.s0 ? p.s0[st_off + (size_t)(16 * ct + 4 * lq + e) * DV + j0 + lr] : 0.f;
+
+    const IN_T *qg = reinterpret_cast<const IN_T *>(p.q);
+    const IN_T *kg = reinterpret_cast<const IN_T *>(p.k);
+    const IN_T *vg = reinterpret_cast<const IN_T *>(p.v);
+    const int nchunks = (seq_len + CH - 1) / CH;
+
+    for (int ci = 0; ci < nchunks; ++ci) {
+        const int t0 = seq_start + ci * CH;
+        const int nvalid = min(CH, seq_len - ci * CH);
+
+        // -- value slice for the scan, fetched early ------------------------------
+        f32x4_t Vt[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + 4 * lq + e;
+                Vt[rt][e] = r < nvalid ? load_in(vg + ((size_t)(t0 + r) * H + h) * DV + j0 + lr) : 0.f;
+            }
+
+        // -- S1: inputs, per-channel decay products ------------------------------
+        float kv[8][2], qv[8][2], Es[8][2], Ee[8][2];
+        {
+            float al[8][2];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * rg + i;
+                if (r < nvalid) {
+                    const size_t off = ((size_t)(t0 + r) * H + h) * DK + c0;
+                    kv[i][0] = load_in(kg + off); kv[i][1] = load_in(kg + off + 1);
+                    qv[i][0] = load_in(qg + off); qv[i][1] = load_in(qg + off + 1);
+                    const float2 gg = *reinterpret_cast<const float2 *>(p.g + off);
+                    al[i][0] = __expf(gg.x); al[i][1] = __expf(gg.y);
+                } else {
+                    kv[i][0] = kv[i][1] = qv[i][0] = qv[i][1] = 0.f;
+                    al[i][0] = al[i][1] = 1.f;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                float f = 1.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) { f *= al[i][c]; Es[i][c] = f; }
+                float b = 1.f;
+#pragma unroll
+                for (int i = 7; i >= 0; --i) { Ee[i][c] = b; b *= al[i][c]; }
+                s_xchg[rg * DK + c0 + c] = f;   // product over this row group
+            }
+            if (cp == 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 8 * rg + i;
+                    s_beta[r] = r < nvalid ? p.beta[(size_t)(t0 + r) * H + h] : 0.f;
+                }
+            }
+        }
+        __syncthreads();
+        float Pm[4][2], pre[2], post[2], cfac[4][2];
+        {
+            float hp[8][2];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) { hp[m][0] = s_xchg[m * DK + c0]; hp[m][1] = s_xchg[m * DK + c0 + 1]; }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) Pm[m][c] = hp[2 * m][c] * hp[2 * m + 1][c];
+                // rows of the first half before us / of the second half after us
+                const float lead = hf ? s_xchg[(rg - 1) * DK + c0 + c] : 1.f;
+                const float tail = hf ? 1.f : s_xchg[(rg + 1) * DK + c0 + c];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) { Es[i][c] *= lead; Ee[i][c] *= tail; }
+                float pr = 1.f, po = 1.f;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) { if (m < sa) pr *= Pm[m][c]; if (m > sa) po *= Pm[m][c]; }
+                pre[c] = pr; post[c] = po;
+                // column-side factor of tile (a', sa): 1/P_sa on the diagonal, else the
+                // decay of the sub-chunks strictly between sa and a'
+                float run = 1.f;
+#pragma unroll
+                for (int ap = 0; ap < 4; ++ap) {
+                    if (ap == sa) cfac[ap][c] = 1.f / Pm[sa][c];
+                    else if (ap > sa) { cfac[ap][c] = run; run *= Pm[ap][c]; }
+                    else cfac[ap][c] = 0.f;
+                }
+            }
+            if (rg == 0) {
+                s_gc[c0] = Pm[0][0] * Pm[1][0] * Pm[2][0] * Pm[3][0];
+                s_gc[c0 + 1] = Pm[0][1] * Pm[1][1] * Pm[2][1] * Pm[3][1];
+            }
+        }
+
+        // -- S2: Gram operands Ks (rows of sub-chunk sa) and Kn^(a')_sa ------------------
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            const float ks[2] = {kv[i][0] * Es[i][0], kv[i][1] * Es[i][1]};
+            M::template put_hl<2>(smem + L::KQS, L::KQS_PLANE, fofs<KB>(r, c0), ks);
+#pragma unroll
+            for (int ap = 0; ap < 4; ++ap) {
+                if (ap < sa) continue;
+                const int vr = 16 * vidx(ap, sa) + (r - 16 * sa);
+                const float kn[2] = {kv[i][0] * Ee[i][0] * cfac[ap][0], kv[i][1] * Ee[i][1] * cfac[ap][1]};
+                M::template put_hl<2>(smem + L::KN, L::KN_PLANE, fofs<KB>(vr, c0), kn);
+            }
+        }
+        __syncthreads();
+
+        // -- S3: A_kk tiles (transposed products: lane holds A[16a+lr][16b+4lq+e]) --------
+        for (int t = wave; t < 10; t += NW) {
+            const int a = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+            const int b = t - vidx(a, 0);
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KB; ++s) {
+                const F fa = M::template get<true>(smem + L::KN, L::KN_PLANE, fbase<KB>(vidx(a, b), s, lane));
+                const F fb = M::template get<true>(smem + L::KQS, L::KQS_PLANE, fbase<KB>(a, s, lane));
+                mma<true, true>(acc, fa, fb);
+            }
+            const float br = s_beta[16 * a + lr];
+            float4 w;
+            float *wv = reinterpret_cast<float *>(&w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * lq + e;
+                wv[e] = (b < a || i < lr) ? br * acc[e] : 0.f;
+            }
+            *reinterpret_cast<float4 *>(zt + vidx(a, b) * TSZ + lr * TP + 4 * lq) = w;
+        }
+        __syncthreads();
+
+        // -- S4: Qs over Ks; diagonal blocks of (I + A_kk)^{-1} (wave 0) --------------
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            const float qs[2] = {qv[i][0] * Es[i][0], qv[i][1] * Es[i][1]};
+            M::template put_hl<2>(smem + L::KQS, L::KQS_PLANE, fofs<KB>(r, c0), qs);
+        }
+        if (wave == 0) {
+            const int a = lane >> 4, j = lane & 15;
+            float *Lt = zt + vidx(a, a) * TSZ;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == j) ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) acc -= Lt[r * TP + i] * x[i];
+                x[r] = acc;
+            }
+            const float bj = s_beta[16 * a + j];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                Lt[r * TP + j] = x[r];
+                M::put_hl1(smem + L::TM, L::TRI_PLANE, tofs(16 * a + r, 16 * a + j), x[r] * bj);
+            }
+        }
+        __syncthreads();
+
+        // -- S5: A_qk tiles; level-1 off-diagonal inverse blocks M10, M32 --------------
+        for (int t = wave; t < 10; t += NW) {
+            const int a = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+            const int b = t - vidx(a, 0);
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KB; ++s) {
+                const F fa = M::template get<true>(smem + L::KN, L::KN_PLANE, fbase<KB>(vidx(a, b), s, lane));
+                const F fb = M::template get<true>(smem + L::KQS, L::KQS_PLANE, fbase<KB>(a, s, lane));
+                mma<true, true>(acc, fa, fb);
+            }
+            float w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (b < a || 4 * lq + e <= lr) ? acc[e] : 0.f;
+            M::template put_hl<4>(smem + L::AQK, L::TRI_PLANE, tofs(16 * a + lr, 16 * b + 4 * lq), w);
+        }
+        if (wave == NW - 1 || wave == NW - 2) {
+            // M_{a,a-1} = -M_aa L_{a,a-1} M_{a-1,a-1} for a = 1 (wave NW-2) and a = 3 (wave NW-1)
+            const int a = wave == NW - 2 ? 1 : 3;
+            f32x4_t R = {0.f, 0.f, 0.f, 0.f}, Mo = {0.f, 0.f, 0.f, 0.f};
+            tmm_ll(R, zt + vidx(a, a - 1) * TSZ, zt + vidx(a - 1, a - 1) * TSZ, lane);
+            tmm_lr(Mo, zt + vidx(a, a) * TSZ, R, lane);
+            const float bj = s_beta[16 * (a - 1) + lr];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Mo[e] = -Mo[e];
+                M::put_hl1(smem + L::TM, L::TRI_PLANE, tofs(16 * a + 4 * lq + e, 16 * (a - 1) + lr), Mo[e] * bj);
+            }
+            tile_store(zt + vidx(a, a - 1) * TSZ, Mo, lane);
+        }
+        __syncthreads();
+
+        // -- S6: scan operands (region X over G); X = L_BL M_TL (waves 0..3) ------------
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            M::put_h2(smem + L::GK, fofs<KB>(r, c0), kv[i][0] * Es[i][0] * pre[0], kv[i][1] * Es[i][1] * pre[1]);
+            const float qt[2] = {qv[i][0] * Es[i][0] * pre[0], qv[i][1] * Es[i][1] * pre[1]};
+            M::template put_hl<2>(smem + L::QT, L::QT_PLANE, fofs<KB>(r, c0), qt);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            const int r = 8 * rg + i;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const float kh[2] = {kv[i][c] * Ee[i][c] * post[c], kv[i + 1][c] * Ee[i + 1][c] * post[c]};
+                M::template put_hl<2>(smem + L::KHT, L::KHT_PLANE, fofs<2>(c0 + c, r), kh);
+            }
+        }
+        if (wave < 4) {
+            // X_20 = L20 M00 + L21 M10 ; X_21 = L21 M11 ; X_30 = L30 M00 + L31 M10 ; X_31 = L31 M11
+            const int a = 2 + (wave >> 1), b = wave & 1;
+            f32x4_t X = {0.f, 0.f, 0.f, 0.f};
+            if (b == 0) {
+                tmm_ll(X, zt + vidx(a, 0) * TSZ, zt + vidx(0, 0) * TSZ, lane);
+                tmm_ll(X, zt + vidx(a, 1) * TSZ, zt + vidx(1, 0) * TSZ, lane);
+            } else {
+                tmm_ll(X, zt + vidx(a, 1) * TSZ, zt + vidx(1, 1) * TSZ, lane);
+            }
+            tile_store(zt + (10 + wave) * TSZ, X, lane);
+        }
+        __syncthreads();
+
+        // -- S7: M_BL = -M_BR X (waves 0..3) and its T blocks ------------------------------
+        if (wave < 4) {
+            const int a = 2 + (wave >> 1), b = wave & 1;
+            f32x4_t Mo = {0.f, 0.f, 0.f, 0.f};
+            if (a == 2) {
+                tmm_ll(Mo, zt + vidx(2, 2) * TSZ, zt + (10 + b) * TSZ, lane);
+            } else {
+                tmm_ll(Mo, zt + vidx(3, 2) * TSZ, zt + (10 + b) * TSZ, lane);
+                tmm_ll(Mo, zt + vidx(3, 3) * TSZ, zt + (12 + b) * TSZ, lane);
+            }
+            const float bj = s_beta[16 * b + lr];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                M::put_hl1(smem + L::TM, L::TRI_PLANE, tofs(16 * a + 4 * lq + e, 16 * b + lr), -Mo[e] * bj);
+        }
+        __syncthreads();
+
+        // -- S8: scan for value columns [j0, j0+16) ------------------------------------------
+        {
+            F SFh[KB], SFhl[KB];
+#pragma unroll
+            for (int s = 0; s < KB; ++s) {
+                SFh[s] = M::template from_tiles<false>(Sr[2 * s], Sr[2 * s + 1]);
+                SFhl[s] = M::template from_tiles<true>(Sr[2 * s], Sr[2 * s + 1]);
+            }
+            // Y = V - (Gamma*K) S
+            f32x4_t Y[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KB; ++s) {
+                    const F fa = M::template get<false>(smem + L::GK, 0, fbase<KB>(rt, s, lane));
+                    mma<false, false>(acc, fa, SFh[s]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Y[rt][e] = Vt[rt][e] - acc[e];
+            }
+            F YF[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) YF[s] = M::template from_tiles<true>(Y[2 * s], Y[2 * s + 1]);
+            // U = T Y
+            f32x4_t U[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s <= (rt >> 1); ++s) {
+                    const F fa = M::template get<true>(smem + L::TM, L::TRI_PLANE, tbase(rt, s, lane));
+                    mma<true, true>(acc, fa, YF[s]);
+                }
+                U[rt] = acc;
+            }
+            F UF[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) UF[s] = M::template from_tiles<true>(U[2 * s], U[2 * s + 1]);
+            // O = scale [ (Gamma*Q) S + A_qk U ]
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KB; ++s) {
+                    const F fa = M::template get<true>(smem + L::QT, L::QT_PLANE, fbase<KB>(rt, s, lane));
+                    mma<true, true>(acc, fa, SFhl[s]);
+                }
+#pragma unroll
+                for (int s = 0; s <= (rt >> 1); ++s) {
+                    const F fa = M::template get<true>(smem + L::AQK, L::TRI_PLANE, tbase(rt, s, lane));
+                    mma<true, true>(acc, fa, UF[s]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rt + 4 * lq + e;
+                    if (r < nvalid) p.o[((size_t)(t0 + r) * H + h) * DV + j0 + lr] = p.scale * acc[e];
+                }
+            }
+            // S <- Diag(Gamma_last) S + (e^{G_last-G} K)^T U
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) {
+                f32x4_t acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = s_gc[16 * ct + 4 * lq + e] * Sr[ct][e];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const F fa = M::template get<true>(smem + L::KHT, L::KHT_PLANE, fbase<2>(ct, s, lane));
+                    mma<true, true>(acc, fa, UF[s]);
+                }
+                Sr[ct] = acc;
+            }
+            // state snapshot at in-sequence positions that are multiples of `every`
+            if (p.every > 0 && nvalid == CH && ((ci + 1) * CH) % p.every == 0) {
+                const int64_t m = p.ckpt_base[n] + ((ci + 1) * CH) / p.every - 1;
+                float *dst = p.ckpt + ((size_t)m * H + h) * DK * DV;
+#pragma unroll
+                for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lq + e) * DV + j0 + lr] = Sr[ct][e];
+            }
+        }
+        __syncthreads();
+    }
+
+    if (p.sf) {
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.sf[st_off + (size_t)(16 * ct + 4 * lq + e) * DV + j0 + lr] = Sr[ct][e];
+    }
+}
+
+// Launch plan: sequences ordered longest first (ties: lower index first), so the
+// longest (sequence, head) chains are dispatched first; and, per sequence, the
+// index of its first checkpoint.  One workgroup.
+__global__ void __launch_bounds__(1024)
+plan_kernel(const int32_t *__restrict__ cu, int N, int every, int32_t *__restrict__ order,
+            int64_t *__restrict__ ckpt_base) {
+    for (int nn = threadIdx.x; nn < N; nn += blockDim.x) {
+        const int Ln = cu[nn + 1] - cu[nn];
+        int rank = 0;
+        for (int m = 0; m < N; ++m) {
+            const int Lm = cu[m + 1] - cu[m];
+            rank += (Lm > Ln) || (Lm == Ln && m < nn);
+        }
+        order[rank] = nn;
+    }
+    if (every > 0) {
+        __shared__ int64_t carry;
+        if (threadIdx.x == 0) carry = 0;
+        __syncthreads();
+        __shared__ int64_t part[1024];
+        for (int base = 0; base < N; base += blockDim.x) {
+            const int nn = base + threadIdx.x;
+            const int64_t c = nn < N ? (int64_t)((cu[nn + 1] - cu[nn]) / every) : 0;
+            part[threadIdx.x] = c;
+            __syncthreads();
+            for (int off = 1; off < (int)blockDim.x; off <<= 1) {   // inclusive scan
+                const int64_t v = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0;
+                __syncthreads();
+                part[threadIdx.x] += v;
+                __syncthreads();
+            }
+            if (nn < N) ckpt_base[nn] = carry + part[threadIdx.x] - c;
+            __syncthreads();
+            if (threadIdx.x == blockDim.x - 1) carry += part[threadIdx.x];
+            __syncthreads();
+        }
+    }
+}
+
+}  // namespace kda
+
+// Workspace: [order: N int32, padded to 256 B][ckpt_base: N int64].
+extern "C" __attribute__((visibility("hidden"))) size_t kda_chunk_workspace_layout(int N, size_t *order_off, size_t *base_off) {
+    const size_t o = 0, b = ((size_t)N * 4 + 255) / 256 * 256;
+    if (order_off) *order_off = o;
+    if (base_off) *base_off = b;
+    return b + ((size_t)N * 8 + 255) / 256 * 256 + 256;
+}
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int dk, int in_bf16, int N, int H, const void *q, const void *k,
+                                       const void *v, const float *g, const float *beta, const int32_t *cu,
+                                       const float *s0, float *sf, int every, float *ckpt, float *o,
+                                       float scale, void *workspace, hipStream_t stream) {
+    if (N == 0) return hipSuccess;
+    size_t oo, bo;
+    kda_chunk_workspace_layout(N, &oo, &bo);
+    int32_t *order = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + oo);
+    int64_t *base = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + bo);
+    hipLaunchKernelGGL(kda::plan_kernel, dim3(1), dim3(1024), 0, stream, cu, N, every, order, base);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
+    kda::ChunkParams p;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu_seqlens = cu; p.order = order;
+    p.ckpt_base = base; p.s0 = s0; p.sf = sf; p.ckpt = ckpt; p.o = o; p.H = H; p.every = every;
+    p.scale = scale;
+    const dim3 grid((unsigned)N * (unsigned)H);
+#define KDA_CHUNK(DKV, F32P, T) \
+    hipLaunchKernelGGL((kda::chunk_fwd_kernel<DKV, F32P, T>), grid, dim3(DKV * 4), 0, stream, p)
+    if (dk == 128 && in_bf16) KDA_CHUNK(128, false, uint16_t);
+    else if (dk == 128) KDA_CHUNK(128, true, float);
+    else if (dk == 64 && in_bf16) KDA_CHUNK(64, false, uint16_t);
+    else if (dk == 64) KDA_CHUNK(64, true, float);
+    else return hipErrorInvalidValue;
+#undef KDA_CHUNK
+    return hipGetLastError();
+}

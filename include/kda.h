@@ -1,0 +1,165 @@
+/*
+ * kda.h -- C ABI of libkda, an MI355X (gfx950) implementation of the Kimi
+ * Delta Attention (KDA) operator: a gated delta-rule linear attention with a
+ * per-channel forget gate.
+ *
+ * The operator (per sequence n, per head h, tokens t in order; S is d_k x d_v,
+ * fp32, row-major, one per (sequence, head)):
+ *
+ *     S   <- Diag(exp(g_t)) S                      per-channel forget gate
+ *     u_t  = beta_t * (v_t - S^T k_t)              delta-rule residual
+ *     S   <- S + k_t u_t^T                         targeted overwrite
+ *     o_t  = scale * S^T q_t                       read-out after the write
+ *
+ * i.e. S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ * alpha_t = exp(g_t).  Sources (pages on the Kimi K3 technical report):
+ *   - "Attention->K3 30-day course, Day 21", quiz Q9 (the delta rule: the old
+ *     memory predicts v_t and only the residual is written back), Q8 and
+ *     interview answer D19 (fixed d x d state formed as K^T V, per-channel
+ *     decay gate), D17 and Q5 (decode is memory-bound);
+ *   - skillsmp "kimi-k3-tech-report" skill card, quick facts: the log-decay is
+ *     a lower-bounded scaled sigmoid with g_min = -5, which lets the diagonal
+ *     tiles of the chunked form run as dense matrix-core products;
+ *   - t.iss.one digest of the report: a fixed-size recurrent state per KDA
+ *     layer, and prefix reuse at 512-token boundaries (the checkpoints below).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the name ends in _host.
+ *   - Layouts are token-major with heads interleaved and contiguous:
+ *       q, k, g : [tokens, H, d_k]   v, o : [tokens, H, d_v]   beta : [tokens, H]
+ *       states  : [sequences, H, d_k, d_v]  (row-major d_k x d_v per head)
+ *   - g is the natural-log decay.  Results are defined for g in [-5, 0] (the
+ *     range of -5*sigmoid(x)); values below -5 may overflow the in-chunk
+ *     factorisation.  Inputs must be finite.  Neither is checked.
+ *   - The caller owns every buffer, including the workspace; the library never
+ *     allocates device memory.  All work is enqueued asynchronously on
+ *     `stream` (a hipStream_t passed as void*; NULL = the default stream).
+ *   - Errors are returned synchronously as kda_status.  Argument validation is
+ *     pure host code and runs before any launch; a failed launch returns
+ *     KDA_ERR_DEVICE.  Faults during execution surface at the caller's next
+ *     synchronisation.
+ *   - Supported in ABI v1: d_k == d_v in {64, 128}; chunk_size == 64;
+ *     in_dtype KDA_F32 or KDA_BF16.  Other values -> KDA_ERR_UNSUPPORTED.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1u
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1,
+    KDA_ERR_UNSUPPORTED = 2,
+    KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+    KDA_ERR_DEVICE = 4
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * Chunked prefill over packed variable-length sequences.
+ *
+ * Sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]) of the packed token
+ * axis.  Each sequence is cut into chunks of `chunk_size` tokens aligned to its
+ * own start (the last may be partial; no chunk spans two sequences) and
+ * starts from its own initial state.
+ *
+ * Fields:
+ *   struct_size      sizeof(kda_fwd_args) as compiled by the caller.
+ *   num_seqs         N >= 0.  total_tokens: T >= 0, must equal cu_seqlens[N].
+ *   num_heads        H >= 1.   dk, dv: head dims.  chunk_size: 64.
+ *   in_dtype         element type of q, k, v (bf16 = raw 16-bit bf16 words).
+ *   scale            multiplies every output (o = scale * S^T q).
+ *   q, k, v, g, beta see layouts above; 16-byte aligned.
+ *   cu_seqlens       device int32 [N+1]; cu_seqlens_host: a host copy of the
+ *                    same values (validation and launch sizing without a device
+ *                    read).  The library does not check that they agree.
+ *   initial_state    NULL => zeros; else fp32 [N, H, dk, dv].
+ *   final_state      NULL => not written; else fp32 [N, H, dk, dv].  May alias
+ *                    initial_state (each (n,h) slice is read before it is written).
+ *   checkpoint_every 0 => none; else a positive multiple of chunk_size.  The state
+ *                    after in-sequence positions every*m, m = 1..floor(L_n/every),
+ *                    is written to `checkpoints`.
+ *   checkpoints      fp32 [sum_n floor(L_n/every), H, dk, dv], sequence-major then
+ *                    position.  Required iff checkpoint_every > 0.
+ *   o                fp32 [T, H, dv]; must not alias any input.
+ */
+typedef struct {
+    uint32_t struct_size;
+    int32_t num_seqs;
+    int32_t total_tokens;
+    int32_t num_heads;
+    int32_t dk;
+    int32_t dv;
+    int32_t chunk_size;
+    kda_dtype in_dtype;
+    float scale;
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *g;
+    const float *beta;
+    const int32_t *cu_seqlens;
+    const int32_t *cu_seqlens_host;
+    const float *initial_state;
+    float *final_state;
+    int32_t checkpoint_every;
+    float *checkpoints;
+    float *o;
+} kda_fwd_args;
+
+/* Device workspace (bytes) that kda_chunk_fwd needs for `args` (host only; no
+ * device access).  Returns 0 when args are invalid. */
+size_t kda_chunk_fwd_workspace_bytes(const kda_fwd_args *args);
+
+/* Enqueue the chunked forward.  `workspace` must hold at least
+ * kda_chunk_fwd_workspace_bytes(args) bytes of device memory, 256-byte aligned;
+ * it is scratch for the launch plan and is overwritten. */
+kda_status kda_chunk_fwd(const kda_fwd_args *args, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step: for each of N independent sequences and each head, consume
+ * one token and update that (sequence, head) state in place.
+ *   q, k, g : [N, H, dk]    v : [N, H, dv]    beta : [N, H]
+ *   state   : fp32 [N, H, dk, dv], read and overwritten in place
+ *   o       : fp32 [N, H, dv]
+ *   state_indices must be NULL in ABI v1.
+ */
+typedef struct {
+    uint32_t struct_size;
+    int32_t num_seqs;
+    int32_t num_heads;
+    int32_t dk;
+    int32_t dv;
+    kda_dtype in_dtype;
+    float scale;
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *g;
+    const float *beta;
+    float *state;
+    const int32_t *state_indices;
+    float *o;
+} kda_decode_args;
+
+kda_status kda_decode_step(const kda_decode_args *args, void *stream);
+
+/* Static string for a status code. */
+const char *kda_status_str(kda_status status);
+
+/* KDA_ABI_VERSION of the library. */
+uint32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

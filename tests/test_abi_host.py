@@ -1,0 +1,178 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+symbol include/kda.h declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_49_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_49_amd import build
+        build.build()
+    return kda.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kda_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings(L):
+    assert kda.kda_abi_version() == 1
+    for code, name in enumerate(["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
+                                 "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_DEVICE"]):
+        assert kda.kda_status_str(code) == name
+    assert kda.kda_status_str(99) == "KDA_ERR_UNKNOWN"
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """Every field offset and the size of both argument structs, as compiled from
+    include/kda.h by the C compiler, equal the ctypes layouts of the binding."""
+    import subprocess
+    prog = ["#include <stdio.h>", "#include <stddef.h>", '#include "kda.h"', "int main(void) {"]
+    for cname, pyt in (("kda_fwd_args", kda.KdaFwdArgs), ("kda_decode_args", kda.KdaDecodeArgs)):
+        prog.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in pyt._fields_:
+            prog.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    prog.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(prog))
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)])
+    got = {}
+    for line in subprocess.check_output([str(exe)], text=True).splitlines():
+        c, f, v = line.split()
+        got[(c, f)] = int(v)
+    for cname, pyt in (("kda_fwd_args", kda.KdaFwdArgs), ("kda_decode_args", kda.KdaDecodeArgs)):
+        assert got[(cname, "size")] == ctypes.sizeof(pyt)
+        for f, _ in pyt._fields_:
+            assert got[(cname, f)] == getattr(pyt, f).offset, (cname, f)
+
+
+FAKE = 0x10000  # 64 KiB-aligned fake device address: never dereferenced by host validation
+
+
+def fwd_args(**over):
+    cu = over.pop("cu", [0, 100, 228])
+    cu_arr = (ctypes.c_int32 * len(cu))(*cu)
+    a = kda.KdaFwdArgs()
+    a.struct_size = ctypes.sizeof(kda.KdaFwdArgs)
+    a.num_seqs = len(cu) - 1
+    a.total_tokens = cu[-1]
+    a.num_heads = 4
+    a.dk = a.dv = 128
+    a.chunk_size = 64
+    a.in_dtype = kda.KDA_BF16
+    a.scale = 1.0
+    a.q, a.k, a.v, a.g, a.beta, a.o = (FAKE * (i + 1) for i in range(6))
+    a.cu_seqlens = FAKE * 8
+    a.cu_seqlens_host = ctypes.cast(cu_arr, ctypes.c_void_p).value
+    a.checkpoint_every = 0
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a, cu_arr
+
+
+def status(L, a, ws=FAKE * 16, ws_bytes=1 << 20):
+    return L.kda_chunk_fwd(ctypes.byref(a), ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("struct_size", 8, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("num_heads", 0, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("dk", 96, kda.KDA_ERR_UNSUPPORTED),
+    ("dv", 64, kda.KDA_ERR_UNSUPPORTED),
+    ("chunk_size", 32, kda.KDA_ERR_UNSUPPORTED),
+    ("in_dtype", 7, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("q", None, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("g", FAKE + 4, kda.KDA_ERR_INVALID_ARGUMENT),          # misaligned
+    ("o", FAKE * 1, kda.KDA_ERR_INVALID_ARGUMENT),          # aliases q
+    ("checkpoint_every", 100, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("checkpoint_every", 64, kda.KDA_ERR_INVALID_ARGUMENT),  # checkpoints pointer missing
+    ("total_tokens", 227, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("scale", float("nan"), kda.KDA_ERR_INVALID_ARGUMENT),
+])
+def test_fwd_validation(L, field, value, expect):
+    a, keep = fwd_args(**{field: value})
+    assert status(L, a) == expect
+    assert L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == 0
+
+
+@pytest.mark.parametrize("cu", [[1, 100], [0, 50, 40], [0, 100, 90, 228]])
+def test_bad_cu_seqlens(L, cu):
+    a, keep = fwd_args(cu=cu)
+    a.total_tokens = cu[-1]
+    assert status(L, a) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_checks(L):
+    a, keep = fwd_args()
+    need = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a))
+    assert need >= 2 * (4 + 8) and need % 256 == 0
+    assert status(L, a, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert status(L, a, ws=0) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert status(L, a, ws=FAKE * 16 + 64, ws_bytes=need) == kda.KDA_ERR_INVALID_ARGUMENT  # unaligned
+    # workspace grows with the number of sequences, not with tokens
+    b, keep2 = fwd_args(cu=[0] + [10 * (i + 1) for i in range(300)])
+    assert L.kda_chunk_fwd_workspace_bytes(ctypes.byref(b)) > need
+
+
+def test_empty_batch_is_a_no_op(L):
+    a, keep = fwd_args(cu=[0])
+    a.num_seqs, a.total_tokens = 0, 0
+    assert status(L, a, ws=0, ws_bytes=0) == kda.KDA_OK
+
+
+def decode_args(**over):
+    a = kda.KdaDecodeArgs()
+    a.struct_size = ctypes.sizeof(kda.KdaDecodeArgs)
+    a.num_seqs, a.num_heads, a.dk, a.dv = 8, 4, 128, 128
+    a.in_dtype = kda.KDA_BF16
+    a.scale = 1.0
+    a.q, a.k, a.v, a.g, a.beta, a.state, a.o = (FAKE * (i + 1) for i in range(7))
+    a.state_indices = None
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("struct_size", 4, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("dk", 32, kda.KDA_ERR_UNSUPPORTED),
+    ("state_indices", FAKE, kda.KDA_ERR_UNSUPPORTED),
+    ("state", None, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("state", FAKE + 8, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("o", FAKE * 6, kda.KDA_ERR_INVALID_ARGUMENT),          # aliases state
+    ("num_heads", -1, kda.KDA_ERR_INVALID_ARGUMENT),
+])
+def test_decode_validation(L, field, value, expect):
+    a = decode_args(**{field: value})
+    assert L.kda_decode_step(ctypes.byref(a), None) == expect
+
+
+def test_decode_empty_is_a_no_op(L):
+    a = decode_args(num_seqs=0)
+    assert L.kda_decode_step(ctypes.byref(a), None) == kda.KDA_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib
+    monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(kda, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        kda.lib()
