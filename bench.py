@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one chunked prefill of the long-context workload (T=65536 tokens,
+H=96 heads, d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state, initial state) plus one
+decode step of the decode workload (256 sequences x 96 heads, fp32 state
+[256,96,128,128] updated in place).  Inputs are seeded synthetic data
+(workloads.make_config) resident in HBM before the timed region.
+
+Prints ONE JSON line: value = prefill tokens/s; decode GB/s and the roofline
+of the dominant kernel are reported beside it; cpu_baseline times the fp64 CPU
+oracle on a bounded sample of the prefill workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "KDA prefill tokens/s (H=96,d=128) + decode state-update HBM GB/s, 1 GPU"
+
+
+def prefill_bytes(T, H, dk, dv, in_bytes=2, with_states=True):
+    """Algorithmic HBM bytes of one prefill launch: read q,k,v,g,beta once, write o once,
+    plus the initial/final states."""
+    per_tok_head = in_bytes * (2 * dk + dv) + 4 * dk + 4 + 4 * dv
+    return T * H * per_tok_head + (2 * H * dk * dv * 4 if with_states else 0)
+
+
+def decode_bytes(N, H, dk, dv, in_bytes=2):
+    """Algorithmic bytes of one decode step: state read + written once, token inputs, o."""
+    return N * H * (2 * dk * dv * 4 + in_bytes * (2 * dk + dv) + 4 * dk + 4 + 4 * dv)
+
+
+PREFILL_ALG_FLOP_PER_TOKHEAD = lambda C, dk, dv: 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
+    ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (profiling runs)")
+    ap.add_argument("--chunk", type=int, default=32, choices=(32, 64), help="token block of the chunked form")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(the operator shards by head / sequence with no communication, "
+                                   "but no multi-GPU path is built)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_49_amd as kda
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    t_gen = time.time()
+    wp = W.make_config(2)
+    wd = W.make_config(3)
+    gen_s = time.time() - t_gen
+
+    def up(x, dt):
+        return torch.from_numpy(x).to(dev, dt)
+
+    bf = torch.bfloat16
+    q, k, v = up(wp.q, bf), up(wp.k, bf), up(wp.v, bf)
+    g, beta = up(wp.g, torch.float32), up(wp.beta, torch.float32)
+    s0 = up(wp.s0, torch.float32)
+    T, H, dk = wp.q.shape
+    dv = wp.v.shape[2]
+    cu_h = torch.tensor(list(wp.cu_seqlens), dtype=torch.int32)
+    cu_d = cu_h.to(dev)
+    o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    sf = torch.empty_like(s0)
+    A = kda.make_fwd_args(q, k, v, g, beta, cu_d, cu_h, 1.0, s0, sf, 0, None, o, args.chunk)
+    L = kda.lib()
+    ws_bytes = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(A))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    N, Hd, dkd = wd.q.shape
+    dq, dk_, dvv = up(wd.q, bf), up(wd.k, bf), up(wd.v, bf)
+    dg, db = up(wd.g, torch.float32), up(wd.beta, torch.float32)
+    state = up(wd.s0, torch.float32)
+    od = torch.empty((N, Hd, wd.v.shape[2]), dtype=torch.float32, device=dev)
+    D = kda.make_decode_args(dq, dk_, dvv, dg, db, state, od, 1.0)
+    del wd
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    wsp, wsn = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel())
+
+    def prefill():
+        st = L.kda_chunk_fwd(ctypes.byref(A), wsp, wsn, sptr)
+        if st != 0:
+            raise RuntimeError(kda.kda_status_str(st))
+
+    def decode():
+        st = L.kda_decode_step(ctypes.byref(D), sptr)
+        if st != 0:
+            raise RuntimeError(kda.kda_status_str(st))
+
+    for _ in range(args.warmup):
+        prefill()
+        if not args.prefill_only:
+            decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        prefill()
+        ev[i][1].record(stream)
+        if not args.prefill_only:
+            decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    pre_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    pre_avg = float(np.mean(pre_ms))
+    dec_avg = float(np.mean(dec_ms)) if not args.prefill_only else None
+
+    tokens = T
+    value = tokens / (pre_avg * 1e-3)
+    pbytes = prefill_bytes(T, H, dk, dv)
+    pflop = PREFILL_ALG_FLOP_PER_TOKHEAD(args.chunk, dk, dv) * T * H
+    achieved_gbps = pbytes / (pre_avg * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; workloads.make_config 2 and 3)",
+        "config": {"workload": "prefill T=65536 H=96 d_k=d_v=128 bf16 q/k/v, fp32 g/beta/state, initial state; "
+                               "+ decode N=256 H=96 d=128 fp32 state in place",
+                   "chunk": args.chunk, "tokens_per_step": T, "heads": H},
+        "prefill": {"ms": round(pre_avg, 4), "ms_p10": round(float(np.percentile(pre_ms, 10)), 4),
+                    "ms_p90": round(float(np.percentile(pre_ms, 90)), 4), "tokens_per_s": round(value, 1),
+                    "alg_GBps": round(achieved_gbps, 1), "alg_TFLOPs": round(pflop / (pre_avg * 1e-3) / 1e12, 2),
+                    "alg_bytes": pbytes, "alg_flop": pflop},
+        "roofline": {"kernel": ("chunk32_kernel<128,bf16>" if args.chunk == 32 else "chunk_fwd_kernel<128,bf16>"), "bound": "hbm", "achieved": round(achieved_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+        "precision": "MFMA bf16 operands (hi+lo split pairs on all output-facing products), fp32 accumulate, "
+                     "fp32 o and state",
+        "gen_s": round(gen_s, 1),
+    }
+    if dec_avg is not None:
+        dbytes = decode_bytes(N, Hd, dkd, dvv.shape[2])
+        dgbps = dbytes / (dec_avg * 1e-3) / 1e9
+        res["decode"] = {"ms": round(dec_avg, 4), "GBps": round(dgbps, 1), "alg_bytes": dbytes,
+                         "frac_of_hbm_peak": round(dgbps / HBM_PEAK_GBPS, 4),
+                         "ms_p10": round(float(np.percentile(dec_ms, 10)), 4),
+                         "ms_p90": round(float(np.percentile(dec_ms, 90)), 4)}
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wp, args.cpu_seconds, H)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(wp, target_s, H_full):
+    """fp64 oracle on a bounded sample of the prefill workload: the first `Ts` tokens of
+    `Hs` heads (one chain per core), sized from a short calibration run to take about
+    target_s seconds; reported as equivalent tokens/s for all H_full heads."""
+    import numpy as np
+
+    import oracle
+    cores = oracle.default_threads()
+    Hs = min(cores, wp.q.shape[1])
+
+    def run(Ts):
+        sl = (slice(0, Ts), slice(0, Hs))
+        t = time.perf_counter()
+        oracle.forward(wp.q[sl], wp.k[sl], wp.v[sl], wp.g[sl], wp.beta[sl], None, 1.0,
+                       wp.s0[:, :Hs], n_threads=cores)
+        return time.perf_counter() - t
+
+    cal_T = 256
+    cal = run(cal_T)
+    Ts = int(min(wp.q.shape[0], max(cal_T, cal_T * target_s / max(cal, 1e-3))))
+    el = run(Ts)
+    tokhead_per_s = Ts * Hs / el
+    return {"value": round(tokhead_per_s / H_full, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {Ts} tokens x {Hs} heads of the T=65536 H=96 prefill (fp64 C recurrence, "
+                      f"{Hs} chains on {cores} threads), {el:.1f} s; value = token-heads/s / 96",
+            "seconds": round(el, 2)}
+
+
+if __name__ == "__main__":
+    main()

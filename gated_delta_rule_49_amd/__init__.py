@@ -113,8 +113,11 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+DEFAULT_CHUNK = 32
+
+
 def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final_state, checkpoint_every,
-                  checkpoints, o):
+                  checkpoints, o, chunk_size=DEFAULT_CHUNK):
     T, H, dk = q.shape
     a = KdaFwdArgs()
     a.struct_size = ctypes.sizeof(KdaFwdArgs)
@@ -123,7 +126,7 @@ def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final
     a.num_heads = int(H)
     a.dk = int(dk)
     a.dv = int(v.shape[2])
-    a.chunk_size = 64
+    a.chunk_size = int(chunk_size)
     a.in_dtype = _dtype_code(q)
     a.scale = float(scale)
     a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
@@ -138,12 +141,13 @@ def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final
 
 
 def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, output_final_state=True,
-                  checkpoint_every=0, stream=None):
+                  checkpoint_every=0, stream=None, chunk_size=DEFAULT_CHUNK):
     """Chunked KDA prefill (packed varlen).
 
     q, k: [T, H, dk]; v: [T, H, dv] (bf16 or fp32, CUDA, contiguous); g: [T, H, dk] fp32;
     beta: [T, H] fp32; cu_seqlens: int sequence offsets [N+1] (list / CPU or CUDA tensor,
     None = one sequence); initial_state: fp32 [N, H, dk, dv] or None.
+    chunk_size: token block of the chunked form, 32 (software-pipelined kernel) or 64.
     Returns (o [T,H,dv] fp32, final_state [N,H,dk,dv] fp32 or None, checkpoints or None).
     """
     T, H, dk = q.shape
@@ -163,7 +167,8 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
     if checkpoint_every:
         M = int(((cu_host[1:] - cu_host[:-1]) // checkpoint_every).sum())
         ck = torch.empty((M, H, dk, dv), dtype=torch.float32, device=dev)
-    a = make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, sf, checkpoint_every, ck, o)
+    a = make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, sf, checkpoint_every, ck, o,
+                      chunk_size)
     L = lib()
     ws_bytes = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a))
     if ws_bytes == 0 and N > 0:

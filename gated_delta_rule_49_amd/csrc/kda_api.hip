@@ -12,7 +12,7 @@ extern "C" hipError_t kda_launch_decode(int dk, int in_bf16, int N, int H, const
                                         const void *v, const float *g, const float *beta, float *state,
                                         float *o, float scale, hipStream_t stream);
 extern "C" size_t kda_chunk_workspace_layout(int N, size_t *order_off, size_t *base_off);
-extern "C" hipError_t kda_launch_chunk(int dk, int in_bf16, int N, int H, const void *q, const void *k,
+extern "C" hipError_t kda_launch_chunk(int chunk, int dk, int in_bf16, int N, int H, const void *q, const void *k,
                                        const void *v, const float *g, const float *beta, const int32_t *cu,
                                        const float *s0, float *sf, int every, float *ckpt, float *o,
                                        float scale, void *workspace, hipStream_t stream);
@@ -35,7 +35,7 @@ kda_status validate_fwd(const kda_fwd_args *a) {
     if (a->num_seqs < 0 || a->total_tokens < 0 || a->num_heads <= 0) return KDA_ERR_INVALID_ARGUMENT;
     const kda_status d = check_dims(a->dk, a->dv, a->in_dtype);
     if (d != KDA_OK) return d;
-    if (a->chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+    if (a->chunk_size != 32 && a->chunk_size != 64) return KDA_ERR_UNSUPPORTED;
     if (a->checkpoint_every < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (a->checkpoint_every > 0 && a->checkpoint_every % a->chunk_size != 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!a->cu_seqlens_host) return KDA_ERR_INVALID_ARGUMENT;
@@ -96,7 +96,7 @@ kda_status kda_chunk_fwd(const kda_fwd_args *a, void *workspace, size_t workspac
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_INVALID_ARGUMENT;
     }
     if (a->num_seqs == 0) return KDA_OK;
-    const hipError_t e = kda_launch_chunk(a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->q, a->k,
+    const hipError_t e = kda_launch_chunk(a->chunk_size, a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->q, a->k,
                                           a->v, a->g, a->beta, a->cu_seqlens, a->initial_state, a->final_state,
                                           a->checkpoint_every, a->checkpoints, a->o, a->scale, workspace,
                                           static_cast<hipStream_t>(stream));

@@ -38,180 +38,11 @@
 //     from hi+lo bf16 operand pairs except V - (Gamma*K) S, which uses single bf16
 //     operands; accumulation is fp32; o and S are fp32.  The fp32 path uses fp32
 //     MFMA throughout.
-#include "kda_common.h"
+#include "kda_frag.h"
 
 namespace kda {
 
 constexpr int CH = 64;    // chunk size (tokens)
-constexpr int SUB = 16;   // sub-chunk size (rows of one MFMA tile)
-constexpr int TP = 20;    // row pitch (floats) of the fp32 16x16 tiles used by the inverse
-constexpr int TSZ = 16 * TP;
-
-// ---- fragment-major LDS operand layout ---------------------------------------
-// A matrix with R rows and K contraction columns is stored in blocks of 16 rows
-// x 32 columns; inside a block, the 8 values lane l feeds to one MFMA K-step
-// are contiguous (16 B as bf16, 32 B as fp32) so a fragment is one wide read.
-// Column k of a block maps to (lane group q, slot e):
-//     k%32 <  16 : q = (k%16)/4, e = k%4          k%32 >= 16 : q = (k%16)/4, e = 4 + k%4
-// which is also the row order of a pair of 16x16 MFMA output tiles, so an
-// output pair can be fed back as an operand straight from registers.
-__device__ __forceinline__ int frag_slot(int rr, int q, int kb) { return 16 * q + (rr ^ ((2 * q + 8 * kb) & 15)); }
-
-template <int KB>
-__device__ __forceinline__ int fofs(int r, int k) {
-    const int rb = r >> 4, rr = r & 15, kb = k >> 5, kk = k & 31;
-    const int q = (kk & 15) >> 2, e = (kk & 3) | ((kk >> 4) << 2);
-    return ((rb * KB + kb) * 64 + frag_slot(rr, q, kb)) * 8 + e;
-}
-template <int KB>
-__device__ __forceinline__ int fbase(int rb, int kb, int lane) {
-    return ((rb * KB + kb) * 64 + frag_slot(lane & 15, lane >> 4, kb)) * 8;
-}
-// 64x64 lower-block-triangular matrices (T, A_qk): only blocks (rb, kb <= rb/2) exist.
-__device__ __forceinline__ int tri_block(int rb, int kb) { return rb < 2 ? rb : 2 + 2 * (rb - 2) + kb; }
-__device__ __forceinline__ int tofs(int r, int k) {
-    const int rb = r >> 4, rr = r & 15, kb = k >> 5, kk = k & 31;
-    const int q = (kk & 15) >> 2, e = (kk & 3) | ((kk >> 4) << 2);
-    return (tri_block(rb, kb) * 64 + frag_slot(rr, q, kb)) * 8 + e;
-}
-__device__ __forceinline__ int tbase(int rb, int kb, int lane) {
-    return (tri_block(rb, kb) * 64 + frag_slot(lane & 15, lane >> 4, kb)) * 8;
-}
-
-// ---- precision policies -------------------------------------------------------
-template <bool F32P> struct Frag;
-template <> struct Frag<false> { bf16x8_t hi, lo; };
-template <> struct Frag<true> { float v[8]; };
-
-// Matrix storage: "HL" = value carried at ~16 bits (bf16 hi + lo planes, or fp32),
-// "H" = single precision carrier (one bf16 plane, or fp32).
-template <bool F32P> struct Mat;
-template <> struct Mat<false> {
-    static constexpr int ES = 2;  // element bytes per plane
-    template <int N> __device__ static void put_hl(char *base, int plane_bytes, int off, const float (&x)[N]) {
-        __bf16 *hi = reinterpret_cast<__bf16 *>(base) + off;
-        __bf16 *lo = reinterpret_cast<__bf16 *>(base + plane_bytes) + off;
-        if constexpr (N == 2) {
-            __bf16 h0, l0, h1, l1;
-            split_hl(x[0], h0, l0);
-            split_hl(x[1], h1, l1);
-            *reinterpret_cast<uint32_t *>(hi) = (uint32_t)bf16_raw(h0) | ((uint32_t)bf16_raw(h1) << 16);
-            *reinterpret_cast<uint32_t *>(lo) = (uint32_t)bf16_raw(l0) | ((uint32_t)bf16_raw(l1) << 16);
-        } else if constexpr (N == 4) {
-            __bf16 h[4], l[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) split_hl(x[i], h[i], l[i]);
-            uint2 H, L;
-            H.x = (uint32_t)bf16_raw(h[0]) | ((uint32_t)bf16_raw(h[1]) << 16);
-            H.y = (uint32_t)bf16_raw(h[2]) | ((uint32_t)bf16_raw(h[3]) << 16);
-            L.x = (uint32_t)bf16_raw(l[0]) | ((uint32_t)bf16_raw(l[1]) << 16);
-            L.y = (uint32_t)bf16_raw(l[2]) | ((uint32_t)bf16_raw(l[3]) << 16);
-            *reinterpret_cast<uint2 *>(hi) = H;
-            *reinterpret_cast<uint2 *>(lo) = L;
-        } else {
-#pragma unroll
-            for (int i = 0; i < N; ++i) split_hl(x[i], hi[i], lo[i]);
-        }
-    }
-    __device__ static void put_hl1(char *base, int plane_bytes, int off, float x) {
-        __bf16 h, l;
-        split_hl(x, h, l);
-        reinterpret_cast<__bf16 *>(base)[off] = h;
-        reinterpret_cast<__bf16 *>(base + plane_bytes)[off] = l;
-    }
-    __device__ static void put_h2(char *base, int off, float x0, float x1) {
-        *reinterpret_cast<uint32_t *>(reinterpret_cast<__bf16 *>(base) + off) =
-            (uint32_t)bf16_raw(to_bf16(x0)) | ((uint32_t)bf16_raw(to_bf16(x1)) << 16);
-    }
-    template <bool LO> __device__ static Frag<false> get(const char *base, int plane_bytes, int off) {
-        Frag<false> f;
-        f.hi = *reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(base) + off);
-        if constexpr (LO) f.lo = *reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(base + plane_bytes) + off);
-        return f;
-    }
-    // Operand fragment from two 16x16 output tiles covering contraction rows
-    // [32s, 32s+16) and [32s+16, 32s+32) (hi only, or hi+lo).
-    template <bool LO> __device__ static Frag<false> from_tiles(const f32x4_t &t0, const f32x4_t &t1) {
-        Frag<false> f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if constexpr (LO) {
-                __bf16 h, l;
-                split_hl(t0[e], h, l); f.hi[e] = h; f.lo[e] = l;
-                split_hl(t1[e], h, l); f.hi[4 + e] = h; f.lo[4 + e] = l;
-            } else {
-                f.hi[e] = to_bf16(t0[e]);
-                f.hi[4 + e] = to_bf16(t1[e]);
-            }
-        }
-        return f;
-    }
-};
-template <> struct Mat<true> {
-    static constexpr int ES = 4;
-    template <int N> __device__ static void put_hl(char *base, int, int off, const float (&x)[N]) {
-        float *p = reinterpret_cast<float *>(base) + off;
-        if constexpr (N == 2) *reinterpret_cast<float2 *>(p) = make_float2(x[0], x[1]);
-        else if constexpr (N == 4) *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
-        else {
-#pragma unroll
-            for (int i = 0; i < N; ++i) p[i] = x[i];
-        }
-    }
-    __device__ static void put_hl1(char *base, int, int off, float x) { reinterpret_cast<float *>(base)[off] = x; }
-    __device__ static void put_h2(char *base, int off, float x0, float x1) {
-        *reinterpret_cast<float2 *>(reinterpret_cast<float *>(base) + off) = make_float2(x0, x1);
-    }
-    template <bool LO> __device__ static Frag<true> get(const char *base, int, int off) {
-        Frag<true> f;
-        const float4 a = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + off);
-        const float4 b = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + off + 4);
-        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-        return f;
-    }
-    template <bool LO> __device__ static Frag<true> from_tiles(const f32x4_t &t0, const f32x4_t &t1) {
-        Frag<true> f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { f.v[e] = t0[e]; f.v[4 + e] = t1[e]; }
-        return f;
-    }
-};
-
-// acc += A * B over one 32-wide K-step.  bf16: hi*hi (+ lo*hi) (+ hi*lo).
-template <bool ALO, bool BLO>
-__device__ __forceinline__ void mma(f32x4_t &acc, const Frag<false> &a, const Frag<false> &b) {
-    if constexpr (ALO) acc = mfma_bf16(a.lo, b.hi, acc);
-    if constexpr (BLO) acc = mfma_bf16(a.hi, b.lo, acc);
-    acc = mfma_bf16(a.hi, b.hi, acc);
-}
-template <bool ALO, bool BLO>
-__device__ __forceinline__ void mma(f32x4_t &acc, const Frag<true> &a, const Frag<true> &b) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = mfma_f32(a.v[e], b.v[e], acc);
-}
-
-// ---- fp32 16x16 tile products for the triangular inverse ------------------------
-// Tiles are row-major [16][TP] fp32 in LDS.  In instruction kk lane l feeds
-// k = 4*(l/16) + kk, which matches the row order of an output tile held in
-// registers (element kk of lane l is row 4*(l/16) + kk).
-__device__ __forceinline__ void tmm_ll(f32x4_t &acc, const float *A, const float *B, int lane) {
-    const int r = lane & 15, q = lane >> 4;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(A[r * TP + 4 * q + kk], B[(4 * q + kk) * TP + r], acc);
-}
-__device__ __forceinline__ void tmm_lr(f32x4_t &acc, const float *A, const f32x4_t &R, int lane) {
-    const int r = lane & 15, q = lane >> 4;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(A[r * TP + 4 * q + kk], R[kk], acc);
-}
-__device__ __forceinline__ void tile_store(float *Tl, const f32x4_t &v, int lane) {
-    const int c = lane & 15, q = lane >> 4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Tl[(4 * q + e) * TP + c] = v[e];
-}
-
-__host__ __device__ constexpr int vidx(int a, int b) { return a * (a + 1) / 2 + b; }
 
 // ---- LDS map -------------------------------------------------------------------
 template <int DK, bool F32P>
@@ -245,20 +76,6 @@ struct Lds {
     static constexpr int TOTAL = GC + DK * 4;
 };
 
-struct ChunkParams {
-    const void *q, *k, *v;
-    const float *g, *beta;
-    const int32_t *cu_seqlens;
-    const int32_t *order;          // sequences, longest first
-    const int64_t *ckpt_base;      // per sequence: index of its first checkpoint
-    const float *s0;
-    float *sf;
-    float *ckpt;
-    float *o;
-    int H;
-    int every;
-    float scale;
-};
 
 template <int DK, bool F32P, typename IN_T>
 __global__ void __launch_bounds__(DK * 4)
@@ -275,11 +92,6 @@ chunk_fwd_kernel(const ChunkParams p) {
     static_assert(NT / NCP == 8, "8 row groups of 8 rows");
 
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-    float *zt = reinterpret_cast<float *>(smem + L::Z);
-    float *s_beta = reinterpret_cast<float *>(smem + L::BETA);
-    float *s_gc = reinterpret_cast<float *>(smem + L::GC);
-    float *s_xchg = reinterpret_cast<float *>(smem + L::XCHG);
-
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4;
 
@@ -289,11 +101,8 @@ chunk_fwd_kernel(const ChunkParams p) {
     const int seq_len = p.cu_seqlens[n + 1] - seq_start;
     const int H = p.H;
 
-    // Elementwise role: channel pair cp (channels 2cp, 2cp+1), rows [8 rg, 8 rg + 8).
-    const int cp = tid % NCP, rg = tid / NCP;
-    const int c0 = 2 * cp;
-    const int sa = rg >> 1, hf = rg & 1;   // sub-chunk and half of this row group
-
+    // Elementwise role (inside the chunk loop): channel pair cp (channels 2cp, 2cp+1),
+    // rows [8 rg, 8 rg + 8), sub-chunk sa = rg/2, half hf = rg%2.
     // Scan role: value columns [j0, j0 + 16).
     const int j0 = 16 * wave;
 
@@ -320,18 +129,20 @@ chunk_fwd_kernel(const ChunkParams p) {
     const int nchunks = (seq_len + CH - 1) / CH;
 
     for (int ci = 0; ci < nchunks; ++ci) {
+        // Per-lane indices and LDS offsets are rederived every chunk (see opaque_v).
+        char *const sm = smem + opaque_s(0);
+        float *const zt = reinterpret_cast<float *>(sm + L::Z);
+        float *const s_beta = reinterpret_cast<float *>(sm + L::BETA);
+        float *const s_gc = reinterpret_cast<float *>(sm + L::GC);
+        float *const s_xchg = reinterpret_cast<float *>(sm + L::XCHG);
+        const int tid = opaque_v((int)threadIdx.x);
+        const int lane = tid & 63;
+        const int lr = lane & 15, lq = lane >> 4;
+        const int cp = tid % NCP, rg = tid / NCP;
+        const int c0 = 2 * cp;
+        const int sa = rg >> 1, hf = rg & 1;
         const int t0 = seq_start + ci * CH;
         const int nvalid = min(CH, seq_len - ci * CH);
-
-        // -- value slice for the scan, fetched early ------------------------------
-        f32x4_t Vt[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rt + 4 * lq + e;
-                Vt[rt][e] = r < nvalid ? load_in(vg + ((size_t)(t0 + r) * H + h) * DV + j0 + lr) : 0.f;
-            }
 
         // -- S1: inputs, per-channel decay products ------------------------------
         float kv[8][2], qv[8][2], Es[8][2], Ee[8][2];
@@ -409,13 +220,13 @@ chunk_fwd_kernel(const ChunkParams p) {
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
             const float ks[2] = {kv[i][0] * Es[i][0], kv[i][1] * Es[i][1]};
-            M::template put_hl<2>(smem + L::KQS, L::KQS_PLANE, fofs<KB>(r, c0), ks);
+            M::template put_hl<2>(sm + L::KQS, L::KQS_PLANE, fofs<KB>(r, c0), ks);
 #pragma unroll
             for (int ap = 0; ap < 4; ++ap) {
                 if (ap < sa) continue;
                 const int vr = 16 * vidx(ap, sa) + (r - 16 * sa);
                 const float kn[2] = {kv[i][0] * Ee[i][0] * cfac[ap][0], kv[i][1] * Ee[i][1] * cfac[ap][1]};
-                M::template put_hl<2>(smem + L::KN, L::KN_PLANE, fofs<KB>(vr, c0), kn);
+                M::template put_hl<2>(sm + L::KN, L::KN_PLANE, fofs<KB>(vr, c0), kn);
             }
         }
         __syncthreads();
@@ -427,9 +238,10 @@ chunk_fwd_kernel(const ChunkParams p) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KB; ++s) {
-                const F fa = M::template get<true>(smem + L::KN, L::KN_PLANE, fbase<KB>(vidx(a, b), s, lane));
-                const F fb = M::template get<true>(smem + L::KQS, L::KQS_PLANE, fbase<KB>(a, s, lane));
+                const F fa = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(vidx(a, b), s, lane));
+                const F fb = M::template get<true>(sm + L::KQS, L::KQS_PLANE, fbase<KB>(a, s, lane));
                 mma<true, true>(acc, fa, fb);
+                __builtin_amdgcn_sched_barrier(0);
             }
             const float br = s_beta[16 * a + lr];
             float4 w;
@@ -448,7 +260,7 @@ chunk_fwd_kernel(const ChunkParams p) {
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
             const float qs[2] = {qv[i][0] * Es[i][0], qv[i][1] * Es[i][1]};
-            M::template put_hl<2>(smem + L::KQS, L::KQS_PLANE, fofs<KB>(r, c0), qs);
+            M::template put_hl<2>(sm + L::KQS, L::KQS_PLANE, fofs<KB>(r, c0), qs);
         }
         if (wave == 0) {
             const int a = lane >> 4, j = lane & 15;
@@ -460,12 +272,13 @@ chunk_fwd_kernel(const ChunkParams p) {
 #pragma unroll
                 for (int i = 0; i < r; ++i) acc -= Lt[r * TP + i] * x[i];
                 x[r] = acc;
+                __builtin_amdgcn_sched_barrier(0);   // keep row loads next to their use
             }
             const float bj = s_beta[16 * a + j];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 Lt[r * TP + j] = x[r];
-                M::put_hl1(smem + L::TM, L::TRI_PLANE, tofs(16 * a + r, 16 * a + j), x[r] * bj);
+                M::put_hl1(sm + L::TM, L::TRI_PLANE, tofs(16 * a + r, 16 * a + j), x[r] * bj);
             }
         }
         __syncthreads();
@@ -477,14 +290,15 @@ chunk_fwd_kernel(const ChunkParams p) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KB; ++s) {
-                const F fa = M::template get<true>(smem + L::KN, L::KN_PLANE, fbase<KB>(vidx(a, b), s, lane));
-                const F fb = M::template get<true>(smem + L::KQS, L::KQS_PLANE, fbase<KB>(a, s, lane));
+                const F fa = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(vidx(a, b), s, lane));
+                const F fb = M::template get<true>(sm + L::KQS, L::KQS_PLANE, fbase<KB>(a, s, lane));
                 mma<true, true>(acc, fa, fb);
+                __builtin_amdgcn_sched_barrier(0);
             }
             float w[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = (b < a || 4 * lq + e <= lr) ? acc[e] : 0.f;
-            M::template put_hl<4>(smem + L::AQK, L::TRI_PLANE, tofs(16 * a + lr, 16 * b + 4 * lq), w);
+            M::template put_hl<4>(sm + L::AQK, L::TRI_PLANE, tofs(16 * a + lr, 16 * b + 4 * lq), w);
         }
         if (wave == NW - 1 || wave == NW - 2) {
             // M_{a,a-1} = -M_aa L_{a,a-1} M_{a-1,a-1} for a = 1 (wave NW-2) and a = 3 (wave NW-1)
@@ -496,19 +310,29 @@ chunk_fwd_kernel(const ChunkParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 Mo[e] = -Mo[e];
-                M::put_hl1(smem + L::TM, L::TRI_PLANE, tofs(16 * a + 4 * lq + e, 16 * (a - 1) + lr), Mo[e] * bj);
+                M::put_hl1(sm + L::TM, L::TRI_PLANE, tofs(16 * a + 4 * lq + e, 16 * (a - 1) + lr), Mo[e] * bj);
             }
             tile_store(zt + vidx(a, a - 1) * TSZ, Mo, lane);
         }
         __syncthreads();
 
         // -- S6: scan operands (region X over G); X = L_BL M_TL (waves 0..3) ------------
+        // -- value slice for the scan (consumed after the next two barriers) --------------
+        f32x4_t Vt[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + 4 * lq + e;
+                Vt[rt][e] = r < nvalid ? load_in(vg + ((size_t)(t0 + r) * H + h) * DV + j0 + lr) : 0.f;
+            }
+
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
-            M::put_h2(smem + L::GK, fofs<KB>(r, c0), kv[i][0] * Es[i][0] * pre[0], kv[i][1] * Es[i][1] * pre[1]);
+            M::put_h2(sm + L::GK, fofs<KB>(r, c0), kv[i][0] * Es[i][0] * pre[0], kv[i][1] * Es[i][1] * pre[1]);
             const float qt[2] = {qv[i][0] * Es[i][0] * pre[0], qv[i][1] * Es[i][1] * pre[1]};
-            M::template put_hl<2>(smem + L::QT, L::QT_PLANE, fofs<KB>(r, c0), qt);
+            M::template put_hl<2>(sm + L::QT, L::QT_PLANE, fofs<KB>(r, c0), qt);
         }
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
@@ -516,7 +340,7 @@ chunk_fwd_kernel(const ChunkParams p) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const float kh[2] = {kv[i][c] * Ee[i][c] * post[c], kv[i + 1][c] * Ee[i + 1][c] * post[c]};
-                M::template put_hl<2>(smem + L::KHT, L::KHT_PLANE, fofs<2>(c0 + c, r), kh);
+                M::template put_hl<2>(sm + L::KHT, L::KHT_PLANE, fofs<2>(c0 + c, r), kh);
             }
         }
         if (wave < 4) {
@@ -546,31 +370,34 @@ chunk_fwd_kernel(const ChunkParams p) {
             const float bj = s_beta[16 * b + lr];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                M::put_hl1(smem + L::TM, L::TRI_PLANE, tofs(16 * a + 4 * lq + e, 16 * b + lr), -Mo[e] * bj);
+                M::put_hl1(sm + L::TM, L::TRI_PLANE, tofs(16 * a + 4 * lq + e, 16 * b + lr), -Mo[e] * bj);
         }
         __syncthreads();
 
         // -- S8: scan for value columns [j0, j0+16) ------------------------------------------
         {
-            F SFh[KB], SFhl[KB];
+            // Y = V - (Gamma*K) S and Oa = (Gamma*Q) S, accumulated over d_k in 32-wide
+            // steps so that only one step's S fragments are live at a time
+            f32x4_t Y[4], Oa[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) { Y[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; Oa[rt] = Y[rt]; }
 #pragma unroll
             for (int s = 0; s < KB; ++s) {
-                SFh[s] = M::template from_tiles<false>(Sr[2 * s], Sr[2 * s + 1]);
-                SFhl[s] = M::template from_tiles<true>(Sr[2 * s], Sr[2 * s + 1]);
-            }
-            // Y = V - (Gamma*K) S
-            f32x4_t Y[4];
+                const F sh = M::template from_tiles<false>(Sr[2 * s], Sr[2 * s + 1]);
+                const F shl = M::template from_tiles<true>(Sr[2 * s], Sr[2 * s + 1]);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < KB; ++s) {
-                    const F fa = M::template get<false>(smem + L::GK, 0, fbase<KB>(rt, s, lane));
-                    mma<false, false>(acc, fa, SFh[s]);
+                for (int rt = 0; rt < 4; ++rt) {
+                    const F fg = M::template get<false>(sm + L::GK, 0, fbase<KB>(rt, s, lane));
+                    mma<false, false>(Y[rt], fg, sh);
+                    const F fq = M::template get<true>(sm + L::QT, L::QT_PLANE, fbase<KB>(rt, s, lane));
+                    mma<true, true>(Oa[rt], fq, shl);
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Y[rt][e] = Vt[rt][e] - acc[e];
+                __builtin_amdgcn_sched_barrier(0);
             }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Y[rt][e] = Vt[rt][e] - Y[rt][e];
             F YF[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) YF[s] = M::template from_tiles<true>(Y[2 * s], Y[2 * s + 1]);
@@ -581,7 +408,7 @@ chunk_fwd_kernel(const ChunkParams p) {
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s <= (rt >> 1); ++s) {
-                    const F fa = M::template get<true>(smem + L::TM, L::TRI_PLANE, tbase(rt, s, lane));
+                    const F fa = M::template get<true>(sm + L::TM, L::TRI_PLANE, tbase(rt, s, lane));
                     mma<true, true>(acc, fa, YF[s]);
                 }
                 U[rt] = acc;
@@ -592,15 +419,10 @@ chunk_fwd_kernel(const ChunkParams p) {
             // O = scale [ (Gamma*Q) S + A_qk U ]
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < KB; ++s) {
-                    const F fa = M::template get<true>(smem + L::QT, L::QT_PLANE, fbase<KB>(rt, s, lane));
-                    mma<true, true>(acc, fa, SFhl[s]);
-                }
+                f32x4_t acc = Oa[rt];
 #pragma unroll
                 for (int s = 0; s <= (rt >> 1); ++s) {
-                    const F fa = M::template get<true>(smem + L::AQK, L::TRI_PLANE, tbase(rt, s, lane));
+                    const F fa = M::template get<true>(sm + L::AQK, L::TRI_PLANE, tbase(rt, s, lane));
                     mma<true, true>(acc, fa, UF[s]);
                 }
 #pragma unroll
@@ -617,7 +439,7 @@ chunk_fwd_kernel(const ChunkParams p) {
                 for (int e = 0; e < 4; ++e) acc[e] = s_gc[16 * ct + 4 * lq + e] * Sr[ct][e];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    const F fa = M::template get<true>(smem + L::KHT, L::KHT_PLANE, fbase<2>(ct, s, lane));
+                    const F fa = M::template get<true>(sm + L::KHT, L::KHT_PLANE, fbase<2>(ct, s, lane));
                     mma<true, true>(acc, fa, UF[s]);
                 }
                 Sr[ct] = acc;
@@ -692,7 +514,11 @@ extern "C" __attribute__((visibility("hidden"))) size_t kda_chunk_workspace_layo
     return b + ((size_t)N * 8 + 255) / 256 * 256 + 256;
 }
 
-extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int dk, int in_bf16, int N, int H, const void *q, const void *k,
+extern "C" __attribute__((visibility("hidden"))) hipError_t
+kda_launch_chunk32(int dk, int in_bf16, unsigned grid, const kda::ChunkParams &p, hipStream_t stream);
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int chunk, int dk, int in_bf16, int N, int H,
+                                       const void *q, const void *k,
                                        const void *v, const float *g, const float *beta, const int32_t *cu,
                                        const float *s0, float *sf, int every, float *ckpt, float *o,
                                        float scale, void *workspace, hipStream_t stream) {
@@ -710,6 +536,7 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int
     p.ckpt_base = base; p.s0 = s0; p.sf = sf; p.ckpt = ckpt; p.o = o; p.H = H; p.every = every;
     p.scale = scale;
     const dim3 grid((unsigned)N * (unsigned)H);
+    if (chunk == 32) return kda_launch_chunk32(dk, in_bf16, grid.x, p, stream);
 #define KDA_CHUNK(DKV, F32P, T) \
     hipLaunchKernelGGL((kda::chunk_fwd_kernel<DKV, F32P, T>), grid, dim3(DKV * 4), 0, stream, p)
     if (dk == 128 && in_bf16) KDA_CHUNK(128, false, uint16_t);

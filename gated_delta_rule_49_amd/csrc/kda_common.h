@@ -24,12 +24,37 @@ __device__ __forceinline__ void split_hl(float x, __bf16 &hi, __bf16 &lo) {
     lo = to_bf16(x - bf16_to_f32(hi));
 }
 
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+// Two floats -> two bf16 (round to nearest even) packed in one word, a at the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v_t){a, b}, bf16x2v_t));
+}
+// hi/lo split of a pair, packed: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split_hl2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = pack_bf16x2(a, b);
+    lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
+
 // Load one input element of type T (float or raw bf16 bits) as fp32.
 template <typename T> __device__ __forceinline__ float load_in(const T *p);
 template <> __device__ __forceinline__ float load_in<float>(const float *p) { return *p; }
 template <> __device__ __forceinline__ float load_in<uint16_t>(const uint16_t *p) {
     return bf16_bits_to_f32(*p);
 }
+
+// Widen one input element (raw bf16 bits or fp32) already held in a register.
+__device__ __forceinline__ float widen(uint16_t b) { return bf16_bits_to_f32(b); }
+__device__ __forceinline__ float widen(float x) { return x; }
+
+// ---- register-pressure control -------------------------------------------------
+// Return x unchanged while hiding its value from the optimizer.  Values derived
+// from the result are recomputed inside a loop body instead of being hoisted
+// out of the loop and kept live in registers for its whole duration (per-lane
+// LDS offsets are cheap to recompute and expensive to hold).  The asm emits no
+// instruction.
+__device__ __forceinline__ int opaque_v(int x) { __asm__ volatile("" : "+v"(x)); return x; }
+__device__ __forceinline__ int opaque_s(int x) { __asm__ volatile("" : "+s"(x)); return x; }
 
 // ---- wave-level helpers ---------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }

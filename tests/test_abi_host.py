@@ -97,12 +97,14 @@ def status(L, a, ws=FAKE * 16, ws_bytes=1 << 20):
     ("num_heads", 0, kda.KDA_ERR_INVALID_ARGUMENT),
     ("dk", 96, kda.KDA_ERR_UNSUPPORTED),
     ("dv", 64, kda.KDA_ERR_UNSUPPORTED),
-    ("chunk_size", 32, kda.KDA_ERR_UNSUPPORTED),
+    ("chunk_size", 16, kda.KDA_ERR_UNSUPPORTED),
+    ("chunk_size", 128, kda.KDA_ERR_UNSUPPORTED),
     ("in_dtype", 7, kda.KDA_ERR_INVALID_ARGUMENT),
     ("q", None, kda.KDA_ERR_INVALID_ARGUMENT),
     ("g", FAKE + 4, kda.KDA_ERR_INVALID_ARGUMENT),          # misaligned
     ("o", FAKE * 1, kda.KDA_ERR_INVALID_ARGUMENT),          # aliases q
     ("checkpoint_every", 100, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("checkpoint_every", 96, kda.KDA_ERR_INVALID_ARGUMENT),   # not a multiple of chunk_size 64
     ("checkpoint_every", 64, kda.KDA_ERR_INVALID_ARGUMENT),  # checkpoints pointer missing
     ("total_tokens", 227, kda.KDA_ERR_INVALID_ARGUMENT),
     ("scale", float("nan"), kda.KDA_ERR_INVALID_ARGUMENT),

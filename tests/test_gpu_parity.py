@@ -32,12 +32,15 @@ def in_dtype(w):
     return torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
 
-def run_gpu(w, scale=1.0, s0=True):
+CHUNKS = [32, 64]
+
+
+def run_gpu(w, scale=1.0, s0=True, chunk=32):
     dt = in_dtype(w)
     o, sf, ck = kda.kda_chunk_fwd(to_dev(w.q, dt), to_dev(w.k, dt), to_dev(w.v, dt), to_dev(w.g, torch.float32),
                                   to_dev(w.beta, torch.float32), list(w.cu_seqlens), scale,
                                   to_dev(w.s0, torch.float32) if (s0 and w.s0 is not None) else None,
-                                  True, w.checkpoint_every)
+                                  True, w.checkpoint_every, chunk_size=chunk)
     torch.cuda.synchronize()
     return o.cpu().numpy(), sf.cpu().numpy(), None if ck is None else ck.cpu().numpy()
 
@@ -47,19 +50,20 @@ def run_ref(w, scale=1.0, s0=True):
                           w.checkpoint_every)
 
 
-def compare(w, tol=None, scale=1.0, label=""):
+def compare(w, tol=None, scale=1.0, label="", chunk=32):
     tol = tol or TOL[w.dtype]
-    o, sf, ck = run_gpu(w, scale)
+    o, sf, ck = run_gpu(w, scale, chunk=chunk)
     o_r, s_r, ck_r = run_ref(w, scale)
     errs = {"o": W.rel_max_err(o, o_r), "S": W.rel_max_err(sf, s_r)}
     if ck_r is not None and ck_r.size:
         errs["ckpt"] = W.rel_max_err(ck, ck_r)
-    print(f"[parity] {label or w.name} seqlens={w.seqlens[:8]}{'...' if len(w.seqlens) > 8 else ''} "
+    label = f"{label or w.name} C={chunk}"
+    print(f"[parity] {label} seqlens={w.seqlens[:8]}{'...' if len(w.seqlens) > 8 else ''} "
           f"H={w.H} d={w.dk} {w.dtype}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     log = os.environ.get("KDA_PARITY_LOG")
     if log:
         with open(log, "a") as f:
-            f.write(json.dumps({"case": label or w.name, "H": w.H, "d": w.dk, "dtype": w.dtype,
+            f.write(json.dumps({"case": label, "chunk": chunk, "H": w.H, "d": w.dk, "dtype": w.dtype,
                                 "tokens": w.total_tokens, "tol": tol, **errs}) + "\n")
     for k_, v_ in errs.items():
         assert v_ <= tol, (k_, v_, tol)
@@ -84,37 +88,42 @@ def test_decode_small(d, dtype):
 
 
 # ---- prefill: small shapes and edge cases ------------------------------------------------------
-def test_prefill_config0_tiny_f32():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_prefill_config0_tiny_f32(chunk):
     w = W.make_config(0, seed=0)
-    compare(w, label="config0")
+    compare(w, label="config0", chunk=chunk)
 
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_prefill_varlen_ragged(d, dtype):
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_prefill_varlen_ragged(d, dtype, chunk):
     """Several tiles and ragged tails: lengths that are not multiples of 64, an empty
     sequence, a single-token sequence; initial states; checkpoints every 64."""
     w = W.make_prefill([200, 64, 1, 0, 130, 333], H=3, dk=d, dv=d, dtype=dtype, seed=22, s0_std=0.1,
                        checkpoint_every=64)
-    compare(w, label=f"varlen d={d} {dtype}")
+    compare(w, label=f"varlen d={d} {dtype}", chunk=chunk)
 
 
 @pytest.mark.parametrize("gate", ["min", "zero", "slow"])
-def test_prefill_gate_extremes(gate):
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_prefill_gate_extremes(gate, chunk):
     """g = -5 everywhere (the bound: the diagonal-tile factor reaches e^80), g = 0 (no
     decay: long-range accumulation), and slow decay (long memory)."""
     w = W.make_prefill([700], H=2, dk=128, dv=128, dtype="bf16", seed=23, s0_std=0.1, gate=gate)
-    compare(w, label=f"gate={gate}")
+    compare(w, label=f"gate={gate}", chunk=chunk)
 
 
-def test_prefill_scalar_gate():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_prefill_scalar_gate(chunk):
     """The gate shared by all channels (scalar-gate special case) through the same kernels."""
     w = W.make_prefill([300], H=2, dk=128, dv=128, dtype="bf16", seed=24, s0_std=0.1)
     w.g = np.repeat(w.g[:, :, :1], 128, axis=2).copy()
-    compare(w, label="scalar gate")
+    compare(w, label="scalar gate", chunk=chunk)
 
 
-def test_prefill_exact_retrieval_bf16():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_prefill_exact_retrieval_bf16(chunk):
     """g = 0, beta = 1, orthonormal keys written once each, then read back with beta = 0:
     the read-out returns the stored values (to the bf16-path bar)."""
     rng = np.random.default_rng(25)
@@ -128,22 +137,23 @@ def test_prefill_exact_retrieval_bf16():
     w.q[:, 0] = np.concatenate([keys, keys])
     w.v[:, 0] = np.concatenate([vals, np.zeros_like(vals)])
     w.beta[:, 0] = np.concatenate([np.ones(m), np.zeros(m)]).astype(np.float32)
-    errs = compare(w, label="retrieval")
-    o, _, _ = run_gpu(w)
+    errs = compare(w, label="retrieval", chunk=chunk)
+    o, _, _ = run_gpu(w, chunk=chunk)
     # the recalled rows are close to the written values (keys are orthonormal only to bf16 rounding)
     assert np.max(np.abs(o[m:, 0] - vals)) / np.sqrt(np.mean(vals ** 2)) < 0.1
 
 
-def test_checkpoint_resume_on_gpu():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_checkpoint_resume_on_gpu(chunk):
     """Resuming the GPU kernel from one of its own checkpoints reproduces the tail."""
     w = W.make_prefill([512], H=2, dk=128, dv=128, dtype="bf16", seed=26, s0_std=0.1, checkpoint_every=128)
-    o, sf, ck = run_gpu(w)
+    o, sf, ck = run_gpu(w, chunk=chunk)
     p = 256
     w2 = W.Workload("tail", [512 - p], 2, 128, 128, "bf16", w.q[p:], w.k[p:], w.v[p:], w.g[p:], w.beta[p:],
                     ck[1][None].astype(np.float32))
-    o2, sf2, _ = run_gpu(w2)
+    o2, sf2, _ = run_gpu(w2, chunk=chunk)
     assert W.rel_max_err(o2, o[p:]) < 1e-5 and W.rel_max_err(sf2, sf) < 1e-5
-    compare(w, label="ckpt")
+    compare(w, label="ckpt", chunk=chunk)
 
 
 def test_decode_equals_prefill_of_one_token():
@@ -168,11 +178,12 @@ def test_decode_equals_prefill_of_one_token():
     assert W.rel_max_err(sp.cpu().numpy(), state.cpu().numpy()) <= TOL["bf16"]
 
 
-def test_bitwise_determinism_and_state_aliasing():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_bitwise_determinism_and_state_aliasing(chunk):
     """Two runs give bit-identical outputs; final_state may alias initial_state."""
     w = W.make_prefill([300, 77], H=2, dk=128, dv=128, dtype="bf16", seed=28, s0_std=0.1)
-    a = run_gpu(w)
-    b = run_gpu(w)
+    a = run_gpu(w, chunk=chunk)
+    b = run_gpu(w, chunk=chunk)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
     # in-place state: pass the same buffer as initial and final state
@@ -181,7 +192,8 @@ def test_bitwise_determinism_and_state_aliasing():
     args = [to_dev(x, dt) for x in (w.q, w.k, w.v)] + [to_dev(w.g, torch.float32), to_dev(w.beta, torch.float32)]
     cu_h = torch.tensor(list(w.cu_seqlens), dtype=torch.int32)
     o = torch.empty((w.total_tokens, 2, 128), dtype=torch.float32, device=dev())
-    A = kda.make_fwd_args(*args, cu_h.to(dev()), cu_h, 1.0, S, S, 0, None, o)
+    cu_d = cu_h.to(dev())   # must stay alive until the launch has been enqueued
+    A = kda.make_fwd_args(*args, cu_d, cu_h, 1.0, S, S, 0, None, o, chunk)
     ws = torch.empty(kda.lib().kda_chunk_fwd_workspace_bytes(kda.ctypes.byref(A)), dtype=torch.uint8, device=dev())
     st = kda.lib().kda_chunk_fwd(kda.ctypes.byref(A), kda.ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                                  kda._stream(None))
