@@ -80,10 +80,13 @@ def _load():
 
 
 def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, at most 16
+    (a fair share of a shared host; the oracle is a checker, not a product)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def _f32(x):

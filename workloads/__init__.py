@@ -123,14 +123,19 @@ def _gen_block(wid, seed, s, b, T0, Tb, H, dk, dv, dtype, gate, out):
 
 
 def make_prefill(seqlens, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.0, gate="config",
-                 checkpoint_every=0, wid=100, name=None, threads=None) -> Workload:
+                 checkpoint_every=0, wid=100, name=None, threads=None, seq_ids=None) -> Workload:
+    """Packed varlen problem.  `seq_ids` (default 0..N-1) are the sequence
+    indices the draws are keyed on: passing a subset of a larger workload's
+    lengths with their original indices regenerates exactly those sequences."""
     seqlens = [int(x) for x in seqlens]
+    seq_ids = list(range(len(seqlens))) if seq_ids is None else [int(x) for x in seq_ids]
+    assert len(seq_ids) == len(seqlens)
     T = sum(seqlens)
     out = {n: np.empty((T, H, d), dtype=np.float32) for n, d in (("q", dk), ("k", dk), ("v", dv), ("g", dk))}
     out["beta"] = np.empty((T, H), dtype=np.float32)
     jobs = []
     off = 0
-    for s, L in enumerate(seqlens):
+    for s, L in zip(seq_ids, seqlens):
         for b in range(0, max(1, math.ceil(L / BLOCK))):
             Tb = min(BLOCK, L - b * BLOCK)
             if Tb > 0:
@@ -146,8 +151,8 @@ def make_prefill(seqlens, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.0, g
     s0 = None
     if s0_std > 0:
         s0 = np.empty((len(seqlens), H, dk, dv), dtype=np.float32)
-        for s in range(len(seqlens)):
-            s0[s] = _rng(wid, s, 0, "s0", seed).standard_normal((H, dk, dv), dtype=np.float32) * np.float32(s0_std)
+        for i, s in enumerate(seq_ids):
+            s0[i] = _rng(wid, s, 0, "s0", seed).standard_normal((H, dk, dv), dtype=np.float32) * np.float32(s0_std)
     return Workload(name or f"prefill_H{H}_d{dk}", seqlens, H, dk, dv, dtype, out["q"], out["k"], out["v"],
                     out["g"], out["beta"], s0, checkpoint_every, {"gate": gate, "seed": seed})
 
@@ -200,6 +205,27 @@ def make_config(cid: int, seed: int = 0, gate: str = "config", threads=None) -> 
     seqlens = c["seqlens"] if c["seqlens"] is not None else config4_lengths()
     return make_prefill(seqlens, c["H"], c["dk"], c["dv"], c["dtype"], seed, c["s0_std"], gate,
                         c["checkpoint_every"], wid=cid, name=c["name"], threads=threads)
+
+
+def config_parts(cid: int, max_tokens: int = 1 << 18, seed: int = 0, threads=None):
+    """Yield (first_seq, token_offset, Workload) pieces that together make
+    config `cid`, each piece a run of whole sequences of at most about
+    `max_tokens` tokens (a longer sequence is a piece of its own).  The values
+    equal those of make_config(cid), so a large workload can be streamed to a
+    device without holding it on the host at once."""
+    c = dict(CONFIGS[cid])
+    assert c["kind"] == "prefill"
+    seqlens = c["seqlens"] if c["seqlens"] is not None else config4_lengths()
+    i, off = 0, 0
+    while i < len(seqlens):
+        j, n = i, 0
+        while j < len(seqlens) and (j == i or n + seqlens[j] <= max_tokens):
+            n += seqlens[j]
+            j += 1
+        yield i, off, make_prefill(seqlens[i:j], c["H"], c["dk"], c["dv"], c["dtype"], seed, c["s0_std"],
+                                   "config", c["checkpoint_every"], wid=cid, name=c["name"], threads=threads,
+                                   seq_ids=range(i, j))
+        i, off = j, off + n
 
 
 def rel_max_err(x, ref) -> float:
