@@ -3,69 +3,74 @@
 // Same operator and chunk algebra as kda_chunk.hip (the chunk-recurrent form of
 // the gated delta rule; "Attention->K3 course, Day 21", quiz Q9 / answer D19;
 // skillsmp K3 skill card, quick facts: per-channel gate, g >= -5), with a chunk
-// of two 16-row sub-chunks.  Within a chunk, with G the in-chunk cumulative
-// log-decay, Gamma = e^G, P_a the decay product of sub-chunk a:
-//     A_kk, A_qk   lower 16x16 Gram tiles (0,0), (1,0), (1,1), as MFMA products
-//                  of k*e^{G-G_ref(a)} with k*e^{G_ref(a)-G} (both in fp32 range)
-//     T  = (I + A_kk)^{-1} Diag(beta)   via M00, M11 by substitution, M10 = -M11 L10 M00
-//     Y  = V - (Gamma*K) S ;  U = T Y ;  O = scale [ (Gamma*Q) S + A_qk U ]
+// of two 16-row sub-chunks a = 0, 1.  With G the in-chunk cumulative log-decay,
+// G_ref(a) its value before the first row of sub-chunk a, P0 = e^{G_ref(1)}:
+//     KS = K * e^{G - G_ref},  QS = Q * e^{G - G_ref}          (entries <= |x|)
+//     Gamma*K equals KS with the columns of its rows 16..31 scaled by P0, so
+//     (Gamma*K) S = KS S on rows 0..15 and KS (Diag(P0) S) on rows 16..31
+//     A_kk, A_qk   lower 16x16 Gram tiles (0,0), (1,0), (1,1) of KS/QS against
+//                  K * e^{G_ref(a) - G} (in fp32 range: 16 * 5 = 80 < 88)
+//     (I + A_kk) U = Diag(beta) Y block by block, A_kk strictly lower, beta-scaled rows:
+//         U0 = T00 Y0,   W = A10 U0,   U1 = T11 Y1 - M11 W
+//         with M_aa = (I + A_aa)^{-1}, T_aa = M_aa Diag(beta_a)
+//     Y  = V - (Gamma*K) S ;  O = scale [ (Gamma*Q) S + A_qk U ]
 //     S <- Diag(Gamma_last) S + (e^{G_last-G} * K)^T U
 //
-// Workgroup = one (sequence, head).  Waves 0..NSW-1 ("scan waves") each own 32
-// value columns and keep that d_k x 32 slice of S in registers (fp32) for the
-// whole sequence.  Waves NSW.. ("prep waves") build the S-independent operands
-// of the NEXT chunk while the scan waves consume the current one.  Each loop
-// iteration i has three segments separated by LDS-only barriers (register
-// prefetches of the inputs stay in flight across them):
+// Workgroup = one (sequence, head): DV/32 "scan waves" and 4*DK/64 "prep waves".
+// Scan wave w owns value columns 32w .. 32w+31 and keeps that d_k x 32 slice of S
+// in registers (fp32) for the whole sequence.  Prep waves build the
+// S-independent operands of the NEXT chunk while the scan waves consume the
+// current one.  The two roles run separate loops with the same three
+// LDS-only barriers per iteration (global loads stay in flight across them):
 //
-//            scan waves                              prep waves
-//   seg 1    b(i): Y = V - Y, U = T Y, O (stores)    P1(i+1): exp(g), running products, exchange
-//   seg 2    c(i): S <- Gamma_last S + Khat^T U     P2(i+1): decayed operands -> LDS
-//   seg 3    a(i+1): Y = (Gamma*K) S, (Gamma*Q) S   P3(i+1): Gram tiles, T, A_qk
+//            scan waves                                prep waves
+//   seg 1    b(i): Y = V - Y, U, O (stores)            P1(i+1): exp(g), 4-row running products
+//   seg 2    c(i): S <- Gamma_last S + Khat^T U        P2(i+1): decayed operands -> LDS
+//   seg 3    a(i+1): (Gamma*K) S, (Gamma*Q) S          P3(i+1): Gram tiles, T00, [-M11 T11], A10, A_qk
 //
-// Every LDS operand is written in a segment that follows its last read by the
-// previous chunk, so one copy suffices, except (e^{G_last-G} K)^T and Gamma_last,
-// which P2 writes while stage c still reads the previous chunk's: those two
-// are double-buffered.  32-token chunks are what lets the operands of one chunk
-// and the prep scratch of the next share the 160 KB LDS.
+// Every LDS operand is written in a segment after its last read by the previous
+// chunk, so one copy suffices, except (e^{G_last-G} K)^T and Gamma_last, which
+// P2 writes while stage c still reads the previous chunk's: those two are
+// double-buffered.  Prep waves load the raw rows of chunk i+2 straight into
+// registers while preparing chunk i+1; every load is unconditional (rows past
+// the end of the sequence re-read its last row and are masked where used).
 //
-// Precision is that of the 64-token kernel: hi+lo bf16 operand pairs on every
-// product feeding the outputs except (Gamma*K) S; fp32 accumulation; fp32 o, S.
+// Precision: hi+lo bf16 operand pairs on every product feeding the outputs
+// except (Gamma*K) S, fp32 accumulation, fp32 o and S.  The fp32-input
+// instantiation uses fp32 MFMA throughout.
 #include "kda_frag.h"
 
 namespace kda {
 
 constexpr int C32 = 32;
 
-template <int DK, bool F32P>
+template <int DK, bool F32P, typename IN_T>
 struct Lds32 {
     static constexpr int ES = Mat<F32P>::ES;
-    static constexpr int GK = 0;                           // [32][DK] single carrier: Gamma*K
-    static constexpr int QT = GK + 32 * DK * ES;           // [32][DK] hl: Gamma*Q
-    static constexpr int QT_PLANE = 32 * DK * ES;
-    static constexpr int KHT = QT + 32 * DK * 4;           // 2 x [DK][32] hl: (e^{G_last-G} K)^T
+    // operands of a chunk, written by the prep waves, read by the scan waves
+    static constexpr int KS = 0;                          // [32][DK] hl: K * e^{G - G_ref}
+    static constexpr int QS = KS + 32 * DK * 4;           // [32][DK] hl: Q * e^{G - G_ref}
+    static constexpr int SQ_PLANE = 32 * DK * ES;
+    static constexpr int KHT = QS + 32 * DK * 4;          // 2 x [DK][32] hl: (e^{G_last-G} K)^T
     static constexpr int KHT_PLANE = DK * 32 * ES;
     static constexpr int KHT_BUF = DK * 32 * 4;
-    static constexpr int TM = KHT + 2 * KHT_BUF;           // [32][32] hl: T
-    static constexpr int TRI_PLANE = 2 * 512 * ES;
-    static constexpr int AQK = TM + 2 * 512 * 4;           // [32][32] hl: A_qk
-    static constexpr int GC = AQK + 2 * 512 * 4;           // 2 x [DK] fp32: Gamma_last
-    static constexpr int KS = GC + 2 * DK * 4;             // [32][DK] hl  (prep scratch from here)
-    static constexpr int QS = KS + 32 * DK * 4;            // [32][DK] hl
-    static constexpr int SQ_PLANE = 32 * DK * ES;
-    static constexpr int KN = QS + 32 * DK * 4;            // [48][DK] hl: Kn(0,0), Kn(1,0), Kn(1,1)
+    static constexpr int TM = KHT + 2 * KHT_BUF;          // [32][32] hl: [T00 0 ; -M11 T11]
+    static constexpr int TRI_PLANE = 32 * 32 * ES;
+    static constexpr int AQK = TM + 32 * 32 * 4;          // [32][32] hl: A_qk, lower incl. diagonal
+    static constexpr int AW = AQK + 32 * 32 * 4;          // [16][32] hl: [A10 0]
+    static constexpr int AW_PLANE = 16 * 32 * ES;
+    static constexpr int GC = AW + 16 * 32 * 4;           // 2 x [DK] fp32: Gamma_last
+    static constexpr int P0 = GC + 2 * DK * 4;            // [DK] fp32: e^{G} at the end of sub-chunk 0
+    static constexpr int VPITCH = DK * (int)sizeof(IN_T) + 16;   // padded row pitch (bytes) of the value rows
+    static constexpr int VB = P0 + DK * 4;                // 2 x [32][VPITCH]: raw value rows of a chunk
+    static constexpr int VB_BUF = 32 * VPITCH;
+    // prep-wave scratch
+    static constexpr int KN = VB + 2 * VB_BUF;            // [48][DK] hl: K e^{G_ref - G} for tiles (0,0), (1,0), (1,1)
     static constexpr int KN_PLANE = 48 * DK * ES;
-    static constexpr int ZT = KN + 48 * DK * 4;            // 3 fp32 tiles: L00/M00, L10, L11/M11
-    static constexpr int XCHG = ZT + 3 * TSZ * 4;          // [4][DK] fp32 half-products
-    static constexpr int BETA = XCHG + 4 * DK * 4;         // [32] fp32
-    // Raw input rows of a chunk staged for the prep waves (bf16 inputs only):
-    // k, q [32][DK] bf16, g [32][DK] fp32, beta [32] fp32.
-    static constexpr bool STAGE = !F32P;
-    static constexpr int STK = BETA + 32 * 4;
-    static constexpr int STQ = STK + (STAGE ? 32 * DK * 2 : 0);
-    static constexpr int STG = STQ + (STAGE ? 32 * DK * 2 : 0);
-    static constexpr int STB = STG + (STAGE ? 32 * DK * 4 : 0);
-    static constexpr int TOTAL = STB + (STAGE ? 32 * 4 : 0);
+    static constexpr int ZT = KN + 48 * DK * 4;           // 2 fp32 tiles: A00 -> M00, A11 -> M11
+    static constexpr int XCHG = ZT + 2 * TSZ * 4;         // [8][DK] fp32: decay over each 4-row group
+    static constexpr int BETA = XCHG + 8 * DK * 4;        // [32] fp32
+    static constexpr int TOTAL = BETA + 32 * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -86,18 +91,21 @@ template <> struct Pair<float> {
     __device__ static float hi(raw w) { return w.y; }
 };
 
+template <int DK> constexpr int chunk32_threads() { return 64 * (DK / 32) + 4 * DK; }
+
 template <int DK, bool F32P, typename IN_T>
-__global__ void __launch_bounds__(DK * 4)
+__global__ void __launch_bounds__(chunk32_threads<DK>())
 chunk32_kernel(const ChunkParams p) {
     constexpr int DV = DK;
     constexpr int NSW = DV / 32;        // scan waves, 32 value columns each
-    constexpr int NPW = DK / 32;        // prep waves: 4 row groups x DK/2 channel pairs lanes
+    constexpr int NPW = DK / 16;        // prep waves: 8 four-row groups x DK/2 channel pairs
     constexpr int KB = DK / 32;         // 32-wide K-steps over d_k
     constexpr int KT = DK / 16;         // 16-row tiles over d_k
     constexpr int NCP = DK / 2;         // channel pairs
-    using L = Lds32<DK, F32P>;
+    using L = Lds32<DK, F32P, IN_T>;
     using M = Mat<F32P>;
     using F = Frag<F32P>;
+    using PR = Pair<IN_T>;
 
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
 
@@ -108,154 +116,72 @@ chunk32_kernel(const ChunkParams p) {
     const int seq_len = p.cu_seqlens[n + 1] - seq_start;
     const int nchunks = (seq_len + C32 - 1) / C32;
     const int wave = threadIdx.x >> 6;
-    const bool is_scan = wave < NSW;    // uniform per wave
 
     const IN_T *qg = reinterpret_cast<const IN_T *>(p.q);
     const IN_T *kg = reinterpret_cast<const IN_T *>(p.k);
     const IN_T *vg = reinterpret_cast<const IN_T *>(p.v);
 
-    // Structurally zero tile (rows 0..15, columns 16..31) of T and A_qk.
-    for (int idx = threadIdx.x; idx < 256; idx += blockDim.x) {
-        const int r = idx >> 4, c = 16 + (idx & 15);
-        M::put_hl1(smem + L::TM, L::TRI_PLANE, fofs<1>(r, c), 0.f);
-        M::put_hl1(smem + L::AQK, L::TRI_PLANE, fofs<1>(r, c), 0.f);
-    }
+    if (wave < NSW) {
+        // ============================== scan waves ==============================
+        // Lane (lq, lr) of scan wave w owns value columns 32w + 2 lr + jt (jt = column parity),
+        // adjacent in memory, so V, o and S move as 2-element pairs.
+        // Sr[jt][ct][e] = S[16 ct + 4 lq + e][32 wave + 2 lr + jt]
+        const size_t st_off = ((size_t)n * H + h) * DK * DV;
+        f32x4_t Sr[2][KT];
+        {
+            const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float2 v = p.s0 ? *reinterpret_cast<const float2 *>(
+                                                p.s0 + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + 32 * wave + 2 * lr)
+                                          : make_float2(0.f, 0.f);
+                    Sr[0][ct][e] = v.x;
+                    Sr[1][ct][e] = v.y;
+                }
+        }
+        f32x4_t Yacc[2][2], Oacc[2][2];
+        F UF[2];
+        const int every_chunks = p.every / C32;   // checkpoint_every is a multiple of the chunk size
+        int ck_left = every_chunks, ck_idx = 0;
 
-    // ---- scan-wave state ----------------------------------------------------------
-    // Scan wave w owns value columns 32w + 2 lr + jt (lane lr, tile jt = column parity), so
-    // each lane's two columns are adjacent in memory: V, o and S move as 2-element pairs.
-    // Sr[jt][ct][e] = S[16 ct + 4 lq + e][32 wave + 2 lr + jt]
-    using PR = Pair<IN_T>;
-    f32x4_t Sr[2][KT];
-    f32x4_t Yacc[2][2], Oacc[2][2];
-    typename PR::raw Vr[2][4];   // raw value pairs of the next chunk (masked and widened when used)
-    F UF[2];
-    const size_t st_off = ((size_t)n * H + h) * DK * DV;
-    if (is_scan) {
-        const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-        for (int ct = 0; ct < KT; ++ct)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float2 v = p.s0 ? *reinterpret_cast<const float2 *>(
-                                            p.s0 + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + 32 * wave + 2 * lr)
-                                      : make_float2(0.f, 0.f);
-                Sr[0][ct][e] = v.x;
-                Sr[1][ct][e] = v.y;
-            }
-    }
+        for (int it = -1; it < nchunks; ++it) {
+            char *const sm = smem + opaque_s(0);
+            const int lane = opaque_v((int)threadIdx.x) & 63, lr = lane & 15, lq = lane >> 4;
 
-    // ---- prep-wave state ----------------------------------------------------------------
-    // bf16 inputs: the raw rows of chunk c+3 are fetched with 16-byte loads (about 32 KB in
-    // flight per workgroup) while chunk c+1 is prepared, staged into LDS one iteration
-    // later, and read back by P1 in the layout it needs.  fp32 inputs (a precision path,
-    // not a throughput one) are fetched per element pair straight into registers.
-    // Every load is unconditional -- rows past the end of the sequence re-read its last
-    // row and are masked where consumed -- so issuing never waits for memory.
-    constexpr bool STAGE = L::STAGE;
-    constexpr int KU = DK / 8, GU = DK / 4;   // 16-byte units per k/q row and per g row
-    uint4 sk[2], sq[2], sg[4];
-    float sb = 0.f;
-    auto stage_load = [&](int ch) {
-        const int pt = opaque_v((int)threadIdx.x - 64 * NSW);
-        const int t0 = seq_start + ch * C32, nv = min(C32, seq_len - ch * C32);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int u = pt + 2 * DK * j, row = min(u / KU, nv - 1), cu = u % KU;
-            const size_t off = ((size_t)(t0 + row) * H + h) * DK + 8 * cu;
-            sk[j] = *reinterpret_cast<const uint4 *>(kg + off);
-            sq[j] = *reinterpret_cast<const uint4 *>(qg + off);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int u = pt + 2 * DK * j, row = min(u / GU, nv - 1), cu = u % GU;
-            sg[j] = *reinterpret_cast<const uint4 *>(p.g + ((size_t)(t0 + row) * H + h) * DK + 4 * cu);
-        }
-        if (pt < C32) sb = p.beta[(size_t)(t0 + min(pt, nv - 1)) * H + h];
-    };
-    auto stage_store = [&](char *sm) {
-        const int pt = opaque_v((int)threadIdx.x - 64 * NSW);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int u = pt + 2 * DK * j, row = u / KU, cu = u % KU;
-            *reinterpret_cast<uint4 *>(sm + L::STK + (row * DK + 8 * cu) * 2) = sk[j];
-            *reinterpret_cast<uint4 *>(sm + L::STQ + (row * DK + 8 * cu) * 2) = sq[j];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int u = pt + 2 * DK * j, row = u / GU, cu = u % GU;
-            *reinterpret_cast<uint4 *>(sm + L::STG + (row * DK + 4 * cu) * 4) = sg[j];
-        }
-        if (pt < C32) reinterpret_cast<float *>(sm + L::STB)[pt] = sb;
-    };
-    typename PR::raw kn_[8], qn_[8];   // fp32 path: element pairs of the next chunk
-    float2 gn_[8];
-    float bn_ = 0.f;
-    auto prefetch = [&](int ch) {
-        const int pt = opaque_v((int)threadIdx.x - 64 * NSW);
-        const int cp = pt % NCP, rgp = pt / NCP, c0 = 2 * cp;
-        const int t0 = seq_start + ch * C32, nv = min(C32, seq_len - ch * C32);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = min(8 * rgp + i, nv - 1);
-            const size_t off = ((size_t)(t0 + r) * H + h) * DK + c0;
-            kn_[i] = PR::load(kg + off);
-            qn_[i] = PR::load(qg + off);
-            gn_[i] = *reinterpret_cast<const float2 *>(p.g + off);
-        }
-        bn_ = p.beta[(size_t)(t0 + min(8 * rgp + (cp & 7), nv - 1)) * H + h];
-    };
-    if (!is_scan && nchunks > 0) {
-        if constexpr (STAGE) {
-            stage_load(0);
-            stage_store(smem);
-            if (nchunks > 1) stage_load(1);
-        } else {
-            prefetch(0);
-        }
-    }
-    lds_barrier();
-
-    typename PR::raw kr[8], qr[8];   // this chunk's k, q pairs (packed) from P1 to P2
-    float Fw[8][2], Bw[8][2];
-
-    for (int it = -1; it < nchunks; ++it) {
-        char *const sm = smem + opaque_s(0);
-        const int tid = opaque_v((int)threadIdx.x);
-        const int lane = tid & 63, lr = lane & 15, lq = lane >> 4;
-        const int nxt = it + 1;                      // chunk the prep waves work on
-        const bool have_nxt = nxt < nchunks;
-
-        // ================================ segment 1 ================================
-        if (is_scan) {
+            // ---- seg 1, b(it): Y = V - (Gamma*K) S ; U ; O = scale [ (Gamma*Q) S + A_qk U ]
             if (it >= 0) {
-                // b(it): Y = V - (Gamma*K) S ; U = T Y ; O = scale [ (Gamma*Q) S + A_qk U ]
                 const int t0 = seq_start + it * C32, nv = min(C32, seq_len - it * C32);
+                const char *vb = sm + L::VB + (it & 1) * L::VB_BUF + (32 * wave + 2 * lr) * (int)sizeof(IN_T);
+                f32x4_t Y[2][2];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float vr = jt ? PR::hi(Vr[rt][e]) : PR::lo(Vr[rt][e]);
-                            const float vv = 16 * rt + 4 * lq + e < nv ? vr : 0.f;
-                            Yacc[rt][jt][e] = vv - Yacc[rt][jt][e];
-                        }
-                F YF[2];
-#pragma unroll
-                for (int jt = 0; jt < 2; ++jt) YF[jt] = M::template from_tiles<true>(Yacc[0][jt], Yacc[1][jt]);
-                f32x4_t U[2][2];
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const F ft = M::template get<true>(sm + L::TM, L::TRI_PLANE, fbase<1>(rt, 0, lane));
-#pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) {
-                        U[rt][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                        mma<true, true>(U[rt][jt], ft, YF[jt]);
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * rt + 4 * lq + e;   // rows past the end hold zeros
+                        const typename PR::raw vw = *reinterpret_cast<const typename PR::raw *>(vb + r * L::VPITCH);
+                        Y[rt][0][e] = PR::lo(vw) - Yacc[rt][0][e];
+                        Y[rt][1][e] = PR::hi(vw) - Yacc[rt][1][e];
                     }
-                }
 #pragma unroll
-                for (int jt = 0; jt < 2; ++jt) UF[jt] = M::template from_tiles<true>(U[0][jt], U[1][jt]);
+                for (int jt = 0; jt < 2; ++jt) {
+                    // U0 = T00 Y0 ; W = A10 U0 ; U1 = T11 Y1 - M11 W
+                    f32x4_t u0 = {0.f, 0.f, 0.f, 0.f}, w = u0, u1 = u0;
+                    {
+                        const F t0f = M::template get<true>(sm + L::TM, L::TRI_PLANE, fbase<1>(0, 0, lane));
+                        mma<true, true>(u0, t0f, M::template from_tiles<true>(Y[0][jt], Y[1][jt]));
+                    }
+                    {
+                        const F awf = M::template get<true>(sm + L::AW, L::AW_PLANE, fbase<1>(0, 0, lane));
+                        mma<true, true>(w, awf, M::template from_tiles<true>(u0, Y[1][jt]));
+                    }
+                    {
+                        const F t1f = M::template get<true>(sm + L::TM, L::TRI_PLANE, fbase<1>(1, 0, lane));
+                        mma<true, true>(u1, t1f, M::template from_tiles<true>(w, Y[1][jt]));
+                    }
+                    UF[jt] = M::template from_tiles<true>(u0, u1);
+                }
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
                     const F fa = M::template get<true>(sm + L::AQK, L::TRI_PLANE, fbase<1>(rt, 0, lane));
@@ -271,77 +197,32 @@ chunk32_kernel(const ChunkParams p) {
                     }
                 }
             }
-        } else if (have_nxt) {
-            // P1(nxt): decay factors alpha = exp(g) and running products within 8-row groups
-            const int pt = tid - 64 * NSW;
-            const int cp = pt % NCP, rgp = pt / NCP, c0 = 2 * cp;
-            float *s_xchg = reinterpret_cast<float *>(sm + L::XCHG);
-            float *s_beta = reinterpret_cast<float *>(sm + L::BETA);
-            const int nv = min(C32, seq_len - nxt * C32);
-            float al[8][2];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int r = 8 * rgp + i;
-                const bool valid = r < nv;   // padded rows: k = q = 0, alpha = 1, beta = 0
-                typename PR::raw kw, qw;
-                float2 gw;
-                if constexpr (STAGE) {
-                    kw = *reinterpret_cast<const typename PR::raw *>(sm + L::STK + (r * DK + c0) * 2);
-                    qw = *reinterpret_cast<const typename PR::raw *>(sm + L::STQ + (r * DK + c0) * 2);
-                    gw = *reinterpret_cast<const float2 *>(sm + L::STG + (r * DK + c0) * 4);
-                } else {
-                    kw = kn_[i];
-                    qw = qn_[i];
-                    gw = gn_[i];
-                }
-                kr[i] = valid ? kw : PR::zero();
-                qr[i] = valid ? qw : PR::zero();
-                al[i][0] = valid ? __expf(gw.x) : 1.f;
-                al[i][1] = valid ? __expf(gw.y) : 1.f;
-            }
-            if (cp < 8) {
-                const int r = 8 * rgp + cp;
-                const float bw = STAGE ? reinterpret_cast<const float *>(sm + L::STB)[r] : bn_;
-                s_beta[r] = r < nv ? bw : 0.f;
-            }
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                float f = 1.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) { f *= al[i][c]; Fw[i][c] = f; }
-                float b = 1.f;
-#pragma unroll
-                for (int i = 7; i >= 0; --i) { Bw[i][c] = b; b *= al[i][c]; }
-                s_xchg[rgp * DK + c0 + c] = f;
-            }
-            if constexpr (!STAGE) {
-                if (nxt + 1 < nchunks) prefetch(nxt + 1);
-            }
-        }
-        lds_barrier();
+            lds_barrier();
 
-        // ================================ segment 2 ================================
-        if (is_scan) {
+            // ---- seg 2, c(it): S <- Diag(Gamma_last) S + (e^{G_last-G} K)^T U
             if (it >= 0) {
-                // c(it): S <- Diag(Gamma_last) S + (e^{G_last-G} K)^T U
                 const int buf = it & 1;
                 const float *s_gc = reinterpret_cast<const float *>(sm + L::GC) + buf * DK;
 #pragma unroll
                 for (int ct = 0; ct < KT; ++ct) {
                     const F fk = M::template get<true>(sm + L::KHT + buf * L::KHT_BUF, L::KHT_PLANE,
                                                        fbase<1>(ct, 0, lane));
+                    const float4 gc = *reinterpret_cast<const float4 *>(s_gc + 16 * ct + 4 * lq);
+                    const float gcv[4] = {gc.x, gc.y, gc.z, gc.w};
 #pragma unroll
                     for (int jt = 0; jt < 2; ++jt) {
                         f32x4_t acc;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[e] = s_gc[16 * ct + 4 * lq + e] * Sr[jt][ct][e];
+                        for (int e = 0; e < 4; ++e) acc[e] = gcv[e] * Sr[jt][ct][e];
                         mma<true, true>(acc, fk, UF[jt]);
                         Sr[jt][ct] = acc;
                     }
                 }
                 const int nv = min(C32, seq_len - it * C32);
-                if (p.every > 0 && nv == C32 && ((it + 1) * C32) % p.every == 0) {
-                    const int64_t m = p.ckpt_base[n] + ((it + 1) * C32) / p.every - 1;
+                if (every_chunks > 0 && --ck_left == 0 && nv == C32) {
+                    // state after in-sequence position (it + 1) * 32, a multiple of checkpoint_every
+                    ck_left = every_chunks;
+                    const int64_t m = p.ckpt_base[n] + ck_idx++;
                     float *dst = p.ckpt + ((size_t)m * H + h) * DK * DV;
 #pragma unroll
                     for (int ct = 0; ct < KT; ++ct)
@@ -351,68 +232,11 @@ chunk32_kernel(const ChunkParams p) {
                                 make_float2(Sr[0][ct][e], Sr[1][ct][e]);
                 }
             }
-        } else if (have_nxt) {
-            // P2(nxt): complete the running products across the two 8-row halves of each
-            // sub-chunk and write the decayed operands.
-            const int pt = tid - 64 * NSW;
-            const int cp = pt % NCP, rgp = pt / NCP, c0 = 2 * cp;
-            const int sa = rgp >> 1, hf = rgp & 1;
-            const float *s_xchg = reinterpret_cast<const float *>(sm + L::XCHG);
-            const int buf = nxt & 1;
-            float lead[2], tail[2], pre[2], post[2], dgf[2];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const float P0 = s_xchg[0 * DK + c0 + c] * s_xchg[1 * DK + c0 + c];
-                const float P1 = s_xchg[2 * DK + c0 + c] * s_xchg[3 * DK + c0 + c];
-                lead[c] = hf ? s_xchg[(rgp - 1) * DK + c0 + c] : 1.f;   // rows of the half before
-                tail[c] = hf ? 1.f : s_xchg[(rgp + 1) * DK + c0 + c];   // rows of the half after
-                pre[c] = sa ? P0 : 1.f;            // e^{G} at the end of the previous sub-chunk
-                post[c] = sa ? 1.f : P1;           // decay from the end of this sub-chunk to the chunk end
-                dgf[c] = 1.f / (sa ? P1 : P0);     // column factor of the diagonal Gram tile
-                if (rgp == 0) reinterpret_cast<float *>(sm + L::GC)[buf * DK + c0 + c] = P0 * P1;
-            }
-            float kend[8][2];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int r = 8 * rgp + i, rl = r - 16 * sa;
-                float ks[2], qs[2], gk[2], qt[2], kd[2];
-                const float kv[2] = {PR::lo(kr[i]), PR::hi(kr[i])}, qv[2] = {PR::lo(qr[i]), PR::hi(qr[i])};
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const float es = Fw[i][c] * lead[c];   // e^{G_r - G_ref}, ref = sub-chunk start
-                    const float ee = Bw[i][c] * tail[c];   // e^{G_end - G_r},  end = sub-chunk end
-                    ks[c] = kv[c] * es;
-                    qs[c] = qv[c] * es;
-                    gk[c] = ks[c] * pre[c];
-                    qt[c] = qs[c] * pre[c];
-                    kend[i][c] = kv[c] * ee;
-                    kd[c] = kend[i][c] * dgf[c];
-                }
-                M::template put_hl<2>(sm + L::KS, L::SQ_PLANE, fofs<KB>(r, c0), ks);
-                M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, fofs<KB>(r, c0), qs);
-                M::put_h2(sm + L::GK, fofs<KB>(r, c0), gk[0], gk[1]);
-                M::template put_hl<2>(sm + L::QT, L::QT_PLANE, fofs<KB>(r, c0), qt);
-                // Kn versions: sub-chunk 0 rows feed tiles (0,0) [x 1/P0] and (1,0) [x 1];
-                // sub-chunk 1 rows feed tile (1,1) [x 1/P1].
-                M::template put_hl<2>(sm + L::KN, L::KN_PLANE, fofs<KB>(32 * sa + rl, c0), kd);
-                if (sa == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, fofs<KB>(16 + rl, c0), kend[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                const int r = 8 * rgp + i;
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const float kh[2] = {kend[i][c] * post[c], kend[i + 1][c] * post[c]};
-                    M::template put_hl<2>(sm + L::KHT + buf * L::KHT_BUF, L::KHT_PLANE, fofs<1>(c0 + c, r), kh);
-                }
-            }
-        }
-        lds_barrier();
+            lds_barrier();
 
-        // ================================ segment 3 ================================
-        if (is_scan) {
-            if (have_nxt) {
-                // a(nxt): Yacc = (Gamma*K) S and Oacc = (Gamma*Q) S for the next chunk
+            // ---- seg 3, a(it+1): Yacc = (Gamma*K) S, Oacc = (Gamma*Q) S for the next chunk
+            if (it + 1 < nchunks) {
+                const float *s_p0 = reinterpret_cast<const float *>(sm + L::P0);
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -422,123 +246,242 @@ chunk32_kernel(const ChunkParams p) {
                     }
 #pragma unroll
                 for (int s = 0; s < KB; ++s) {
-                    F sf[2];
+                    // channels of this K-step held by the lane: 32 s + 4 lq + e and 32 s + 16 + 4 lq + e
+                    const float4 pa = *reinterpret_cast<const float4 *>(s_p0 + 32 * s + 4 * lq);
+                    const float4 pb = *reinterpret_cast<const float4 *>(s_p0 + 32 * s + 16 + 4 * lq);
+                    const float sc[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+                    const F fk0 = M::template get<false>(sm + L::KS, 0, fbase<KB>(0, s, lane));
+                    const F fq0 = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(0, s, lane));
+                    const F fk1 = M::template get<false>(sm + L::KS, 0, fbase<KB>(1, s, lane));
+                    const F fq1 = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(1, s, lane));
 #pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) sf[jt] = M::template from_tiles<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) {
-                        const F fg = M::template get<false>(sm + L::GK, 0, fbase<KB>(rt, s, lane));
-                        const F fq = M::template get<true>(sm + L::QT, L::QT_PLANE, fbase<KB>(rt, s, lane));
-#pragma unroll
-                        for (int jt = 0; jt < 2; ++jt) {
-                            mma<false, false>(Yacc[rt][jt], fg, sf[jt]);
-                            mma<true, true>(Oacc[rt][jt], fq, sf[jt]);
-                        }
+                    for (int jt = 0; jt < 2; ++jt) {
+                        const F sf = M::template from_tiles<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
+                        mma<false, false>(Yacc[0][jt], fk0, sf);
+                        mma<true, true>(Oacc[0][jt], fq0, sf);
+                        const F sp = M::template from_tiles_scaled<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1], sc);
+                        mma<false, false>(Yacc[1][jt], fk1, sp);
+                        mma<true, true>(Oacc[1][jt], fq1, sp);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                // value rows of the next chunk, consumed in its stage b.  The loads are
-                // unconditional (rows past the end read the last valid row) so that nothing
-                // waits for them here; stage b masks and widens them.
-                const int t0 = seq_start + nxt * C32, nv = min(C32, seq_len - nxt * C32);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = min(16 * rt + 4 * lq + e, nv - 1);
-                        Vr[rt][e] = PR::load(vg + ((size_t)(t0 + r) * H + h) * DV + 32 * wave + 2 * lr);
-                    }
             }
-        } else if (have_nxt) {
-            // P3(nxt): Gram tiles, T = (I + A_kk)^{-1} Diag(beta), A_qk
-            const int pw = wave - NSW;
-            float *zt = reinterpret_cast<float *>(sm + L::ZT);
-            const float *s_beta = reinterpret_cast<const float *>(sm + L::BETA);
-            auto gram = [&](int a, int b, int row_base_b, const char *rows_a) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            lds_barrier();
+        }
+
+        if (p.sf) {
+            // (lane index recomputed opaquely: row offsets shared with the initial-state loads
+            // would otherwise be kept live in registers across the whole loop)
+            const int lane = opaque_v((int)threadIdx.x) & 63, lr = lane & 15, lq = lane >> 4;
 #pragma unroll
-                for (int s = 0; s < KB; ++s) {
-                    const F fa = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(row_base_b, s, lane));
-                    const F fb = M::template get<true>(rows_a, L::SQ_PLANE, fbase<KB>(a, s, lane));
-                    mma<true, true>(acc, fa, fb);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                (void)b;
-                return acc;   // lane holds A[16a + lr][16b + 4lq + e]
-            };
-            if (pw == 0) {
-                // A_kk tiles (0,0), (1,0), (1,1) -> beta-scaled, masked fp32 tiles
-#pragma unroll
-                for (int t = 0; t < 3; ++t) {
-                    const int a = t == 0 ? 0 : 1, b = t == 2 ? 1 : 0;
-                    const f32x4_t acc = gram(a, b, t, sm + L::KS);
-                    const float br = s_beta[16 * a + lr];
-                    float4 w;
-                    float *wv = reinterpret_cast<float *>(&w);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) wv[e] = (b < a || 4 * lq + e < lr) ? br * acc[e] : 0.f;
-                    *reinterpret_cast<float4 *>(zt + t * TSZ + lr * TP + 4 * lq) = w;
-                }
-                wave_lds_sync();
-                // diagonal inverses M_aa = (I + L_aa)^{-1}: lane (a, j) owns column j of block a
-                if (lane < 32) {
-                    const int a = lane >> 4, j = lane & 15;
-                    float *Lt = zt + (a == 0 ? 0 : 2) * TSZ;
-                    float x[16];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float acc = (r == j) ? 1.f : 0.f;
-#pragma unroll
-                        for (int i = 0; i < r; ++i) acc -= Lt[r * TP + i] * x[i];
-                        x[r] = acc;
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    const float bj = s_beta[16 * a + j];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        Lt[r * TP + j] = x[r];
-                        M::put_hl1(sm + L::TM, L::TRI_PLANE, fofs<1>(16 * a + r, 16 * a + j), x[r] * bj);
-                    }
-                }
-                wave_lds_sync();
-                // M10 = -M11 L10 M00 ; T10 = M10 Diag(beta_0..15)
-                f32x4_t R = {0.f, 0.f, 0.f, 0.f}, Mo = {0.f, 0.f, 0.f, 0.f};
-                tmm_ll(R, zt + 1 * TSZ, zt + 0 * TSZ, lane);
-                tmm_lr(Mo, zt + 2 * TSZ, R, lane);
-                const float bj = s_beta[lr];
+            for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    M::put_hl1(sm + L::TM, L::TRI_PLANE, fofs<1>(16 + 4 * lq + e, lr), -Mo[e] * bj);
-            } else {
-                // A_qk tiles (lower, including the diagonal)
-                for (int t = pw - 1; t < 3; t += NPW - 1) {
-                    const int a = t == 0 ? 0 : 1, b = t == 2 ? 1 : 0;
-                    const f32x4_t acc = gram(a, b, t, sm + L::QS);
-                    float w[4];
+                    *reinterpret_cast<float2 *>(p.sf + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + 32 * wave + 2 * lr) =
+                        make_float2(Sr[0][ct][e], Sr[1][ct][e]);
+        }
+    } else {
+        // ============================== prep waves ==============================
+        // Thread pt = (rgp, cp): rows 4 rgp .. 4 rgp + 3 of the chunk, channels 2 cp, 2 cp + 1.
+        const int pt = (int)threadIdx.x - 64 * NSW;
+        const int pw = wave - NSW;
+
+        // structurally zero blocks: columns 16..31 of TM rows 0..15, of AQK rows 0..15, of AW
+        for (int idx = pt; idx < 256; idx += 64 * NPW) {
+            const int r = idx >> 4, c = 16 + (idx & 15);
+            M::put_hl1(smem + L::TM, L::TRI_PLANE, fofs<1>(r, c), 0.f);
+            M::put_hl1(smem + L::AQK, L::TRI_PLANE, fofs<1>(r, c), 0.f);
+            M::put_hl1(smem + L::AW, L::AW_PLANE, fofs<1>(r, c), 0.f);
+        }
+
+        typename PR::raw kn_[4], qn_[4], vn_[4];   // raw rows of the chunk prepared next
+        float2 gn_[4];
+        float bn_ = 0.f;
+        auto prefetch = [&](int ch) {
+            const int t = opaque_v(pt);
+            const int cp = t % NCP, rgp = t / NCP, c0 = 2 * cp;
+            const int t0 = seq_start + ch * C32, nv = min(C32, seq_len - ch * C32);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = (b < a || 4 * lq + e <= lr) ? acc[e] : 0.f;
-                    M::template put_hl<4>(sm + L::AQK, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * b + 4 * lq), w);
+            for (int i = 0; i < 4; ++i) {
+                const int r = min(4 * rgp + i, nv - 1);
+                const size_t off = ((size_t)(t0 + r) * H + h) * DK + c0;
+                kn_[i] = PR::load(kg + off);
+                qn_[i] = PR::load(qg + off);
+                vn_[i] = PR::load(vg + off);   // DV == DK: the same element offsets
+                gn_[i] = *reinterpret_cast<const float2 *>(p.g + off);
+            }
+            bn_ = p.beta[(size_t)(t0 + min(4 * rgp + (cp & 3), nv - 1)) * H + h];
+        };
+        if (nchunks > 0) prefetch(0);
+
+        typename PR::raw kr[4], qr[4];   // this chunk's k, q pairs from P1 to P2
+        float Fw[4][2], Bw[4][2];        // decay products within the 4-row group: through row i / after row i
+
+        for (int it = -1; it < nchunks; ++it) {
+            char *const sm = smem + opaque_s(0);
+            const int t = opaque_v(pt);
+            const int cp = t % NCP, rgp = t / NCP, c0 = 2 * cp, sa = rgp >> 2;
+            const int lane = t & 63, lr = lane & 15, lq = lane >> 4;
+            const int nxt = it + 1;
+            const bool have = nxt < nchunks;
+            float *s_xchg = reinterpret_cast<float *>(sm + L::XCHG);
+            float *s_beta = reinterpret_cast<float *>(sm + L::BETA);
+
+            // ---- seg 1, P1(nxt): alpha = exp(g), running products over the 4-row group
+            if (have) {
+                const int nv = min(C32, seq_len - nxt * C32);
+                float al[4][2];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool valid = 4 * rgp + i < nv;   // padded rows: k = q = 0, alpha = 1, beta = 0
+                    kr[i] = valid ? kn_[i] : PR::zero();
+                    qr[i] = valid ? qn_[i] : PR::zero();
+                    *reinterpret_cast<typename PR::raw *>(sm + L::VB + (nxt & 1) * L::VB_BUF + (4 * rgp + i) * L::VPITCH +
+                                                          c0 * (int)sizeof(IN_T)) = valid ? vn_[i] : PR::zero();
+                    al[i][0] = valid ? __expf(gn_[i].x) : 1.f;
+                    al[i][1] = valid ? __expf(gn_[i].y) : 1.f;
+                }
+                if (cp < 4) s_beta[4 * rgp + cp] = 4 * rgp + cp < nv ? bn_ : 0.f;
+                float tot[2];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    float f = 1.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) { f *= al[i][c]; Fw[i][c] = f; }
+                    float b = 1.f;
+#pragma unroll
+                    for (int i = 3; i >= 0; --i) { Bw[i][c] = b; b *= al[i][c]; }
+                    tot[c] = f;
+                }
+                *reinterpret_cast<float2 *>(s_xchg + rgp * DK + c0) = make_float2(tot[0], tot[1]);
+                if (nxt + 1 < nchunks) prefetch(nxt + 1);
+            }
+            lds_barrier();
+
+            // ---- seg 2, P2(nxt): decayed operands
+            if (have) {
+                const int buf = nxt & 1;
+                float lead[2] = {1.f, 1.f}, tail[2] = {1.f, 1.f}, P0[2] = {1.f, 1.f}, P1[2] = {1.f, 1.f};
+#pragma unroll
+                for (int g = 0; g < 8; ++g) {
+                    const float2 x2 = *reinterpret_cast<const float2 *>(s_xchg + g * DK + c0);
+                    const float x[2] = {x2.x, x2.y};
+                    const bool same = (g >> 2) == sa;
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        if (g < 4) P0[c] *= x[c]; else P1[c] *= x[c];
+                        if (same && g < rgp) lead[c] *= x[c];
+                        if (same && g > rgp) tail[c] *= x[c];
+                    }
+                }
+                float post[2], dgf[2];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    post[c] = sa ? 1.f : P1[c];            // decay from the end of this sub-chunk to the chunk end
+                    dgf[c] = 1.f / (sa ? P1[c] : P0[c]);   // column factor of the diagonal Gram tile
+                }
+                if (rgp == 0) {
+                    *reinterpret_cast<float2 *>(sm + L::GC + (buf * DK + c0) * 4) = make_float2(P0[0] * P1[0], P0[1] * P1[1]);
+                    *reinterpret_cast<float2 *>(sm + L::P0 + c0 * 4) = make_float2(P0[0], P0[1]);
+                }
+                float kh[2][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * rgp + i, rl = r - 16 * sa;
+                    float ks[2], qs[2], ke[2], kd[2];
+                    const float kv[2] = {PR::lo(kr[i]), PR::hi(kr[i])}, qv[2] = {PR::lo(qr[i]), PR::hi(qr[i])};
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const float es = Fw[i][c] * lead[c];   // e^{G_r - G_ref}
+                        const float ee = Bw[i][c] * tail[c];   // e^{G_end(sub-chunk) - G_r}
+                        ks[c] = kv[c] * es;
+                        qs[c] = qv[c] * es;
+                        ke[c] = kv[c] * ee;
+                        kd[c] = ke[c] * dgf[c];
+                        kh[c][i] = ke[c] * post[c];
+                    }
+                    M::template put_hl<2>(sm + L::KS, L::SQ_PLANE, fofs<KB>(r, c0), ks);
+                    M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, fofs<KB>(r, c0), qs);
+                    // Kn rows: sub-chunk 0 feeds tiles (0,0) [x 1/P0] and (1,0) [x 1]; sub-chunk 1 feeds (1,1) [x 1/P1]
+                    M::template put_hl<2>(sm + L::KN, L::KN_PLANE, fofs<KB>(32 * sa + rl, c0), kd);
+                    if (sa == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, fofs<KB>(16 + rl, c0), ke);
+                }
+                // (e^{G_last-G} K)^T: the 4 rows of this group are 4 consecutive K-slots of one fragment
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    M::template put_hl<4>(sm + L::KHT + buf * L::KHT_BUF, L::KHT_PLANE, fofs<1>(c0 + c, 4 * rgp), kh[c]);
+            }
+            lds_barrier();
+
+            // ---- seg 3, P3(nxt): Gram tiles, T00, [-M11 T11], A10, A_qk
+            if (have) {
+                auto gram = [&](int knb, const char *rows, int a) {
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KB; ++s) {
+                        const F fa = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(knb, s, lane));
+                        const F fb = M::template get<true>(rows, L::SQ_PLANE, fbase<KB>(a, s, lane));
+                        mma<true, true>(acc, fa, fb);
+                    }
+                    return acc;   // lane holds G[16 a + lr][16 b + 4 lq + e] of the tile against Kn block knb
+                };
+                for (int task = pw; task < 6; task += NPW) {
+                    if (task < 2) {
+                        // diagonal block a: A_aa (strictly lower, beta-scaled rows) -> M_aa by substitution
+                        const int a = task;
+                        float *zt = reinterpret_cast<float *>(sm + L::ZT) + a * TSZ;
+                        const f32x4_t acc = gram(2 * a, sm + L::KS, a);
+                        const float br = s_beta[16 * a + lr];
+                        float4 w;
+                        float *wv = reinterpret_cast<float *>(&w);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) wv[e] = 4 * lq + e < lr ? br * acc[e] : 0.f;
+                        *reinterpret_cast<float4 *>(zt + lr * TP + 4 * lq) = w;
+                        wave_lds_sync();
+                        if (lane < 16) {
+                            const int j = lane;   // column j of M_aa
+                            float x[16];
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                float s = (r == j) ? 1.f : 0.f;
+#pragma unroll
+                                for (int i = 0; i < r; ++i) s -= zt[r * TP + i] * x[i];
+                                x[r] = s;
+                            }
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) zt[r * TP + j] = x[r];
+                        }
+                        wave_lds_sync();
+                        const float4 m4 = *reinterpret_cast<const float4 *>(zt + lr * TP + 4 * lq);
+                        const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+                        const float4 b4 = *reinterpret_cast<const float4 *>(s_beta + 16 * a + 4 * lq);
+                        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+                        float tv[4], nm[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { tv[e] = mv[e] * bv[e]; nm[e] = -mv[e]; }
+                        M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * a + 4 * lq), tv);
+                        if (a == 1) M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 + lr, 4 * lq), nm);
+                    } else if (task == 2) {
+                        // A10 (beta-scaled rows of sub-chunk 1)
+                        const f32x4_t acc = gram(1, sm + L::KS, 1);
+                        const float br = s_beta[16 + lr];
+                        float w[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[e] = br * acc[e];
+                        M::template put_hl<4>(sm + L::AW, L::AW_PLANE, fofs<1>(lr, 4 * lq), w);
+                    } else {
+                        // A_qk tile (a, b), lower including the diagonal
+                        const int tq = task - 3, a = tq == 0 ? 0 : 1, b = tq == 2 ? 1 : 0;
+                        const f32x4_t acc = gram(tq, sm + L::QS, a);
+                        float w[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[e] = (b < a || 4 * lq + e <= lr) ? acc[e] : 0.f;
+                        M::template put_hl<4>(sm + L::AQK, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * b + 4 * lq), w);
+                    }
                 }
             }
+            lds_barrier();
         }
-        if constexpr (STAGE) {
-            // stage chunk it+2 (fetched one iteration ago) and fetch chunk it+3
-            if (!is_scan) {
-                if (it + 2 < nchunks) stage_store(sm);
-                if (it + 3 < nchunks) stage_load(it + 3);
-            }
-        }
-        lds_barrier();
-    }
-
-    if (is_scan && p.sf) {
-        const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-        for (int ct = 0; ct < KT; ++ct)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                *reinterpret_cast<float2 *>(p.sf + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + 32 * wave + 2 * lr) =
-                    make_float2(Sr[0][ct][e], Sr[1][ct][e]);
     }
 }
 
@@ -547,7 +490,7 @@ chunk32_kernel(const ChunkParams p) {
 extern "C" __attribute__((visibility("hidden"))) hipError_t
 kda_launch_chunk32(int dk, int in_bf16, unsigned grid, const kda::ChunkParams &p, hipStream_t stream) {
 #define KDA_C32(DKV, F32P, T) \
-    hipLaunchKernelGGL((kda::chunk32_kernel<DKV, F32P, T>), dim3(grid), dim3(DKV * 4), 0, stream, p)
+    hipLaunchKernelGGL((kda::chunk32_kernel<DKV, F32P, T>), dim3(grid), dim3(kda::chunk32_threads<DKV>()), 0, stream, p)
     if (dk == 128 && in_bf16) KDA_C32(128, false, uint16_t);
     else if (dk == 128) KDA_C32(128, true, float);
     else if (dk == 64 && in_bf16) KDA_C32(64, false, uint16_t);
