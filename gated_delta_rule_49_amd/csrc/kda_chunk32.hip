@@ -24,16 +24,20 @@
 // LDS-only barriers per iteration (global loads stay in flight across them):
 //
 //            scan waves                                prep waves
-//   seg 1    b(i): Y = V - Y, U, O (stores)            P1(i+1): exp(g), 4-row running products
-//   seg 2    c(i): S <- Gamma_last S + Khat^T U        P2(i+1): decayed operands -> LDS
-//   seg 3    a(i+1): (Gamma*K) S, (Gamma*Q) S          P3(i+1): Gram tiles, T00, [-M11 T11], A10, A_qk
+//   seg 1    -                                         P1(i+1): exp(g), 4-row running products;
+//                                                      inverses of chunk i's diagonal blocks -> T00, [-M11 T11]
+//   seg 2    b(i), o(i), c(i): Y = V - Y, U, O,        P2(i+1): decayed operands -> LDS
+//            S <- Gamma_last S + Khat^T U
+//   seg 3    a(i+1): (Gamma*K) S, (Gamma*Q) S          P3(i+1): Khat^T, Gram tiles, A10, A_qk
 //
 // Every LDS operand is written in a segment after its last read by the previous
-// chunk, so one copy suffices, except (e^{G_last-G} K)^T and Gamma_last, which
-// P2 writes while stage c still reads the previous chunk's: those two are
-// double-buffered.  Prep waves load the raw rows of chunk i+2 straight into
-// registers while preparing chunk i+1; every load is unconditional (rows past
-// the end of the sequence re-read its last row and are masked where used).
+// chunk, so one copy suffices; (e^{G_last-G} K)^T and Gamma_last, which stage c
+// reads in segment 2, are therefore written in segment 3.  Only the raw value
+// rows (written in segment 1, read by stage b in segment 1 of the next
+// iteration) are double-buffered.  Prep waves load the raw rows of chunk i+2
+// straight into registers while preparing chunk i+1; every load is
+// unconditional (rows past the end of the sequence re-read its last row and are
+// masked where used).
 //
 // Precision: hi+lo bf16 operand pairs on every product feeding the outputs
 // except (Gamma*K) S, fp32 accumulation, fp32 o and S.  The fp32-input
@@ -51,26 +55,25 @@ struct Lds32 {
     static constexpr int KS = 0;                          // [32][DK] hl: K * e^{G - G_ref}
     static constexpr int QS = KS + 32 * DK * 4;           // [32][DK] hl: Q * e^{G - G_ref}
     static constexpr int SQ_PLANE = 32 * DK * ES;
-    static constexpr int KHT = QS + 32 * DK * 4;          // 2 x [DK][32] hl: (e^{G_last-G} K)^T
+    static constexpr int KHT = QS + 32 * DK * 4;          // [DK][32] hl: (e^{G_last-G} K)^T
     static constexpr int KHT_PLANE = DK * 32 * ES;
-    static constexpr int KHT_BUF = DK * 32 * 4;
-    static constexpr int TM = KHT + 2 * KHT_BUF;          // [32][32] hl: [T00 0 ; -M11 T11]
+    static constexpr int TM = KHT + DK * 32 * 4;          // [32][32] hl: [T00 0 ; -M11 T11]
     static constexpr int TRI_PLANE = 32 * 32 * ES;
     static constexpr int AQK = TM + 32 * 32 * 4;          // [32][32] hl: A_qk, lower incl. diagonal
     static constexpr int AW = AQK + 32 * 32 * 4;          // [16][32] hl: [A10 0]
     static constexpr int AW_PLANE = 16 * 32 * ES;
-    static constexpr int GC = AW + 16 * 32 * 4;           // 2 x [DK] fp32: Gamma_last
-    static constexpr int P0 = GC + 2 * DK * 4;            // [DK] fp32: e^{G} at the end of sub-chunk 0
+    static constexpr int GC = AW + 16 * 32 * 4;           // [DK] fp32: Gamma_last
+    static constexpr int P0 = GC + DK * 4;                // [DK] fp32: e^{G} at the end of sub-chunk 0
     static constexpr int VPITCH = DK * (int)sizeof(IN_T) + 16;   // padded row pitch (bytes) of the value rows
     static constexpr int VB = P0 + DK * 4;                // 2 x [32][VPITCH]: raw value rows of a chunk
     static constexpr int VB_BUF = 32 * VPITCH;
     // prep-wave scratch
     static constexpr int KN = VB + 2 * VB_BUF;            // [48][DK] hl: K e^{G_ref - G} for tiles (0,0), (1,0), (1,1)
     static constexpr int KN_PLANE = 48 * DK * ES;
-    static constexpr int ZT = KN + 48 * DK * 4;           // 2 fp32 tiles: A00 -> M00, A11 -> M11
+    static constexpr int ZT = KN + 48 * DK * 4;           // 2 fp32 tiles: L^T of the diagonal A_kk blocks
     static constexpr int XCHG = ZT + 2 * TSZ * 4;         // [8][DK] fp32: decay over each 4-row group
-    static constexpr int BETA = XCHG + 8 * DK * 4;        // [32] fp32
-    static constexpr int TOTAL = BETA + 32 * 4;
+    static constexpr int BETA = XCHG + 8 * DK * 4;        // 2 x [32] fp32
+    static constexpr int TOTAL = BETA + 2 * 32 * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -150,7 +153,11 @@ chunk32_kernel(const ChunkParams p) {
             char *const sm = smem + opaque_s(0);
             const int lane = opaque_v((int)threadIdx.x) & 63, lr = lane & 15, lq = lane >> 4;
 
-            // ---- seg 1, b(it): Y = V - (Gamma*K) S ; U ; O = scale [ (Gamma*Q) S + A_qk U ]
+            // ---- seg 1: nothing for the scan (the prep waves invert this chunk's diagonal blocks)
+            lds_barrier();
+
+            // ---- seg 2, b(it): Y = V - (Gamma*K) S, U ; o(it) = scale [ (Gamma*Q) S + A_qk U ] ;
+            //             c(it): S <- Diag(Gamma_last) S + (e^{G_last-G} K)^T U
             if (it >= 0) {
                 const int t0 = seq_start + it * C32, nv = min(C32, seq_len - it * C32);
                 const char *vb = sm + L::VB + (it & 1) * L::VB_BUF + (32 * wave + 2 * lr) * (int)sizeof(IN_T);
@@ -196,17 +203,10 @@ chunk32_kernel(const ChunkParams p) {
                                 make_float2(p.scale * acc[0][e], p.scale * acc[1][e]);
                     }
                 }
-            }
-            lds_barrier();
-
-            // ---- seg 2, c(it): S <- Diag(Gamma_last) S + (e^{G_last-G} K)^T U
-            if (it >= 0) {
-                const int buf = it & 1;
-                const float *s_gc = reinterpret_cast<const float *>(sm + L::GC) + buf * DK;
+                const float *s_gc = reinterpret_cast<const float *>(sm + L::GC);
 #pragma unroll
                 for (int ct = 0; ct < KT; ++ct) {
-                    const F fk = M::template get<true>(sm + L::KHT + buf * L::KHT_BUF, L::KHT_PLANE,
-                                                       fbase<1>(ct, 0, lane));
+                    const F fk = M::template get<true>(sm + L::KHT, L::KHT_PLANE, fbase<1>(ct, 0, lane));
                     const float4 gc = *reinterpret_cast<const float4 *>(s_gc + 16 * ct + 4 * lq);
                     const float gcv[4] = {gc.x, gc.y, gc.z, gc.w};
 #pragma unroll
@@ -218,7 +218,6 @@ chunk32_kernel(const ChunkParams p) {
                         Sr[jt][ct] = acc;
                     }
                 }
-                const int nv = min(C32, seq_len - it * C32);
                 if (every_chunks > 0 && --ck_left == 0 && nv == C32) {
                     // state after in-sequence position (it + 1) * 32, a multiple of checkpoint_every
                     ck_left = every_chunks;
@@ -316,6 +315,8 @@ chunk32_kernel(const ChunkParams p) {
 
         typename PR::raw kr[4], qr[4];   // this chunk's k, q pairs from P1 to P2
         float Fw[4][2], Bw[4][2];        // decay products within the 4-row group: through row i / after row i
+        float kh[2][4], gl[2];           // (e^{G_last-G} K)^T entries and Gamma_last, from P2 to P3
+        float lw[4] = {0.f, 0.f, 0.f, 0.f};   // diagonal Gram block (waves 0, 1), from P3 to the next segment 1
 
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
@@ -325,7 +326,7 @@ chunk32_kernel(const ChunkParams p) {
             const int nxt = it + 1;
             const bool have = nxt < nchunks;
             float *s_xchg = reinterpret_cast<float *>(sm + L::XCHG);
-            float *s_beta = reinterpret_cast<float *>(sm + L::BETA);
+            float *s_beta = reinterpret_cast<float *>(sm + L::BETA) + (nxt & 1) * 32;   // chunk nxt's
 
             // ---- seg 1, P1(nxt): alpha = exp(g), running products over the 4-row group
             if (have) {
@@ -354,13 +355,57 @@ chunk32_kernel(const ChunkParams p) {
                     tot[c] = f;
                 }
                 *reinterpret_cast<float2 *>(s_xchg + rgp * DK + c0) = make_float2(tot[0], tot[1]);
-                if (nxt + 1 < nchunks) prefetch(nxt + 1);
+                // Unconditional (the last chunk re-reads itself): a conditional refill would make
+                // the loop-carried registers a join of old and new values, and the compiler
+                // would then wait for the loads right here to copy them over.
+                prefetch(min(nxt + 1, nchunks - 1));
+            }
+            if (it >= 0 && pw < 2) {
+                // Diagonal block a = pw of chunk it: M = (I + N)^{-1} for the strictly lower N this
+                // wave's Gram tile left in lw (row lr, columns 4 lq + e) one segment ago, as
+                //     M = (I + X)(I + X^2)(I + X^4)(I + X^8),  X = -N,  N^16 = 0,
+                // with fp32 16x16x4 MFMA products (five dependent levels instead of a 16-step
+                // substitution).  T_aa = M Diag(beta_a) (and -M11) -> TM, read by stage b in segment 2.
+                const int a = pw;
+                float *zt = reinterpret_cast<float *>(sm + L::ZT) + a * TSZ;
+                const float *beta_it = reinterpret_cast<const float *>(sm + L::BETA) + (it & 1) * 32;
+                // forms of a 16x16 Z held by lane (lq, lr): "A" = Z[lr][4 lq + e], "B" = Z[4 lq + e][lr]
+#pragma unroll
+                for (int e = 0; e < 4; ++e) zt[(4 * lq + e) * TP + lr] = lw[e];
+                wave_lds_sync();
+                const float4 nb4 = *reinterpret_cast<const float4 *>(zt + lr * TP + 4 * lq);
+                const f32x4_t XA = {-lw[0], -lw[1], -lw[2], -lw[3]}, XB = {-nb4.x, -nb4.y, -nb4.z, -nb4.w};
+                // (Z W) in B form = mm(Z_A, W_B); in A form = mm(W_B, Z_A)
+                auto mm = [](const f32x4_t &za, const f32x4_t &wb) {
+                    f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) d = mfma_f32(za[kk], wb[kk], d);
+                    return d;
+                };
+                const f32x4_t X2B = mm(XA, XB), X2A = mm(XB, XA);
+                const f32x4_t X4B = mm(X2A, X2B), X4A = mm(X2B, X2A), X3A = mm(X2B, XA);
+                const f32x4_t X8B = mm(X4A, X4B);
+                const f32x4_t X12B = mm(X4A, X8B);
+                f32x4_t P1A, P2B;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float id = (4 * lq + e == lr) ? 1.f : 0.f;
+                    P1A[e] = id + XA[e] + X2A[e] + X3A[e];     // I + X + X^2 + X^3
+                    P2B[e] = id + X4B[e] + X8B[e] + X12B[e];   // I + X^4 + X^8 + X^12
+                }
+                const f32x4_t MA = mm(P2B, P1A);                // M = P1 P2, A form: M[lr][4 lq + e]
+                const float4 b4 = *reinterpret_cast<const float4 *>(beta_it + 16 * a + 4 * lq);
+                const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+                float tv[4], nm[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { tv[e] = MA[e] * bv[e]; nm[e] = -MA[e]; }
+                M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * a + 4 * lq), tv);
+                if (a == 1) M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 + lr, 4 * lq), nm);
             }
             lds_barrier();
 
             // ---- seg 2, P2(nxt): decayed operands
             if (have) {
-                const int buf = nxt & 1;
                 float lead[2] = {1.f, 1.f}, tail[2] = {1.f, 1.f}, P0[2] = {1.f, 1.f}, P1[2] = {1.f, 1.f};
 #pragma unroll
                 for (int g = 0; g < 8; ++g) {
@@ -380,11 +425,9 @@ chunk32_kernel(const ChunkParams p) {
                     post[c] = sa ? 1.f : P1[c];            // decay from the end of this sub-chunk to the chunk end
                     dgf[c] = 1.f / (sa ? P1[c] : P0[c]);   // column factor of the diagonal Gram tile
                 }
-                if (rgp == 0) {
-                    *reinterpret_cast<float2 *>(sm + L::GC + (buf * DK + c0) * 4) = make_float2(P0[0] * P1[0], P0[1] * P1[1]);
-                    *reinterpret_cast<float2 *>(sm + L::P0 + c0 * 4) = make_float2(P0[0], P0[1]);
-                }
-                float kh[2][4];
+                gl[0] = P0[0] * P1[0];
+                gl[1] = P0[1] * P1[1];
+                if (rgp == 0) *reinterpret_cast<float2 *>(sm + L::P0 + c0 * 4) = make_float2(P0[0], P0[1]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 4 * rgp + i, rl = r - 16 * sa;
@@ -406,78 +449,53 @@ chunk32_kernel(const ChunkParams p) {
                     M::template put_hl<2>(sm + L::KN, L::KN_PLANE, fofs<KB>(32 * sa + rl, c0), kd);
                     if (sa == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, fofs<KB>(16 + rl, c0), ke);
                 }
-                // (e^{G_last-G} K)^T: the 4 rows of this group are 4 consecutive K-slots of one fragment
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    M::template put_hl<4>(sm + L::KHT + buf * L::KHT_BUF, L::KHT_PLANE, fofs<1>(c0 + c, 4 * rgp), kh[c]);
             }
             lds_barrier();
 
             // ---- seg 3, P3(nxt): Gram tiles, T00, [-M11 T11], A10, A_qk
+            // Prep wave pw < 3 takes one Kn block and forms both Gram tiles that share it:
+            //   pw 0: tile (0,0)  A_kk -> M00 -> T00      and A_qk(0,0)
+            //   pw 1: tile (1,1)  A_kk -> M11 -> T11, -M11 and A_qk(1,1)
+            //   pw 2: tile (1,0)  A10                     and A_qk(1,0)
             if (have) {
-                auto gram = [&](int knb, const char *rows, int a) {
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                // (e^{G_last-G} K)^T and Gamma_last of chunk nxt: read by stage c of the next iteration,
+                // after stage c of this one has finished with chunk it's.  The 4 rows of this group
+                // are 4 consecutive K-slots of one fragment.
 #pragma unroll
-                    for (int s = 0; s < KB; ++s) {
-                        const F fa = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(knb, s, lane));
-                        const F fb = M::template get<true>(rows, L::SQ_PLANE, fbase<KB>(a, s, lane));
-                        mma<true, true>(acc, fa, fb);
-                    }
-                    return acc;   // lane holds G[16 a + lr][16 b + 4 lq + e] of the tile against Kn block knb
-                };
-                for (int task = pw; task < 6; task += NPW) {
-                    if (task < 2) {
-                        // diagonal block a: A_aa (strictly lower, beta-scaled rows) -> M_aa by substitution
-                        const int a = task;
-                        float *zt = reinterpret_cast<float *>(sm + L::ZT) + a * TSZ;
-                        const f32x4_t acc = gram(2 * a, sm + L::KS, a);
-                        const float br = s_beta[16 * a + lr];
-                        float4 w;
-                        float *wv = reinterpret_cast<float *>(&w);
+                for (int c = 0; c < 2; ++c)
+                    M::template put_hl<4>(sm + L::KHT, L::KHT_PLANE, fofs<1>(c0 + c, 4 * rgp), kh[c]);
+                if (rgp == 0) *reinterpret_cast<float2 *>(sm + L::GC + c0 * 4) = make_float2(gl[0], gl[1]);
+            }
+            if (have && pw < 3) {
+                const int knb = pw == 0 ? 0 : (pw == 1 ? 2 : 1);
+                const int a = pw == 0 ? 0 : 1, b = pw == 1 ? 1 : 0;
+                f32x4_t gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) wv[e] = 4 * lq + e < lr ? br * acc[e] : 0.f;
-                        *reinterpret_cast<float4 *>(zt + lr * TP + 4 * lq) = w;
-                        wave_lds_sync();
-                        if (lane < 16) {
-                            const int j = lane;   // column j of M_aa
-                            float x[16];
+                for (int s = 0; s < KB; ++s) {
+                    const F fn = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(knb, s, lane));
+                    const F fk = M::template get<true>(sm + L::KS, L::SQ_PLANE, fbase<KB>(a, s, lane));
+                    const F fq = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(a, s, lane));
+                    mma<true, true>(gk, fn, fk);
+                    mma<true, true>(gq, fn, fq);
+                }
+                // lane holds tile element (16 a + lr, 16 b + 4 lq + e)
+                {
+                    float w[4];
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                float s = (r == j) ? 1.f : 0.f;
+                    for (int e = 0; e < 4; ++e) w[e] = (b < a || 4 * lq + e <= lr) ? gq[e] : 0.f;
+                    M::template put_hl<4>(sm + L::AQK, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * b + 4 * lq), w);
+                }
+                const float br = s_beta[16 * a + lr];
+                if (pw == 2) {
+                    float w[4];
 #pragma unroll
-                                for (int i = 0; i < r; ++i) s -= zt[r * TP + i] * x[i];
-                                x[r] = s;
-                            }
+                    for (int e = 0; e < 4; ++e) w[e] = br * gk[e];
+                    M::template put_hl<4>(sm + L::AW, L::AW_PLANE, fofs<1>(lr, 4 * lq), w);
+                } else {
+                    // strictly lower part of A_kk(a, a) with beta-scaled rows, kept for the inversion
+                    // in segment 1 of the next iteration (this lane: row lr, columns 4 lq + e)
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) zt[r * TP + j] = x[r];
-                        }
-                        wave_lds_sync();
-                        const float4 m4 = *reinterpret_cast<const float4 *>(zt + lr * TP + 4 * lq);
-                        const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
-                        const float4 b4 = *reinterpret_cast<const float4 *>(s_beta + 16 * a + 4 * lq);
-                        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
-                        float tv[4], nm[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) { tv[e] = mv[e] * bv[e]; nm[e] = -mv[e]; }
-                        M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * a + 4 * lq), tv);
-                        if (a == 1) M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 + lr, 4 * lq), nm);
-                    } else if (task == 2) {
-                        // A10 (beta-scaled rows of sub-chunk 1)
-                        const f32x4_t acc = gram(1, sm + L::KS, 1);
-                        const float br = s_beta[16 + lr];
-                        float w[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) w[e] = br * acc[e];
-                        M::template put_hl<4>(sm + L::AW, L::AW_PLANE, fofs<1>(lr, 4 * lq), w);
-                    } else {
-                        // A_qk tile (a, b), lower including the diagonal
-                        const int tq = task - 3, a = tq == 0 ? 0 : 1, b = tq == 2 ? 1 : 0;
-                        const f32x4_t acc = gram(tq, sm + L::QS, a);
-                        float w[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) w[e] = (b < a || 4 * lq + e <= lr) ? acc[e] : 0.f;
-                        M::template put_hl<4>(sm + L::AQK, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * b + 4 * lq), w);
-                    }
+                    for (int e = 0; e < 4; ++e) lw[e] = 4 * lq + e < lr ? br * gk[e] : 0.f;
                 }
             }
             lds_barrier();

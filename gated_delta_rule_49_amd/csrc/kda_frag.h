@@ -16,27 +16,33 @@ constexpr int TSZ = 16 * TP;
 //     k%32 <  16 : q = (k%16)/4, e = k%4          k%32 >= 16 : q = (k%16)/4, e = 4 + k%4
 // which is also the row order of a pair of 16x16 MFMA output tiles, so an
 // output pair can be fed back as an operand straight from registers.
-__device__ __forceinline__ int frag_slot(int rr, int q, int kb) { return 16 * q + (rr ^ ((2 * q + 8 * kb) & 15)); }
+// Inside a block, the 16 fragments of lane group q are permuted by XOR with
+// (q + 4 kb + rb): any such permutation keeps the 16-byte fragment reads
+// conflict-free, and this one spreads the 4-byte writes of one row across all
+// 32 banks, and the writes of one column across 8 fragment slots.
+__device__ __forceinline__ int frag_slot(int rr, int q, int kb, int rb) {
+    return 16 * q + (rr ^ ((q + 4 * kb + rb) & 15));
+}
 
 template <int KB>
 __device__ __forceinline__ int fofs(int r, int k) {
     const int rb = r >> 4, rr = r & 15, kb = k >> 5, kk = k & 31;
     const int q = (kk & 15) >> 2, e = (kk & 3) | ((kk >> 4) << 2);
-    return ((rb * KB + kb) * 64 + frag_slot(rr, q, kb)) * 8 + e;
+    return ((rb * KB + kb) * 64 + frag_slot(rr, q, kb, rb)) * 8 + e;
 }
 template <int KB>
 __device__ __forceinline__ int fbase(int rb, int kb, int lane) {
-    return ((rb * KB + kb) * 64 + frag_slot(lane & 15, lane >> 4, kb)) * 8;
+    return ((rb * KB + kb) * 64 + frag_slot(lane & 15, lane >> 4, kb, rb)) * 8;
 }
 // 64x64 lower-block-triangular matrices (T, A_qk): only blocks (rb, kb <= rb/2) exist.
 __device__ __forceinline__ int tri_block(int rb, int kb) { return rb < 2 ? rb : 2 + 2 * (rb - 2) + kb; }
 __device__ __forceinline__ int tofs(int r, int k) {
     const int rb = r >> 4, rr = r & 15, kb = k >> 5, kk = k & 31;
     const int q = (kk & 15) >> 2, e = (kk & 3) | ((kk >> 4) << 2);
-    return (tri_block(rb, kb) * 64 + frag_slot(rr, q, kb)) * 8 + e;
+    return (tri_block(rb, kb) * 64 + frag_slot(rr, q, kb, rb)) * 8 + e;
 }
 __device__ __forceinline__ int tbase(int rb, int kb, int lane) {
-    return (tri_block(rb, kb) * 64 + frag_slot(lane & 15, lane >> 4, kb)) * 8;
+    return (tri_block(rb, kb) * 64 + frag_slot(lane & 15, lane >> 4, kb, rb)) * 8;
 }
 
 // ---- precision policies -------------------------------------------------------
