@@ -284,6 +284,22 @@ chunk32_kernel(const ChunkParams p) {
         // Thread pt = (rgp, cp): rows 4 rgp .. 4 rgp + 3 of the chunk, channels 2 cp, 2 cp + 1.
         const int pt = (int)threadIdx.x - 64 * NSW;
         const int pw = wave - NSW;
+        const int cp = pt % NCP, c0 = 2 * cp;
+        // the 4-row group is uniform across a wave when a wave covers one group (DK = 128)
+        const int rgp = NCP >= 64 ? __builtin_amdgcn_readfirstlane(pt / NCP) : pt / NCP;
+        const int sa = rgp >> 2, gi = rgp & 3;
+        const int lane = pt & 63, lr = lane & 15, lq = lane >> 4;
+        // per-thread LDS element offsets and input row offsets, fixed for the whole sequence
+        int ks_off[4], kn_off[4], kn2_off[4], vb_off[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * rgp + i, rl = r - 16 * sa;
+            ks_off[i] = fofs<KB>(r, c0);                 // KS and QS share the layout
+            kn_off[i] = fofs<KB>(32 * sa + rl, c0);
+            kn2_off[i] = fofs<KB>(16 + rl, c0);
+            vb_off[i] = r * L::VPITCH + c0 * (int)sizeof(IN_T);
+        }
+        const int kht_off0 = fofs<1>(c0, 4 * rgp), kht_off1 = fofs<1>(c0 + 1, 4 * rgp);
 
         // structurally zero blocks: columns 16..31 of TM rows 0..15, of AQK rows 0..15, of AW
         for (int idx = pt; idx < 256; idx += 64 * NPW) {
@@ -297,19 +313,21 @@ chunk32_kernel(const ChunkParams p) {
         float2 gn_[4];
         float bn_ = 0.f;
         auto prefetch = [&](int ch) {
-            const int t = opaque_v(pt);
-            const int cp = t % NCP, rgp = t / NCP, c0 = 2 * cp;
+            // chunk base in a scalar register, per-thread 32-bit row offsets
             const int t0 = seq_start + ch * C32, nv = min(C32, seq_len - ch * C32);
+            const size_t base = (size_t)t0 * H * DK;
+            const IN_T *kb = kg + base, *qb = qg + base, *vb = vg + base;
+            const float *gb = p.g + base;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = min(4 * rgp + i, nv - 1);
-                const size_t off = ((size_t)(t0 + r) * H + h) * DK + c0;
-                kn_[i] = PR::load(kg + off);
-                qn_[i] = PR::load(qg + off);
-                vn_[i] = PR::load(vg + off);   // DV == DK: the same element offsets
-                gn_[i] = *reinterpret_cast<const float2 *>(p.g + off);
+                const unsigned off = (unsigned)((r * H + h) * DK + c0);
+                kn_[i] = PR::load(kb + off);
+                qn_[i] = PR::load(qb + off);
+                vn_[i] = PR::load(vb + off);   // DV == DK: the same element offsets
+                gn_[i] = *reinterpret_cast<const float2 *>(gb + off);
             }
-            bn_ = p.beta[(size_t)(t0 + min(4 * rgp + (cp & 3), nv - 1)) * H + h];
+            bn_ = p.beta[(size_t)t0 * H + (unsigned)(min(4 * rgp + (cp & 3), nv - 1) * H + h)];
         };
         if (nchunks > 0) prefetch(0);
 
@@ -320,9 +338,6 @@ chunk32_kernel(const ChunkParams p) {
 
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
-            const int t = opaque_v(pt);
-            const int cp = t % NCP, rgp = t / NCP, c0 = 2 * cp, sa = rgp >> 2;
-            const int lane = t & 63, lr = lane & 15, lq = lane >> 4;
             const int nxt = it + 1;
             const bool have = nxt < nchunks;
             float *s_xchg = reinterpret_cast<float *>(sm + L::XCHG);
@@ -337,8 +352,8 @@ chunk32_kernel(const ChunkParams p) {
                     const bool valid = 4 * rgp + i < nv;   // padded rows: k = q = 0, alpha = 1, beta = 0
                     kr[i] = valid ? kn_[i] : PR::zero();
                     qr[i] = valid ? qn_[i] : PR::zero();
-                    *reinterpret_cast<typename PR::raw *>(sm + L::VB + (nxt & 1) * L::VB_BUF + (4 * rgp + i) * L::VPITCH +
-                                                          c0 * (int)sizeof(IN_T)) = valid ? vn_[i] : PR::zero();
+                    *reinterpret_cast<typename PR::raw *>(sm + L::VB + (nxt & 1) * L::VB_BUF + vb_off[i]) =
+                        valid ? vn_[i] : PR::zero();
                     al[i][0] = valid ? __expf(gn_[i].x) : 1.f;
                     al[i][1] = valid ? __expf(gn_[i].y) : 1.f;
                 }
@@ -406,24 +421,29 @@ chunk32_kernel(const ChunkParams p) {
 
             // ---- seg 2, P2(nxt): decayed operands
             if (have) {
-                float lead[2] = {1.f, 1.f}, tail[2] = {1.f, 1.f}, P0[2] = {1.f, 1.f}, P1[2] = {1.f, 1.f};
+                // group products of this sub-chunk (xs) and of the other one (xo)
+                float xs[4][2], xo[2] = {1.f, 1.f};
 #pragma unroll
-                for (int g = 0; g < 8; ++g) {
-                    const float2 x2 = *reinterpret_cast<const float2 *>(s_xchg + g * DK + c0);
-                    const float x[2] = {x2.x, x2.y};
-                    const bool same = (g >> 2) == sa;
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        if (g < 4) P0[c] *= x[c]; else P1[c] *= x[c];
-                        if (same && g < rgp) lead[c] *= x[c];
-                        if (same && g > rgp) tail[c] *= x[c];
-                    }
+                for (int m = 0; m < 4; ++m) {
+                    const float2 a2 = *reinterpret_cast<const float2 *>(s_xchg + (4 * sa + m) * DK + c0);
+                    const float2 o2 = *reinterpret_cast<const float2 *>(s_xchg + (4 * (1 - sa) + m) * DK + c0);
+                    xs[m][0] = a2.x; xs[m][1] = a2.y;
+                    xo[0] *= o2.x; xo[1] *= o2.y;
                 }
-                float post[2], dgf[2];
+                float lead[2], tail[2], P0[2], P1[2], post[2], dgf[2];
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    post[c] = sa ? 1.f : P1[c];            // decay from the end of this sub-chunk to the chunk end
-                    dgf[c] = 1.f / (sa ? P1[c] : P0[c]);   // column factor of the diagonal Gram tile
+                    lead[c] = gi > 0 ? xs[0][c] : 1.f;
+                    if (gi > 1) lead[c] *= xs[1][c];
+                    if (gi > 2) lead[c] *= xs[2][c];
+                    tail[c] = gi < 3 ? xs[3][c] : 1.f;
+                    if (gi < 2) tail[c] *= xs[2][c];
+                    if (gi < 1) tail[c] *= xs[1][c];
+                    const float psub = (xs[0][c] * xs[1][c]) * (xs[2][c] * xs[3][c]);
+                    P0[c] = sa ? xo[c] : psub;
+                    P1[c] = sa ? psub : xo[c];
+                    post[c] = sa ? 1.f : P1[c];                       // decay from the end of this sub-chunk to the chunk end
+                    dgf[c] = __builtin_amdgcn_rcpf(sa ? P1[c] : P0[c]);   // column factor of the diagonal Gram tile
                 }
                 gl[0] = P0[0] * P1[0];
                 gl[1] = P0[1] * P1[1];
@@ -443,11 +463,11 @@ chunk32_kernel(const ChunkParams p) {
                         kd[c] = ke[c] * dgf[c];
                         kh[c][i] = ke[c] * post[c];
                     }
-                    M::template put_hl<2>(sm + L::KS, L::SQ_PLANE, fofs<KB>(r, c0), ks);
-                    M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, fofs<KB>(r, c0), qs);
+                    M::template put_hl<2>(sm + L::KS, L::SQ_PLANE, ks_off[i], ks);
+                    M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, ks_off[i], qs);
                     // Kn rows: sub-chunk 0 feeds tiles (0,0) [x 1/P0] and (1,0) [x 1]; sub-chunk 1 feeds (1,1) [x 1/P1]
-                    M::template put_hl<2>(sm + L::KN, L::KN_PLANE, fofs<KB>(32 * sa + rl, c0), kd);
-                    if (sa == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, fofs<KB>(16 + rl, c0), ke);
+                    M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn_off[i], kd);
+                    if (sa == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn2_off[i], ke);
                 }
             }
             lds_barrier();
@@ -461,9 +481,8 @@ chunk32_kernel(const ChunkParams p) {
                 // (e^{G_last-G} K)^T and Gamma_last of chunk nxt: read by stage c of the next iteration,
                 // after stage c of this one has finished with chunk it's.  The 4 rows of this group
                 // are 4 consecutive K-slots of one fragment.
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    M::template put_hl<4>(sm + L::KHT, L::KHT_PLANE, fofs<1>(c0 + c, 4 * rgp), kh[c]);
+                M::template put_hl<4>(sm + L::KHT, L::KHT_PLANE, kht_off0, kh[0]);
+                M::template put_hl<4>(sm + L::KHT, L::KHT_PLANE, kht_off1, kh[1]);
                 if (rgp == 0) *reinterpret_cast<float2 *>(sm + L::GC + c0 * 4) = make_float2(gl[0], gl[1]);
             }
             if (have && pw < 3) {
