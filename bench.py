@@ -54,7 +54,19 @@ def main():
     ap.add_argument("--chunk", type=int, default=32, choices=(32, 64), help="token block of the chunked form")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scales the HBM byte counters)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="only write the kernel-trace summaries under profiles/ from a rocprofv3 csv run of "
+                         "bench.py and the JSON line that run printed")
+    ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "MFMA"),
+                    help="only write the counter summary of the prefill kernel under profiles/ from five "
+                         "rocprofv3 --pmc output folders (csv)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.chunk, *args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
                                    "(the operator shards by head / sequence with no communication, "
@@ -226,6 +238,138 @@ def measured_counters(chunk):
         return None
     d["file"] = "profiles/" + COUNTER_FILE[chunk]
     return d
+
+
+def _counter_rows(folder, name_part):
+    """Per-dispatch sums (over the whole chip) of each counter for kernels whose name contains name_part."""
+    import csv
+    import glob
+    path = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not path:
+        raise FileNotFoundError(f"no counter_collection.csv under {folder}")
+    per = {}
+    with open(path[0]) as f:
+        for r in csv.DictReader(f):
+            if name_part in r["Kernel_Name"]:
+                d = per.setdefault(int(r["Dispatch_Id"]), {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise ValueError(f"no dispatch of a kernel matching {name_part!r} in {path[0]}")
+    return list(per.values())
+
+
+def _mean(rows, key):
+    return sum(r[key] for r in rows) / len(rows)
+
+
+def summarize_counters(chunk, fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma_dir):
+    """Write profiles/<kernel>_counters.json and .md: HBM bytes per launch of the prefill kernel from
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for a plain
+    copy of known size, and MFMA busy / bf16 MOPS from a third pass."""
+    kname = {32: "chunk32_kernel<128, false", 64: "chunk_fwd_kernel<128, false"}[chunk]
+    copy_name = "elementwise_kernel"
+    fetch = _mean(_counter_rows(fetch_dir, kname), "FETCH_SIZE")
+    write = _mean(_counter_rows(write_dir, kname), "WRITE_SIZE")
+    # the copy reads and writes `copy_bytes` each call (bench.py --copy-calibration 2048)
+    copy_bytes = 2048 * (1 << 20)
+    cf = _mean(_counter_rows(cfetch_dir, copy_name)[-3:], "FETCH_SIZE")
+    cw = _mean(_counter_rows(cwrite_dir, copy_name)[-3:], "WRITE_SIZE")
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    m = _counter_rows(mfma_dir, kname)
+    busy, gui = _mean(m, "SQ_VALU_MFMA_BUSY_CYCLES"), _mean(m, "GRBM_GUI_ACTIVE")
+    mops = _mean(m, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    xcd, simds = 8, 1024          # GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs
+    d = {
+        "kernel": KERNEL_NAME[chunk],
+        "workload": "prefill T=65536 H=96 d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state, initial state "
+                    f"(bench.py prefill launch, chunk {chunk})",
+        "source_digest": kernel_digest(chunk),
+        "fetch_kib_per_launch": round(fetch, 1),
+        "write_kib_per_launch": round(write, 1),
+        "copy_calibration": {"bytes_read_and_written": copy_bytes, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
+                             "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
+        "hbm_read_bytes_per_launch": round(fetch * 1024 * fs),
+        "hbm_write_bytes_per_launch": round(write * 1024 * ws),
+        "hbm_bytes_per_launch": round(fetch * 1024 * fs + write * 1024 * ws),
+        "mfma_bf16_flop_per_launch": round(mops * 512),
+        "mfma_busy_cycles": busy,
+        "gui_active_cycles_per_xcd": gui / xcd,
+        "mfma_util_pct": round(100.0 * busy / (gui / xcd * simds), 2),
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 bench.py --steps 2 "
+            f"--warmup 0 --no-cpu-baseline --prefill-only --chunk {chunk}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 bench.py --steps 2 "
+            f"--warmup 0 --no-cpu-baseline --prefill-only --chunk {chunk}",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cfetch_dir} -o run -- python3 bench.py "
+            "--copy-calibration 2048",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cwrite_dir} -o run -- python3 bench.py "
+            "--copy-calibration 2048",
+            "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES "
+            f"SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d {mfma_dir} -o run -- python3 bench.py --steps 2 "
+            f"--warmup 0 --no-cpu-baseline --prefill-only --chunk {chunk}",
+            f"python3 bench.py --chunk {chunk} --summarize-counters {fetch_dir} {write_dir} {cfetch_dir} "
+            f"{cwrite_dir} {mfma_dir}",
+        ],
+    }
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    base = os.path.join(ROOT, "profiles", COUNTER_FILE[chunk])
+    with open(base, "w") as f:
+        json.dump(d, f, indent=1)
+    alg = prefill_bytes(65536, 96, 128, 128)
+    with open(base[:-5] + ".md", "w") as f:
+        f.write(f"# {d['kernel']}: HBM traffic and MFMA counters\n\n")
+        f.write(f"Workload: {d['workload']}.  Kernel source digest {d['source_digest']}.\n\n")
+        f.write("| quantity | value |\n|---|---|\n")
+        f.write(f"| FETCH_SIZE per launch | {d['fetch_kib_per_launch']} KiB |\n")
+        f.write(f"| WRITE_SIZE per launch | {d['write_kib_per_launch']} KiB |\n")
+        f.write(f"| copy calibration: FETCH_SIZE / WRITE_SIZE for {copy_bytes} B read + written | "
+                f"{d['copy_calibration']['fetch_kib']} / {d['copy_calibration']['write_kib']} KiB |\n")
+        f.write(f"| scale factors (bytes per counted byte) | fetch {fs:.4f}, write {ws:.4f} |\n")
+        f.write(f"| HBM bytes read / written per launch | {d['hbm_read_bytes_per_launch']} / "
+                f"{d['hbm_write_bytes_per_launch']} |\n")
+        f.write(f"| algorithmic bytes per launch | {alg} |\n")
+        f.write(f"| measured / algorithmic | {d['hbm_bytes_per_launch'] / alg:.3f} |\n")
+        f.write(f"| MFMA bf16 flop per launch (MOPS x 512) | {d['mfma_bf16_flop_per_launch']:.4g} |\n")
+        f.write(f"| MFMA busy (all 1024 SIMDs) | {d['mfma_util_pct']} % |\n\n")
+        f.write("Commands (each counter group in its own run):\n\n")
+        for c in d["commands"]:
+            f.write(f"    {c}\n")
+    print(json.dumps(d, indent=1))
+
+
+def summarize_trace(trace_dir, bench_json):
+    """Write profiles/*_kernel_trace.md (one per hot kernel) from a rocprofv3 --kernel-trace --stats
+    csv run of bench.py, next to the per-launch durations bench.py measured with HIP events."""
+    import csv
+    import glob
+    path = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    with open(path) as f:
+        rows = list(csv.DictReader(f))
+    with open(bench_json) as f:
+        b = json.loads(f.read().strip().splitlines()[-1])
+    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o run -- python3 bench.py "
+           f"--steps {b['steps']} --warmup {b['warmup']} --no-cpu-baseline --chunk {b['config']['chunk']}")
+    table = "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |\n|---|---|---|---|---|---|\n"
+    for r in rows:
+        table += (f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                  f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} % |\n")
+    out = {
+        "chunk32_prefill_T65536_H96_d128_kernel_trace.md": (
+            "prefill T=65536 H=96 d_k=d_v=128 (bf16 q/k/v, fp32 g/beta/state, initial state)", "chunk32_kernel",
+            b["prefill"]["ms"]),
+        "decode_N256_H96_d128_kernel_trace.md": (
+            "decode step N=256 H=96 d_k=d_v=128 (bf16 q/k/v, fp32 g/beta, fp32 state in place)", "decode_kernel",
+            b.get("decode", {}).get("ms")),
+    }
+    for fname, (wl, kname, ev_ms) in out.items():
+        avg = [float(r["AverageNs"]) for r in rows if kname in r["Name"]]
+        with open(os.path.join(ROOT, "profiles", fname), "w") as f:
+            f.write(f"# {kname}: rocprofv3 kernel trace\n\nWorkload: {wl}.\n\n")
+            if avg:
+                f.write(f"rocprofv3 average duration of {kname}: {avg[0] / 1e6:.4f} ms; bench.py HIP-event "
+                        f"average over the timed steps (same process): {ev_ms} ms.\n\n")
+            f.write(f"Command:\n\n    {cmd}\n\nAll kernels of the run:\n\n{table}")
+    print("wrote", ", ".join(out))
 
 
 def copy_calibration(mib):

@@ -262,7 +262,7 @@ chunk32_kernel(const ChunkParams p) {
                         mma<false, false>(Yacc[1][jt], fk1, sp);
                         mma<true, true>(Oacc[1][jt], fq1, sp);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
+
                 }
             }
             lds_barrier();
