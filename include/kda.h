@@ -38,7 +38,7 @@
  *     pure host code and runs before any launch; a failed launch returns
  *     KDA_ERR_DEVICE.  Faults during execution surface at the caller's next
  *     synchronisation.
- *   - Supported in ABI v1: d_k == d_v in {64, 128}; chunk_size == 64;
+ *   - Supported in ABI v1: d_k == d_v in {64, 128}; chunk_size 32 or 64;
  *     in_dtype KDA_F32 or KDA_BF16.  Other values -> KDA_ERR_UNSUPPORTED.
  */
 #ifndef KDA_H_
@@ -74,7 +74,11 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * Fields:
  *   struct_size      sizeof(kda_fwd_args) as compiled by the caller.
  *   num_seqs         N >= 0.  total_tokens: T >= 0, must equal cu_seqlens[N].
- *   num_heads        H >= 1.   dk, dv: head dims.  chunk_size: 64.
+ *   num_heads        H >= 1.   dk, dv: head dims.
+ *   chunk_size       32 or 64: the token block of the chunked form.  32 runs the
+ *                    software-pipelined kernel (the fast path); 64 runs a simpler
+ *                    one-phase-at-a-time kernel.  Both compute the same operator
+ *                    (results differ by rounding only).
  *   in_dtype         element type of q, k, v (bf16 = raw 16-bit bf16 words).
  *   scale            multiplies every output (o = scale * S^T q).
  *   q, k, v, g, beta see layouts above; 16-byte aligned.
