@@ -23,21 +23,19 @@
 // current one.  The two roles run separate loops with the same three
 // LDS-only barriers per iteration (global loads stay in flight across them):
 //
-//            scan waves                                prep waves
-//   seg 1    -                                         P1(i+1): exp(g), 4-row running products;
+//            scan waves (chunk i)                      prep waves (chunk i+1)
+//   seg 1    a(i): (Gamma*K) S, (Gamma*Q) S            P1: exp(g), 4-row running products, group totals;
 //                                                      inverses of chunk i's diagonal blocks -> T00, [-M11 T11]
-//   seg 2    b(i), o(i), c(i): Y = V - Y, U, O,        P2(i+1): decayed operands -> LDS
-//            S <- Gamma_last S + Khat^T U
-//   seg 3    a(i+1): (Gamma*K) S, (Gamma*Q) S          P3(i+1): Khat^T, Gram tiles, A10, A_qk
+//   seg 2    b(i): Y = V - (Gamma*K)S, U; o(i): O      P2: decayed operands KS, QS, Gamma*Q, Kn -> LDS
+//   seg 3    c(i): S <- Gamma_last S + Khat^T U        P3: Khat^T, Gamma_last, value rows -> LDS; Gram tiles
 //
-// Every LDS operand is written in a segment after its last read by the previous
-// chunk, so one copy suffices; (e^{G_last-G} K)^T and Gamma_last, which stage c
-// reads in segment 2, are therefore written in segment 3.  Only the raw value
-// rows (written in segment 1, read by stage b in segment 1 of the next
-// iteration) are double-buffered.  Prep waves load the raw rows of chunk i+2
-// straight into registers while preparing chunk i+1; every load is
-// unconditional (rows past the end of the sequence re-read its last row and are
-// masked where used).
+// so the scan's dependent chain a -> b -> c occupies every segment.  Every LDS
+// operand is written in a segment after its last read by the previous chunk;
+// (e^{G_last-G} K)^T and Gamma_last, written in segment 3 while stage c reads
+// the previous chunk's, are double-buffered.  Prep waves load the raw rows of
+// chunk i+2 straight into registers while preparing chunk i+1; every load is
+// unconditional (rows past the end of the sequence re-read its last row and
+// are masked where used).
 //
 // Precision: hi+lo bf16 operand pairs on every product feeding the outputs
 // except (Gamma*K) S, fp32 accumulation, fp32 o and S.  The fp32-input
@@ -55,25 +53,29 @@ struct Lds32 {
     static constexpr int KS = 0;                          // [32][DK] hl: K * e^{G - G_ref}
     static constexpr int QS = KS + 32 * DK * 4;           // [32][DK] hl: Q * e^{G - G_ref}
     static constexpr int SQ_PLANE = 32 * DK * ES;
-    static constexpr int KHT = QS + 32 * DK * 4;          // [DK][32] hl: (e^{G_last-G} K)^T
+    static constexpr int QT = QS + 32 * DK * 4;           // [32][DK] hl: Gamma * Q (decay from the chunk start)
+    static constexpr int KHT = QT + 32 * DK * 4;          // 2 x [DK][32] hl: (e^{G_last-G} K)^T
     static constexpr int KHT_PLANE = DK * 32 * ES;
-    static constexpr int TM = KHT + DK * 32 * 4;          // [32][32] hl: [T00 0 ; -M11 T11]
+    static constexpr int KHT_BUF = DK * 32 * 4;
+    static constexpr int TM = KHT + 2 * KHT_BUF;          // [32][32] hl: [T00 0 ; -M11 T11]
     static constexpr int TRI_PLANE = 32 * 32 * ES;
     static constexpr int AQK = TM + 32 * 32 * 4;          // [32][32] hl: A_qk, lower incl. diagonal
     static constexpr int AW = AQK + 32 * 32 * 4;          // [16][32] hl: [A10 0]
     static constexpr int AW_PLANE = 16 * 32 * ES;
-    static constexpr int GC = AW + 16 * 32 * 4;           // [DK] fp32: Gamma_last
-    static constexpr int P0 = GC + DK * 4;                // [DK] fp32: e^{G} at the end of sub-chunk 0
+    static constexpr int GC = AW + 16 * 32 * 4;           // 2 x [DK] fp32: Gamma_last
+    static constexpr int P0 = GC + 2 * DK * 4;            // [DK] fp32: e^{G} at the end of sub-chunk 0
     static constexpr int VPITCH = DK * (int)sizeof(IN_T) + 16;   // padded row pitch (bytes) of the value rows
-    static constexpr int VB = P0 + DK * 4;                // 2 x [32][VPITCH]: raw value rows of a chunk
-    static constexpr int VB_BUF = 32 * VPITCH;
+    static constexpr int VB = P0 + DK * 4;                // [32][VPITCH]: raw value rows of a chunk
     // prep-wave scratch
-    static constexpr int KN = VB + 2 * VB_BUF;            // [48][DK] hl: K e^{G_ref - G} for tiles (0,0), (1,0), (1,1)
+    static constexpr int KN = VB + 32 * VPITCH;           // [48][DK] hl: K e^{G_ref - G} for tiles (0,0), (1,0), (1,1)
     static constexpr int KN_PLANE = 48 * DK * ES;
     static constexpr int ZT = KN + 48 * DK * 4;           // 2 fp32 tiles: L^T of the diagonal A_kk blocks
     static constexpr int XCHG = ZT + 2 * TSZ * 4;         // [8][DK] fp32: decay over each 4-row group
     static constexpr int BETA = XCHG + 8 * DK * 4;        // 2 x [32] fp32
-    static constexpr int TOTAL = BETA + 2 * 32 * 4;
+    // scan-wave stash: each scan lane parks its 16 (Gamma*Q) S partial outputs here between
+    // segments 1 and 2 (register pressure), element j of lane l at OST + (j * 64 NSW + l) * 16 bytes
+    static constexpr int OST = BETA + 2 * 32 * 4;
+    static constexpr int TOTAL = OST + 4 * 64 * (DK / 32) * 16;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -144,23 +146,58 @@ chunk32_kernel(const ChunkParams p) {
                     Sr[1][ct][e] = v.y;
                 }
         }
-        f32x4_t Yacc[2][2], Oacc[2][2];
-        F UF[2];
         const int every_chunks = p.every / C32;   // checkpoint_every is a multiple of the chunk size
         int ck_left = every_chunks, ck_idx = 0;
 
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
             const int lane = opaque_v((int)threadIdx.x) & 63, lr = lane & 15, lq = lane >> 4;
+            const int t0 = seq_start + it * C32, nv = min(C32, seq_len - it * C32);
+            f32x4_t Yacc[2][2], Oacc[2][2];
+            F UF[2];
 
-            // ---- seg 1: nothing for the scan (the prep waves invert this chunk's diagonal blocks)
+            // ---- seg 1, a(it): Yacc = (Gamma*K) S and Oacc = (Gamma*Q) S, S = the state entering chunk it.
+            // (Gamma*K) S is KS S on rows 0..15 and KS (Diag(P0) S) on rows 16..31 (single bf16);
+            // (Gamma*Q) is stored as such (QT).  The prep waves invert this chunk's diagonal blocks.
+            if (it >= 0) {
+                const float *s_p0 = reinterpret_cast<const float *>(sm + L::P0);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int jt = 0; jt < 2; ++jt) {
+                        Yacc[rt][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        Oacc[rt][jt] = Yacc[rt][jt];
+                    }
+#pragma unroll
+                for (int s = 0; s < KB; ++s) {
+                    // channels of this K-step held by the lane: 32 s + 4 lq + e and 32 s + 16 + 4 lq + e
+                    const float4 pa = *reinterpret_cast<const float4 *>(s_p0 + 32 * s + 4 * lq);
+                    const float4 pb = *reinterpret_cast<const float4 *>(s_p0 + 32 * s + 16 + 4 * lq);
+                    const float sc[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+                    const F fk0 = M::template get<false>(sm + L::KS, 0, fbase<KB>(0, s, lane));
+                    const F fk1 = M::template get<false>(sm + L::KS, 0, fbase<KB>(1, s, lane));
+                    const F fq0 = M::template get<true>(sm + L::QT, L::SQ_PLANE, fbase<KB>(0, s, lane));
+                    const F fq1 = M::template get<true>(sm + L::QT, L::SQ_PLANE, fbase<KB>(1, s, lane));
+#pragma unroll
+                    for (int jt = 0; jt < 2; ++jt) {
+                        const F sf = M::template from_tiles<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
+                        mma<false, false>(Yacc[0][jt], fk0, sf);
+                        mma<true, true>(Oacc[0][jt], fq0, sf);
+                        mma<true, true>(Oacc[1][jt], fq1, sf);
+                        const F sp = M::template from_tiles_scaled<false>(Sr[jt][2 * s], Sr[jt][2 * s + 1], sc);
+                        mma<false, false>(Yacc[1][jt], fk1, sp);
+                    }
+                }
+                // park the output partials in LDS until stage o (this lane's private slots)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<f32x4_t *>(sm + L::OST + (j * 64 * NSW + 64 * wave + lane) * 16) = Oacc[j >> 1][j & 1];
+            }
             lds_barrier();
 
-            // ---- seg 2, b(it): Y = V - (Gamma*K) S, U ; o(it) = scale [ (Gamma*Q) S + A_qk U ] ;
-            //             c(it): S <- Diag(Gamma_last) S + (e^{G_last-G} K)^T U
+            // ---- seg 2, b(it): Y = V - (Gamma*K) S, U ;  o(it) = scale [ (Gamma*Q) S + A_qk U ]
             if (it >= 0) {
-                const int t0 = seq_start + it * C32, nv = min(C32, seq_len - it * C32);
-                const char *vb = sm + L::VB + (it & 1) * L::VB_BUF + (32 * wave + 2 * lr) * (int)sizeof(IN_T);
+                const char *vb = sm + L::VB + (32 * wave + 2 * lr) * (int)sizeof(IN_T);
                 f32x4_t Y[2][2];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
@@ -192,7 +229,10 @@ chunk32_kernel(const ChunkParams p) {
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
                     const F fa = M::template get<true>(sm + L::AQK, L::TRI_PLANE, fbase<1>(rt, 0, lane));
-                    f32x4_t acc[2] = {Oacc[rt][0], Oacc[rt][1]};
+                    f32x4_t acc[2];
+#pragma unroll
+                    for (int jt = 0; jt < 2; ++jt)
+                        acc[jt] = *reinterpret_cast<const f32x4_t *>(sm + L::OST + ((2 * rt + jt) * 64 * NSW + 64 * wave + lane) * 16);
 #pragma unroll
                     for (int jt = 0; jt < 2; ++jt) mma<true, true>(acc[jt], fa, UF[jt]);
 #pragma unroll
@@ -203,10 +243,17 @@ chunk32_kernel(const ChunkParams p) {
                                 make_float2(p.scale * acc[0][e], p.scale * acc[1][e]);
                     }
                 }
-                const float *s_gc = reinterpret_cast<const float *>(sm + L::GC);
+            }
+            lds_barrier();
+
+            // ---- seg 3, c(it): S <- Diag(Gamma_last) S + (e^{G_last-G} K)^T U
+            if (it >= 0) {
+                const int buf = it & 1;
+                const float *s_gc = reinterpret_cast<const float *>(sm + L::GC) + buf * DK;
 #pragma unroll
                 for (int ct = 0; ct < KT; ++ct) {
-                    const F fk = M::template get<true>(sm + L::KHT, L::KHT_PLANE, fbase<1>(ct, 0, lane));
+                    const F fk = M::template get<true>(sm + L::KHT + buf * L::KHT_BUF, L::KHT_PLANE,
+                                                       fbase<1>(ct, 0, lane));
                     const float4 gc = *reinterpret_cast<const float4 *>(s_gc + 16 * ct + 4 * lq);
                     const float gcv[4] = {gc.x, gc.y, gc.z, gc.w};
 #pragma unroll
@@ -229,40 +276,6 @@ chunk32_kernel(const ChunkParams p) {
                         for (int e = 0; e < 4; ++e)
                             *reinterpret_cast<float2 *>(dst + (size_t)(16 * ct + 4 * lq + e) * DV + 32 * wave + 2 * lr) =
                                 make_float2(Sr[0][ct][e], Sr[1][ct][e]);
-                }
-            }
-            lds_barrier();
-
-            // ---- seg 3, a(it+1): Yacc = (Gamma*K) S, Oacc = (Gamma*Q) S for the next chunk
-            if (it + 1 < nchunks) {
-                const float *s_p0 = reinterpret_cast<const float *>(sm + L::P0);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) {
-                        Yacc[rt][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                        Oacc[rt][jt] = Yacc[rt][jt];
-                    }
-#pragma unroll
-                for (int s = 0; s < KB; ++s) {
-                    // channels of this K-step held by the lane: 32 s + 4 lq + e and 32 s + 16 + 4 lq + e
-                    const float4 pa = *reinterpret_cast<const float4 *>(s_p0 + 32 * s + 4 * lq);
-                    const float4 pb = *reinterpret_cast<const float4 *>(s_p0 + 32 * s + 16 + 4 * lq);
-                    const float sc[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-                    const F fk0 = M::template get<false>(sm + L::KS, 0, fbase<KB>(0, s, lane));
-                    const F fq0 = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(0, s, lane));
-                    const F fk1 = M::template get<false>(sm + L::KS, 0, fbase<KB>(1, s, lane));
-                    const F fq1 = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(1, s, lane));
-#pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) {
-                        const F sf = M::template from_tiles<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
-                        mma<false, false>(Yacc[0][jt], fk0, sf);
-                        mma<true, true>(Oacc[0][jt], fq0, sf);
-                        const F sp = M::template from_tiles_scaled<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1], sc);
-                        mma<false, false>(Yacc[1][jt], fk1, sp);
-                        mma<true, true>(Oacc[1][jt], fq1, sp);
-                    }
-
                 }
             }
             lds_barrier();
@@ -316,7 +329,7 @@ chunk32_kernel(const ChunkParams p) {
             // chunk base in a scalar register, per-thread 32-bit row offsets
             const int t0 = seq_start + ch * C32, nv = min(C32, seq_len - ch * C32);
             const size_t base = (size_t)t0 * H * DK;
-            const IN_T *kb = kg + base, *qb = qg + base, *vb = vg + base;
+            const IN_T *kb = kg + base, *qb = qg + base;
             const float *gb = p.g + base;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -324,12 +337,23 @@ chunk32_kernel(const ChunkParams p) {
                 const unsigned off = (unsigned)((r * H + h) * DK + c0);
                 kn_[i] = PR::load(kb + off);
                 qn_[i] = PR::load(qb + off);
-                vn_[i] = PR::load(vb + off);   // DV == DK: the same element offsets
                 gn_[i] = *reinterpret_cast<const float2 *>(gb + off);
             }
             bn_ = p.beta[(size_t)t0 * H + (unsigned)(min(4 * rgp + (cp & 3), nv - 1) * H + h)];
         };
-        if (nchunks > 0) prefetch(0);
+        auto vfetch = [&](int ch) {   // value rows: staged to LDS in segment 3, so fetched separately
+            const int t0 = seq_start + ch * C32, nv = min(C32, seq_len - ch * C32);
+            const IN_T *vb = vg + (size_t)t0 * H * DV;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = min(4 * rgp + i, nv - 1);
+                vn_[i] = PR::load(vb + (unsigned)((r * H + h) * DV + c0));
+            }
+        };
+        if (nchunks > 0) {
+            prefetch(0);
+            vfetch(0);
+        }
 
         typename PR::raw kr[4], qr[4];   // this chunk's k, q pairs from P1 to P2
         float Fw[4][2], Bw[4][2];        // decay products within the 4-row group: through row i / after row i
@@ -352,8 +376,6 @@ chunk32_kernel(const ChunkParams p) {
                     const bool valid = 4 * rgp + i < nv;   // padded rows: k = q = 0, alpha = 1, beta = 0
                     kr[i] = valid ? kn_[i] : PR::zero();
                     qr[i] = valid ? qn_[i] : PR::zero();
-                    *reinterpret_cast<typename PR::raw *>(sm + L::VB + (nxt & 1) * L::VB_BUF + vb_off[i]) =
-                        valid ? vn_[i] : PR::zero();
                     al[i][0] = valid ? __expf(gn_[i].x) : 1.f;
                     al[i][1] = valid ? __expf(gn_[i].y) : 1.f;
                 }
@@ -379,8 +401,8 @@ chunk32_kernel(const ChunkParams p) {
                 // Diagonal block a = pw of chunk it: M = (I + N)^{-1} for the strictly lower N this
                 // wave's Gram tile left in lw (row lr, columns 4 lq + e) one segment ago, as
                 //     M = (I + X)(I + X^2)(I + X^4)(I + X^8),  X = -N,  N^16 = 0,
-                // with fp32 16x16x4 MFMA products (five dependent levels instead of a 16-step
-                // substitution).  T_aa = M Diag(beta_a) (and -M11) -> TM, read by stage b in segment 2.
+                // with 16x16 MFMA products held in registers (five dependent levels instead of a
+                // 16-step substitution; hi/lo bf16 operands, or fp32 MFMA for fp32 inputs).  T_aa = M Diag(beta_a) (and -M11) -> TM, read by stage b in segment 2.
                 const int a = pw;
                 float *zt = reinterpret_cast<float *>(sm + L::ZT) + a * TSZ;
                 const float *beta_it = reinterpret_cast<const float *>(sm + L::BETA) + (it & 1) * 32;
@@ -393,8 +415,24 @@ chunk32_kernel(const ChunkParams p) {
                 // (Z W) in B form = mm(Z_A, W_B); in A form = mm(W_B, Z_A)
                 auto mm = [](const f32x4_t &za, const f32x4_t &wb) {
                     f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (F32P) {
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) d = mfma_f32(za[kk], wb[kk], d);
+                        for (int kk = 0; kk < 4; ++kk) d = mfma_f32(za[kk], wb[kk], d);
+                    } else {
+                        // hi/lo bf16 split in two 16x16x32 MFMAs: K-slots 0..15 carry the hi parts and
+                        // 16..31 the lo parts of Z, so [Zh Zl][Wh; Wh] + [Zh Zh][Wl; 0] = Zh Wh + Zl Wh + Zh Wl
+                        uint32_t zh[2], zl[2], wh[2], wl[2];
+                        split_hl2(za[0], za[1], zh[0], zl[0]);
+                        split_hl2(za[2], za[3], zh[1], zl[1]);
+                        split_hl2(wb[0], wb[1], wh[0], wl[0]);
+                        split_hl2(wb[2], wb[3], wh[1], wl[1]);
+                        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, (uint4){zh[0], zh[1], zl[0], zl[1]});
+                        const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, (uint4){wh[0], wh[1], wh[0], wh[1]});
+                        const bf16x8_t a2 = __builtin_bit_cast(bf16x8_t, (uint4){zh[0], zh[1], zh[0], zh[1]});
+                        const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, (uint4){wl[0], wl[1], 0u, 0u});
+                        d = mfma_bf16(a1, b1, d);
+                        d = mfma_bf16(a2, b2, d);
+                    }
                     return d;
                 };
                 const f32x4_t X2B = mm(XA, XB), X2A = mm(XB, XA);
@@ -430,7 +468,7 @@ chunk32_kernel(const ChunkParams p) {
                     xs[m][0] = a2.x; xs[m][1] = a2.y;
                     xo[0] *= o2.x; xo[1] *= o2.y;
                 }
-                float lead[2], tail[2], P0[2], P1[2], post[2], dgf[2];
+                float lead[2], tail[2], P0[2], P1[2], post[2], dgf[2], pre[2];
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
                     lead[c] = gi > 0 ? xs[0][c] : 1.f;
@@ -443,6 +481,7 @@ chunk32_kernel(const ChunkParams p) {
                     P0[c] = sa ? xo[c] : psub;
                     P1[c] = sa ? psub : xo[c];
                     post[c] = sa ? 1.f : P1[c];                       // decay from the end of this sub-chunk to the chunk end
+                    pre[c] = sa ? P0[c] : 1.f;                        // decay from the chunk start to this sub-chunk
                     dgf[c] = __builtin_amdgcn_rcpf(sa ? P1[c] : P0[c]);   // column factor of the diagonal Gram tile
                 }
                 gl[0] = P0[0] * P1[0];
@@ -451,7 +490,7 @@ chunk32_kernel(const ChunkParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 4 * rgp + i, rl = r - 16 * sa;
-                    float ks[2], qs[2], ke[2], kd[2];
+                    float ks[2], qs[2], qt[2], ke[2], kd[2];
                     const float kv[2] = {PR::lo(kr[i]), PR::hi(kr[i])}, qv[2] = {PR::lo(qr[i]), PR::hi(qr[i])};
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
@@ -459,12 +498,14 @@ chunk32_kernel(const ChunkParams p) {
                         const float ee = Bw[i][c] * tail[c];   // e^{G_end(sub-chunk) - G_r}
                         ks[c] = kv[c] * es;
                         qs[c] = qv[c] * es;
+                        qt[c] = qs[c] * pre[c];                // Gamma * q (decay from the chunk start)
                         ke[c] = kv[c] * ee;
                         kd[c] = ke[c] * dgf[c];
                         kh[c][i] = ke[c] * post[c];
                     }
                     M::template put_hl<2>(sm + L::KS, L::SQ_PLANE, ks_off[i], ks);
                     M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, ks_off[i], qs);
+                    M::template put_hl<2>(sm + L::QT, L::SQ_PLANE, ks_off[i], qt);
                     // Kn rows: sub-chunk 0 feeds tiles (0,0) [x 1/P0] and (1,0) [x 1]; sub-chunk 1 feeds (1,1) [x 1/P1]
                     M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn_off[i], kd);
                     if (sa == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn2_off[i], ke);
@@ -478,12 +519,22 @@ chunk32_kernel(const ChunkParams p) {
             //   pw 1: tile (1,1)  A_kk -> M11 -> T11, -M11 and A_qk(1,1)
             //   pw 2: tile (1,0)  A10                     and A_qk(1,0)
             if (have) {
-                // (e^{G_last-G} K)^T and Gamma_last of chunk nxt: read by stage c of the next iteration,
-                // after stage c of this one has finished with chunk it's.  The 4 rows of this group
-                // are 4 consecutive K-slots of one fragment.
-                M::template put_hl<4>(sm + L::KHT, L::KHT_PLANE, kht_off0, kh[0]);
-                M::template put_hl<4>(sm + L::KHT, L::KHT_PLANE, kht_off1, kh[1]);
-                if (rgp == 0) *reinterpret_cast<float2 *>(sm + L::GC + c0 * 4) = make_float2(gl[0], gl[1]);
+                // (e^{G_last-G} K)^T and Gamma_last of chunk nxt, read by stage c in segment 3 of the
+                // next iteration (double-buffered: stage c of chunk it reads the other buffer now).
+                // The 4 rows of this group are 4 consecutive K-slots of one fragment.
+                const int buf = nxt & 1;
+                M::template put_hl<4>(sm + L::KHT + buf * L::KHT_BUF, L::KHT_PLANE, kht_off0, kh[0]);
+                M::template put_hl<4>(sm + L::KHT + buf * L::KHT_BUF, L::KHT_PLANE, kht_off1, kh[1]);
+                if (rgp == 0)
+                    *reinterpret_cast<float2 *>(sm + L::GC + (buf * DK + c0) * 4) = make_float2(gl[0], gl[1]);
+                // value rows of chunk nxt, read by stage b in segment 2 of the next iteration (stage b
+                // of chunk it has finished with the buffer); then fetch chunk nxt + 1's
+                const int nv = min(C32, seq_len - nxt * C32);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<typename PR::raw *>(sm + L::VB + vb_off[i]) =
+                        4 * rgp + i < nv ? vn_[i] : PR::zero();
+                vfetch(min(nxt + 1, nchunks - 1));
             }
             if (have && pw < 3) {
                 const int knb = pw == 0 ? 0 : (pw == 1 ? 2 : 1);
