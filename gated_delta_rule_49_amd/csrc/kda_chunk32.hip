@@ -46,7 +46,7 @@ namespace kda {
 
 constexpr int C32 = 32;
 
-template <int DK, bool F32P, typename IN_T>
+template <int DK, int NSW, bool F32P, typename IN_T>
 struct Lds32 {
     static constexpr int ES = Mat<F32P>::ES;
     // operands of a chunk, written by the prep waves, read by the scan waves
@@ -75,7 +75,7 @@ struct Lds32 {
     // scan-wave stash: each scan lane parks its 16 (Gamma*Q) S partial outputs here between
     // segments 1 and 2 (register pressure), element j of lane l at OST + (j * 64 NSW + l) * 16 bytes
     static constexpr int OST = BETA + 2 * 32 * 4;
-    static constexpr int TOTAL = OST + 4 * 64 * (DK / 32) * 16;
+    static constexpr int TOTAL = OST + 4 * 64 * NSW * 16;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -96,18 +96,20 @@ template <> struct Pair<float> {
     __device__ static float hi(raw w) { return w.y; }
 };
 
-template <int DK> constexpr int chunk32_threads() { return 64 * (DK / 32) + 4 * DK; }
+// SPLIT workgroups share one (sequence, head), each owning DV / SPLIT value columns (the
+// state's columns evolve independently) and each preparing the chunk operands itself.
+template <int DK, int SPLIT> constexpr int chunk32_threads() { return 64 * (DK / 32 / SPLIT) + 4 * DK; }
 
-template <int DK, bool F32P, typename IN_T>
-__global__ void __launch_bounds__(chunk32_threads<DK>())
+template <int DK, int SPLIT, bool F32P, typename IN_T>
+__global__ void __launch_bounds__((chunk32_threads<DK, SPLIT>()))
 chunk32_kernel(const ChunkParams p) {
     constexpr int DV = DK;
-    constexpr int NSW = DV / 32;        // scan waves, 32 value columns each
+    constexpr int NSW = DV / 32 / SPLIT;   // scan waves, 32 value columns each
     constexpr int NPW = DK / 16;        // prep waves: 8 four-row groups x DK/2 channel pairs
     constexpr int KB = DK / 32;         // 32-wide K-steps over d_k
     constexpr int KT = DK / 16;         // 16-row tiles over d_k
     constexpr int NCP = DK / 2;         // channel pairs
-    using L = Lds32<DK, F32P, IN_T>;
+    using L = Lds32<DK, NSW, F32P, IN_T>;
     using M = Mat<F32P>;
     using F = Frag<F32P>;
     using PR = Pair<IN_T>;
@@ -115,8 +117,10 @@ chunk32_kernel(const ChunkParams p) {
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
 
     const int H = p.H;
-    const int h = blockIdx.x % H;
-    const int n = p.order[blockIdx.x / H];
+    const int part = (int)blockIdx.x % SPLIT, hn = (int)blockIdx.x / SPLIT;
+    const int h = hn % H;
+    const int n = p.order[hn / H];
+    const int col0 = 32 * NSW * part;     // first value column of this workgroup
     const int seq_start = p.cu_seqlens[n];
     const int seq_len = p.cu_seqlens[n + 1] - seq_start;
     const int nchunks = (seq_len + C32 - 1) / C32;
@@ -140,7 +144,7 @@ chunk32_kernel(const ChunkParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float2 v = p.s0 ? *reinterpret_cast<const float2 *>(
-                                                p.s0 + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + 32 * wave + 2 * lr)
+                                                p.s0 + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * wave + 2 * lr)
                                           : make_float2(0.f, 0.f);
                     Sr[0][ct][e] = v.x;
                     Sr[1][ct][e] = v.y;
@@ -197,7 +201,7 @@ chunk32_kernel(const ChunkParams p) {
 
             // ---- seg 2, b(it): Y = V - (Gamma*K) S, U ;  o(it) = scale [ (Gamma*Q) S + A_qk U ]
             if (it >= 0) {
-                const char *vb = sm + L::VB + (32 * wave + 2 * lr) * (int)sizeof(IN_T);
+                const char *vb = sm + L::VB + (col0 + 32 * wave + 2 * lr) * (int)sizeof(IN_T);
                 f32x4_t Y[2][2];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
@@ -239,7 +243,7 @@ chunk32_kernel(const ChunkParams p) {
                     for (int e = 0; e < 4; ++e) {
                         const int r = 16 * rt + 4 * lq + e;
                         if (r < nv)
-                            *reinterpret_cast<float2 *>(p.o + ((size_t)(t0 + r) * H + h) * DV + 32 * wave + 2 * lr) =
+                            *reinterpret_cast<float2 *>(p.o + ((size_t)(t0 + r) * H + h) * DV + col0 + 32 * wave + 2 * lr) =
                                 make_float2(p.scale * acc[0][e], p.scale * acc[1][e]);
                     }
                 }
@@ -274,7 +278,7 @@ chunk32_kernel(const ChunkParams p) {
                     for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            *reinterpret_cast<float2 *>(dst + (size_t)(16 * ct + 4 * lq + e) * DV + 32 * wave + 2 * lr) =
+                            *reinterpret_cast<float2 *>(dst + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * wave + 2 * lr) =
                                 make_float2(Sr[0][ct][e], Sr[1][ct][e]);
                 }
             }
@@ -289,7 +293,7 @@ chunk32_kernel(const ChunkParams p) {
             for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    *reinterpret_cast<float2 *>(p.sf + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + 32 * wave + 2 * lr) =
+                    *reinterpret_cast<float2 *>(p.sf + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * wave + 2 * lr) =
                         make_float2(Sr[0][ct][e], Sr[1][ct][e]);
         }
     } else {
@@ -575,15 +579,40 @@ chunk32_kernel(const ChunkParams p) {
 
 }  // namespace kda
 
+// Compute units of the current device (queried once per device).
+static int kda_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
 extern "C" __attribute__((visibility("hidden"))) hipError_t
-kda_launch_chunk32(int dk, int in_bf16, unsigned grid, const kda::ChunkParams &p, hipStream_t stream) {
-#define KDA_C32(DKV, F32P, T) \
-    hipLaunchKernelGGL((kda::chunk32_kernel<DKV, F32P, T>), dim3(grid), dim3(kda::chunk32_threads<DKV>()), 0, stream, p)
-    if (dk == 128 && in_bf16) KDA_C32(128, false, uint16_t);
-    else if (dk == 128) KDA_C32(128, true, float);
-    else if (dk == 64 && in_bf16) KDA_C32(64, false, uint16_t);
-    else if (dk == 64) KDA_C32(64, true, float);
-    else return hipErrorInvalidValue;
+kda_launch_chunk32(int dk, int in_bf16, unsigned chains, const kda::ChunkParams &p, hipStream_t stream) {
+    // One workgroup per (sequence, head) chain; when the chains would leave more than half the
+    // compute units idle, split each chain's value columns over two workgroups.
+    const int split = (long long)chains * 2 <= kda_cu_count() ? 2 : 1;
+#define KDA_C32(DKV, SP, F32P, T)                                                                        \
+    hipLaunchKernelGGL((kda::chunk32_kernel<DKV, SP, F32P, T>), dim3(chains * SP),                      \
+                       dim3(kda::chunk32_threads<DKV, SP>()), 0, stream, p)
+    if (split == 2) {
+        if (dk == 128 && in_bf16) KDA_C32(128, 2, false, uint16_t);
+        else if (dk == 128) KDA_C32(128, 2, true, float);
+        else if (dk == 64 && in_bf16) KDA_C32(64, 2, false, uint16_t);
+        else if (dk == 64) KDA_C32(64, 2, true, float);
+        else return hipErrorInvalidValue;
+    } else {
+        if (dk == 128 && in_bf16) KDA_C32(128, 1, false, uint16_t);
+        else if (dk == 128) KDA_C32(128, 1, true, float);
+        else if (dk == 64 && in_bf16) KDA_C32(64, 1, false, uint16_t);
+        else if (dk == 64) KDA_C32(64, 1, true, float);
+        else return hipErrorInvalidValue;
+    }
 #undef KDA_C32
     return hipGetLastError();
 }
