@@ -125,12 +125,19 @@ chunk32_kernel(const ChunkParams p) {
     const int seq_len = p.cu_seqlens[n + 1] - seq_start;
     const int nchunks = (seq_len + C32 - 1) / C32;
     const int wave = threadIdx.x >> 6;
+    // Waves are placed on the 4 SIMDs round-robin.  The scan waves take the indices that put them on
+    // the SIMDs holding the fewest waves (with 10 waves: SIMDs 2 and 3, which then carry one prep
+    // wave each); the prep waves take the rest, in order.
+    constexpr int NWAVES = NSW + DK / 16;
+    constexpr int SCAN0 = NWAVES % 4;
+    const bool is_scan = wave >= SCAN0 && wave < SCAN0 + NSW;
+    const int sw = wave - SCAN0;                     // scan wave index (scan waves only)
 
     const IN_T *qg = reinterpret_cast<const IN_T *>(p.q);
     const IN_T *kg = reinterpret_cast<const IN_T *>(p.k);
     const IN_T *vg = reinterpret_cast<const IN_T *>(p.v);
 
-    if (wave < NSW) {
+    if (is_scan) {
         // ============================== scan waves ==============================
         // Lane (lq, lr) of scan wave w owns value columns 32w + 2 lr + jt (jt = column parity),
         // adjacent in memory, so V, o and S move as 2-element pairs.
@@ -144,7 +151,7 @@ chunk32_kernel(const ChunkParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float2 v = p.s0 ? *reinterpret_cast<const float2 *>(
-                                                p.s0 + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * wave + 2 * lr)
+                                                p.s0 + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * sw + 2 * lr)
                                           : make_float2(0.f, 0.f);
                     Sr[0][ct][e] = v.x;
                     Sr[1][ct][e] = v.y;
@@ -195,13 +202,13 @@ chunk32_kernel(const ChunkParams p) {
                 // park the output partials in LDS until stage o (this lane's private slots)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<f32x4_t *>(sm + L::OST + (j * 64 * NSW + 64 * wave + lane) * 16) = Oacc[j >> 1][j & 1];
+                    *reinterpret_cast<f32x4_t *>(sm + L::OST + (j * 64 * NSW + 64 * sw + lane) * 16) = Oacc[j >> 1][j & 1];
             }
             lds_barrier();
 
             // ---- seg 2, b(it): Y = V - (Gamma*K) S, U ;  o(it) = scale [ (Gamma*Q) S + A_qk U ]
             if (it >= 0) {
-                const char *vb = sm + L::VB + (col0 + 32 * wave + 2 * lr) * (int)sizeof(IN_T);
+                const char *vb = sm + L::VB + (col0 + 32 * sw + 2 * lr) * (int)sizeof(IN_T);
                 f32x4_t Y[2][2];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
@@ -236,14 +243,14 @@ chunk32_kernel(const ChunkParams p) {
                     f32x4_t acc[2];
 #pragma unroll
                     for (int jt = 0; jt < 2; ++jt)
-                        acc[jt] = *reinterpret_cast<const f32x4_t *>(sm + L::OST + ((2 * rt + jt) * 64 * NSW + 64 * wave + lane) * 16);
+                        acc[jt] = *reinterpret_cast<const f32x4_t *>(sm + L::OST + ((2 * rt + jt) * 64 * NSW + 64 * sw + lane) * 16);
 #pragma unroll
                     for (int jt = 0; jt < 2; ++jt) mma<true, true>(acc[jt], fa, UF[jt]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 16 * rt + 4 * lq + e;
                         if (r < nv)
-                            *reinterpret_cast<float2 *>(p.o + ((size_t)(t0 + r) * H + h) * DV + col0 + 32 * wave + 2 * lr) =
+                            *reinterpret_cast<float2 *>(p.o + ((size_t)(t0 + r) * H + h) * DV + col0 + 32 * sw + 2 * lr) =
                                 make_float2(p.scale * acc[0][e], p.scale * acc[1][e]);
                     }
                 }
@@ -278,7 +285,7 @@ chunk32_kernel(const ChunkParams p) {
                     for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            *reinterpret_cast<float2 *>(dst + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * wave + 2 * lr) =
+                            *reinterpret_cast<float2 *>(dst + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * sw + 2 * lr) =
                                 make_float2(Sr[0][ct][e], Sr[1][ct][e]);
                 }
             }
@@ -293,14 +300,14 @@ chunk32_kernel(const ChunkParams p) {
             for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    *reinterpret_cast<float2 *>(p.sf + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * wave + 2 * lr) =
+                    *reinterpret_cast<float2 *>(p.sf + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * sw + 2 * lr) =
                         make_float2(Sr[0][ct][e], Sr[1][ct][e]);
         }
     } else {
         // ============================== prep waves ==============================
         // Thread pt = (rgp, cp): rows 4 rgp .. 4 rgp + 3 of the chunk, channels 2 cp, 2 cp + 1.
-        const int pt = (int)threadIdx.x - 64 * NSW;
-        const int pw = wave - NSW;
+        const int pw = wave < SCAN0 ? wave : wave - NSW;     // prep wave index
+        const int pt = 64 * pw + ((int)threadIdx.x & 63);
         const int cp = pt % NCP, c0 = 2 * cp;
         // the 4-row group is uniform across a wave when a wave covers one group (DK = 128)
         const int rgp = NCP >= 64 ? __builtin_amdgcn_readfirstlane(pt / NCP) : pt / NCP;
