@@ -26,8 +26,9 @@
 //            scan waves (chunk i)                      prep waves (chunk i+1)
 //   seg 1    a(i): (Gamma*K) S, (Gamma*Q) S            P1: exp(g), 4-row running products, group totals;
 //                                                      inverses of chunk i's diagonal blocks -> T00, [-M11 T11]
-//   seg 2    b(i): Y = V - (Gamma*K)S, U; o(i): O      P2: decayed operands KS, QS, Gamma*Q, Kn -> LDS
-//   seg 3    c(i): S <- Gamma_last S + Khat^T U        P3: Khat^T, Gamma_last, value rows -> LDS; Gram tiles
+//   seg 2    b(i): Y = V - (Gamma*K)S, U; o(i): O      P2: decayed operands KS, QS, Kn -> LDS
+//   seg 3    c(i): S <- Gamma_last S + Khat^T U        P3: Khat^T, Gamma_last, Gamma*Q, value rows -> LDS;
+//                                                      Gram tiles
 //
 // so the scan's dependent chain a -> b -> c occupies every segment.  Every LDS
 // operand is written in a segment after its last read by the previous chunk;
@@ -124,7 +125,7 @@ chunk32_kernel(const ChunkParams p) {
     const int seq_start = p.cu_seqlens[n];
     const int seq_len = p.cu_seqlens[n + 1] - seq_start;
     const int nchunks = (seq_len + C32 - 1) / C32;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // wave-uniform: scalar register
     // Waves are placed on the 4 SIMDs round-robin.  The scan waves take the indices that put them on
     // the SIMDs holding the fewest waves (with 10 waves: SIMDs 2 and 3, which then carry one prep
     // wave each); the prep waves take the rest, in order.
@@ -162,7 +163,7 @@ chunk32_kernel(const ChunkParams p) {
 
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
-            const int lane = opaque_v((int)threadIdx.x) & 63, lr = lane & 15, lq = lane >> 4;
+            const int lane = lane_id(), lr = lane & 15, lq = lane >> 4;
             const int t0 = seq_start + it * C32, nv = min(C32, seq_len - it * C32);
             f32x4_t Yacc[2][2], Oacc[2][2];
             F UF[2];
@@ -246,11 +247,13 @@ chunk32_kernel(const ChunkParams p) {
                         acc[jt] = *reinterpret_cast<const f32x4_t *>(sm + L::OST + ((2 * rt + jt) * 64 * NSW + 64 * sw + lane) * 16);
 #pragma unroll
                     for (int jt = 0; jt < 2; ++jt) mma<true, true>(acc[jt], fa, UF[jt]);
+                    // chunk base in scalar registers, 32-bit per-lane offsets
+                    float *const obase = p.o + ((size_t)t0 * H + h) * DV + col0;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 16 * rt + 4 * lq + e;
                         if (r < nv)
-                            *reinterpret_cast<float2 *>(p.o + ((size_t)(t0 + r) * H + h) * DV + col0 + 32 * sw + 2 * lr) =
+                            *reinterpret_cast<float2 *>(obase + (unsigned)(r * H * DV + 32 * sw + 2 * lr)) =
                                 make_float2(p.scale * acc[0][e], p.scale * acc[1][e]);
                     }
                 }
@@ -280,12 +283,12 @@ chunk32_kernel(const ChunkParams p) {
                     // state after in-sequence position (it + 1) * 32, a multiple of checkpoint_every
                     ck_left = every_chunks;
                     const int64_t m = p.ckpt_base[n] + ck_idx++;
-                    float *dst = p.ckpt + ((size_t)m * H + h) * DK * DV;
+                    float *const dst = p.ckpt + ((size_t)m * H + h) * DK * DV + col0;
 #pragma unroll
                     for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            *reinterpret_cast<float2 *>(dst + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * sw + 2 * lr) =
+                            *reinterpret_cast<float2 *>(dst + (unsigned)((16 * ct + 4 * lq + e) * DV + 32 * sw + 2 * lr)) =
                                 make_float2(Sr[0][ct][e], Sr[1][ct][e]);
                 }
             }
@@ -295,7 +298,7 @@ chunk32_kernel(const ChunkParams p) {
         if (p.sf) {
             // (lane index recomputed opaquely: row offsets shared with the initial-state loads
             // would otherwise be kept live in registers across the whole loop)
-            const int lane = opaque_v((int)threadIdx.x) & 63, lr = lane & 15, lq = lane >> 4;
+            const int lane = lane_id(), lr = lane & 15, lq = lane >> 4;
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
@@ -369,6 +372,7 @@ chunk32_kernel(const ChunkParams p) {
         typename PR::raw kr[4], qr[4];   // this chunk's k, q pairs from P1 to P2
         float Fw[4][2], Bw[4][2];        // decay products within the 4-row group: through row i / after row i
         float kh[2][4], gl[2];           // (e^{G_last-G} K)^T entries and Gamma_last, from P2 to P3
+        float qtv[4][2];                 // Gamma * q of this thread's rows, from P2 to P3
         float lw[4] = {0.f, 0.f, 0.f, 0.f};   // diagonal Gram block (waves 0, 1), from P3 to the next segment 1
 
         for (int it = -1; it < nchunks; ++it) {
@@ -501,7 +505,7 @@ chunk32_kernel(const ChunkParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 4 * rgp + i, rl = r - 16 * sa;
-                    float ks[2], qs[2], qt[2], ke[2], kd[2];
+                    float ks[2], qs[2], ke[2], kd[2];
                     const float kv[2] = {PR::lo(kr[i]), PR::hi(kr[i])}, qv[2] = {PR::lo(qr[i]), PR::hi(qr[i])};
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
@@ -509,14 +513,13 @@ chunk32_kernel(const ChunkParams p) {
                         const float ee = Bw[i][c] * tail[c];   // e^{G_end(sub-chunk) - G_r}
                         ks[c] = kv[c] * es;
                         qs[c] = qv[c] * es;
-                        qt[c] = qs[c] * pre[c];                // Gamma * q (decay from the chunk start)
+                        qtv[i][c] = qs[c] * pre[c];            // Gamma * q (decay from the chunk start)
                         ke[c] = kv[c] * ee;
                         kd[c] = ke[c] * dgf[c];
                         kh[c][i] = ke[c] * post[c];
                     }
                     M::template put_hl<2>(sm + L::KS, L::SQ_PLANE, ks_off[i], ks);
                     M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, ks_off[i], qs);
-                    M::template put_hl<2>(sm + L::QT, L::SQ_PLANE, ks_off[i], qt);
                     // Kn rows: sub-chunk 0 feeds tiles (0,0) [x 1/P0] and (1,0) [x 1]; sub-chunk 1 feeds (1,1) [x 1/P1]
                     M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn_off[i], kd);
                     if (sa == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn2_off[i], ke);
@@ -538,6 +541,9 @@ chunk32_kernel(const ChunkParams p) {
                 M::template put_hl<4>(sm + L::KHT + buf * L::KHT_BUF, L::KHT_PLANE, kht_off1, kh[1]);
                 if (rgp == 0)
                     *reinterpret_cast<float2 *>(sm + L::GC + (buf * DK + c0) * 4) = make_float2(gl[0], gl[1]);
+                // Gamma * Q of chunk nxt, read by stage a in segment 1 of the next iteration
+#pragma unroll
+                for (int i = 0; i < 4; ++i) M::template put_hl<2>(sm + L::QT, L::SQ_PLANE, ks_off[i], qtv[i]);
                 // value rows of chunk nxt, read by stage b in segment 2 of the next iteration (stage b
                 // of chunk it has finished with the buffer); then fetch chunk nxt + 1's
                 const int nv = min(C32, seq_len - nxt * C32);

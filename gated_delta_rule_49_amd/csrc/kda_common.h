@@ -55,6 +55,12 @@ __device__ __forceinline__ float widen(float x) { return x; }
 // instruction.
 __device__ __forceinline__ int opaque_v(int x) { __asm__ volatile("" : "+v"(x)); return x; }
 __device__ __forceinline__ int opaque_s(int x) { __asm__ volatile("" : "+s"(x)); return x; }
+// Lane index 0..63, recomputed where it is called (v_mbcnt): unlike threadIdx.x & 63 it needs no
+// register kept live across a loop, and the opaque mask keeps it from being hoisted.
+__device__ __forceinline__ int lane_id() {
+    const unsigned m = (unsigned)opaque_s(-1);
+    return (int)__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u));
+}
 
 // ---- wave-level helpers ---------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
