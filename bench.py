@@ -210,7 +210,7 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-KERNEL_NAME = {32: "chunk32_kernel<128,bf16>", 64: "chunk_fwd_kernel<128,bf16>"}
+KERNEL_NAME = {32: "chunk32_kernel<128,split2,bf16>", 64: "chunk_fwd_kernel<128,bf16>"}
 KERNEL_SOURCES = {32: ["kda_chunk32.hip", "kda_frag.h", "kda_common.h"], 64: ["kda_chunk.hip", "kda_frag.h",
                                                                                   "kda_common.h"]}
 COUNTER_FILE = {32: "chunk32_prefill_T65536_H96_d128_counters.json",
@@ -266,7 +266,7 @@ def summarize_counters(chunk, fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma
     """Write profiles/<kernel>_counters.json and .md: HBM bytes per launch of the prefill kernel from
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for a plain
     copy of known size, and MFMA busy / bf16 MOPS from a third pass."""
-    kname = {32: "chunk32_kernel<128, false", 64: "chunk_fwd_kernel<128, false"}[chunk]
+    kname = {32: "chunk32_kernel<128, 2, false", 64: "chunk_fwd_kernel<128, false"}[chunk]
     copy_name = "elementwise_kernel"
     fetch = _mean(_counter_rows(fetch_dir, kname), "FETCH_SIZE")
     write = _mean(_counter_rows(write_dir, kname), "WRITE_SIZE")

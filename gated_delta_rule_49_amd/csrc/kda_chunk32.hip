@@ -6,14 +6,16 @@
 // of two 16-row sub-chunks a = 0, 1.  With G the in-chunk cumulative log-decay,
 // G_ref(a) its value before the first row of sub-chunk a, P0 = e^{G_ref(1)}:
 //     KS = K * e^{G - G_ref},  QS = Q * e^{G - G_ref}          (entries <= |x|)
-//     Gamma*K equals KS with the columns of its rows 16..31 scaled by P0, so
-//     (Gamma*K) S = KS S on rows 0..15 and KS (Diag(P0) S) on rows 16..31
+//     Gamma*K and Gamma*Q equal KS and QS on rows 0..15 (G_ref(0) = 0); rows
+//     16..31 are KS and QS times P0, stored separately (KG, QT)
 //     A_kk, A_qk   lower 16x16 Gram tiles (0,0), (1,0), (1,1) of KS/QS against
 //                  K * e^{G_ref(a) - G} (in fp32 range: 16 * 5 = 80 < 88)
 //     (I + A_kk) U = Diag(beta) Y block by block, A_kk strictly lower, beta-scaled rows:
 //         U0 = T00 Y0,   W = A10 U0,   U1 = T11 Y1 - M11 W
 //         with M_aa = (I + A_aa)^{-1}, T_aa = M_aa Diag(beta_a)
 //     Y  = V - (Gamma*K) S ;  O = scale [ (Gamma*Q) S + A_qk U ]
+//     (the scan accumulates -Y = (Gamma*K) S - V on top of -V, and the diagonal
+//     blocks are stored as -T_aa, so U comes out with the right sign)
 //     S <- Diag(Gamma_last) S + (e^{G_last-G} * K)^T U
 //
 // Workgroup = one (sequence, head): DV/32 "scan waves" and 4*DK/64 "prep waves".
@@ -24,10 +26,10 @@
 // LDS-only barriers per iteration (global loads stay in flight across them):
 //
 //            scan waves (chunk i)                      prep waves (chunk i+1)
-//   seg 1    a(i): (Gamma*K) S, (Gamma*Q) S            P1: exp(g), 4-row running products, group totals;
-//                                                      inverses of chunk i's diagonal blocks -> T00, [-M11 T11]
-//   seg 2    b(i): Y = V - (Gamma*K)S, U; o(i): O      P2: decayed operands KS, QS, Kn -> LDS
-//   seg 3    c(i): S <- Gamma_last S + Khat^T U        P3: Khat^T, Gamma_last, Gamma*Q, value rows -> LDS;
+//   seg 1    a(i): -Y = (Gamma*K) S - V, (Gamma*Q) S   P1: exp(g), 4-row running products, group totals;
+//                                                      inverses of chunk i's diagonal blocks -> -T00, [-M11 -T11]
+//   seg 2    b(i): U; o(i): O                          P2: decayed operands KS, QS, KG, Kn -> LDS
+//   seg 3    c(i): S <- Gamma_last S + Khat^T U        P3: Khat^T, Gamma_last, Gamma*Q, -V -> LDS;
 //                                                      Gram tiles
 //
 // so the scan's dependent chain a -> b -> c occupies every segment.  Every LDS
@@ -54,8 +56,14 @@ struct Lds32 {
     static constexpr int KS = 0;                          // [32][DK] hl: K * e^{G - G_ref}
     static constexpr int QS = KS + 32 * DK * 4;           // [32][DK] hl: Q * e^{G - G_ref}
     static constexpr int SQ_PLANE = 32 * DK * ES;
-    static constexpr int QT = QS + 32 * DK * 4;           // [32][DK] hl: Gamma * Q (decay from the chunk start)
-    static constexpr int KHT = QT + 32 * DK * 4;          // 2 x [DK][32] hl: (e^{G_last-G} K)^T
+    // rows 16..31 only of the next two (rows 0..15 of Gamma*K and Gamma*Q are those of KS and QS);
+    // addressed with the 32-row offsets from a base moved back by 16 rows (QT_AT, KG_AT)
+    static constexpr int QT = QS + 32 * DK * 4;           // [16][DK] hl: Gamma * Q, rows 16..31
+    static constexpr int QT_PLANE = 16 * DK * ES;
+    static constexpr int QT_AT = QT - 16 * DK * ES;
+    static constexpr int KG = QT + 16 * DK * 4;           // [16][DK] single: Gamma * K, rows 16..31
+    static constexpr int KG_AT = KG - 16 * DK * ES;
+    static constexpr int KHT = KG + 16 * DK * ES;         // 2 x [DK][32] hl: (e^{G_last-G} K)^T
     static constexpr int KHT_PLANE = DK * 32 * ES;
     static constexpr int KHT_BUF = DK * 32 * 4;
     static constexpr int TM = KHT + 2 * KHT_BUF;          // [32][32] hl: [T00 0 ; -M11 T11]
@@ -64,9 +72,9 @@ struct Lds32 {
     static constexpr int AW = AQK + 32 * 32 * 4;          // [16][32] hl: [A10 0]
     static constexpr int AW_PLANE = 16 * 32 * ES;
     static constexpr int GC = AW + 16 * 32 * 4;           // 2 x [DK] fp32: Gamma_last
-    static constexpr int P0 = GC + 2 * DK * 4;            // [DK] fp32: e^{G} at the end of sub-chunk 0
-    static constexpr int VPITCH = DK * (int)sizeof(IN_T) + 16;   // padded row pitch (bytes) of the value rows
-    static constexpr int VB = P0 + DK * 4;                // [32][VPITCH]: raw value rows of a chunk
+    // padded row pitch (bytes) of the value rows: 4-row steps land 32 banks apart
+    static constexpr int VPITCH = DK * 4 + 32;
+    static constexpr int VB = GC + 2 * DK * 4;            // [32][VPITCH] fp32: -V of a chunk
     // prep-wave scratch
     static constexpr int KN = VB + 32 * VPITCH;           // [48][DK] hl: K e^{G_ref - G} for tiles (0,0), (1,0), (1,1)
     static constexpr int KN_PLANE = 48 * DK * ES;
@@ -106,6 +114,7 @@ __global__ void __launch_bounds__((chunk32_threads<DK, SPLIT>()))
 chunk32_kernel(const ChunkParams p) {
     constexpr int DV = DK;
     constexpr int NSW = DV / 32 / SPLIT;   // scan waves, 32 value columns each
+    static_assert(SPLIT == 1 || SPLIT == 2, "a chain's value columns go to one or two workgroups");
     constexpr int NPW = DK / 16;        // prep waves: 8 four-row groups x DK/2 channel pairs
     constexpr int KB = DK / 32;         // 32-wide K-steps over d_k
     constexpr int KT = DK / 16;         // 16-row tiles over d_k
@@ -118,7 +127,22 @@ chunk32_kernel(const ChunkParams p) {
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
 
     const int H = p.H;
-    const int part = (int)blockIdx.x % SPLIT, hn = (int)blockIdx.x / SPLIT;
+    // Workgroups are handed to the 8 XCDs round-robin by index, and each XCD has its own L2.  The
+    // workgroups that split one chain read the same k, q, g and beta, so they take indices 8 apart
+    // (same XCD, one L2 fetch serves both): within each group of 16, index 8 r + x (r = 0, 1) is
+    // part r of chain 8 j + x.  A tail of fewer than 16 falls back to adjacent indices.
+    int part, hn;
+    {
+        const int b = (int)blockIdx.x;
+        const int full = SPLIT == 1 ? 0 : ((int)gridDim.x & ~15);
+        if (SPLIT == 1) {
+            part = 0; hn = b;
+        } else if (b < full) {
+            part = (b >> 3) & 1; hn = ((b >> 4) << 3) + (b & 7);
+        } else {
+            part = (b - full) & 1; hn = (full >> 1) + ((b - full) >> 1);
+        }
+    }
     const int h = hn % H;
     const int n = p.order[hn / H];
     const int col0 = 32 * NSW * part;     // first value column of this workgroup
@@ -168,36 +192,36 @@ chunk32_kernel(const ChunkParams p) {
             f32x4_t Yacc[2][2], Oacc[2][2];
             F UF[2];
 
-            // ---- seg 1, a(it): Yacc = (Gamma*K) S and Oacc = (Gamma*Q) S, S = the state entering chunk it.
-            // (Gamma*K) S is KS S on rows 0..15 and KS (Diag(P0) S) on rows 16..31 (single bf16);
-            // (Gamma*Q) is stored as such (QT).  The prep waves invert this chunk's diagonal blocks.
+            // ---- seg 1, a(it): Yacc = (Gamma*K) S - V and Oacc = (Gamma*Q) S, S = the state entering
+            // chunk it ((Gamma*K) single bf16).  The prep waves invert this chunk's diagonal blocks.
             if (it >= 0) {
-                const float *s_p0 = reinterpret_cast<const float *>(sm + L::P0);
+                // Yacc starts from -V (rows past the end hold zeros)
+                const char *vb = sm + L::VB + (col0 + 32 * sw + 2 * lr) * 4;
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) {
-                        Yacc[rt][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                        Oacc[rt][jt] = Yacc[rt][jt];
+                    for (int e = 0; e < 4; ++e) {
+                        const float2 nv2 = *reinterpret_cast<const float2 *>(vb + (16 * rt + 4 * lq + e) * L::VPITCH);
+                        Yacc[rt][0][e] = nv2.x;
+                        Yacc[rt][1][e] = nv2.y;
                     }
 #pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int jt = 0; jt < 2; ++jt) Oacc[rt][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
                 for (int s = 0; s < KB; ++s) {
-                    // channels of this K-step held by the lane: 32 s + 4 lq + e and 32 s + 16 + 4 lq + e
-                    const float4 pa = *reinterpret_cast<const float4 *>(s_p0 + 32 * s + 4 * lq);
-                    const float4 pb = *reinterpret_cast<const float4 *>(s_p0 + 32 * s + 16 + 4 * lq);
-                    const float sc[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
                     const F fk0 = M::template get<false>(sm + L::KS, 0, fbase<KB>(0, s, lane));
-                    const F fk1 = M::template get<false>(sm + L::KS, 0, fbase<KB>(1, s, lane));
-                    const F fq0 = M::template get<true>(sm + L::QT, L::SQ_PLANE, fbase<KB>(0, s, lane));
-                    const F fq1 = M::template get<true>(sm + L::QT, L::SQ_PLANE, fbase<KB>(1, s, lane));
+                    const F fk1 = M::template get<false>(sm + L::KG_AT, 0, fbase<KB>(1, s, lane));
+                    const F fq0 = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(0, s, lane));
+                    const F fq1 = M::template get<true>(sm + L::QT_AT, L::QT_PLANE, fbase<KB>(1, s, lane));
 #pragma unroll
                     for (int jt = 0; jt < 2; ++jt) {
                         const F sf = M::template from_tiles<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
                         mma<false, false>(Yacc[0][jt], fk0, sf);
                         mma<true, true>(Oacc[0][jt], fq0, sf);
                         mma<true, true>(Oacc[1][jt], fq1, sf);
-                        const F sp = M::template from_tiles_scaled<false>(Sr[jt][2 * s], Sr[jt][2 * s + 1], sc);
-                        mma<false, false>(Yacc[1][jt], fk1, sp);
+                        mma<false, false>(Yacc[1][jt], fk1, sf);
                     }
                 }
                 // park the output partials in LDS until stage o (this lane's private slots)
@@ -207,22 +231,12 @@ chunk32_kernel(const ChunkParams p) {
             }
             lds_barrier();
 
-            // ---- seg 2, b(it): Y = V - (Gamma*K) S, U ;  o(it) = scale [ (Gamma*Q) S + A_qk U ]
+            // ---- seg 2, b(it): U from -Y = Yacc ;  o(it) = scale [ (Gamma*Q) S + A_qk U ]
             if (it >= 0) {
-                const char *vb = sm + L::VB + (col0 + 32 * sw + 2 * lr) * (int)sizeof(IN_T);
-                f32x4_t Y[2][2];
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * rt + 4 * lq + e;   // rows past the end hold zeros
-                        const typename PR::raw vw = *reinterpret_cast<const typename PR::raw *>(vb + r * L::VPITCH);
-                        Y[rt][0][e] = PR::lo(vw) - Yacc[rt][0][e];
-                        Y[rt][1][e] = PR::hi(vw) - Yacc[rt][1][e];
-                    }
+                const f32x4_t (&Y)[2][2] = Yacc;   // -Y
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt) {
-                    // U0 = T00 Y0 ; W = A10 U0 ; U1 = T11 Y1 - M11 W
+                    // U0 = (-T00)(-Y0) ; W = A10 U0 ; U1 = (-T11)(-Y1) - M11 W
                     f32x4_t u0 = {0.f, 0.f, 0.f, 0.f}, w = u0, u1 = u0;
                     {
                         const F t0f = M::template get<true>(sm + L::TM, L::TRI_PLANE, fbase<1>(0, 0, lane));
@@ -324,7 +338,7 @@ chunk32_kernel(const ChunkParams p) {
             ks_off[i] = fofs<KB>(r, c0);                 // KS and QS share the layout
             kn_off[i] = fofs<KB>(32 * sa + rl, c0);
             kn2_off[i] = fofs<KB>(16 + rl, c0);
-            vb_off[i] = r * L::VPITCH + c0 * (int)sizeof(IN_T);
+            vb_off[i] = r * L::VPITCH + c0 * 4;
         }
         const int kht_off0 = fofs<1>(c0, 4 * rgp), kht_off1 = fofs<1>(c0 + 1, 4 * rgp);
 
@@ -417,7 +431,8 @@ chunk32_kernel(const ChunkParams p) {
                 // wave's Gram tile left in lw (row lr, columns 4 lq + e) one segment ago, as
                 //     M = (I + X)(I + X^2)(I + X^4)(I + X^8),  X = -N,  N^16 = 0,
                 // with 16x16 MFMA products held in registers (five dependent levels instead of a
-                // 16-step substitution; hi/lo bf16 operands, or fp32 MFMA for fp32 inputs).  T_aa = M Diag(beta_a) (and -M11) -> TM, read by stage b in segment 2.
+                // 16-step substitution; hi/lo bf16 operands, or fp32 MFMA for fp32 inputs).  -T_aa = -M Diag(beta_a)
+                // (and -M11) -> TM, read by stage b in segment 2.
                 const int a = pw;
                 float *zt = reinterpret_cast<float *>(sm + L::ZT) + a * TSZ;
                 const float *beta_it = reinterpret_cast<const float *>(sm + L::BETA) + (it & 1) * 32;
@@ -466,7 +481,7 @@ chunk32_kernel(const ChunkParams p) {
                 const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
                 float tv[4], nm[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) { tv[e] = MA[e] * bv[e]; nm[e] = -MA[e]; }
+                for (int e = 0; e < 4; ++e) { tv[e] = -(MA[e] * bv[e]); nm[e] = -MA[e]; }
                 M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * a + 4 * lq), tv);
                 if (a == 1) M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 + lr, 4 * lq), nm);
             }
@@ -501,7 +516,6 @@ chunk32_kernel(const ChunkParams p) {
                 }
                 gl[0] = P0[0] * P1[0];
                 gl[1] = P0[1] * P1[1];
-                if (rgp == 0) *reinterpret_cast<float2 *>(sm + L::P0 + c0 * 4) = make_float2(P0[0], P0[1]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 4 * rgp + i, rl = r - 16 * sa;
@@ -523,6 +537,7 @@ chunk32_kernel(const ChunkParams p) {
                     // Kn rows: sub-chunk 0 feeds tiles (0,0) [x 1/P0] and (1,0) [x 1]; sub-chunk 1 feeds (1,1) [x 1/P1]
                     M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn_off[i], kd);
                     if (sa == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn2_off[i], ke);
+                    else M::put_h2(sm + L::KG_AT, ks_off[i], ks[0] * pre[0], ks[1] * pre[1]);   // Gamma * K
                 }
             }
             lds_barrier();
@@ -541,16 +556,17 @@ chunk32_kernel(const ChunkParams p) {
                 M::template put_hl<4>(sm + L::KHT + buf * L::KHT_BUF, L::KHT_PLANE, kht_off1, kh[1]);
                 if (rgp == 0)
                     *reinterpret_cast<float2 *>(sm + L::GC + (buf * DK + c0) * 4) = make_float2(gl[0], gl[1]);
-                // Gamma * Q of chunk nxt, read by stage a in segment 1 of the next iteration
+                // Gamma * Q of chunk nxt (rows 16..31), read by stage a in segment 1 of the next iteration
+                if (sa)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) M::template put_hl<2>(sm + L::QT, L::SQ_PLANE, ks_off[i], qtv[i]);
-                // value rows of chunk nxt, read by stage b in segment 2 of the next iteration (stage b
+                    for (int i = 0; i < 4; ++i) M::template put_hl<2>(sm + L::QT_AT, L::QT_PLANE, ks_off[i], qtv[i]);
+                // -V of chunk nxt in fp32, read by stage a in segment 1 of the next iteration (stage a
                 // of chunk it has finished with the buffer); then fetch chunk nxt + 1's
                 const int nv = min(C32, seq_len - nxt * C32);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<typename PR::raw *>(sm + L::VB + vb_off[i]) =
-                        4 * rgp + i < nv ? vn_[i] : PR::zero();
+                    *reinterpret_cast<float2 *>(sm + L::VB + vb_off[i]) =
+                        4 * rgp + i < nv ? make_float2(-PR::lo(vn_[i]), -PR::hi(vn_[i])) : make_float2(0.f, 0.f);
                 vfetch(min(nxt + 1, nchunks - 1));
             }
             if (have && pw < 3) {
