@@ -49,7 +49,7 @@ namespace kda {
 
 constexpr int C32 = 32;
 
-template <int DK, int NSW, bool F32P, typename IN_T>
+template <int DK, int NSW, int JT, bool F32P, typename IN_T>
 struct Lds32 {
     static constexpr int ES = Mat<F32P>::ES;
     // operands of a chunk, written by the prep waves, read by the scan waves
@@ -72,8 +72,9 @@ struct Lds32 {
     static constexpr int AW = AQK + 32 * 32 * 4;          // [16][32] hl: [A10 0]
     static constexpr int AW_PLANE = 16 * 32 * ES;
     static constexpr int GC = AW + 16 * 32 * 4;           // 2 x [DK] fp32: Gamma_last
-    // padded row pitch (bytes) of the value rows: 4-row steps land 32 banks apart
-    static constexpr int VPITCH = DK * 4 + 32;
+    // padded row pitch (bytes) of the value rows: the rows 4 apart that one read spans start
+    // 8 (JT = 2) or 4 (JT = 1) banks apart modulo the row of 64 banks it reads
+    static constexpr int VPITCH = DK * 4 + 16 * JT;
     static constexpr int VB = GC + 2 * DK * 4;            // [32][VPITCH] fp32: -V of a chunk
     // prep-wave scratch
     static constexpr int KN = VB + 32 * VPITCH;           // [48][DK] hl: K e^{G_ref - G} for tiles (0,0), (1,0), (1,1)
@@ -81,10 +82,10 @@ struct Lds32 {
     static constexpr int ZT = KN + 48 * DK * 4;           // 2 fp32 tiles: L^T of the diagonal A_kk blocks
     static constexpr int XCHG = ZT + 2 * TSZ * 4;         // [8][DK] fp32: decay over each 4-row group
     static constexpr int BETA = XCHG + 8 * DK * 4;        // 2 x [32] fp32
-    // scan-wave stash: each scan lane parks its 16 (Gamma*Q) S partial outputs here between
-    // segments 1 and 2 (register pressure), element j of lane l at OST + (j * 64 NSW + l) * 16 bytes
+    // scan-wave stash: each scan lane parks its 8 JT (Gamma*Q) S partial outputs here between
+    // segments 1 and 2 (register pressure), tile j of lane l at OST + (j * 64 NSW + l) * 16 bytes
     static constexpr int OST = BETA + 2 * 32 * 4;
-    static constexpr int TOTAL = OST + 4 * 64 * NSW * 16;
+    static constexpr int TOTAL = OST + 2 * JT * 64 * NSW * 16;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -106,20 +107,42 @@ template <> struct Pair<float> {
 };
 
 // SPLIT workgroups share one (sequence, head), each owning DV / SPLIT value columns (the
-// state's columns evolve independently) and each preparing the chunk operands itself.
-template <int DK, int SPLIT> constexpr int chunk32_threads() { return 64 * (DK / 32 / SPLIT) + 4 * DK; }
+// state's columns evolve independently) and each preparing the chunk operands itself.  A scan
+// wave owns 16 value columns when a workgroup has at most 64, else 32: with d_k = 128 a
+// workgroup then has 4 scan waves and 8 prep waves, 3 per SIMD, one of them a scan wave.
+template <int DK, int SPLIT> constexpr int chunk32_scan_cols() { return DK / SPLIT <= 64 ? 16 : 32; }
+template <int DK, int SPLIT> constexpr int chunk32_threads() {
+    return 64 * (DK / SPLIT / chunk32_scan_cols<DK, SPLIT>()) + 4 * DK;
+}
+
+// JT adjacent fp32 values (the columns one scan lane owns in a row) from / to memory
+template <int JT> __device__ __forceinline__ void load_cols(const float *ptr, float (&x)[JT]) {
+    if constexpr (JT == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(ptr);
+        x[0] = v.x;
+        x[1] = v.y;
+    } else {
+        x[0] = *ptr;
+    }
+}
+template <int JT> __device__ __forceinline__ void store_cols(float *ptr, const float (&x)[JT]) {
+    if constexpr (JT == 2) *reinterpret_cast<float2 *>(ptr) = make_float2(x[0], x[1]);
+    else *ptr = x[0];
+}
 
 template <int DK, int SPLIT, bool F32P, typename IN_T>
 __global__ void __launch_bounds__((chunk32_threads<DK, SPLIT>()))
 chunk32_kernel(const ChunkParams p) {
     constexpr int DV = DK;
-    constexpr int NSW = DV / 32 / SPLIT;   // scan waves, 32 value columns each
+    constexpr int SWC = chunk32_scan_cols<DK, SPLIT>();   // value columns of a scan wave
+    constexpr int JT = SWC / 16;                          // 16-column MFMA tiles of a scan wave
+    constexpr int NSW = DV / SPLIT / SWC;                 // scan waves
     static_assert(SPLIT == 1 || SPLIT == 2, "a chain's value columns go to one or two workgroups");
     constexpr int NPW = DK / 16;        // prep waves: 8 four-row groups x DK/2 channel pairs
     constexpr int KB = DK / 32;         // 32-wide K-steps over d_k
     constexpr int KT = DK / 16;         // 16-row tiles over d_k
     constexpr int NCP = DK / 2;         // channel pairs
-    using L = Lds32<DK, NSW, F32P, IN_T>;
+    using L = Lds32<DK, NSW, JT, F32P, IN_T>;
     using M = Mat<F32P>;
     using F = Frag<F32P>;
     using PR = Pair<IN_T>;
@@ -145,14 +168,14 @@ chunk32_kernel(const ChunkParams p) {
     }
     const int h = hn % H;
     const int n = p.order[hn / H];
-    const int col0 = 32 * NSW * part;     // first value column of this workgroup
+    const int col0 = (DV / SPLIT) * part;     // first value column of this workgroup
     const int seq_start = p.cu_seqlens[n];
     const int seq_len = p.cu_seqlens[n + 1] - seq_start;
     const int nchunks = (seq_len + C32 - 1) / C32;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // wave-uniform: scalar register
     // Waves are placed on the 4 SIMDs round-robin.  The scan waves take the indices that put them on
-    // the SIMDs holding the fewest waves (with 10 waves: SIMDs 2 and 3, which then carry one prep
-    // wave each); the prep waves take the rest, in order.
+    // the SIMDs holding the fewest waves (with 12 waves: one on each SIMD; with 10: SIMDs 2 and 3);
+    // the prep waves take the rest, in order.
     constexpr int NWAVES = NSW + DK / 16;
     constexpr int SCAN0 = NWAVES % 4;
     const bool is_scan = wave >= SCAN0 && wave < SCAN0 + NSW;
@@ -164,22 +187,24 @@ chunk32_kernel(const ChunkParams p) {
 
     if (is_scan) {
         // ============================== scan waves ==============================
-        // Lane (lq, lr) of scan wave w owns value columns 32w + 2 lr + jt (jt = column parity),
-        // adjacent in memory, so V, o and S move as 2-element pairs.
-        // Sr[jt][ct][e] = S[16 ct + 4 lq + e][32 wave + 2 lr + jt]
+        // Lane (lq, lr) of scan wave w owns value columns c(jt) = SWC w + JT lr + jt (jt < JT),
+        // adjacent in memory, so V, o and S move as JT-element groups.
+        // Sr[jt][ct][e] = S[16 ct + 4 lq + e][col0 + c(jt)]
         const size_t st_off = ((size_t)n * H + h) * DK * DV;
-        f32x4_t Sr[2][KT];
+        f32x4_t Sr[JT][KT];
         {
             const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float2 v = p.s0 ? *reinterpret_cast<const float2 *>(
-                                                p.s0 + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * sw + 2 * lr)
-                                          : make_float2(0.f, 0.f);
-                    Sr[0][ct][e] = v.x;
-                    Sr[1][ct][e] = v.y;
+                    float x[JT];
+#pragma unroll
+                    for (int jt = 0; jt < JT; ++jt) x[jt] = 0.f;
+                    if (p.s0)
+                        load_cols<JT>(p.s0 + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + SWC * sw + JT * lr, x);
+#pragma unroll
+                    for (int jt = 0; jt < JT; ++jt) Sr[jt][ct][e] = x[jt];
                 }
         }
         const int every_chunks = p.every / C32;   // checkpoint_every is a multiple of the chunk size
@@ -189,26 +214,27 @@ chunk32_kernel(const ChunkParams p) {
             char *const sm = smem + opaque_s(0);
             const int lane = lane_id(), lr = lane & 15, lq = lane >> 4;
             const int t0 = seq_start + it * C32, nv = min(C32, seq_len - it * C32);
-            f32x4_t Yacc[2][2], Oacc[2][2];
-            F UF[2];
+            f32x4_t Yacc[2][JT], Oacc[2][JT];
+            F UF[JT];
 
             // ---- seg 1, a(it): Yacc = (Gamma*K) S - V and Oacc = (Gamma*Q) S, S = the state entering
             // chunk it ((Gamma*K) single bf16).  The prep waves invert this chunk's diagonal blocks.
             if (it >= 0) {
                 // Yacc starts from -V (rows past the end hold zeros)
-                const char *vb = sm + L::VB + (col0 + 32 * sw + 2 * lr) * 4;
+                const char *vb = sm + L::VB + (col0 + SWC * sw + JT * lr) * 4;
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float2 nv2 = *reinterpret_cast<const float2 *>(vb + (16 * rt + 4 * lq + e) * L::VPITCH);
-                        Yacc[rt][0][e] = nv2.x;
-                        Yacc[rt][1][e] = nv2.y;
+                        float x[JT];
+                        load_cols<JT>(reinterpret_cast<const float *>(vb + (16 * rt + 4 * lq + e) * L::VPITCH), x);
+#pragma unroll
+                        for (int jt = 0; jt < JT; ++jt) Yacc[rt][jt][e] = x[jt];
                     }
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) Oacc[rt][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    for (int jt = 0; jt < JT; ++jt) Oacc[rt][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < KB; ++s) {
                     const F fk0 = M::template get<false>(sm + L::KS, 0, fbase<KB>(0, s, lane));
@@ -216,7 +242,7 @@ chunk32_kernel(const ChunkParams p) {
                     const F fq0 = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(0, s, lane));
                     const F fq1 = M::template get<true>(sm + L::QT_AT, L::QT_PLANE, fbase<KB>(1, s, lane));
 #pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) {
+                    for (int jt = 0; jt < JT; ++jt) {
                         const F sf = M::template from_tiles<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
                         mma<false, false>(Yacc[0][jt], fk0, sf);
                         mma<true, true>(Oacc[0][jt], fq0, sf);
@@ -226,16 +252,16 @@ chunk32_kernel(const ChunkParams p) {
                 }
                 // park the output partials in LDS until stage o (this lane's private slots)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<f32x4_t *>(sm + L::OST + (j * 64 * NSW + 64 * sw + lane) * 16) = Oacc[j >> 1][j & 1];
+                for (int j = 0; j < 2 * JT; ++j)
+                    *reinterpret_cast<f32x4_t *>(sm + L::OST + (j * 64 * NSW + 64 * sw + lane) * 16) = Oacc[j / JT][j % JT];
             }
             lds_barrier();
 
             // ---- seg 2, b(it): U from -Y = Yacc ;  o(it) = scale [ (Gamma*Q) S + A_qk U ]
             if (it >= 0) {
-                const f32x4_t (&Y)[2][2] = Yacc;   // -Y
+                const f32x4_t (&Y)[2][JT] = Yacc;   // -Y
 #pragma unroll
-                for (int jt = 0; jt < 2; ++jt) {
+                for (int jt = 0; jt < JT; ++jt) {
                     // U0 = (-T00)(-Y0) ; W = A10 U0 ; U1 = (-T11)(-Y1) - M11 W
                     f32x4_t u0 = {0.f, 0.f, 0.f, 0.f}, w = u0, u1 = u0;
                     {
@@ -255,20 +281,23 @@ chunk32_kernel(const ChunkParams p) {
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
                     const F fa = M::template get<true>(sm + L::AQK, L::TRI_PLANE, fbase<1>(rt, 0, lane));
-                    f32x4_t acc[2];
+                    f32x4_t acc[JT];
 #pragma unroll
-                    for (int jt = 0; jt < 2; ++jt)
-                        acc[jt] = *reinterpret_cast<const f32x4_t *>(sm + L::OST + ((2 * rt + jt) * 64 * NSW + 64 * sw + lane) * 16);
+                    for (int jt = 0; jt < JT; ++jt)
+                        acc[jt] = *reinterpret_cast<const f32x4_t *>(sm + L::OST + ((JT * rt + jt) * 64 * NSW + 64 * sw + lane) * 16);
 #pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) mma<true, true>(acc[jt], fa, UF[jt]);
+                    for (int jt = 0; jt < JT; ++jt) mma<true, true>(acc[jt], fa, UF[jt]);
                     // chunk base in scalar registers, 32-bit per-lane offsets
                     float *const obase = p.o + ((size_t)t0 * H + h) * DV + col0;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 16 * rt + 4 * lq + e;
-                        if (r < nv)
-                            *reinterpret_cast<float2 *>(obase + (unsigned)(r * H * DV + 32 * sw + 2 * lr)) =
-                                make_float2(p.scale * acc[0][e], p.scale * acc[1][e]);
+                        if (r < nv) {
+                            float x[JT];
+#pragma unroll
+                            for (int jt = 0; jt < JT; ++jt) x[jt] = p.scale * acc[jt][e];
+                            store_cols<JT>(obase + (unsigned)(r * H * DV + SWC * sw + JT * lr), x);
+                        }
                     }
                 }
             }
@@ -285,7 +314,7 @@ chunk32_kernel(const ChunkParams p) {
                     const float4 gc = *reinterpret_cast<const float4 *>(s_gc + 16 * ct + 4 * lq);
                     const float gcv[4] = {gc.x, gc.y, gc.z, gc.w};
 #pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) {
+                    for (int jt = 0; jt < JT; ++jt) {
                         f32x4_t acc;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) acc[e] = gcv[e] * Sr[jt][ct][e];
@@ -301,9 +330,12 @@ chunk32_kernel(const ChunkParams p) {
 #pragma unroll
                     for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            *reinterpret_cast<float2 *>(dst + (unsigned)((16 * ct + 4 * lq + e) * DV + 32 * sw + 2 * lr)) =
-                                make_float2(Sr[0][ct][e], Sr[1][ct][e]);
+                        for (int e = 0; e < 4; ++e) {
+                            float x[JT];
+#pragma unroll
+                            for (int jt = 0; jt < JT; ++jt) x[jt] = Sr[jt][ct][e];
+                            store_cols<JT>(dst + (unsigned)((16 * ct + 4 * lq + e) * DV + SWC * sw + JT * lr), x);
+                        }
                 }
             }
             lds_barrier();
@@ -316,9 +348,12 @@ chunk32_kernel(const ChunkParams p) {
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    *reinterpret_cast<float2 *>(p.sf + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + 32 * sw + 2 * lr) =
-                        make_float2(Sr[0][ct][e], Sr[1][ct][e]);
+                for (int e = 0; e < 4; ++e) {
+                    float x[JT];
+#pragma unroll
+                    for (int jt = 0; jt < JT; ++jt) x[jt] = Sr[jt][ct][e];
+                    store_cols<JT>(p.sf + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + SWC * sw + JT * lr, x);
+                }
         }
     } else {
         // ============================== prep waves ==============================
