@@ -79,7 +79,10 @@ struct Lds32 {
     // prep-wave scratch
     static constexpr int KN = VB + 32 * VPITCH;           // [48][DK] hl: K e^{G_ref - G} for tiles (0,0), (1,0), (1,1)
     static constexpr int KN_PLANE = 48 * DK * ES;
-    static constexpr int ZT = KN + 48 * DK * 4;           // 2 fp32 tiles: L^T of the diagonal A_kk blocks
+    // the strictly lower, beta-scaled diagonal A_kk blocks, from the Gram tiles to the inverses:
+    // block a as Z (ZR + a TSZ) and as Z^T (ZT + a TSZ), fp32 [16][TP]
+    static constexpr int ZR = KN + 48 * DK * 4;
+    static constexpr int ZT = ZR + 2 * TSZ * 4;
     static constexpr int XCHG = ZT + 2 * TSZ * 4;         // [8][DK] fp32: decay over each 4-row group
     static constexpr int BETA = XCHG + 8 * DK * 4;        // 2 x [32] fp32
     // scan-wave stash: each scan lane parks its 8 JT (Gamma*Q) S partial outputs here between
@@ -108,11 +111,17 @@ template <> struct Pair<float> {
 
 // SPLIT workgroups share one (sequence, head), each owning DV / SPLIT value columns (the
 // state's columns evolve independently) and each preparing the chunk operands itself.  A scan
-// wave owns 16 value columns when a workgroup has at most 64, else 32: with d_k = 128 a
-// workgroup then has 4 scan waves and 8 prep waves, 3 per SIMD, one of them a scan wave.
+// wave owns 16 value columns when a workgroup has at most 64, else 32.  With four 16-column scan
+// waves (d_k = 128, two workgroups per chain) the workgroup also gets 4 "role" waves for the
+// diagonal inverses and Gram tiles: 16 waves, 4 per SIMD, one scan, two prep and one role wave
+// on each.  Otherwise prep waves 0..2 take those roles on top of their own work.
 template <int DK, int SPLIT> constexpr int chunk32_scan_cols() { return DK / SPLIT <= 64 ? 16 : 32; }
+template <int DK, int SPLIT> constexpr int chunk32_scan_waves() { return DK / SPLIT / chunk32_scan_cols<DK, SPLIT>(); }
+template <int DK, int SPLIT> constexpr int chunk32_role_waves() {
+    return chunk32_scan_waves<DK, SPLIT>() == 4 && chunk32_scan_cols<DK, SPLIT>() == 16 ? 4 : 0;
+}
 template <int DK, int SPLIT> constexpr int chunk32_threads() {
-    return 64 * (DK / SPLIT / chunk32_scan_cols<DK, SPLIT>()) + 4 * DK;
+    return 64 * (chunk32_scan_waves<DK, SPLIT>() + DK / 16 + chunk32_role_waves<DK, SPLIT>());
 }
 
 // JT adjacent fp32 values (the columns one scan lane owns in a row) from / to memory
@@ -137,6 +146,7 @@ chunk32_kernel(const ChunkParams p) {
     constexpr int SWC = chunk32_scan_cols<DK, SPLIT>();   // value columns of a scan wave
     constexpr int JT = SWC / 16;                          // 16-column MFMA tiles of a scan wave
     constexpr int NSW = DV / SPLIT / SWC;                 // scan waves
+    constexpr int NRW = chunk32_role_waves<DK, SPLIT>();  // role waves (inverses, Gram tiles)
     static_assert(SPLIT == 1 || SPLIT == 2, "a chain's value columns go to one or two workgroups");
     constexpr int NPW = DK / 16;        // prep waves: 8 four-row groups x DK/2 channel pairs
     constexpr int KB = DK / 32;         // 32-wide K-steps over d_k
@@ -176,16 +186,139 @@ chunk32_kernel(const ChunkParams p) {
     // Waves are placed on the 4 SIMDs round-robin.  The scan waves take the indices that put them on
     // the SIMDs holding the fewest waves (with 12 waves: one on each SIMD; with 10: SIMDs 2 and 3);
     // the prep waves take the rest, in order.
-    constexpr int NWAVES = NSW + DK / 16;
-    constexpr int SCAN0 = NWAVES % 4;
+    constexpr int NWAVES = NSW + DK / 16 + NRW;
+    constexpr int SCAN0 = (NSW + DK / 16) % 4;
     const bool is_scan = wave >= SCAN0 && wave < SCAN0 + NSW;
+    const bool is_role = wave >= NSW + DK / 16;      // role waves come last
     const int sw = wave - SCAN0;                     // scan wave index (scan waves only)
 
     const IN_T *qg = reinterpret_cast<const IN_T *>(p.q);
     const IN_T *kg = reinterpret_cast<const IN_T *>(p.k);
     const IN_T *vg = reinterpret_cast<const IN_T *>(p.v);
 
-    if (is_scan) {
+    // Diagonal block a of chunk ch: M = (I + N)^{-1} for the strictly lower, beta-scaled N that the
+    // Gram tile left in ZR / ZT, as
+    //     M = (I + X)(I + X^2)(I + X^4)(I + X^8),  X = -N,  N^16 = 0,
+    // with 16x16 MFMA products held in registers (five dependent levels instead of a 16-step
+    // substitution; hi/lo bf16 operands, or fp32 MFMA for fp32 inputs).  -T_aa = -M Diag(beta_a)
+    // (and -M11) -> TM, read by stage b in segment 2.
+    auto diag_inverse = [&](char *sm, int a, int ch, int lane) {
+        const int lr = lane & 15, lq = lane >> 4;
+        const float *zr = reinterpret_cast<const float *>(sm + L::ZR) + a * TSZ;
+        const float *zt = reinterpret_cast<const float *>(sm + L::ZT) + a * TSZ;
+        const float *beta_ch = reinterpret_cast<const float *>(sm + L::BETA) + (ch & 1) * 32;
+        // forms of a 16x16 Z held by lane (lq, lr): "A" = Z[lr][4 lq + e], "B" = Z[4 lq + e][lr]
+        const float4 na4 = *reinterpret_cast<const float4 *>(zr + lr * TP + 4 * lq);
+        const float4 nb4 = *reinterpret_cast<const float4 *>(zt + lr * TP + 4 * lq);
+        const f32x4_t XA = {-na4.x, -na4.y, -na4.z, -na4.w}, XB = {-nb4.x, -nb4.y, -nb4.z, -nb4.w};
+        // (Z W) in B form = mm(Z_A, W_B); in A form = mm(W_B, Z_A)
+        auto mm = [](const f32x4_t &za, const f32x4_t &wb) {
+            f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (F32P) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) d = mfma_f32(za[kk], wb[kk], d);
+            } else {
+                // hi/lo bf16 split in two 16x16x32 MFMAs: K-slots 0..15 carry the hi parts and
+                // 16..31 the lo parts of Z, so [Zh Zl][Wh; Wh] + [Zh Zh][Wl; 0] = Zh Wh + Zl Wh + Zh Wl
+                uint32_t zh[2], zl[2], wh[2], wl[2];
+                split_hl2(za[0], za[1], zh[0], zl[0]);
+                split_hl2(za[2], za[3], zh[1], zl[1]);
+                split_hl2(wb[0], wb[1], wh[0], wl[0]);
+                split_hl2(wb[2], wb[3], wh[1], wl[1]);
+                const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, (uint4){zh[0], zh[1], zl[0], zl[1]});
+                const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, (uint4){wh[0], wh[1], wh[0], wh[1]});
+                const bf16x8_t a2 = __builtin_bit_cast(bf16x8_t, (uint4){zh[0], zh[1], zh[0], zh[1]});
+                const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, (uint4){wl[0], wl[1], 0u, 0u});
+                d = mfma_bf16(a1, b1, d);
+                d = mfma_bf16(a2, b2, d);
+            }
+            return d;
+        };
+        const f32x4_t X2B = mm(XA, XB), X2A = mm(XB, XA);
+        const f32x4_t X4B = mm(X2A, X2B), X4A = mm(X2B, X2A), X3A = mm(X2B, XA);
+        const f32x4_t X8B = mm(X4A, X4B);
+        const f32x4_t X12B = mm(X4A, X8B);
+        f32x4_t P1A, P2B;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float id = (4 * lq + e == lr) ? 1.f : 0.f;
+            P1A[e] = id + XA[e] + X2A[e] + X3A[e];     // I + X + X^2 + X^3
+            P2B[e] = id + X4B[e] + X8B[e] + X12B[e];   // I + X^4 + X^8 + X^12
+        }
+        const f32x4_t MA = mm(P2B, P1A);                // M = P1 P2, A form: M[lr][4 lq + e]
+        const float4 b4 = *reinterpret_cast<const float4 *>(beta_ch + 16 * a + 4 * lq);
+        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+        float tv[4], nm[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { tv[e] = -(MA[e] * bv[e]); nm[e] = -MA[e]; }
+        M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * a + 4 * lq), tv);
+        if (a == 1) M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 + lr, 4 * lq), nm);
+    };
+
+    // Gram tile t of chunk ch, from the Kn block it shares with the A_qk tile of the same place:
+    //   t 0: tile (0,0)  A_kk -> ZR/ZT block 0   and A_qk(0,0)
+    //   t 1: tile (1,1)  A_kk -> ZR/ZT block 1   and A_qk(1,1)
+    //   t 2: tile (1,0)  A10 -> AW               and A_qk(1,0)
+    auto gram_tile = [&](char *sm, int t, int ch, int lane) {
+        const int lr = lane & 15, lq = lane >> 4;
+        const int knb = t == 0 ? 0 : (t == 1 ? 2 : 1);
+        const int a = t == 0 ? 0 : 1, b = t == 1 ? 1 : 0;
+        f32x4_t gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
+#pragma unroll
+        for (int s = 0; s < KB; ++s) {
+            const F fn = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(knb, s, lane));
+            const F fk = M::template get<true>(sm + L::KS, L::SQ_PLANE, fbase<KB>(a, s, lane));
+            const F fq = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(a, s, lane));
+            mma<true, true>(gk, fn, fk);
+            mma<true, true>(gq, fn, fq);
+        }
+        // lane holds tile element (16 a + lr, 16 b + 4 lq + e)
+        {
+            float w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (b < a || 4 * lq + e <= lr) ? gq[e] : 0.f;
+            M::template put_hl<4>(sm + L::AQK, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * b + 4 * lq), w);
+        }
+        const float br = reinterpret_cast<const float *>(sm + L::BETA)[(ch & 1) * 32 + 16 * a + lr];
+        if (t == 2) {
+            float w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = br * gk[e];
+            M::template put_hl<4>(sm + L::AW, L::AW_PLANE, fofs<1>(lr, 4 * lq), w);
+        } else {
+            // strictly lower part of A_kk(a, a) with beta-scaled rows (row lr, columns 4 lq + e)
+            float4 z;
+            z.x = 4 * lq + 0 < lr ? br * gk[0] : 0.f;
+            z.y = 4 * lq + 1 < lr ? br * gk[1] : 0.f;
+            z.z = 4 * lq + 2 < lr ? br * gk[2] : 0.f;
+            z.w = 4 * lq + 3 < lr ? br * gk[3] : 0.f;
+            float *zr = reinterpret_cast<float *>(sm + L::ZR) + t * TSZ;
+            float *zt = reinterpret_cast<float *>(sm + L::ZT) + t * TSZ;
+            *reinterpret_cast<float4 *>(zr + lr * TP + 4 * lq) = z;
+            zt[(4 * lq + 0) * TP + lr] = z.x;
+            zt[(4 * lq + 1) * TP + lr] = z.y;
+            zt[(4 * lq + 2) * TP + lr] = z.z;
+            zt[(4 * lq + 3) * TP + lr] = z.w;
+        }
+    };
+
+    if (NRW > 0 && is_role) {
+        // ============================== role waves ==============================
+        // wave rw: segment 1 of iteration it inverts diagonal block rw (< 2) of chunk it, segment 3
+        // forms Gram tile rw (< 3) of chunk it + 1.
+        const int rw = wave - (NSW + DK / 16);
+        // their work is a chain of dependent MFMA products: issue it ahead of the other waves
+        __builtin_amdgcn_s_setprio(3);
+        for (int it = -1; it < nchunks; ++it) {
+            char *const sm = smem + opaque_s(0);
+            const int lane = lane_id();
+            if (it >= 0 && rw < 2) diag_inverse(sm, rw, it, lane);
+            lds_barrier();
+            lds_barrier();
+            if (it + 1 < nchunks && rw < 3) gram_tile(sm, rw, it + 1, lane);
+            lds_barrier();
+        }
+    } else if (is_scan) {
         // ============================== scan waves ==============================
         // Lane (lq, lr) of scan wave w owns value columns c(jt) = SWC w + JT lr + jt (jt < JT),
         // adjacent in memory, so V, o and S move as JT-element groups.
@@ -422,7 +555,6 @@ chunk32_kernel(const ChunkParams p) {
         float Fw[4][2], Bw[4][2];        // decay products within the 4-row group: through row i / after row i
         float kh[2][4], gl[2];           // (e^{G_last-G} K)^T entries and Gamma_last, from P2 to P3
         float qtv[4][2];                 // Gamma * q of this thread's rows, from P2 to P3
-        float lw[4] = {0.f, 0.f, 0.f, 0.f};   // diagonal Gram block (waves 0, 1), from P3 to the next segment 1
 
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
@@ -461,65 +593,7 @@ chunk32_kernel(const ChunkParams p) {
                 // would then wait for the loads right here to copy them over.
                 prefetch(min(nxt + 1, nchunks - 1));
             }
-            if (it >= 0 && pw < 2) {
-                // Diagonal block a = pw of chunk it: M = (I + N)^{-1} for the strictly lower N this
-                // wave's Gram tile left in lw (row lr, columns 4 lq + e) one segment ago, as
-                //     M = (I + X)(I + X^2)(I + X^4)(I + X^8),  X = -N,  N^16 = 0,
-                // with 16x16 MFMA products held in registers (five dependent levels instead of a
-                // 16-step substitution; hi/lo bf16 operands, or fp32 MFMA for fp32 inputs).  -T_aa = -M Diag(beta_a)
-                // (and -M11) -> TM, read by stage b in segment 2.
-                const int a = pw;
-                float *zt = reinterpret_cast<float *>(sm + L::ZT) + a * TSZ;
-                const float *beta_it = reinterpret_cast<const float *>(sm + L::BETA) + (it & 1) * 32;
-                // forms of a 16x16 Z held by lane (lq, lr): "A" = Z[lr][4 lq + e], "B" = Z[4 lq + e][lr]
-#pragma unroll
-                for (int e = 0; e < 4; ++e) zt[(4 * lq + e) * TP + lr] = lw[e];
-                wave_lds_sync();
-                const float4 nb4 = *reinterpret_cast<const float4 *>(zt + lr * TP + 4 * lq);
-                const f32x4_t XA = {-lw[0], -lw[1], -lw[2], -lw[3]}, XB = {-nb4.x, -nb4.y, -nb4.z, -nb4.w};
-                // (Z W) in B form = mm(Z_A, W_B); in A form = mm(W_B, Z_A)
-                auto mm = [](const f32x4_t &za, const f32x4_t &wb) {
-                    f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-                    if constexpr (F32P) {
-#pragma unroll
-                        for (int kk = 0; kk < 4; ++kk) d = mfma_f32(za[kk], wb[kk], d);
-                    } else {
-                        // hi/lo bf16 split in two 16x16x32 MFMAs: K-slots 0..15 carry the hi parts and
-                        // 16..31 the lo parts of Z, so [Zh Zl][Wh; Wh] + [Zh Zh][Wl; 0] = Zh Wh + Zl Wh + Zh Wl
-                        uint32_t zh[2], zl[2], wh[2], wl[2];
-                        split_hl2(za[0], za[1], zh[0], zl[0]);
-                        split_hl2(za[2], za[3], zh[1], zl[1]);
-                        split_hl2(wb[0], wb[1], wh[0], wl[0]);
-                        split_hl2(wb[2], wb[3], wh[1], wl[1]);
-                        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, (uint4){zh[0], zh[1], zl[0], zl[1]});
-                        const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, (uint4){wh[0], wh[1], wh[0], wh[1]});
-                        const bf16x8_t a2 = __builtin_bit_cast(bf16x8_t, (uint4){zh[0], zh[1], zh[0], zh[1]});
-                        const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, (uint4){wl[0], wl[1], 0u, 0u});
-                        d = mfma_bf16(a1, b1, d);
-                        d = mfma_bf16(a2, b2, d);
-                    }
-                    return d;
-                };
-                const f32x4_t X2B = mm(XA, XB), X2A = mm(XB, XA);
-                const f32x4_t X4B = mm(X2A, X2B), X4A = mm(X2B, X2A), X3A = mm(X2B, XA);
-                const f32x4_t X8B = mm(X4A, X4B);
-                const f32x4_t X12B = mm(X4A, X8B);
-                f32x4_t P1A, P2B;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float id = (4 * lq + e == lr) ? 1.f : 0.f;
-                    P1A[e] = id + XA[e] + X2A[e] + X3A[e];     // I + X + X^2 + X^3
-                    P2B[e] = id + X4B[e] + X8B[e] + X12B[e];   // I + X^4 + X^8 + X^12
-                }
-                const f32x4_t MA = mm(P2B, P1A);                // M = P1 P2, A form: M[lr][4 lq + e]
-                const float4 b4 = *reinterpret_cast<const float4 *>(beta_it + 16 * a + 4 * lq);
-                const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
-                float tv[4], nm[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { tv[e] = -(MA[e] * bv[e]); nm[e] = -MA[e]; }
-                M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * a + 4 * lq), tv);
-                if (a == 1) M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 + lr, 4 * lq), nm);
-            }
+            if (NRW == 0 && it >= 0 && pw < 2) diag_inverse(sm, pw, it, lane);
             lds_barrier();
 
             // ---- seg 2, P2(nxt): decayed operands
@@ -577,11 +651,7 @@ chunk32_kernel(const ChunkParams p) {
             }
             lds_barrier();
 
-            // ---- seg 3, P3(nxt): Gram tiles, T00, [-M11 T11], A10, A_qk
-            // Prep wave pw < 3 takes one Kn block and forms both Gram tiles that share it:
-            //   pw 0: tile (0,0)  A_kk -> M00 -> T00      and A_qk(0,0)
-            //   pw 1: tile (1,1)  A_kk -> M11 -> T11, -M11 and A_qk(1,1)
-            //   pw 2: tile (1,0)  A10                     and A_qk(1,0)
+            // ---- seg 3, P3(nxt): Khat^T, Gamma_last, Gamma*Q, -V; Gram tiles (here or on the scan waves)
             if (have) {
                 // (e^{G_last-G} K)^T and Gamma_last of chunk nxt, read by stage c in segment 3 of the
                 // next iteration (double-buffered: stage c of chunk it reads the other buffer now).
@@ -604,38 +674,7 @@ chunk32_kernel(const ChunkParams p) {
                         4 * rgp + i < nv ? make_float2(-PR::lo(vn_[i]), -PR::hi(vn_[i])) : make_float2(0.f, 0.f);
                 vfetch(min(nxt + 1, nchunks - 1));
             }
-            if (have && pw < 3) {
-                const int knb = pw == 0 ? 0 : (pw == 1 ? 2 : 1);
-                const int a = pw == 0 ? 0 : 1, b = pw == 1 ? 1 : 0;
-                f32x4_t gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
-#pragma unroll
-                for (int s = 0; s < KB; ++s) {
-                    const F fn = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(knb, s, lane));
-                    const F fk = M::template get<true>(sm + L::KS, L::SQ_PLANE, fbase<KB>(a, s, lane));
-                    const F fq = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(a, s, lane));
-                    mma<true, true>(gk, fn, fk);
-                    mma<true, true>(gq, fn, fq);
-                }
-                // lane holds tile element (16 a + lr, 16 b + 4 lq + e)
-                {
-                    float w[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = (b < a || 4 * lq + e <= lr) ? gq[e] : 0.f;
-                    M::template put_hl<4>(sm + L::AQK, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * b + 4 * lq), w);
-                }
-                const float br = s_beta[16 * a + lr];
-                if (pw == 2) {
-                    float w[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = br * gk[e];
-                    M::template put_hl<4>(sm + L::AW, L::AW_PLANE, fofs<1>(lr, 4 * lq), w);
-                } else {
-                    // strictly lower part of A_kk(a, a) with beta-scaled rows, kept for the inversion
-                    // in segment 1 of the next iteration (this lane: row lr, columns 4 lq + e)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) lw[e] = 4 * lq + e < lr ? br * gk[e] : 0.f;
-                }
-            }
+            if (NRW == 0 && have && pw < 3) gram_tile(sm, pw, nxt, lane);
             lds_barrier();
         }
     }
