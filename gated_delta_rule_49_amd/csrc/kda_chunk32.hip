@@ -41,8 +41,11 @@
 // are masked where used).
 //
 // Precision: hi+lo bf16 operand pairs on every product feeding the outputs
-// except (Gamma*K) S, fp32 accumulation, fp32 o and S.  The fp32-input
-// instantiation uses fp32 MFMA throughout.
+// except (Gamma*K) S and the KS side of A_kk (single bf16 there), fp32
+// accumulation, fp32 o and S.  The fp32-input instantiation uses fp32 MFMA
+// throughout.
+#include <type_traits>
+
 #include "kda_frag.h"
 
 namespace kda {
@@ -53,8 +56,8 @@ template <int DK, int NSW, int JT, bool F32P, typename IN_T>
 struct Lds32 {
     static constexpr int ES = Mat<F32P>::ES;
     // operands of a chunk, written by the prep waves, read by the scan waves
-    static constexpr int KS = 0;                          // [32][DK] hl: K * e^{G - G_ref}
-    static constexpr int QS = KS + 32 * DK * 4;           // [32][DK] hl: Q * e^{G - G_ref}
+    static constexpr int KS = 0;                          // [32][DK] single: K * e^{G - G_ref}
+    static constexpr int QS = KS + 32 * DK * ES;          // [32][DK] hl: Q * e^{G - G_ref}
     static constexpr int SQ_PLANE = 32 * DK * ES;
     // rows 16..31 only of the next two (rows 0..15 of Gamma*K and Gamma*Q are those of KS and QS);
     // addressed with the 32-row offsets from a base moved back by 16 rows (QT_AT, KG_AT)
@@ -196,21 +199,16 @@ chunk32_kernel(const ChunkParams p) {
     const IN_T *kg = reinterpret_cast<const IN_T *>(p.k);
     const IN_T *vg = reinterpret_cast<const IN_T *>(p.v);
 
-    // Diagonal block a of chunk ch: M = (I + N)^{-1} for the strictly lower, beta-scaled N that the
-    // Gram tile left in ZR / ZT, as
+    // Diagonal block a of chunk ch: M = (I + N)^{-1} for the strictly lower, beta-scaled N, given
+    // as NA = N[lr][4 lq + e] ("A" form) and NB = N[4 lq + e][lr] ("B" form), as
     //     M = (I + X)(I + X^2)(I + X^4)(I + X^8),  X = -N,  N^16 = 0,
     // with 16x16 MFMA products held in registers (five dependent levels instead of a 16-step
     // substitution; hi/lo bf16 operands, or fp32 MFMA for fp32 inputs).  -T_aa = -M Diag(beta_a)
     // (and -M11) -> TM, read by stage b in segment 2.
-    auto diag_inverse = [&](char *sm, int a, int ch, int lane) {
+    auto diag_inverse = [&](char *sm, int a, int ch, int lane, const f32x4_t &NA, const f32x4_t &NB) {
         const int lr = lane & 15, lq = lane >> 4;
-        const float *zr = reinterpret_cast<const float *>(sm + L::ZR) + a * TSZ;
-        const float *zt = reinterpret_cast<const float *>(sm + L::ZT) + a * TSZ;
         const float *beta_ch = reinterpret_cast<const float *>(sm + L::BETA) + (ch & 1) * 32;
-        // forms of a 16x16 Z held by lane (lq, lr): "A" = Z[lr][4 lq + e], "B" = Z[4 lq + e][lr]
-        const float4 na4 = *reinterpret_cast<const float4 *>(zr + lr * TP + 4 * lq);
-        const float4 nb4 = *reinterpret_cast<const float4 *>(zt + lr * TP + 4 * lq);
-        const f32x4_t XA = {-na4.x, -na4.y, -na4.z, -na4.w}, XB = {-nb4.x, -nb4.y, -nb4.z, -nb4.w};
+        const f32x4_t XA = {-NA[0], -NA[1], -NA[2], -NA[3]}, XB = {-NB[0], -NB[1], -NB[2], -NB[3]};
         // (Z W) in B form = mm(Z_A, W_B); in A form = mm(W_B, Z_A)
         auto mm = [](const f32x4_t &za, const f32x4_t &wb) {
             f32x4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -255,7 +253,69 @@ chunk32_kernel(const ChunkParams p) {
         if (a == 1) M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 + lr, 4 * lq), nm);
     };
 
-    // Gram tile t of chunk ch, from the Kn block it shares with the A_qk tile of the same place:
+    // Gram product of Kn block knb (16 rows) with rows 16 a .. 16 a + 15 of KS (or QS): lane holds
+    // element (row 16 a + lr, Kn row 4 lq + e) of the tile
+    // (one accumulator per K-step: the MFMA chains stay short)
+    auto gram_prod = [&](char *sm, int knb, int a, bool use_q, int lane) {
+        f32x4_t acc[KB];
+#pragma unroll
+        for (int s = 0; s < KB; ++s) {
+            const F fn = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(knb, s, lane));
+            acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (use_q) mma<true, true>(acc[s], fn, M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(a, s, lane)));
+            else mma<true, false>(acc[s], fn, M::template get<false>(sm + L::KS, 0, fbase<KB>(a, s, lane)));
+        }
+#pragma unroll
+        for (int s = 1; s < KB; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[0][e] += acc[s][e];
+        return acc[0];
+    };
+    // The same product of Kn block knb with KS rows 16 a .. 16 a + 15 in both orientations: gA as
+    // gram_prod, gB[e] = element (row 16 a + 4 lq + e, Kn row lr) (operands swapped)
+    auto gram_prod_ab = [&](char *sm, int knb, int a, int lane, f32x4_t &gA, f32x4_t &gB) {
+        f32x4_t accA[KB], accB[KB];
+#pragma unroll
+        for (int s = 0; s < KB; ++s) {
+            const F fn = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(knb, s, lane));
+            const F fx = M::template get<false>(sm + L::KS, 0, fbase<KB>(a, s, lane));
+            accA[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            accB[s] = accA[s];
+            mma<true, false>(accA[s], fn, fx);
+            mma<false, true>(accB[s], fx, fn);
+        }
+#pragma unroll
+        for (int s = 1; s < KB; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                accA[0][e] += accA[s][e];
+                accB[0][e] += accB[s][e];
+            }
+        gA = accA[0];
+        gB = accB[0];
+    };
+    // A_qk tile (a, b) (lower incl. diagonal on the diagonal tiles) -> AQK
+    auto store_aqk = [&](char *sm, int a, int b, const f32x4_t &gq, int lane) {
+        const int lr = lane & 15, lq = lane >> 4;
+        float w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (b < a || 4 * lq + e <= lr) ? gq[e] : 0.f;
+        M::template put_hl<4>(sm + L::AQK, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * b + 4 * lq), w);
+    };
+    // beta-scaled rows of a Gram tile of sub-chunk a of chunk ch (row lr of the lane)
+    auto beta_row = [&](char *sm, int a, int ch, int lane) {
+        return reinterpret_cast<const float *>(sm + L::BETA)[(ch & 1) * 32 + 16 * a + (lane & 15)];
+    };
+    // strictly lower part of a diagonal A_kk tile with beta-scaled rows (A form)
+    auto strict_lower = [&](const f32x4_t &gk, float br, int lane) {
+        const int lr = lane & 15, lq = lane >> 4;
+        f32x4_t z;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = 4 * lq + e < lr ? br * gk[e] : 0.f;
+        return z;
+    };
+    // Gram tile t of chunk ch, from the Kn block it shares with the A_qk tile of the same place
+    // (the waves that invert the diagonal blocks run in a later segment and read ZR / ZT):
     //   t 0: tile (0,0)  A_kk -> ZR/ZT block 0   and A_qk(0,0)
     //   t 1: tile (1,1)  A_kk -> ZR/ZT block 1   and A_qk(1,1)
     //   t 2: tile (1,0)  A10 -> AW               and A_qk(1,0)
@@ -263,59 +323,74 @@ chunk32_kernel(const ChunkParams p) {
         const int lr = lane & 15, lq = lane >> 4;
         const int knb = t == 0 ? 0 : (t == 1 ? 2 : 1);
         const int a = t == 0 ? 0 : 1, b = t == 1 ? 1 : 0;
-        f32x4_t gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
-#pragma unroll
-        for (int s = 0; s < KB; ++s) {
-            const F fn = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(knb, s, lane));
-            const F fk = M::template get<true>(sm + L::KS, L::SQ_PLANE, fbase<KB>(a, s, lane));
-            const F fq = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(a, s, lane));
-            mma<true, true>(gk, fn, fk);
-            mma<true, true>(gq, fn, fq);
-        }
-        // lane holds tile element (16 a + lr, 16 b + 4 lq + e)
-        {
-            float w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = (b < a || 4 * lq + e <= lr) ? gq[e] : 0.f;
-            M::template put_hl<4>(sm + L::AQK, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * b + 4 * lq), w);
-        }
-        const float br = reinterpret_cast<const float *>(sm + L::BETA)[(ch & 1) * 32 + 16 * a + lr];
+        const f32x4_t gk = gram_prod(sm, knb, a, false, lane);
+        store_aqk(sm, a, b, gram_prod(sm, knb, a, true, lane), lane);
+        const float br = beta_row(sm, a, ch, lane);
         if (t == 2) {
             float w[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = br * gk[e];
             M::template put_hl<4>(sm + L::AW, L::AW_PLANE, fofs<1>(lr, 4 * lq), w);
         } else {
-            // strictly lower part of A_kk(a, a) with beta-scaled rows (row lr, columns 4 lq + e)
-            float4 z;
-            z.x = 4 * lq + 0 < lr ? br * gk[0] : 0.f;
-            z.y = 4 * lq + 1 < lr ? br * gk[1] : 0.f;
-            z.z = 4 * lq + 2 < lr ? br * gk[2] : 0.f;
-            z.w = 4 * lq + 3 < lr ? br * gk[3] : 0.f;
+            const f32x4_t z = strict_lower(gk, br, lane);
             float *zr = reinterpret_cast<float *>(sm + L::ZR) + t * TSZ;
             float *zt = reinterpret_cast<float *>(sm + L::ZT) + t * TSZ;
-            *reinterpret_cast<float4 *>(zr + lr * TP + 4 * lq) = z;
-            zt[(4 * lq + 0) * TP + lr] = z.x;
-            zt[(4 * lq + 1) * TP + lr] = z.y;
-            zt[(4 * lq + 2) * TP + lr] = z.z;
-            zt[(4 * lq + 3) * TP + lr] = z.w;
+            *reinterpret_cast<float4 *>(zr + lr * TP + 4 * lq) = make_float4(z[0], z[1], z[2], z[3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zt[(4 * lq + e) * TP + lr] = z[e];
         }
+    };
+    // the inverse of diagonal block a of chunk ch from the tile gram_tile left in ZR / ZT
+    auto diag_inverse_lds = [&](char *sm, int a, int ch, int lane) {
+        const int lr = lane & 15, lq = lane >> 4;
+        const float4 na4 = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(sm + L::ZR) + a * TSZ + lr * TP + 4 * lq);
+        const float4 nb4 = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(sm + L::ZT) + a * TSZ + lr * TP + 4 * lq);
+        diag_inverse(sm, a, ch, lane, f32x4_t{na4.x, na4.y, na4.z, na4.w}, f32x4_t{nb4.x, nb4.y, nb4.z, nb4.w});
     };
 
     if (NRW > 0 && is_role) {
         // ============================== role waves ==============================
-        // wave rw: segment 1 of iteration it inverts diagonal block rw (< 2) of chunk it, segment 3
-        // forms Gram tile rw (< 3) of chunk it + 1.
+        // In segment 3 of iteration it, the operands of chunk it + 1 being in LDS, wave rw forms
+        //   rw 0, 1: A_kk(rw, rw), then inverts diagonal block rw -> TM
+        //   rw 2:    A_qk(0,0), A_qk(1,1)
+        //   rw 3:    A10 -> AW, A_qk(1,0)
         const int rw = wave - (NSW + DK / 16);
         // their work is a chain of dependent MFMA products: issue it ahead of the other waves
         __builtin_amdgcn_s_setprio(3);
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
-            const int lane = lane_id();
-            if (it >= 0 && rw < 2) diag_inverse(sm, rw, it, lane);
+            const int lane = lane_id(), lr = lane & 15, lq = lane >> 4;
             lds_barrier();
             lds_barrier();
-            if (it + 1 < nchunks && rw < 3) gram_tile(sm, rw, it + 1, lane);
+            const int ch = it + 1;
+            if (ch < nchunks) {
+                if (rw < 2) {
+                    // A_kk(rw, rw) with beta-scaled rows, strictly lower, in both forms
+                    f32x4_t gA, gB, z, zb;
+                    gram_prod_ab(sm, rw == 0 ? 0 : 2, rw, lane, gA, gB);
+                    const float *bt = reinterpret_cast<const float *>(sm + L::BETA) + (ch & 1) * 32 + 16 * rw;
+                    const float br = bt[lr];
+                    const float4 bc = *reinterpret_cast<const float4 *>(bt + 4 * lq);
+                    const float bcv[4] = {bc.x, bc.y, bc.z, bc.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        z[e] = 4 * lq + e < lr ? br * gA[e] : 0.f;          // (lr, 4 lq + e)
+                        zb[e] = lr < 4 * lq + e ? bcv[e] * gB[e] : 0.f;     // (4 lq + e, lr)
+                    }
+                    diag_inverse(sm, rw, ch, lane, z, zb);
+                } else if (rw == 2) {
+                    store_aqk(sm, 0, 0, gram_prod(sm, 0, 0, true, lane), lane);
+                    store_aqk(sm, 1, 1, gram_prod(sm, 2, 1, true, lane), lane);
+                } else {
+                    const f32x4_t gk = gram_prod(sm, 1, 1, false, lane);
+                    const float br = beta_row(sm, 1, ch, lane);
+                    float w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = br * gk[e];
+                    M::template put_hl<4>(sm + L::AW, L::AW_PLANE, fofs<1>(lr, 4 * lq), w);
+                    store_aqk(sm, 1, 0, gram_prod(sm, 1, 1, true, lane), lane);
+                }
+            }
             lds_barrier();
         }
     } else if (is_scan) {
@@ -593,41 +668,42 @@ chunk32_kernel(const ChunkParams p) {
                 // would then wait for the loads right here to copy them over.
                 prefetch(min(nxt + 1, nchunks - 1));
             }
-            if (NRW == 0 && it >= 0 && pw < 2) diag_inverse(sm, pw, it, lane);
+            if (NRW == 0 && it >= 0 && pw < 2) diag_inverse_lds(sm, pw, it, lane);
             lds_barrier();
 
             // ---- seg 2, P2(nxt): decayed operands
-            if (have) {
+            // (sub-chunk SA and group GI of this thread's rows: compile-time constants where a wave
+            // holds one row group, so the selections below fold away)
+            auto p2 = [&](auto sa_c, auto gi_c) {
+                const int SA = sa_c, GI = gi_c;
                 // group products of this sub-chunk (xs) and of the other one (xo)
                 float xs[4][2], xo[2] = {1.f, 1.f};
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const float2 a2 = *reinterpret_cast<const float2 *>(s_xchg + (4 * sa + m) * DK + c0);
-                    const float2 o2 = *reinterpret_cast<const float2 *>(s_xchg + (4 * (1 - sa) + m) * DK + c0);
+                    const float2 a2 = *reinterpret_cast<const float2 *>(s_xchg + (4 * SA + m) * DK + c0);
+                    const float2 o2 = *reinterpret_cast<const float2 *>(s_xchg + (4 * (1 - SA) + m) * DK + c0);
                     xs[m][0] = a2.x; xs[m][1] = a2.y;
                     xo[0] *= o2.x; xo[1] *= o2.y;
                 }
-                float lead[2], tail[2], P0[2], P1[2], post[2], dgf[2], pre[2];
+                float lead[2], tail[2], P0[2], P1[2], dgf[2];
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    lead[c] = gi > 0 ? xs[0][c] : 1.f;
-                    if (gi > 1) lead[c] *= xs[1][c];
-                    if (gi > 2) lead[c] *= xs[2][c];
-                    tail[c] = gi < 3 ? xs[3][c] : 1.f;
-                    if (gi < 2) tail[c] *= xs[2][c];
-                    if (gi < 1) tail[c] *= xs[1][c];
+                    lead[c] = 1.f;   // decay from the sub-chunk start to this group
+                    tail[c] = 1.f;   // decay from the end of this group to the sub-chunk end
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        if (m < GI) lead[c] *= xs[m][c];
+                        if (m > GI) tail[c] *= xs[m][c];
+                    }
                     const float psub = (xs[0][c] * xs[1][c]) * (xs[2][c] * xs[3][c]);
-                    P0[c] = sa ? xo[c] : psub;
-                    P1[c] = sa ? psub : xo[c];
-                    post[c] = sa ? 1.f : P1[c];                       // decay from the end of this sub-chunk to the chunk end
-                    pre[c] = sa ? P0[c] : 1.f;                        // decay from the chunk start to this sub-chunk
-                    dgf[c] = __builtin_amdgcn_rcpf(sa ? P1[c] : P0[c]);   // column factor of the diagonal Gram tile
+                    P0[c] = SA ? xo[c] : psub;
+                    P1[c] = SA ? psub : xo[c];
+                    dgf[c] = __builtin_amdgcn_rcpf(SA ? P1[c] : P0[c]);   // column factor of the diagonal Gram tile
                 }
                 gl[0] = P0[0] * P1[0];
                 gl[1] = P0[1] * P1[1];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * rgp + i, rl = r - 16 * sa;
                     float ks[2], qs[2], ke[2], kd[2];
                     const float kv[2] = {PR::lo(kr[i]), PR::hi(kr[i])}, qv[2] = {PR::lo(qr[i]), PR::hi(qr[i])};
 #pragma unroll
@@ -636,17 +712,36 @@ chunk32_kernel(const ChunkParams p) {
                         const float ee = Bw[i][c] * tail[c];   // e^{G_end(sub-chunk) - G_r}
                         ks[c] = kv[c] * es;
                         qs[c] = qv[c] * es;
-                        qtv[i][c] = qs[c] * pre[c];            // Gamma * q (decay from the chunk start)
                         ke[c] = kv[c] * ee;
                         kd[c] = ke[c] * dgf[c];
-                        kh[c][i] = ke[c] * post[c];
+                        // (e^{G_last-G} K)^T entry: sub-chunk 0 decays on through sub-chunk 1
+                        kh[c][i] = SA ? ke[c] : ke[c] * P1[c];
+                        if (SA) qtv[i][c] = qs[c] * P0[c];    // Gamma * q (decay from the chunk start)
                     }
-                    M::template put_hl<2>(sm + L::KS, L::SQ_PLANE, ks_off[i], ks);
+                    M::put_h2(sm + L::KS, ks_off[i], ks[0], ks[1]);
                     M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, ks_off[i], qs);
                     // Kn rows: sub-chunk 0 feeds tiles (0,0) [x 1/P0] and (1,0) [x 1]; sub-chunk 1 feeds (1,1) [x 1/P1]
                     M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn_off[i], kd);
-                    if (sa == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn2_off[i], ke);
-                    else M::put_h2(sm + L::KG_AT, ks_off[i], ks[0] * pre[0], ks[1] * pre[1]);   // Gamma * K
+                    if (SA == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn2_off[i], ke);
+                    else M::put_h2(sm + L::KG_AT, ks_off[i], ks[0] * P0[0], ks[1] * P0[1]);   // Gamma * K
+                }
+            };
+            if (have) {
+                if constexpr (NCP >= 64) {
+                    using Z = std::integral_constant<int, 0>;
+                    using O = std::integral_constant<int, 1>;
+                    switch (rgp) {
+                        case 0: p2(Z{}, Z{}); break;
+                        case 1: p2(Z{}, O{}); break;
+                        case 2: p2(Z{}, std::integral_constant<int, 2>{}); break;
+                        case 3: p2(Z{}, std::integral_constant<int, 3>{}); break;
+                        case 4: p2(O{}, Z{}); break;
+                        case 5: p2(O{}, O{}); break;
+                        case 6: p2(O{}, std::integral_constant<int, 2>{}); break;
+                        default: p2(O{}, std::integral_constant<int, 3>{}); break;
+                    }
+                } else {
+                    p2(sa, gi);
                 }
             }
             lds_barrier();
