@@ -571,7 +571,8 @@ chunk32_kernel(const ChunkParams p) {
         const int cp = pt % NCP, c0 = 2 * cp;
         // the 4-row group is uniform across a wave when a wave covers one group (DK = 128)
         const int rgp = NCP >= 64 ? __builtin_amdgcn_readfirstlane(pt / NCP) : pt / NCP;
-        const int sa = rgp >> 2, gi = rgp & 3;
+        // the sub-chunk is wave-uniform either way (with DK = 64 a wave holds groups 2 pw, 2 pw + 1)
+        const int sa = __builtin_amdgcn_readfirstlane(rgp >> 2), gi = rgp & 3;
         const int lane = pt & 63, lr = lane & 15, lq = lane >> 4;
         // per-thread LDS element offsets and input row offsets, fixed for the whole sequence
         int ks_off[4], kn_off[4], kn2_off[4], vb_off[4];
@@ -741,7 +742,9 @@ chunk32_kernel(const ChunkParams p) {
                         default: p2(O{}, std::integral_constant<int, 3>{}); break;
                     }
                 } else {
-                    p2(sa, gi);
+                    // (a wave's rows share their sub-chunk: dispatch on it, the group stays per lane)
+                    if (sa) p2(std::integral_constant<int, 1>{}, gi);
+                    else p2(std::integral_constant<int, 0>{}, gi);
                 }
             }
             lds_barrier();

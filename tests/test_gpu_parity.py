@@ -106,11 +106,12 @@ def test_prefill_varlen_ragged(d, dtype, chunk):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_prefill_many_chains_one_workgroup_each(d):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_many_chains_one_workgroup_each(d, dtype):
     # 4 x 40 = 160 (sequence, head) chains: more than half the compute units, so the chunk-32
     # launch gives each chain a single workgroup (fewer chains split the value columns over two)
-    w = W.make_prefill([100, 37, 64, 65], 40, d, d, "bf16", seed=9, s0_std=0.1, checkpoint_every=64)
-    compare(w, label=f"many chains d={d}", chunk=32)
+    w = W.make_prefill([100, 37, 64, 65], 40, d, d, dtype, seed=9, s0_std=0.1, checkpoint_every=64)
+    compare(w, label=f"many chains d={d} {dtype}", chunk=32)
 
 
 @pytest.mark.parametrize("gate", ["min", "zero", "slow"])
