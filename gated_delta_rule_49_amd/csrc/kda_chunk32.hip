@@ -202,7 +202,7 @@ chunk32_kernel(const ChunkParams p) {
     // Diagonal block a of chunk ch: M = (I + N)^{-1} for the strictly lower, beta-scaled N, given
     // as NA = N[lr][4 lq + e] ("A" form) and NB = N[4 lq + e][lr] ("B" form), as
     //     M = (I + X)(I + X^2)(I + X^4)(I + X^8),  X = -N,  N^16 = 0,
-    // with 16x16 MFMA products held in registers (five dependent levels instead of a 16-step
+    // with 16x16 MFMA products held in registers (four dependent levels instead of a 16-step
     // substitution; hi/lo bf16 operands, or fp32 MFMA for fp32 inputs).  -T_aa = -M Diag(beta_a)
     // (and -M11) -> TM, read by stage b in segment 2.
     auto diag_inverse = [&](char *sm, int a, int ch, int lane, const f32x4_t &NA, const f32x4_t &NB) {
@@ -232,18 +232,24 @@ chunk32_kernel(const ChunkParams p) {
             }
             return d;
         };
-        const f32x4_t X2B = mm(XA, XB), X2A = mm(XB, XA);
-        const f32x4_t X4B = mm(X2A, X2B), X4A = mm(X2B, X2A), X3A = mm(X2B, XA);
-        const f32x4_t X8B = mm(X4A, X4B);
-        const f32x4_t X12B = mm(X4A, X8B);
-        f32x4_t P1A, P2B;
+        // M = A1 (I + X^2)(I + X^4)(I + X^8) with A1 = I + X, each factor applied as A += A X^(2^k):
+        // four dependent levels of products
+        f32x4_t A1A;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float id = (4 * lq + e == lr) ? 1.f : 0.f;
-            P1A[e] = id + XA[e] + X2A[e] + X3A[e];     // I + X + X^2 + X^3
-            P2B[e] = id + X4B[e] + X8B[e] + X12B[e];   // I + X^4 + X^8 + X^12
-        }
-        const f32x4_t MA = mm(P2B, P1A);                // M = P1 P2, A form: M[lr][4 lq + e]
+        for (int e = 0; e < 4; ++e) A1A[e] = ((4 * lq + e == lr) ? 1.f : 0.f) + XA[e];
+        const f32x4_t X2B = mm(XA, XB), X2A = mm(XB, XA);
+        const f32x4_t X4B = mm(X2A, X2B), X4A = mm(X2B, X2A), Y2A = mm(X2B, A1A);
+        f32x4_t A2A;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) A2A[e] = A1A[e] + Y2A[e];
+        const f32x4_t X8B = mm(X4A, X4B), Y3A = mm(X4B, A2A);
+        f32x4_t A3A;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) A3A[e] = A2A[e] + Y3A[e];
+        const f32x4_t Y4A = mm(X8B, A3A);
+        f32x4_t MA;                                      // A form: M[lr][4 lq + e]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) MA[e] = A3A[e] + Y4A[e];
         const float4 b4 = *reinterpret_cast<const float4 *>(beta_ch + 16 * a + 4 * lq);
         const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
         float tv[4], nm[4];
