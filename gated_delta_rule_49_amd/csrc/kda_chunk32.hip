@@ -503,10 +503,11 @@ chunk32_kernel(const ChunkParams p) {
                     for (int jt = 0; jt < JT; ++jt) mma<true, true>(acc[jt], fa, UF[jt]);
                     // chunk base in scalar registers, 32-bit per-lane offsets
                     float *const obase = p.o + ((size_t)t0 * H + h) * DV + col0;
+                    const bool full = nv == C32;   // (uniform) no row past the end
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 16 * rt + 4 * lq + e;
-                        if (r < nv) {
+                        if (full || r < nv) {
                             float x[JT];
 #pragma unroll
                             for (int jt = 0; jt < JT; ++jt) x[jt] = p.scale * acc[jt][e];
@@ -785,19 +786,6 @@ chunk32_kernel(const ChunkParams p) {
 }
 
 }  // namespace kda
-
-// Compute units of the current device (queried once per device).
-static int kda_cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        cached[dev] = cus;
-    }
-    return cached[dev];
-}
 
 extern "C" __attribute__((visibility("hidden"))) hipError_t
 kda_launch_chunk32(int dk, int in_bf16, unsigned chains, const kda::ChunkParams &p, hipStream_t stream) {

@@ -78,3 +78,16 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, const f32x4_t &c) 
 }
 
 }  // namespace kda
+
+// Compute units of the current device (host side; queried once per device).
+inline int kda_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}

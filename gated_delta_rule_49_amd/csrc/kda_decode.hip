@@ -11,106 +11,120 @@
 // matrix-vector pass bound by memory bandwidth).
 //
 // The pass is HBM-bound: each state (d_k*d_v fp32) is read once and written
-// once.  One workgroup owns one (n, h) state and holds it in registers between
-// the column reductions and the update, so S crosses HBM exactly twice.
+// once.  A workgroup holds a state in registers between the column reductions
+// and the update, so S crosses HBM exactly twice.  Workgroups are persistent
+// (one per compute unit, or fewer states) and walk the (n, h) states with a
+// stride of the grid, loading the next state while they reduce and write back
+// the current one, so every compute unit keeps reads in flight throughout.
 // Thread t owns 4 consecutive columns (float4) of every RG-th row: a wave's
-// loads cover whole 512-byte rows and are fully coalesced.
+// loads cover whole rows and are fully coalesced.
 #include "kda_common.h"
 
 namespace kda {
 
-constexpr int DEC_THREADS = 256;
+constexpr int DEC_THREADS = 1024;
 
 template <int DK, int DV, typename IN_T>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_kernel(const IN_T *__restrict__ q, const IN_T *__restrict__ k, const IN_T *__restrict__ v,
               const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
-              float *__restrict__ o, int H, float scale) {
+              float *__restrict__ o, int NH, float scale) {
     constexpr int CG = DV / 4;                 // column groups (float4 each)
     constexpr int RG = DEC_THREADS / CG;       // row groups
     constexpr int RPT = DK / RG;               // rows per thread
     constexpr int NWAVE = DEC_THREADS / 64;
-    static_assert(DK % RG == 0 && CG <= 64, "shape");
+    static_assert(DK % RG == 0 && CG <= 64 && 64 % CG == 0, "shape");
 
-    const int nh = blockIdx.x;                 // n * H + h
     const int t = threadIdx.x;
     const int cg = t % CG, rg = t / CG;
-
-    f32x4_t *S4 = reinterpret_cast<f32x4_t *>(state + (size_t)nh * DK * DV);
-
-    // Issue the state loads first; they dominate the runtime.
-    f32x4_t s[RPT];
-#pragma unroll
-    for (int m = 0; m < RPT; ++m)
-        s[m] = __builtin_nontemporal_load(&S4[(rg + RG * m) * CG + cg]);
 
     __shared__ float s_aq[DK], s_ak[DK], s_al[DK], s_k[DK], s_qk[DK], s_v[DV];
     __shared__ float s_red[NWAVE][CG][9];
 
-    const size_t tok_k = (size_t)nh * DK, tok_v = (size_t)nh * DV;
-    if (t < DK) {
-        const float al = __expf(g[tok_k + t]);
-        const float qi = load_in(q + tok_k + t), ki = load_in(k + tok_k + t);
-        s_al[t] = al;
-        s_aq[t] = al * qi;
-        s_ak[t] = al * ki;
-        s_k[t] = ki;
-        s_qk[t] = qi * ki;
+    int nh = blockIdx.x;                       // n * H + h
+    f32x4_t s[RPT], sn[RPT];                   // this state, the next one
+    {
+        const f32x4_t *S4 = reinterpret_cast<const f32x4_t *>(state + (size_t)nh * DK * DV);
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S4[(rg + RG * m) * CG + cg]);
     }
-    if (t < DV) s_v[t] = load_in(v + tok_v + t);
-    const float b = beta[nh];
-    __syncthreads();
+    for (; nh < NH; nh += gridDim.x) {
+        const int nxt = nh + (int)gridDim.x;
+        if (nxt < NH) {
+            const f32x4_t *S4n = reinterpret_cast<const f32x4_t *>(state + (size_t)nxt * DK * DV);
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) sn[m] = __builtin_nontemporal_load(&S4n[(rg + RG * m) * CG + cg]);
+        }
 
-    float a[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0}, qk = 0.f;
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int i = rg + RG * m;
-        const float aq = s_aq[i], ak = s_ak[i];
-        a[0] += aq * s[m][0]; a[1] += aq * s[m][1]; a[2] += aq * s[m][2]; a[3] += aq * s[m][3];
-        p[0] += ak * s[m][0]; p[1] += ak * s[m][1]; p[2] += ak * s[m][2]; p[3] += ak * s[m][3];
-        qk += s_qk[i];   // every column group sums the same rows; column group 0 is used
-    }
+        const size_t tok_k = (size_t)nh * DK, tok_v = (size_t)nh * DV;
+        if (t < DK) {
+            const float al = __expf(g[tok_k + t]);
+            const float qi = load_in(q + tok_k + t), ki = load_in(k + tok_k + t);
+            s_al[t] = al;
+            s_aq[t] = al * qi;
+            s_ak[t] = al * ki;
+            s_k[t] = ki;
+            s_qk[t] = qi * ki;
+        }
+        if (t < DV) s_v[t] = load_in(v + tok_v + t);
+        const float b = beta[nh];
+        __syncthreads();
 
-    // Reduce the 9 partials across the row groups: first inside the wave
-    // (lanes with equal cg differ by multiples of CG), then across waves.
-    float r9[9] = {a[0], a[1], a[2], a[3], p[0], p[1], p[2], p[3], qk};
+        float a[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0}, qk = 0.f;
 #pragma unroll
-    for (int off = CG; off < 64; off *= 2)
-#pragma unroll
-        for (int j = 0; j < 9; ++j) r9[j] += shfl_xor(r9[j], off);
-    const int wave = t / 64, lane = t % 64;
-    if (lane < CG)
-#pragma unroll
-        for (int j = 0; j < 9; ++j) s_red[wave][lane][j] = r9[j];
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 9; ++j) {
-        float acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) acc += s_red[w][cg][j];
-        r9[j] = acc;
-    }
-    const float qk_all = r9[8];   // every column group summed the same rows of q*k
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + RG * m;
+            const float aq = s_aq[i], ak = s_ak[i];
+            a[0] += aq * s[m][0]; a[1] += aq * s[m][1]; a[2] += aq * s[m][2]; a[3] += aq * s[m][3];
+            p[0] += ak * s[m][0]; p[1] += ak * s[m][1]; p[2] += ak * s[m][2]; p[3] += ak * s[m][3];
+            qk += s_qk[i];   // every column group sums the same rows; column group 0 is used
+        }
 
-    float u[4], ov[4];
+        // Reduce the 9 partials across the row groups: first inside the wave
+        // (lanes with equal cg differ by multiples of CG), then across waves.
+        float r9[9] = {a[0], a[1], a[2], a[3], p[0], p[1], p[2], p[3], qk};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        u[c] = b * (s_v[4 * cg + c] - r9[4 + c]);
-        ov[c] = scale * (r9[c] + qk_all * u[c]);
-    }
-    if (rg == 0)
-        reinterpret_cast<float4 *>(o + tok_v)[cg] = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        for (int off = CG; off < 64; off *= 2)
+#pragma unroll
+            for (int j = 0; j < 9; ++j) r9[j] += shfl_xor(r9[j], off);
+        const int wave = t / 64, lane = t % 64;
+        if (lane < CG)
+#pragma unroll
+            for (int j = 0; j < 9; ++j) s_red[wave][lane][j] = r9[j];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+            float acc = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWAVE; ++w) acc += s_red[w][cg][j];
+            r9[j] = acc;
+        }
+        const float qk_all = r9[8];   // every column group summed the same rows of q*k
 
+        float u[4], ov[4];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int i = rg + RG * m;
-        const float al = s_al[i], ki = s_k[i];
-        f32x4_t r;
-        r[0] = al * s[m][0] + ki * u[0];
-        r[1] = al * s[m][1] + ki * u[1];
-        r[2] = al * s[m][2] + ki * u[2];
-        r[3] = al * s[m][3] + ki * u[3];
-        __builtin_nontemporal_store(r, &S4[i * CG + cg]);
+        for (int c = 0; c < 4; ++c) {
+            u[c] = b * (s_v[4 * cg + c] - r9[4 + c]);
+            ov[c] = scale * (r9[c] + qk_all * u[c]);
+        }
+        if (rg == 0)
+            reinterpret_cast<float4 *>(o + tok_v)[cg] = make_float4(ov[0], ov[1], ov[2], ov[3]);
+
+        f32x4_t *S4 = reinterpret_cast<f32x4_t *>(state + (size_t)nh * DK * DV);
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + RG * m;
+            const float al = s_al[i], ki = s_k[i];
+            f32x4_t r;
+            r[0] = al * s[m][0] + ki * u[0];
+            r[1] = al * s[m][1] + ki * u[1];
+            r[2] = al * s[m][2] + ki * u[2];
+            r[3] = al * s[m][3] + ki * u[3];
+            __builtin_nontemporal_store(r, &S4[i * CG + cg]);
+        }
+        __syncthreads();   // the shared vectors and partials are rewritten for the next state
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) s[m] = sn[m];
     }
 }
 
@@ -120,11 +134,14 @@ decode_kernel(const IN_T *__restrict__ q, const IN_T *__restrict__ k, const IN_T
 extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_decode(int dk, int in_bf16, int N, int H, const void *q, const void *k,
                                         const void *v, const float *g, const float *beta, float *state,
                                         float *o, float scale, hipStream_t stream) {
-    const dim3 grid((unsigned)N * (unsigned)H), block(kda::DEC_THREADS);
-    if (N == 0) return hipSuccess;
+    if (N == 0 || H == 0) return hipSuccess;
+    const long long nh = (long long)N * H;
+    if (nh > 0x7fffffffLL) return hipErrorInvalidValue;
+    // persistent: one workgroup per compute unit (or per state, if fewer)
+    const int grid = (int)(nh < kda_cu_count() ? nh : kda_cu_count());
 #define KDA_DEC(DKV, T)                                                                                \
-    hipLaunchKernelGGL((kda::decode_kernel<DKV, DKV, T>), grid, block, 0, stream, (const T *)q,       \
-                       (const T *)k, (const T *)v, g, beta, state, o, H, scale)
+    hipLaunchKernelGGL((kda::decode_kernel<DKV, DKV, T>), dim3(grid), dim3(kda::DEC_THREADS), 0, stream, \
+                       (const T *)q, (const T *)k, (const T *)v, g, beta, state, o, (int)nh, scale)
     if (dk == 128 && in_bf16) KDA_DEC(128, uint16_t);
     else if (dk == 128) KDA_DEC(128, float);
     else if (dk == 64 && in_bf16) KDA_DEC(64, uint16_t);
