@@ -52,6 +52,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (profiling runs)")
     ap.add_argument("--chunk", type=int, default=32, choices=(32, 64), help="token block of the chunked form")
+    ap.add_argument("--workload", type=int, default=0, choices=(0, 1, 4),
+                    help="instead of the benchmark step, time the prefill of workload 1 (T=4096, H=32) or 4 "
+                         "(64 packed sequences, H=32, checkpoints every 512) and print its own JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scales the HBM byte counters)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
@@ -78,6 +81,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.workload:
+        other_workload(args.workload, args.chunk, args.steps, args.warmup)
         return
 
     import gated_delta_rule_49_amd as kda
@@ -370,6 +376,94 @@ def summarize_trace(trace_dir, bench_json):
                         f"average over the timed steps (same process): {ev_ms} ms.\n\n")
             f.write(f"Command:\n\n    {cmd}\n\nAll kernels of the run:\n\n{table}")
     print("wrote", ", ".join(out))
+
+
+def other_workload(cid, chunk, steps, warmup):
+    """Prefill tokens/s of workload 1 or 4 (one JSON line).  Workload 1 uses the seeded host
+    generator; workload 4 (about 1.85M tokens x 32 heads, ~110 GB with o and checkpoints) is drawn
+    on the device with torch's seeded generator from the same distributions (lengths from the
+    seeded host draw), since only timing, not parity, is taken from it."""
+    import numpy as np
+    import torch
+    import gated_delta_rule_49_amd as kda
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    if cid == 1:
+        w = W.make_config(1)
+        up = lambda x, dt: torch.from_numpy(x).to(dev, dt)
+        q, k, v = up(w.q, bf), up(w.k, bf), up(w.v, bf)
+        g, beta = up(w.g, torch.float32), up(w.beta, torch.float32)
+        seqlens = list(w.seqlens)
+        H, dk, dv = w.H, w.dk, w.dv
+        s0 = None
+        every = 0
+        desc = "prefill T=4096 H=32 d_k=d_v=128 bf16 q/k/v, fp32 g/beta, zero initial state"
+    else:
+        seqlens = W.config4_lengths()
+        H, dk, dv = 32, 128, 128
+        T = int(sum(seqlens))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(20261203)
+        q = torch.empty((T, H, dk), dtype=bf, device=dev)
+        k = torch.empty_like(q)
+        v = torch.empty((T, H, dv), dtype=bf, device=dev)
+        g = torch.empty((T, H, dk), dtype=torch.float32, device=dev)
+        beta = torch.empty((T, H), dtype=torch.float32, device=dev)
+        step = 1 << 16
+        for a in range(0, T, step):
+            b = min(T, a + step)
+            x = torch.randn((b - a, H, dk), generator=gen, device=dev)
+            q[a:b] = (x / x.norm(dim=-1, keepdim=True) * dk ** -0.5).to(bf)
+            x = torch.randn((b - a, H, dk), generator=gen, device=dev)
+            k[a:b] = (x / x.norm(dim=-1, keepdim=True)).to(bf)
+            v[a:b] = torch.randn((b - a, H, dv), generator=gen, device=dev).to(bf)
+            g[a:b] = -5.0 * torch.sigmoid(torch.randn((b - a, H, dk), generator=gen, device=dev))
+            beta[a:b] = torch.sigmoid(torch.randn((b - a, H), generator=gen, device=dev))
+        s0 = 0.1 * torch.randn((len(seqlens), H, dk, dv), generator=gen, device=dev)
+        every = 512
+        desc = (f"varlen prefill, {len(seqlens)} packed sequences (log-uniform 512..131072, T={T}), H=32, "
+                "d_k=d_v=128 bf16 q/k/v, fp32 g/beta, per-sequence initial state, checkpoints every 512")
+    T = int(sum(seqlens))
+    cu_h = torch.tensor([0] + list(np.cumsum(seqlens)), dtype=torch.int32)
+    cu_d = cu_h.to(dev)
+    o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    sf = torch.empty((len(seqlens), H, dk, dv), dtype=torch.float32, device=dev)
+    n_ck = sum(L // every for L in seqlens) if every else 0
+    ck = torch.empty((max(n_ck, 1), H, dk, dv), dtype=torch.float32, device=dev) if n_ck else None
+    A = kda.make_fwd_args(q, k, v, g, beta, cu_d, cu_h, 1.0, s0, sf, every, ck, o, chunk)
+    L = kda.lib()
+    ws = torch.empty(L.kda_chunk_fwd_workspace_bytes(ctypes.byref(A)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def prefill():
+        st = L.kda_chunk_fwd(ctypes.byref(A), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()), sptr)
+        if st != 0:
+            raise RuntimeError(kda.kda_status_str(st))
+
+    for _ in range(warmup):
+        prefill()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        prefill()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = float(np.median(ms))
+    nbytes = prefill_bytes(T, H, dk, dv, with_states=False) + len(seqlens) * H * dk * dv * 4 * (2 if s0 is not None else 1) \
+        + n_ck * H * dk * dv * 4
+    print(json.dumps({
+        "metric": "KDA prefill tokens/s", "workload": desc, "tokens": T, "heads": H, "chunk": chunk,
+        "value": round(T / (med * 1e-3), 1), "unit": "tokens/s", "ms": round(med, 4),
+        "ms_p10": round(float(np.percentile(ms, 10)), 4), "ms_p90": round(float(np.percentile(ms, 90)), 4),
+        "alg_bytes": int(nbytes), "alg_GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "data": "synthetic (seeded)"}), flush=True)
 
 
 def copy_calibration(mib):
