@@ -33,6 +33,8 @@ class KdaFwdArgs(ctypes.Structure):
         ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
         ("initial_state", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
         ("checkpoint_every", ctypes.c_int32), ("checkpoints", ctypes.c_void_p), ("o", ctypes.c_void_p),
+        ("initial_state_indices", ctypes.c_void_p), ("checkpoint_indices", ctypes.c_void_p),
+        ("num_slots", ctypes.c_int32),
     ]
 
 
@@ -42,7 +44,7 @@ class KdaDecodeArgs(ctypes.Structure):
         ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("state", ctypes.c_void_p),
-        ("state_indices", ctypes.c_void_p), ("o", ctypes.c_void_p),
+        ("state_indices", ctypes.c_void_p), ("o", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
     ]
 
 
@@ -117,7 +119,8 @@ DEFAULT_CHUNK = 32
 
 
 def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final_state, checkpoint_every,
-                  checkpoints, o, chunk_size=DEFAULT_CHUNK):
+                  checkpoints, o, chunk_size=DEFAULT_CHUNK, initial_state_indices=None, checkpoint_indices=None,
+                  num_slots=0):
     T, H, dk = q.shape
     a = KdaFwdArgs()
     a.struct_size = ctypes.sizeof(KdaFwdArgs)
@@ -137,17 +140,25 @@ def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final
     a.checkpoint_every = int(checkpoint_every)
     a.checkpoints = _ptr(checkpoints)
     a.o = _ptr(o)
+    a.initial_state_indices = _ptr(initial_state_indices)
+    a.checkpoint_indices = _ptr(checkpoint_indices)
+    a.num_slots = int(num_slots)
     return a
 
 
 def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, output_final_state=True,
-                  checkpoint_every=0, stream=None, chunk_size=DEFAULT_CHUNK):
+                  checkpoint_every=0, stream=None, chunk_size=DEFAULT_CHUNK, initial_state_indices=None,
+                  state_pool=None, checkpoint_indices=None):
     """Chunked KDA prefill (packed varlen).
 
     q, k: [T, H, dk]; v: [T, H, dv] (bf16 or fp32, CUDA, contiguous); g: [T, H, dk] fp32;
     beta: [T, H] fp32; cu_seqlens: int sequence offsets [N+1] (list / CPU or CUDA tensor,
     None = one sequence); initial_state: fp32 [N, H, dk, dv] or None.
     chunk_size: token block of the chunked form, 32 (software-pipelined kernel) or 64.
+    Paged state pool: with state_pool fp32 [P, H, dk, dv], initial_state_indices int32 [N]
+    (CUDA; -1 = zeros) picks each sequence's initial state from the pool (initial_state is then
+    ignored), and checkpoint_indices int32 [M] (CUDA; -1 = not written) writes checkpoint m
+    into pool slot checkpoint_indices[m] instead of returning a checkpoint tensor.
     Returns (o [T,H,dv] fp32, final_state [N,H,dk,dv] fp32 or None, checkpoints or None).
     """
     T, H, dk = q.shape
@@ -164,11 +175,14 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
     o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
     sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
     ck = None
-    if checkpoint_every:
+    if checkpoint_every and checkpoint_indices is None:
         M = int(((cu_host[1:] - cu_host[:-1]) // checkpoint_every).sum())
         ck = torch.empty((M, H, dk, dv), dtype=torch.float32, device=dev)
-    a = make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, sf, checkpoint_every, ck, o,
-                      chunk_size)
+    s0 = state_pool if initial_state_indices is not None else initial_state
+    ck_arg = state_pool if checkpoint_indices is not None else ck
+    nslots = int(state_pool.shape[0]) if state_pool is not None else 0
+    a = make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, s0, sf, checkpoint_every, ck_arg, o,
+                      chunk_size, initial_state_indices, checkpoint_indices, nslots)
     L = lib()
     ws_bytes = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a))
     if ws_bytes == 0 and N > 0:
@@ -180,7 +194,7 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
     return o, sf, ck
 
 
-def make_decode_args(q, k, v, g, beta, state, o, scale):
+def make_decode_args(q, k, v, g, beta, state, o, scale, state_indices=None):
     N, H, dk = q.shape
     a = KdaDecodeArgs()
     a.struct_size = ctypes.sizeof(KdaDecodeArgs)
@@ -192,16 +206,18 @@ def make_decode_args(q, k, v, g, beta, state, o, scale):
     a.scale = float(scale)
     a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
     a.state = _ptr(state)
-    a.state_indices = None
+    a.state_indices = _ptr(state_indices)
     a.o = _ptr(o)
+    a.num_slots = int(state.shape[0]) if state_indices is not None else 0
     return a
 
 
-def kda_decode_step(q, k, v, g, beta, state, scale=1.0, out=None, stream=None):
-    """One decode token per sequence; `state` [N,H,dk,dv] fp32 is updated in place.
-    Returns o [N, H, dv] fp32."""
+def kda_decode_step(q, k, v, g, beta, state, scale=1.0, out=None, stream=None, state_indices=None):
+    """One decode token per sequence; `state` [N,H,dk,dv] fp32 is updated in place.  With
+    state_indices (int32 [N], CUDA), `state` is a pool [P,H,dk,dv] and sequence n uses slot
+    state_indices[n] (-1: inactive, o = 0).  Returns o [N, H, dv] fp32."""
     N, H, dk = q.shape
     o = out if out is not None else torch.empty((N, H, v.shape[2]), dtype=torch.float32, device=q.device)
-    a = make_decode_args(q, k, v, g, beta, state, o, scale)
+    a = make_decode_args(q, k, v, g, beta, state, o, scale, state_indices)
     _check(lib().kda_decode_step(ctypes.byref(a), _stream(stream)))
     return o

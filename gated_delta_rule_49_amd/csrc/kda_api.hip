@@ -10,12 +10,14 @@
 
 extern "C" hipError_t kda_launch_decode(int dk, int in_bf16, int N, int H, const void *q, const void *k,
                                         const void *v, const float *g, const float *beta, float *state,
-                                        float *o, float scale, hipStream_t stream);
+                                        const int32_t *slots, int nslots, float *o, float scale,
+                                        hipStream_t stream);
 extern "C" size_t kda_chunk_workspace_layout(int N, size_t *order_off, size_t *base_off);
 extern "C" hipError_t kda_launch_chunk(int chunk, int dk, int in_bf16, int N, int H, const void *q, const void *k,
                                        const void *v, const float *g, const float *beta, const int32_t *cu,
                                        const float *s0, float *sf, int every, float *ckpt, float *o,
-                                       float scale, void *workspace, hipStream_t stream);
+                                       float scale, const int32_t *s0_idx, const int32_t *ck_idx,
+                                       int nslots, void *workspace, hipStream_t stream);
 
 namespace {
 
@@ -62,6 +64,10 @@ kda_status validate_fwd(const kda_fwd_args *a) {
         if (m > 0 && (!a->checkpoints || !aligned16(a->checkpoints))) return KDA_ERR_INVALID_ARGUMENT;
     }
     if (!(a->scale == a->scale)) return KDA_ERR_INVALID_ARGUMENT;  // NaN scale
+    // paged pool: the indices need their pool, and the pool a size
+    if ((a->initial_state_indices || a->checkpoint_indices) && a->num_slots < 1) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->initial_state_indices && a->num_seqs > 0 && !a->initial_state) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->checkpoint_indices && a->checkpoint_every == 0) return KDA_ERR_INVALID_ARGUMENT;
     return KDA_OK;
 }
 
@@ -98,8 +104,9 @@ kda_status kda_chunk_fwd(const kda_fwd_args *a, void *workspace, size_t workspac
     if (a->num_seqs == 0) return KDA_OK;
     const hipError_t e = kda_launch_chunk(a->chunk_size, a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->q, a->k,
                                           a->v, a->g, a->beta, a->cu_seqlens, a->initial_state, a->final_state,
-                                          a->checkpoint_every, a->checkpoints, a->o, a->scale, workspace,
-                                          static_cast<hipStream_t>(stream));
+                                          a->checkpoint_every, a->checkpoints, a->o, a->scale,
+                                          a->initial_state_indices, a->checkpoint_indices, a->num_slots,
+                                          workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
 
@@ -108,7 +115,7 @@ kda_status kda_decode_step(const kda_decode_args *a, void *stream) {
     if (a->num_seqs < 0 || a->num_heads <= 0) return KDA_ERR_INVALID_ARGUMENT;
     const kda_status d = check_dims(a->dk, a->dv, a->in_dtype);
     if (d != KDA_OK) return d;
-    if (a->state_indices) return KDA_ERR_UNSUPPORTED;
+    if (a->state_indices && a->num_slots < 1) return KDA_ERR_INVALID_ARGUMENT;
     if (!(a->scale == a->scale)) return KDA_ERR_INVALID_ARGUMENT;
     if (a->num_seqs == 0) return KDA_OK;
     if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->state || !a->o) return KDA_ERR_INVALID_ARGUMENT;
@@ -117,8 +124,8 @@ kda_status kda_decode_step(const kda_decode_args *a, void *stream) {
         return KDA_ERR_INVALID_ARGUMENT;
     if ((void *)a->o == (void *)a->state) return KDA_ERR_INVALID_ARGUMENT;
     const hipError_t e = kda_launch_decode(a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->q, a->k,
-                                           a->v, a->g, a->beta, a->state, a->o, a->scale,
-                                           static_cast<hipStream_t>(stream));
+                                           a->v, a->g, a->beta, a->state, a->state_indices, a->num_slots, a->o,
+                                           a->scale, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
 

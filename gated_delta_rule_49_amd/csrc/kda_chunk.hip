@@ -117,11 +117,12 @@ chunk_fwd_kernel(const ChunkParams p) {
     // State slice in registers: Sr[ct][e] = S[16 ct + 4 lq + e][j0 + lr].
     f32x4_t Sr[KT];
     const size_t st_off = ((size_t)n * H + h) * DK * DV;
+    const long long s0o = s0_offset(p, n, h, DK * DV);
 #pragma unroll
     for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            Sr[ct][e] = p.s0 ? p.s0[st_off + (size_t)(16 * ct + 4 * lq + e) * DV + j0 + lr] : 0.f;
+            Sr[ct][e] = s0o >= 0 ? p.s0[s0o + (16 * ct + 4 * lq + e) * DV + j0 + lr] : 0.f;
 
     const IN_T *qg = reinterpret_cast<const IN_T *>(p.q);
     const IN_T *kg = reinterpret_cast<const IN_T *>(p.k);
@@ -447,11 +448,12 @@ chunk_fwd_kernel(const ChunkParams p) {
             // state snapshot at in-sequence positions that are multiples of `every`
             if (p.every > 0 && nvalid == CH && ((ci + 1) * CH) % p.every == 0) {
                 const int64_t m = p.ckpt_base[n] + ((ci + 1) * CH) / p.every - 1;
-                float *dst = p.ckpt + ((size_t)m * H + h) * DK * DV;
+                float *dst = ckpt_dst(p, m, h, DK * DV);
+                if (dst)
 #pragma unroll
-                for (int ct = 0; ct < KT; ++ct)
+                    for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lq + e) * DV + j0 + lr] = Sr[ct][e];
+                        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lq + e) * DV + j0 + lr] = Sr[ct][e];
             }
         }
         __syncthreads();
@@ -521,7 +523,8 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int
                                        const void *q, const void *k,
                                        const void *v, const float *g, const float *beta, const int32_t *cu,
                                        const float *s0, float *sf, int every, float *ckpt, float *o,
-                                       float scale, void *workspace, hipStream_t stream) {
+                                       float scale, const int32_t *s0_idx, const int32_t *ck_idx,
+                                       int nslots, void *workspace, hipStream_t stream) {
     if (N == 0) return hipSuccess;
     size_t oo, bo;
     kda_chunk_workspace_layout(N, &oo, &bo);
@@ -534,7 +537,7 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int
     kda::ChunkParams p;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu_seqlens = cu; p.order = order;
     p.ckpt_base = base; p.s0 = s0; p.sf = sf; p.ckpt = ckpt; p.o = o; p.H = H; p.every = every;
-    p.scale = scale;
+    p.scale = scale; p.s0_idx = s0_idx; p.ck_idx = ck_idx; p.nslots = nslots;
     const dim3 grid((unsigned)N * (unsigned)H);
     if (chunk == 32) return kda_launch_chunk32(dk, in_bf16, grid.x, p, stream);
 #define KDA_CHUNK(DKV, F32P, T) \

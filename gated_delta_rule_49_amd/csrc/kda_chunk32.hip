@@ -407,6 +407,7 @@ chunk32_kernel(const ChunkParams p) {
         const size_t st_off = ((size_t)n * H + h) * DK * DV;
         f32x4_t Sr[JT][KT];
         {
+            const long long s0o = s0_offset(p, n, h, DK * DV);
             const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct)
@@ -415,8 +416,8 @@ chunk32_kernel(const ChunkParams p) {
                     float x[JT];
 #pragma unroll
                     for (int jt = 0; jt < JT; ++jt) x[jt] = 0.f;
-                    if (p.s0)
-                        load_cols<JT>(p.s0 + st_off + (size_t)(16 * ct + 4 * lq + e) * DV + col0 + SWC * sw + JT * lr, x);
+                    if (s0o >= 0)
+                        load_cols<JT>(p.s0 + s0o + (16 * ct + 4 * lq + e) * DV + col0 + SWC * sw + JT * lr, x);
 #pragma unroll
                     for (int jt = 0; jt < JT; ++jt) Sr[jt][ct][e] = x[jt];
                 }
@@ -541,16 +542,19 @@ chunk32_kernel(const ChunkParams p) {
                     // state after in-sequence position (it + 1) * 32, a multiple of checkpoint_every
                     ck_left = every_chunks;
                     const int64_t m = p.ckpt_base[n] + ck_idx++;
-                    float *const dst = p.ckpt + ((size_t)m * H + h) * DK * DV + col0;
+                    float *const dbase = ckpt_dst(p, m, h, DK * DV);   // NULL: not kept
+                    if (dbase) {
+                        float *const dst = dbase + col0;
 #pragma unroll
-                    for (int ct = 0; ct < KT; ++ct)
+                        for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            float x[JT];
+                            for (int e = 0; e < 4; ++e) {
+                                float x[JT];
 #pragma unroll
-                            for (int jt = 0; jt < JT; ++jt) x[jt] = Sr[jt][ct][e];
-                            store_cols<JT>(dst + (unsigned)((16 * ct + 4 * lq + e) * DV + SWC * sw + JT * lr), x);
-                        }
+                                for (int jt = 0; jt < JT; ++jt) x[jt] = Sr[jt][ct][e];
+                                store_cols<JT>(dst + (unsigned)((16 * ct + 4 * lq + e) * DV + SWC * sw + JT * lr), x);
+                            }
+                    }
                 }
             }
             lds_barrier();

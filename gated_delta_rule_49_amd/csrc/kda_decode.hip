@@ -28,7 +28,8 @@ template <int DK, int DV, typename IN_T>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_kernel(const IN_T *__restrict__ q, const IN_T *__restrict__ k, const IN_T *__restrict__ v,
               const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
-              float *__restrict__ o, int NH, float scale) {
+              const int32_t *__restrict__ slots, int nslots, float *__restrict__ o, int H, int NH,
+              float scale) {
     constexpr int CG = DV / 4;                 // column groups (float4 each)
     constexpr int RG = DEC_THREADS / CG;       // row groups
     constexpr int RPT = DK / RG;               // rows per thread
@@ -41,19 +42,37 @@ decode_kernel(const IN_T *__restrict__ q, const IN_T *__restrict__ k, const IN_T
     __shared__ float s_aq[DK], s_ak[DK], s_al[DK], s_k[DK], s_qk[DK], s_v[DV];
     __shared__ float s_red[NWAVE][CG][9];
 
+    // state slot of (n, h) = nh: n itself, or the pool slot slots[n]; -1 (or out of range) when
+    // the sequence is inactive (no state access, o = 0)
+    auto slot_of = [&](int nh_) -> long long {
+        const int n = nh_ / H, h = nh_ - n * H;
+        const long long sl = slots ? (long long)slots[n] : (long long)n;
+        return sl >= 0 && sl < nslots ? sl * H + h : -1;
+    };
     int nh = blockIdx.x;                       // n * H + h
+    long long sl = slot_of(nh);
     f32x4_t s[RPT], sn[RPT];                   // this state, the next one
-    {
-        const f32x4_t *S4 = reinterpret_cast<const f32x4_t *>(state + (size_t)nh * DK * DV);
+    if (sl >= 0) {
+        const f32x4_t *S4 = reinterpret_cast<const f32x4_t *>(state + sl * DK * DV);
 #pragma unroll
         for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S4[(rg + RG * m) * CG + cg]);
     }
     for (; nh < NH; nh += gridDim.x) {
         const int nxt = nh + (int)gridDim.x;
-        if (nxt < NH) {
-            const f32x4_t *S4n = reinterpret_cast<const f32x4_t *>(state + (size_t)nxt * DK * DV);
+        const long long sln = nxt < NH ? slot_of(nxt) : -1;
+        if (sln >= 0) {
+            const f32x4_t *S4n = reinterpret_cast<const f32x4_t *>(state + sln * DK * DV);
 #pragma unroll
             for (int m = 0; m < RPT; ++m) sn[m] = __builtin_nontemporal_load(&S4n[(rg + RG * m) * CG + cg]);
+        }
+        if (sl < 0) {
+            // inactive sequence: o = 0, state untouched
+            const size_t tok_v = (size_t)nh * DV;
+            if (rg == 0) reinterpret_cast<float4 *>(o + tok_v)[cg] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) s[m] = sn[m];
+            sl = sln;
+            continue;
         }
 
         const size_t tok_k = (size_t)nh * DK, tok_v = (size_t)nh * DV;
@@ -110,7 +129,7 @@ decode_kernel(const IN_T *__restrict__ q, const IN_T *__restrict__ k, const IN_T
         if (rg == 0)
             reinterpret_cast<float4 *>(o + tok_v)[cg] = make_float4(ov[0], ov[1], ov[2], ov[3]);
 
-        f32x4_t *S4 = reinterpret_cast<f32x4_t *>(state + (size_t)nh * DK * DV);
+        f32x4_t *S4 = reinterpret_cast<f32x4_t *>(state + sl * DK * DV);
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int i = rg + RG * m;
@@ -125,6 +144,7 @@ decode_kernel(const IN_T *__restrict__ q, const IN_T *__restrict__ k, const IN_T
         __syncthreads();   // the shared vectors and partials are rewritten for the next state
 #pragma unroll
         for (int m = 0; m < RPT; ++m) s[m] = sn[m];
+        sl = sln;
     }
 }
 
@@ -133,7 +153,8 @@ decode_kernel(const IN_T *__restrict__ q, const IN_T *__restrict__ k, const IN_T
 // Launcher used by the C ABI (kda_api.hip).  Returns a hipError_t.
 extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_decode(int dk, int in_bf16, int N, int H, const void *q, const void *k,
                                         const void *v, const float *g, const float *beta, float *state,
-                                        float *o, float scale, hipStream_t stream) {
+                                        const int32_t *slots, int nslots, float *o, float scale,
+                                        hipStream_t stream) {
     if (N == 0 || H == 0) return hipSuccess;
     const long long nh = (long long)N * H;
     if (nh > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -141,7 +162,8 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_decode(in
     const int grid = (int)(nh < kda_cu_count() ? nh : kda_cu_count());
 #define KDA_DEC(DKV, T)                                                                                \
     hipLaunchKernelGGL((kda::decode_kernel<DKV, DKV, T>), dim3(grid), dim3(kda::DEC_THREADS), 0, stream, \
-                       (const T *)q, (const T *)k, (const T *)v, g, beta, state, o, (int)nh, scale)
+                       (const T *)q, (const T *)k, (const T *)v, g, beta, state, slots, slots ? nslots : N, o, \
+                       H, (int)nh, scale)
     if (dk == 128 && in_bf16) KDA_DEC(128, uint16_t);
     else if (dk == 128) KDA_DEC(128, float);
     else if (dk == 64 && in_bf16) KDA_DEC(64, uint16_t);

@@ -203,10 +203,37 @@ struct ChunkParams {
     float *sf;
     float *ckpt;
     float *o;
+    const int32_t *s0_idx;         // NULL, or the pool slot of each sequence's initial state (-1: zeros)
+    const int32_t *ck_idx;         // NULL, or the pool slot of each checkpoint (-1: not written)
+    int nslots;                    // slots of the pool(s) when an index array is set
     int H;
     int every;
     float scale;
 };
+
+// Element offset of the initial state of (n, h) in p.s0, or -1 for a zero state (no initial
+// state, or a pool index of -1 or out of range).
+__device__ __forceinline__ long long s0_offset(const ChunkParams &p, int n, int h, int dkdv) {
+    if (!p.s0) return -1;
+    long long slot = n;
+    if (p.s0_idx) {
+        const int s = p.s0_idx[n];
+        if (s < 0 || s >= p.nslots) return -1;
+        slot = s;
+    }
+    return (slot * p.H + h) * dkdv;
+}
+// Destination of checkpoint m of head h, or NULL when it is not written (pool index -1 or out of
+// range).
+__device__ __forceinline__ float *ckpt_dst(const ChunkParams &p, int64_t m, int h, int dkdv) {
+    int64_t slot = m;
+    if (p.ck_idx) {
+        const int s = p.ck_idx[m];
+        if (s < 0 || s >= p.nslots) return nullptr;
+        slot = s;
+    }
+    return p.ckpt + (slot * p.H + h) * dkdv;
+}
 
 // Workgroup barrier that orders LDS accesses only: outstanding global loads
 // (prefetches into registers) stay in flight across it.

@@ -38,8 +38,15 @@
  *     pure host code and runs before any launch; a failed launch returns
  *     KDA_ERR_DEVICE.  Faults during execution surface at the caller's next
  *     synchronisation.
- *   - Supported in ABI v1: d_k == d_v in {64, 128}; chunk_size 32 or 64;
- *     in_dtype KDA_F32 or KDA_BF16.  Other values -> KDA_ERR_UNSUPPORTED.
+ *   - Supported: d_k == d_v in {64, 128}; chunk_size 32 or 64; in_dtype
+ *     KDA_F32 or KDA_BF16.  Other values -> KDA_ERR_UNSUPPORTED.
+ *   - Paged state pool (ABI v2; the digest's inference paragraph: a pool of
+ *     recurrent states with prefix reuse at 512-token boundaries): a pool is
+ *     fp32 [num_slots, H, d_k, d_v]; an index array maps each sequence (or
+ *     checkpoint) to a slot.  Index -1 means "no slot"; an index outside
+ *     [-1, num_slots) is treated as -1.  The kernels check the range; the
+ *     caller guarantees that the slots written in one call are distinct and
+ *     are not also read in that call.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -51,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1u
+#define KDA_ABI_VERSION 2u
 
 typedef enum {
     KDA_OK = 0,
@@ -94,6 +101,15 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *   checkpoints      fp32 [sum_n floor(L_n/every), H, dk, dv], sequence-major then
  *                    position.  Required iff checkpoint_every > 0.
  *   o                fp32 [T, H, dv]; must not alias any input.
+ *   initial_state_indices  NULL => initial_state as above.  Else device int32 [N]:
+ *                    initial_state is a pool of num_slots states and sequence n
+ *                    starts from slot initial_state_indices[n] (-1: zeros).
+ *   checkpoint_indices     NULL => checkpoints as above.  Else device int32
+ *                    [sum_n floor(L_n/every)] (checkpoint m in the order above):
+ *                    checkpoints is a pool of num_slots states and checkpoint m is
+ *                    written to slot checkpoint_indices[m] (-1: not written).
+ *   num_slots        >= 1 when either index array is set; else ignored.
+ *                    final_state stays [N, H, dk, dv] either way.
  */
 typedef struct {
     uint32_t struct_size;
@@ -117,6 +133,9 @@ typedef struct {
     int32_t checkpoint_every;
     float *checkpoints;
     float *o;
+    const int32_t *initial_state_indices;
+    const int32_t *checkpoint_indices;
+    int32_t num_slots;
 } kda_fwd_args;
 
 /* Device workspace (bytes) that kda_chunk_fwd needs for `args` (host only; no
@@ -132,9 +151,13 @@ kda_status kda_chunk_fwd(const kda_fwd_args *args, void *workspace, size_t works
  * One decode step: for each of N independent sequences and each head, consume
  * one token and update that (sequence, head) state in place.
  *   q, k, g : [N, H, dk]    v : [N, H, dv]    beta : [N, H]
- *   state   : fp32 [N, H, dk, dv], read and overwritten in place
+ *   state   : fp32 [N, H, dk, dv], read and overwritten in place; or, when
+ *             state_indices is set, a pool fp32 [num_slots, H, dk, dv] in which
+ *             sequence n uses slot state_indices[n] (device int32 [N]).  A
+ *             sequence with slot -1 is inactive: its state is not touched and
+ *             its o is 0.  Active slots must be distinct.
  *   o       : fp32 [N, H, dv]
- *   state_indices must be NULL in ABI v1.
+ *   num_slots >= 1 when state_indices is set; else ignored.
  */
 typedef struct {
     uint32_t struct_size;
@@ -152,6 +175,7 @@ typedef struct {
     float *state;
     const int32_t *state_indices;
     float *o;
+    int32_t num_slots;
 } kda_decode_args;
 
 kda_status kda_decode_step(const kda_decode_args *args, void *stream);

@@ -150,6 +150,60 @@ def decode(q, k, v, g, beta, state, scale=1.0, n_threads=None):
     return o, Sn
 
 
+# ---- paged state pool (the digest's inference paragraph: a pool of recurrent states with prefix
+# reuse at 512-token boundaries).  A pool is [P, H, dk, dv]; an index of -1, or any index outside
+# [0, P), means "no slot".  These are plain gathers and scatters around forward / decode.
+
+def _slot(idx, P):
+    i = int(idx)
+    return i if 0 <= i < P else -1
+
+
+def forward_paged(q, k, v, g, beta, cu_seqlens, scale, pool, initial_state_indices=None,
+                  checkpoint_every=0, checkpoint_indices=None):
+    """forward() with the initial states gathered from pool slots (initial_state_indices [N];
+    -1: zeros) and the checkpoints scattered into pool slots (checkpoint_indices [M]; -1: not
+    kept).  Returns (o, final_state, new_pool) fp64; new_pool is a copy of `pool` with the
+    checkpoint slots overwritten."""
+    pool = np.asarray(pool, dtype=np.float64)
+    P, H, dk, dv = pool.shape
+    cu = np.asarray(cu_seqlens if cu_seqlens is not None else [0, np.asarray(q).shape[0]], dtype=np.int64)
+    N = len(cu) - 1
+    s0 = None
+    if initial_state_indices is not None:
+        s0 = np.zeros((N, H, dk, dv), dtype=np.float64)
+        for n in range(N):
+            sl = _slot(initial_state_indices[n], P)
+            if sl >= 0:
+                s0[n] = pool[sl]
+    o, sf, ck = forward(q, k, v, g, beta, cu, scale, s0, checkpoint_every=checkpoint_every)
+    new_pool = pool.copy()
+    if checkpoint_indices is not None and ck is not None:
+        for m in range(ck.shape[0]):
+            sl = _slot(checkpoint_indices[m], P)
+            if sl >= 0:
+                new_pool[sl] = ck[m]
+    return o, sf, new_pool
+
+
+def decode_paged(q, k, v, g, beta, pool, state_indices, scale=1.0):
+    """decode() on pool slots: sequence n updates slot state_indices[n]; a sequence with no slot
+    is inactive (o = 0, pool untouched).  Returns (o, new_pool) fp64."""
+    pool = np.asarray(pool, dtype=np.float64)
+    P = pool.shape[0]
+    N = np.asarray(q).shape[0]
+    act = [n for n in range(N) if _slot(state_indices[n], P) >= 0]
+    o = np.zeros((N,) + np.asarray(v).shape[1:], dtype=np.float64)
+    new_pool = pool.copy()
+    if act:
+        sl = [_slot(state_indices[n], P) for n in act]
+        sel = lambda x: np.asarray(x)[act]
+        oa, sa = decode(sel(q), sel(k), sel(v), sel(g), sel(beta), pool[sl], scale)
+        o[act] = oa
+        new_pool[sl] = sa
+    return o, new_pool
+
+
 def forward_from_library(path):
     """A `forward` bound to another build of kda_oracle.c (used by the mutation
     test, which compiles deliberately broken copies of the oracle source)."""

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert kda.kda_abi_version() == 1
+    assert kda.kda_abi_version() == 2
     for code, name in enumerate(["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
                                  "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_DEVICE"]):
         assert kda.kda_status_str(code) == name
@@ -108,11 +108,26 @@ def status(L, a, ws=FAKE * 16, ws_bytes=1 << 20):
     ("checkpoint_every", 64, kda.KDA_ERR_INVALID_ARGUMENT),  # checkpoints pointer missing
     ("total_tokens", 227, kda.KDA_ERR_INVALID_ARGUMENT),
     ("scale", float("nan"), kda.KDA_ERR_INVALID_ARGUMENT),
+    ("initial_state_indices", FAKE * 9, kda.KDA_ERR_INVALID_ARGUMENT),   # no pool size, no pool
+    ("checkpoint_indices", FAKE * 9, kda.KDA_ERR_INVALID_ARGUMENT),      # no pool size
 ])
 def test_fwd_validation(L, field, value, expect):
     a, keep = fwd_args(**{field: value})
     assert status(L, a) == expect
     assert L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_pool_validation(L):
+    # indices need a pool size, the initial-state indices need the pool, and checkpoint
+    # indices need checkpoints
+    a, keep = fwd_args(initial_state_indices=FAKE * 9, num_slots=4)
+    assert status(L, a) == kda.KDA_ERR_INVALID_ARGUMENT            # initial_state (the pool) missing
+    a, keep = fwd_args(checkpoint_indices=FAKE * 9, num_slots=4)
+    assert status(L, a) == kda.KDA_ERR_INVALID_ARGUMENT            # checkpoint_every is 0
+    a, keep = fwd_args(initial_state_indices=FAKE * 9, initial_state=FAKE * 10, num_slots=0)
+    assert status(L, a) == kda.KDA_ERR_INVALID_ARGUMENT
+    a, keep = fwd_args(initial_state_indices=FAKE * 9, initial_state=FAKE * 10, num_slots=4)
+    assert L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) > 0   # valid
 
 
 @pytest.mark.parametrize("cu", [[1, 100], [0, 50, 40], [0, 100, 90, 228]])
@@ -156,7 +171,7 @@ def decode_args(**over):
 @pytest.mark.parametrize("field,value,expect", [
     ("struct_size", 4, kda.KDA_ERR_INVALID_ARGUMENT),
     ("dk", 32, kda.KDA_ERR_UNSUPPORTED),
-    ("state_indices", FAKE, kda.KDA_ERR_UNSUPPORTED),
+    ("state_indices", FAKE * 9, kda.KDA_ERR_INVALID_ARGUMENT),   # pool without num_slots
     ("state", None, kda.KDA_ERR_INVALID_ARGUMENT),
     ("state", FAKE + 8, kda.KDA_ERR_INVALID_ARGUMENT),
     ("o", FAKE * 6, kda.KDA_ERR_INVALID_ARGUMENT),          # aliases state

@@ -210,3 +210,72 @@ def test_bitwise_determinism_and_state_aliasing(chunk):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(S.cpu().numpy(), a[1])
     np.testing.assert_array_equal(o.cpu().numpy(), a[0])
+
+
+# ---- paged state pool ---------------------------------------------------------------------------
+def _log(label, errs, tol):
+    print(f"[parity] {label}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    log = os.environ.get("KDA_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(json.dumps({"case": label, "tol": tol, **errs}) + "\n")
+    for k_, v_ in errs.items():
+        assert v_ <= tol, (k_, v_, tol)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_paged_pool(dtype):
+    """Decode on a pool of 2N+1 slots: distinct random slots, two inactive sequences (-1 and an
+    index past the pool).  Active slots match the oracle; every other slot is bit-unchanged and
+    inactive sequences read o = 0."""
+    d = W.make_decode(12, 5, 128, 128, dtype, seed=41)
+    N, P = 12, 25
+    rng = np.random.default_rng(41)
+    slots = rng.permutation(P)[:N].astype(np.int32)
+    slots[3], slots[9] = -1, P + 4
+    pool = (0.1 * rng.standard_normal((P, 5, 128, 128))).astype(np.float32)
+    dt = in_dtype(d)
+    pool_d = to_dev(pool, torch.float32)
+    o = kda.kda_decode_step(to_dev(d.q, dt), to_dev(d.k, dt), to_dev(d.v, dt), to_dev(d.g, torch.float32),
+                            to_dev(d.beta, torch.float32), pool_d, 0.9,
+                            state_indices=to_dev(slots, torch.int32))
+    torch.cuda.synchronize()
+    o_r, pool_r = oracle.decode_paged(d.q, d.k, d.v, d.g, d.beta, pool, slots, 0.9)
+    o, pool_g = o.cpu().numpy(), pool_d.cpu().numpy()
+    act = [n for n in range(N) if 0 <= slots[n] < P]
+    touched = slots[act]
+    _log(f"decode paged {dtype}", {"o": W.rel_max_err(o[act], o_r[act]),
+                                   "S": W.rel_max_err(pool_g[touched], pool_r[touched])}, 1e-4)
+    assert not o[[3, 9]].any()
+    rest = [s for s in range(P) if s not in set(touched.tolist())]
+    np.testing.assert_array_equal(pool_g[rest], pool[rest])
+
+
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_prefill_paged_pool(chunk):
+    """Prefill with initial states gathered from pool slots (one -1: zeros) and checkpoints
+    scattered to pool slots (some -1: not kept), as for prefix reuse at checkpoint boundaries."""
+    w = W.make_prefill([200, 64, 130, 333], H=3, dk=128, dv=128, dtype="bf16", seed=42, s0_std=0.1,
+                       checkpoint_every=64)
+    N, P = 4, 16
+    M = sum(L // 64 for L in w.seqlens)                     # 3 + 1 + 2 + 5 = 11 checkpoints
+    rng = np.random.default_rng(42)
+    pool = (0.1 * rng.standard_normal((P, 3, 128, 128))).astype(np.float32)
+    sidx = np.array([5, -1, 11, 2], dtype=np.int32)
+    cidx = np.array([0, 1, -1, 3, 4, -1, 6, 7, 8, 9, 10], dtype=np.int32)[:M]   # slots 0..10 minus two
+    assert not set(sidx[sidx >= 0]) & set(cidx[cidx >= 0])
+    dt = in_dtype(w)
+    pool_d = to_dev(pool, torch.float32)
+    o, sf, _ = kda.kda_chunk_fwd(to_dev(w.q, dt), to_dev(w.k, dt), to_dev(w.v, dt), to_dev(w.g, torch.float32),
+                                 to_dev(w.beta, torch.float32), list(w.cu_seqlens), 1.0, None, True, 64,
+                                 chunk_size=chunk, initial_state_indices=to_dev(sidx, torch.int32),
+                                 state_pool=pool_d, checkpoint_indices=to_dev(cidx, torch.int32))
+    torch.cuda.synchronize()
+    o_r, sf_r, pool_r = oracle.forward_paged(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, 1.0, pool, sidx, 64, cidx)
+    pool_g = pool_d.cpu().numpy()
+    written = cidx[cidx >= 0]
+    _log(f"prefill paged C={chunk}", {"o": W.rel_max_err(o.cpu().numpy(), o_r),
+                                      "S": W.rel_max_err(sf.cpu().numpy(), sf_r),
+                                      "ckpt": W.rel_max_err(pool_g[written], pool_r[written])}, TOL["bf16"])
+    rest = [s for s in range(P) if s not in set(written.tolist())]
+    np.testing.assert_array_equal(pool_g[rest], pool[rest])

@@ -283,3 +283,58 @@ def test_workload_generator_properties():
     assert abs(float(np.std(w.s0)) - 0.1) < 0.01
     L = W.config4_lengths()
     assert len(L) == 64 and all(512 <= x <= 131072 and x % 512 == 0 for x in L)
+
+
+# ---- paged state pool --------------------------------------------------------------------------
+def test_decode_paged_is_decode_on_the_selected_slots():
+    """The pool form of decode: identity slots reproduce decode; a permutation moves each result
+    to its slot; a sequence with no slot (-1, or out of range) leaves the pool alone and reads 0."""
+    d = W.make_decode(6, 2, 8, 6, "f32", seed=31)
+    od, Sd = oracle.decode(d.q, d.k, d.v, d.g, d.beta, d.s0, 0.7)
+    o1, p1 = oracle.decode_paged(d.q, d.k, d.v, d.g, d.beta, d.s0, np.arange(6), 0.7)
+    np.testing.assert_array_equal(o1, od)
+    np.testing.assert_array_equal(p1, Sd)
+    # pool of 9 slots; sequence n lives in slot perm[n]; sequences 2 and 5 are inactive
+    rng = np.random.default_rng(5)
+    pool = rng.standard_normal((9, 2, 8, 6)).astype(np.float32)
+    perm = np.array([7, 0, -1, 3, 8, 9])            # 9 is out of range: inactive too
+    pool[perm[[0, 1, 3, 4]]] = d.s0[[0, 1, 3, 4]]
+    o2, p2 = oracle.decode_paged(d.q, d.k, d.v, d.g, d.beta, pool, perm, 0.7)
+    for n in (0, 1, 3, 4):
+        np.testing.assert_array_equal(o2[n], od[n])
+        np.testing.assert_array_equal(p2[perm[n]], Sd[n])
+    for n in (2, 5):
+        assert not o2[n].any()
+    untouched = [s for s in range(9) if s not in (7, 0, 3, 8)]
+    np.testing.assert_array_equal(p2[untouched], pool[untouched].astype(np.float64))
+
+
+def test_forward_paged_prefix_reuse():
+    """Prefix reuse through the pool: a run writes its 512-token-style checkpoints (here every
+    16) into pool slots; a second run that starts from one of those slots over the remaining
+    tokens reproduces the tail of running the whole sequence (P-g through the pool)."""
+    w = W.make_prefill([80], H=2, dk=5, dv=4, dtype="f32", seed=32, s0_std=0.3)
+    o, S, ck = oracle.forward(w.q, w.k, w.v, w.g, w.beta, None, 1.0, w.s0, checkpoint_every=16)
+    pool = np.zeros((8, 2, 5, 4), dtype=np.float32)
+    pool[6] = w.s0[0]
+    cidx = np.array([1, -1, 4, 2, 0])                # checkpoint 1 is not kept
+    o1, S1, pool1 = oracle.forward_paged(w.q, w.k, w.v, w.g, w.beta, None, 1.0, pool,
+                                         initial_state_indices=np.array([6]), checkpoint_every=16,
+                                         checkpoint_indices=cidx)
+    np.testing.assert_array_equal(o1, o)
+    np.testing.assert_array_equal(S1, S)
+    for m, sl in enumerate(cidx):
+        if sl >= 0:
+            np.testing.assert_array_equal(pool1[sl], ck[m])
+    np.testing.assert_array_equal(pool1[[3, 5, 6, 7]], pool[[3, 5, 6, 7]].astype(np.float64))
+    # resume from the checkpoint after token 48 (checkpoint 2, slot 4) over tokens 48..79
+    tail = slice(48, None)
+    o2, S2, _ = oracle.forward_paged(w.q[tail], w.k[tail], w.v[tail], w.g[tail], w.beta[tail], None, 1.0,
+                                     pool1.astype(np.float32), initial_state_indices=np.array([4]))
+    np.testing.assert_allclose(o2, o[tail], rtol=1e-6, atol=1e-6)   # the slot holds fp32 values
+    np.testing.assert_allclose(S2, S, rtol=1e-6, atol=1e-6)
+    # a slot index of -1 starts from zeros
+    o3, _, _ = oracle.forward_paged(w.q, w.k, w.v, w.g, w.beta, None, 1.0, pool,
+                                    initial_state_indices=np.array([-1]))
+    o0, _, _ = oracle.forward(w.q, w.k, w.v, w.g, w.beta, None, 1.0, None)
+    np.testing.assert_array_equal(o3, o0)
