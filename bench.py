@@ -199,6 +199,26 @@ def main():
                          "frac_of_hbm_peak": round(dgbps / HBM_PEAK_GBPS, 4),
                          "ms_p10": round(float(np.percentile(dec_ms, 10)), 4),
                          "ms_p90": round(float(np.percentile(dec_ms, 90)), 4)}
+        # the same decode through the paged pool: the state buffer as a pool of 256 slots,
+        # sequence n in slot perm[n] (a seeded permutation); timed after the steps, not in them
+        perm = torch.from_numpy(np.random.default_rng(3).permutation(N).astype(np.int32)).to(dev)
+        Dp = kda.make_decode_args(dq, dk_, dvv, dg, db, state, od, 1.0, state_indices=perm)
+
+        def decode_paged():
+            st = L.kda_decode_step(ctypes.byref(Dp), sptr)
+            if st != 0:
+                raise RuntimeError(kda.kda_status_str(st))
+
+        decode_paged()
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            pev[i][0].record(stream)
+            decode_paged()
+            pev[i][1].record(stream)
+        torch.cuda.synchronize()
+        pms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pev]))
+        res["decode"]["paged"] = {"ms": round(pms, 4), "GBps": round(dbytes / (pms * 1e-3) / 1e9, 1),
+                                  "slots": "permutation of 256 pool slots"}
 
     prof = measured_counters(args.chunk)
     if prof is not None:
