@@ -150,6 +150,30 @@ def decode(q, k, v, g, beta, state, scale=1.0, n_threads=None):
     return o, Sn
 
 
+# ---- fused prologue (the skill card's quick facts: the log-decay is a lower-bounded scaled
+# sigmoid with g_min = -5; q and k are L2-normalised per token and head)
+
+def prologue(q, k, g_pre, b_pre, normalize=True):
+    """The operator's inputs from raw ones, in fp64: g = -5 sigmoid(a), beta = sigmoid(b), and
+    q, k divided by their L2 norm over d_k (a zero vector stays zero)."""
+    q, k, a, b = (np.asarray(x, dtype=np.float64) for x in (q, k, g_pre, b_pre))
+    g = -5.0 / (1.0 + np.exp(-a))
+    beta = 1.0 / (1.0 + np.exp(-b))
+    if normalize:
+        def unit(x):
+            n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+            return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+        q, k = unit(q), unit(k)
+    return q, k, g, beta
+
+
+def forward_fused(q, k, v, g_pre, b_pre, cu_seqlens=None, scale=1.0, initial_state=None,
+                  checkpoint_every=0, normalize=True):
+    """forward() on the prologue's outputs (the recurrence takes them rounded to fp32)."""
+    qn, kn, g, beta = prologue(q, k, g_pre, b_pre, normalize)
+    return forward(qn, kn, v, g, beta, cu_seqlens, scale, initial_state, checkpoint_every=checkpoint_every)
+
+
 # ---- paged state pool (the digest's inference paragraph: a pool of recurrent states with prefix
 # reuse at 512-token boundaries).  A pool is [P, H, dk, dv]; an index of -1, or any index outside
 # [0, P), means "no slot".  These are plain gathers and scatters around forward / decode.

@@ -338,3 +338,40 @@ def test_forward_paged_prefix_reuse():
                                     initial_state_indices=np.array([-1]))
     o0, _, _ = oracle.forward(w.q, w.k, w.v, w.g, w.beta, None, 1.0, None)
     np.testing.assert_array_equal(o3, o0)
+
+
+# ---- fused prologue ------------------------------------------------------------------------------
+def test_prologue_closed_values():
+    """g = -5 sigmoid(a): -2.5 at a = 0, -> -5 and -> 0 at the tails; beta = sigmoid(b): 0.5 at 0;
+    L2 normalisation: (3, 4) -> (0.6, 0.8), a zero vector stays zero."""
+    a = np.array([[[0.0, 40.0, -40.0, 1.0]]])
+    b = np.array([[0.0]])
+    q = np.array([[[3.0, 4.0, 0.0, 0.0]]])
+    k = np.zeros((1, 1, 4))
+    qn, kn, g, beta = oracle.prologue(q, k, a, b)
+    assert g[0, 0, 0] == -2.5 and beta[0, 0] == 0.5
+    assert abs(g[0, 0, 1] + 5.0) < 1e-15 and abs(g[0, 0, 2]) < 1e-15
+    assert abs(g[0, 0, 3] + 5.0 / (1.0 + np.exp(-1.0))) < 1e-15
+    np.testing.assert_allclose(qn[0, 0], [0.6, 0.8, 0.0, 0.0], rtol=0, atol=1e-16)
+    assert not kn.any()
+
+
+def test_fused_forward_is_invariant_to_the_scale_of_q_and_k():
+    """With normalisation, rescaling each raw q and k row by positive factors leaves the output
+    unchanged (up to the fp32 rounding of the normalised inputs), and equals forward() on the
+    normalised, gated inputs."""
+    w = W.make_prefill_raw([40, 17], H=2, dk=8, dv=6, seed=7, s0_std=0.2)
+    o, S, _ = oracle.forward_fused(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, 0.5, w.s0)
+    rng = np.random.default_rng(3)
+    cq = rng.uniform(0.1, 10.0, size=w.q.shape[:2] + (1,))
+    ck = rng.uniform(0.1, 10.0, size=w.k.shape[:2] + (1,))
+    o2, S2, _ = oracle.forward_fused(w.q * cq, w.k * ck, w.v, w.g, w.beta, w.cu_seqlens, 0.5, w.s0)
+    np.testing.assert_allclose(o2, o, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(S2, S, rtol=1e-5, atol=1e-6)
+    qn = w.q / np.linalg.norm(w.q.astype(np.float64), axis=-1, keepdims=True)
+    kn = w.k / np.linalg.norm(w.k.astype(np.float64), axis=-1, keepdims=True)
+    g = -5.0 * (1.0 / (1.0 + np.exp(-w.g.astype(np.float64))))
+    beta = 1.0 / (1.0 + np.exp(-w.beta.astype(np.float64)))
+    o3, S3, _ = oracle.forward(qn, kn, w.v, g, beta, w.cu_seqlens, 0.5, w.s0)
+    np.testing.assert_array_equal(o3, o)
+    np.testing.assert_array_equal(S3, S)

@@ -157,6 +157,41 @@ def make_prefill(seqlens, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.0, g
                     out["g"], out["beta"], s0, checkpoint_every, {"gate": gate, "seed": seed})
 
 
+def make_prefill_raw(seqlens, H, dk=128, dv=128, seed=0, s0_std=0.0, checkpoint_every=0, wid=110,
+                     name=None) -> Workload:
+    """Inputs for the fused prologue: the same draws as the config distributions, before the
+    gate and the normalisation.  q, k ~ N(0,1) unnormalised, v ~ N(0,1) (all bf16-exact),
+    ``g`` holds the bf16-exact gate pre-activations a ~ N(0,1) [T,H,dk] and ``beta`` the fp32
+    pre-activations b ~ N(0,1) [T,H].  (The operator then uses g = -5 sigmoid(a),
+    beta = sigmoid(b) and L2-normalised q, k.)"""
+    seqlens = [int(x) for x in seqlens]
+    T = sum(seqlens)
+    q = np.empty((T, H, dk), dtype=np.float32)
+    k, a = np.empty_like(q), np.empty_like(q)
+    v = np.empty((T, H, dv), dtype=np.float32)
+    b = np.empty((T, H), dtype=np.float32)
+    off = 0
+    for s, L in enumerate(seqlens):
+        for blk in range(0, max(1, math.ceil(L / BLOCK))):
+            Tb = min(BLOCK, L - blk * BLOCK)
+            if Tb <= 0:
+                continue
+            sl = slice(off + blk * BLOCK, off + blk * BLOCK + Tb)
+            q[sl] = round_bf16(_rng(wid, s, blk, "q", seed).standard_normal((Tb, H, dk), dtype=np.float32))
+            k[sl] = round_bf16(_rng(wid, s, blk, "k", seed).standard_normal((Tb, H, dk), dtype=np.float32))
+            v[sl] = round_bf16(_rng(wid, s, blk, "v", seed).standard_normal((Tb, H, dv), dtype=np.float32))
+            a[sl] = round_bf16(_rng(wid, s, blk, "g", seed).standard_normal((Tb, H, dk), dtype=np.float32))
+            b[sl] = _rng(wid, s, blk, "beta", seed).standard_normal((Tb, H), dtype=np.float32)
+        off += L
+    s0 = None
+    if s0_std > 0:
+        s0 = np.empty((len(seqlens), H, dk, dv), dtype=np.float32)
+        for i in range(len(seqlens)):
+            s0[i] = _rng(wid, i, 0, "s0", seed).standard_normal((H, dk, dv), dtype=np.float32) * np.float32(s0_std)
+    return Workload(name or f"prefill_raw_H{H}_d{dk}", seqlens, H, dk, dv, "bf16", q, k, v, a, b, s0,
+                    checkpoint_every, {"raw": True, "seed": seed})
+
+
 def make_decode(N, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.1, gate="config", wid=103,
                 name=None, threads=None) -> Workload:
     """N independent sequences, one new token each; the state is [N, H, dk, dv]."""
