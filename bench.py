@@ -52,7 +52,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (profiling runs)")
     ap.add_argument("--chunk", type=int, default=32, choices=(32, 64), help="token block of the chunked form")
-    ap.add_argument("--workload", type=int, default=0, choices=(0, 1, 4),
+    ap.add_argument("--prologue", action="store_true",
+                    help="with --workload 2: fused gate/normalisation prologue (raw q, k, bf16 gate "
+                         "pre-activations)")
+    ap.add_argument("--workload", type=int, default=0, choices=(0, 1, 2, 4),
                     help="instead of the benchmark step, time the prefill of workload 1 (T=4096, H=32) or 4 "
                          "(64 packed sequences, H=32, checkpoints every 512) and print its own JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -83,7 +86,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.workload:
-        other_workload(args.workload, args.chunk, args.steps, args.warmup)
+        other_workload(args.workload, args.chunk, args.steps, args.warmup, args.prologue)
         return
 
     import gated_delta_rule_49_amd as kda
@@ -398,7 +401,7 @@ def summarize_trace(trace_dir, bench_json):
     print("wrote", ", ".join(out))
 
 
-def other_workload(cid, chunk, steps, warmup):
+def other_workload(cid, chunk, steps, warmup, prologue=False):
     """Prefill tokens/s of workload 1 or 4 (one JSON line).  Workload 1 uses the seeded host
     generator; workload 4 (about 1.85M tokens x 32 heads, ~110 GB with o and checkpoints) is drawn
     on the device with torch's seeded generator from the same distributions (lengths from the
@@ -410,7 +413,32 @@ def other_workload(cid, chunk, steps, warmup):
 
     dev = torch.device("cuda:0")
     bf = torch.bfloat16
-    if cid == 1:
+    pro = {}
+    if cid == 2:
+        # workload 2's shape with raw inputs for the fused prologue: q, k ~ N(0,1) unnormalised,
+        # bf16 gate pre-activations a ~ N(0,1), fp32 b ~ N(0,1); drawn on the device
+        T, H, dk, dv = 65536, 96, 128, 128
+        seqlens = [T]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(20261203)
+        q = torch.randn((T, H, dk), generator=gen, device=dev).to(bf)
+        k = torch.randn((T, H, dk), generator=gen, device=dev).to(bf)
+        v = torch.randn((T, H, dv), generator=gen, device=dev).to(bf)
+        if prologue:
+            g = torch.randn((T, H, dk), generator=gen, device=dev).to(bf)
+            beta = torch.randn((T, H), generator=gen, device=dev)
+            pro = dict(gate_preactivation=True, normalize_qk=True)
+        else:
+            q = (q.float() / q.float().norm(dim=-1, keepdim=True) * dk ** -0.5).to(bf)
+            k = (k.float() / k.float().norm(dim=-1, keepdim=True)).to(bf)
+            g = -5.0 * torch.sigmoid(torch.randn((T, H, dk), generator=gen, device=dev))
+            beta = torch.sigmoid(torch.randn((T, H), generator=gen, device=dev))
+        s0 = 0.1 * torch.randn((1, H, dk, dv), generator=gen, device=dev)
+        every = 0
+        desc = ("prefill T=65536 H=96 d_k=d_v=128 bf16 q/k/v, initial state; " +
+                ("fused prologue: bf16 gate pre-activations, fp32 beta pre-activations, q and k "
+                 "normalised inside" if prologue else "fp32 g/beta, normalised q/k"))
+    elif cid == 1:
         w = W.make_config(1)
         up = lambda x, dt: torch.from_numpy(x).to(dev, dt)
         q, k, v = up(w.q, bf), up(w.k, bf), up(w.v, bf)
@@ -452,7 +480,8 @@ def other_workload(cid, chunk, steps, warmup):
     sf = torch.empty((len(seqlens), H, dk, dv), dtype=torch.float32, device=dev)
     n_ck = sum(L // every for L in seqlens) if every else 0
     ck = torch.empty((max(n_ck, 1), H, dk, dv), dtype=torch.float32, device=dev) if n_ck else None
-    A = kda.make_fwd_args(q, k, v, g, beta, cu_d, cu_h, 1.0, s0, sf, every, ck, o, chunk)
+    A = kda.make_fwd_args(q, k, v, g, beta, cu_d, cu_h, (dk ** -0.5) if pro else 1.0, s0, sf, every, ck, o,
+                          chunk, **pro)
     L = kda.lib()
     ws = torch.empty(L.kda_chunk_fwd_workspace_bytes(ctypes.byref(A)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -476,7 +505,7 @@ def other_workload(cid, chunk, steps, warmup):
         ms.append(e0.elapsed_time(e1))
     med = float(np.median(ms))
     nbytes = prefill_bytes(T, H, dk, dv, with_states=False) + len(seqlens) * H * dk * dv * 4 * (2 if s0 is not None else 1) \
-        + n_ck * H * dk * dv * 4
+        + n_ck * H * dk * dv * 4 - (T * H * dk * 2 if pro else 0)   # a bf16 gate stream: 2 B per channel less
     print(json.dumps({
         "metric": "KDA prefill tokens/s", "workload": desc, "tokens": T, "heads": H, "chunk": chunk,
         "value": round(T / (med * 1e-3), 1), "unit": "tokens/s", "ms": round(med, 4),

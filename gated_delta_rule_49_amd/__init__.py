@@ -34,7 +34,7 @@ class KdaFwdArgs(ctypes.Structure):
         ("initial_state", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
         ("checkpoint_every", ctypes.c_int32), ("checkpoints", ctypes.c_void_p), ("o", ctypes.c_void_p),
         ("initial_state_indices", ctypes.c_void_p), ("checkpoint_indices", ctypes.c_void_p),
-        ("num_slots", ctypes.c_int32),
+        ("num_slots", ctypes.c_int32), ("gate_mode", ctypes.c_int32), ("normalize_qk", ctypes.c_int32),
     ]
 
 
@@ -120,7 +120,7 @@ DEFAULT_CHUNK = 32
 
 def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final_state, checkpoint_every,
                   checkpoints, o, chunk_size=DEFAULT_CHUNK, initial_state_indices=None, checkpoint_indices=None,
-                  num_slots=0):
+                  num_slots=0, gate_preactivation=False, normalize_qk=False):
     T, H, dk = q.shape
     a = KdaFwdArgs()
     a.struct_size = ctypes.sizeof(KdaFwdArgs)
@@ -143,12 +143,14 @@ def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final
     a.initial_state_indices = _ptr(initial_state_indices)
     a.checkpoint_indices = _ptr(checkpoint_indices)
     a.num_slots = int(num_slots)
+    a.gate_mode = 1 if gate_preactivation else 0
+    a.normalize_qk = 1 if normalize_qk else 0
     return a
 
 
 def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, output_final_state=True,
                   checkpoint_every=0, stream=None, chunk_size=DEFAULT_CHUNK, initial_state_indices=None,
-                  state_pool=None, checkpoint_indices=None):
+                  state_pool=None, checkpoint_indices=None, gate_preactivation=False, normalize_qk=False):
     """Chunked KDA prefill (packed varlen).
 
     q, k: [T, H, dk]; v: [T, H, dv] (bf16 or fp32, CUDA, contiguous); g: [T, H, dk] fp32;
@@ -159,6 +161,9 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
     (CUDA; -1 = zeros) picks each sequence's initial state from the pool (initial_state is then
     ignored), and checkpoint_indices int32 [M] (CUDA; -1 = not written) writes checkpoint m
     into pool slot checkpoint_indices[m] instead of returning a checkpoint tensor.
+    Fused prologue (chunk_size 32): gate_preactivation=True takes g as bf16 pre-activations a
+    and beta as fp32 pre-activations b (g = -5 sigmoid(a), beta = sigmoid(b)); normalize_qk=True
+    L2-normalises q and k per (token, head) inside the operator.
     Returns (o [T,H,dv] fp32, final_state [N,H,dk,dv] fp32 or None, checkpoints or None).
     """
     T, H, dk = q.shape
@@ -182,7 +187,8 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
     ck_arg = state_pool if checkpoint_indices is not None else ck
     nslots = int(state_pool.shape[0]) if state_pool is not None else 0
     a = make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, s0, sf, checkpoint_every, ck_arg, o,
-                      chunk_size, initial_state_indices, checkpoint_indices, nslots)
+                      chunk_size, initial_state_indices, checkpoint_indices, nslots, gate_preactivation,
+                      normalize_qk)
     L = lib()
     ws_bytes = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a))
     if ws_bytes == 0 and N > 0:

@@ -17,7 +17,7 @@ extern "C" hipError_t kda_launch_chunk(int chunk, int dk, int in_bf16, int N, in
                                        const void *v, const float *g, const float *beta, const int32_t *cu,
                                        const float *s0, float *sf, int every, float *ckpt, float *o,
                                        float scale, const int32_t *s0_idx, const int32_t *ck_idx,
-                                       int nslots, void *workspace, hipStream_t stream);
+                                       int nslots, int flags, void *workspace, hipStream_t stream);
 
 namespace {
 
@@ -68,6 +68,13 @@ kda_status validate_fwd(const kda_fwd_args *a) {
     if ((a->initial_state_indices || a->checkpoint_indices) && a->num_slots < 1) return KDA_ERR_INVALID_ARGUMENT;
     if (a->initial_state_indices && a->num_seqs > 0 && !a->initial_state) return KDA_ERR_INVALID_ARGUMENT;
     if (a->checkpoint_indices && a->checkpoint_every == 0) return KDA_ERR_INVALID_ARGUMENT;
+    // fused prologue
+    if ((a->gate_mode != KDA_GATE_LOG_DECAY && a->gate_mode != KDA_GATE_PREACTIVATION) ||
+        (a->normalize_qk != 0 && a->normalize_qk != 1))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if ((a->gate_mode != KDA_GATE_LOG_DECAY || a->normalize_qk) &&
+        (a->chunk_size != 32 || a->in_dtype != KDA_BF16 || a->dk != 128))
+        return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
 }
 
@@ -106,6 +113,7 @@ kda_status kda_chunk_fwd(const kda_fwd_args *a, void *workspace, size_t workspac
                                           a->v, a->g, a->beta, a->cu_seqlens, a->initial_state, a->final_state,
                                           a->checkpoint_every, a->checkpoints, a->o, a->scale,
                                           a->initial_state_indices, a->checkpoint_indices, a->num_slots,
+                                          (a->gate_mode == KDA_GATE_PREACTIVATION ? 1 : 0) | (a->normalize_qk ? 2 : 0),
                                           workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }

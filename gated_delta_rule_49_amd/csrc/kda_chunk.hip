@@ -524,8 +524,9 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int
                                        const void *v, const float *g, const float *beta, const int32_t *cu,
                                        const float *s0, float *sf, int every, float *ckpt, float *o,
                                        float scale, const int32_t *s0_idx, const int32_t *ck_idx,
-                                       int nslots, void *workspace, hipStream_t stream) {
+                                       int nslots, int flags, void *workspace, hipStream_t stream) {
     if (N == 0) return hipSuccess;
+    if (flags != 0 && chunk != 32) return hipErrorInvalidValue;   // fused prologue: chunk 32 only
     size_t oo, bo;
     kda_chunk_workspace_layout(N, &oo, &bo);
     int32_t *order = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + oo);
@@ -537,7 +538,7 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int
     kda::ChunkParams p;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu_seqlens = cu; p.order = order;
     p.ckpt_base = base; p.s0 = s0; p.sf = sf; p.ckpt = ckpt; p.o = o; p.H = H; p.every = every;
-    p.scale = scale; p.s0_idx = s0_idx; p.ck_idx = ck_idx; p.nslots = nslots;
+    p.scale = scale; p.s0_idx = s0_idx; p.ck_idx = ck_idx; p.nslots = nslots; p.flags = flags;
     const dim3 grid((unsigned)N * (unsigned)H);
     if (chunk == 32) return kda_launch_chunk32(dk, in_bf16, grid.x, p, stream);
 #define KDA_CHUNK(DKV, F32P, T) \

@@ -90,7 +90,8 @@ struct Lds32 {
     static constexpr int BETA = XCHG + 8 * DK * 4;        // 2 x [32] fp32
     // scan-wave stash: each scan lane parks its 8 JT (Gamma*Q) S partial outputs here between
     // segments 1 and 2 (register pressure), tile j of lane l at OST + (j * 64 NSW + l) * 16 bytes
-    static constexpr int OST = BETA + 2 * 32 * 4;
+    static constexpr int NRM = BETA + 2 * 32 * 4;         // [32][2] fp32: 1/|k|, 1/|q| per row (fused prologue)
+    static constexpr int OST = NRM + 32 * 2 * 4;
     static constexpr int TOTAL = OST + 2 * JT * 64 * NSW * 16;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -142,7 +143,9 @@ template <int JT> __device__ __forceinline__ void store_cols(float *ptr, const f
     else *ptr = x[0];
 }
 
-template <int DK, int SPLIT, bool F32P, typename IN_T>
+// PRO: the fused prologue (KDA_PRO_* bits), a compile-time choice so that the plain path keeps
+// none of its code.
+template <int DK, int SPLIT, bool F32P, typename IN_T, int PRO = 0>
 __global__ void __launch_bounds__((chunk32_threads<DK, SPLIT>()))
 chunk32_kernel(const ChunkParams p) {
     constexpr int DV = DK;
@@ -614,13 +617,16 @@ chunk32_kernel(const ChunkParams p) {
             const size_t base = (size_t)t0 * H * DK;
             const IN_T *kb = kg + base, *qb = qg + base;
             const float *gb = p.g + base;
+            const uint16_t *ab = reinterpret_cast<const uint16_t *>(p.g) + base;   // bf16 pre-activations
+            constexpr bool pre = PRO & KDA_PRO_GATE;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = min(4 * rgp + i, nv - 1);
                 const unsigned off = (unsigned)((r * H + h) * DK + c0);
                 kn_[i] = PR::load(kb + off);
                 qn_[i] = PR::load(qb + off);
-                gn_[i] = *reinterpret_cast<const float2 *>(gb + off);
+                if constexpr (pre) gn_[i].x = __uint_as_float(*reinterpret_cast<const uint32_t *>(ab + off));   // a pair
+                else gn_[i] = *reinterpret_cast<const float2 *>(gb + off);
             }
             bn_ = p.beta[(size_t)t0 * H + (unsigned)(min(4 * rgp + (cp & 3), nv - 1) * H + h)];
         };
@@ -653,16 +659,59 @@ chunk32_kernel(const ChunkParams p) {
             // ---- seg 1, P1(nxt): alpha = exp(g), running products over the 4-row group
             if (have) {
                 const int nv = min(C32, seq_len - nxt * C32);
+                constexpr bool pre = PRO & KDA_PRO_GATE;
                 float al[4][2];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const bool valid = 4 * rgp + i < nv;   // padded rows: k = q = 0, alpha = 1, beta = 0
                     kr[i] = valid ? kn_[i] : PR::zero();
                     qr[i] = valid ? qn_[i] : PR::zero();
-                    al[i][0] = valid ? __expf(gn_[i].x) : 1.f;
-                    al[i][1] = valid ? __expf(gn_[i].y) : 1.f;
+                    float gx[2] = {gn_[i].x, gn_[i].y};
+                    if constexpr (pre) {
+                        // fused gate: g = -5 sigmoid(a), a a bf16 pair
+                        const uint32_t ab = __float_as_uint(gn_[i].x);
+                        gx[0] = -5.f * __builtin_amdgcn_rcpf(1.f + __expf(-lo_bf16_of(ab)));
+                        gx[1] = -5.f * __builtin_amdgcn_rcpf(1.f + __expf(-hi_bf16_of(ab)));
+                    }
+                    al[i][0] = valid ? __expf(gx[0]) : 1.f;
+                    al[i][1] = valid ? __expf(gx[1]) : 1.f;
                 }
-                if (cp < 4) s_beta[4 * rgp + cp] = 4 * rgp + cp < nv ? bn_ : 0.f;
+                if (cp < 4) {
+                    float bv = bn_;
+                    if constexpr (pre) bv = __builtin_amdgcn_rcpf(1.f + __expf(-bn_));   // sigmoid(b)
+                    s_beta[4 * rgp + cp] = 4 * rgp + cp < nv ? bv : 0.f;
+                }
+                if constexpr ((PRO & KDA_PRO_NORM) != 0) {
+                    // 1/|k|, 1/|q| of each row (0 for a zero row): sums of squares over the NCP lanes
+                    // holding the row, then one lane per group -> LDS for P2
+                    float ss[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float k0 = PR::lo(kr[i]), k1 = PR::hi(kr[i]), q0 = PR::lo(qr[i]), q1 = PR::hi(qr[i]);
+                        ss[2 * i] = k0 * k0 + k1 * k1;
+                        ss[2 * i + 1] = q0 * q0 + q1 * q1;
+                    }
+                    // inside each row of 16 lanes by DPP rotations, then across the rows
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        ss[j] += dpp_f32<0x128>(ss[j]);   // row_ror:8
+                        ss[j] += dpp_f32<0x124>(ss[j]);   // row_ror:4
+                        ss[j] += dpp_f32<0x122>(ss[j]);   // row_ror:2
+                        ss[j] += dpp_f32<0x121>(ss[j]);   // row_ror:1
+                    }
+#pragma unroll
+                    for (int off = 16; off < NCP; off <<= 1)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) ss[j] += shfl_xor(ss[j], off);
+                    if (cp == 0) {
+                        float nr[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) nr[j] = ss[j] > 0.f ? rsqrtf(ss[j]) : 0.f;
+                        float4 *dn = reinterpret_cast<float4 *>(sm + L::NRM + 4 * rgp * 8);
+                        dn[0] = make_float4(nr[0], nr[1], nr[2], nr[3]);
+                        dn[1] = make_float4(nr[4], nr[5], nr[6], nr[7]);
+                    }
+                }
                 float tot[2];
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
@@ -717,7 +766,12 @@ chunk32_kernel(const ChunkParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float ks[2], qs[2], ke[2], kd[2];
-                    const float kv[2] = {PR::lo(kr[i]), PR::hi(kr[i])}, qv[2] = {PR::lo(qr[i]), PR::hi(qr[i])};
+                    float kv[2] = {PR::lo(kr[i]), PR::hi(kr[i])}, qv[2] = {PR::lo(qr[i]), PR::hi(qr[i])};
+                    if constexpr ((PRO & KDA_PRO_NORM) != 0) {   // fused normalisation: row factors from P1
+                        const float2 nr = *reinterpret_cast<const float2 *>(sm + L::NRM + (4 * rgp + i) * 8);
+                        kv[0] *= nr.x; kv[1] *= nr.x;
+                        qv[0] *= nr.y; qv[1] *= nr.y;
+                    }
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
                         const float es = Fw[i][c] * lead[c];   // e^{G_r - G_ref}
@@ -796,20 +850,34 @@ kda_launch_chunk32(int dk, int in_bf16, unsigned chains, const kda::ChunkParams 
     // One workgroup per (sequence, head) chain; when the chains would leave more than half the
     // compute units idle, split each chain's value columns over two workgroups.
     const int split = (long long)chains * 2 <= kda_cu_count() ? 2 : 1;
-#define KDA_C32(DKV, SP, F32P, T)                                                                        \
-    hipLaunchKernelGGL((kda::chunk32_kernel<DKV, SP, F32P, T>), dim3(chains * SP),                      \
+#define KDA_C32(DKV, SP, F32P, T, PRO)                                                                   \
+    hipLaunchKernelGGL((kda::chunk32_kernel<DKV, SP, F32P, T, PRO>), dim3(chains * SP),                 \
                        dim3(kda::chunk32_threads<DKV, SP>()), 0, stream, p)
+    if (p.flags != 0) {
+        // fused prologue: bf16 inputs, d_k = 128
+        if (dk != 128 || !in_bf16 || p.flags > 3) return hipErrorInvalidValue;
+        if (split == 2) {
+            if (p.flags == 1) KDA_C32(128, 2, false, uint16_t, 1);
+            else if (p.flags == 2) KDA_C32(128, 2, false, uint16_t, 2);
+            else KDA_C32(128, 2, false, uint16_t, 3);
+        } else {
+            if (p.flags == 1) KDA_C32(128, 1, false, uint16_t, 1);
+            else if (p.flags == 2) KDA_C32(128, 1, false, uint16_t, 2);
+            else KDA_C32(128, 1, false, uint16_t, 3);
+        }
+        return hipGetLastError();
+    }
     if (split == 2) {
-        if (dk == 128 && in_bf16) KDA_C32(128, 2, false, uint16_t);
-        else if (dk == 128) KDA_C32(128, 2, true, float);
-        else if (dk == 64 && in_bf16) KDA_C32(64, 2, false, uint16_t);
-        else if (dk == 64) KDA_C32(64, 2, true, float);
+        if (dk == 128 && in_bf16) KDA_C32(128, 2, false, uint16_t, 0);
+        else if (dk == 128) KDA_C32(128, 2, true, float, 0);
+        else if (dk == 64 && in_bf16) KDA_C32(64, 2, false, uint16_t, 0);
+        else if (dk == 64) KDA_C32(64, 2, true, float, 0);
         else return hipErrorInvalidValue;
     } else {
-        if (dk == 128 && in_bf16) KDA_C32(128, 1, false, uint16_t);
-        else if (dk == 128) KDA_C32(128, 1, true, float);
-        else if (dk == 64 && in_bf16) KDA_C32(64, 1, false, uint16_t);
-        else if (dk == 64) KDA_C32(64, 1, true, float);
+        if (dk == 128 && in_bf16) KDA_C32(128, 1, false, uint16_t, 0);
+        else if (dk == 128) KDA_C32(128, 1, true, float, 0);
+        else if (dk == 64 && in_bf16) KDA_C32(64, 1, false, uint16_t, 0);
+        else if (dk == 64) KDA_C32(64, 1, true, float, 0);
         else return hipErrorInvalidValue;
     }
 #undef KDA_C32

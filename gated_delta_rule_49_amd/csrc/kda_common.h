@@ -64,6 +64,14 @@ __device__ __forceinline__ int lane_id() {
 
 // ---- wave-level helpers ---------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+// v from another lane of the same 16-lane row, by a DPP control (e.g. 0x121..0x12F: row_ror:1..15)
+template <int CTRL> __device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Fused prologue of the chunked prefill (bits of ChunkParams::flags).
+constexpr int KDA_PRO_GATE = 1;   // g holds bf16 pre-activations a (g = -5 sigmoid(a)), beta fp32 b (sigmoid(b))
+constexpr int KDA_PRO_NORM = 2;   // q and k are L2-normalised per (token, head) over d_k
 
 // ---- MFMA ------------------------------------------------------------------
 // 16x16 output tiles: lane l holds D[4*(l/16) + e][l % 16], e = 0..3.

@@ -206,6 +206,7 @@ struct ChunkParams {
     const int32_t *s0_idx;         // NULL, or the pool slot of each sequence's initial state (-1: zeros)
     const int32_t *ck_idx;         // NULL, or the pool slot of each checkpoint (-1: not written)
     int nslots;                    // slots of the pool(s) when an index array is set
+    int flags;                     // KDA_PRO_GATE: g, beta are pre-activations; KDA_PRO_NORM: normalise q, k
     int H;
     int every;
     float scale;

@@ -70,6 +70,15 @@ typedef enum {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
+/* What kda_fwd_args.g and .beta hold. */
+typedef enum {
+    KDA_GATE_LOG_DECAY = 0,      /* g: fp32 log-decay [T,H,dk]; beta: fp32 [T,H] */
+    KDA_GATE_PREACTIVATION = 1   /* g: bf16 pre-activations a [T,H,dk] (raw 16-bit words); beta: fp32
+                                    pre-activations b [T,H]; the operator uses g = -5*sigmoid(a) and
+                                    beta = sigmoid(b) (skill card quick facts: lower-bounded scaled
+                                    sigmoid, g_min = -5) */
+} kda_gate_mode;
+
 /*
  * Chunked prefill over packed variable-length sequences.
  *
@@ -110,6 +119,14 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *                    written to slot checkpoint_indices[m] (-1: not written).
  *   num_slots        >= 1 when either index array is set; else ignored.
  *                    final_state stays [N, H, dk, dv] either way.
+ *   gate_mode        kda_gate_mode: KDA_GATE_PREACTIVATION fuses the gate
+ *                    (g = -5 sigmoid(a), beta = sigmoid(b)) into the first stage, halving
+ *                    the bytes of g.
+ *   normalize_qk     1: q and k are L2-normalised per (token, head) over dk inside the
+ *                    operator (a zero vector stays zero); `scale` still applies.  0: used
+ *                    as given.
+ *                    Either prologue needs chunk_size 32, bf16 inputs and dk = 128 (else
+ *                    KDA_ERR_UNSUPPORTED).
  */
 typedef struct {
     uint32_t struct_size;
@@ -136,6 +153,8 @@ typedef struct {
     const int32_t *initial_state_indices;
     const int32_t *checkpoint_indices;
     int32_t num_slots;
+    int32_t gate_mode;
+    int32_t normalize_qk;
 } kda_fwd_args;
 
 /* Device workspace (bytes) that kda_chunk_fwd needs for `args` (host only; no

@@ -279,3 +279,36 @@ def test_prefill_paged_pool(chunk):
                                       "ckpt": W.rel_max_err(pool_g[written], pool_r[written])}, TOL["bf16"])
     rest = [s for s in range(P) if s not in set(written.tolist())]
     np.testing.assert_array_equal(pool_g[rest], pool[rest])
+
+
+# ---- fused gate / normalisation prologue ---------------------------------------------------------
+@pytest.mark.parametrize("gate,norm", [(True, True), (True, False), (False, True)])
+def test_prefill_fused_prologue(gate, norm):
+    """chunk 32 with the gate (g = -5 sigmoid(a) from bf16 a, beta = sigmoid(b)) and/or the L2
+    normalisation of q, k fused into the first stage, against the oracle's prologue + recurrence.
+    Ragged sequences, initial states, checkpoints every 64."""
+    w = W.make_prefill_raw([200, 1, 0, 130, 333], H=3, dk=128, dv=128, seed=51, s0_std=0.1,
+                           checkpoint_every=64)
+    scale = 128 ** -0.5
+    qn, kn, g64, b64 = oracle.prologue(w.q, w.k, w.g, w.beta, normalize=norm)
+    if not norm:
+        # unnormalised q, k would make the recurrence blow up: use unit rows (still bf16-exact)
+        qn = W.round_bf16((w.q / np.linalg.norm(w.q, axis=-1, keepdims=True)).astype(np.float32))
+        kn = W.round_bf16((w.k / np.linalg.norm(w.k, axis=-1, keepdims=True)).astype(np.float32))
+    q_in, k_in = (w.q, w.k) if norm else (qn, kn)
+    if gate:
+        g_in, b_in = to_dev(w.g, torch.bfloat16), to_dev(w.beta, torch.float32)
+        g_ref, b_ref = g64, b64
+    else:
+        g32, b32 = g64.astype(np.float32), b64.astype(np.float32)
+        g_in, b_in = to_dev(g32, torch.float32), to_dev(b32, torch.float32)
+        g_ref, b_ref = g32, b32
+    o, sf, ck = kda.kda_chunk_fwd(to_dev(q_in, torch.bfloat16), to_dev(k_in, torch.bfloat16),
+                                  to_dev(w.v, torch.bfloat16), g_in, b_in, list(w.cu_seqlens), scale,
+                                  to_dev(w.s0, torch.float32), True, 64, chunk_size=32,
+                                  gate_preactivation=gate, normalize_qk=norm)
+    torch.cuda.synchronize()
+    o_r, sf_r, ck_r = oracle.forward(qn, kn, w.v, g_ref, b_ref, w.cu_seqlens, scale, w.s0, checkpoint_every=64)
+    _log(f"fused prologue gate={gate} norm={norm}",
+         {"o": W.rel_max_err(o.cpu().numpy(), o_r), "S": W.rel_max_err(sf.cpu().numpy(), sf_r),
+          "ckpt": W.rel_max_err(ck.cpu().numpy(), ck_r)}, TOL["bf16"])
