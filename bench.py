@@ -390,13 +390,25 @@ def summarize_trace(trace_dir, bench_json):
             "decode step N=256 H=96 d_k=d_v=128 (bf16 q/k/v, fp32 g/beta, fp32 state in place)", "decode_kernel",
             b.get("decode", {}).get("ms")),
     }
+    # per-dispatch durations, in launch order, to average over the timed launches only (the
+    # warm-up launches come first; the paged decode launches after the timed steps)
+    tpath = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    disp = []
+    if tpath:
+        with open(tpath[0]) as f:
+            disp = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+                           for r in csv.DictReader(f)), key=lambda x: x[0])
     for fname, (wl, kname, ev_ms) in out.items():
         avg = [float(r["AverageNs"]) for r in rows if kname in r["Name"]]
+        durs = [e - s_ for s_, e, n in disp if kname in n][b["warmup"]:b["warmup"] + b["steps"]]
         with open(os.path.join(ROOT, "profiles", fname), "w") as f:
             f.write(f"# {kname}: rocprofv3 kernel trace\n\nWorkload: {wl}.\n\n")
             if avg:
-                f.write(f"rocprofv3 average duration of {kname}: {avg[0] / 1e6:.4f} ms; bench.py HIP-event "
-                        f"average over the timed steps (same process): {ev_ms} ms.\n\n")
+                f.write(f"rocprofv3 average duration of {kname} over all its dispatches: {avg[0] / 1e6:.4f} ms")
+                if durs:
+                    f.write(f"; over the {len(durs)} timed launches (warm-up excluded): "
+                            f"{sum(durs) / len(durs) / 1e6:.4f} ms")
+                f.write(f".  bench.py HIP-event average over the timed steps (same process): {ev_ms} ms.\n\n")
             f.write(f"Command:\n\n    {cmd}\n\nAll kernels of the run:\n\n{table}")
     print("wrote", ", ".join(out))
 
