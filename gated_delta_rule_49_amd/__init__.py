@@ -3,8 +3,9 @@ implementation of the Kimi Delta Attention (KDA) operator.
 
 This module only marshals arguments: it takes torch tensors for device memory
 and the current HIP stream, and calls the C ABI declared in ``include/kda.h``
-(same names: ``kda_chunk_fwd``, ``kda_decode_step``,
-``kda_chunk_fwd_workspace_bytes``, ``kda_status_str``, ``kda_abi_version``).
+(same names: ``kda_chunk_fwd``, ``kda_chunk_bwd``, ``kda_decode_step``,
+``kda_chunk_fwd_workspace_bytes``, ``kda_chunk_bwd_workspace_bytes``, ``kda_status_str``,
+``kda_abi_version``).
 Every step of the computation runs in the library's HIP kernels; there is no
 fallback of any kind -- if ``libkda.so`` is missing or fails to load, every
 call raises.
@@ -48,8 +49,22 @@ class KdaDecodeArgs(ctypes.Structure):
     ]
 
 
-EXPORTED = ["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_status_str",
-            "kda_abi_version"]
+class KdaBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+        ("initial_state", ctypes.c_void_p), ("d_o", ctypes.c_void_p), ("d_final_state", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk_out", ctypes.c_void_p), ("dv_out", ctypes.c_void_p),
+        ("dg", ctypes.c_void_p), ("dbeta", ctypes.c_void_p), ("d_initial_state", ctypes.c_void_p),
+    ]
+
+
+EXPORTED = ["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
+            "kda_decode_step", "kda_status_str", "kda_abi_version"]
 
 _lib = None
 _lock = threading.Lock()
@@ -69,6 +84,11 @@ def lib():
             L.kda_chunk_fwd.restype = ctypes.c_int
             L.kda_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(KdaFwdArgs)]
             L.kda_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+            L.kda_chunk_bwd.argtypes = [ctypes.POINTER(KdaBwdArgs), ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]
+            L.kda_chunk_bwd.restype = ctypes.c_int
+            L.kda_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(KdaBwdArgs)]
+            L.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
             L.kda_decode_step.argtypes = [ctypes.POINTER(KdaDecodeArgs), ctypes.c_void_p]
             L.kda_decode_step.restype = ctypes.c_int
             L.kda_status_str.argtypes = [ctypes.c_int]
@@ -198,6 +218,70 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
     _check(L.kda_chunk_fwd(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
                            _stream(stream)))
     return o, sf, ck
+
+
+def _cu_host(cu_seqlens, T):
+    if cu_seqlens is None:
+        return torch.tensor([0, T], dtype=torch.int32)
+    if isinstance(cu_seqlens, torch.Tensor):
+        return cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+    return torch.tensor(list(cu_seqlens), dtype=torch.int32)
+
+
+def make_bwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, d_o, d_final_state, dq, dk, dv, dg,
+                  dbeta, d_initial_state):
+    T, H, dk_ = q.shape
+    a = KdaBwdArgs()
+    a.struct_size = ctypes.sizeof(KdaBwdArgs)
+    a.num_seqs = int(cu_host.numel() - 1)
+    a.total_tokens = int(T)
+    a.num_heads = int(H)
+    a.dk = int(dk_)
+    a.dv = int(v.shape[2])
+    a.in_dtype = _dtype_code(q)
+    a.scale = float(scale)
+    a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
+    a.cu_seqlens = _ptr(cu_dev)
+    a.cu_seqlens_host = cu_host.data_ptr()
+    a.initial_state = _ptr(initial_state)
+    a.d_o = _ptr(d_o)
+    a.d_final_state = _ptr(d_final_state)
+    a.dq, a.dk_out, a.dv_out, a.dg, a.dbeta = (_ptr(x) for x in (dq, dk, dv, dg, dbeta))
+    a.d_initial_state = _ptr(d_initial_state)
+    return a
+
+
+def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_state=None, d_final_state=None,
+                  output_d_initial_state=True, stream=None, workspace=None):
+    """Backward of kda_chunk_fwd (log-decay gates): gradients of
+    L = sum(d_o * o) + sum(d_final_state * final_state).
+
+    Inputs as for kda_chunk_fwd; d_o: fp32 [T, H, dv]; d_final_state: fp32 [N, H, dk, dv] or None
+    (zeros).  workspace: optional uint8 CUDA tensor of at least the queried size (reused by callers
+    that run the backward repeatedly).  Returns (dq, dk, dv, dg, dbeta, d_initial_state or None),
+    all fp32."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    cu_host = _cu_host(cu_seqlens, T)
+    cu_dev = cu_host.to(dev)
+    N = cu_host.numel() - 1
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dkk, dg = (torch.empty((T, H, dk), **f32) for _ in range(3))
+    dvv = torch.empty((T, H, dv), **f32)
+    db = torch.empty((T, H), **f32)
+    ds0 = torch.empty((N, H, dk, dv), **f32) if output_d_initial_state else None
+    a = make_bwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, d_o, d_final_state, dq, dkk, dvv,
+                      dg, db, ds0)
+    L = lib()
+    ws_bytes = int(L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a)))
+    if ws_bytes == 0 and N > 0:
+        _check(L.kda_chunk_bwd(ctypes.byref(a), None, 0, _stream(stream)))
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(L.kda_chunk_bwd(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
+                           ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return dq, dkk, dvv, dg, db, ds0
 
 
 def make_decode_args(q, k, v, g, beta, state, o, scale, state_indices=None):

@@ -18,6 +18,13 @@ extern "C" hipError_t kda_launch_chunk(int chunk, int dk, int in_bf16, int N, in
                                        const float *s0, float *sf, int every, float *ckpt, float *o,
                                        float scale, const int32_t *s0_idx, const int32_t *ck_idx,
                                        int nslots, int flags, void *workspace, hipStream_t stream);
+extern "C" size_t kda_bwd_workspace_layout(int N, int H, int T, int dk, int dv, int64_t n_ck, int64_t n_chunks,
+                                           size_t *off);
+extern "C" hipError_t kda_launch_bwd(int dk, int in_bf16, int N, int H, int T, int64_t n_ck, int64_t n_chunks,
+                                     const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                     const int32_t *cu, const float *s0, const float *dO, const float *dSf, float *dq,
+                                     float *dkk, float *dv, float *dg, float *dbeta, float *dS0, float scale,
+                                     void *workspace, hipStream_t stream);
 
 namespace {
 
@@ -78,6 +85,50 @@ kda_status validate_fwd(const kda_fwd_args *a) {
     return KDA_OK;
 }
 
+// Validation of kda_chunk_bwd (and its workspace query); also counts the 32-token checkpoints
+// and chunks the workspace holds.
+kda_status validate_bwd(const kda_bwd_args *a, int64_t *n_ck, int64_t *n_chunks) {
+    if (!a) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->struct_size != sizeof(kda_bwd_args)) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->num_seqs < 0 || a->total_tokens < 0 || a->num_heads <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    const kda_status d = check_dims(a->dk, a->dv, a->in_dtype);
+    if (d != KDA_OK) return d;
+    if (!(a->scale == a->scale)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!a->cu_seqlens_host) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->num_seqs > 0 && !a->cu_seqlens) return KDA_ERR_INVALID_ARGUMENT;
+    const int32_t *cu = a->cu_seqlens_host;
+    if (cu[0] != 0) return KDA_ERR_INVALID_ARGUMENT;
+    int64_t ck = 0, ch = 0;
+    for (int n = 0; n < a->num_seqs; ++n) {
+        if (cu[n + 1] < cu[n]) return KDA_ERR_INVALID_ARGUMENT;
+        ck += (cu[n + 1] - cu[n]) / 32;
+        ch += (cu[n + 1] - cu[n] + 31) / 32;
+    }
+    if (cu[a->num_seqs] != a->total_tokens) return KDA_ERR_INVALID_ARGUMENT;
+    const void *in[] = {a->q, a->k, a->v, a->g, a->beta, a->d_o, a->initial_state, a->d_final_state};
+    const void *out[] = {a->dq, a->dk_out, a->dv_out, a->dg, a->dbeta, a->d_initial_state};
+    if (a->total_tokens > 0) {
+        for (int i = 0; i < 6; ++i)
+            if (!in[i] || !aligned16(in[i])) return KDA_ERR_INVALID_ARGUMENT;
+        for (int i = 0; i < 5; ++i)
+            if (!out[i] || !aligned16(out[i])) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if ((a->initial_state && !aligned16(a->initial_state)) || (a->d_final_state && !aligned16(a->d_final_state)) ||
+        (a->d_initial_state && !aligned16(a->d_initial_state)))
+        return KDA_ERR_INVALID_ARGUMENT;
+    // no output may alias another output or an input
+    for (int i = 0; i < 6; ++i) {
+        if (!out[i]) continue;
+        for (int j = 0; j < 8; ++j)
+            if (out[i] == in[j]) return KDA_ERR_INVALID_ARGUMENT;
+        for (int j = i + 1; j < 6; ++j)
+            if (out[i] == out[j]) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if (n_ck) *n_ck = ck;
+    if (n_chunks) *n_chunks = ch;
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -115,6 +166,28 @@ kda_status kda_chunk_fwd(const kda_fwd_args *a, void *workspace, size_t workspac
                                           a->initial_state_indices, a->checkpoint_indices, a->num_slots,
                                           (a->gate_mode == KDA_GATE_PREACTIVATION ? 1 : 0) | (a->normalize_qk ? 2 : 0),
                                           workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+size_t kda_chunk_bwd_workspace_bytes(const kda_bwd_args *a) {
+    int64_t ck, ch;
+    if (validate_bwd(a, &ck, &ch) != KDA_OK) return 0;
+    return kda_bwd_workspace_layout(a->num_seqs, a->num_heads, a->total_tokens, a->dk, a->dv, ck, ch, nullptr);
+}
+
+kda_status kda_chunk_bwd(const kda_bwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
+    int64_t ck = 0, ch = 0;
+    const kda_status st = validate_bwd(a, &ck, &ch);
+    if (st != KDA_OK) return st;
+    if (a->num_seqs == 0) return KDA_OK;
+    const size_t need = kda_bwd_workspace_layout(a->num_seqs, a->num_heads, a->total_tokens, a->dk, a->dv, ck, ch,
+                                                 nullptr);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_INVALID_ARGUMENT;
+    const hipError_t e = kda_launch_bwd(a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->total_tokens,
+                                        ck, ch, a->q, a->k, a->v, a->g, a->beta, a->cu_seqlens, a->initial_state,
+                                        a->d_o, a->d_final_state, a->dq, a->dk_out, a->dv_out, a->dg, a->dbeta,
+                                        a->d_initial_state, a->scale, workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
 

@@ -1,0 +1,693 @@
+// kda_bwd.hip -- backward of the chunked KDA prefill (gfx950): gradients of
+// L = sum(dO * O) + sum(dS_T * S_T) with respect to q, k, v, g, beta and S_0.
+//
+// The recurrence (the delta rule of the "Attention->K3 course, Day 21" quiz Q9 with the
+// per-channel forget gate of the skill card's quick facts), written per 32-token chunk with
+// S the state entering the chunk, B_r = sum_{r' <= r} g_r' (in-chunk cumulative log decay),
+// Gam_r = exp(B_r), Gam_C = exp(B_last), and per-pair factors e^{B_r - B_s} (per channel):
+//     A_rs  = sum_i k_ri k_si e^{B_ri - B_si}   (s < r)       T = (I + Diag(beta) A)^-1
+//     Aq_rs = sum_i q_ri k_si e^{B_ri - B_si}   (s <= r)
+//     X = (Gam K) S,   R = V - X,   Z = Diag(beta) R,   U = T Z
+//     O = scale ((Gam Q) S + Aq U),   S' = Gam_C S + Kbar^T U,   Kbar_s = e^{B_last - B_s} k_s
+// Given D = dL/dS' (gradient at the chunk's end) its adjoint is
+//     dU = scale Aq^T dO + Kbar D                 dZ = T^T dU         dV = Diag(beta) dZ
+//     dL/dS = Gam_C D + scale (Gam Q)^T dO - W^T dU,   W = T Diag(beta) (Gam K)
+//     dbeta_r = <dZ_r, R_r> - sum_{s<r} <dZ_r, U_s> A_rs
+//     dA_rs = -beta_r <dZ_r, U_s> (s < r)        dAq_rs = scale <dO_r, U_s> (s <= r)
+//     d(Gam Q) = scale dO S^T    d(Gam K) = -Diag(beta) dZ S^T    dKbar = U D^T
+// plus the pair terms of A and Aq.  Every factor that multiplies k_ri with e^{+B_ri} is the
+// "row side" of k (dkp), every one with e^{-B_si} the "column side" (dkm); then
+// dB = q dq + k dkp - k dkm, the last row also gets Gam_C rowsum(S * D) + sum_s Kbar_s dKbar_s,
+// and dg is the reverse cumulative sum of dB over the chunk.
+//
+// Four launches: the forward with a checkpoint every 32 tokens (states at chunk starts); a
+// per-chunk prep kernel (A, Aq, T, W, E = scale Aq^T dO); the state-gradient scan, sequential
+// over the chunks of a (sequence, head) and split over 16-column blocks of d_v; and the
+// per-chunk gradient kernel.  All products run on the fp32 MFMA (16x16x4): lane l supplies
+// row (or column) l % 16 and contraction index 4 (l / 16) + kk in instruction kk; an output
+// tile holds element (4 (l / 16) + e, l % 16) in slot e.
+//
+// The pair factors use a reference row m per 16x16 tile (7 and 23 on the diagonal tiles, 15
+// below them): e^{B_r - B_s} = e^{B_r - B_m} e^{B_m - B_s} with both factors within e^{40}
+// for decays g >= -5.
+#include "kda_frag.h"
+
+namespace kda {
+
+constexpr int BC = 32;   // chunk of the backward
+
+struct BwdParams {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const int32_t *cu;
+    const int32_t *order;          // sequences, longest first (forward plan)
+    const int64_t *ck_base;        // per sequence: its first 32-token checkpoint (forward plan)
+    const int32_t *cbase;          // [N + 1]: first chunk of each sequence
+    const float *ckpt;             // states after every 32 tokens
+    const float *s0, *dO, *dSf;
+    float *Dck;                    // [chunks, H, dk, dv]: dL/dS at the end of each chunk
+    float *Wk;                     // [chunks, H, 32, dk]
+    float *Ek;                     // [chunks, H, 32, dv]
+    float *TAk;                    // [chunks, H, 2, 32, 32]: A (masked), T
+    float *dq, *dk, *dv, *dg, *dbeta, *dS0;
+    int N, H;
+    float scale;
+};
+
+// Reference row and tile coordinates of the three lower 16x16 tiles of a 32x32 chunk matrix.
+__device__ __forceinline__ void tile_of(int tl, int &rt, int &st, int &m) {
+    rt = tl == 0 ? 0 : 1;
+    st = tl == 2 ? 1 : 0;
+    m = tl == 0 ? 7 : (tl == 1 ? 15 : 23);
+}
+
+// Largest n < N with cbase[n] <= gc (the sequence that owns chunk gc; empty sequences own none).
+__device__ __forceinline__ int seq_of_chunk(const int32_t *cbase, int N, int gc) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cbase[mid] <= gc) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ float red16(float t) {   // sum over the 16 lanes of a row group
+    t += shfl_xor(t, 1);
+    t += shfl_xor(t, 2);
+    t += shfl_xor(t, 4);
+    t += shfl_xor(t, 8);
+    return t;
+}
+
+// cbase[n] = sum_{m < n} ceil(L_m / 32), cbase[N] = total (one workgroup of 1024 threads).
+__global__ void __launch_bounds__(1024) bwd_plan_kernel(const int32_t *__restrict__ cu, int N,
+                                                         int32_t *__restrict__ cbase) {
+    __shared__ int32_t part[1024];
+    __shared__ int32_t carry;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base < N; base += 1024) {
+        const int n = base + (int)threadIdx.x;
+        const int c = n < N ? (cu[n + 1] - cu[n] + BC - 1) / BC : 0;
+        part[threadIdx.x] = c;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int32_t v = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0;
+            __syncthreads();
+            part[threadIdx.x] += v;
+            __syncthreads();
+        }
+        if (n < N) cbase[n] = carry + part[threadIdx.x] - c;
+        __syncthreads();
+        if (threadIdx.x == 1023) carry += part[1023];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) cbase[N] = carry;
+}
+
+// ---- per-chunk prep: A, T, W = T Diag(beta) (Gam K), E = scale Aq^T dO --------------------
+// One workgroup of dk/16 waves per (chunk, head).
+template <int DK, typename IN_T>
+__global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
+    constexpr int NW = DK / 16, NT = DK * 4, P = DK + 4, DV = DK;
+    __shared__ __attribute__((aligned(16))) float sk[BC][P], sq[BC][P], sb[BC][P], sdo[BC][P];
+    __shared__ float sA[BC][BC + 1], sAq[BC][BC + 1], sT[BC][BC + 1];
+    __shared__ float sbeta[BC];
+
+    const int H = p.H;
+    const int gc = (int)blockIdx.x / H, h = (int)blockIdx.x % H;
+    const int n = seq_of_chunk(p.cbase, p.N, gc);
+    const int t0 = p.cu[n] + BC * (gc - p.cbase[n]);
+    const int nv = min(BC, p.cu[n + 1] - t0);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, q4 = lane >> 4;
+    const IN_T *qg = static_cast<const IN_T *>(p.q), *kg = static_cast<const IN_T *>(p.k);
+
+    for (int idx = tid; idx < BC * DK; idx += NT) {
+        const int r = idx / DK, i = idx % DK;
+        const bool ok = r < nv;
+        const size_t off = ((size_t)(t0 + r) * H + h) * DK + i;
+        sk[r][i] = ok ? load_in(kg + off) : 0.f;
+        sq[r][i] = ok ? load_in(qg + off) : 0.f;
+        sb[r][i] = ok ? p.g[off] : 0.f;
+        sdo[r][i] = ok ? p.dO[off] : 0.f;
+    }
+    if (tid < BC) sbeta[tid] = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    for (int idx = tid; idx < BC * BC; idx += NT) {
+        sA[idx / BC][idx % BC] = 0.f;
+        sAq[idx / BC][idx % BC] = 0.f;
+    }
+    __syncthreads();
+    if (tid < DK) {
+        float a = 0.f;
+        for (int r = 0; r < BC; ++r) {
+            a += sb[r][tid];
+            sb[r][tid] = a;
+        }
+    }
+    __syncthreads();
+
+    // lower tiles of A (k against k) and Aq (q against k), each over the whole d_k
+    for (int it = w; it < 6; it += NW) {
+        int rt, st, m;
+        tile_of(it % 3, rt, st, m);
+        const bool isq = it >= 3;
+        const float *xa = isq ? sq[16 * rt + c] : sk[16 * rt + c];
+        const float *ba = sb[16 * rt + c], *bm = sb[m], *kb = sk[16 * st + c], *bb = sb[16 * st + c];
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int kg4 = 0; kg4 < DK / 4; ++kg4) {
+            const int i = 16 * (kg4 >> 2) + 4 * q4 + (kg4 & 3);
+            acc = mfma_f32(xa[i] * __expf(ba[i] - bm[i]), kb[i] * __expf(bm[i] - bb[i]), acc);
+        }
+        float(*M)[BC + 1] = isq ? sAq : sA;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rt + 4 * q4 + e, s = 16 * st + c;
+            M[r][s] = (isq ? s <= r : s < r) ? acc[e] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // T = (I + Diag(beta) A)^-1 by forward substitution: lane s of wave 0 owns column s
+    if (w == 0 && lane < BC) {
+        const int s = lane;
+        float t[BC];
+#pragma unroll
+        for (int r = 0; r < BC; ++r) {
+            float a = 0.f;
+#pragma unroll
+            for (int mm = 0; mm < r; ++mm) a += sA[r][mm] * t[mm];
+            t[r] = (r == s ? 1.f : 0.f) - sbeta[r] * a;
+        }
+#pragma unroll
+        for (int r = 0; r < BC; ++r) sT[r][s] = t[r];
+    }
+    __syncthreads();
+
+    const size_t cb = blockIdx.x;   // = chunk * H + head
+    // W = T Diag(beta) (Gam K): wave w writes columns 16 w .. 16 w + 15
+    {
+        const int i = 16 * w + c;
+        float *Wd = p.Wk + cb * BC * DK;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            for (int st = 0; st <= rt; ++st)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int s = 16 * st + 4 * q4 + kk;
+                    acc = mfma_f32(sT[16 * rt + c][s], sbeta[s] * sk[s][i] * __expf(sb[s][i]), acc);
+                }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Wd[(size_t)(16 * rt + 4 * q4 + e) * DK + i] = acc[e];
+        }
+    }
+    // E = scale Aq^T dO: wave w writes value columns 16 w .. 16 w + 15
+    {
+        const int jj = 16 * w + c;
+        float *Ed = p.Ek + cb * BC * DV;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            for (int rt = st; rt < 2; ++rt)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int r = 16 * rt + 4 * q4 + kk;
+                    acc = mfma_f32(sAq[r][16 * st + c], sdo[r][jj], acc);
+                }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ed[(size_t)(16 * st + 4 * q4 + e) * DV + jj] = p.scale * acc[e];
+        }
+    }
+    float *ta = p.TAk + cb * 2 * BC * BC;
+    for (int idx = tid; idx < BC * BC; idx += NT) {
+        ta[idx] = sA[idx / BC][idx % BC];
+        ta[BC * BC + idx] = sT[idx / BC][idx % BC];
+    }
+}
+
+// ---- state-gradient scan ------------------------------------------------------------------
+// One workgroup of 4 waves per (chain, 16-column block of d_v); wave w holds rows
+// [dk/4 w, dk/4 (w+1)) of the block of D in registers.  Walking the chunks last to first it
+// stores D (the gradient at the chunk's end) and applies
+//     D <- Gam_C D + scale (Gam Q)^T dO - W^T (E + Kbar D).
+template <int DK, typename IN_T>
+__global__ void __launch_bounds__(256) bwd_dstate_kernel(const BwdParams p) {
+    constexpr int DV = DK, NBV = DV / 16, KS = DK / 4, RT = KS / 16;
+    __shared__ float part[2][4][BC][17];   // partial Kbar D of each wave, double-buffered
+    __shared__ float scr[4][BC][KS + 1];   // per wave: cumulative log decay of its rows of d_k
+
+    const int H = p.H, chains = p.N * H;
+    // the NBV workgroups of one chain are consecutive modulo 8, so they share an XCD
+    const int b = blockIdx.x;
+    const int grp = b / (8 * NBV), within = b % (8 * NBV);
+    const int gsz = min(8, chains - grp * 8);
+    const int ci = grp * 8 + within % gsz, jb = within / gsz;
+    const int n = p.order[ci / H], h = ci % H;
+    const int seq0 = p.cu[n], L = p.cu[n + 1] - seq0, nch = (L + BC - 1) / BC;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, q4 = lane >> 4;
+    const int j0 = 16 * jb, kr0 = KS * w;
+    const size_t st_off = ((size_t)n * H + h) * DK * DV;
+    const IN_T *qg = static_cast<const IN_T *>(p.q), *kg = static_cast<const IN_T *>(p.k);
+
+    f32x4_t Dr[RT];   // D[kr0 + 16 kt + 4 q4 + e][j0 + c]
+#pragma unroll
+    for (int kt = 0; kt < RT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            Dr[kt][e] = p.dSf ? p.dSf[st_off + (size_t)(kr0 + 16 * kt + 4 * q4 + e) * DV + j0 + c] : 0.f;
+    float(*sc)[KS + 1] = scr[w];
+
+    for (int jc = nch - 1; jc >= 0; --jc) {
+        const int t0 = seq0 + BC * jc, nv = min(BC, L - BC * jc);
+        const size_t cb = (size_t)(p.cbase[n] + jc) * H + h;
+        float *dd = p.Dck + cb * DK * DV;
+#pragma unroll
+        for (int kt = 0; kt < RT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dd[(size_t)(kr0 + 16 * kt + 4 * q4 + e) * DV + j0 + c] = Dr[kt][e];
+
+        for (int idx = lane; idx < BC * KS; idx += 64) {
+            const int r = idx / KS, col = idx % KS;
+            sc[r][col] = r < nv ? p.g[((size_t)(t0 + r) * H + h) * DK + kr0 + col] : 0.f;
+        }
+        wave_lds_sync();
+        if (lane < KS) {
+            float a = 0.f;
+            for (int r = 0; r < BC; ++r) {
+                a += sc[r][lane];
+                sc[r][lane] = a;
+            }
+        }
+        wave_lds_sync();
+
+        // partial Kbar D over this wave's rows of d_k
+        float(*pp)[17] = part[jc & 1][w];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            const int r = 16 * rt + c;
+#pragma unroll
+            for (int kt = 0; kt < RT; ++kt)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int col = 16 * kt + 4 * q4 + kk;
+                    const float kv = r < nv ? load_in(kg + ((size_t)(t0 + r) * H + h) * DK + kr0 + col) : 0.f;
+                    acc = mfma_f32(kv * __expf(sc[BC - 1][col] - sc[r][col]), Dr[kt][kk], acc);
+                }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pp[16 * rt + 4 * q4 + e][c] = acc[e];
+        }
+        lds_barrier();
+
+        const float *E = p.Ek + cb * BC * DV;
+        float ndU[2][4], dOs[2][4];
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int r = 16 * rg + 4 * q4 + kk;
+                float a = E[(size_t)r * DV + j0 + c];
+#pragma unroll
+                for (int ww = 0; ww < 4; ++ww) a += part[jc & 1][ww][r][c];
+                ndU[rg][kk] = -a;
+                dOs[rg][kk] = r < nv ? p.scale * p.dO[((size_t)(t0 + r) * H + h) * DV + j0 + c] : 0.f;
+            }
+        const float *W = p.Wk + cb * BC * DK;
+#pragma unroll
+        for (int kt = 0; kt < RT; ++kt) {
+            f32x4_t acc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __expf(sc[BC - 1][16 * kt + 4 * q4 + e]) * Dr[kt][e];
+            const int col = 16 * kt + c;
+#pragma unroll
+            for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int r = 16 * rg + 4 * q4 + kk;
+                    const float qv = r < nv ? load_in(qg + ((size_t)(t0 + r) * H + h) * DK + kr0 + col) : 0.f;
+                    acc = mfma_f32(qv * __expf(sc[r][col]), dOs[rg][kk], acc);
+                    acc = mfma_f32(W[(size_t)r * DK + kr0 + col], ndU[rg][kk], acc);
+                }
+            Dr[kt] = acc;
+        }
+    }
+    if (p.dS0)
+#pragma unroll
+        for (int kt = 0; kt < RT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.dS0[st_off + (size_t)(kr0 + 16 * kt + 4 * q4 + e) * DV + j0 + c] = Dr[kt][e];
+}
+
+// ---- per-chunk gradients --------------------------------------------------------------------
+// One workgroup of dk/16 waves per (chunk, head).  Stage 1: wave w owns value columns
+// 16w..16w+15 (X, Kbar D, dZ, U, dv, the <dZ, R> part of dbeta).  Stage 2: the 32x32 products
+// <dZ_r, U_s> and <dO_r, U_s>.  Stage 3: wave w owns key channels 16w..16w+15 (dq, dk, dg).
+template <int DK, typename IN_T>
+__global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
+    constexpr int NW = DK / 16, NT = DK * 4, P = DK + 4, DV = DK;
+    __shared__ __attribute__((aligned(16))) float sk[BC][P], sq[BC][P], sb[BC][P], sdo[BC][P], sx[BC][P], sz[BC][P];
+    __shared__ float sA[BC][BC + 1], sT[BC][BC + 1], sdAq[BC][BC + 1];
+    __shared__ float sbeta[BC], sdb1[NW][BC], sdb2[3][BC];
+
+    const int H = p.H;
+    const int gc = (int)blockIdx.x / H, h = (int)blockIdx.x % H;
+    const int n = seq_of_chunk(p.cbase, p.N, gc);
+    const int jc = gc - p.cbase[n];
+    const int t0 = p.cu[n] + BC * jc;
+    const int nv = min(BC, p.cu[n + 1] - t0);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, q4 = lane >> 4;
+    const IN_T *qg = static_cast<const IN_T *>(p.q), *kg = static_cast<const IN_T *>(p.k),
+               *vg = static_cast<const IN_T *>(p.v);
+    const size_t cb = blockIdx.x;
+    const float *S = jc == 0 ? (p.s0 ? p.s0 + ((size_t)n * H + h) * DK * DV : nullptr)
+                             : p.ckpt + ((size_t)(p.ck_base[n] + jc - 1) * H + h) * DK * DV;
+    const float *D = p.Dck + cb * DK * DV;
+
+    for (int idx = tid; idx < BC * DK; idx += NT) {
+        const int r = idx / DK, i = idx % DK;
+        const bool ok = r < nv;
+        const size_t off = ((size_t)(t0 + r) * H + h) * DK + i;
+        sk[r][i] = ok ? load_in(kg + off) : 0.f;
+        sq[r][i] = ok ? load_in(qg + off) : 0.f;
+        sb[r][i] = ok ? p.g[off] : 0.f;
+        sdo[r][i] = ok ? p.dO[off] : 0.f;
+    }
+    if (tid < BC) sbeta[tid] = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    {
+        const float *ta = p.TAk + cb * 2 * BC * BC;
+        for (int idx = tid; idx < BC * BC; idx += NT) {
+            sA[idx / BC][idx % BC] = ta[idx];
+            sT[idx / BC][idx % BC] = ta[BC * BC + idx];
+            sdAq[idx / BC][idx % BC] = 0.f;
+        }
+    }
+    __syncthreads();
+    if (tid < DK) {
+        float a = 0.f;
+        for (int r = 0; r < BC; ++r) {
+            a += sb[r][tid];
+            sb[r][tid] = a;
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 1: value columns jj = 16 w + c
+    {
+        const int jj = 16 * w + c;
+        f32x4_t X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4_t Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int kt = 0; kt < DK / 16; ++kt) {
+            float sv[4], dv4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * kt + 4 * q4 + e;
+                sv[e] = S ? S[(size_t)i * DV + jj] : 0.f;
+                dv4[e] = D[(size_t)i * DV + jj];
+            }
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int i = 16 * kt + 4 * q4 + kk, r = 16 * rt + c;
+                    const float kv = sk[r][i], bi = sb[r][i];
+                    X[rt] = mfma_f32(kv * __expf(bi), sv[kk], X[rt]);
+                    Y[rt] = mfma_f32(kv * __expf(sb[BC - 1][i] - bi), dv4[kk], Y[rt]);
+                }
+        }
+        // dU = E + Kbar D, then dZ = T^T dU
+        const float *E = p.Ek + cb * BC * DV;
+        float dU[2][4];
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dU[rg][e] = E[(size_t)(16 * rg + 4 * q4 + e) * DV + jj] + Y[rg][e];
+        f32x4_t dZ[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            dZ[st] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rg = st; rg < 2; ++rg)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) dZ[st] = mfma_f32(sT[16 * rg + 4 * q4 + kk][16 * st + c], dU[rg][kk], dZ[st]);
+        }
+        // R = V - X, Z = beta R; dv = beta dZ; dbeta part <dZ_r, R_r>
+        float Zv[2][4];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 16 * st + 4 * q4 + e;
+                const bool ok = s < nv;
+                const size_t off = ((size_t)(t0 + s) * H + h) * DV + jj;
+                const float R = (ok ? load_in(vg + off) : 0.f) - X[st][e];
+                const float bs = sbeta[s];
+                Zv[st][e] = bs * R;
+                if (ok) p.dv[off] = bs * dZ[st][e];
+                const float t = red16(dZ[st][e] * R);
+                if (c == 0) sdb1[w][s] = t;
+                sz[s][jj] = dZ[st][e];
+            }
+        // U = T Z
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st <= rt; ++st)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(sT[16 * rt + c][16 * st + 4 * q4 + kk], Zv[st][kk], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sx[16 * rt + 4 * q4 + e][jj] = acc[e];
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 2: <dZ_r, U_s> -> dA (in place of A) and the A part of dbeta; <dO_r, U_s> -> dAq
+    for (int it = w; it < 6; it += NW) {
+        int rt, st, m;
+        tile_of(it % 3, rt, st, m);
+        const bool isq = it >= 3;
+        const float *xa = isq ? sdo[16 * rt + c] : sz[16 * rt + c];
+        const float *ub = sx[16 * st + c];
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int jg = 0; jg < DV / 16; ++jg) {
+            const float4 a = *reinterpret_cast<const float4 *>(xa + 16 * jg + 4 * q4);
+            const float4 u = *reinterpret_cast<const float4 *>(ub + 16 * jg + 4 * q4);
+            acc = mfma_f32(a.x, u.x, acc);
+            acc = mfma_f32(a.y, u.y, acc);
+            acc = mfma_f32(a.z, u.z, acc);
+            acc = mfma_f32(a.w, u.w, acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rt + 4 * q4 + e, s = 16 * st + c;
+            if (isq) {
+                sdAq[r][s] = s <= r ? p.scale * acc[e] : 0.f;
+            } else {
+                const bool keep = s < r;
+                const float t = red16(keep ? -acc[e] * sA[r][s] : 0.f);
+                if (c == 0) sdb2[it % 3][r] = t;
+                sA[r][s] = keep ? -sbeta[r] * acc[e] : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+
+    if (tid < nv) {
+        float a = tid < 16 ? sdb2[0][tid] : sdb2[1][tid] + sdb2[2][tid];
+        for (int ww = 0; ww < NW; ++ww) a += sdb1[ww][tid];
+        p.dbeta[(size_t)(t0 + tid) * H + h] = a;
+    }
+
+    // ---- stage 3: key channel i = 16 w + c
+    {
+        const int i = 16 * w + c;
+        f32x4_t dQt[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4_t dKt[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4_t dKb[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        float rsd = 0.f;
+        for (int jg = 0; jg < DV / 16; ++jg) {
+            const int j = 16 * jg + 4 * q4;
+            const float4 s4 = S ? *reinterpret_cast<const float4 *>(S + (size_t)i * DV + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 d4 = *reinterpret_cast<const float4 *>(D + (size_t)i * DV + j);
+            rsd += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const float4 o4 = *reinterpret_cast<const float4 *>(&sdo[16 * rt + c][j]);
+                const float4 z4 = *reinterpret_cast<const float4 *>(&sz[16 * rt + c][j]);
+                const float4 u4 = *reinterpret_cast<const float4 *>(&sx[16 * rt + c][j]);
+                dQt[rt] = mfma_f32(o4.x, s4.x, dQt[rt]);
+                dQt[rt] = mfma_f32(o4.y, s4.y, dQt[rt]);
+                dQt[rt] = mfma_f32(o4.z, s4.z, dQt[rt]);
+                dQt[rt] = mfma_f32(o4.w, s4.w, dQt[rt]);
+                dKt[rt] = mfma_f32(z4.x, s4.x, dKt[rt]);
+                dKt[rt] = mfma_f32(z4.y, s4.y, dKt[rt]);
+                dKt[rt] = mfma_f32(z4.z, s4.z, dKt[rt]);
+                dKt[rt] = mfma_f32(z4.w, s4.w, dKt[rt]);
+                dKb[rt] = mfma_f32(u4.x, d4.x, dKb[rt]);
+                dKb[rt] = mfma_f32(u4.y, d4.y, dKb[rt]);
+                dKb[rt] = mfma_f32(u4.z, d4.z, dKb[rt]);
+                dKb[rt] = mfma_f32(u4.w, d4.w, dKb[rt]);
+            }
+        }
+        rsd += shfl_xor(rsd, 16);
+        rsd += shfl_xor(rsd, 32);   // rowsum(S * D) of row i
+
+        // pair terms of A and Aq, tile by tile with the tile's reference row m
+        f32x4_t G1[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4_t G3[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4_t G24[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int tl = 0; tl < 3; ++tl) {
+            int rt, st, m;
+            tile_of(tl, rt, st, m);
+            const float bm = sb[m][i];
+            // row side (output rows r of tile rt, contraction over s of tile st)
+            f32x4_t t1 = {0.f, 0.f, 0.f, 0.f}, t3 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int s = 16 * st + 4 * q4 + kk;
+                const float kh = sk[s][i] * __expf(bm - sb[s][i]);
+                t1 = mfma_f32(sA[16 * rt + c][s], kh, t1);
+                t3 = mfma_f32(sdAq[16 * rt + c][s], kh, t3);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float f = __expf(sb[16 * rt + 4 * q4 + e][i] - bm);
+                G1[rt][e] += f * t1[e];
+                G3[rt][e] += f * t3[e];
+            }
+            // column side (output rows s of tile st, contraction over r of tile rt)
+            f32x4_t t2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int r = 16 * rt + 4 * q4 + kk;
+                const float f = __expf(sb[r][i] - bm);
+                t2 = mfma_f32(sA[r][16 * st + c], sk[r][i] * f, t2);
+                t2 = mfma_f32(sdAq[r][16 * st + c], sq[r][i] * f, t2);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) G24[st][e] += __expf(bm - sb[16 * st + 4 * q4 + e][i]) * t2[e];
+        }
+
+        // assemble dq, dk and dB (into sq: this wave's columns only)
+        const float bl = sb[BC - 1][i];
+        float cs = 0.f, dBv[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + 4 * q4 + e;
+                const float br = sb[r][i], gm = __expf(br), eb = __expf(bl - br);
+                const float dqv = gm * p.scale * dQt[rt][e] + G3[rt][e];
+                const float dkp = -gm * sbeta[r] * dKt[rt][e] + G1[rt][e];
+                const float kbg = eb * dKb[rt][e];
+                const float dkm = kbg + G24[rt][e];
+                const float kr = sk[r][i];
+                cs += kr * kbg;
+                dBv[rt][e] = sq[r][i] * dqv + kr * (dkp - dkm);
+                if (r < nv) {
+                    const size_t off = ((size_t)(t0 + r) * H + h) * DK + i;
+                    p.dq[off] = dqv;
+                    p.dk[off] = dkp + dkm;
+                }
+            }
+        cs += shfl_xor(cs, 16);
+        cs += shfl_xor(cs, 32);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sq[16 * rt + 4 * q4 + e][i] = dBv[rt][e];
+        wave_lds_sync();
+        if (q4 == 0) {
+            // dB of the last row also carries dL/dB_last; dg = reverse cumulative sum over the chunk
+            float a = cs + __expf(bl) * rsd;
+            for (int r = nv - 1; r >= 0; --r) {
+                a += sq[r][i];
+                p.dg[((size_t)(t0 + r) * H + h) * DK + i] = a;
+            }
+        }
+    }
+}
+
+}  // namespace kda
+
+extern "C" size_t kda_chunk_workspace_layout(int N, size_t *order_off, size_t *base_off);
+
+// Backward workspace: [forward plan][chunk bases][checkpoints every 32][forward o][D per chunk]
+// [W per chunk][E per chunk][A, T per chunk].
+extern "C" __attribute__((visibility("hidden"))) size_t kda_bwd_workspace_layout(int N, int H, int T, int dk, int dv,
+                                                                                  int64_t n_ck, int64_t n_chunks,
+                                                                                  size_t *off) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    size_t o[8];
+    o[0] = up(kda_chunk_workspace_layout(N, nullptr, nullptr));           // cbase
+    o[1] = o[0] + up((size_t)(N + 1) * 4);                                 // checkpoints
+    o[2] = o[1] + up((size_t)n_ck * H * dk * dv * 4);                       // forward o
+    o[3] = o[2] + up((size_t)T * H * dv * 4);                               // D
+    o[4] = o[3] + up((size_t)n_chunks * H * dk * dv * 4);                   // W
+    o[5] = o[4] + up((size_t)n_chunks * H * kda::BC * dk * 4);              // E
+    o[6] = o[5] + up((size_t)n_chunks * H * kda::BC * dv * 4);              // A, T
+    o[7] = o[6] + up((size_t)n_chunks * H * 2 * kda::BC * kda::BC * 4);     // end
+    if (off)
+        for (int i = 0; i < 8; ++i) off[i] = o[i];
+    return o[7];
+}
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(
+    int chunk, int dk, int in_bf16, int N, int H, const void *q, const void *k, const void *v, const float *g,
+    const float *beta, const int32_t *cu, const float *s0, float *sf, int every, float *ckpt, float *o, float scale,
+    const int32_t *s0_idx, const int32_t *ck_idx, int nslots, int flags, void *workspace, hipStream_t stream);
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
+    int dk, int in_bf16, int N, int H, int T, int64_t n_ck, int64_t n_chunks, const void *q, const void *k,
+    const void *v, const float *g, const float *beta, const int32_t *cu, const float *s0, const float *dO,
+    const float *dSf, float *dq, float *dkk, float *dv, float *dg, float *dbeta, float *dS0, float scale,
+    void *workspace, hipStream_t stream) {
+    if (N == 0) return hipSuccess;
+    size_t off[8];
+    kda_bwd_workspace_layout(N, H, T, dk, dk, n_ck, n_chunks, off);
+    char *ws = static_cast<char *>(workspace);
+    // states at every 32-token boundary (the forward's plan lands at the start of the workspace)
+    hipError_t e = kda_launch_chunk(32, dk, in_bf16, N, H, q, k, v, g, beta, cu, s0, nullptr, kda::BC,
+                                    reinterpret_cast<float *>(ws + off[1]), reinterpret_cast<float *>(ws + off[2]),
+                                    scale, nullptr, nullptr, 0, 0, ws, stream);
+    if (e != hipSuccess) return e;
+    size_t order_off, base_off;
+    kda_chunk_workspace_layout(N, &order_off, &base_off);
+    kda::BwdParams p;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu = cu;
+    p.order = reinterpret_cast<const int32_t *>(ws + order_off);
+    p.ck_base = reinterpret_cast<const int64_t *>(ws + base_off);
+    p.cbase = reinterpret_cast<const int32_t *>(ws + off[0]);
+    p.ckpt = reinterpret_cast<const float *>(ws + off[1]);
+    p.s0 = s0; p.dO = dO; p.dSf = dSf;
+    p.Dck = reinterpret_cast<float *>(ws + off[3]);
+    p.Wk = reinterpret_cast<float *>(ws + off[4]);
+    p.Ek = reinterpret_cast<float *>(ws + off[5]);
+    p.TAk = reinterpret_cast<float *>(ws + off[6]);
+    p.dq = dq; p.dk = dkk; p.dv = dv; p.dg = dg; p.dbeta = dbeta; p.dS0 = dS0;
+    p.N = N; p.H = H; p.scale = scale;
+    hipLaunchKernelGGL(kda::bwd_plan_kernel, dim3(1), dim3(1024), 0, stream, cu, N,
+                       reinterpret_cast<int32_t *>(ws + off[0]));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const unsigned chunk_blocks = (unsigned)(n_chunks * H);
+    const unsigned scan_blocks = (unsigned)N * (unsigned)H * (unsigned)(dk / 16);
+#define KDA_BWD(DKV, T_)                                                                                           \
+    do {                                                                                                           \
+        if (chunk_blocks)                                                                                          \
+            hipLaunchKernelGGL((kda::bwd_prep_kernel<DKV, T_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, p); \
+        hipLaunchKernelGGL((kda::bwd_dstate_kernel<DKV, T_>), dim3(scan_blocks), dim3(256), 0, stream, p);         \
+        if (chunk_blocks)                                                                                          \
+            hipLaunchKernelGGL((kda::bwd_grad_kernel<DKV, T_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, p); \
+    } while (0)
+    if (dk == 128 && in_bf16) KDA_BWD(128, uint16_t);
+    else if (dk == 128) KDA_BWD(128, float);
+    else if (dk == 64 && in_bf16) KDA_BWD(64, uint16_t);
+    else if (dk == 64) KDA_BWD(64, float);
+    else return hipErrorInvalidValue;
+#undef KDA_BWD
+    return hipGetLastError();
+}

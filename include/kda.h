@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2u
+#define KDA_ABI_VERSION 3u
 
 typedef enum {
     KDA_OK = 0,
@@ -198,6 +198,75 @@ typedef struct {
 } kda_decode_args;
 
 kda_status kda_decode_step(const kda_decode_args *args, void *stream);
+
+/*
+ * Backward of the chunked prefill (the pre-training kernel of the Kimi Linear
+ * page, section 5.1.1, implies one): for the scalar
+ *
+ *     L = sum(d_o * o) + sum(d_final_state * final_state)
+ *
+ * of the forward over the same inputs (log-decay gates, no pool, no fused
+ * prologue), write dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta and dL/dS_0.  Per token,
+ * walking each sequence backwards with dS = dL/dS_t, the adjoint of the
+ * recurrence is
+ *     dS += scale q_t d_o_t^T;  dq_t = scale S_t d_o_t;  du = dS^T k_t;
+ *     dv_t = beta_t du;  dbeta_t = <du, v_t - p_t>;  dp = -beta_t du;
+ *     dk_t = dS u_t + St~ dp;  dg_t = alpha_t * rowsum((dS + k_t dp^T) * S_{t-1});
+ *     dS <- Diag(alpha_t) (dS + k_t dp^T)
+ * with St~ = Diag(alpha_t) S_{t-1}, p_t = St~^T k_t, u_t = beta_t (v_t - p_t).
+ * The library evaluates it chunk by chunk (32 tokens): it recomputes the states
+ * at chunk boundaries with the forward, runs the state gradient backwards over
+ * the chunks, then forms every chunk's gradients in parallel.
+ *
+ * Fields (layouts, sizes and alignment as for kda_fwd_args):
+ *   struct_size, num_seqs, total_tokens, num_heads, dk, dv, in_dtype, scale,
+ *   q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state
+ *                    as in kda_fwd_args (initial_state NULL => zeros).
+ *   d_o              fp32 [T, H, dv]: dL/do.
+ *   d_final_state    NULL => zeros; else fp32 [N, H, dk, dv].
+ *   dq, dk_out, dg   fp32 [T, H, dk];  dv_out fp32 [T, H, dv];  dbeta fp32 [T, H].
+ *                    Written in full; none may alias another buffer of the call.
+ *   d_initial_state  NULL => not written; else fp32 [N, H, dk, dv].
+ * Supported: d_k == d_v in {64, 128}; in_dtype KDA_F32 or KDA_BF16.  The
+ * workspace (kda_chunk_bwd_workspace_bytes) holds the recomputed states, the
+ * state gradients at every chunk boundary and per-chunk factors: about
+ * (2 dk dv + 2 * 32 (dk + dv) + 3 * 32^2) * 4 bytes per (32-token chunk, head)
+ * plus T*H*dv*4 bytes.  Results are fp32 and deterministic.
+ */
+typedef struct {
+    uint32_t struct_size;
+    int32_t num_seqs;
+    int32_t total_tokens;
+    int32_t num_heads;
+    int32_t dk;
+    int32_t dv;
+    kda_dtype in_dtype;
+    float scale;
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *g;
+    const float *beta;
+    const int32_t *cu_seqlens;
+    const int32_t *cu_seqlens_host;
+    const float *initial_state;
+    const float *d_o;
+    const float *d_final_state;
+    float *dq;
+    float *dk_out;
+    float *dv_out;
+    float *dg;
+    float *dbeta;
+    float *d_initial_state;
+} kda_bwd_args;
+
+/* Device workspace (bytes) that kda_chunk_bwd needs for `args` (host only).
+ * Returns 0 when args are invalid. */
+size_t kda_chunk_bwd_workspace_bytes(const kda_bwd_args *args);
+
+/* Enqueue the backward.  `workspace`: at least kda_chunk_bwd_workspace_bytes(args)
+ * bytes of device memory, 256-byte aligned, overwritten. */
+kda_status kda_chunk_bwd(const kda_bwd_args *args, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static string for a status code. */
 const char *kda_status_str(kda_status status);

@@ -33,19 +33,23 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert kda.kda_abi_version() == 2
+    assert kda.kda_abi_version() == 3
     for code, name in enumerate(["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
                                  "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_DEVICE"]):
         assert kda.kda_status_str(code) == name
     assert kda.kda_status_str(99) == "KDA_ERR_UNKNOWN"
 
 
+STRUCTS = (("kda_fwd_args", kda.KdaFwdArgs), ("kda_decode_args", kda.KdaDecodeArgs),
+           ("kda_bwd_args", kda.KdaBwdArgs))
+
+
 def test_struct_layouts_match_header(tmp_path):
-    """Every field offset and the size of both argument structs, as compiled from
+    """Every field offset and the size of each argument struct, as compiled from
     include/kda.h by the C compiler, equal the ctypes layouts of the binding."""
     import subprocess
     prog = ["#include <stdio.h>", "#include <stddef.h>", '#include "kda.h"', "int main(void) {"]
-    for cname, pyt in (("kda_fwd_args", kda.KdaFwdArgs), ("kda_decode_args", kda.KdaDecodeArgs)):
+    for cname, pyt in STRUCTS:
         prog.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
         for f, _ in pyt._fields_:
             prog.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
@@ -58,7 +62,7 @@ def test_struct_layouts_match_header(tmp_path):
     for line in subprocess.check_output([str(exe)], text=True).splitlines():
         c, f, v = line.split()
         got[(c, f)] = int(v)
-    for cname, pyt in (("kda_fwd_args", kda.KdaFwdArgs), ("kda_decode_args", kda.KdaDecodeArgs)):
+    for cname, pyt in STRUCTS:
         assert got[(cname, "size")] == ctypes.sizeof(pyt)
         for f, _ in pyt._fields_:
             assert got[(cname, f)] == getattr(pyt, f).offset, (cname, f)
@@ -193,3 +197,63 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kda, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         kda.lib()
+
+
+def bwd_args(**over):
+    cu = over.pop("cu", [0, 100, 228])
+    cu_arr = (ctypes.c_int32 * len(cu))(*cu)
+    a = kda.KdaBwdArgs()
+    a.struct_size = ctypes.sizeof(kda.KdaBwdArgs)
+    a.num_seqs = len(cu) - 1
+    a.total_tokens = cu[-1]
+    a.num_heads = 4
+    a.dk = a.dv = 128
+    a.in_dtype = kda.KDA_BF16
+    a.scale = 1.0
+    a.q, a.k, a.v, a.g, a.beta, a.d_o = (FAKE * (i + 1) for i in range(6))
+    a.dq, a.dk_out, a.dv_out, a.dg, a.dbeta = (FAKE * (i + 20) for i in range(5))
+    a.cu_seqlens = FAKE * 8
+    a.cu_seqlens_host = ctypes.cast(cu_arr, ctypes.c_void_p).value
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a, cu_arr
+
+
+def bwd_status(L, a, ws=FAKE * 64, ws_bytes=1 << 40):
+    return L.kda_chunk_bwd(ctypes.byref(a), ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("struct_size", 8, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("num_heads", 0, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("dk", 96, kda.KDA_ERR_UNSUPPORTED),
+    ("dv", 64, kda.KDA_ERR_UNSUPPORTED),
+    ("in_dtype", 5, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("d_o", None, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("dg", None, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("dbeta", FAKE * 30 + 4, kda.KDA_ERR_INVALID_ARGUMENT),   # misaligned
+    ("dq", FAKE * 1, kda.KDA_ERR_INVALID_ARGUMENT),           # aliases q
+    ("dv_out", FAKE * 20, kda.KDA_ERR_INVALID_ARGUMENT),      # aliases dq
+    ("d_initial_state", FAKE * 6, kda.KDA_ERR_INVALID_ARGUMENT),   # aliases d_o
+    ("total_tokens", 229, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("scale", float("nan"), kda.KDA_ERR_INVALID_ARGUMENT),
+])
+def test_bwd_validation(L, field, value, expect):
+    a, keep = bwd_args(**{field: value})
+    assert bwd_status(L, a) == expect
+    assert L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_bwd_workspace(L):
+    # one sequence of 100 tokens (3 checkpoints, 4 chunks) and one of 128 (4 and 4), 4 heads, d = 128
+    a, keep = bwd_args()
+    need = L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a))
+    # checkpoints (7), forward o, and per chunk (8): D, W, E, A and T
+    expect = (7 * 4 * 128 * 128 + 228 * 4 * 128 + 8 * 4 * (128 * 128 + 2 * 32 * 128 + 2 * 32 * 32)) * 4
+    assert need % 256 == 0 and need >= expect
+    assert bwd_status(L, a, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd_status(L, a, ws=0, ws_bytes=need) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd_status(L, a, ws=FAKE * 64 + 128, ws_bytes=need) == kda.KDA_ERR_INVALID_ARGUMENT
+    b, keep2 = bwd_args(cu=[0])
+    b.num_seqs, b.total_tokens = 0, 0
+    assert bwd_status(L, b, ws=0, ws_bytes=0) == kda.KDA_OK

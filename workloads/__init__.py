@@ -33,7 +33,7 @@ import numpy as np
 
 ROOT_SEED = 20261203
 BLOCK = 4096
-_TID = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "s0": 5, "lengths": 6}
+_TID = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "s0": 5, "lengths": 6, "do": 7, "dsf": 8}
 
 
 def _rng(wid, seq, block, tensor, seed):
@@ -261,6 +261,21 @@ def config_parts(cid: int, max_tokens: int = 1 << 18, seed: int = 0, threads=Non
                                    "config", c["checkpoint_every"], wid=cid, name=c["name"], threads=threads,
                                    seq_ids=range(i, j))
         i, off = j, off + n
+
+
+def make_cotangents(w: Workload, seed=0, d_final=True, wid=120):
+    """Seeded upstream gradients for the backward of workload `w`: d_o ~ N(0, 1) fp32 [T, H, dv]
+    and (if d_final) dS_T ~ N(0, 1) fp32 [N, H, dk, dv]; drawn per sequence."""
+    do = np.empty((w.total_tokens, w.H, w.dv), dtype=np.float32)
+    cu = w.cu_seqlens
+    for s, L in enumerate(w.seqlens):
+        if L:
+            do[cu[s]:cu[s + 1]] = _rng(wid, s, 0, "do", seed).standard_normal((L, w.H, w.dv), dtype=np.float32)
+    dsf = None
+    if d_final:
+        dsf = np.stack([_rng(wid, s, 0, "dsf", seed).standard_normal((w.H, w.dk, w.dv), dtype=np.float32)
+                        for s in range(len(w.seqlens))]) if w.seqlens else np.zeros((0, w.H, w.dk, w.dv), np.float32)
+    return do, dsf
 
 
 def rel_max_err(x, ref) -> float:
