@@ -58,6 +58,9 @@ def main():
     ap.add_argument("--workload", type=int, default=0, choices=(0, 1, 2, 4),
                     help="instead of the benchmark step, time the prefill of workload 1 (T=4096, H=32) or 4 "
                          "(64 packed sequences, H=32, checkpoints every 512) and print its own JSON line")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the benchmark step, time the backward (kda_chunk_bwd) on workload 2's shape "
+                         "and print its own JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scales the HBM byte counters)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
@@ -84,6 +87,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.backward:
+        backward_workload(args.steps, args.warmup)
         return
     if args.workload:
         other_workload(args.workload, args.chunk, args.steps, args.warmup, args.prologue)
@@ -525,6 +531,81 @@ def other_workload(cid, chunk, steps, warmup, prologue=False):
         "alg_bytes": int(nbytes), "alg_GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "data": "synthetic (seeded)"}), flush=True)
+
+
+def bwd_alg_bytes(T, H, dk, dv, N, in_bytes=2):
+    """Algorithmic HBM bytes of one backward: read q, k, v, g, beta, d_o and the initial / final-state
+    gradient inputs once, write dq, dk, dv, dg, dbeta and dS_0 once (fp32 gradients)."""
+    per_tok_head = in_bytes * (2 * dk + dv) + 4 * dk + 4 + 4 * dv + 4 * (3 * dk + dv + 1)
+    return T * H * per_tok_head + 3 * N * H * dk * dv * 4
+
+
+def backward_workload(steps, warmup):
+    """Backward tokens/s on workload 2's shape (one sequence, T=65536, H=96, d=128, bf16 q/k/v,
+    initial state, d_o and dS_T upstream gradients), inputs drawn on the device with torch's seeded
+    generator from the workload distributions (timing only)."""
+    import numpy as np
+    import torch
+    import gated_delta_rule_49_amd as kda
+
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    T, H, dk, dv = 65536, 96, 128, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261203)
+    rn = lambda *shape: torch.randn(shape, generator=gen, device=dev)
+    x = rn(T, H, dk)
+    q = (x / x.norm(dim=-1, keepdim=True) * dk ** -0.5).to(bf)
+    x = rn(T, H, dk)
+    k = (x / x.norm(dim=-1, keepdim=True)).to(bf)
+    del x
+    v = rn(T, H, dv).to(bf)
+    g = -5.0 * torch.sigmoid(rn(T, H, dk))
+    beta = torch.sigmoid(rn(T, H))
+    s0 = 0.1 * rn(1, H, dk, dv)
+    do = rn(T, H, dv)
+    dsf = rn(1, H, dk, dv)
+    cu = [0, T]
+    ws = torch.empty(0, dtype=torch.uint8, device=dev)
+    out = None
+
+    def run():
+        nonlocal out, ws
+        out = kda.kda_chunk_bwd(q, k, v, g, beta, do, cu, 1.0, s0, dsf, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    # reuse one workspace (the binding allocates one per call when none is passed)
+    ws = torch.empty(_bwd_ws_bytes(kda, q, k, v, g, beta, do, cu, s0, dsf, out), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ms = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = float(np.median(ms))
+    nbytes = bwd_alg_bytes(T, H, dk, dv, 1)
+    print(json.dumps({
+        "metric": "KDA backward tokens/s", "workload": "backward of the prefill T=65536 H=96 d_k=d_v=128 bf16 "
+                                                      "q/k/v, fp32 g/beta, initial state, d_o and dS_T",
+        "tokens": T, "heads": H, "value": round(T / (med * 1e-3), 1), "unit": "tokens/s", "ms": round(med, 4),
+        "ms_p10": round(float(np.percentile(ms, 10)), 4), "ms_p90": round(float(np.percentile(ms, 90)), 4),
+        "alg_bytes": int(nbytes), "alg_GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "workspace_GB": round(ws.numel() / 1e9, 2), "data": "synthetic (seeded)"}), flush=True)
+
+
+def _bwd_ws_bytes(kda, q, k, v, g, beta, do, cu, s0, dsf, out):
+    import torch
+    cu_h = torch.tensor(cu, dtype=torch.int32)
+    a = kda.make_bwd_args(q, k, v, g, beta, cu_h.to(q.device), cu_h, 1.0, s0, do, dsf, *out)
+    return int(kda.lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(a)))
 
 
 def copy_calibration(mib):

@@ -46,12 +46,22 @@ struct BwdParams {
     const float *ckpt;             // states after every 32 tokens
     const float *s0, *dO, *dSf;
     float *Dck;                    // [chunks, H, dk, dv]: dL/dS at the end of each chunk
-    float *Wk;                     // [chunks, H, 32, dk]
-    float *Ek;                     // [chunks, H, 32, dv]
+    float *SCk;                    // [chunks, H] records of the scan's operands (ScanRec)
     float *TAk;                    // [chunks, H, 2, 32, 32]: A (masked), T
     float *dq, *dk, *dv, *dg, *dbeta, *dS0;
     int N, H;
     float scale;
+};
+
+// Per (chunk, head): the operands of the state-gradient scan, fp32, laid out so that each lane
+// of the scan reads 4 consecutive values:
+//   KB [32][dk]  Kbar = e^{B_last - B} k        QT [dk][32]  (scale Gam Q)^T
+//   WT [dk][32]  W^T                             ET [dv][32]  E^T
+//   GL [dk]      Gam_C = e^{B_last}
+template <int DK> struct ScanRec {
+    static constexpr int DV = DK;
+    static constexpr int KB = 0, QT = 32 * DK, WT = 64 * DK, ET = 96 * DK, GL = 96 * DK + 32 * DV;
+    static constexpr int SIZE = GL + DK;
 };
 
 // Reference row and tile coordinates of the three lower 16x16 tiles of a 32x32 chunk matrix.
@@ -147,6 +157,19 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
     }
     __syncthreads();
 
+    using SR = ScanRec<DK>;
+    const size_t cb = blockIdx.x;   // = chunk * H + head
+    float *rec = p.SCk + cb * SR::SIZE;
+    for (int idx = tid; idx < BC * DK; idx += NT) {
+        const int r = idx / DK, i = idx % DK;
+        rec[SR::KB + idx] = sk[r][i] * __expf(sb[BC - 1][i] - sb[r][i]);
+    }
+    for (int idx = tid; idx < BC * DK; idx += NT) {
+        const int i = idx / BC, r = idx % BC;
+        rec[SR::QT + idx] = p.scale * sq[r][i] * __expf(sb[r][i]);
+    }
+    if (tid < DK) rec[SR::GL + tid] = __expf(sb[BC - 1][tid]);
+
     // lower tiles of A (k against k) and Aq (q against k), each over the whole d_k
     for (int it = w; it < 6; it += NW) {
         int rt, st, m;
@@ -185,11 +208,9 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
     }
     __syncthreads();
 
-    const size_t cb = blockIdx.x;   // = chunk * H + head
-    // W = T Diag(beta) (Gam K): wave w writes columns 16 w .. 16 w + 15
+    // W = T Diag(beta) (Gam K), stored transposed: wave w writes columns 16 w .. 16 w + 15
     {
         const int i = 16 * w + c;
-        float *Wd = p.Wk + cb * BC * DK;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -199,14 +220,12 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
                     const int s = 16 * st + 4 * q4 + kk;
                     acc = mfma_f32(sT[16 * rt + c][s], sbeta[s] * sk[s][i] * __expf(sb[s][i]), acc);
                 }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Wd[(size_t)(16 * rt + 4 * q4 + e) * DK + i] = acc[e];
+            *reinterpret_cast<float4 *>(rec + SR::WT + i * BC + 16 * rt + 4 * q4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
-    // E = scale Aq^T dO: wave w writes value columns 16 w .. 16 w + 15
+    // E = scale Aq^T dO, stored transposed: wave w writes value columns 16 w .. 16 w + 15
     {
         const int jj = 16 * w + c;
-        float *Ed = p.Ek + cb * BC * DV;
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -216,8 +235,8 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
                     const int r = 16 * rt + 4 * q4 + kk;
                     acc = mfma_f32(sAq[r][16 * st + c], sdo[r][jj], acc);
                 }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Ed[(size_t)(16 * st + 4 * q4 + e) * DV + jj] = p.scale * acc[e];
+            *reinterpret_cast<float4 *>(rec + SR::ET + jj * BC + 16 * st + 4 * q4) =
+                make_float4(p.scale * acc[0], p.scale * acc[1], p.scale * acc[2], p.scale * acc[3]);
         }
     }
     float *ta = p.TAk + cb * 2 * BC * BC;
@@ -231,12 +250,52 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
 // One workgroup of 4 waves per (chain, 16-column block of d_v); wave w holds rows
 // [dk/4 w, dk/4 (w+1)) of the block of D in registers.  Walking the chunks last to first it
 // stores D (the gradient at the chunk's end) and applies
-//     D <- Gam_C D + scale (Gam Q)^T dO - W^T (E + Kbar D).
-template <int DK, typename IN_T>
+//     D <- Gam_C D + (scale Gam Q)^T dO - W^T (E + Kbar D),
+// with the operands of chunk j-1 loading into registers while chunk j is processed.
+template <int DK> struct ScanOps {
+    static constexpr int RT = DK / 64;   // 16-row tiles of d_k per wave
+    float4 kb[2][RT];                     // Kbar[16 rt + c][kr0 + 16 kt + 4 q4 ..]
+    float4 qt[RT][2], wt[RT][2];          // QT / WT[kr0 + 16 kt + c][16 rg + 4 q4 ..]
+    float4 et[2];                         // ET[j0 + c][16 rg + 4 q4 ..]
+    float4 gl[RT];                        // GL[kr0 + 16 kt + 4 q4 ..]
+    float dov[2][4];                      // dO[t0 + 16 rg + 4 q4 + kk][j0 + c]
+};
+
+template <int DK>
+__device__ __forceinline__ void scan_load(ScanOps<DK> &o, const BwdParams &p, size_t cb, int t0, int nv, int h,
+                                          int kr0, int j0, int c, int q4) {
+    using SR = ScanRec<DK>;
+    constexpr int RT = ScanOps<DK>::RT, DV = DK;
+    const float *rec = p.SCk + cb * SR::SIZE;
+#pragma unroll
+    for (int kt = 0; kt < RT; ++kt) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+            o.kb[rt][kt] = *reinterpret_cast<const float4 *>(rec + SR::KB + (16 * rt + c) * DK + kr0 + 16 * kt + 4 * q4);
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+            o.qt[kt][rg] = *reinterpret_cast<const float4 *>(rec + SR::QT + (kr0 + 16 * kt + c) * BC + 16 * rg + 4 * q4);
+            o.wt[kt][rg] = *reinterpret_cast<const float4 *>(rec + SR::WT + (kr0 + 16 * kt + c) * BC + 16 * rg + 4 * q4);
+        }
+        o.gl[kt] = *reinterpret_cast<const float4 *>(rec + SR::GL + kr0 + 16 * kt + 4 * q4);
+    }
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+        o.et[rg] = *reinterpret_cast<const float4 *>(rec + SR::ET + (j0 + c) * BC + 16 * rg + 4 * q4);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int r = 16 * rg + 4 * q4 + kk;
+            o.dov[rg][kk] = r < nv ? p.dO[((size_t)(t0 + r) * p.H + h) * DV + j0 + c] : 0.f;
+        }
+    }
+}
+
+__device__ __forceinline__ float f4(const float4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+
+template <int DK>
 __global__ void __launch_bounds__(256) bwd_dstate_kernel(const BwdParams p) {
-    constexpr int DV = DK, NBV = DV / 16, KS = DK / 4, RT = KS / 16;
+    constexpr int DV = DK, NBV = DV / 16, KS = DK / 4, RT = ScanOps<DK>::RT;
     __shared__ float part[2][4][BC][17];   // partial Kbar D of each wave, double-buffered
-    __shared__ float scr[4][BC][KS + 1];   // per wave: cumulative log decay of its rows of d_k
 
     const int H = p.H, chains = p.N * H;
     // the NBV workgroups of one chain are consecutive modulo 8, so they share an XCD
@@ -249,7 +308,7 @@ __global__ void __launch_bounds__(256) bwd_dstate_kernel(const BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, q4 = lane >> 4;
     const int j0 = 16 * jb, kr0 = KS * w;
     const size_t st_off = ((size_t)n * H + h) * DK * DV;
-    const IN_T *qg = static_cast<const IN_T *>(p.q), *kg = static_cast<const IN_T *>(p.k);
+    const int cb0 = p.cbase[n];
 
     f32x4_t Dr[RT];   // D[kr0 + 16 kt + 4 q4 + e][j0 + c]
 #pragma unroll
@@ -257,81 +316,69 @@ __global__ void __launch_bounds__(256) bwd_dstate_kernel(const BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             Dr[kt][e] = p.dSf ? p.dSf[st_off + (size_t)(kr0 + 16 * kt + 4 * q4 + e) * DV + j0 + c] : 0.f;
-    float(*sc)[KS + 1] = scr[w];
 
-    for (int jc = nch - 1; jc >= 0; --jc) {
-        const int t0 = seq0 + BC * jc, nv = min(BC, L - BC * jc);
-        const size_t cb = (size_t)(p.cbase[n] + jc) * H + h;
+    // one chunk of the scan with its operands in `cur`
+    auto step = [&](const ScanOps<DK> &cur, int jc) {
+        const size_t cb = (size_t)(cb0 + jc) * H + h;
         float *dd = p.Dck + cb * DK * DV;
 #pragma unroll
         for (int kt = 0; kt < RT; ++kt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) dd[(size_t)(kr0 + 16 * kt + 4 * q4 + e) * DV + j0 + c] = Dr[kt][e];
 
-        for (int idx = lane; idx < BC * KS; idx += 64) {
-            const int r = idx / KS, col = idx % KS;
-            sc[r][col] = r < nv ? p.g[((size_t)(t0 + r) * H + h) * DK + kr0 + col] : 0.f;
-        }
-        wave_lds_sync();
-        if (lane < KS) {
-            float a = 0.f;
-            for (int r = 0; r < BC; ++r) {
-                a += sc[r][lane];
-                sc[r][lane] = a;
-            }
-        }
-        wave_lds_sync();
-
         // partial Kbar D over this wave's rows of d_k
         float(*pp)[17] = part[jc & 1][w];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            const int r = 16 * rt + c;
 #pragma unroll
             for (int kt = 0; kt < RT; ++kt)
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int col = 16 * kt + 4 * q4 + kk;
-                    const float kv = r < nv ? load_in(kg + ((size_t)(t0 + r) * H + h) * DK + kr0 + col) : 0.f;
-                    acc = mfma_f32(kv * __expf(sc[BC - 1][col] - sc[r][col]), Dr[kt][kk], acc);
-                }
+                for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(f4(cur.kb[rt][kt], kk), Dr[kt][kk], acc);
 #pragma unroll
             for (int e = 0; e < 4; ++e) pp[16 * rt + 4 * q4 + e][c] = acc[e];
         }
         lds_barrier();
 
-        const float *E = p.Ek + cb * BC * DV;
-        float ndU[2][4], dOs[2][4];
+        float ndU[2][4];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int r = 16 * rg + 4 * q4 + kk;
-                float a = E[(size_t)r * DV + j0 + c];
+                float a = f4(cur.et[rg], kk);
 #pragma unroll
                 for (int ww = 0; ww < 4; ++ww) a += part[jc & 1][ww][r][c];
                 ndU[rg][kk] = -a;
-                dOs[rg][kk] = r < nv ? p.scale * p.dO[((size_t)(t0 + r) * H + h) * DV + j0 + c] : 0.f;
             }
-        const float *W = p.Wk + cb * BC * DK;
 #pragma unroll
         for (int kt = 0; kt < RT; ++kt) {
             f32x4_t acc;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = __expf(sc[BC - 1][16 * kt + 4 * q4 + e]) * Dr[kt][e];
-            const int col = 16 * kt + c;
+            for (int e = 0; e < 4; ++e) acc[e] = f4(cur.gl[kt], e) * Dr[kt][e];
 #pragma unroll
             for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const int r = 16 * rg + 4 * q4 + kk;
-                    const float qv = r < nv ? load_in(qg + ((size_t)(t0 + r) * H + h) * DK + kr0 + col) : 0.f;
-                    acc = mfma_f32(qv * __expf(sc[r][col]), dOs[rg][kk], acc);
-                    acc = mfma_f32(W[(size_t)r * DK + kr0 + col], ndU[rg][kk], acc);
+                    acc = mfma_f32(f4(cur.qt[kt][rg], kk), cur.dov[rg][kk], acc);
+                    acc = mfma_f32(f4(cur.wt[kt][rg], kk), ndU[rg][kk], acc);
                 }
             Dr[kt] = acc;
         }
+    };
+    auto fetch = [&](ScanOps<DK> &o, int jc) {
+        const int jn = jc > 0 ? jc : 0;
+        scan_load<DK>(o, p, (size_t)(cb0 + jn) * H + h, seq0 + BC * jn, min(BC, L - BC * jn), h, kr0, j0, c, q4);
+    };
+    // two operand sets used in turn: chunk j is processed while chunk j - 1 loads
+    ScanOps<DK> opA, opB;
+    if (nch > 0) fetch(opA, nch - 1);
+    for (int jc = nch - 1; jc >= 0; jc -= 2) {
+        fetch(opB, jc - 1);
+        step(opA, jc);
+        if (jc == 0) break;
+        fetch(opA, jc - 2);
+        step(opB, jc - 1);
     }
     if (p.dS0)
 #pragma unroll
@@ -345,10 +392,17 @@ __global__ void __launch_bounds__(256) bwd_dstate_kernel(const BwdParams p) {
 // 16w..16w+15 (X, Kbar D, dZ, U, dv, the <dZ, R> part of dbeta).  Stage 2: the 32x32 products
 // <dZ_r, U_s> and <dO_r, U_s>.  Stage 3: wave w owns key channels 16w..16w+15 (dq, dk, dg).
 template <int DK, typename IN_T>
-__global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(DK * 4) __attribute__((amdgpu_waves_per_eu(4)))
+bwd_grad_kernel(const BwdParams p) {
     constexpr int NW = DK / 16, NT = DK * 4, P = DK + 4, DV = DK;
-    __shared__ __attribute__((aligned(16))) float sk[BC][P], sq[BC][P], sb[BC][P], sdo[BC][P], sx[BC][P], sz[BC][P];
-    __shared__ float sA[BC][BC + 1], sT[BC][BC + 1], sdAq[BC][BC + 1];
+    // k and q in their input type; sb holds the cumulative log decay, then (per wave, its own
+    // columns) dB; sTq holds T for stage 1, then dAq.  With bf16 inputs and d = 128 two
+    // workgroups fit in one CU's LDS.
+    __shared__ __attribute__((aligned(16))) IN_T sk[BC][P], sq[BC][P];
+    __shared__ __attribute__((aligned(16))) float sb[BC][P], sx[BC][P], sz[BC][P];
+    __shared__ float sA[BC][BC + 1], sTq[BC][BC + 1];
+    float(*sT)[BC + 1] = sTq;
+    float(*sdAq)[BC + 1] = sTq;
     __shared__ float sbeta[BC], sdb1[NW][BC], sdb2[3][BC];
 
     const int H = p.H;
@@ -369,10 +423,9 @@ __global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
         const int r = idx / DK, i = idx % DK;
         const bool ok = r < nv;
         const size_t off = ((size_t)(t0 + r) * H + h) * DK + i;
-        sk[r][i] = ok ? load_in(kg + off) : 0.f;
-        sq[r][i] = ok ? load_in(qg + off) : 0.f;
+        sk[r][i] = ok ? kg[off] : IN_T(0);
+        sq[r][i] = ok ? qg[off] : IN_T(0);
         sb[r][i] = ok ? p.g[off] : 0.f;
-        sdo[r][i] = ok ? p.dO[off] : 0.f;
     }
     if (tid < BC) sbeta[tid] = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
     {
@@ -380,7 +433,6 @@ __global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
         for (int idx = tid; idx < BC * BC; idx += NT) {
             sA[idx / BC][idx % BC] = ta[idx];
             sT[idx / BC][idx % BC] = ta[BC * BC + idx];
-            sdAq[idx / BC][idx % BC] = 0.f;
         }
     }
     __syncthreads();
@@ -411,18 +463,22 @@ __global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int i = 16 * kt + 4 * q4 + kk, r = 16 * rt + c;
-                    const float kv = sk[r][i], bi = sb[r][i];
+                    const float kv = widen(sk[r][i]), bi = sb[r][i];
                     X[rt] = mfma_f32(kv * __expf(bi), sv[kk], X[rt]);
                     Y[rt] = mfma_f32(kv * __expf(sb[BC - 1][i] - bi), dv4[kk], Y[rt]);
                 }
         }
         // dU = E + Kbar D, then dZ = T^T dU
-        const float *E = p.Ek + cb * BC * DV;
+        const float *ET = p.SCk + cb * ScanRec<DK>::SIZE + ScanRec<DK>::ET + jj * BC;
         float dU[2][4];
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dU[rg][e] = E[(size_t)(16 * rg + 4 * q4 + e) * DV + jj] + Y[rg][e];
+        for (int rg = 0; rg < 2; ++rg) {
+            const float4 e4 = *reinterpret_cast<const float4 *>(ET + 16 * rg + 4 * q4);
+            dU[rg][0] = e4.x + Y[rg][0];
+            dU[rg][1] = e4.y + Y[rg][1];
+            dU[rg][2] = e4.z + Y[rg][2];
+            dU[rg][3] = e4.w + Y[rg][3];
+        }
         f32x4_t dZ[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
@@ -463,17 +519,24 @@ __global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
     }
     __syncthreads();
 
+    // dO[t0 + r][h][j .. j + 3] (zero past the chunk's valid rows)
+    auto do4 = [&](int r, int j) {
+        return r < nv ? *reinterpret_cast<const float4 *>(p.dO + ((size_t)(t0 + r) * H + h) * DV + j)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+
     // ---- stage 2: <dZ_r, U_s> -> dA (in place of A) and the A part of dbeta; <dO_r, U_s> -> dAq
     for (int it = w; it < 6; it += NW) {
         int rt, st, m;
         tile_of(it % 3, rt, st, m);
         const bool isq = it >= 3;
-        const float *xa = isq ? sdo[16 * rt + c] : sz[16 * rt + c];
+        const float *xa = sz[16 * rt + c];
         const float *ub = sx[16 * st + c];
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
         for (int jg = 0; jg < DV / 16; ++jg) {
-            const float4 a = *reinterpret_cast<const float4 *>(xa + 16 * jg + 4 * q4);
+            const float4 a = isq ? do4(16 * rt + c, 16 * jg + 4 * q4)
+                                 : *reinterpret_cast<const float4 *>(xa + 16 * jg + 4 * q4);
             const float4 u = *reinterpret_cast<const float4 *>(ub + 16 * jg + 4 * q4);
             acc = mfma_f32(a.x, u.x, acc);
             acc = mfma_f32(a.y, u.y, acc);
@@ -515,7 +578,7 @@ __global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
             rsd += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                const float4 o4 = *reinterpret_cast<const float4 *>(&sdo[16 * rt + c][j]);
+                const float4 o4 = do4(16 * rt + c, j);
                 const float4 z4 = *reinterpret_cast<const float4 *>(&sz[16 * rt + c][j]);
                 const float4 u4 = *reinterpret_cast<const float4 *>(&sx[16 * rt + c][j]);
                 dQt[rt] = mfma_f32(o4.x, s4.x, dQt[rt]);
@@ -549,7 +612,7 @@ __global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int s = 16 * st + 4 * q4 + kk;
-                const float kh = sk[s][i] * __expf(bm - sb[s][i]);
+                const float kh = widen(sk[s][i]) * __expf(bm - sb[s][i]);
                 t1 = mfma_f32(sA[16 * rt + c][s], kh, t1);
                 t3 = mfma_f32(sdAq[16 * rt + c][s], kh, t3);
             }
@@ -565,14 +628,14 @@ __global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
             for (int kk = 0; kk < 4; ++kk) {
                 const int r = 16 * rt + 4 * q4 + kk;
                 const float f = __expf(sb[r][i] - bm);
-                t2 = mfma_f32(sA[r][16 * st + c], sk[r][i] * f, t2);
-                t2 = mfma_f32(sdAq[r][16 * st + c], sq[r][i] * f, t2);
+                t2 = mfma_f32(sA[r][16 * st + c], widen(sk[r][i]) * f, t2);
+                t2 = mfma_f32(sdAq[r][16 * st + c], widen(sq[r][i]) * f, t2);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) G24[st][e] += __expf(bm - sb[16 * st + 4 * q4 + e][i]) * t2[e];
         }
 
-        // assemble dq, dk and dB (into sq: this wave's columns only)
+        // assemble dq, dk and dB (into sb: this wave's columns only, after its last read of them)
         const float bl = sb[BC - 1][i];
         float cs = 0.f, dBv[2][4];
 #pragma unroll
@@ -585,9 +648,9 @@ __global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
                 const float dkp = -gm * sbeta[r] * dKt[rt][e] + G1[rt][e];
                 const float kbg = eb * dKb[rt][e];
                 const float dkm = kbg + G24[rt][e];
-                const float kr = sk[r][i];
+                const float kr = widen(sk[r][i]);
                 cs += kr * kbg;
-                dBv[rt][e] = sq[r][i] * dqv + kr * (dkp - dkm);
+                dBv[rt][e] = widen(sq[r][i]) * dqv + kr * (dkp - dkm);
                 if (r < nv) {
                     const size_t off = ((size_t)(t0 + r) * H + h) * DK + i;
                     p.dq[off] = dqv;
@@ -599,13 +662,13 @@ __global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sq[16 * rt + 4 * q4 + e][i] = dBv[rt][e];
+            for (int e = 0; e < 4; ++e) sb[16 * rt + 4 * q4 + e][i] = dBv[rt][e];
         wave_lds_sync();
         if (q4 == 0) {
             // dB of the last row also carries dL/dB_last; dg = reverse cumulative sum over the chunk
             float a = cs + __expf(bl) * rsd;
             for (int r = nv - 1; r >= 0; --r) {
-                a += sq[r][i];
+                a += sb[r][i];
                 p.dg[((size_t)(t0 + r) * H + h) * DK + i] = a;
             }
         }
@@ -617,23 +680,23 @@ __global__ void __launch_bounds__(DK * 4) bwd_grad_kernel(const BwdParams p) {
 extern "C" size_t kda_chunk_workspace_layout(int N, size_t *order_off, size_t *base_off);
 
 // Backward workspace: [forward plan][chunk bases][checkpoints every 32][forward o][D per chunk]
-// [W per chunk][E per chunk][A, T per chunk].
+// [scan operands per chunk][A, T per chunk].
 extern "C" __attribute__((visibility("hidden"))) size_t kda_bwd_workspace_layout(int N, int H, int T, int dk, int dv,
                                                                                   int64_t n_ck, int64_t n_chunks,
                                                                                   size_t *off) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    size_t o[8];
+    const size_t rec = dk == 128 ? kda::ScanRec<128>::SIZE : kda::ScanRec<64>::SIZE;
+    size_t o[7];
     o[0] = up(kda_chunk_workspace_layout(N, nullptr, nullptr));           // cbase
     o[1] = o[0] + up((size_t)(N + 1) * 4);                                 // checkpoints
     o[2] = o[1] + up((size_t)n_ck * H * dk * dv * 4);                       // forward o
     o[3] = o[2] + up((size_t)T * H * dv * 4);                               // D
-    o[4] = o[3] + up((size_t)n_chunks * H * dk * dv * 4);                   // W
-    o[5] = o[4] + up((size_t)n_chunks * H * kda::BC * dk * 4);              // E
-    o[6] = o[5] + up((size_t)n_chunks * H * kda::BC * dv * 4);              // A, T
-    o[7] = o[6] + up((size_t)n_chunks * H * 2 * kda::BC * kda::BC * 4);     // end
+    o[4] = o[3] + up((size_t)n_chunks * H * dk * dv * 4);                   // scan operands
+    o[5] = o[4] + up((size_t)n_chunks * H * rec * 4);                       // A, T
+    o[6] = o[5] + up((size_t)n_chunks * H * 2 * kda::BC * kda::BC * 4);     // end
     if (off)
-        for (int i = 0; i < 8; ++i) off[i] = o[i];
-    return o[7];
+        for (int i = 0; i < 7; ++i) off[i] = o[i];
+    return o[6];
 }
 
 extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(
@@ -647,7 +710,7 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     const float *dSf, float *dq, float *dkk, float *dv, float *dg, float *dbeta, float *dS0, float scale,
     void *workspace, hipStream_t stream) {
     if (N == 0) return hipSuccess;
-    size_t off[8];
+    size_t off[7];
     kda_bwd_workspace_layout(N, H, T, dk, dk, n_ck, n_chunks, off);
     char *ws = static_cast<char *>(workspace);
     // states at every 32-token boundary (the forward's plan lands at the start of the workspace)
@@ -665,9 +728,8 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     p.ckpt = reinterpret_cast<const float *>(ws + off[1]);
     p.s0 = s0; p.dO = dO; p.dSf = dSf;
     p.Dck = reinterpret_cast<float *>(ws + off[3]);
-    p.Wk = reinterpret_cast<float *>(ws + off[4]);
-    p.Ek = reinterpret_cast<float *>(ws + off[5]);
-    p.TAk = reinterpret_cast<float *>(ws + off[6]);
+    p.SCk = reinterpret_cast<float *>(ws + off[4]);
+    p.TAk = reinterpret_cast<float *>(ws + off[5]);
     p.dq = dq; p.dk = dkk; p.dv = dv; p.dg = dg; p.dbeta = dbeta; p.dS0 = dS0;
     p.N = N; p.H = H; p.scale = scale;
     hipLaunchKernelGGL(kda::bwd_plan_kernel, dim3(1), dim3(1024), 0, stream, cu, N,
@@ -679,7 +741,7 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     do {                                                                                                           \
         if (chunk_blocks)                                                                                          \
             hipLaunchKernelGGL((kda::bwd_prep_kernel<DKV, T_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, p); \
-        hipLaunchKernelGGL((kda::bwd_dstate_kernel<DKV, T_>), dim3(scan_blocks), dim3(256), 0, stream, p);         \
+        hipLaunchKernelGGL((kda::bwd_dstate_kernel<DKV>), dim3(scan_blocks), dim3(256), 0, stream, p);             \
         if (chunk_blocks)                                                                                          \
             hipLaunchKernelGGL((kda::bwd_grad_kernel<DKV, T_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, p); \
     } while (0)
