@@ -66,6 +66,9 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
                     help="only write the kernel-trace summaries under profiles/ from a rocprofv3 csv run of "
                          "bench.py and the JSON line that run printed")
+    ap.add_argument("--summarize-backward-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="only write profiles/backward_T65536_H96_d128_kernel_trace.md from a rocprofv3 csv run of "
+                         "bench.py --backward and the JSON line that run printed")
     ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "MFMA"),
                     help="only write the counter summary of the prefill kernel under profiles/ from five "
                          "rocprofv3 --pmc output folders (csv)")
@@ -75,6 +78,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_backward_trace:
+        summarize_backward_trace(*args.summarize_backward_trace)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
@@ -417,6 +423,31 @@ def summarize_trace(trace_dir, bench_json):
                 f.write(f".  bench.py HIP-event average over the timed steps (same process): {ev_ms} ms.\n\n")
             f.write(f"Command:\n\n    {cmd}\n\nAll kernels of the run:\n\n{table}")
     print("wrote", ", ".join(out))
+
+
+def summarize_backward_trace(trace_dir, bench_log):
+    """Write profiles/backward_T65536_H96_d128_kernel_trace.md: per-kernel rocprofv3 averages of a
+    `bench.py --backward` run under --kernel-trace --stats, next to that run's event-timed total."""
+    import csv
+    import glob
+    path = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    with open(path) as f:
+        rows = [r for r in csv.DictReader(f) if "kda" in r["Name"]]
+    with open(bench_log) as f:
+        b = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    total = sum(float(r["AverageNs"]) for r in rows) / 1e6
+    with open(os.path.join(ROOT, "profiles", "backward_T65536_H96_d128_kernel_trace.md"), "w") as f:
+        f.write("# Backward (kda_chunk_bwd): rocprofv3 kernel trace\n\n")
+        f.write(f"Workload: {b['workload']}.\n\n")
+        f.write(f"bench.py HIP-event median of one backward (same process): {b['ms']} ms "
+                f"({b['value']:.0f} tokens/s); sum of the per-kernel rocprof averages below: {total:.3f} ms.\n\n")
+        f.write("Command:\n\n    rocprofv3 --kernel-trace --stats -d " + trace_dir + " -o run --output-format csv "
+                "-- python -u bench.py --backward --steps 5 --warmup 1\n\n")
+        f.write("| kernel | calls | average (ms) | min (ms) | max (ms) |\n|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+                    f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} |\n")
+    print("wrote profiles/backward_T65536_H96_d128_kernel_trace.md")
 
 
 def other_workload(cid, chunk, steps, warmup, prologue=False):

@@ -200,8 +200,9 @@ typedef struct {
 kda_status kda_decode_step(const kda_decode_args *args, void *stream);
 
 /*
- * Backward of the chunked prefill (the pre-training kernel of the Kimi Linear
- * page, section 5.1.1, implies one): for the scalar
+ * Backward of the chunked prefill (the scripod shownote of the K3 report
+ * reading lists a KDA kernel under pre-training, section 5.1.1; training needs
+ * the operator's gradients): for the scalar
  *
  *     L = sum(d_o * o) + sum(d_final_state * final_state)
  *
