@@ -53,15 +53,17 @@ struct BwdParams {
     float scale;
 };
 
-// Per (chunk, head): the operands of the state-gradient scan, fp32, laid out so that each lane
-// of the scan reads 4 consecutive values:
-//   KB [32][dk]  Kbar = e^{B_last - B} k        QT [dk][32]  (scale Gam Q)^T
-//   WT [dk][32]  W^T                             ET [dv][32]  E^T
-//   GL [dk]      Gam_C = e^{B_last}
+// Per (chunk, head): the operands of the state-gradient scan (and E for the gradient kernel),
+// fp32, laid out so that each lane reads 4 consecutive values:
+//   KB [32][dk]   Kbar = e^{B_last - B} k       WT [dk][32]  W^T
+//   ET [dv][32]   E^T                          GL [dk]      Gam_C = e^{B_last}
+//   RC [dk][dv]   R = scale (Gam Q - Aq W)^T dO = scale (Gam Q)^T dO - W^T E, the part of the
+//                 update that does not depend on D, in 16x16 tiles (tile (i/16, j/16), then lane
+//                 4 (i % 16 / 4) ... as an MFMA output tile: 64 lanes x 4 values)
 template <int DK> struct ScanRec {
     static constexpr int DV = DK;
-    static constexpr int KB = 0, QT = 32 * DK, WT = 64 * DK, ET = 96 * DK, GL = 96 * DK + 32 * DV;
-    static constexpr int SIZE = GL + DK;
+    static constexpr int KB = 0, WT = 32 * DK, ET = 64 * DK, GL = 64 * DK + 32 * DV, RC = GL + DK;
+    static constexpr int SIZE = RC + DK * DV;
 };
 
 // Reference row and tile coordinates of the three lower 16x16 tiles of a 32x32 chunk matrix.
@@ -116,7 +118,7 @@ __global__ void __launch_bounds__(1024) bwd_plan_kernel(const int32_t *__restric
     if (threadIdx.x == 0) cbase[N] = carry;
 }
 
-// ---- per-chunk prep: A, T, W = T Diag(beta) (Gam K), E = scale Aq^T dO --------------------
+// ---- per-chunk prep: A, T, W = T Diag(beta) (Gam K), E = scale Aq^T dO, R -------------------
 // One workgroup of dk/16 waves per (chunk, head).
 template <int DK, typename IN_T>
 __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
@@ -164,10 +166,6 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
         const int r = idx / DK, i = idx % DK;
         rec[SR::KB + idx] = sk[r][i] * __expf(sb[BC - 1][i] - sb[r][i]);
     }
-    for (int idx = tid; idx < BC * DK; idx += NT) {
-        const int i = idx / BC, r = idx % BC;
-        rec[SR::QT + idx] = p.scale * sq[r][i] * __expf(sb[r][i]);
-    }
     if (tid < DK) rec[SR::GL + tid] = __expf(sb[BC - 1][tid]);
 
     // lower tiles of A (k against k) and Aq (q against k), each over the whole d_k
@@ -208,9 +206,11 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
     }
     __syncthreads();
 
-    // W = T Diag(beta) (Gam K), stored transposed: wave w writes columns 16 w .. 16 w + 15
+    // W = T Diag(beta) (Gam K), stored transposed: wave w writes columns 16 w .. 16 w + 15; then
+    // R = scale (Gam Q - Aq W)^T dO for rows 16 w .. 16 w + 15 of R
     {
         const int i = 16 * w + c;
+        f32x4_t Wt[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -220,7 +220,31 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
                     const int s = 16 * st + 4 * q4 + kk;
                     acc = mfma_f32(sT[16 * rt + c][s], sbeta[s] * sk[s][i] * __expf(sb[s][i]), acc);
                 }
+            Wt[rt] = acc;
             *reinterpret_cast<float4 *>(rec + SR::WT + i * BC + 16 * rt + 4 * q4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+        float Qp[2][4];   // scale (Gam Q - Aq W)[16 rt + 4 q4 + e][i]
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x4_t aw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st <= rt; ++st)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) aw = mfma_f32(sAq[16 * rt + c][16 * st + 4 * q4 + kk], Wt[st][kk], aw);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + 4 * q4 + e;
+                Qp[rt][e] = p.scale * (sq[r][i] * __expf(sb[r][i]) - aw[e]);
+            }
+        }
+        float *Rt = rec + SR::RC + (size_t)w * (DV / 16) * 256 + 4 * lane;
+        for (int jt = 0; jt < DV / 16; ++jt) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(Qp[rg][kk], sdo[16 * rg + 4 * q4 + kk][16 * jt + c], acc);
+            *reinterpret_cast<float4 *>(Rt + jt * 256) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
     // E = scale Aq^T dO, stored transposed: wave w writes value columns 16 w .. 16 w + 15
@@ -250,22 +274,21 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
 // One workgroup of 4 waves per (chain, 16-column block of d_v); wave w holds rows
 // [dk/4 w, dk/4 (w+1)) of the block of D in registers.  Walking the chunks last to first it
 // stores D (the gradient at the chunk's end) and applies
-//     D <- Gam_C D + (scale Gam Q)^T dO - W^T (E + Kbar D),
+//     D <- Gam_C D + R - W^T (Kbar D),    R = scale (Gam Q)^T dO - W^T E,
 // with the operands of chunk j-1 loading into registers while chunk j is processed.
 template <int DK> struct ScanOps {
     static constexpr int RT = DK / 64;   // 16-row tiles of d_k per wave
     float4 kb[2][RT];                     // Kbar[16 rt + c][kr0 + 16 kt + 4 q4 ..]
-    float4 qt[RT][2], wt[RT][2];          // QT / WT[kr0 + 16 kt + c][16 rg + 4 q4 ..]
-    float4 et[2];                         // ET[j0 + c][16 rg + 4 q4 ..]
+    float4 wt[RT][2];                     // WT[kr0 + 16 kt + c][16 rg + 4 q4 ..]
     float4 gl[RT];                        // GL[kr0 + 16 kt + 4 q4 ..]
-    float dov[2][4];                      // dO[t0 + 16 rg + 4 q4 + kk][j0 + c]
+    float4 rc[RT];                        // R[kr0 + 16 kt + 4 q4 + e][j0 + c]
 };
 
 template <int DK>
-__device__ __forceinline__ void scan_load(ScanOps<DK> &o, const BwdParams &p, size_t cb, int t0, int nv, int h,
-                                          int kr0, int j0, int c, int q4) {
+__device__ __forceinline__ void scan_load(ScanOps<DK> &o, const BwdParams &p, size_t cb, int kr0, int jb, int lane) {
     using SR = ScanRec<DK>;
     constexpr int RT = ScanOps<DK>::RT, DV = DK;
+    const int c = lane & 15, q4 = lane >> 4;
     const float *rec = p.SCk + cb * SR::SIZE;
 #pragma unroll
     for (int kt = 0; kt < RT; ++kt) {
@@ -273,20 +296,10 @@ __device__ __forceinline__ void scan_load(ScanOps<DK> &o, const BwdParams &p, si
         for (int rt = 0; rt < 2; ++rt)
             o.kb[rt][kt] = *reinterpret_cast<const float4 *>(rec + SR::KB + (16 * rt + c) * DK + kr0 + 16 * kt + 4 * q4);
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg) {
-            o.qt[kt][rg] = *reinterpret_cast<const float4 *>(rec + SR::QT + (kr0 + 16 * kt + c) * BC + 16 * rg + 4 * q4);
+        for (int rg = 0; rg < 2; ++rg)
             o.wt[kt][rg] = *reinterpret_cast<const float4 *>(rec + SR::WT + (kr0 + 16 * kt + c) * BC + 16 * rg + 4 * q4);
-        }
         o.gl[kt] = *reinterpret_cast<const float4 *>(rec + SR::GL + kr0 + 16 * kt + 4 * q4);
-    }
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-        o.et[rg] = *reinterpret_cast<const float4 *>(rec + SR::ET + (j0 + c) * BC + 16 * rg + 4 * q4);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int r = 16 * rg + 4 * q4 + kk;
-            o.dov[rg][kk] = r < nv ? p.dO[((size_t)(t0 + r) * p.H + h) * DV + j0 + c] : 0.f;
-        }
+        o.rc[kt] = *reinterpret_cast<const float4 *>(rec + SR::RC + (size_t)((kr0 / 16 + kt) * (DV / 16) + jb) * 256 + 4 * lane);
     }
 }
 
@@ -340,36 +353,30 @@ __global__ void __launch_bounds__(256) bwd_dstate_kernel(const BwdParams p) {
         }
         lds_barrier();
 
-        float ndU[2][4];
+        float nY[2][4];   // -(Kbar D)[16 rg + 4 q4 + kk][j0 + c]
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int r = 16 * rg + 4 * q4 + kk;
-                float a = f4(cur.et[rg], kk);
+                float a = 0.f;
 #pragma unroll
                 for (int ww = 0; ww < 4; ++ww) a += part[jc & 1][ww][r][c];
-                ndU[rg][kk] = -a;
+                nY[rg][kk] = -a;
             }
 #pragma unroll
         for (int kt = 0; kt < RT; ++kt) {
             f32x4_t acc;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = f4(cur.gl[kt], e) * Dr[kt][e];
+            for (int e = 0; e < 4; ++e) acc[e] = f4(cur.gl[kt], e) * Dr[kt][e] + f4(cur.rc[kt], e);
 #pragma unroll
             for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    acc = mfma_f32(f4(cur.qt[kt][rg], kk), cur.dov[rg][kk], acc);
-                    acc = mfma_f32(f4(cur.wt[kt][rg], kk), ndU[rg][kk], acc);
-                }
+                for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(f4(cur.wt[kt][rg], kk), nY[rg][kk], acc);
             Dr[kt] = acc;
         }
     };
-    auto fetch = [&](ScanOps<DK> &o, int jc) {
-        const int jn = jc > 0 ? jc : 0;
-        scan_load<DK>(o, p, (size_t)(cb0 + jn) * H + h, seq0 + BC * jn, min(BC, L - BC * jn), h, kr0, j0, c, q4);
-    };
+    auto fetch = [&](ScanOps<DK> &o, int jc) { scan_load<DK>(o, p, (size_t)(cb0 + (jc > 0 ? jc : 0)) * H + h, kr0, jb, lane); };
     // two operand sets used in turn: chunk j is processed while chunk j - 1 loads
     ScanOps<DK> opA, opB;
     if (nch > 0) fetch(opA, nch - 1);
