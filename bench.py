@@ -69,6 +69,10 @@ def main():
     ap.add_argument("--summarize-backward-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
                     help="only write profiles/backward_T65536_H96_d128_kernel_trace.md from a rocprofv3 csv run of "
                          "bench.py --backward and the JSON line that run printed")
+    ap.add_argument("--summarize-backward-counters", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE",
+                                                                       "MFMA"),
+                    help="only write profiles/backward_T65536_H96_d128_counters.md from five rocprofv3 --pmc "
+                         "output folders of bench.py --backward (and the copy calibration)")
     ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "MFMA"),
                     help="only write the counter summary of the prefill kernel under profiles/ from five "
                          "rocprofv3 --pmc output folders (csv)")
@@ -78,6 +82,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_backward_counters:
+        summarize_backward_counters(*args.summarize_backward_counters)
         return
     if args.summarize_backward_trace:
         summarize_backward_trace(*args.summarize_backward_trace)
@@ -376,6 +383,51 @@ def summarize_counters(chunk, fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma
         for c in d["commands"]:
             f.write(f"    {c}\n")
     print(json.dumps(d, indent=1))
+
+
+def summarize_backward_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma_dir):
+    """Write profiles/backward_T65536_H96_d128_counters.md: per backward kernel, HBM bytes per launch
+    (FETCH_SIZE / WRITE_SIZE scaled by a plain copy of known size) and fp32 MFMA busy."""
+    copy_bytes = 2048 * (1 << 20)
+    cf = _mean(_counter_rows(cfetch_dir, "elementwise_kernel")[-3:], "FETCH_SIZE")
+    cw = _mean(_counter_rows(cwrite_dir, "elementwise_kernel")[-3:], "WRITE_SIZE")
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    kernels = [("chunk32_kernel<128, 2, false", "forward recompute (checkpoint every 32)"),
+               ("bwd_prep_kernel<128", "prep"), ("bwd_dstate_kernel<128", "state-gradient scan"),
+               ("bwd_grad_kernel<128", "gradients")]
+    xcd, simds = 8, 1024
+    lines = []
+    for kn, role in kernels:
+        f = _mean(_counter_rows(fetch_dir, kn), "FETCH_SIZE") * 1024 * fs
+        w = _mean(_counter_rows(write_dir, kn), "WRITE_SIZE") * 1024 * ws
+        m = _counter_rows(mfma_dir, kn)
+        busy, gui = _mean(m, "SQ_VALU_MFMA_BUSY_CYCLES"), _mean(m, "GRBM_GUI_ACTIVE")
+        lines.append(f"| `{kn}...>` ({role}) | {f / 1e9:.2f} | {w / 1e9:.2f} | "
+                     f"{100.0 * busy / (gui / xcd * simds):.1f} % |\n")
+    cmd = "python3 bench.py --backward --steps 1 --warmup 0"
+    with open(os.path.join(ROOT, "profiles", "backward_T65536_H96_d128_counters.md"), "w") as f:
+        f.write("# Backward (kda_chunk_bwd): HBM traffic and MFMA counters\n\n")
+        f.write("Workload: backward of the prefill T=65536 H=96 d_k=d_v=128, bf16 q/k/v, fp32 g/beta, initial "
+                "state, d_o and dS_T (one `bench.py --backward` call).\n\n")
+        f.write(f"HBM bytes = counter x scale, scales from a plain copy of {copy_bytes} B read + written: "
+                f"fetch {fs:.4f}, write {ws:.4f}.  MFMA busy over all 1024 SIMDs (these kernels issue "
+                "fp32 MFMA only, besides the forward).\n\n")
+        f.write("| kernel | HBM read (GB) | HBM written (GB) | MFMA busy |\n|---|---|---|---|\n")
+        for ln in lines:
+            f.write(ln)
+        f.write("\nCommands (each counter group in its own run):\n\n")
+        for c in (f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- {cmd}",
+                  f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- {cmd}",
+                  f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cfetch_dir} -o run -- python3 bench.py "
+                  "--copy-calibration 2048",
+                  f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cwrite_dir} -o run -- python3 bench.py "
+                  "--copy-calibration 2048",
+                  f"rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
+                  f"GRBM_GUI_ACTIVE --output-format csv -d {mfma_dir} -o run -- {cmd}",
+                  f"python3 bench.py --summarize-backward-counters {fetch_dir} {write_dir} {cfetch_dir} "
+                  f"{cwrite_dir} {mfma_dir}"):
+            f.write(f"    {c}\n")
+    print("wrote profiles/backward_T65536_H96_d128_counters.md")
 
 
 def summarize_trace(trace_dir, bench_json):
