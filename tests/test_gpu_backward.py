@@ -93,6 +93,17 @@ def test_backward_gate_extremes(gate):
     check(w, do, dsf, label=f"gate={gate}")
 
 
+@pytest.mark.parametrize("lens", [[0, 5, 0], [0, 0]])
+def test_backward_empty_sequences(lens):
+    # an empty sequence passes its final-state gradient through: dS0 = dS_T
+    w = W.make_prefill(lens, H=2, dk=64, dv=64, dtype="f32", seed=28, s0_std=0.1)
+    do, dsf = W.make_cotangents(w, seed=28)
+    got = check(w, do, dsf, label=f"empty {lens}")
+    for n, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(got[5][n], dsf[n])
+
+
 def test_backward_deterministic():
     w = W.make_prefill([150, 77], H=4, dk=128, dv=128, dtype="bf16", seed=26, s0_std=0.1)
     do, dsf = W.make_cotangents(w, seed=26)

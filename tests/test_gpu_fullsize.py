@@ -79,6 +79,39 @@ def test_config2_prefill_T65536_H96_sampled_heads():
     _report(f"config2 T=65536 H=96 heads={heads}", {"o": W.rel_max_err(o_s, o_r), "S": W.rel_max_err(s_s, s_r)})
 
 
+@pytest.mark.timeout(900)
+def test_config2_backward_T65536_H96_sampled_head_and_identity():
+    """The backward at the benchmark's shape: every gradient finite; one whole head (65,536 tokens)
+    against the fp64 oracle adjoint; and over all 96 heads the identity that holds because o and S_T
+    are linear in (S_0, V) jointly: sum(dv v) + sum(dS0 S0) = sum(d_o o) + sum(dS_T S_T), with o and
+    S_T from the forward."""
+    from oracle import backward as OB
+    w = W.make_config(2)
+    do, dsf = W.make_cotangents(w, seed=31)
+    d = dev()
+    q, k, v = _bf16(w.q).to(d), _bf16(w.k).to(d), _bf16(w.v).to(d)
+    g, b, s0 = _f32(w.g).to(d), _f32(w.beta).to(d), _f32(w.s0).to(d)
+    do_d, dsf_d = _f32(do).to(d), _f32(dsf).to(d)
+    dq, dk, dv, dg, db, ds0 = kda.kda_chunk_bwd(q, k, v, g, b, do_d, list(w.cu_seqlens), 1.0, s0, dsf_d)
+    o, sf, _ = kda.kda_chunk_fwd(q, k, v, g, b, list(w.cu_seqlens), 1.0, s0, True, 0, chunk_size=CHUNK)
+    torch.cuda.synchronize()
+    for x in (dq, dk, dv, dg, db, ds0):
+        assert bool(torch.isfinite(x).all())
+    lhs = float((dv.double() * v.double()).sum() + (ds0.double() * s0.double()).sum())
+    rhs = float((do_d.double() * o.double()).sum() + (dsf_d.double() * sf.double()).sum())
+    norm = float(torch.sqrt((dv.double() ** 2).sum() * (v.double() ** 2).sum()))
+    print(f"[fullsize] config2 backward identity: {lhs:.6e} vs {rhs:.6e} (scale {norm:.3e})", flush=True)
+    assert abs(lhs - rhs) <= 1e-3 * norm, (lhs, rhs, norm)
+    del o, sf
+    h = [41]
+    qh, kh, vh, gh, bh, s0h = _sub(w, h)
+    ref = OB.backward(qh, kh, vh, gh, bh, w.cu_seqlens, 1.0, s0h, np.ascontiguousarray(do[:, h]),
+                      np.ascontiguousarray(dsf[:, h]))
+    got = [x[:, h[0]:h[0] + 1].cpu().numpy() for x in (dq, dk, dv, dg, db, ds0)]
+    _report(f"config2 backward head {h[0]}", {n: W.rel_max_err(a, r) for n, a, r in
+                                              zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got, ref)})
+
+
 def test_config3_decode_N256_H96_every_state():
     w = W.make_config(3)
     d = dev()
