@@ -90,7 +90,7 @@ def main():
         summarize_backward_trace(*args.summarize_backward_trace)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "the benchmark runs on exactly one GPU; --gpus must be 1 "
                                    "(the operator shards by head / sequence with no communication, "
                                    "but no multi-GPU path is built)"}))
         sys.exit(2)
