@@ -84,6 +84,12 @@ __device__ __forceinline__ int seq_of_chunk(const int32_t *cbase, int N, int gc)
     return lo;
 }
 
+// v if ok, else zeros, selected per element (a select between whole vectors can end up as a
+// select between two stack addresses)
+__device__ __forceinline__ float4 keep4(bool ok, const float4 &v) {
+    return make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
+}
+
 __device__ __forceinline__ float red16(float t) {   // sum over the 16 lanes of a row group
     t += shfl_xor(t, 1);
     t += shfl_xor(t, 2);
@@ -135,19 +141,65 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, q4 = lane >> 4;
     const IN_T *qg = static_cast<const IN_T *>(p.q), *kg = static_cast<const IN_T *>(p.k);
 
-    for (int idx = tid; idx < BC * DK; idx += NT) {
-        const int r = idx / DK, i = idx % DK;
-        const bool ok = r < nv;
-        const size_t off = ((size_t)(t0 + r) * H + h) * DK + i;
-        sk[r][i] = ok ? load_in(kg + off) : 0.f;
-        sq[r][i] = ok ? load_in(qg + off) : 0.f;
-        sb[r][i] = ok ? p.g[off] : 0.f;
-        sdo[r][i] = ok ? p.dO[off] : 0.f;
-    }
-    if (tid < BC) sbeta[tid] = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
-    for (int idx = tid; idx < BC * BC; idx += NT) {
-        sA[idx / BC][idx % BC] = 0.f;
-        sAq[idx / BC][idx % BC] = 0.f;
+    // staging: every load issued as a 16-byte vector before the first LDS write; rows past the
+    // chunk read its last row and are zeroed (no branch around a load)
+    {
+        constexpr int VE = 16 / (int)sizeof(IN_T);                   // input elements per vector
+        constexpr int NKV = BC * DK / VE, NFV = BC * DK / 4;         // vectors of k (q), of g (dO)
+        constexpr int UK = (NKV + NT - 1) / NT, UF = (NFV + NT - 1) / NT;
+        uint4 kv[UK], qv[UK];
+        float4 gv[UF], ov[UF];
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            const int idx = min(tid + u * NT, NKV - 1), r = idx / (DK / VE), i = idx % (DK / VE) * VE;
+            const size_t off = ((size_t)(t0 + min(r, nv - 1)) * H + h) * DK + i;
+            kv[u] = *reinterpret_cast<const uint4 *>(kg + off);
+            qv[u] = *reinterpret_cast<const uint4 *>(qg + off);
+        }
+#pragma unroll
+        for (int u = 0; u < UF; ++u) {
+            const int idx = min(tid + u * NT, NFV - 1), r = idx / (DK / 4), i = idx % (DK / 4) * 4;
+            const size_t off = ((size_t)(t0 + min(r, nv - 1)) * H + h) * DK + i;
+            gv[u] = *reinterpret_cast<const float4 *>(p.g + off);
+            ov[u] = *reinterpret_cast<const float4 *>(p.dO + off);
+        }
+        const float bv = p.beta[(size_t)(t0 + min(tid % BC, nv - 1)) * H + h];
+        // widen the VE inputs of a 16-byte vector to fp32 and store them at dst (zeros if !ok)
+        auto put = [&](float *dst, const uint4 x, bool ok) {
+            const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int j = 0; j < VE / 4; ++j) {
+                float4 f;
+                if constexpr (sizeof(IN_T) == 2)   // bf16 pairs, the lower element in the low half
+                    f = make_float4(lo_bf16_of(wd[2 * j]), hi_bf16_of(wd[2 * j]), lo_bf16_of(wd[2 * j + 1]),
+                                    hi_bf16_of(wd[2 * j + 1]));
+                else
+                    f = make_float4(__uint_as_float(wd[0]), __uint_as_float(wd[1]), __uint_as_float(wd[2]),
+                                    __uint_as_float(wd[3]));
+                *reinterpret_cast<float4 *>(dst + 4 * j) = keep4(ok, f);
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            const int idx = tid + u * NT, r = idx / (DK / VE), i = idx % (DK / VE) * VE;
+            if (idx < NKV) {
+                put(&sk[r][i], kv[u], r < nv);
+                put(&sq[r][i], qv[u], r < nv);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UF; ++u) {
+            const int idx = tid + u * NT, r = idx / (DK / 4), i = idx % (DK / 4) * 4;
+            if (idx < NFV) {
+                *reinterpret_cast<float4 *>(&sb[r][i]) = keep4(r < nv, gv[u]);
+                *reinterpret_cast<float4 *>(&sdo[r][i]) = keep4(r < nv, ov[u]);
+            }
+        }
+        if (tid < BC) sbeta[tid] = tid < nv ? bv : 0.f;
+        for (int idx = tid; idx < BC * BC; idx += NT) {
+            sA[idx / BC][idx % BC] = 0.f;
+            sAq[idx / BC][idx % BC] = 0.f;
+        }
     }
     __syncthreads();
     if (tid < DK) {
@@ -190,19 +242,38 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
     }
     __syncthreads();
 
-    // T = (I + Diag(beta) A)^-1 by forward substitution: lane s of wave 0 owns column s
-    if (w == 0 && lane < BC) {
-        const int s = lane;
-        float t[BC];
+    // T = (I + Diag(beta) A)^-1 (unit lower triangular) by blocks: the 16x16 diagonal blocks by
+    // forward substitution (wave b inverts block b, lane s owns its column s), then
+    // T10 = -T11 (Diag(beta) A)10 T00 as two 16x16 fp32 MFMA products on wave 0
+    if (w < 2 && lane < 16) {
+        const int o = __builtin_amdgcn_readfirstlane(16 * w), s = lane;
+        const float *Ab = &sA[o][o], *bb = &sbeta[o];
+        float *Tb = &sT[o][o + s];
+        float t[16];
 #pragma unroll
-        for (int r = 0; r < BC; ++r) {
+        for (int r = 0; r < 16; ++r) {
             float a = 0.f;
 #pragma unroll
-            for (int mm = 0; mm < r; ++mm) a += sA[r][mm] * t[mm];
-            t[r] = (r == s ? 1.f : 0.f) - sbeta[r] * a;
+            for (int mm = 0; mm < r; ++mm) a += Ab[r * (BC + 1) + mm] * t[mm];
+            t[r] = (r == s ? 1.f : 0.f) - bb[r] * a;
         }
 #pragma unroll
-        for (int r = 0; r < BC; ++r) sT[r][s] = t[r];
+        for (int r = 0; r < 16; ++r) Tb[r * (BC + 1)] = t[r];
+        if (o == 0)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sT[r][16 + s] = 0.f;   // block above the diagonal
+    }
+    __syncthreads();
+    if (w == 0) {
+        f32x4_t P = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)   // P = (Diag(beta) A)10 T00
+            P = mfma_f32(sbeta[16 + c] * sA[16 + c][4 * q4 + kk], sT[4 * q4 + kk][c], P);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)   // Q = T11 P
+            Q = mfma_f32(sT[16 + c][16 + 4 * q4 + kk], P[kk], Q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sT[16 + 4 * q4 + e][c] = -Q[e];
     }
     __syncthreads();
 
@@ -528,8 +599,7 @@ bwd_grad_kernel(const BwdParams p) {
 
     // dO[t0 + r][h][j .. j + 3] (zero past the chunk's valid rows)
     auto do4 = [&](int r, int j) {
-        return r < nv ? *reinterpret_cast<const float4 *>(p.dO + ((size_t)(t0 + r) * H + h) * DV + j)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        return keep4(r < nv, *reinterpret_cast<const float4 *>(p.dO + ((size_t)(t0 + min(r, nv - 1)) * H + h) * DV + j));
     };
 
     // ---- stage 2: <dZ_r, U_s> -> dA (in place of A) and the A part of dbeta; <dO_r, U_s> -> dAq
@@ -580,7 +650,7 @@ bwd_grad_kernel(const BwdParams p) {
         float rsd = 0.f;
         for (int jg = 0; jg < DV / 16; ++jg) {
             const int j = 16 * jg + 4 * q4;
-            const float4 s4 = S ? *reinterpret_cast<const float4 *>(S + (size_t)i * DV + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 s4 = keep4(S != nullptr, *reinterpret_cast<const float4 *>((S ? S : D) + (size_t)i * DV + j));
             const float4 d4 = *reinterpret_cast<const float4 *>(D + (size_t)i * DV + j);
             rsd += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
 #pragma unroll
