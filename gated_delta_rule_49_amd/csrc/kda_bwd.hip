@@ -476,7 +476,8 @@ bwd_grad_kernel(const BwdParams p) {
     // k and q in their input type; sb holds the cumulative log decay, then (per wave, its own
     // columns) dB; sTq holds T for stage 1, then dAq.  With bf16 inputs and d = 128 two
     // workgroups fit in one CU's LDS.
-    __shared__ __attribute__((aligned(16))) IN_T sk[BC][P], sq[BC][P];
+    constexpr int PK = DK + 16 / (int)sizeof(IN_T);   // row pitch of sk, sq: rows start 16-byte aligned
+    __shared__ __attribute__((aligned(16))) IN_T sk[BC][PK], sq[BC][PK];
     __shared__ __attribute__((aligned(16))) float sb[BC][P], sx[BC][P], sz[BC][P];
     __shared__ float sA[BC][BC + 1], sTq[BC][BC + 1];
     float(*sT)[BC + 1] = sTq;
@@ -497,29 +498,75 @@ bwd_grad_kernel(const BwdParams p) {
                              : p.ckpt + ((size_t)(p.ck_base[n] + jc - 1) * H + h) * DK * DV;
     const float *D = p.Dck + cb * DK * DV;
 
-    for (int idx = tid; idx < BC * DK; idx += NT) {
-        const int r = idx / DK, i = idx % DK;
-        const bool ok = r < nv;
-        const size_t off = ((size_t)(t0 + r) * H + h) * DK + i;
-        sk[r][i] = ok ? kg[off] : IN_T(0);
-        sq[r][i] = ok ? qg[off] : IN_T(0);
-        sb[r][i] = ok ? p.g[off] : 0.f;
-    }
-    if (tid < BC) sbeta[tid] = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    // staging: every load issued as a 16-byte vector before the first LDS write; rows past the
+    // chunk read its last row and are zeroed (no branch around a load)
     {
-        const float *ta = p.TAk + cb * 2 * BC * BC;
-        for (int idx = tid; idx < BC * BC; idx += NT) {
-            sA[idx / BC][idx % BC] = ta[idx];
-            sT[idx / BC][idx % BC] = ta[BC * BC + idx];
+        constexpr int VE = 16 / (int)sizeof(IN_T);                 // input elements per vector
+        constexpr int NKV = BC * DK / VE, NGV = BC * DK / 4, NTA = 2 * BC * BC / 4;
+        constexpr int UK = (NKV + NT - 1) / NT, UG = (NGV + NT - 1) / NT, UT = (NTA + NT - 1) / NT;
+        uint4 kv[UK], qv[UK];
+        float4 gv[UG], tav[UT];
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            const int idx = min(tid + u * NT, NKV - 1), r = idx / (DK / VE), i = idx % (DK / VE) * VE;
+            const size_t off = ((size_t)(t0 + min(r, nv - 1)) * H + h) * DK + i;
+            kv[u] = *reinterpret_cast<const uint4 *>(kg + off);
+            qv[u] = *reinterpret_cast<const uint4 *>(qg + off);
         }
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+            const int idx = min(tid + u * NT, NGV - 1), r = idx / (DK / 4), i = idx % (DK / 4) * 4;
+            gv[u] = *reinterpret_cast<const float4 *>(p.g + ((size_t)(t0 + min(r, nv - 1)) * H + h) * DK + i);
+        }
+        const float *ta = p.TAk + cb * 2 * BC * BC;
+#pragma unroll
+        for (int u = 0; u < UT; ++u) tav[u] = *reinterpret_cast<const float4 *>(ta + 4 * min(tid + u * NT, NTA - 1));
+        const float bv = p.beta[(size_t)(t0 + min(tid % BC, nv - 1)) * H + h];
+        const uint4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            const int idx = tid + u * NT, r = idx / (DK / VE), i = idx % (DK / VE) * VE;
+            if (idx < NKV) {
+                const bool ok = r < nv;
+                *reinterpret_cast<uint4 *>(&sk[r][i]) =
+                    make_uint4(ok ? kv[u].x : z.x, ok ? kv[u].y : z.y, ok ? kv[u].z : z.z, ok ? kv[u].w : z.w);
+                *reinterpret_cast<uint4 *>(&sq[r][i]) =
+                    make_uint4(ok ? qv[u].x : z.x, ok ? qv[u].y : z.y, ok ? qv[u].z : z.z, ok ? qv[u].w : z.w);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+            const int idx = tid + u * NT, r = idx / (DK / 4), i = idx % (DK / 4) * 4;
+            if (idx < NGV) *reinterpret_cast<float4 *>(&sb[r][i]) = keep4(r < nv, gv[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < UT; ++u) {
+            const int e4 = 4 * (tid + u * NT);
+            if (e4 < 2 * BC * BC) {
+                const int rs = e4 % (BC * BC), r = rs / BC, s0c = rs % BC;
+                float *dst = e4 < BC * BC ? &sA[r][s0c] : &sT[r][s0c];
+                dst[0] = tav[u].x;
+                dst[1] = tav[u].y;
+                dst[2] = tav[u].z;
+                dst[3] = tav[u].w;
+            }
+        }
+        if (tid < BC) sbeta[tid] = tid < nv ? bv : 0.f;
     }
     __syncthreads();
-    if (tid < DK) {
-        float a = 0.f;
-        for (int r = 0; r < BC; ++r) {
-            a += sb[r][tid];
-            sb[r][tid] = a;
-        }
+    // cumulative log decay down the 32 rows: thread (column i, quarter qq) scans 8 rows, the
+    // quarter totals pass through sz (free until stage 1 writes it)
+    {
+        const int i = tid % DK, qq = tid / DK;   // NT = 4 DK
+        float a[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) a[r] = sb[8 * qq + r][i] + (r ? a[r - 1] : 0.f);
+        sz[qq][i] = a[7];
+        __syncthreads();
+        float pre = 0.f;
+        for (int u = 0; u < qq; ++u) pre += sz[u][i];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) sb[8 * qq + r][i] = a[r] + pre;
     }
     __syncthreads();
 
