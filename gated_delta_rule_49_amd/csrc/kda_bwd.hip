@@ -787,15 +787,20 @@ bwd_grad_kernel(const BwdParams p) {
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) sb[16 * rt + 4 * q4 + e][i] = dBv[rt][e];
+        // dB of the last row also carries dL/dB_last; dg = reverse cumulative sum over the chunk:
+        // lane (c, q4) sums rows 8 q4 .. 8 q4 + 7 of column i, the quarter totals pass by shuffles
         wave_lds_sync();
-        if (q4 == 0) {
-            // dB of the last row also carries dL/dB_last; dg = reverse cumulative sum over the chunk
-            float a = cs + __expf(bl) * rsd;
-            for (int r = nv - 1; r >= 0; --r) {
-                a += sb[r][i];
-                p.dg[((size_t)(t0 + r) * H + h) * DK + i] = a;
-            }
-        }
+        if (q4 == 0) sb[nv - 1][i] += cs + __expf(bl) * rsd;
+        wave_lds_sync();
+        float a[8];
+#pragma unroll
+        for (int r = 7; r >= 0; --r) a[r] = (8 * q4 + r < nv ? sb[8 * q4 + r][i] : 0.f) + (r < 7 ? a[r + 1] : 0.f);
+        // totals of quarters q4 ^ 1, q4 ^ 2, q4 ^ 3; each quarter adds those of the later ones
+        const float t1 = shfl_xor(a[0], 16), t2 = shfl_xor(a[0], 32), t3 = shfl_xor(t1, 32);
+        const float later = q4 == 0 ? t1 + t2 + t3 : q4 == 1 ? t2 + t3 : q4 == 2 ? t1 : 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            if (8 * q4 + r < nv) p.dg[((size_t)(t0 + 8 * q4 + r) * H + h) * DK + i] = a[r] + later;
     }
 }
 
