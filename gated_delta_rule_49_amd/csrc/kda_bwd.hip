@@ -575,14 +575,18 @@ bwd_grad_kernel(const BwdParams p) {
         const int jj = 16 * w + c;
         f32x4_t X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4_t Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        for (int kt = 0; kt < DK / 16; ++kt) {
-            float sv[4], dv4[4];
+        // S and D tiles of column block jj, rows 16 kt + 4 q4 + e; the pair for k-tile kt + 1 loads
+        // while the pair for kt is used
+        const float *Sc = (S ? S : D) + jj, *Dc = D + jj;
+        auto ld = [&](float (&sv)[4], float (&dv4)[4], int kt) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * kt + 4 * q4 + e;
-                sv[e] = S ? S[(size_t)i * DV + jj] : 0.f;
-                dv4[e] = D[(size_t)i * DV + jj];
+                sv[e] = S ? Sc[(size_t)i * DV] : 0.f;
+                dv4[e] = Dc[(size_t)i * DV];
             }
+        };
+        auto use = [&](const float (&sv)[4], const float (&dv4)[4], int kt) {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -592,6 +596,14 @@ bwd_grad_kernel(const BwdParams p) {
                     X[rt] = mfma_f32(kv * __expf(bi), sv[kk], X[rt]);
                     Y[rt] = mfma_f32(kv * __expf(sb[BC - 1][i] - bi), dv4[kk], Y[rt]);
                 }
+        };
+        float sa4[4], da4[4], sb4[4], db4[4];
+        ld(sa4, da4, 0);
+        for (int kt = 0; kt < DK / 16; kt += 2) {
+            ld(sb4, db4, kt + 1);
+            use(sa4, da4, kt);
+            if (kt + 2 < DK / 16) ld(sa4, da4, kt + 2);
+            use(sb4, db4, kt + 1);
         }
         // dU = E + Kbar D, then dZ = T^T dU
         const float *ET = p.SCk + cb * ScanRec<DK>::SIZE + ScanRec<DK>::ET + jj * BC;
