@@ -707,10 +707,17 @@ bwd_grad_kernel(const BwdParams p) {
         f32x4_t dKt[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4_t dKb[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         float rsd = 0.f;
+        // row i of S and D, columns 16 jg + 4 q4 ..; the pair for jg + 1 loads while jg's is used
+        const float *Sr = (S ? S : D) + (size_t)i * DV + 4 * q4, *Dr_ = D + (size_t)i * DV + 4 * q4;
+        float4 sN = keep4(S != nullptr, *reinterpret_cast<const float4 *>(Sr));
+        float4 dN = *reinterpret_cast<const float4 *>(Dr_);
         for (int jg = 0; jg < DV / 16; ++jg) {
             const int j = 16 * jg + 4 * q4;
-            const float4 s4 = keep4(S != nullptr, *reinterpret_cast<const float4 *>((S ? S : D) + (size_t)i * DV + j));
-            const float4 d4 = *reinterpret_cast<const float4 *>(D + (size_t)i * DV + j);
+            const float4 s4 = sN, d4 = dN;
+            if (jg + 1 < DV / 16) {
+                sN = keep4(S != nullptr, *reinterpret_cast<const float4 *>(Sr + 16 * (jg + 1)));
+                dN = *reinterpret_cast<const float4 *>(Dr_ + 16 * (jg + 1));
+            }
             rsd += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
