@@ -90,6 +90,8 @@ __device__ __forceinline__ float4 keep4(bool ok, const float4 &v) {
     return make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
 }
 
+__device__ __forceinline__ f32x4_t f4v(const float4 &v) { return f32x4_t{v.x, v.y, v.z, v.w}; }
+
 __device__ __forceinline__ float red16(float t) {   // sum over the 16 lanes of a row group
     t += shfl_xor(t, 1);
     t += shfl_xor(t, 2);
@@ -478,7 +480,16 @@ bwd_grad_kernel(const BwdParams p) {
     // workgroups fit in one CU's LDS.
     constexpr int PK = DK + 16 / (int)sizeof(IN_T);   // row pitch of sk, sq: rows start 16-byte aligned
     __shared__ __attribute__((aligned(16))) IN_T sk[BC][PK], sq[BC][PK];
-    __shared__ __attribute__((aligned(16))) float sb[BC][P], sx[BC][P], sz[BC][P];
+    // U (sx) and dZ (sz): fp32 rows, or with bf16 inputs hi and lo bf16 planes (written once by the
+    // wave that forms them, read as 8-element MFMA fragments in stages 2 and 3)
+    constexpr bool HL = sizeof(IN_T) == 2;
+    constexpr int PB = DK + 8;                              // bf16 plane row pitch (elements)
+    constexpr int PLANE = BC * PB * 2;                      // bytes of one plane
+    constexpr int XB = HL ? 2 * PLANE : BC * P * 4;
+    __shared__ __attribute__((aligned(16))) float sb[BC][P];
+    __shared__ __attribute__((aligned(16))) char sxb[XB], szb[XB];
+    float(*sx)[P] = reinterpret_cast<float(*)[P]>(sxb);
+    float(*sz)[P] = reinterpret_cast<float(*)[P]>(szb);
     __shared__ float sA[BC][BC + 1], sTq[BC][BC + 1];
     float(*sT)[BC + 1] = sTq;
     float(*sdAq)[BC + 1] = sTq;
@@ -640,7 +651,8 @@ bwd_grad_kernel(const BwdParams p) {
                 if (ok) p.dv[off] = bs * dZ[st][e];
                 const float t = red16(dZ[st][e] * R);
                 if (c == 0) sdb1[w][s] = t;
-                sz[s][jj] = dZ[st][e];
+                if constexpr (HL) Mat<false>::put_hl1(szb, PLANE, s * PB + jj, dZ[st][e]);
+                else sz[s][jj] = dZ[st][e];
             }
         // U = T Z
 #pragma unroll
@@ -651,7 +663,10 @@ bwd_grad_kernel(const BwdParams p) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(sT[16 * rt + c][16 * st + 4 * q4 + kk], Zv[st][kk], acc);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sx[16 * rt + 4 * q4 + e][jj] = acc[e];
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (HL) Mat<false>::put_hl1(sxb, PLANE, (16 * rt + 4 * q4 + e) * PB + jj, acc[e]);
+                else sx[16 * rt + 4 * q4 + e][jj] = acc[e];
+            }
         }
     }
     __syncthreads();
@@ -666,18 +681,31 @@ bwd_grad_kernel(const BwdParams p) {
         int rt, st, m;
         tile_of(it % 3, rt, st, m);
         const bool isq = it >= 3;
-        const float *xa = sz[16 * rt + c];
-        const float *ub = sx[16 * st + c];
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (HL) {
+            // 32 value columns per step: lane group q4, slot e <-> column 32 jb + 8 q4 + e
+#pragma unroll 2
+            for (int jb = 0; jb < DV / 32; ++jb) {
+                const int j = 32 * jb + 8 * q4;
+                Frag<false> A;
+                if (isq) A = Mat<false>::from_tiles<true>(f4v(do4(16 * rt + c, j)), f4v(do4(16 * rt + c, j + 4)));
+                else A = Mat<false>::get<true>(szb, PLANE, (16 * rt + c) * PB + j);
+                const Frag<false> B = Mat<false>::get<true>(sxb, PLANE, (16 * st + c) * PB + j);
+                mma<true, true>(acc, A, B);
+            }
+        } else {
+            const float *xa = sz[16 * rt + c];
+            const float *ub = sx[16 * st + c];
 #pragma unroll 4
-        for (int jg = 0; jg < DV / 16; ++jg) {
-            const float4 a = isq ? do4(16 * rt + c, 16 * jg + 4 * q4)
-                                 : *reinterpret_cast<const float4 *>(xa + 16 * jg + 4 * q4);
-            const float4 u = *reinterpret_cast<const float4 *>(ub + 16 * jg + 4 * q4);
-            acc = mfma_f32(a.x, u.x, acc);
-            acc = mfma_f32(a.y, u.y, acc);
-            acc = mfma_f32(a.z, u.z, acc);
-            acc = mfma_f32(a.w, u.w, acc);
+            for (int jg = 0; jg < DV / 16; ++jg) {
+                const float4 a = isq ? do4(16 * rt + c, 16 * jg + 4 * q4)
+                                     : *reinterpret_cast<const float4 *>(xa + 16 * jg + 4 * q4);
+                const float4 u = *reinterpret_cast<const float4 *>(ub + 16 * jg + 4 * q4);
+                acc = mfma_f32(a.x, u.x, acc);
+                acc = mfma_f32(a.y, u.y, acc);
+                acc = mfma_f32(a.z, u.z, acc);
+                acc = mfma_f32(a.w, u.w, acc);
+            }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -707,6 +735,38 @@ bwd_grad_kernel(const BwdParams p) {
         f32x4_t dKt[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4_t dKb[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         float rsd = 0.f;
+        if constexpr (HL) {
+            // row i of S and D, columns 32 m + 8 q4 .. + 7 (slot e <-> column 32 m + 8 q4 + e); the block
+            // for m + 1 loads while m's is used
+            const float *Sr = (S ? S : D) + (size_t)i * DV + 8 * q4, *Dr_ = D + (size_t)i * DV + 8 * q4;
+            float4 sN0 = keep4(S != nullptr, *reinterpret_cast<const float4 *>(Sr));
+            float4 sN1 = keep4(S != nullptr, *reinterpret_cast<const float4 *>(Sr + 4));
+            float4 dN0 = *reinterpret_cast<const float4 *>(Dr_), dN1 = *reinterpret_cast<const float4 *>(Dr_ + 4);
+            for (int m = 0; m < DV / 32; ++m) {
+                const int j = 32 * m + 8 * q4;
+                const float4 s0 = sN0, s1 = sN1, d0 = dN0, d1 = dN1;
+                if (m + 1 < DV / 32) {
+                    sN0 = keep4(S != nullptr, *reinterpret_cast<const float4 *>(Sr + 32 * (m + 1)));
+                    sN1 = keep4(S != nullptr, *reinterpret_cast<const float4 *>(Sr + 32 * (m + 1) + 4));
+                    dN0 = *reinterpret_cast<const float4 *>(Dr_ + 32 * (m + 1));
+                    dN1 = *reinterpret_cast<const float4 *>(Dr_ + 32 * (m + 1) + 4);
+                }
+                rsd += s0.x * d0.x + s0.y * d0.y + s0.z * d0.z + s0.w * d0.w;
+                rsd += s1.x * d1.x + s1.y * d1.y + s1.z * d1.z + s1.w * d1.w;
+                const Frag<false> Bs = Mat<false>::from_tiles<true>(f4v(s0), f4v(s1));
+                const Frag<false> Bd = Mat<false>::from_tiles<true>(f4v(d0), f4v(d1));
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const Frag<false> Ao =
+                        Mat<false>::from_tiles<true>(f4v(do4(16 * rt + c, j)), f4v(do4(16 * rt + c, j + 4)));
+                    const Frag<false> Az = Mat<false>::get<true>(szb, PLANE, (16 * rt + c) * PB + j);
+                    const Frag<false> Au = Mat<false>::get<true>(sxb, PLANE, (16 * rt + c) * PB + j);
+                    mma<true, true>(dQt[rt], Ao, Bs);
+                    mma<true, true>(dKt[rt], Az, Bs);
+                    mma<true, true>(dKb[rt], Au, Bd);
+                }
+            }
+        } else {
         // row i of S and D, columns 16 jg + 4 q4 ..; the pair for jg + 1 loads while jg's is used
         const float *Sr = (S ? S : D) + (size_t)i * DV + 4 * q4, *Dr_ = D + (size_t)i * DV + 4 * q4;
         float4 sN = keep4(S != nullptr, *reinterpret_cast<const float4 *>(Sr));
@@ -737,6 +797,7 @@ bwd_grad_kernel(const BwdParams p) {
                 dKb[rt] = mfma_f32(u4.z, d4.z, dKb[rt]);
                 dKb[rt] = mfma_f32(u4.w, d4.w, dKb[rt]);
             }
+        }
         }
         rsd += shfl_xor(rsd, 16);
         rsd += shfl_xor(rsd, 32);   // rowsum(S * D) of row i
