@@ -79,3 +79,29 @@ def backward(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, d
                 dS = al[:, None] * dSt
             dS0[n, h] = dS
     return dq_, dk_, dvv, dg_, db_, dS0
+
+
+def backward_fused(q, k, v, g_pre, b_pre, cu_seqlens=None, scale=1.0, initial_state=None, do=None, dS_final=None,
+                   normalize=True):
+    """Gradients through the fused prologue (the operator takes g = -5 sigmoid(a), beta = sigmoid(b)
+    and, with normalize, q / |q| and k / |k| over d_k): backward() on the prologue's outputs, then
+    the chain rule back to the raw inputs, per (token, head):
+        dL/da = dL/dg * (-5) s (1 - s),  s = sigmoid(a);      dL/db = dL/dbeta * beta (1 - beta);
+        dL/dq = (dL/dq_n - q_n <q_n, dL/dq_n>) / |q|   (0 for a zero row), the same for k.
+    Returns (dq, dk, dv, da, db, dS0) for the raw q, k, v, a, b and S0, fp64."""
+    from . import prologue
+    qn, kn, g, beta = prologue(q, k, g_pre, b_pre, normalize)
+    dqn, dkn, dv, dg, dbeta, dS0 = backward(qn, kn, v, g, beta, cu_seqlens, scale, initial_state, do, dS_final)
+    s = 1.0 / (1.0 + np.exp(-np.asarray(g_pre, dtype=np.float64)))
+    da = dg * (-5.0) * s * (1.0 - s)
+    db = dbeta * beta * (1.0 - beta)
+
+    def through_unit(x, xn, dxn):
+        if not normalize:
+            return dxn
+        x = np.asarray(x, dtype=np.float64)
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        proj = dxn - xn * np.sum(xn * dxn, axis=-1, keepdims=True)
+        return np.divide(proj, n, out=np.zeros_like(proj), where=n > 0)
+
+    return through_unit(q, qn, dqn), through_unit(k, kn, dkn), dv, da, db, dS0

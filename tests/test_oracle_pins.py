@@ -419,6 +419,40 @@ def test_backward_matches_finite_differences():
             assert abs(fd - gx[idx]) <= 1e-7 * max(1.0, abs(fd)), (which, idx, fd, gx[idx])
 
 
+def test_backward_fused_prologue_matches_finite_differences():
+    """Central differences of the same L, now a function of the raw q, k, the gate pre-activations
+    a, b (g = -5 sigmoid(a), beta = sigmoid(b)) and v, S0, against backward_fused, with and
+    without the q/k normalisation."""
+    import oracle
+    from oracle.backward import backward_fused
+    rng = np.random.default_rng(29)
+    T, H, dk, dv, cu = 6, 2, 3, 4, [0, 2, 6]
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    a = rng.standard_normal((T, H, dk))
+    b = rng.standard_normal((T, H))
+    S0 = rng.standard_normal((2, H, dk, dv)) * 0.5
+    do = rng.standard_normal((T, H, dv))
+    dSf = rng.standard_normal((2, H, dk, dv))
+    scale = 0.8
+    for normalize in (True, False):
+        def loss(q_, k_, v_, a_, b_, S0_):
+            qn, kn, g, beta = oracle.prologue(q_, k_, a_, b_, normalize)
+            return _loss(qn, kn, v_, g, beta, S0_, do, dSf, scale, cu)
+        grads = backward_fused(q, k, v, a, b, cu, scale, S0, do, dSf, normalize)
+        args = [q, k, v, a, b, S0]
+        eps = 1e-6
+        for which, (x, gx) in enumerate(zip(args, grads)):
+            for idx in np.ndindex(*x.shape):
+                xp = [y.copy() for y in args]
+                xm = [y.copy() for y in args]
+                xp[which][idx] += eps
+                xm[which][idx] -= eps
+                fd = (loss(*xp) - loss(*xm)) / (2 * eps)
+                assert abs(fd - gx[idx]) <= 1e-7 * max(1.0, abs(fd)), (normalize, which, idx, fd, gx[idx])
+
+
 def test_backward_pure_decay_closed_form():
     """beta = 0: o_t = scale S0^T (e^{G_t} * q_t) and S_T = Diag(e^{G_T}) S0, so
     dq_t = scale e^{G_t} * (S0 do_t), dv = dk = 0 (k and v enter only through u = 0), and
