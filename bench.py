@@ -53,8 +53,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (profiling runs)")
     ap.add_argument("--chunk", type=int, default=32, choices=(32, 64), help="token block of the chunked form")
     ap.add_argument("--prologue", action="store_true",
-                    help="with --workload 2: fused gate/normalisation prologue (raw q, k, bf16 gate "
-                         "pre-activations)")
+                    help="with --workload 2 or --backward: fused gate/normalisation prologue (raw q, k, bf16 "
+                         "gate pre-activations)")
     ap.add_argument("--workload", type=int, default=0, choices=(0, 1, 2, 4),
                     help="instead of the benchmark step, time the prefill of workload 1 (T=4096, H=32) or 4 "
                          "(64 packed sequences, H=32, checkpoints every 512) and print its own JSON line")
@@ -102,7 +102,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.backward:
-        backward_workload(args.steps, args.warmup)
+        backward_workload(args.steps, args.warmup, args.prologue)
         return
     if args.workload:
         other_workload(args.workload, args.chunk, args.steps, args.warmup, args.prologue)
@@ -478,8 +478,9 @@ def summarize_trace(trace_dir, bench_json):
 
 
 def summarize_backward_trace(trace_dir, bench_log):
-    """Write profiles/backward_T65536_H96_d128_kernel_trace.md: per-kernel rocprofv3 averages of a
-    `bench.py --backward` run under --kernel-trace --stats, next to that run's event-timed total."""
+    """Write profiles/backward[_prologue]_T65536_H96_d128_kernel_trace.md: per-kernel rocprofv3
+    averages of a `bench.py --backward [--prologue]` run under --kernel-trace --stats, next to that
+    run's event-timed total."""
     import csv
     import glob
     path = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
@@ -487,19 +488,22 @@ def summarize_backward_trace(trace_dir, bench_log):
         rows = [r for r in csv.DictReader(f) if "kda" in r["Name"]]
     with open(bench_log) as f:
         b = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    fused = "fused" in b["workload"]
+    name = "backward_prologue_T65536_H96_d128_kernel_trace.md" if fused else "backward_T65536_H96_d128_kernel_trace.md"
     total = sum(float(r["AverageNs"]) for r in rows) / 1e6
-    with open(os.path.join(ROOT, "profiles", "backward_T65536_H96_d128_kernel_trace.md"), "w") as f:
-        f.write("# Backward (kda_chunk_bwd): rocprofv3 kernel trace\n\n")
+    with open(os.path.join(ROOT, "profiles", name), "w") as f:
+        f.write("# Backward (kda_chunk_bwd" + (", fused gate / normalisation prologue" if fused else "")
+                + "): rocprofv3 kernel trace\n\n")
         f.write(f"Workload: {b['workload']}.\n\n")
         f.write(f"bench.py HIP-event median of one backward (same process): {b['ms']} ms "
                 f"({b['value']:.0f} tokens/s); sum of the per-kernel rocprof averages below: {total:.3f} ms.\n\n")
         f.write("Command:\n\n    rocprofv3 --kernel-trace --stats -d " + trace_dir + " -o run --output-format csv "
-                "-- python -u bench.py --backward --steps 5 --warmup 1\n\n")
+                "-- python -u bench.py --backward " + ("--prologue " if fused else "") + "--steps 5 --warmup 1\n\n")
         f.write("| kernel | calls | average (ms) | min (ms) | max (ms) |\n|---|---|---|---|---|\n")
         for r in rows:
             f.write(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
                     f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} |\n")
-    print("wrote profiles/backward_T65536_H96_d128_kernel_trace.md")
+    print("wrote profiles/" + name)
 
 
 def other_workload(cid, chunk, steps, warmup, prologue=False):
@@ -616,17 +620,20 @@ def other_workload(cid, chunk, steps, warmup, prologue=False):
         "data": "synthetic (seeded)"}), flush=True)
 
 
-def bwd_alg_bytes(T, H, dk, dv, N, in_bytes=2):
-    """Algorithmic HBM bytes of one backward: read q, k, v, g, beta, d_o and the initial / final-state
-    gradient inputs once, write dq, dk, dv, dg, dbeta and dS_0 once (fp32 gradients)."""
-    per_tok_head = in_bytes * (2 * dk + dv) + 4 * dk + 4 + 4 * dv + 4 * (3 * dk + dv + 1)
+def bwd_alg_bytes(T, H, dk, dv, N, fused=False, in_bytes=2):
+    """Algorithmic HBM bytes of one backward: read q, k, v, g (bf16 pre-activations when fused),
+    beta, d_o and the initial / final-state gradient inputs once, write dq, dk, dv, dg, dbeta and
+    dS_0 once (fp32 gradients)."""
+    per_tok_head = in_bytes * (2 * dk + dv) + (2 if fused else 4) * dk + 4 + 4 * dv + 4 * (3 * dk + dv + 1)
     return T * H * per_tok_head + 3 * N * H * dk * dv * 4
 
 
-def backward_workload(steps, warmup):
+def backward_workload(steps, warmup, fused=False):
     """Backward tokens/s on workload 2's shape (one sequence, T=65536, H=96, d=128, bf16 q/k/v,
     initial state, d_o and dS_T upstream gradients), inputs drawn on the device with torch's seeded
-    generator from the workload distributions (timing only)."""
+    generator from the workload distributions (timing only).  With fused, the inputs are the raw
+    ones of the fused prologue (q, k ~ N(0,1) unnormalised, bf16 gate pre-activations a ~ N(0,1),
+    b ~ N(0,1)) and the gradients are taken through the gate and the normalisation."""
     import numpy as np
     import torch
     import gated_delta_rule_49_amd as kda
@@ -637,14 +644,21 @@ def backward_workload(steps, warmup):
     gen = torch.Generator(device=dev)
     gen.manual_seed(20261203)
     rn = lambda *shape: torch.randn(shape, generator=gen, device=dev)
-    x = rn(T, H, dk)
-    q = (x / x.norm(dim=-1, keepdim=True) * dk ** -0.5).to(bf)
-    x = rn(T, H, dk)
-    k = (x / x.norm(dim=-1, keepdim=True)).to(bf)
-    del x
-    v = rn(T, H, dv).to(bf)
-    g = -5.0 * torch.sigmoid(rn(T, H, dk))
-    beta = torch.sigmoid(rn(T, H))
+    scale = 1.0
+    if fused:
+        q, k = rn(T, H, dk).to(bf), rn(T, H, dk).to(bf)
+        v = rn(T, H, dv).to(bf)
+        g, beta = rn(T, H, dk).to(bf), rn(T, H)
+        scale = dk ** -0.5
+    else:
+        x = rn(T, H, dk)
+        q = (x / x.norm(dim=-1, keepdim=True) * dk ** -0.5).to(bf)
+        x = rn(T, H, dk)
+        k = (x / x.norm(dim=-1, keepdim=True)).to(bf)
+        del x
+        v = rn(T, H, dv).to(bf)
+        g = -5.0 * torch.sigmoid(rn(T, H, dk))
+        beta = torch.sigmoid(rn(T, H))
     s0 = 0.1 * rn(1, H, dk, dv)
     do = rn(T, H, dv)
     dsf = rn(1, H, dk, dv)
@@ -654,12 +668,14 @@ def backward_workload(steps, warmup):
 
     def run():
         nonlocal out, ws
-        out = kda.kda_chunk_bwd(q, k, v, g, beta, do, cu, 1.0, s0, dsf, workspace=ws)
+        out = kda.kda_chunk_bwd(q, k, v, g, beta, do, cu, scale, s0, dsf, workspace=ws, gate_preactivation=fused,
+                                normalize_qk=fused)
 
     run()
     torch.cuda.synchronize()
     # reuse one workspace (the binding allocates one per call when none is passed)
-    ws = torch.empty(_bwd_ws_bytes(kda, q, k, v, g, beta, do, cu, s0, dsf, out), dtype=torch.uint8, device=dev)
+    ws = torch.empty(_bwd_ws_bytes(kda, q, k, v, g, beta, do, cu, s0, dsf, out, fused), dtype=torch.uint8,
+                     device=dev)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -673,10 +689,12 @@ def backward_workload(steps, warmup):
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
     med = float(np.median(ms))
-    nbytes = bwd_alg_bytes(T, H, dk, dv, 1)
+    nbytes = bwd_alg_bytes(T, H, dk, dv, 1, fused)
+    what = ("raw bf16 q/k/v, bf16 gate pre-activations a, fp32 b, gradients through the fused gate and "
+            "q/k normalisation" if fused else "bf16 q/k/v, fp32 g/beta")
     print(json.dumps({
-        "metric": "KDA backward tokens/s", "workload": "backward of the prefill T=65536 H=96 d_k=d_v=128 bf16 "
-                                                      "q/k/v, fp32 g/beta, initial state, d_o and dS_T",
+        "metric": "KDA backward tokens/s", "workload": "backward of the prefill T=65536 H=96 d_k=d_v=128 "
+                                                      + what + ", initial state, d_o and dS_T",
         "tokens": T, "heads": H, "value": round(T / (med * 1e-3), 1), "unit": "tokens/s", "ms": round(med, 4),
         "ms_p10": round(float(np.percentile(ms, 10)), 4), "ms_p90": round(float(np.percentile(ms, 90)), 4),
         "alg_bytes": int(nbytes), "alg_GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
@@ -684,10 +702,11 @@ def backward_workload(steps, warmup):
         "workspace_GB": round(ws.numel() / 1e9, 2), "data": "synthetic (seeded)"}), flush=True)
 
 
-def _bwd_ws_bytes(kda, q, k, v, g, beta, do, cu, s0, dsf, out):
+def _bwd_ws_bytes(kda, q, k, v, g, beta, do, cu, s0, dsf, out, fused=False):
     import torch
     cu_h = torch.tensor(cu, dtype=torch.int32)
-    a = kda.make_bwd_args(q, k, v, g, beta, cu_h.to(q.device), cu_h, 1.0, s0, do, dsf, *out)
+    a = kda.make_bwd_args(q, k, v, g, beta, cu_h.to(q.device), cu_h, 1.0, s0, do, dsf, *out,
+                          gate_preactivation=fused, normalize_qk=fused)
     return int(kda.lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(a)))
 
 

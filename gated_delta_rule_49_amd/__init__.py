@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_DEVICE = range(5)
 KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_LOG_DECAY, KDA_GATE_PREACTIVATION = 0, 1
 
 
 class KdaFwdArgs(ctypes.Structure):
@@ -60,6 +61,7 @@ class KdaBwdArgs(ctypes.Structure):
         ("initial_state", ctypes.c_void_p), ("d_o", ctypes.c_void_p), ("d_final_state", ctypes.c_void_p),
         ("dq", ctypes.c_void_p), ("dk_out", ctypes.c_void_p), ("dv_out", ctypes.c_void_p),
         ("dg", ctypes.c_void_p), ("dbeta", ctypes.c_void_p), ("d_initial_state", ctypes.c_void_p),
+        ("gate_mode", ctypes.c_int32), ("normalize_qk", ctypes.c_int32),
     ]
 
 
@@ -163,7 +165,7 @@ def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final
     a.initial_state_indices = _ptr(initial_state_indices)
     a.checkpoint_indices = _ptr(checkpoint_indices)
     a.num_slots = int(num_slots)
-    a.gate_mode = 1 if gate_preactivation else 0
+    a.gate_mode = KDA_GATE_PREACTIVATION if gate_preactivation else KDA_GATE_LOG_DECAY
     a.normalize_qk = 1 if normalize_qk else 0
     return a
 
@@ -229,7 +231,7 @@ def _cu_host(cu_seqlens, T):
 
 
 def make_bwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, d_o, d_final_state, dq, dk, dv, dg,
-                  dbeta, d_initial_state):
+                  dbeta, d_initial_state, gate_preactivation=False, normalize_qk=False):
     T, H, dk_ = q.shape
     a = KdaBwdArgs()
     a.struct_size = ctypes.sizeof(KdaBwdArgs)
@@ -248,18 +250,22 @@ def make_bwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, d_o, 
     a.d_final_state = _ptr(d_final_state)
     a.dq, a.dk_out, a.dv_out, a.dg, a.dbeta = (_ptr(x) for x in (dq, dk, dv, dg, dbeta))
     a.d_initial_state = _ptr(d_initial_state)
+    a.gate_mode = KDA_GATE_PREACTIVATION if gate_preactivation else KDA_GATE_LOG_DECAY
+    a.normalize_qk = 1 if normalize_qk else 0
     return a
 
 
 def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_state=None, d_final_state=None,
-                  output_d_initial_state=True, stream=None, workspace=None):
-    """Backward of kda_chunk_fwd (log-decay gates): gradients of
-    L = sum(d_o * o) + sum(d_final_state * final_state).
+                  output_d_initial_state=True, stream=None, workspace=None, gate_preactivation=False,
+                  normalize_qk=False):
+    """Backward of kda_chunk_fwd: gradients of L = sum(d_o * o) + sum(d_final_state * final_state).
 
-    Inputs as for kda_chunk_fwd; d_o: fp32 [T, H, dv]; d_final_state: fp32 [N, H, dk, dv] or None
-    (zeros).  workspace: optional uint8 CUDA tensor of at least the queried size (reused by callers
-    that run the backward repeatedly).  Returns (dq, dk, dv, dg, dbeta, d_initial_state or None),
-    all fp32."""
+    Inputs as for kda_chunk_fwd (with gate_preactivation / normalize_qk as there: g, beta are then
+    the gate pre-activations and q, k the raw vectors, and the returned dg, dbeta, dq, dk are the
+    gradients with respect to those); d_o: fp32 [T, H, dv]; d_final_state: fp32 [N, H, dk, dv] or
+    None (zeros).  workspace: optional uint8 CUDA tensor of at least the queried size (reused by
+    callers that run the backward repeatedly).  Returns (dq, dk, dv, dg, dbeta, d_initial_state or
+    None), all fp32."""
     T, H, dk = q.shape
     dv = v.shape[2]
     dev = q.device
@@ -272,7 +278,7 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_sta
     db = torch.empty((T, H), **f32)
     ds0 = torch.empty((N, H, dk, dv), **f32) if output_d_initial_state else None
     a = make_bwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, d_o, d_final_state, dq, dkk, dvv,
-                      dg, db, ds0)
+                      dg, db, ds0, gate_preactivation, normalize_qk)
     L = lib()
     ws_bytes = int(L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a)))
     if ws_bytes == 0 and N > 0:

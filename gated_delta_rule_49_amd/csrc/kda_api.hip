@@ -19,12 +19,12 @@ extern "C" hipError_t kda_launch_chunk(int chunk, int dk, int in_bf16, int N, in
                                        float scale, const int32_t *s0_idx, const int32_t *ck_idx,
                                        int nslots, int flags, void *workspace, hipStream_t stream);
 extern "C" size_t kda_bwd_workspace_layout(int N, int H, int T, int dk, int dv, int64_t n_ck, int64_t n_chunks,
-                                           size_t *off);
+                                           int flags, size_t *off);
 extern "C" hipError_t kda_launch_bwd(int dk, int in_bf16, int N, int H, int T, int64_t n_ck, int64_t n_chunks,
                                      const void *q, const void *k, const void *v, const float *g, const float *beta,
                                      const int32_t *cu, const float *s0, const float *dO, const float *dSf, float *dq,
                                      float *dkk, float *dv, float *dg, float *dbeta, float *dS0, float scale,
-                                     void *workspace, hipStream_t stream);
+                                     int flags, void *workspace, hipStream_t stream);
 
 namespace {
 
@@ -124,9 +124,18 @@ kda_status validate_bwd(const kda_bwd_args *a, int64_t *n_ck, int64_t *n_chunks)
         for (int j = i + 1; j < 6; ++j)
             if (out[i] == out[j]) return KDA_ERR_INVALID_ARGUMENT;
     }
+    // fused prologue (as in the forward): gate pre-activations and/or normalisation, bf16 inputs
+    if ((a->gate_mode != KDA_GATE_LOG_DECAY && a->gate_mode != KDA_GATE_PREACTIVATION) ||
+        (a->normalize_qk != 0 && a->normalize_qk != 1))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if ((a->gate_mode != KDA_GATE_LOG_DECAY || a->normalize_qk) && a->in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (n_ck) *n_ck = ck;
     if (n_chunks) *n_chunks = ch;
     return KDA_OK;
+}
+
+int bwd_flags(const kda_bwd_args *a) {
+    return (a->gate_mode == KDA_GATE_PREACTIVATION ? 1 : 0) | (a->normalize_qk ? 2 : 0);
 }
 
 }  // namespace
@@ -172,7 +181,8 @@ kda_status kda_chunk_fwd(const kda_fwd_args *a, void *workspace, size_t workspac
 size_t kda_chunk_bwd_workspace_bytes(const kda_bwd_args *a) {
     int64_t ck, ch;
     if (validate_bwd(a, &ck, &ch) != KDA_OK) return 0;
-    return kda_bwd_workspace_layout(a->num_seqs, a->num_heads, a->total_tokens, a->dk, a->dv, ck, ch, nullptr);
+    return kda_bwd_workspace_layout(a->num_seqs, a->num_heads, a->total_tokens, a->dk, a->dv, ck, ch, bwd_flags(a),
+                                    nullptr);
 }
 
 kda_status kda_chunk_bwd(const kda_bwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
@@ -181,13 +191,14 @@ kda_status kda_chunk_bwd(const kda_bwd_args *a, void *workspace, size_t workspac
     if (st != KDA_OK) return st;
     if (a->num_seqs == 0) return KDA_OK;
     const size_t need = kda_bwd_workspace_layout(a->num_seqs, a->num_heads, a->total_tokens, a->dk, a->dv, ck, ch,
-                                                 nullptr);
+                                                 bwd_flags(a), nullptr);
     if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_INVALID_ARGUMENT;
     const hipError_t e = kda_launch_bwd(a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->total_tokens,
                                         ck, ch, a->q, a->k, a->v, a->g, a->beta, a->cu_seqlens, a->initial_state,
                                         a->d_o, a->d_final_state, a->dq, a->dk_out, a->dv_out, a->dg, a->dbeta,
-                                        a->d_initial_state, a->scale, workspace, static_cast<hipStream_t>(stream));
+                                        a->d_initial_state, a->scale, bwd_flags(a), workspace,
+                                        static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
 

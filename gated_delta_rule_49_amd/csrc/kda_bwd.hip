@@ -884,28 +884,133 @@ bwd_grad_kernel(const BwdParams p) {
     }
 }
 
+// ---- fused prologue: the operator's inputs from the raw ones, and the chain rule back ---------
+// g = -5 sigmoid(a), beta = sigmoid(b), q / |q| and k / |k| over d_k (the skill card's quick facts:
+// lower-bounded scaled sigmoid, g_min = -5).  One wave per (token, head) row; lane l holds the
+// row's elements l, l + 64, ...
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += shfl_xor(x, off);
+    return x;
+}
+
+// With the normalisation the unit vectors stay fp32 (as in the forward's fused prologue), so the
+// rest of the backward runs on fp32 inputs and v is widened alongside.
+template <int DK>
+__global__ void __launch_bounds__(256) bwd_prologue_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                            const uint16_t *__restrict__ v, const uint16_t *__restrict__ a,
+                                                            const float *__restrict__ b, long long rows, int flags,
+                                                            float *__restrict__ qn, float *__restrict__ kn,
+                                                            float *__restrict__ vf, float *__restrict__ g,
+                                                            float *__restrict__ beta) {
+    constexpr int EPL = DK / 64;
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;   // whole waves
+    const size_t base = (size_t)row * DK + lane;
+    if (flags & KDA_PRO_NORM) {
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const uint16_t *src = which ? k : q;
+            float *dst = which ? kn : qn;
+            float x[EPL], ss = 0.f;
+#pragma unroll
+            for (int m = 0; m < EPL; ++m) {
+                x[m] = bf16_bits_to_f32(src[base + 64 * m]);
+                ss += x[m] * x[m];
+            }
+            ss = wave_sum(ss);
+            const float inv = ss > 0.f ? rsqrtf(ss) : 0.f;   // a zero row stays zero
+#pragma unroll
+            for (int m = 0; m < EPL; ++m) dst[base + 64 * m] = x[m] * inv;
+        }
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) vf[base + 64 * m] = bf16_bits_to_f32(v[base + 64 * m]);
+    }
+    if (flags & KDA_PRO_GATE) {
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) g[base + 64 * m] = -5.f / (1.f + __expf(-bf16_bits_to_f32(a[base + 64 * m])));
+        if (lane == 0) beta[row] = 1.f / (1.f + __expf(-b[row]));
+    }
+}
+
+// dL/d(raw) from dL/d(prologue output), in place: dq <- (dq - q_n <q_n, dq>) / |q| (the same for k),
+// dg <- dg * (-5) s (1 - s) with s = sigmoid(a), dbeta <- dbeta * beta (1 - beta).
+template <int DK>
+__global__ void __launch_bounds__(256) bwd_epilogue_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                            const uint16_t *__restrict__ a, const float *__restrict__ b,
+                                                            long long rows, int flags, float *__restrict__ dq,
+                                                            float *__restrict__ dk, float *__restrict__ dg,
+                                                            float *__restrict__ dbeta) {
+    constexpr int EPL = DK / 64;
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;   // whole waves
+    const size_t base = (size_t)row * DK + lane;
+    if (flags & KDA_PRO_NORM) {
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const uint16_t *src = which ? k : q;
+            float *d = which ? dk : dq;
+            float x[EPL], dx[EPL], ss = 0.f;
+#pragma unroll
+            for (int m = 0; m < EPL; ++m) {
+                x[m] = bf16_bits_to_f32(src[base + 64 * m]);
+                dx[m] = d[base + 64 * m];
+                ss += x[m] * x[m];
+            }
+            ss = wave_sum(ss);
+            const float inv = ss > 0.f ? rsqrtf(ss) : 0.f;
+            float dot = 0.f;
+#pragma unroll
+            for (int m = 0; m < EPL; ++m) dot += x[m] * inv * dx[m];
+            dot = wave_sum(dot);
+#pragma unroll
+            for (int m = 0; m < EPL; ++m) d[base + 64 * m] = (dx[m] - x[m] * inv * dot) * inv;
+        }
+    }
+    if (flags & KDA_PRO_GATE) {
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) {
+            const float sg = 1.f / (1.f + __expf(-bf16_bits_to_f32(a[base + 64 * m])));
+            dg[base + 64 * m] *= -5.f * sg * (1.f - sg);
+        }
+        if (lane == 0) {
+            const float sb = 1.f / (1.f + __expf(-b[row]));
+            dbeta[row] *= sb * (1.f - sb);
+        }
+    }
+}
+
 }  // namespace kda
 
 extern "C" size_t kda_chunk_workspace_layout(int N, size_t *order_off, size_t *base_off);
 
 // Backward workspace: [forward plan][chunk bases][checkpoints every 32][forward o][D per chunk]
-// [scan operands per chunk][A, T per chunk].
+// [scan operands per chunk][A, T per chunk][with the fused prologue: q_n, k_n, v (fp32, with the
+// normalisation), g, beta (with the gate)].
 extern "C" __attribute__((visibility("hidden"))) size_t kda_bwd_workspace_layout(int N, int H, int T, int dk, int dv,
                                                                                   int64_t n_ck, int64_t n_chunks,
-                                                                                  size_t *off) {
+                                                                                  int flags, size_t *off) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t rec = dk == 128 ? kda::ScanRec<128>::SIZE : kda::ScanRec<64>::SIZE;
-    size_t o[7];
+    size_t o[12];
     o[0] = up(kda_chunk_workspace_layout(N, nullptr, nullptr));           // cbase
     o[1] = o[0] + up((size_t)(N + 1) * 4);                                 // checkpoints
     o[2] = o[1] + up((size_t)n_ck * H * dk * dv * 4);                       // forward o
     o[3] = o[2] + up((size_t)T * H * dv * 4);                               // D
     o[4] = o[3] + up((size_t)n_chunks * H * dk * dv * 4);                   // scan operands
     o[5] = o[4] + up((size_t)n_chunks * H * rec * 4);                       // A, T
-    o[6] = o[5] + up((size_t)n_chunks * H * 2 * kda::BC * kda::BC * 4);     // end
+    o[6] = o[5] + up((size_t)n_chunks * H * 2 * kda::BC * kda::BC * 4);     // q_n
+    const bool nrm = flags & kda::KDA_PRO_NORM, gate = flags & kda::KDA_PRO_GATE;
+    o[7] = o[6] + (nrm ? up((size_t)T * H * dk * 4) : 0);                  // k_n
+    o[8] = o[7] + (nrm ? up((size_t)T * H * dk * 4) : 0);                  // v (fp32)
+    o[9] = o[8] + (nrm ? up((size_t)T * H * dv * 4) : 0);                  // g
+    o[10] = o[9] + (gate ? up((size_t)T * H * dk * 4) : 0);                // beta
+    o[11] = o[10] + (gate ? up((size_t)T * H * 4) : 0);                    // end
     if (off)
-        for (int i = 0; i < 7; ++i) off[i] = o[i];
-    return o[6];
+        for (int i = 0; i < 12; ++i) off[i] = o[i];
+    return o[11];
 }
 
 extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(
@@ -917,15 +1022,45 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     int dk, int in_bf16, int N, int H, int T, int64_t n_ck, int64_t n_chunks, const void *q, const void *k,
     const void *v, const float *g, const float *beta, const int32_t *cu, const float *s0, const float *dO,
     const float *dSf, float *dq, float *dkk, float *dv, float *dg, float *dbeta, float *dS0, float scale,
-    void *workspace, hipStream_t stream) {
+    int flags, void *workspace, hipStream_t stream) {
     if (N == 0) return hipSuccess;
-    size_t off[7];
-    kda_bwd_workspace_layout(N, H, T, dk, dk, n_ck, n_chunks, off);
+    size_t off[12];
+    kda_bwd_workspace_layout(N, H, T, dk, dk, n_ck, n_chunks, flags, off);
     char *ws = static_cast<char *>(workspace);
+    hipError_t e;
+    // fused prologue: the operator's inputs, materialised (fp32 q_n, k_n, v; fp32 g, beta) for
+    // the per-chunk kernels; the forward recompute applies the prologue itself, exactly as the
+    // forward does
+    const void *q_raw = q, *k_raw = k, *v_raw = v;
+    const float *a_raw = g, *b_raw = beta;
+    const int raw_bf16 = in_bf16;
+    const long long rows = (long long)T * H;
+    const unsigned row_blocks = (unsigned)((rows + 3) / 4);
+    if (flags && rows > 0) {
+        float *qn = reinterpret_cast<float *>(ws + off[6]), *kn = reinterpret_cast<float *>(ws + off[7]);
+        float *vf = reinterpret_cast<float *>(ws + off[8]);
+        float *gm = reinterpret_cast<float *>(ws + off[9]), *bm = reinterpret_cast<float *>(ws + off[10]);
+        const uint16_t *qr = static_cast<const uint16_t *>(q), *kr = static_cast<const uint16_t *>(k);
+        const uint16_t *vr = static_cast<const uint16_t *>(v);
+        const uint16_t *ar = reinterpret_cast<const uint16_t *>(g);
+        if (dk == 128)
+            hipLaunchKernelGGL(kda::bwd_prologue_kernel<128>, dim3(row_blocks), dim3(256), 0, stream, qr, kr, vr, ar,
+                               beta, rows, flags, qn, kn, vf, gm, bm);
+        else
+            hipLaunchKernelGGL(kda::bwd_prologue_kernel<64>, dim3(row_blocks), dim3(256), 0, stream, qr, kr, vr, ar,
+                               beta, rows, flags, qn, kn, vf, gm, bm);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (flags & kda::KDA_PRO_NORM) { q = qn; k = kn; v = vf; in_bf16 = 0; }
+        if (flags & kda::KDA_PRO_GATE) { g = gm; beta = bm; }
+    }
     // states at every 32-token boundary (the forward's plan lands at the start of the workspace)
-    hipError_t e = kda_launch_chunk(32, dk, in_bf16, N, H, q, k, v, g, beta, cu, s0, nullptr, kda::BC,
-                                    reinterpret_cast<float *>(ws + off[1]), reinterpret_cast<float *>(ws + off[2]),
-                                    scale, nullptr, nullptr, 0, 0, ws, stream);
+    // (the forward's fused prologue exists for d = 128; at d = 64 the recompute reads the
+    // materialised inputs)
+    const bool fused_fwd = flags && dk == 128;
+    e = kda_launch_chunk(32, dk, fused_fwd ? raw_bf16 : in_bf16, N, H, fused_fwd ? q_raw : q, fused_fwd ? k_raw : k,
+                         fused_fwd ? v_raw : v, fused_fwd ? a_raw : g, fused_fwd ? b_raw : beta, cu, s0, nullptr,
+                         kda::BC, reinterpret_cast<float *>(ws + off[1]), reinterpret_cast<float *>(ws + off[2]),
+                         scale, nullptr, nullptr, 0, fused_fwd ? flags : 0, ws, stream);
     if (e != hipSuccess) return e;
     size_t order_off, base_off;
     kda_chunk_workspace_layout(N, &order_off, &base_off);
@@ -960,5 +1095,17 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     else if (dk == 64) KDA_BWD(64, float);
     else return hipErrorInvalidValue;
 #undef KDA_BWD
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // fused prologue: gradients with respect to the raw inputs
+    if (flags && rows > 0) {
+        const uint16_t *qr = static_cast<const uint16_t *>(q_raw), *kr = static_cast<const uint16_t *>(k_raw);
+        const uint16_t *ar = reinterpret_cast<const uint16_t *>(a_raw);
+        if (dk == 128)
+            hipLaunchKernelGGL(kda::bwd_epilogue_kernel<128>, dim3(row_blocks), dim3(256), 0, stream, qr, kr, ar, b_raw,
+                               rows, flags, dq, dkk, dg, dbeta);
+        else
+            hipLaunchKernelGGL(kda::bwd_epilogue_kernel<64>, dim3(row_blocks), dim3(256), 0, stream, qr, kr, ar, b_raw,
+                               rows, flags, dq, dkk, dg, dbeta);
+    }
     return hipGetLastError();
 }

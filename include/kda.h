@@ -228,6 +228,16 @@ kda_status kda_decode_step(const kda_decode_args *args, void *stream);
  *   dq, dk_out, dg   fp32 [T, H, dk];  dv_out fp32 [T, H, dv];  dbeta fp32 [T, H].
  *                    Written in full; none may alias another buffer of the call.
  *   d_initial_state  NULL => not written; else fp32 [N, H, dk, dv].
+ *   gate_mode        as in kda_fwd_args.  KDA_GATE_PREACTIVATION: g holds the bf16
+ *                    pre-activations a (raw 16-bit words) and beta the fp32 pre-activations
+ *                    b; dg and dbeta are then dL/da and dL/db (through g = -5 sigmoid(a),
+ *                    beta = sigmoid(b)).
+ *   normalize_qk     as in kda_fwd_args: 1 normalises q and k inside; dq and dk are then
+ *                    the gradients with respect to the raw q and k (zero for a zero row).
+ *                    Either prologue needs bf16 inputs (else KDA_ERR_UNSUPPORTED).  The
+ *                    prologue's outputs are materialised in the workspace: q / |q|, k / |k|
+ *                    and v in fp32 (3 * T*H*dk*4 bytes; the unit vectors are not rounded to
+ *                    bf16, as in the forward) and g, beta in fp32 (T*H*(dk + 1)*4 bytes).
  * Supported: d_k == d_v in {64, 128}; in_dtype KDA_F32 or KDA_BF16.  The
  * workspace (kda_chunk_bwd_workspace_bytes) holds the recomputed states, the
  * state gradients at every chunk boundary and per-chunk factors: about
@@ -259,6 +269,8 @@ typedef struct {
     float *dg;
     float *dbeta;
     float *d_initial_state;
+    int32_t gate_mode;
+    int32_t normalize_qk;
 } kda_bwd_args;
 
 /* Device workspace (bytes) that kda_chunk_bwd needs for `args` (host only).

@@ -82,19 +82,25 @@ def backward(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, d
 
 
 def backward_fused(q, k, v, g_pre, b_pre, cu_seqlens=None, scale=1.0, initial_state=None, do=None, dS_final=None,
-                   normalize=True):
-    """Gradients through the fused prologue (the operator takes g = -5 sigmoid(a), beta = sigmoid(b)
-    and, with normalize, q / |q| and k / |k| over d_k): backward() on the prologue's outputs, then
-    the chain rule back to the raw inputs, per (token, head):
+                   normalize=True, gate=True):
+    """Gradients through the fused prologue (the operator takes, with gate, g = -5 sigmoid(a),
+    beta = sigmoid(b) and, with normalize, q / |q| and k / |k| over d_k): backward() on the
+    prologue's outputs, then the chain rule back to the raw inputs, per (token, head):
         dL/da = dL/dg * (-5) s (1 - s),  s = sigmoid(a);      dL/db = dL/dbeta * beta (1 - beta);
         dL/dq = (dL/dq_n - q_n <q_n, dL/dq_n>) / |q|   (0 for a zero row), the same for k.
+    Without gate, g_pre and b_pre are g and beta themselves (their gradients pass unchanged).
     Returns (dq, dk, dv, da, db, dS0) for the raw q, k, v, a, b and S0, fp64."""
     from . import prologue
     qn, kn, g, beta = prologue(q, k, g_pre, b_pre, normalize)
+    if not gate:
+        g, beta = np.asarray(g_pre, dtype=np.float64), np.asarray(b_pre, dtype=np.float64)
     dqn, dkn, dv, dg, dbeta, dS0 = backward(qn, kn, v, g, beta, cu_seqlens, scale, initial_state, do, dS_final)
-    s = 1.0 / (1.0 + np.exp(-np.asarray(g_pre, dtype=np.float64)))
-    da = dg * (-5.0) * s * (1.0 - s)
-    db = dbeta * beta * (1.0 - beta)
+    if gate:
+        s = 1.0 / (1.0 + np.exp(-np.asarray(g_pre, dtype=np.float64)))
+        da = dg * (-5.0) * s * (1.0 - s)
+        db = dbeta * beta * (1.0 - beta)
+    else:
+        da, db = dg, dbeta
 
     def through_unit(x, xn, dxn):
         if not normalize:

@@ -237,11 +237,35 @@ def bwd_status(L, a, ws=FAKE * 64, ws_bytes=1 << 40):
     ("d_initial_state", FAKE * 6, kda.KDA_ERR_INVALID_ARGUMENT),   # aliases d_o
     ("total_tokens", 229, kda.KDA_ERR_INVALID_ARGUMENT),
     ("scale", float("nan"), kda.KDA_ERR_INVALID_ARGUMENT),
+    ("gate_mode", 5, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("normalize_qk", 2, kda.KDA_ERR_INVALID_ARGUMENT),
 ])
 def test_bwd_validation(L, field, value, expect):
     a, keep = bwd_args(**{field: value})
     assert bwd_status(L, a) == expect
     assert L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a)) == 0
+
+
+@pytest.mark.parametrize("field", ["gate_mode", "normalize_qk"])
+def test_bwd_prologue_needs_bf16(L, field):
+    a, keep = bwd_args(**{field: 1, "in_dtype": kda.KDA_F32})
+    assert bwd_status(L, a) == kda.KDA_ERR_UNSUPPORTED
+    assert L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_bwd_prologue_workspace(L):
+    # the prologue's outputs are materialised: fp32 q_n, k_n and v with the normalisation, fp32 g
+    # and beta with the gate
+    base = L.kda_chunk_bwd_workspace_bytes(ctypes.byref(bwd_args()[0]))
+    a, keep = bwd_args(gate_mode=kda.KDA_GATE_PREACTIVATION, normalize_qk=1)
+    need = L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a))
+    rows = 228 * 4
+    assert need >= base + rows * (3 * 128 * 4 + 128 * 4 + 4)
+    assert bwd_status(L, a, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    g, keep2 = bwd_args(gate_mode=kda.KDA_GATE_PREACTIVATION)
+    n, keep3 = bwd_args(normalize_qk=1)
+    assert base < L.kda_chunk_bwd_workspace_bytes(ctypes.byref(g)) < need
+    assert base < L.kda_chunk_bwd_workspace_bytes(ctypes.byref(n)) < need
 
 
 def test_bwd_workspace(L):

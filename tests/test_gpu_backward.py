@@ -139,3 +139,49 @@ def test_backward_config1_sampled_heads_and_linearity():
     scale_ = float(np.sqrt(np.sum(dv.astype(np.float64) ** 2) * np.sum(w.v.astype(np.float64) ** 2)))
     print(f"[bwd identity] sum(dv v) = {lhs:.6e}  sum(do o) + sum(dST ST) = {rhs:.6e}", flush=True)
     assert abs(lhs - rhs) <= 1e-3 * scale_, (lhs, rhs, scale_)
+
+
+@pytest.mark.parametrize("gate,norm,d", [(True, True, 128), (True, False, 128), (False, True, 128), (True, True, 64)])
+def test_backward_fused_prologue(gate, norm, d):
+    """Gradients with respect to the raw inputs of the fused prologue (gate pre-activations a, b
+    with g = -5 sigmoid(a), beta = sigmoid(b); raw q, k normalised over d_k) against the oracle's
+    backward through the same prologue.  bf16 inputs, ragged sequences, initial and final states;
+    with the normalisation one q row and one k row are zero (their gradients are zero)."""
+    w = W.make_prefill_raw([200, 1, 0, 130, 77], H=3, dk=d, dv=d, seed=52, s0_std=0.1)
+    scale = d ** -0.5
+    q, k = w.q.copy(), w.k.copy()
+    if norm:
+        q[5, 0] = 0.0
+        k[7, 1] = 0.0
+    else:
+        # unnormalised q, k would make the recurrence blow up: use unit rows (still bf16-exact)
+        q = W.round_bf16((q / np.linalg.norm(q, axis=-1, keepdims=True)).astype(np.float32))
+        k = W.round_bf16((k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32))
+    if gate:
+        a_ref, b_ref = w.g, w.beta
+        g_in, b_in = to_dev(w.g, torch.bfloat16), to_dev(w.beta, torch.float32)
+    else:
+        g64 = -5.0 / (1.0 + np.exp(-w.g.astype(np.float64)))
+        b64 = 1.0 / (1.0 + np.exp(-w.beta.astype(np.float64)))
+        a_ref, b_ref = g64.astype(np.float32), b64.astype(np.float32)
+        g_in, b_in = to_dev(a_ref, torch.float32), to_dev(b_ref, torch.float32)
+    do, dsf = W.make_cotangents(w, seed=52)
+    outs = kda.kda_chunk_bwd(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(w.v, torch.bfloat16),
+                             g_in, b_in, to_dev(do, torch.float32), list(w.cu_seqlens), scale,
+                             to_dev(w.s0, torch.float32), to_dev(dsf, torch.float32),
+                             gate_preactivation=gate, normalize_qk=norm)
+    torch.cuda.synchronize()
+    got = [x.cpu().numpy() for x in outs]
+    ref = OB.backward_fused(q, k, w.v, a_ref, b_ref, w.cu_seqlens, scale, w.s0, do, dsf, normalize=norm, gate=gate)
+    errs = {n: W.rel_max_err(x, y) for n, x, y in zip(NAMES, got, ref)}
+    label = f"fused prologue gate={gate} norm={norm} d={d}"
+    print(f"[bwd parity] {label}: " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    log = os.environ.get("KDA_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(json.dumps({"case": "bwd " + label, "H": w.H, "d": d, "dtype": "bf16",
+                                "tokens": w.total_tokens, "tol": TOL["bf16"], **errs}) + "\n")
+    for k_, v_ in errs.items():
+        assert v_ <= TOL["bf16"], (k_, v_)
+    if norm:
+        assert np.all(got[0][5, 0] == 0) and np.all(got[1][7, 1] == 0)

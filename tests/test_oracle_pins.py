@@ -421,8 +421,8 @@ def test_backward_matches_finite_differences():
 
 def test_backward_fused_prologue_matches_finite_differences():
     """Central differences of the same L, now a function of the raw q, k, the gate pre-activations
-    a, b (g = -5 sigmoid(a), beta = sigmoid(b)) and v, S0, against backward_fused, with and
-    without the q/k normalisation."""
+    a, b (g = -5 sigmoid(a), beta = sigmoid(b)) and v, S0, against backward_fused: gate and
+    normalisation, the gate alone, the normalisation alone (then a, b are g and beta)."""
     import oracle
     from oracle.backward import backward_fused
     rng = np.random.default_rng(29)
@@ -436,12 +436,16 @@ def test_backward_fused_prologue_matches_finite_differences():
     do = rng.standard_normal((T, H, dv))
     dSf = rng.standard_normal((2, H, dk, dv))
     scale = 0.8
-    for normalize in (True, False):
+    for gate, normalize in ((True, True), (True, False), (False, True)):
+        a_in, b_in = (a, b) if gate else (-0.5 * np.abs(a), 1.0 / (1.0 + np.exp(-b)))
+
         def loss(q_, k_, v_, a_, b_, S0_):
             qn, kn, g, beta = oracle.prologue(q_, k_, a_, b_, normalize)
+            if not gate:
+                g, beta = a_, b_
             return _loss(qn, kn, v_, g, beta, S0_, do, dSf, scale, cu)
-        grads = backward_fused(q, k, v, a, b, cu, scale, S0, do, dSf, normalize)
-        args = [q, k, v, a, b, S0]
+        grads = backward_fused(q, k, v, a_in, b_in, cu, scale, S0, do, dSf, normalize, gate)
+        args = [q, k, v, a_in, b_in, S0]
         eps = 1e-6
         for which, (x, gx) in enumerate(zip(args, grads)):
             for idx in np.ndindex(*x.shape):
@@ -450,7 +454,7 @@ def test_backward_fused_prologue_matches_finite_differences():
                 xp[which][idx] += eps
                 xm[which][idx] -= eps
                 fd = (loss(*xp) - loss(*xm)) / (2 * eps)
-                assert abs(fd - gx[idx]) <= 1e-7 * max(1.0, abs(fd)), (normalize, which, idx, fd, gx[idx])
+                assert abs(fd - gx[idx]) <= 1e-7 * max(1.0, abs(fd)), (gate, normalize, which, idx, fd, gx[idx])
 
 
 def test_backward_pure_decay_closed_form():
