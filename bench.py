@@ -410,8 +410,8 @@ def summarize_backward_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, mf
         f.write("Workload: backward of the prefill T=65536 H=96 d_k=d_v=128, bf16 q/k/v, fp32 g/beta, initial "
                 "state, d_o and dS_T (one `bench.py --backward` call).\n\n")
         f.write(f"HBM bytes = counter x scale, scales from a plain copy of {copy_bytes} B read + written: "
-                f"fetch {fs:.4f}, write {ws:.4f}.  MFMA busy over all 1024 SIMDs (these kernels issue "
-                "fp32 MFMA only, besides the forward).\n\n")
+                f"fetch {fs:.4f}, write {ws:.4f}.  MFMA busy over all 1024 SIMDs (fp32 MFMA, and bf16 hi+lo "
+                "products in the gradient kernel and the forward recompute).\n\n")
         f.write("| kernel | HBM read (GB) | HBM written (GB) | MFMA busy |\n|---|---|---|---|\n")
         for ln in lines:
             f.write(ln)
