@@ -234,7 +234,8 @@ kda_status kda_decode_step(const kda_decode_args *args, void *stream);
  *                    beta = sigmoid(b)).
  *   normalize_qk     as in kda_fwd_args: 1 normalises q and k inside; dq and dk are then
  *                    the gradients with respect to the raw q and k (zero for a zero row).
- *                    Either prologue needs bf16 inputs (else KDA_ERR_UNSUPPORTED).  The
+ *                    Either prologue needs bf16 inputs (else KDA_ERR_UNSUPPORTED); unlike
+ *                    the forward's, it is supported at d_k = 64 and 128.  The
  *                    prologue's outputs are materialised in the workspace: q / |q|, k / |k|
  *                    and v in fp32 (3 * T*H*dk*4 bytes; the unit vectors are not rounded to
  *                    bf16, as in the forward) and g, beta in fp32 (T*H*(dk + 1)*4 bytes).

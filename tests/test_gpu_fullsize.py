@@ -112,6 +112,53 @@ def test_config2_backward_T65536_H96_sampled_head_and_identity():
                                               zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got, ref)})
 
 
+@pytest.mark.timeout(900)
+def test_config2_backward_fused_prologue_T65536_H96_sampled_head_and_identity():
+    """The backward through the fused gate / normalisation prologue at the benchmark's shape and in
+    its launch configuration (`bench.py --backward --prologue`): raw bf16 q, k ~ N(0,1), bf16 gate
+    pre-activations a ~ N(0,1), fp32 b ~ N(0,1), scale d^-1/2, drawn on the device with a seeded
+    generator.  Every gradient finite; one whole head against the oracle's adjoint through the
+    same prologue; over all 96 heads the linearity identity (the prologue touches neither v nor S_0)."""
+    from oracle import backward as OB
+    d = dev()
+    T, H, D = 65536, 96, 128
+    gen = torch.Generator(device=d)
+    gen.manual_seed(33)
+
+    def rn(*shape):
+        return torch.randn(shape, generator=gen, device=d)
+
+    bf = torch.bfloat16
+    q, k, v, a = rn(T, H, D).to(bf), rn(T, H, D).to(bf), rn(T, H, D).to(bf), rn(T, H, D).to(bf)
+    b = rn(T, H)
+    s0, do, dsf = 0.1 * rn(1, H, D, D), rn(T, H, D), rn(1, H, D, D)
+    scale = D ** -0.5
+    pro = dict(gate_preactivation=True, normalize_qk=True)
+    grads = kda.kda_chunk_bwd(q, k, v, a, b, do, [0, T], scale, s0, dsf, **pro)
+    o, sf, _ = kda.kda_chunk_fwd(q, k, v, a, b, [0, T], scale, s0, True, 0, chunk_size=32, **pro)
+    torch.cuda.synchronize()
+    for x in grads:
+        assert bool(torch.isfinite(x).all())
+    dv, ds0 = grads[2], grads[5]
+    lhs = float((dv.double() * v.double()).sum() + (ds0.double() * s0.double()).sum())
+    rhs = float((do.double() * o.double()).sum() + (dsf.double() * sf.double()).sum())
+    norm = float(torch.sqrt((dv.double() ** 2).sum() * (v.double() ** 2).sum()))
+    print(f"[fullsize] config2 fused-prologue backward identity: {lhs:.6e} vs {rhs:.6e} (scale {norm:.3e})",
+          flush=True)
+    assert abs(lhs - rhs) <= 1e-3 * norm, (lhs, rhs, norm)
+    del o, sf
+    h = 57
+
+    def host(x):
+        return x[:, h:h + 1].float().cpu().numpy().astype(np.float64)
+
+    ref = OB.backward_fused(host(q), host(k), host(v), host(a), host(b), [0, T], scale, host(s0), host(do),
+                            host(dsf), normalize=True, gate=True)
+    got = [host(x) for x in grads]
+    _report(f"config2 fused-prologue backward head {h}",
+            {n: W.rel_max_err(x, r) for n, x, r in zip(("dq", "dk", "dv", "da", "db", "dS0"), got, ref)})
+
+
 def test_config3_decode_N256_H96_every_state():
     w = W.make_config(3)
     d = dev()
