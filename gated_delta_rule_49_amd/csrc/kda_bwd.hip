@@ -986,7 +986,7 @@ __global__ void __launch_bounds__(256) bwd_epilogue_kernel(const uint16_t *__res
 
 extern "C" size_t kda_chunk_workspace_layout(int N, size_t *order_off, size_t *base_off);
 
-// Backward workspace: [forward plan][chunk bases][checkpoints every 32][forward o][D per chunk]
+// Backward workspace: [forward plan][chunk bases][checkpoints every 32][D per chunk]
 // [scan operands per chunk][A, T per chunk][with the fused prologue: q_n, k_n, v (fp32, with the
 // normalisation), g, beta (with the gate)].
 extern "C" __attribute__((visibility("hidden"))) size_t kda_bwd_workspace_layout(int N, int H, int T, int dk, int dv,
@@ -997,8 +997,8 @@ extern "C" __attribute__((visibility("hidden"))) size_t kda_bwd_workspace_layout
     size_t o[12];
     o[0] = up(kda_chunk_workspace_layout(N, nullptr, nullptr));           // cbase
     o[1] = o[0] + up((size_t)(N + 1) * 4);                                 // checkpoints
-    o[2] = o[1] + up((size_t)n_ck * H * dk * dv * 4);                       // forward o
-    o[3] = o[2] + up((size_t)T * H * dv * 4);                               // D
+    o[2] = o[1] + up((size_t)n_ck * H * dk * dv * 4);                       // (no region)
+    o[3] = o[2];                                                            // D
     o[4] = o[3] + up((size_t)n_chunks * H * dk * dv * 4);                   // scan operands
     o[5] = o[4] + up((size_t)n_chunks * H * rec * 4);                       // A, T
     o[6] = o[5] + up((size_t)n_chunks * H * 2 * kda::BC * kda::BC * 4);     // q_n
@@ -1053,14 +1053,14 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
         if (flags & kda::KDA_PRO_NORM) { q = qn; k = kn; v = vf; in_bf16 = 0; }
         if (flags & kda::KDA_PRO_GATE) { g = gm; beta = bm; }
     }
-    // states at every 32-token boundary (the forward's plan lands at the start of the workspace)
-    // (the forward's fused prologue exists for d = 128; at d = 64 the recompute reads the
-    // materialised inputs)
+    // states at every 32-token boundary, without the outputs (the forward's plan lands at the start
+    // of the workspace); the forward's fused prologue exists for d = 128, at d = 64 the recompute
+    // reads the materialised inputs
     const bool fused_fwd = flags && dk == 128;
     e = kda_launch_chunk(32, dk, fused_fwd ? raw_bf16 : in_bf16, N, H, fused_fwd ? q_raw : q, fused_fwd ? k_raw : k,
                          fused_fwd ? v_raw : v, fused_fwd ? a_raw : g, fused_fwd ? b_raw : beta, cu, s0, nullptr,
-                         kda::BC, reinterpret_cast<float *>(ws + off[1]), reinterpret_cast<float *>(ws + off[2]),
-                         scale, nullptr, nullptr, 0, fused_fwd ? flags : 0, ws, stream);
+                         kda::BC, reinterpret_cast<float *>(ws + off[1]), nullptr, scale, nullptr, nullptr, 0,
+                         (fused_fwd ? flags : 0) | kda::KDA_STATES_ONLY, ws, stream);
     if (e != hipSuccess) return e;
     size_t order_off, base_off;
     kda_chunk_workspace_layout(N, &order_off, &base_off);

@@ -144,7 +144,7 @@ template <int JT> __device__ __forceinline__ void store_cols(float *ptr, const f
 }
 
 // PRO: the fused prologue (KDA_PRO_* bits), a compile-time choice so that the plain path keeps
-// none of its code.
+// none of its code; with KDA_STATES_ONLY the kernel produces the states alone (no q, no o).
 template <int DK, int SPLIT, bool F32P, typename IN_T, int PRO = 0>
 __global__ void __launch_bounds__((chunk32_threads<DK, SPLIT>()))
 chunk32_kernel(const ChunkParams p) {
@@ -162,6 +162,7 @@ chunk32_kernel(const ChunkParams p) {
     using M = Mat<F32P>;
     using F = Frag<F32P>;
     using PR = Pair<IN_T>;
+    constexpr bool SO = (PRO & KDA_STATES_ONLY) != 0;   // states only: q, Gamma*Q, A_qk and o skipped
 
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
 
@@ -333,7 +334,7 @@ chunk32_kernel(const ChunkParams p) {
         const int knb = t == 0 ? 0 : (t == 1 ? 2 : 1);
         const int a = t == 0 ? 0 : 1, b = t == 1 ? 1 : 0;
         const f32x4_t gk = gram_prod(sm, knb, a, false, lane);
-        store_aqk(sm, a, b, gram_prod(sm, knb, a, true, lane), lane);
+        if constexpr (!SO) store_aqk(sm, a, b, gram_prod(sm, knb, a, true, lane), lane);
         const float br = beta_row(sm, a, ch, lane);
         if (t == 2) {
             float w[4];
@@ -388,8 +389,10 @@ chunk32_kernel(const ChunkParams p) {
                     }
                     diag_inverse(sm, rw, ch, lane, z, zb);
                 } else if (rw == 2) {
-                    store_aqk(sm, 0, 0, gram_prod(sm, 0, 0, true, lane), lane);
-                    store_aqk(sm, 1, 1, gram_prod(sm, 2, 1, true, lane), lane);
+                    if constexpr (!SO) {
+                        store_aqk(sm, 0, 0, gram_prod(sm, 0, 0, true, lane), lane);
+                        store_aqk(sm, 1, 1, gram_prod(sm, 2, 1, true, lane), lane);
+                    }
                 } else {
                     const f32x4_t gk = gram_prod(sm, 1, 1, false, lane);
                     const float br = beta_row(sm, 1, ch, lane);
@@ -397,7 +400,7 @@ chunk32_kernel(const ChunkParams p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = br * gk[e];
                     M::template put_hl<4>(sm + L::AW, L::AW_PLANE, fofs<1>(lr, 4 * lq), w);
-                    store_aqk(sm, 1, 0, gram_prod(sm, 1, 1, true, lane), lane);
+                    if constexpr (!SO) store_aqk(sm, 1, 0, gram_prod(sm, 1, 1, true, lane), lane);
                 }
             }
             lds_barrier();
@@ -457,21 +460,31 @@ chunk32_kernel(const ChunkParams p) {
                 for (int s = 0; s < KB; ++s) {
                     const F fk0 = M::template get<false>(sm + L::KS, 0, fbase<KB>(0, s, lane));
                     const F fk1 = M::template get<false>(sm + L::KG_AT, 0, fbase<KB>(1, s, lane));
-                    const F fq0 = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(0, s, lane));
-                    const F fq1 = M::template get<true>(sm + L::QT_AT, L::QT_PLANE, fbase<KB>(1, s, lane));
+                    if constexpr (SO) {
 #pragma unroll
-                    for (int jt = 0; jt < JT; ++jt) {
-                        const F sf = M::template from_tiles<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
-                        mma<false, false>(Yacc[0][jt], fk0, sf);
-                        mma<true, true>(Oacc[0][jt], fq0, sf);
-                        mma<true, true>(Oacc[1][jt], fq1, sf);
-                        mma<false, false>(Yacc[1][jt], fk1, sf);
+                        for (int jt = 0; jt < JT; ++jt) {
+                            const F sf = M::template from_tiles<false>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
+                            mma<false, false>(Yacc[0][jt], fk0, sf);
+                            mma<false, false>(Yacc[1][jt], fk1, sf);
+                        }
+                    } else {
+                        const F fq0 = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(0, s, lane));
+                        const F fq1 = M::template get<true>(sm + L::QT_AT, L::QT_PLANE, fbase<KB>(1, s, lane));
+#pragma unroll
+                        for (int jt = 0; jt < JT; ++jt) {
+                            const F sf = M::template from_tiles<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
+                            mma<false, false>(Yacc[0][jt], fk0, sf);
+                            mma<true, true>(Oacc[0][jt], fq0, sf);
+                            mma<true, true>(Oacc[1][jt], fq1, sf);
+                            mma<false, false>(Yacc[1][jt], fk1, sf);
+                        }
                     }
                 }
                 // park the output partials in LDS until stage o (this lane's private slots)
+                if constexpr (!SO)
 #pragma unroll
-                for (int j = 0; j < 2 * JT; ++j)
-                    *reinterpret_cast<f32x4_t *>(sm + L::OST + (j * 64 * NSW + 64 * sw + lane) * 16) = Oacc[j / JT][j % JT];
+                    for (int j = 0; j < 2 * JT; ++j)
+                        *reinterpret_cast<f32x4_t *>(sm + L::OST + (j * 64 * NSW + 64 * sw + lane) * 16) = Oacc[j / JT][j % JT];
             }
             lds_barrier();
 
@@ -497,7 +510,7 @@ chunk32_kernel(const ChunkParams p) {
                     UF[jt] = M::template from_tiles<true>(u0, u1);
                 }
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
+                for (int rt = 0; rt < 2 && !SO; ++rt) {
                     const F fa = M::template get<true>(sm + L::AQK, L::TRI_PLANE, fbase<1>(rt, 0, lane));
                     f32x4_t acc[JT];
 #pragma unroll
@@ -624,7 +637,8 @@ chunk32_kernel(const ChunkParams p) {
                 const int r = min(4 * rgp + i, nv - 1);
                 const unsigned off = (unsigned)((r * H + h) * DK + c0);
                 kn_[i] = PR::load(kb + off);
-                qn_[i] = PR::load(qb + off);
+                if constexpr (SO) qn_[i] = PR::zero();
+                else qn_[i] = PR::load(qb + off);
                 if constexpr (pre) gn_[i].x = __uint_as_float(*reinterpret_cast<const uint32_t *>(ab + off));   // a pair
                 else gn_[i] = *reinterpret_cast<const float2 *>(gb + off);
             }
@@ -785,7 +799,7 @@ chunk32_kernel(const ChunkParams p) {
                         if (SA) qtv[i][c] = qs[c] * P0[c];    // Gamma * q (decay from the chunk start)
                     }
                     M::put_h2(sm + L::KS, ks_off[i], ks[0], ks[1]);
-                    M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, ks_off[i], qs);
+                    if constexpr (!SO) M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, ks_off[i], qs);
                     // Kn rows: sub-chunk 0 feeds tiles (0,0) [x 1/P0] and (1,0) [x 1]; sub-chunk 1 feeds (1,1) [x 1/P1]
                     M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn_off[i], kd);
                     if (SA == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn2_off[i], ke);
@@ -825,7 +839,7 @@ chunk32_kernel(const ChunkParams p) {
                 if (rgp == 0)
                     *reinterpret_cast<float2 *>(sm + L::GC + (buf * DK + c0) * 4) = make_float2(gl[0], gl[1]);
                 // Gamma * Q of chunk nxt (rows 16..31), read by stage a in segment 1 of the next iteration
-                if (sa)
+                if (!SO && sa)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) M::template put_hl<2>(sm + L::QT_AT, L::QT_PLANE, ks_off[i], qtv[i]);
                 // -V of chunk nxt in fp32, read by stage a in segment 1 of the next iteration (stage a
@@ -853,33 +867,35 @@ kda_launch_chunk32(int dk, int in_bf16, unsigned chains, const kda::ChunkParams 
 #define KDA_C32(DKV, SP, F32P, T, PRO)                                                                   \
     hipLaunchKernelGGL((kda::chunk32_kernel<DKV, SP, F32P, T, PRO>), dim3(chains * SP),                 \
                        dim3(kda::chunk32_threads<DKV, SP>()), 0, stream, p)
-    if (p.flags != 0) {
-        // fused prologue: bf16 inputs, d_k = 128
-        if (dk != 128 || !in_bf16 || p.flags > 3) return hipErrorInvalidValue;
-        if (split == 2) {
-            if (p.flags == 1) KDA_C32(128, 2, false, uint16_t, 1);
-            else if (p.flags == 2) KDA_C32(128, 2, false, uint16_t, 2);
-            else KDA_C32(128, 2, false, uint16_t, 3);
-        } else {
-            if (p.flags == 1) KDA_C32(128, 1, false, uint16_t, 1);
-            else if (p.flags == 2) KDA_C32(128, 1, false, uint16_t, 2);
-            else KDA_C32(128, 1, false, uint16_t, 3);
-        }
-        return hipGetLastError();
-    }
-    if (split == 2) {
-        if (dk == 128 && in_bf16) KDA_C32(128, 2, false, uint16_t, 0);
-        else if (dk == 128) KDA_C32(128, 2, true, float, 0);
-        else if (dk == 64 && in_bf16) KDA_C32(64, 2, false, uint16_t, 0);
-        else if (dk == 64) KDA_C32(64, 2, true, float, 0);
-        else return hipErrorInvalidValue;
-    } else {
-        if (dk == 128 && in_bf16) KDA_C32(128, 1, false, uint16_t, 0);
-        else if (dk == 128) KDA_C32(128, 1, true, float, 0);
-        else if (dk == 64 && in_bf16) KDA_C32(64, 1, false, uint16_t, 0);
-        else if (dk == 64) KDA_C32(64, 1, true, float, 0);
-        else return hipErrorInvalidValue;
-    }
+    const int pro = p.flags & (kda::KDA_PRO_GATE | kda::KDA_PRO_NORM);
+    if (p.flags & ~(kda::KDA_PRO_GATE | kda::KDA_PRO_NORM | kda::KDA_STATES_ONLY)) return hipErrorInvalidValue;
+    if (pro != 0 && (dk != 128 || !in_bf16)) return hipErrorInvalidValue;   // fused prologue: bf16, d_k = 128
+    // (S: SPLIT, F: the flags, both compile-time)
+#define KDA_C32_DT(S, F)                                                                                    \
+    do {                                                                                                   \
+        if (dk == 128 && in_bf16) KDA_C32(128, S, false, uint16_t, F);                                     \
+        else if (dk == 128) KDA_C32(128, S, true, float, F);                                               \
+        else if (dk == 64 && in_bf16) KDA_C32(64, S, false, uint16_t, F);                                  \
+        else if (dk == 64) KDA_C32(64, S, true, float, F);                                                 \
+        else return hipErrorInvalidValue;                                                                  \
+    } while (0)
+#define KDA_C32_FLAGS(S)                                                                                    \
+    do {                                                                                                   \
+        switch (p.flags) {                                                                                 \
+            case 0: KDA_C32_DT(S, 0); break;                                                               \
+            case 1: KDA_C32(128, S, false, uint16_t, 1); break;                                            \
+            case 2: KDA_C32(128, S, false, uint16_t, 2); break;                                            \
+            case 3: KDA_C32(128, S, false, uint16_t, 3); break;                                            \
+            case 4: KDA_C32_DT(S, 4); break;                                                               \
+            case 5: KDA_C32(128, S, false, uint16_t, 5); break;                                            \
+            case 6: KDA_C32(128, S, false, uint16_t, 6); break;                                            \
+            default: KDA_C32(128, S, false, uint16_t, 7); break;                                           \
+        }                                                                                                  \
+    } while (0)
+    if (split == 2) KDA_C32_FLAGS(2);
+    else KDA_C32_FLAGS(1);
+#undef KDA_C32_FLAGS
+#undef KDA_C32_DT
 #undef KDA_C32
     return hipGetLastError();
 }

@@ -72,6 +72,9 @@ template <int CTRL> __device__ __forceinline__ float dpp_f32(float v) {
 // Fused prologue of the chunked prefill (bits of ChunkParams::flags).
 constexpr int KDA_PRO_GATE = 1;   // g holds bf16 pre-activations a (g = -5 sigmoid(a)), beta fp32 b (sigmoid(b))
 constexpr int KDA_PRO_NORM = 2;   // q and k are L2-normalised per (token, head) over d_k
+// Internal (the backward's recompute of the chunk-start states): o is neither formed nor written,
+// and q is not read.
+constexpr int KDA_STATES_ONLY = 4;
 
 // ---- MFMA ------------------------------------------------------------------
 // 16x16 output tiles: lane l holds D[4*(l/16) + e][l % 16], e = 0..3.

@@ -242,8 +242,8 @@ kda_status kda_decode_step(const kda_decode_args *args, void *stream);
  * Supported: d_k == d_v in {64, 128}; in_dtype KDA_F32 or KDA_BF16.  The
  * workspace (kda_chunk_bwd_workspace_bytes) holds the recomputed states, the
  * state gradients at every chunk boundary and per-chunk factors: about
- * (2 dk dv + 2 * 32 (dk + dv) + 3 * 32^2) * 4 bytes per (32-token chunk, head)
- * plus T*H*dv*4 bytes.  Results are fp32 and deterministic.
+ * (3 dk dv + 32 (2 dk + dv) + dk + 2 * 32^2) * 4 bytes per (32-token chunk,
+ * head).  Results are fp32 and deterministic.
  */
 typedef struct {
     uint32_t struct_size;

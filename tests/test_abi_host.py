@@ -272,8 +272,8 @@ def test_bwd_workspace(L):
     # one sequence of 100 tokens (3 checkpoints, 4 chunks) and one of 128 (4 and 4), 4 heads, d = 128
     a, keep = bwd_args()
     need = L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a))
-    # checkpoints (7), forward o, and per chunk (8): D, W, E, A and T
-    expect = (7 * 4 * 128 * 128 + 228 * 4 * 128 + 8 * 4 * (128 * 128 + 2 * 32 * 128 + 2 * 32 * 32)) * 4
+    # checkpoints (7) and per chunk (8): D, W, E, A and T
+    expect = (7 * 4 * 128 * 128 + 8 * 4 * (128 * 128 + 2 * 32 * 128 + 2 * 32 * 32)) * 4
     assert need % 256 == 0 and need >= expect
     assert bwd_status(L, a, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
     assert bwd_status(L, a, ws=0, ws_bytes=need) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
