@@ -471,7 +471,9 @@ __global__ void __launch_bounds__(256) bwd_dstate_kernel(const BwdParams p) {
 // One workgroup of dk/16 waves per (chunk, head).  Stage 1: wave w owns value columns
 // 16w..16w+15 (X, Kbar D, dZ, U, dv, the <dZ, R> part of dbeta).  Stage 2: the 32x32 products
 // <dZ_r, U_s> and <dO_r, U_s>.  Stage 3: wave w owns key channels 16w..16w+15 (dq, dk, dg).
-template <int DK, typename IN_T>
+// HL: the stage-2 and stage-3 products take bf16 hi+lo operands (the bf16-input error budget; also
+// for the fp32 unit vectors of the fused normalisation), else fp32 MFMA.
+template <int DK, typename IN_T, bool HL = sizeof(IN_T) == 2>
 __global__ void __launch_bounds__(DK * 4) __attribute__((amdgpu_waves_per_eu(4)))
 bwd_grad_kernel(const BwdParams p) {
     constexpr int NW = DK / 16, NT = DK * 4, P = DK + 4, DV = DK;
@@ -480,9 +482,8 @@ bwd_grad_kernel(const BwdParams p) {
     // workgroups fit in one CU's LDS.
     constexpr int PK = DK + 16 / (int)sizeof(IN_T);   // row pitch of sk, sq: rows start 16-byte aligned
     __shared__ __attribute__((aligned(16))) IN_T sk[BC][PK], sq[BC][PK];
-    // U (sx) and dZ (sz): fp32 rows, or with bf16 inputs hi and lo bf16 planes (written once by the
-    // wave that forms them, read as 8-element MFMA fragments in stages 2 and 3)
-    constexpr bool HL = sizeof(IN_T) == 2;
+    // U (sx) and dZ (sz): fp32 rows, or with HL hi and lo bf16 planes (written once by the wave that
+    // forms them, read as 8-element MFMA fragments in stages 2 and 3)
     constexpr int PB = DK + 8;                              // bf16 plane row pitch (elements)
     constexpr int PLANE = BC * PB * 2;                      // bytes of one plane
     constexpr int XB = HL ? 2 * PLANE : BC * P * 4;
@@ -1081,18 +1082,22 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned chunk_blocks = (unsigned)(n_chunks * H);
     const unsigned scan_blocks = (unsigned)N * (unsigned)H * (unsigned)(dk / 16);
-#define KDA_BWD(DKV, T_)                                                                                           \
+    // (with the normalising prologue the inputs are fp32 unit vectors, the error budget bf16's)
+#define KDA_BWD(DKV, T_, HL_)                                                                                      \
     do {                                                                                                           \
         if (chunk_blocks)                                                                                          \
             hipLaunchKernelGGL((kda::bwd_prep_kernel<DKV, T_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, p); \
         hipLaunchKernelGGL((kda::bwd_dstate_kernel<DKV>), dim3(scan_blocks), dim3(256), 0, stream, p);             \
         if (chunk_blocks)                                                                                          \
-            hipLaunchKernelGGL((kda::bwd_grad_kernel<DKV, T_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, p); \
+            hipLaunchKernelGGL((kda::bwd_grad_kernel<DKV, T_, HL_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, \
+                               p);                                                                                 \
     } while (0)
-    if (dk == 128 && in_bf16) KDA_BWD(128, uint16_t);
-    else if (dk == 128) KDA_BWD(128, float);
-    else if (dk == 64 && in_bf16) KDA_BWD(64, uint16_t);
-    else if (dk == 64) KDA_BWD(64, float);
+    if (dk == 128 && in_bf16) KDA_BWD(128, uint16_t, true);
+    else if (dk == 128 && raw_bf16) KDA_BWD(128, float, true);
+    else if (dk == 128) KDA_BWD(128, float, false);
+    else if (dk == 64 && in_bf16) KDA_BWD(64, uint16_t, true);
+    else if (dk == 64 && raw_bf16) KDA_BWD(64, float, true);
+    else if (dk == 64) KDA_BWD(64, float, false);
     else return hipErrorInvalidValue;
 #undef KDA_BWD
     if ((e = hipGetLastError()) != hipSuccess) return e;
