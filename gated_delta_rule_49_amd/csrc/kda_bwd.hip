@@ -20,12 +20,15 @@
 // dB = q dq + k dkp - k dkm, the last row also gets Gam_C rowsum(S * D) + sum_s Kbar_s dKbar_s,
 // and dg is the reverse cumulative sum of dB over the chunk.
 //
-// Four launches: the forward with a checkpoint every 32 tokens (states at chunk starts); a
-// per-chunk prep kernel (A, Aq, T, W, E = scale Aq^T dO); the state-gradient scan, sequential
-// over the chunks of a (sequence, head) and split over 16-column blocks of d_v; and the
-// per-chunk gradient kernel.  All products run on the fp32 MFMA (16x16x4): lane l supplies
-// row (or column) l % 16 and contraction index 4 (l / 16) + kk in instruction kk; an output
-// tile holds element (4 (l / 16) + e, l % 16) in slot e.
+// Four launches: the forward in its states-only form with a checkpoint every 32 tokens (states
+// at chunk starts, no outputs); a per-chunk prep kernel (A, Aq, T, W, E = scale Aq^T dO); the
+// state-gradient scan, sequential over the chunks of a (sequence, head) and split over
+// 16-column blocks of d_v; and the per-chunk gradient kernel.  With the fused prologue, a
+// prologue kernel materialises the operator's inputs first and an epilogue kernel takes the
+// gradients back to the raw inputs last.  Products run on the fp32 MFMA (16x16x4): lane l
+// supplies row (or column) l % 16 and contraction index 4 (l / 16) + kk in instruction kk; an
+// output tile holds element (4 (l / 16) + e, l % 16) in slot e.  The gradient kernel's stage-2
+// and stage-3 products take bf16 hi+lo operand pairs instead when the inputs are bf16.
 //
 // The pair factors use a reference row m per 16x16 tile (7 and 23 on the diagonal tiles, 15
 // below them): e^{B_r - B_s} = e^{B_r - B_m} e^{B_m - B_s} with both factors within e^{40}
