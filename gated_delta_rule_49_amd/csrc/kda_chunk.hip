@@ -467,21 +467,34 @@ chunk_fwd_kernel(const ChunkParams p) {
     }
 }
 
-// Launch plan: sequences ordered longest first (ties: lower index first), so the
-// longest (sequence, head) chains are dispatched first; and, per sequence, the
-// index of its first checkpoint.  One workgroup.
-__global__ void __launch_bounds__(1024)
-plan_kernel(const int32_t *__restrict__ cu, int N, int every, int32_t *__restrict__ order,
-            int64_t *__restrict__ ckpt_base) {
-    for (int nn = threadIdx.x; nn < N; nn += blockDim.x) {
-        const int Ln = cu[nn + 1] - cu[nn];
-        int rank = 0;
-        for (int m = 0; m < N; ++m) {
-            const int Lm = cu[m + 1] - cu[m];
-            rank += (Lm > Ln) || (Lm == Ln && m < nn);
+// Launch plan, part 1: sequences ordered longest first (ties: lower index first), so the
+// longest (sequence, head) chains are dispatched first.  One thread per sequence counts the
+// sequences that go before it; the lengths are staged through LDS 1024 at a time.
+constexpr int PLAN_RANK_THREADS = 256;
+__global__ void __launch_bounds__(PLAN_RANK_THREADS)
+plan_rank_kernel(const int32_t *__restrict__ cu, int N, int32_t *__restrict__ order) {
+    __shared__ int32_t sl[1024];
+    const int nn = (int)blockIdx.x * PLAN_RANK_THREADS + (int)threadIdx.x;
+    const int Ln = nn < N ? cu[nn + 1] - cu[nn] : 0;
+    int rank = 0;
+    for (int base = 0; base < N; base += 1024) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < 1024; i += PLAN_RANK_THREADS)
+            sl[i] = base + i < N ? cu[base + i + 1] - cu[base + i] : 0;
+        __syncthreads();
+        const int lim = min(1024, N - base);
+        for (int m = 0; m < lim; ++m) {
+            const int Lm = sl[m];
+            rank += (Lm > Ln) || (Lm == Ln && base + m < nn);
         }
-        order[rank] = nn;
     }
+    if (nn < N) order[rank] = nn;
+}
+
+// Launch plan, part 2: per sequence, the index of its first checkpoint (an exclusive scan of
+// floor(L / every)).  One workgroup.
+__global__ void __launch_bounds__(1024)
+plan_kernel(const int32_t *__restrict__ cu, int N, int every, int64_t *__restrict__ ckpt_base) {
     if (every > 0) {
         __shared__ int64_t carry;
         if (threadIdx.x == 0) carry = 0;
@@ -531,9 +544,14 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int
     kda_chunk_workspace_layout(N, &oo, &bo);
     int32_t *order = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + oo);
     int64_t *base = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + bo);
-    hipLaunchKernelGGL(kda::plan_kernel, dim3(1), dim3(1024), 0, stream, cu, N, every, order, base);
+    hipLaunchKernelGGL(kda::plan_rank_kernel, dim3((N + kda::PLAN_RANK_THREADS - 1) / kda::PLAN_RANK_THREADS),
+                       dim3(kda::PLAN_RANK_THREADS), 0, stream, cu, N, order);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (every > 0) {
+        hipLaunchKernelGGL(kda::plan_kernel, dim3(1), dim3(1024), 0, stream, cu, N, every, base);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
 
     kda::ChunkParams p;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu_seqlens = cu; p.order = order;

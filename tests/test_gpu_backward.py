@@ -86,6 +86,15 @@ def test_backward_many_chains():
     check(w, do, dsf, label="37 seqs x 3 heads")
 
 
+def test_backward_more_sequences_than_one_plan_tile():
+    # 1500 sequences (lengths 0..70): the launch plan and the chunk bases span two tiles of 1024
+    rng = np.random.default_rng(62)
+    lens = [int(x) for x in rng.integers(0, 71, size=1500)]
+    w = W.make_prefill(lens, H=1, dk=64, dv=64, dtype="bf16", seed=62, s0_std=0.1)
+    do, dsf = W.make_cotangents(w, seed=62)
+    check(w, do, dsf, label="1500 sequences")
+
+
 @pytest.mark.parametrize("gate", ["min", "zero", "slow"])
 def test_backward_gate_extremes(gate):
     w = W.make_prefill([100, 64], H=2, dk=128, dv=128, dtype="bf16", seed=25, s0_std=0.1, gate=gate)

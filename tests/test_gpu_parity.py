@@ -114,6 +114,17 @@ def test_prefill_many_chains_one_workgroup_each(d, dtype):
     compare(w, label=f"many chains d={d} {dtype}", chunk=32)
 
 
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_prefill_more_sequences_than_one_plan_tile(chunk):
+    """3000 sequences (lengths 0..70, some empty): the launch plan ranks them over several
+    workgroups and LDS tiles of 1024 lengths, and the checkpoint bases are scanned over three
+    tiles of 1024; initial states, checkpoints every 64."""
+    rng = np.random.default_rng(61)
+    lens = [int(x) for x in rng.integers(0, 71, size=3000)]
+    w = W.make_prefill(lens, H=1, dk=64, dv=64, dtype="bf16", seed=61, s0_std=0.1, checkpoint_every=64)
+    compare(w, label="3000 sequences", chunk=chunk)
+
+
 @pytest.mark.parametrize("gate", ["min", "zero", "slow"])
 @pytest.mark.parametrize("chunk", CHUNKS)
 def test_prefill_gate_extremes(gate, chunk):
