@@ -206,8 +206,9 @@ kda_status kda_decode_step(const kda_decode_args *args, void *stream);
  *
  *     L = sum(d_o * o) + sum(d_final_state * final_state)
  *
- * of the forward over the same inputs (log-decay gates, no pool, no fused
- * prologue), write dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta and dL/dS_0.  Per token,
+ * of the forward over the same inputs (dense initial states, no pool; the fused
+ * prologue is optional, see gate_mode and normalize_qk below), write dL/dq,
+ * dL/dk, dL/dv, dL/dg, dL/dbeta and dL/dS_0.  Per token,
  * walking each sequence backwards with dS = dL/dS_t, the adjoint of the
  * recurrence is
  *     dS += scale q_t d_o_t^T;  dq_t = scale S_t d_o_t;  du = dS^T k_t;
