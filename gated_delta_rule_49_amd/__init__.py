@@ -183,9 +183,10 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
     (CUDA; -1 = zeros) picks each sequence's initial state from the pool (initial_state is then
     ignored), and checkpoint_indices int32 [M] (CUDA; -1 = not written) writes checkpoint m
     into pool slot checkpoint_indices[m] instead of returning a checkpoint tensor.
-    Fused prologue (chunk_size 32): gate_preactivation=True takes g as bf16 pre-activations a
-    and beta as fp32 pre-activations b (g = -5 sigmoid(a), beta = sigmoid(b)); normalize_qk=True
-    L2-normalises q and k per (token, head) inside the operator.
+    Prologue (bf16 inputs; fused into the kernel at chunk_size 32 and dk 128, a pass of its own
+    otherwise): gate_preactivation=True takes g as bf16 pre-activations a and beta as fp32
+    pre-activations b (g = -5 sigmoid(a), beta = sigmoid(b)); normalize_qk=True L2-normalises
+    q and k per (token, head) inside the operator.
     Returns (o [T,H,dv] fp32, final_state [N,H,dk,dv] fp32 or None, checkpoints or None).
     """
     T, H, dk = q.shape

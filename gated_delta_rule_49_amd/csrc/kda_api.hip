@@ -18,6 +18,9 @@ extern "C" hipError_t kda_launch_chunk(int chunk, int dk, int in_bf16, int N, in
                                        const float *s0, float *sf, int every, float *ckpt, float *o,
                                        float scale, const int32_t *s0_idx, const int32_t *ck_idx,
                                        int nslots, int flags, void *workspace, hipStream_t stream);
+extern "C" hipError_t kda_launch_prologue(int dk, long long rows, int flags, const void *q, const void *k,
+                                          const void *v, const float *a, const float *b, float *qn, float *kn,
+                                          float *vf, float *g, float *beta, hipStream_t stream);
 extern "C" size_t kda_bwd_workspace_layout(int N, int H, int T, int dk, int dv, int64_t n_ck, int64_t n_chunks,
                                            int flags, size_t *off);
 extern "C" hipError_t kda_launch_bwd(int dk, int in_bf16, int N, int H, int T, int64_t n_ck, int64_t n_chunks,
@@ -79,10 +82,33 @@ kda_status validate_fwd(const kda_fwd_args *a) {
     if ((a->gate_mode != KDA_GATE_LOG_DECAY && a->gate_mode != KDA_GATE_PREACTIVATION) ||
         (a->normalize_qk != 0 && a->normalize_qk != 1))
         return KDA_ERR_INVALID_ARGUMENT;
-    if ((a->gate_mode != KDA_GATE_LOG_DECAY || a->normalize_qk) &&
-        (a->chunk_size != 32 || a->in_dtype != KDA_BF16 || a->dk != 128))
-        return KDA_ERR_UNSUPPORTED;
+    if ((a->gate_mode != KDA_GATE_LOG_DECAY || a->normalize_qk) && a->in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
+}
+
+int fwd_flags(const kda_fwd_args *a) {
+    return (a->gate_mode == KDA_GATE_PREACTIVATION ? 1 : 0) | (a->normalize_qk ? 2 : 0);
+}
+
+// The forward's workspace: the launch plan, then, when the prologue cannot be fused (it is fused
+// for chunk 32 at dk = 128), its outputs: fp32 q / |q|, k / |k|, v (normalisation) and g, beta
+// (gate).  off[0..5]: qn, kn, vf, g, beta, end.
+size_t fwd_workspace(const kda_fwd_args *a, size_t *off) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const int flags = fwd_flags(a);
+    const bool mat = flags != 0 && !(a->chunk_size == 32 && a->dk == 128);
+    const size_t rows = (size_t)a->total_tokens * a->num_heads;
+    size_t o[6];
+    o[0] = up(kda_chunk_workspace_layout(a->num_seqs, nullptr, nullptr));
+    const bool nrm = mat && (flags & 2), gate = mat && (flags & 1);
+    o[1] = o[0] + (nrm ? up(rows * a->dk * 4) : 0);
+    o[2] = o[1] + (nrm ? up(rows * a->dk * 4) : 0);
+    o[3] = o[2] + (nrm ? up(rows * a->dv * 4) : 0);
+    o[4] = o[3] + (gate ? up(rows * a->dk * 4) : 0);
+    o[5] = o[4] + (gate ? up(rows * 4) : 0);
+    if (off)
+        for (int i = 0; i < 6; ++i) off[i] = o[i];
+    return mat ? o[5] : kda_chunk_workspace_layout(a->num_seqs, nullptr, nullptr);
 }
 
 // Validation of kda_chunk_bwd (and its workspace query); also counts the 32-token checkpoints
@@ -157,24 +183,40 @@ const char *kda_status_str(kda_status s) {
 
 size_t kda_chunk_fwd_workspace_bytes(const kda_fwd_args *a) {
     if (validate_fwd(a) != KDA_OK) return 0;
-    return kda_chunk_workspace_layout(a->num_seqs, nullptr, nullptr);
+    return fwd_workspace(a, nullptr);
 }
 
 kda_status kda_chunk_fwd(const kda_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
     const kda_status st = validate_fwd(a);
     if (st != KDA_OK) return st;
-    const size_t need = kda_chunk_workspace_layout(a->num_seqs, nullptr, nullptr);
+    size_t off[6];
+    const size_t need = fwd_workspace(a, off);
     if (a->num_seqs > 0) {
         if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_INVALID_ARGUMENT;
     }
     if (a->num_seqs == 0) return KDA_OK;
-    const hipError_t e = kda_launch_chunk(a->chunk_size, a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->q, a->k,
-                                          a->v, a->g, a->beta, a->cu_seqlens, a->initial_state, a->final_state,
-                                          a->checkpoint_every, a->checkpoints, a->o, a->scale,
-                                          a->initial_state_indices, a->checkpoint_indices, a->num_slots,
-                                          (a->gate_mode == KDA_GATE_PREACTIVATION ? 1 : 0) | (a->normalize_qk ? 2 : 0),
-                                          workspace, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int flags = fwd_flags(a), in_bf16 = a->in_dtype == KDA_BF16;
+    const void *q = a->q, *k = a->k, *v = a->v;
+    const float *g = a->g, *beta = a->beta;
+    if (flags != 0 && !(a->chunk_size == 32 && a->dk == 128)) {
+        // the prologue runs as its own pass; the kernels then see its outputs
+        char *ws = static_cast<char *>(workspace);
+        float *qn = reinterpret_cast<float *>(ws + off[0]), *kn = reinterpret_cast<float *>(ws + off[1]);
+        float *vf = reinterpret_cast<float *>(ws + off[2]), *gm = reinterpret_cast<float *>(ws + off[3]);
+        float *bm = reinterpret_cast<float *>(ws + off[4]);
+        if (kda_launch_prologue(a->dk, (long long)a->total_tokens * a->num_heads, flags, q, k, v, g, beta, qn, kn,
+                                vf, gm, bm, s) != hipSuccess)
+            return KDA_ERR_DEVICE;
+        if (flags & 2) { q = qn; k = kn; v = vf; in_bf16 = 0; }
+        if (flags & 1) { g = gm; beta = bm; }
+        flags = 0;
+    }
+    const hipError_t e = kda_launch_chunk(a->chunk_size, a->dk, in_bf16, a->num_seqs, a->num_heads, q, k, v, g, beta,
+                                          a->cu_seqlens, a->initial_state, a->final_state, a->checkpoint_every,
+                                          a->checkpoints, a->o, a->scale, a->initial_state_indices,
+                                          a->checkpoint_indices, a->num_slots, flags, workspace, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
 

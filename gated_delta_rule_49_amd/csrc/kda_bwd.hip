@@ -901,7 +901,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // With the normalisation the unit vectors stay fp32 (as in the forward's fused prologue), so the
 // rest of the backward runs on fp32 inputs and v is widened alongside.
 template <int DK>
-__global__ void __launch_bounds__(256) bwd_prologue_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+__global__ void __launch_bounds__(256) prologue_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                             const uint16_t *__restrict__ v, const uint16_t *__restrict__ a,
                                                             const float *__restrict__ b, long long rows, int flags,
                                                             float *__restrict__ qn, float *__restrict__ kn,
@@ -1022,6 +1022,27 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(
     const float *beta, const int32_t *cu, const float *s0, float *sf, int every, float *ckpt, float *o, float scale,
     const int32_t *s0_idx, const int32_t *ck_idx, int nslots, int flags, void *workspace, hipStream_t stream);
 
+// The fused prologue's outputs, materialised (one wave per (token, head) row; see prologue_kernel):
+// with KDA_PRO_NORM fp32 q / |q|, k / |k| and v into qn, kn, vf; with KDA_PRO_GATE fp32 g, beta.
+// q, k, v are bf16, a (in g's place) bf16 and b fp32, as the ABI's gate_mode defines them.
+extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_prologue(
+    int dk, long long rows, int flags, const void *q, const void *k, const void *v, const float *a, const float *b,
+    float *qn, float *kn, float *vf, float *g, float *beta, hipStream_t stream) {
+    if (rows <= 0 || flags == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((rows + 3) / 4);
+    const uint16_t *qr = static_cast<const uint16_t *>(q), *kr = static_cast<const uint16_t *>(k);
+    const uint16_t *vr = static_cast<const uint16_t *>(v), *ar = reinterpret_cast<const uint16_t *>(a);
+    if (dk == 128)
+        hipLaunchKernelGGL(kda::prologue_kernel<128>, dim3(blocks), dim3(256), 0, stream, qr, kr, vr, ar, b, rows,
+                           flags, qn, kn, vf, g, beta);
+    else if (dk == 64)
+        hipLaunchKernelGGL(kda::prologue_kernel<64>, dim3(blocks), dim3(256), 0, stream, qr, kr, vr, ar, b, rows,
+                           flags, qn, kn, vf, g, beta);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     int dk, int in_bf16, int N, int H, int T, int64_t n_ck, int64_t n_chunks, const void *q, const void *k,
     const void *v, const float *g, const float *beta, const int32_t *cu, const float *s0, const float *dO,
@@ -1044,16 +1065,8 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
         float *qn = reinterpret_cast<float *>(ws + off[6]), *kn = reinterpret_cast<float *>(ws + off[7]);
         float *vf = reinterpret_cast<float *>(ws + off[8]);
         float *gm = reinterpret_cast<float *>(ws + off[9]), *bm = reinterpret_cast<float *>(ws + off[10]);
-        const uint16_t *qr = static_cast<const uint16_t *>(q), *kr = static_cast<const uint16_t *>(k);
-        const uint16_t *vr = static_cast<const uint16_t *>(v);
-        const uint16_t *ar = reinterpret_cast<const uint16_t *>(g);
-        if (dk == 128)
-            hipLaunchKernelGGL(kda::bwd_prologue_kernel<128>, dim3(row_blocks), dim3(256), 0, stream, qr, kr, vr, ar,
-                               beta, rows, flags, qn, kn, vf, gm, bm);
-        else
-            hipLaunchKernelGGL(kda::bwd_prologue_kernel<64>, dim3(row_blocks), dim3(256), 0, stream, qr, kr, vr, ar,
-                               beta, rows, flags, qn, kn, vf, gm, bm);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = kda_launch_prologue(dk, rows, flags, q, k, v, g, beta, qn, kn, vf, gm, bm, stream)) != hipSuccess)
+            return e;
         if (flags & kda::KDA_PRO_NORM) { q = qn; k = kn; v = vf; in_bf16 = 0; }
         if (flags & kda::KDA_PRO_GATE) { g = gm; beta = bm; }
     }

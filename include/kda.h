@@ -125,8 +125,12 @@ typedef enum {
  *   normalize_qk     1: q and k are L2-normalised per (token, head) over dk inside the
  *                    operator (a zero vector stays zero); `scale` still applies.  0: used
  *                    as given.
- *                    Either prologue needs chunk_size 32, bf16 inputs and dk = 128 (else
- *                    KDA_ERR_UNSUPPORTED).
+ *                    Either prologue needs bf16 inputs (else KDA_ERR_UNSUPPORTED).  With
+ *                    chunk_size 32 and dk = 128 it is fused into the kernel's first stage;
+ *                    otherwise it runs as a pass of its own whose outputs the workspace
+ *                    holds (fp32 q / |q|, k / |k| and v with the normalisation, the rest
+ *                    of the forward then computing on fp32 inputs; fp32 g and beta with
+ *                    the gate), and kda_chunk_fwd_workspace_bytes includes them.
  */
 typedef struct {
     uint32_t struct_size;

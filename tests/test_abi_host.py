@@ -153,6 +153,33 @@ def test_workspace_checks(L):
     assert L.kda_chunk_fwd_workspace_bytes(ctypes.byref(b)) > need
 
 
+@pytest.mark.parametrize("field", ["gate_mode", "normalize_qk"])
+def test_fwd_prologue_needs_bf16(L, field):
+    a, keep = fwd_args(**{field: 1, "in_dtype": kda.KDA_F32})
+    assert status(L, a) == kda.KDA_ERR_UNSUPPORTED
+    assert L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_fwd_prologue_workspace(L):
+    """Fused into the kernel at chunk 32 and d_k = 128 (no extra workspace); at other shapes the
+    prologue's outputs are materialised: fp32 q_n, k_n, v with the normalisation, g, beta with
+    the gate."""
+    rows = 228 * 4
+    plain = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(fwd_args(chunk_size=32)[0]))
+    both = dict(gate_mode=kda.KDA_GATE_PREACTIVATION, normalize_qk=1)
+    assert L.kda_chunk_fwd_workspace_bytes(ctypes.byref(fwd_args(chunk_size=32, **both)[0])) == plain
+    for over in (dict(chunk_size=64), dict(chunk_size=32, dk=64, dv=64)):
+        d = over.get("dk", 128)
+        base = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(fwd_args(**over)[0]))
+        a, keep = fwd_args(**over, **both)
+        need = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a))
+        assert need >= base + rows * (3 * d * 4 + d * 4 + 4)
+        assert status(L, a, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+        g = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(fwd_args(**over, gate_mode=1)[0]))
+        n = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(fwd_args(**over, normalize_qk=1)[0]))
+        assert base < g < need and base < n < need
+
+
 def test_empty_batch_is_a_no_op(L):
     a, keep = fwd_args(cu=[0])
     a.num_seqs, a.total_tokens = 0, 0

@@ -293,14 +293,18 @@ def test_prefill_paged_pool(chunk):
 
 
 # ---- fused gate / normalisation prologue ---------------------------------------------------------
-@pytest.mark.parametrize("gate,norm", [(True, True), (True, False), (False, True)])
-def test_prefill_fused_prologue(gate, norm):
-    """chunk 32 with the gate (g = -5 sigmoid(a) from bf16 a, beta = sigmoid(b)) and/or the L2
-    normalisation of q, k fused into the first stage, against the oracle's prologue + recurrence.
-    Ragged sequences, initial states, checkpoints every 64."""
-    w = W.make_prefill_raw([200, 1, 0, 130, 333], H=3, dk=128, dv=128, seed=51, s0_std=0.1,
+@pytest.mark.parametrize("gate,norm,d,chunk", [(True, True, 128, 32), (True, False, 128, 32),
+                                              (False, True, 128, 32), (True, True, 64, 32),
+                                              (True, True, 128, 64), (True, False, 64, 64),
+                                              (False, True, 64, 64)])
+def test_prefill_fused_prologue(gate, norm, d, chunk):
+    """The gate (g = -5 sigmoid(a) from bf16 a, beta = sigmoid(b)) and/or the L2 normalisation
+    of q, k, against the oracle's prologue + recurrence: fused into the first stage at chunk 32
+    and d = 128, a pass of its own at the other shapes.  Ragged sequences, initial states,
+    checkpoints every 64."""
+    w = W.make_prefill_raw([200, 1, 0, 130, 333], H=3, dk=d, dv=d, seed=51, s0_std=0.1,
                            checkpoint_every=64)
-    scale = 128 ** -0.5
+    scale = d ** -0.5
     qn, kn, g64, b64 = oracle.prologue(w.q, w.k, w.g, w.beta, normalize=norm)
     if not norm:
         # unnormalised q, k would make the recurrence blow up: use unit rows (still bf16-exact)
@@ -316,10 +320,10 @@ def test_prefill_fused_prologue(gate, norm):
         g_ref, b_ref = g32, b32
     o, sf, ck = kda.kda_chunk_fwd(to_dev(q_in, torch.bfloat16), to_dev(k_in, torch.bfloat16),
                                   to_dev(w.v, torch.bfloat16), g_in, b_in, list(w.cu_seqlens), scale,
-                                  to_dev(w.s0, torch.float32), True, 64, chunk_size=32,
+                                  to_dev(w.s0, torch.float32), True, 64, chunk_size=chunk,
                                   gate_preactivation=gate, normalize_qk=norm)
     torch.cuda.synchronize()
     o_r, sf_r, ck_r = oracle.forward(qn, kn, w.v, g_ref, b_ref, w.cu_seqlens, scale, w.s0, checkpoint_every=64)
-    _log(f"fused prologue gate={gate} norm={norm}",
+    _log(f"fused prologue gate={gate} norm={norm} d={d} C={chunk}",
          {"o": W.rel_max_err(o.cpu().numpy(), o_r), "S": W.rel_max_err(sf.cpu().numpy(), sf_r),
           "ckpt": W.rel_max_err(ck.cpu().numpy(), ck_r)}, TOL["bf16"])
