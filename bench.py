@@ -241,6 +241,33 @@ def main():
         pms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pev]))
         res["decode"]["paged"] = {"ms": round(pms, 4), "GBps": round(dbytes / (pms * 1e-3) / 1e9, 1),
                                   "slots": "permutation of 256 pool slots"}
+        # and through the prologue: bf16 gate pre-activations a, fp32 b (device draws), q and k
+        # normalised inside; the g stream is 2 bytes per channel instead of 4
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(4)
+        a_pre = torch.randn(dg.shape, generator=gen, device=dev).to(torch.bfloat16)
+        b_pre = torch.randn(db.shape, generator=gen, device=dev)
+        Dq = kda.make_decode_args(dq, dk_, dvv, a_pre, b_pre, state, od, dkd ** -0.5, gate_preactivation=True,
+                                  normalize_qk=True)
+
+        def decode_prologue():
+            st = L.kda_decode_step(ctypes.byref(Dq), sptr)
+            if st != 0:
+                raise RuntimeError(kda.kda_status_str(st))
+
+        decode_prologue()
+        qev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            qev[i][0].record(stream)
+            decode_prologue()
+            qev[i][1].record(stream)
+        torch.cuda.synchronize()
+        qms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in qev]))
+        qbytes = dbytes - N * Hd * dkd * 2
+        res["decode"]["prologue"] = {"ms": round(qms, 4), "GBps": round(qbytes / (qms * 1e-3) / 1e9, 1),
+                                     "alg_bytes": qbytes,
+                                     "inputs": "bf16 gate pre-activations, fp32 beta pre-activations, "
+                                               "q and k normalised inside"}
 
     prof = measured_counters(args.chunk)
     if prof is not None:
@@ -448,14 +475,14 @@ def summarize_trace(trace_dir, bench_json):
                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} % |\n")
     out = {
         "chunk32_prefill_T65536_H96_d128_kernel_trace.md": (
-            "prefill T=65536 H=96 d_k=d_v=128 (bf16 q/k/v, fp32 g/beta/state, initial state)", "chunk32_kernel",
-            b["prefill"]["ms"]),
+            "prefill T=65536 H=96 d_k=d_v=128 (bf16 q/k/v, fp32 g/beta/state, initial state)",
+            "chunk32_kernel<128, 2, false, unsigned short, 0>", b["prefill"]["ms"]),
         "decode_N256_H96_d128_kernel_trace.md": (
-            "decode step N=256 H=96 d_k=d_v=128 (bf16 q/k/v, fp32 g/beta, fp32 state in place)", "decode_kernel",
-            b.get("decode", {}).get("ms")),
+            "decode step N=256 H=96 d_k=d_v=128 (bf16 q/k/v, fp32 g/beta, fp32 state in place)",
+            "decode_kernel<128, 128, unsigned short, 0>", b.get("decode", {}).get("ms")),
     }
     # per-dispatch durations, in launch order, to average over the timed launches only (the
-    # warm-up launches come first; the paged decode launches after the timed steps)
+    # warm-up launches come first; the paged and prologue decode launches after the timed steps)
     tpath = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     disp = []
     if tpath:

@@ -47,6 +47,7 @@ class KdaDecodeArgs(ctypes.Structure):
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("state", ctypes.c_void_p),
         ("state_indices", ctypes.c_void_p), ("o", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
+        ("gate_mode", ctypes.c_int32), ("normalize_qk", ctypes.c_int32),
     ]
 
 
@@ -291,7 +292,8 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_sta
     return dq, dkk, dvv, dg, db, ds0
 
 
-def make_decode_args(q, k, v, g, beta, state, o, scale, state_indices=None):
+def make_decode_args(q, k, v, g, beta, state, o, scale, state_indices=None, gate_preactivation=False,
+                     normalize_qk=False):
     N, H, dk = q.shape
     a = KdaDecodeArgs()
     a.struct_size = ctypes.sizeof(KdaDecodeArgs)
@@ -306,15 +308,19 @@ def make_decode_args(q, k, v, g, beta, state, o, scale, state_indices=None):
     a.state_indices = _ptr(state_indices)
     a.o = _ptr(o)
     a.num_slots = int(state.shape[0]) if state_indices is not None else 0
+    a.gate_mode = KDA_GATE_PREACTIVATION if gate_preactivation else KDA_GATE_LOG_DECAY
+    a.normalize_qk = 1 if normalize_qk else 0
     return a
 
 
-def kda_decode_step(q, k, v, g, beta, state, scale=1.0, out=None, stream=None, state_indices=None):
+def kda_decode_step(q, k, v, g, beta, state, scale=1.0, out=None, stream=None, state_indices=None,
+                    gate_preactivation=False, normalize_qk=False):
     """One decode token per sequence; `state` [N,H,dk,dv] fp32 is updated in place.  With
     state_indices (int32 [N], CUDA), `state` is a pool [P,H,dk,dv] and sequence n uses slot
-    state_indices[n] (-1: inactive, o = 0).  Returns o [N, H, dv] fp32."""
+    state_indices[n] (-1: inactive, o = 0).  gate_preactivation / normalize_qk: the prologue,
+    as in kda_chunk_fwd (bf16 inputs).  Returns o [N, H, dv] fp32."""
     N, H, dk = q.shape
     o = out if out is not None else torch.empty((N, H, v.shape[2]), dtype=torch.float32, device=q.device)
-    a = make_decode_args(q, k, v, g, beta, state, o, scale, state_indices)
+    a = make_decode_args(q, k, v, g, beta, state, o, scale, state_indices, gate_preactivation, normalize_qk)
     _check(lib().kda_decode_step(ctypes.byref(a), _stream(stream)))
     return o

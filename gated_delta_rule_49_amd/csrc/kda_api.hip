@@ -10,7 +10,7 @@
 
 extern "C" hipError_t kda_launch_decode(int dk, int in_bf16, int N, int H, const void *q, const void *k,
                                         const void *v, const float *g, const float *beta, float *state,
-                                        const int32_t *slots, int nslots, float *o, float scale,
+                                        const int32_t *slots, int nslots, float *o, float scale, int flags,
                                         hipStream_t stream);
 extern "C" size_t kda_chunk_workspace_layout(int N, size_t *order_off, size_t *base_off);
 extern "C" hipError_t kda_launch_chunk(int chunk, int dk, int in_bf16, int N, int H, const void *q, const void *k,
@@ -251,6 +251,10 @@ kda_status kda_decode_step(const kda_decode_args *a, void *stream) {
     if (d != KDA_OK) return d;
     if (a->state_indices && a->num_slots < 1) return KDA_ERR_INVALID_ARGUMENT;
     if (!(a->scale == a->scale)) return KDA_ERR_INVALID_ARGUMENT;
+    if ((a->gate_mode != KDA_GATE_LOG_DECAY && a->gate_mode != KDA_GATE_PREACTIVATION) ||
+        (a->normalize_qk != 0 && a->normalize_qk != 1))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if ((a->gate_mode != KDA_GATE_LOG_DECAY || a->normalize_qk) && a->in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (a->num_seqs == 0) return KDA_OK;
     if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->state || !a->o) return KDA_ERR_INVALID_ARGUMENT;
     if (!aligned16(a->state) || !aligned16(a->o) || !aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) ||
@@ -259,7 +263,9 @@ kda_status kda_decode_step(const kda_decode_args *a, void *stream) {
     if ((void *)a->o == (void *)a->state) return KDA_ERR_INVALID_ARGUMENT;
     const hipError_t e = kda_launch_decode(a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->q, a->k,
                                            a->v, a->g, a->beta, a->state, a->state_indices, a->num_slots, a->o,
-                                           a->scale, static_cast<hipStream_t>(stream));
+                                           a->scale,
+                                           (a->gate_mode == KDA_GATE_PREACTIVATION ? 1 : 0) | (a->normalize_qk ? 2 : 0),
+                                           static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
 

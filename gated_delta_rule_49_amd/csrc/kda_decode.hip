@@ -18,13 +18,17 @@
 // the current one, so every compute unit keeps reads in flight throughout.
 // Thread t owns 4 consecutive columns (float4) of every RG-th row: a wave's
 // loads cover whole rows and are fully coalesced.
+//
+// PRO (compile-time, KDA_PRO_* bits): the prologue of the skill card's quick facts,
+// g = -5 sigmoid(a) from bf16 pre-activations a in g's place and beta = sigmoid(b), and/or
+// q and k divided by their L2 norm over d_k (a zero vector stays zero).
 #include "kda_common.h"
 
 namespace kda {
 
 constexpr int DEC_THREADS = 1024;
 
-template <int DK, int DV, typename IN_T>
+template <int DK, int DV, typename IN_T, int PRO = 0>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_kernel(const IN_T *__restrict__ q, const IN_T *__restrict__ k, const IN_T *__restrict__ v,
               const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
@@ -76,9 +80,40 @@ decode_kernel(const IN_T *__restrict__ q, const IN_T *__restrict__ k, const IN_T
         }
 
         const size_t tok_k = (size_t)nh * DK, tok_v = (size_t)nh * DV;
+        float qi = 0.f, ki = 0.f, gi = 0.f;
         if (t < DK) {
-            const float al = __expf(g[tok_k + t]);
-            const float qi = load_in(q + tok_k + t), ki = load_in(k + tok_k + t);
+            qi = load_in(q + tok_k + t);
+            ki = load_in(k + tok_k + t);
+            if constexpr (PRO & KDA_PRO_GATE) {
+                const float ai = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(g)[tok_k + t]);
+                gi = -5.f * __builtin_amdgcn_rcpf(1.f + __expf(-ai));
+            } else {
+                gi = g[tok_k + t];
+            }
+        }
+        if constexpr ((PRO & KDA_PRO_NORM) != 0) {
+            // |q|^2 and |k|^2, formed by each of the first DK / 64 waves on its own (every lane
+            // reads DK / 64 elements of each, then a wave reduction): no workgroup barrier
+            if (t < DK) {
+                const int ln = t & 63;
+                float sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int m = 0; m < DK / 64; ++m) {
+                    const float x = load_in(q + tok_k + ln + 64 * m), y = load_in(k + tok_k + ln + 64 * m);
+                    sq += x * x;
+                    sk += y * y;
+                }
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) {
+                    sq += shfl_xor(sq, off);
+                    sk += shfl_xor(sk, off);
+                }
+                qi *= sq > 0.f ? rsqrtf(sq) : 0.f;
+                ki *= sk > 0.f ? rsqrtf(sk) : 0.f;
+            }
+        }
+        if (t < DK) {
+            const float al = __expf(gi);
             s_al[t] = al;
             s_aq[t] = al * qi;
             s_ak[t] = al * ki;
@@ -86,7 +121,8 @@ decode_kernel(const IN_T *__restrict__ q, const IN_T *__restrict__ k, const IN_T
             s_qk[t] = qi * ki;
         }
         if (t < DV) s_v[t] = load_in(v + tok_v + t);
-        const float b = beta[nh];
+        float b = beta[nh];
+        if constexpr (PRO & KDA_PRO_GATE) b = __builtin_amdgcn_rcpf(1.f + __expf(-b));
         __syncthreads();
 
         float a[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0}, qk = 0.f;
@@ -153,22 +189,35 @@ decode_kernel(const IN_T *__restrict__ q, const IN_T *__restrict__ k, const IN_T
 // Launcher used by the C ABI (kda_api.hip).  Returns a hipError_t.
 extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_decode(int dk, int in_bf16, int N, int H, const void *q, const void *k,
                                         const void *v, const float *g, const float *beta, float *state,
-                                        const int32_t *slots, int nslots, float *o, float scale,
+                                        const int32_t *slots, int nslots, float *o, float scale, int flags,
                                         hipStream_t stream) {
     if (N == 0 || H == 0) return hipSuccess;
     const long long nh = (long long)N * H;
     if (nh > 0x7fffffffLL) return hipErrorInvalidValue;
     // persistent: one workgroup per compute unit (or per state, if fewer)
     const int grid = (int)(nh < kda_cu_count() ? nh : kda_cu_count());
-#define KDA_DEC(DKV, T)                                                                                \
-    hipLaunchKernelGGL((kda::decode_kernel<DKV, DKV, T>), dim3(grid), dim3(kda::DEC_THREADS), 0, stream, \
-                       (const T *)q, (const T *)k, (const T *)v, g, beta, state, slots, slots ? nslots : N, o, \
+#define KDA_DEC(DKV, T, PRO)                                                                                   \
+    hipLaunchKernelGGL((kda::decode_kernel<DKV, DKV, T, PRO>), dim3(grid), dim3(kda::DEC_THREADS), 0, stream,   \
+                       (const T *)q, (const T *)k, (const T *)v, g, beta, state, slots, slots ? nslots : N, o,  \
                        H, (int)nh, scale)
-    if (dk == 128 && in_bf16) KDA_DEC(128, uint16_t);
-    else if (dk == 128) KDA_DEC(128, float);
-    else if (dk == 64 && in_bf16) KDA_DEC(64, uint16_t);
-    else if (dk == 64) KDA_DEC(64, float);
+#define KDA_DEC_PRO(DKV)                                                                                       \
+    do {                                                                                                       \
+        if (flags == 1) KDA_DEC(DKV, uint16_t, 1);                                                             \
+        else if (flags == 2) KDA_DEC(DKV, uint16_t, 2);                                                        \
+        else KDA_DEC(DKV, uint16_t, 3);                                                                        \
+    } while (0)
+    if (flags != 0) {
+        // the prologue: bf16 inputs
+        if (!in_bf16 || flags > 3) return hipErrorInvalidValue;
+        if (dk == 128) KDA_DEC_PRO(128);
+        else if (dk == 64) KDA_DEC_PRO(64);
+        else return hipErrorInvalidValue;
+    } else if (dk == 128 && in_bf16) KDA_DEC(128, uint16_t, 0);
+    else if (dk == 128) KDA_DEC(128, float, 0);
+    else if (dk == 64 && in_bf16) KDA_DEC(64, uint16_t, 0);
+    else if (dk == 64) KDA_DEC(64, float, 0);
     else return hipErrorInvalidValue;
+#undef KDA_DEC_PRO
 #undef KDA_DEC
     return hipGetLastError();
 }

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3u
+#define KDA_ABI_VERSION 4u
 
 typedef enum {
     KDA_OK = 0,
@@ -181,6 +181,10 @@ kda_status kda_chunk_fwd(const kda_fwd_args *args, void *workspace, size_t works
  *             its o is 0.  Active slots must be distinct.
  *   o       : fp32 [N, H, dv]
  *   num_slots >= 1 when state_indices is set; else ignored.
+ *   gate_mode, normalize_qk: the prologue, as in kda_fwd_args (g then holds the bf16
+ *             pre-activations a and beta the fp32 pre-activations b; q and k are
+ *             normalised over dk inside); either needs bf16 inputs (else
+ *             KDA_ERR_UNSUPPORTED).
  */
 typedef struct {
     uint32_t struct_size;
@@ -199,6 +203,8 @@ typedef struct {
     const int32_t *state_indices;
     float *o;
     int32_t num_slots;
+    int32_t gate_mode;
+    int32_t normalize_qk;
 } kda_decode_args;
 
 kda_status kda_decode_step(const kda_decode_args *args, void *stream);

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert kda.kda_abi_version() == 3
+    assert kda.kda_abi_version() == 4
     for code, name in enumerate(["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
                                  "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_DEVICE"]):
         assert kda.kda_status_str(code) == name
@@ -207,10 +207,18 @@ def decode_args(**over):
     ("state", FAKE + 8, kda.KDA_ERR_INVALID_ARGUMENT),
     ("o", FAKE * 6, kda.KDA_ERR_INVALID_ARGUMENT),          # aliases state
     ("num_heads", -1, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("gate_mode", 2, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("normalize_qk", -1, kda.KDA_ERR_INVALID_ARGUMENT),
 ])
 def test_decode_validation(L, field, value, expect):
     a = decode_args(**{field: value})
     assert L.kda_decode_step(ctypes.byref(a), None) == expect
+
+
+@pytest.mark.parametrize("field", ["gate_mode", "normalize_qk"])
+def test_decode_prologue_needs_bf16(L, field):
+    a = decode_args(**{field: 1, "in_dtype": kda.KDA_F32})
+    assert L.kda_decode_step(ctypes.byref(a), None) == kda.KDA_ERR_UNSUPPORTED
 
 
 def test_decode_empty_is_a_no_op(L):

@@ -87,6 +87,37 @@ def test_decode_small(d, dtype):
     assert eo <= 1e-4 and es <= 1e-4
 
 
+@pytest.mark.parametrize("gate,norm,d", [(True, True, 128), (True, False, 128), (False, True, 128),
+                                         (True, True, 64)])
+def test_decode_prologue(gate, norm, d):
+    """Decode with the gate (g = -5 sigmoid(a) from bf16 a, beta = sigmoid(b)) and/or the L2
+    normalisation of q and k inside, against the oracle's prologue + decode step; with the
+    normalisation one q row and one k row are zero (they stay zero)."""
+    N, H = 9, 3
+    w = W.make_prefill_raw([1] * N, H=H, dk=d, dv=d, seed=63, s0_std=0.1)
+    q, k = w.q.copy(), w.k.copy()
+    if norm:
+        q[2, 1] = 0.0
+        k[4, 0] = 0.0
+    else:
+        q = W.round_bf16((q / np.linalg.norm(q, axis=-1, keepdims=True)).astype(np.float32))
+        k = W.round_bf16((k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32))
+    qn, kn, g64, b64 = oracle.prologue(q, k, w.g, w.beta, normalize=norm)
+    if gate:
+        g_in, b_in, g_ref, b_ref = to_dev(w.g, torch.bfloat16), to_dev(w.beta, torch.float32), g64, b64
+    else:
+        g32, b32 = g64.astype(np.float32), b64.astype(np.float32)
+        g_in, b_in, g_ref, b_ref = to_dev(g32, torch.float32), to_dev(b32, torch.float32), g32, b32
+    state = to_dev(w.s0, torch.float32).clone()
+    scale = d ** -0.5
+    o = kda.kda_decode_step(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(w.v, torch.bfloat16),
+                            g_in, b_in, state, scale, gate_preactivation=gate, normalize_qk=norm)
+    torch.cuda.synchronize()
+    o_r, s_r = oracle.decode(qn, kn, w.v, g_ref, b_ref, w.s0, scale)
+    _log(f"decode prologue gate={gate} norm={norm} d={d}",
+         {"o": W.rel_max_err(o.cpu().numpy(), o_r), "S": W.rel_max_err(state.cpu().numpy(), s_r)}, 1e-4)
+
+
 # ---- prefill: small shapes and edge cases ------------------------------------------------------
 @pytest.mark.parametrize("chunk", CHUNKS)
 def test_prefill_config0_tiny_f32(chunk):
