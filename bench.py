@@ -722,6 +722,21 @@ def backward_workload(steps, warmup, fused=False):
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
     med = float(np.median(ms))
+    # the same backward reading the forward's states at every 32-token boundary (a forward run
+    # with checkpoint_every = 32, untimed) instead of recomputing them
+    _, _, states = kda.kda_chunk_fwd(q, k, v, g, beta, cu, scale, s0, False, 32, chunk_size=32,
+                                     gate_preactivation=fused, normalize_qk=fused)
+    ms_s = []
+    for _ in range(max(1, steps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kda.kda_chunk_bwd(q, k, v, g, beta, do, cu, scale, s0, dsf, workspace=ws, gate_preactivation=fused,
+                          normalize_qk=fused, states=states)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_s.append(e0.elapsed_time(e1))
+    med_s = float(np.median(ms_s))
+    del states
     nbytes = bwd_alg_bytes(T, H, dk, dv, 1, fused)
     what = ("raw bf16 q/k/v, bf16 gate pre-activations a, fp32 b, gradients through the fused gate and "
             "q/k normalisation" if fused else "bf16 q/k/v, fp32 g/beta")
@@ -732,7 +747,10 @@ def backward_workload(steps, warmup, fused=False):
         "ms_p10": round(float(np.percentile(ms, 10)), 4), "ms_p90": round(float(np.percentile(ms, 90)), 4),
         "alg_bytes": int(nbytes), "alg_GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "workspace_GB": round(ws.numel() / 1e9, 2), "data": "synthetic (seeded)"}), flush=True)
+        "workspace_GB": round(ws.numel() / 1e9, 2),
+        "with_forward_states": {"ms": round(med_s, 4), "tokens_per_s": round(T / (med_s * 1e-3), 1),
+                                "note": "the forward's checkpoints every 32 tokens passed in, not recomputed"},
+        "data": "synthetic (seeded)"}), flush=True)
 
 
 def _bwd_ws_bytes(kda, q, k, v, g, beta, do, cu, s0, dsf, out, fused=False):

@@ -62,7 +62,7 @@ class KdaBwdArgs(ctypes.Structure):
         ("initial_state", ctypes.c_void_p), ("d_o", ctypes.c_void_p), ("d_final_state", ctypes.c_void_p),
         ("dq", ctypes.c_void_p), ("dk_out", ctypes.c_void_p), ("dv_out", ctypes.c_void_p),
         ("dg", ctypes.c_void_p), ("dbeta", ctypes.c_void_p), ("d_initial_state", ctypes.c_void_p),
-        ("gate_mode", ctypes.c_int32), ("normalize_qk", ctypes.c_int32),
+        ("gate_mode", ctypes.c_int32), ("normalize_qk", ctypes.c_int32), ("states", ctypes.c_void_p),
     ]
 
 
@@ -233,7 +233,7 @@ def _cu_host(cu_seqlens, T):
 
 
 def make_bwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, d_o, d_final_state, dq, dk, dv, dg,
-                  dbeta, d_initial_state, gate_preactivation=False, normalize_qk=False):
+                  dbeta, d_initial_state, gate_preactivation=False, normalize_qk=False, states=None):
     T, H, dk_ = q.shape
     a = KdaBwdArgs()
     a.struct_size = ctypes.sizeof(KdaBwdArgs)
@@ -254,20 +254,22 @@ def make_bwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, d_o, 
     a.d_initial_state = _ptr(d_initial_state)
     a.gate_mode = KDA_GATE_PREACTIVATION if gate_preactivation else KDA_GATE_LOG_DECAY
     a.normalize_qk = 1 if normalize_qk else 0
+    a.states = _ptr(states)
     return a
 
 
 def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_state=None, d_final_state=None,
                   output_d_initial_state=True, stream=None, workspace=None, gate_preactivation=False,
-                  normalize_qk=False):
+                  normalize_qk=False, states=None):
     """Backward of kda_chunk_fwd: gradients of L = sum(d_o * o) + sum(d_final_state * final_state).
 
     Inputs as for kda_chunk_fwd (with gate_preactivation / normalize_qk as there: g, beta are then
     the gate pre-activations and q, k the raw vectors, and the returned dg, dbeta, dq, dk are the
     gradients with respect to those); d_o: fp32 [T, H, dv]; d_final_state: fp32 [N, H, dk, dv] or
     None (zeros).  workspace: optional uint8 CUDA tensor of at least the queried size (reused by
-    callers that run the backward repeatedly).  Returns (dq, dk, dv, dg, dbeta, d_initial_state or
-    None), all fp32."""
+    callers that run the backward repeatedly).  states: the forward's checkpoints with
+    checkpoint_every=32 (fp32 [sum floor(L/32), H, dk, dv]) to read instead of recomputing them, or
+    None.  Returns (dq, dk, dv, dg, dbeta, d_initial_state or None), all fp32."""
     T, H, dk = q.shape
     dv = v.shape[2]
     dev = q.device
@@ -280,7 +282,7 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_sta
     db = torch.empty((T, H), **f32)
     ds0 = torch.empty((N, H, dk, dv), **f32) if output_d_initial_state else None
     a = make_bwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, d_o, d_final_state, dq, dkk, dvv,
-                      dg, db, ds0, gate_preactivation, normalize_qk)
+                      dg, db, ds0, gate_preactivation, normalize_qk, states)
     L = lib()
     ws_bytes = int(L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a)))
     if ws_bytes == 0 and N > 0:

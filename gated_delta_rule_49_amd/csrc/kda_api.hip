@@ -27,7 +27,7 @@ extern "C" hipError_t kda_launch_bwd(int dk, int in_bf16, int N, int H, int T, i
                                      const void *q, const void *k, const void *v, const float *g, const float *beta,
                                      const int32_t *cu, const float *s0, const float *dO, const float *dSf, float *dq,
                                      float *dkk, float *dv, float *dg, float *dbeta, float *dS0, float scale,
-                                     int flags, void *workspace, hipStream_t stream);
+                                     const float *states, int flags, void *workspace, hipStream_t stream);
 
 namespace {
 
@@ -131,7 +131,7 @@ kda_status validate_bwd(const kda_bwd_args *a, int64_t *n_ck, int64_t *n_chunks)
         ch += (cu[n + 1] - cu[n] + 31) / 32;
     }
     if (cu[a->num_seqs] != a->total_tokens) return KDA_ERR_INVALID_ARGUMENT;
-    const void *in[] = {a->q, a->k, a->v, a->g, a->beta, a->d_o, a->initial_state, a->d_final_state};
+    const void *in[] = {a->q, a->k, a->v, a->g, a->beta, a->d_o, a->initial_state, a->d_final_state, a->states};
     const void *out[] = {a->dq, a->dk_out, a->dv_out, a->dg, a->dbeta, a->d_initial_state};
     if (a->total_tokens > 0) {
         for (int i = 0; i < 6; ++i)
@@ -140,12 +140,12 @@ kda_status validate_bwd(const kda_bwd_args *a, int64_t *n_ck, int64_t *n_chunks)
             if (!out[i] || !aligned16(out[i])) return KDA_ERR_INVALID_ARGUMENT;
     }
     if ((a->initial_state && !aligned16(a->initial_state)) || (a->d_final_state && !aligned16(a->d_final_state)) ||
-        (a->d_initial_state && !aligned16(a->d_initial_state)))
+        (a->d_initial_state && !aligned16(a->d_initial_state)) || (a->states && !aligned16(a->states)))
         return KDA_ERR_INVALID_ARGUMENT;
     // no output may alias another output or an input
     for (int i = 0; i < 6; ++i) {
         if (!out[i]) continue;
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 9; ++j)
             if (out[i] == in[j]) return KDA_ERR_INVALID_ARGUMENT;
         for (int j = i + 1; j < 6; ++j)
             if (out[i] == out[j]) return KDA_ERR_INVALID_ARGUMENT;
@@ -160,8 +160,9 @@ kda_status validate_bwd(const kda_bwd_args *a, int64_t *n_ck, int64_t *n_chunks)
     return KDA_OK;
 }
 
+// prologue bits, and 8 when the caller passes the states (the workspace then holds none)
 int bwd_flags(const kda_bwd_args *a) {
-    return (a->gate_mode == KDA_GATE_PREACTIVATION ? 1 : 0) | (a->normalize_qk ? 2 : 0);
+    return (a->gate_mode == KDA_GATE_PREACTIVATION ? 1 : 0) | (a->normalize_qk ? 2 : 0) | (a->states ? 8 : 0);
 }
 
 }  // namespace
@@ -239,7 +240,7 @@ kda_status kda_chunk_bwd(const kda_bwd_args *a, void *workspace, size_t workspac
     const hipError_t e = kda_launch_bwd(a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->total_tokens,
                                         ck, ch, a->q, a->k, a->v, a->g, a->beta, a->cu_seqlens, a->initial_state,
                                         a->d_o, a->d_final_state, a->dq, a->dk_out, a->dv_out, a->dg, a->dbeta,
-                                        a->d_initial_state, a->scale, bwd_flags(a), workspace,
+                                        a->d_initial_state, a->scale, a->states, bwd_flags(a) & 3, workspace,
                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }

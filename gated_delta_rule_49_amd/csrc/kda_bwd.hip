@@ -1001,7 +1001,8 @@ extern "C" __attribute__((visibility("hidden"))) size_t kda_bwd_workspace_layout
     size_t o[12];
     o[0] = up(kda_chunk_workspace_layout(N, nullptr, nullptr));           // cbase
     o[1] = o[0] + up((size_t)(N + 1) * 4);                                 // checkpoints
-    o[2] = o[1] + up((size_t)n_ck * H * dk * dv * 4);                       // (no region)
+    const bool given = flags & kda::KDA_BWD_STATES_GIVEN;
+    o[2] = o[1] + (given ? 0 : up((size_t)n_ck * H * dk * dv * 4));         // (no region)
     o[3] = o[2];                                                            // D
     o[4] = o[3] + up((size_t)n_chunks * H * dk * dv * 4);                   // scan operands
     o[5] = o[4] + up((size_t)n_chunks * H * rec * 4);                       // A, T
@@ -1021,6 +1022,8 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(
     int chunk, int dk, int in_bf16, int N, int H, const void *q, const void *k, const void *v, const float *g,
     const float *beta, const int32_t *cu, const float *s0, float *sf, int every, float *ckpt, float *o, float scale,
     const int32_t *s0_idx, const int32_t *ck_idx, int nslots, int flags, void *workspace, hipStream_t stream);
+extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_plan(int N, const int32_t *cu, int every,
+                                                                           void *workspace, hipStream_t stream);
 
 // The fused prologue's outputs, materialised (one wave per (token, head) row; see prologue_kernel):
 // with KDA_PRO_NORM fp32 q / |q|, k / |k| and v into qn, kn, vf; with KDA_PRO_GATE fp32 g, beta.
@@ -1047,10 +1050,13 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     int dk, int in_bf16, int N, int H, int T, int64_t n_ck, int64_t n_chunks, const void *q, const void *k,
     const void *v, const float *g, const float *beta, const int32_t *cu, const float *s0, const float *dO,
     const float *dSf, float *dq, float *dkk, float *dv, float *dg, float *dbeta, float *dS0, float scale,
-    int flags, void *workspace, hipStream_t stream) {
+    const float *states, int flags, void *workspace, hipStream_t stream) {
     if (N == 0) return hipSuccess;
+    if (states) flags |= kda::KDA_BWD_STATES_GIVEN;
+    const int given = flags & kda::KDA_BWD_STATES_GIVEN;
+    flags &= kda::KDA_PRO_GATE | kda::KDA_PRO_NORM;   // the prologue bits from here on
     size_t off[12];
-    kda_bwd_workspace_layout(N, H, T, dk, dk, n_ck, n_chunks, flags, off);
+    kda_bwd_workspace_layout(N, H, T, dk, dk, n_ck, n_chunks, flags | given, off);
     char *ws = static_cast<char *>(workspace);
     hipError_t e;
     // fused prologue: the operator's inputs, materialised (fp32 q_n, k_n, v; fp32 g, beta) for
@@ -1073,11 +1079,16 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     // states at every 32-token boundary, without the outputs (the forward's plan lands at the start
     // of the workspace); the forward's fused prologue exists for d = 128, at d = 64 the recompute
     // reads the materialised inputs
+    // (given by the caller instead: the launch plan alone)
     const bool fused_fwd = flags && dk == 128;
-    e = kda_launch_chunk(32, dk, fused_fwd ? raw_bf16 : in_bf16, N, H, fused_fwd ? q_raw : q, fused_fwd ? k_raw : k,
-                         fused_fwd ? v_raw : v, fused_fwd ? a_raw : g, fused_fwd ? b_raw : beta, cu, s0, nullptr,
-                         kda::BC, reinterpret_cast<float *>(ws + off[1]), nullptr, scale, nullptr, nullptr, 0,
-                         (fused_fwd ? flags : 0) | kda::KDA_STATES_ONLY, ws, stream);
+    if (given)
+        e = kda_launch_plan(N, cu, kda::BC, ws, stream);
+    else
+        e = kda_launch_chunk(32, dk, fused_fwd ? raw_bf16 : in_bf16, N, H, fused_fwd ? q_raw : q,
+                             fused_fwd ? k_raw : k, fused_fwd ? v_raw : v, fused_fwd ? a_raw : g,
+                             fused_fwd ? b_raw : beta, cu, s0, nullptr, kda::BC,
+                             reinterpret_cast<float *>(ws + off[1]), nullptr, scale, nullptr, nullptr, 0,
+                             (fused_fwd ? flags : 0) | kda::KDA_STATES_ONLY, ws, stream);
     if (e != hipSuccess) return e;
     size_t order_off, base_off;
     kda_chunk_workspace_layout(N, &order_off, &base_off);
@@ -1086,7 +1097,7 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     p.order = reinterpret_cast<const int32_t *>(ws + order_off);
     p.ck_base = reinterpret_cast<const int64_t *>(ws + base_off);
     p.cbase = reinterpret_cast<const int32_t *>(ws + off[0]);
-    p.ckpt = reinterpret_cast<const float *>(ws + off[1]);
+    p.ckpt = given ? states : reinterpret_cast<const float *>(ws + off[1]);
     p.s0 = s0; p.dO = dO; p.dSf = dSf;
     p.Dck = reinterpret_cast<float *>(ws + off[3]);
     p.SCk = reinterpret_cast<float *>(ws + off[4]);

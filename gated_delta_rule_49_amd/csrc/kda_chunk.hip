@@ -532,6 +532,23 @@ extern "C" __attribute__((visibility("hidden"))) size_t kda_chunk_workspace_layo
 extern "C" __attribute__((visibility("hidden"))) hipError_t
 kda_launch_chunk32(int dk, int in_bf16, unsigned grid, const kda::ChunkParams &p, hipStream_t stream);
 
+// The launch plan alone (sequence order, per-sequence checkpoint bases for `every`) into the
+// start of `workspace`, as kda_launch_chunk lays it out.
+extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_plan(int N, const int32_t *cu, int every,
+                                                                           void *workspace, hipStream_t stream) {
+    if (N == 0) return hipSuccess;
+    size_t oo, bo;
+    kda_chunk_workspace_layout(N, &oo, &bo);
+    int32_t *order = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + oo);
+    int64_t *base = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + bo);
+    hipLaunchKernelGGL(kda::plan_rank_kernel, dim3((N + kda::PLAN_RANK_THREADS - 1) / kda::PLAN_RANK_THREADS),
+                       dim3(kda::PLAN_RANK_THREADS), 0, stream, cu, N, order);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || every <= 0) return err;
+    hipLaunchKernelGGL(kda::plan_kernel, dim3(1), dim3(1024), 0, stream, cu, N, every, base);
+    return hipGetLastError();
+}
+
 extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int chunk, int dk, int in_bf16, int N, int H,
                                        const void *q, const void *k,
                                        const void *v, const float *g, const float *beta, const int32_t *cu,
@@ -542,16 +559,10 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int
     if (flags != 0 && chunk != 32) return hipErrorInvalidValue;   // fused prologue: chunk 32 only
     size_t oo, bo;
     kda_chunk_workspace_layout(N, &oo, &bo);
-    int32_t *order = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + oo);
-    int64_t *base = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + bo);
-    hipLaunchKernelGGL(kda::plan_rank_kernel, dim3((N + kda::PLAN_RANK_THREADS - 1) / kda::PLAN_RANK_THREADS),
-                       dim3(kda::PLAN_RANK_THREADS), 0, stream, cu, N, order);
-    hipError_t err = hipGetLastError();
+    const int32_t *order = reinterpret_cast<const int32_t *>(static_cast<char *>(workspace) + oo);
+    const int64_t *base = reinterpret_cast<const int64_t *>(static_cast<char *>(workspace) + bo);
+    hipError_t err = kda_launch_plan(N, cu, every, workspace, stream);
     if (err != hipSuccess) return err;
-    if (every > 0) {
-        hipLaunchKernelGGL(kda::plan_kernel, dim3(1), dim3(1024), 0, stream, cu, N, every, base);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
 
     kda::ChunkParams p;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu_seqlens = cu; p.order = order;

@@ -75,6 +75,9 @@ constexpr int KDA_PRO_NORM = 2;   // q and k are L2-normalised per (token, head)
 // Internal (the backward's recompute of the chunk-start states): o is neither formed nor written,
 // and q is not read.
 constexpr int KDA_STATES_ONLY = 4;
+// Internal (the backward's workspace and launch): the caller passes the states at every
+// 32-token boundary, so they are neither recomputed nor held in the workspace.
+constexpr int KDA_BWD_STATES_GIVEN = 8;
 
 // ---- MFMA ------------------------------------------------------------------
 // 16x16 output tiles: lane l holds D[4*(l/16) + e][l % 16], e = 0..3.

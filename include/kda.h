@@ -243,6 +243,11 @@ kda_status kda_decode_step(const kda_decode_args *args, void *stream);
  *                    pre-activations a (raw 16-bit words) and beta the fp32 pre-activations
  *                    b; dg and dbeta are then dL/da and dL/db (through g = -5 sigmoid(a),
  *                    beta = sigmoid(b)).
+ *   states           NULL: the states at every 32-token boundary are recomputed (into the
+ *                    workspace).  Else fp32 [sum_n floor(L_n / 32), H, dk, dv]: exactly the
+ *                    checkpoints kda_chunk_fwd writes for the same inputs and prologue with
+ *                    checkpoint_every = 32, read instead of recomputed (the workspace is then
+ *                    smaller by their size).  16-byte aligned; no output may alias it.
  *   normalize_qk     as in kda_fwd_args: 1 normalises q and k inside; dq and dk are then
  *                    the gradients with respect to the raw q and k (zero for a zero row).
  *                    Either prologue needs bf16 inputs (else KDA_ERR_UNSUPPORTED); unlike
@@ -283,6 +288,7 @@ typedef struct {
     float *d_initial_state;
     int32_t gate_mode;
     int32_t normalize_qk;
+    const float *states;
 } kda_bwd_args;
 
 /* Device workspace (bytes) that kda_chunk_bwd needs for `args` (host only).

@@ -274,6 +274,8 @@ def bwd_status(L, a, ws=FAKE * 64, ws_bytes=1 << 40):
     ("scale", float("nan"), kda.KDA_ERR_INVALID_ARGUMENT),
     ("gate_mode", 5, kda.KDA_ERR_INVALID_ARGUMENT),
     ("normalize_qk", 2, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("states", FAKE * 40 + 8, kda.KDA_ERR_INVALID_ARGUMENT),   # misaligned
+    ("states", FAKE * 21, kda.KDA_ERR_INVALID_ARGUMENT),       # aliases dk_out
 ])
 def test_bwd_validation(L, field, value, expect):
     a, keep = bwd_args(**{field: value})
@@ -301,6 +303,16 @@ def test_bwd_prologue_workspace(L):
     n, keep3 = bwd_args(normalize_qk=1)
     assert base < L.kda_chunk_bwd_workspace_bytes(ctypes.byref(g)) < need
     assert base < L.kda_chunk_bwd_workspace_bytes(ctypes.byref(n)) < need
+
+
+def test_bwd_given_states_workspace(L):
+    # states passed in (the forward's checkpoints every 32 tokens): the workspace holds none
+    base = L.kda_chunk_bwd_workspace_bytes(ctypes.byref(bwd_args()[0]))
+    a, keep = bwd_args(states=FAKE * 40)
+    need = L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a))
+    n_ck = 100 // 32 + 128 // 32
+    assert need <= base - n_ck * 4 * 128 * 128 * 4
+    assert bwd_status(L, a, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_bwd_workspace(L):

@@ -113,6 +113,37 @@ def test_backward_empty_sequences(lens):
             assert np.array_equal(got[5][n], dsf[n])
 
 
+@pytest.mark.parametrize("pro", [False, True])
+def test_backward_from_the_forwards_states(pro):
+    """The forward run with checkpoint_every = 32, its checkpoints passed to the backward instead
+    of being recomputed: the same gradients as the recomputing backward (d = 128 bf16, ragged
+    sequences, S0 and dS_T; with and without the fused prologue)."""
+    lens = [200, 1, 0, 64, 95]
+    if pro:
+        w = W.make_prefill_raw(lens, H=3, dk=128, dv=128, seed=64, s0_std=0.1)
+        g_in = to_dev(w.g, torch.bfloat16)
+        scale = 128 ** -0.5
+    else:
+        w = W.make_prefill(lens, H=3, dk=128, dv=128, dtype="bf16", seed=64, s0_std=0.1)
+        g_in = to_dev(w.g, torch.float32)
+        scale = 1.0
+    do, dsf = W.make_cotangents(w, seed=64)
+    q, k, v = (to_dev(x, torch.bfloat16) for x in (w.q, w.k, w.v))
+    b, s0 = to_dev(w.beta, torch.float32), to_dev(w.s0, torch.float32)
+    kw = dict(gate_preactivation=pro, normalize_qk=pro)
+    _, _, ck = kda.kda_chunk_fwd(q, k, v, g_in, b, list(w.cu_seqlens), scale, s0, True, 32, chunk_size=32, **kw)
+    assert ck.shape[0] == sum(L // 32 for L in lens)
+    args = (q, k, v, g_in, b, to_dev(do, torch.float32), list(w.cu_seqlens), scale, s0, to_dev(dsf, torch.float32))
+    ref = kda.kda_chunk_bwd(*args, **kw)
+    got = kda.kda_chunk_bwd(*args, states=ck, **kw)
+    torch.cuda.synchronize()
+    errs = {n: W.rel_max_err(x.cpu().numpy(), y.cpu().numpy()) for n, x, y in zip(NAMES, got, ref)}
+    print(f"[bwd parity] given states (prologue={pro}) vs recomputed: "
+          + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    for k_, v_ in errs.items():
+        assert v_ <= 1e-6, (k_, v_)
+
+
 def test_backward_deterministic():
     w = W.make_prefill([150, 77], H=4, dk=128, dv=128, dtype="bf16", seed=26, s0_std=0.1)
     do, dsf = W.make_cotangents(w, seed=26)
