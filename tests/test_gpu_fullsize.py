@@ -80,6 +80,20 @@ def test_config2_prefill_T65536_H96_sampled_heads():
 
 
 @pytest.mark.timeout(900)
+def test_prefill_one_million_tokens_two_heads():
+    """A 1,048,576-token context (the longest the pages speak of), two heads, bf16, initial state,
+    checkpoints every 65536: every output, the final states and the checkpoints against the
+    fp64 oracle over the whole chain (32,768 chunks through the recurrence)."""
+    w = W.make_prefill([1 << 20], H=2, dk=128, dv=128, dtype="bf16", seed=71, s0_std=0.1,
+                       checkpoint_every=1 << 16)
+    o, sf, ck = _run_whole(w)
+    torch.cuda.synchronize()
+    o_r, s_r, ck_r = oracle.forward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, 1.0, w.s0, 1 << 16)
+    _report("T=1048576 H=2", {"o": W.rel_max_err(o.cpu().numpy(), o_r), "S": W.rel_max_err(sf.cpu().numpy(), s_r),
+                              "ckpt": W.rel_max_err(ck.cpu().numpy(), ck_r)})
+
+
+@pytest.mark.timeout(900)
 def test_config2_backward_T65536_H96_sampled_head_and_identity():
     """The backward at the benchmark's shape: every gradient finite; one whole head (65,536 tokens)
     against the fp64 oracle adjoint; and over all 96 heads the identity that holds because o and S_T
