@@ -419,7 +419,9 @@ def summarize_backward_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, mf
     cf = _mean(_counter_rows(cfetch_dir, "elementwise_kernel")[-3:], "FETCH_SIZE")
     cw = _mean(_counter_rows(cwrite_dir, "elementwise_kernel")[-3:], "WRITE_SIZE")
     fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
-    kernels = [("chunk32_kernel<128, 2, false", "forward recompute (checkpoint every 32)"),
+    # (the recompute is the states-only variant of the chunk kernel, flag 4; the run's other
+    # chunk32 launch is the forward that provides the states for the second timing)
+    kernels = [("chunk32_kernel<128, 2, false, unsigned short, 4", "forward recompute (checkpoint every 32)"),
                ("bwd_prep_kernel<128", "prep"), ("bwd_dstate_kernel<128", "state-gradient scan"),
                ("bwd_grad_kernel<128", "gradients")]
     xcd, simds = 8, 1024
@@ -435,7 +437,8 @@ def summarize_backward_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, mf
     with open(os.path.join(ROOT, "profiles", "backward_T65536_H96_d128_counters.md"), "w") as f:
         f.write("# Backward (kda_chunk_bwd): HBM traffic and MFMA counters\n\n")
         f.write("Workload: backward of the prefill T=65536 H=96 d_k=d_v=128, bf16 q/k/v, fp32 g/beta, initial "
-                "state, d_o and dS_T (one `bench.py --backward` call).\n\n")
+                "state, d_o and dS_T (one `bench.py --backward` call).  Per dispatch: prep, scan and gradient "
+                "kernels also run once more reading the forward's states, with the same work.\n\n")
         f.write(f"HBM bytes = counter x scale, scales from a plain copy of {copy_bytes} B read + written: "
                 f"fetch {fs:.4f}, write {ws:.4f}.  MFMA busy over all 1024 SIMDs (fp32 MFMA, and bf16 hi+lo "
                 "products in the gradient kernel and the forward recompute).\n\n")
@@ -511,8 +514,16 @@ def summarize_backward_trace(trace_dir, bench_log):
     import csv
     import glob
     path = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    # the backward's kernels: its own, the launch plan and the states-only recompute (flags >= 4);
+    # the run's plain forward (which provides the states for the second timing) is left out
+    def ours(name):
+        if "kda" not in name:
+            return False
+        if "chunk32_kernel" in name:
+            return int(name.split(">")[0].split(",")[-1]) >= 4
+        return True
     with open(path) as f:
-        rows = [r for r in csv.DictReader(f) if "kda" in r["Name"]]
+        rows = [r for r in csv.DictReader(f) if ours(r["Name"])]
     with open(bench_log) as f:
         b = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
     fused = "fused" in b["workload"]
@@ -523,7 +534,8 @@ def summarize_backward_trace(trace_dir, bench_log):
                 + "): rocprofv3 kernel trace\n\n")
         f.write(f"Workload: {b['workload']}.\n\n")
         f.write(f"bench.py HIP-event median of one backward (same process): {b['ms']} ms "
-                f"({b['value']:.0f} tokens/s); sum of the per-kernel rocprof averages below: {total:.3f} ms.\n\n")
+                f"({b['value']:.0f} tokens/s); sum of the per-kernel rocprof averages below: {total:.3f} ms (prep, scan and gradient kernels "
+                "averaged over both timings, recomputing and reading the forward's states: the same work).\n\n")
         f.write("Command:\n\n    rocprofv3 --kernel-trace --stats -d " + trace_dir + " -o run --output-format csv "
                 "-- python -u bench.py --backward " + ("--prologue " if fused else "") + "--steps 5 --warmup 1\n\n")
         f.write("| kernel | calls | average (ms) | min (ms) | max (ms) |\n|---|---|---|---|---|\n")
