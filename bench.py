@@ -5,7 +5,7 @@ One step = one chunked prefill of the long-context workload (T=65536 tokens,
 H=96 heads, d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state, initial state) plus one
 decode step of the decode workload (256 sequences x 96 heads, fp32 state
 [256,96,128,128] updated in place).  Inputs are seeded synthetic data
-(workloads.make_config) resident in HBM before the timed region.
+(workloads.make_workload) resident in HBM before the timed region.
 
 Prints ONE JSON line: value = prefill tokens/s; decode GB/s and the roofline
 of the dominant kernel are reported beside it; cpu_baseline times the fp64 CPU
@@ -113,8 +113,8 @@ def main():
 
     dev = torch.device("cuda:0")
     t_gen = time.time()
-    wp = W.make_config(2)
-    wd = W.make_config(3)
+    wp = W.make_workload(2)
+    wd = W.make_workload(3)
     gen_s = time.time() - t_gen
 
     def up(x, dt):
@@ -199,7 +199,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; workloads.make_config 2 and 3)",
+        "data": "synthetic (seeded; workloads.make_workload 2 and 3)",
         "config": {"workload": "prefill T=65536 H=96 d_k=d_v=128 bf16 q/k/v, fp32 g/beta/state, initial state; "
                                "+ decode N=256 H=96 d=128 fp32 state in place",
                    "chunk": args.chunk, "tokens_per_step": T, "heads": H},
@@ -583,7 +583,7 @@ def other_workload(cid, chunk, steps, warmup, prologue=False):
                 ("fused prologue: bf16 gate pre-activations, fp32 beta pre-activations, q and k "
                  "normalised inside" if prologue else "fp32 g/beta, normalised q/k"))
     elif cid == 1:
-        w = W.make_config(1)
+        w = W.make_workload(1)
         up = lambda x, dt: torch.from_numpy(x).to(dev, dt)
         q, k, v = up(w.q, bf), up(w.k, bf), up(w.v, bf)
         g, beta = up(w.g, torch.float32), up(w.beta, torch.float32)
@@ -593,7 +593,7 @@ def other_workload(cid, chunk, steps, warmup, prologue=False):
         every = 0
         desc = "prefill T=4096 H=32 d_k=d_v=128 bf16 q/k/v, fp32 g/beta, zero initial state"
     else:
-        seqlens = W.config4_lengths()
+        seqlens = W.varlen_lengths()
         H, dk, dv = 32, 128, 128
         T = int(sum(seqlens))
         gen = torch.Generator(device=dev)

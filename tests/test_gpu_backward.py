@@ -153,11 +153,11 @@ def test_backward_deterministic():
         assert np.array_equal(x, y), n
 
 
-def test_backward_config1_sampled_heads_and_linearity():
+def test_backward_T4096_H32_sampled_heads_and_linearity():
     """Chunked-prefill workload (one sequence, T = 4096, H = 32, d = 128, bf16): two heads
     against the oracle, and over all heads the identity that holds because o and S_T are linear
     in (S_0, v) jointly: sum(dv * v) + sum(dS0 * S0) = sum(d_o * o) + sum(dS_T * S_T)."""
-    w = W.make_config(1)
+    w = W.make_workload(1)
     do, dsf = W.make_cotangents(w, seed=27)
     dq, dk, dv, dg, db, ds0 = run_bwd(w, do, dsf)
     for x in (dq, dk, dv, dg, db, ds0):
@@ -167,7 +167,7 @@ def test_backward_config1_sampled_heads_and_linearity():
                       w.cu_seqlens, 1.0, None, do[:, heads], dsf[:, heads])
     errs = {n: W.rel_max_err(a[:, heads] if n != "dS0" else a[:, heads], b)
             for n, a, b in zip(NAMES, (dq, dk, dv, dg, db, ds0), ref)}
-    print("[bwd parity] config1 heads", heads, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    print("[bwd parity] T=4096 H=32 heads", heads, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     for k_, v_ in errs.items():
         assert v_ <= TOL["bf16"], (k_, v_)
     o, sf, _ = kda.kda_chunk_fwd(to_dev(w.q, torch.bfloat16), to_dev(w.k, torch.bfloat16),

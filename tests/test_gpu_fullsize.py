@@ -56,17 +56,17 @@ def _run_whole(w):
                              chunk_size=CHUNK)
 
 
-def test_config1_prefill_T4096_H32_every_head():
-    w = W.make_config(1)
+def test_prefill_T4096_H32_every_head():
+    w = W.make_workload(1)
     o, sf, _ = _run_whole(w)
     torch.cuda.synchronize()
     o_r, s_r, _ = oracle.forward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, 1.0, w.s0, 0)
-    _report("config1 T=4096 H=32", {"o": W.rel_max_err(o.cpu().numpy(), o_r),
+    _report("T=4096 H=32", {"o": W.rel_max_err(o.cpu().numpy(), o_r),
                                      "S": W.rel_max_err(sf.cpu().numpy(), s_r)})
 
 
-def test_config2_prefill_T65536_H96_sampled_heads():
-    w = W.make_config(2)
+def test_prefill_T65536_H96_sampled_heads():
+    w = W.make_workload(2)
     o, sf, _ = _run_whole(w)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(sf).all())
@@ -76,7 +76,7 @@ def test_config2_prefill_T65536_H96_sampled_heads():
     idx = torch.tensor(heads, device=o.device)
     o_s = o.index_select(1, idx).cpu().numpy()
     s_s = sf.index_select(1, idx).cpu().numpy()
-    _report(f"config2 T=65536 H=96 heads={heads}", {"o": W.rel_max_err(o_s, o_r), "S": W.rel_max_err(s_s, s_r)})
+    _report(f"T=65536 H=96 heads={heads}", {"o": W.rel_max_err(o_s, o_r), "S": W.rel_max_err(s_s, s_r)})
 
 
 @pytest.mark.timeout(900)
@@ -94,13 +94,13 @@ def test_prefill_one_million_tokens_two_heads():
 
 
 @pytest.mark.timeout(900)
-def test_config2_backward_T65536_H96_sampled_head_and_identity():
+def test_backward_T65536_H96_sampled_head_and_identity():
     """The backward at the benchmark's shape: every gradient finite; one whole head (65,536 tokens)
     against the fp64 oracle adjoint; and over all 96 heads the identity that holds because o and S_T
     are linear in (S_0, V) jointly: sum(dv v) + sum(dS0 S0) = sum(d_o o) + sum(dS_T S_T), with o and
     S_T from the forward."""
     from oracle import backward as OB
-    w = W.make_config(2)
+    w = W.make_workload(2)
     do, dsf = W.make_cotangents(w, seed=31)
     d = dev()
     q, k, v = _bf16(w.q).to(d), _bf16(w.k).to(d), _bf16(w.v).to(d)
@@ -114,7 +114,7 @@ def test_config2_backward_T65536_H96_sampled_head_and_identity():
     lhs = float((dv.double() * v.double()).sum() + (ds0.double() * s0.double()).sum())
     rhs = float((do_d.double() * o.double()).sum() + (dsf_d.double() * sf.double()).sum())
     norm = float(torch.sqrt((dv.double() ** 2).sum() * (v.double() ** 2).sum()))
-    print(f"[fullsize] config2 backward identity: {lhs:.6e} vs {rhs:.6e} (scale {norm:.3e})", flush=True)
+    print(f"[fullsize] T=65536 H=96 backward identity: {lhs:.6e} vs {rhs:.6e} (scale {norm:.3e})", flush=True)
     assert abs(lhs - rhs) <= 1e-3 * norm, (lhs, rhs, norm)
     del o, sf
     h = [41]
@@ -122,12 +122,12 @@ def test_config2_backward_T65536_H96_sampled_head_and_identity():
     ref = OB.backward(qh, kh, vh, gh, bh, w.cu_seqlens, 1.0, s0h, np.ascontiguousarray(do[:, h]),
                       np.ascontiguousarray(dsf[:, h]))
     got = [x[:, h[0]:h[0] + 1].cpu().numpy() for x in (dq, dk, dv, dg, db, ds0)]
-    _report(f"config2 backward head {h[0]}", {n: W.rel_max_err(a, r) for n, a, r in
+    _report(f"T=65536 H=96 backward head {h[0]}", {n: W.rel_max_err(a, r) for n, a, r in
                                               zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got, ref)})
 
 
 @pytest.mark.timeout(900)
-def test_config2_backward_fused_prologue_T65536_H96_sampled_head_and_identity():
+def test_backward_prologue_T65536_H96_sampled_head_and_identity():
     """The backward through the fused gate / normalisation prologue at the benchmark's shape and in
     its launch configuration (`bench.py --backward --prologue`): raw bf16 q, k ~ N(0,1), bf16 gate
     pre-activations a ~ N(0,1), fp32 b ~ N(0,1), scale d^-1/2, drawn on the device with a seeded
@@ -157,7 +157,7 @@ def test_config2_backward_fused_prologue_T65536_H96_sampled_head_and_identity():
     lhs = float((dv.double() * v.double()).sum() + (ds0.double() * s0.double()).sum())
     rhs = float((do.double() * o.double()).sum() + (dsf.double() * sf.double()).sum())
     norm = float(torch.sqrt((dv.double() ** 2).sum() * (v.double() ** 2).sum()))
-    print(f"[fullsize] config2 fused-prologue backward identity: {lhs:.6e} vs {rhs:.6e} (scale {norm:.3e})",
+    print(f"[fullsize] T=65536 H=96 prologue backward identity: {lhs:.6e} vs {rhs:.6e} (scale {norm:.3e})",
           flush=True)
     assert abs(lhs - rhs) <= 1e-3 * norm, (lhs, rhs, norm)
     del o, sf
@@ -169,26 +169,26 @@ def test_config2_backward_fused_prologue_T65536_H96_sampled_head_and_identity():
     ref = OB.backward_fused(host(q), host(k), host(v), host(a), host(b), [0, T], scale, host(s0), host(do),
                             host(dsf), normalize=True, gate=True)
     got = [host(x) for x in grads]
-    _report(f"config2 fused-prologue backward head {h}",
+    _report(f"T=65536 H=96 prologue backward head {h}",
             {n: W.rel_max_err(x, r) for n, x, r in zip(("dq", "dk", "dv", "da", "db", "dS0"), got, ref)})
 
 
-def test_config3_decode_N256_H96_every_state():
-    w = W.make_config(3)
+def test_decode_N256_H96_every_state():
+    w = W.make_workload(3)
     d = dev()
     state = _f32(w.s0).to(d)
     o = kda.kda_decode_step(_bf16(w.q).to(d), _bf16(w.k).to(d), _bf16(w.v).to(d), _f32(w.g).to(d),
                             _f32(w.beta).to(d), state, 1.0)
     torch.cuda.synchronize()
     o_r, s_r = oracle.decode(w.q, w.k, w.v, w.g, w.beta, w.s0, 1.0)
-    _report("config3 decode N=256 H=96", {"o": W.rel_max_err(o.cpu().numpy(), o_r),
+    _report("decode N=256 H=96", {"o": W.rel_max_err(o.cpu().numpy(), o_r),
                                           "S": W.rel_max_err(state.cpu().numpy(), s_r)})
 
 
 @pytest.mark.timeout(600)
-def test_config4_varlen_1p85M_tokens_checkpoints_sampled():
-    seqlens = W.config4_lengths()
-    c = W.CONFIGS[4]
+def test_varlen_64seq_1p85M_tokens_checkpoints_sampled():
+    seqlens = W.varlen_lengths()
+    c = W.WORKLOADS[4]
     H, dk, dv, every = c["H"], c["dk"], c["dv"], c["checkpoint_every"]
     T, N = sum(seqlens), len(seqlens)
     d = dev()
@@ -198,7 +198,7 @@ def test_config4_varlen_1p85M_tokens_checkpoints_sampled():
     g = torch.empty((T, H, dk), dtype=torch.float32, device=d)
     beta = torch.empty((T, H), dtype=torch.float32, device=d)
     s0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=d)
-    for first, off, part in W.config_parts(4):
+    for first, off, part in W.workload_parts(4):
         n = part.total_tokens
         q[off:off + n] = _bf16(part.q).to(d)
         k[off:off + n] = _bf16(part.k).to(d)
@@ -206,7 +206,7 @@ def test_config4_varlen_1p85M_tokens_checkpoints_sampled():
         g[off:off + n] = _f32(part.g).to(d)
         beta[off:off + n] = _f32(part.beta).to(d)
         s0[first:first + len(part.seqlens)] = _f32(part.s0).to(d)
-        print(f"[fullsize] config4 generated sequences {first}..{first + len(part.seqlens) - 1}", flush=True)
+        print(f"[fullsize] varlen generated sequences {first}..{first + len(part.seqlens) - 1}", flush=True)
     cu = np.concatenate([[0], np.cumsum(seqlens)])
     o, sf, ck = kda.kda_chunk_fwd(q, k, v, g, beta, list(cu), 1.0, s0, True, every, chunk_size=CHUNK)
     torch.cuda.synchronize()
@@ -221,7 +221,7 @@ def test_config4_varlen_1p85M_tokens_checkpoints_sampled():
     idx = torch.tensor(heads, device=d)
     for s in sample:
         L = seqlens[s]
-        w = W.make_prefill([L], H, dk, dv, c["dtype"], 0, c["s0_std"], "config", every, wid=4, seq_ids=[s])
+        w = W.make_prefill([L], H, dk, dv, c["dtype"], 0, c["s0_std"], "default", every, wid=4, seq_ids=[s])
         qs, ks, vs, gs, bs, s0s = _sub(w, heads)
         o_r, s_r, ck_r = oracle.forward(qs, ks, vs, gs, bs, w.cu_seqlens, 1.0, s0s, every)
         a = int(cu[s])
@@ -229,4 +229,4 @@ def test_config4_varlen_1p85M_tokens_checkpoints_sampled():
                 "S": W.rel_max_err(sf[s:s + 1].index_select(1, idx).cpu().numpy(), s_r)}
         if L // every:
             errs["ckpt"] = W.rel_max_err(ck[ck_first[s]:ck_first[s + 1]].index_select(1, idx).cpu().numpy(), ck_r)
-        _report(f"config4 seq {s} L={L} heads={heads}", errs)
+        _report(f"varlen seq {s} L={L} heads={heads}", errs)

@@ -120,9 +120,9 @@ def test_decode_prologue(gate, norm, d):
 
 # ---- prefill: small shapes and edge cases ------------------------------------------------------
 @pytest.mark.parametrize("chunk", CHUNKS)
-def test_prefill_config0_tiny_f32(chunk):
-    w = W.make_config(0, seed=0)
-    compare(w, label="config0", chunk=chunk)
+def test_prefill_tiny_f32_T256_H2_d64(chunk):
+    w = W.make_workload(0, seed=0)
+    compare(w, label="tiny f32 T=256 H=2 d=64", chunk=chunk)
 
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -281,7 +281,7 @@ def test_workload_generator_properties():
     for x in (w.q, w.k, w.v):
         np.testing.assert_array_equal(W.round_bf16(x), x)
     assert abs(float(np.std(w.s0)) - 0.1) < 0.01
-    L = W.config4_lengths()
+    L = W.varlen_lengths()
     assert len(L) == 64 and all(512 <= x <= 131072 and x % 512 == 0 for x in L)
 
 

@@ -3,7 +3,7 @@ and the smoke check.  This module holds none of the operator's arithmetic:
 only random draws, the input normalisation the workloads prescribe, and bf16
 rounding of inputs.
 
-Distributions (the same for every workload, "config" gate):
+Distributions (the same for every workload, the "default" gate):
   q, k  ~ N(0, 1), L2-normalised per (token, head) over d_k; q is then scaled
           by d_k**-0.5 (so the operator itself runs with scale = 1).
   v     ~ N(0, 1)
@@ -104,7 +104,7 @@ def _gen_block(wid, seed, s, b, T0, Tb, H, dk, dv, dtype, gate, out):
     if dtype == "bf16":
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
     x = rg.standard_normal((Tb, H, dk), dtype=np.float32)
-    if gate == "config":
+    if gate == "default":
         g = np.float32(-5.0) * _sigmoid(x)
     elif gate == "slow":
         g = np.float32(-5.0) * _sigmoid(x - np.float32(6.0))
@@ -122,7 +122,7 @@ def _gen_block(wid, seed, s, b, T0, Tb, H, dk, dv, dtype, gate, out):
     out["beta"][T0:T0 + Tb] = beta
 
 
-def make_prefill(seqlens, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.0, gate="config",
+def make_prefill(seqlens, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.0, gate="default",
                  checkpoint_every=0, wid=100, name=None, threads=None, seq_ids=None) -> Workload:
     """Packed varlen problem.  `seq_ids` (default 0..N-1) are the sequence
     indices the draws are keyed on: passing a subset of a larger workload's
@@ -159,7 +159,7 @@ def make_prefill(seqlens, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.0, g
 
 def make_prefill_raw(seqlens, H, dk=128, dv=128, seed=0, s0_std=0.0, checkpoint_every=0, wid=110,
                      name=None) -> Workload:
-    """Inputs for the fused prologue: the same draws as the config distributions, before the
+    """Inputs for the fused prologue: the same draws as the default distributions, before the
     gate and the normalisation.  q, k ~ N(0,1) unnormalised, v ~ N(0,1) (all bf16-exact),
     ``g`` holds the bf16-exact gate pre-activations a ~ N(0,1) [T,H,dk] and ``beta`` the fp32
     pre-activations b ~ N(0,1) [T,H].  (The operator then uses g = -5 sigmoid(a),
@@ -192,7 +192,7 @@ def make_prefill_raw(seqlens, H, dk=128, dv=128, seed=0, s0_std=0.0, checkpoint_
                     checkpoint_every, {"raw": True, "seed": seed})
 
 
-def make_decode(N, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.1, gate="config", wid=103,
+def make_decode(N, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.1, gate="default", wid=103,
                 name=None, threads=None) -> Workload:
     """N independent sequences, one new token each; the state is [N, H, dk, dv]."""
     w = make_prefill([1] * N, H, dk, dv, dtype, seed, 0.0, gate, 0, wid, name or f"decode_N{N}_H{H}", threads)
@@ -208,7 +208,7 @@ def make_decode(N, H, dk=128, dv=128, dtype="bf16", seed=0, s0_std=0.1, gate="co
     return w
 
 
-def config4_lengths(n=64, lo=512, hi=131072, step=512):
+def varlen_lengths(n=64, lo=512, hi=131072, step=512):
     """64 lengths, log-uniform on [lo, hi], rounded to the nearest multiple of
     `step` inside [lo, hi].  The total is whatever the draw gives (about 1.5M
     expected); it is reported, not rescaled."""
@@ -219,7 +219,7 @@ def config4_lengths(n=64, lo=512, hi=131072, step=512):
 
 
 # The five workloads the operator is measured and checked on.
-CONFIGS = {
+WORKLOADS = {
     0: dict(name="tiny_f32_T256_H2_d64", kind="prefill", seqlens=[256], H=2, dk=64, dv=64, dtype="f32",
             s0_std=0.0, checkpoint_every=0),
     1: dict(name="prefill_T4096_H32_d128", kind="prefill", seqlens=[4096], H=32, dk=128, dv=128, dtype="bf16",
@@ -232,25 +232,25 @@ CONFIGS = {
 }
 
 
-def make_config(cid: int, seed: int = 0, gate: str = "config", threads=None) -> Workload:
-    c = dict(CONFIGS[cid])
+def make_workload(cid: int, seed: int = 0, gate: str = "default", threads=None) -> Workload:
+    c = dict(WORKLOADS[cid])
     if c["kind"] == "decode":
         return make_decode(c["N"], c["H"], c["dk"], c["dv"], c["dtype"], seed, c["s0_std"], gate, wid=cid,
                            name=c["name"], threads=threads)
-    seqlens = c["seqlens"] if c["seqlens"] is not None else config4_lengths()
+    seqlens = c["seqlens"] if c["seqlens"] is not None else varlen_lengths()
     return make_prefill(seqlens, c["H"], c["dk"], c["dv"], c["dtype"], seed, c["s0_std"], gate,
                         c["checkpoint_every"], wid=cid, name=c["name"], threads=threads)
 
 
-def config_parts(cid: int, max_tokens: int = 1 << 18, seed: int = 0, threads=None):
+def workload_parts(cid: int, max_tokens: int = 1 << 18, seed: int = 0, threads=None):
     """Yield (first_seq, token_offset, Workload) pieces that together make
-    config `cid`, each piece a run of whole sequences of at most about
+    workload `cid`, each piece a run of whole sequences of at most about
     `max_tokens` tokens (a longer sequence is a piece of its own).  The values
-    equal those of make_config(cid), so a large workload can be streamed to a
+    equal those of make_workload(cid), so a large workload can be streamed to a
     device without holding it on the host at once."""
-    c = dict(CONFIGS[cid])
+    c = dict(WORKLOADS[cid])
     assert c["kind"] == "prefill"
-    seqlens = c["seqlens"] if c["seqlens"] is not None else config4_lengths()
+    seqlens = c["seqlens"] if c["seqlens"] is not None else varlen_lengths()
     i, off = 0, 0
     while i < len(seqlens):
         j, n = i, 0
@@ -258,7 +258,7 @@ def config_parts(cid: int, max_tokens: int = 1 << 18, seed: int = 0, threads=Non
             n += seqlens[j]
             j += 1
         yield i, off, make_prefill(seqlens[i:j], c["H"], c["dk"], c["dv"], c["dtype"], seed, c["s0_std"],
-                                   "config", c["checkpoint_every"], wid=cid, name=c["name"], threads=threads,
+                                   "default", c["checkpoint_every"], wid=cid, name=c["name"], threads=threads,
                                    seq_ids=range(i, j))
         i, off = j, off + n
 
