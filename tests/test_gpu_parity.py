@@ -358,3 +358,39 @@ def test_prefill_fused_prologue(gate, norm, d, chunk):
     _log(f"fused prologue gate={gate} norm={norm} d={d} C={chunk}",
          {"o": W.rel_max_err(o.cpu().numpy(), o_r), "S": W.rel_max_err(sf.cpu().numpy(), sf_r),
           "ckpt": W.rel_max_err(ck.cpu().numpy(), ck_r)}, TOL["bf16"])
+
+
+# ---- context parallelism: one GPU's share and the combine ----------------------------------------
+def test_context_parallel_segments_combine():
+    """One 512-token sequence cut into 4 segments, as 4 GPUs would hold it: each segment runs from
+    S0 = 0 (outputs o0, final state N_p) and, with v = 0, from S0 = I (outputs oI = scale M_t^T q_t,
+    final state M_p: the identity-column augmentation, d_v = d_k).  The states entering the
+    segments follow S_in(p+1) = M_p S_in(p) + N_p (the exchange step) and o = o0 + S_in^T oI;
+    the result must match the oracle on the unsplit sequence.  Slow decay, so the carried state
+    matters."""
+    P, Lseg, H, d = 4, 128, 2, 128
+    w = W.make_prefill([P * Lseg], H=H, dk=d, dv=d, dtype="bf16", seed=81, s0_std=0.1, gate="slow")
+    cu = [p * Lseg for p in range(P + 1)]
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    q, k, v = to_dev(w.q, bf), to_dev(w.k, bf), to_dev(w.v, bf)
+    g, b = to_dev(w.g, torch.float32), to_dev(w.beta, torch.float32)
+    s0 = torch.zeros((P, H, d, d), dtype=torch.float32, device=dev)
+    o0, n_p, _ = kda.kda_chunk_fwd(q, k, v, g, b, cu, 1.0, s0)
+    eye = torch.eye(d, dtype=torch.float32, device=dev).expand(P, H, d, d).contiguous()
+    oI, m_p, _ = kda.kda_chunk_fwd(q, k, torch.zeros_like(v), g, b, cu, 1.0, eye)
+    torch.cuda.synchronize()
+    o0, oI, n_p, m_p = (x.double().cpu() for x in (o0, oI, n_p, m_p))
+    s_in = torch.from_numpy(w.s0[0]).double()                       # [H, d, d]
+    o = torch.empty_like(o0)
+    carried = 0.0
+    for p in range(P):
+        sl = slice(p * Lseg, (p + 1) * Lseg)
+        corr = torch.einsum("thi,hij->thj", oI[sl], s_in)              # S_in^T oI per token
+        o[sl] = o0[sl] + corr
+        carried = max(carried, float(corr.abs().max() / o0[sl].abs().max()))
+        s_in = torch.einsum("hij,hjk->hik", m_p[p], s_in) + n_p[p]
+    o_r, s_r, _ = oracle.forward(w.q, w.k, w.v, w.g, w.beta, [0, P * Lseg], 1.0, w.s0)
+    _log("context parallel, 4 segments x 128", {"o": W.rel_max_err(o.numpy(), o_r),
+                                                "S": W.rel_max_err(s_in.numpy()[None], s_r)}, TOL["bf16"])
+    assert carried > 0.05, carried   # the segments really depend on the state handed over
