@@ -323,6 +323,49 @@ def test_prefill_paged_pool(chunk):
     np.testing.assert_array_equal(pool_g[rest], pool[rest])
 
 
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_paged_pool_through_the_prologue(chunk):
+    """The pool and the prologue together, as a serving loop would use them: a prefill with raw
+    inputs (gate pre-activations, q and k normalised inside) whose initial states come from pool
+    slots and whose checkpoints go to pool slots, then one decode step through the same prologue
+    on slots the prefill wrote (and one inactive sequence), against the oracle's prologue +
+    forward_paged + decode_paged."""
+    w = W.make_prefill_raw([200, 64, 130, 333], H=3, dk=128, dv=128, seed=43, checkpoint_every=64)
+    P, scale = 16, 128 ** -0.5
+    M = sum(L // 64 for L in w.seqlens)
+    rng = np.random.default_rng(43)
+    pool = (0.1 * rng.standard_normal((P, 3, 128, 128))).astype(np.float32)
+    sidx = np.array([5, -1, 11, 2], dtype=np.int32)
+    cidx = np.array([0, 1, -1, 3, 4, -1, 6, 7, 8, 9, 10], dtype=np.int32)[:M]
+    bf = torch.bfloat16
+    pool_d = to_dev(pool, torch.float32)
+    pro = dict(gate_preactivation=True, normalize_qk=True)
+    o, sf, _ = kda.kda_chunk_fwd(to_dev(w.q, bf), to_dev(w.k, bf), to_dev(w.v, bf), to_dev(w.g, bf),
+                                 to_dev(w.beta, torch.float32), list(w.cu_seqlens), scale, None, True, 64,
+                                 chunk_size=chunk, initial_state_indices=to_dev(sidx, torch.int32),
+                                 state_pool=pool_d, checkpoint_indices=to_dev(cidx, torch.int32), **pro)
+    # decode: sequences on slots 3 and 10 (written above), 6, and one inactive
+    wd = W.make_prefill_raw([1] * 4, H=3, dk=128, dv=128, seed=44)
+    slots = np.array([3, 10, -1, 6], dtype=np.int32)
+    od = kda.kda_decode_step(to_dev(wd.q, bf), to_dev(wd.k, bf), to_dev(wd.v, bf), to_dev(wd.g, bf),
+                             to_dev(wd.beta, torch.float32), pool_d, scale,
+                             state_indices=to_dev(slots, torch.int32), **pro)
+    torch.cuda.synchronize()
+    qn, kn, g64, b64 = oracle.prologue(w.q, w.k, w.g, w.beta, True)
+    o_r, sf_r, pool_r = oracle.forward_paged(qn, kn, w.v, g64, b64, w.cu_seqlens, scale, pool, sidx, 64, cidx)
+    qd, kd, gd, bd = oracle.prologue(wd.q, wd.k, wd.g, wd.beta, True)
+    od_r, pool_r2 = oracle.decode_paged(qd, kd, wd.v, gd, bd, pool_r, slots, scale)
+    pool_g = pool_d.cpu().numpy()
+    touched = sorted(set(cidx[cidx >= 0].tolist()) | set(slots[slots >= 0].tolist()))
+    _log(f"paged + prologue C={chunk}", {"o": W.rel_max_err(o.cpu().numpy(), o_r),
+                                         "S": W.rel_max_err(sf.cpu().numpy(), sf_r),
+                                         "pool": W.rel_max_err(pool_g[touched], pool_r2[touched]),
+                                         "o_dec": W.rel_max_err(od.cpu().numpy(), od_r)}, TOL["bf16"])
+    assert np.all(od.cpu().numpy()[2] == 0)
+    rest = [s_ for s_ in range(P) if s_ not in touched]
+    np.testing.assert_array_equal(pool_g[rest], pool[rest])
+
+
 # ---- fused gate / normalisation prologue ---------------------------------------------------------
 @pytest.mark.parametrize("gate,norm,d,chunk", [(True, True, 128, 32), (True, False, 128, 32),
                                               (False, True, 128, 32), (True, True, 64, 32),
