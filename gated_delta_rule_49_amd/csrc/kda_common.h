@@ -1,6 +1,8 @@
 // kda_common.h -- device helpers shared by the KDA kernels (gfx950 only).
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -95,13 +97,14 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, const f32x4_t &c) 
 
 // Compute units of the current device (host side; queried once per device).
 inline int kda_cu_count() {
-    static int cached[64] = {0};
+    // per device, filled on first use; concurrent first calls store the same value
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int cus = 0;
+    int cus = cached[dev].load(std::memory_order_relaxed);
+    if (!cus) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        cached[dev] = cus;
+        cached[dev].store(cus, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return cus;
 }

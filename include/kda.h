@@ -38,6 +38,11 @@
  *     pure host code and runs before any launch; a failed launch returns
  *     KDA_ERR_DEVICE.  Faults during execution surface at the caller's next
  *     synchronisation.
+ *   - A call only enqueues kernels (no allocation, copy or memset), so calls
+ *     may be captured into a HIP graph.  Calls from several host threads are
+ *     safe; the library's only global state is a per-device compute-unit
+ *     count read once.  Calls that share a workspace or an output must be
+ *     ordered by the caller (same stream, or events).
  *   - Supported: d_k == d_v in {64, 128}; chunk_size 32 or 64; in_dtype
  *     KDA_F32 or KDA_BF16.  Other values -> KDA_ERR_UNSUPPORTED.
  *   - Paged state pool (ABI v2; the digest's inference paragraph: a pool of
