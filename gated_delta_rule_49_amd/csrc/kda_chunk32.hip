@@ -713,10 +713,15 @@ chunk32_kernel(const ChunkParams p) {
                         ss[j] += dpp_f32<0x122>(ss[j]);   // row_ror:2
                         ss[j] += dpp_f32<0x121>(ss[j]);   // row_ror:1
                     }
+                    // across the four 16-lane rows by DPP row broadcasts (rows 1, 3 take the row
+                    // before; rows 2, 3 take lane 31): lane 63 ends with the total, read out uniformly
+                    static_assert(NCP == 64, "a row's channel pairs span the whole wave");
 #pragma unroll
-                    for (int off = 16; off < NCP; off <<= 1)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) ss[j] += shfl_xor(ss[j], off);
+                    for (int j = 0; j < 8; ++j) {
+                        ss[j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss[j]), 0x142, 0xA, 0xF, false));
+                        ss[j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss[j]), 0x143, 0xC, 0xF, false));
+                        ss[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ss[j]), 63));
+                    }
                     if (cp == 0) {
                         float nr[8];
 #pragma unroll
