@@ -69,6 +69,7 @@ class KdaBwdArgs(ctypes.Structure):
 EXPORTED = ["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
             "kda_decode_step", "kda_status_str", "kda_abi_version"]
 
+ABI_VERSION = 4   # KDA_ABI_VERSION of include/kda.h, whose struct layouts the ctypes classes above mirror
 _lib = None
 _lock = threading.Lock()
 
@@ -98,6 +99,9 @@ def lib():
             L.kda_status_str.restype = ctypes.c_char_p
             L.kda_abi_version.argtypes = []
             L.kda_abi_version.restype = ctypes.c_uint32
+            if L.kda_abi_version() != ABI_VERSION:
+                raise RuntimeError(f"{LIB_PATH} has ABI version {L.kda_abi_version()}, this binding expects "
+                                   f"{ABI_VERSION}: rebuild it (`python -c 'import __graft_entry__ as g; g.build()'`)")
             _lib = L
     return _lib
 

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert kda.kda_abi_version() == 4
+    assert kda.kda_abi_version() == 4 == kda.ABI_VERSION
     for code, name in enumerate(["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
                                  "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_DEVICE"]):
         assert kda.kda_status_str(code) == name
