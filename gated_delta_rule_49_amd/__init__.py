@@ -142,12 +142,120 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+
+# ---- argument checks ---------------------------------------------------------------------------
+# The C ABI receives raw device pointers and cannot see dtypes, shapes, devices or strides, so a
+# wrong tensor would make the kernels read or write outside its buffer.  Every entry point below
+# checks its tensors here first and raises ValueError on any mismatch (no library call is made).
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _tensor(name, t, device, shape=None, dtypes=None, optional=False):
+    if t is None:
+        _need(optional, f"{name} is required")
+        return
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+    _need(t.device == device, f"{name} is on {t.device}, expected {device}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtypes is not None:
+        _need(t.dtype in dtypes, f"{name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _inputs(q, k, v, g, beta, gate_preactivation, device):
+    _need(isinstance(q, torch.Tensor) and q.dim() == 3, "q must be a [tokens, H, dk] tensor")
+    T, H, dk = q.shape
+    _need(isinstance(v, torch.Tensor) and v.dim() == 3, "v must be a [tokens, H, dv] tensor")
+    dv = v.shape[2]
+    io = (torch.bfloat16, torch.float32)
+    _tensor("q", q, device, (T, H, dk), io)
+    _tensor("k", k, device, (T, H, dk), (q.dtype,))
+    _tensor("v", v, device, (T, H, dv), (q.dtype,))
+    _tensor("g", g, device, (T, H, dk), (torch.bfloat16,) if gate_preactivation else (torch.float32,))
+    _tensor("beta", beta, device, (T, H), (torch.float32,))
+    return T, H, dk, dv
+
+
+def validate_fwd(q, k, v, g, beta, cu_host, cu_dev=None, initial_state=None, final_state=None, checkpoints=None,
+                 o=None, initial_state_indices=None, checkpoint_indices=None, state_pool_slots=0,
+                 checkpoint_every=0, gate_preactivation=False, device=None):
+    """Check the tensors of a chunked forward; raises ValueError.  cu_host: int32 CPU [N+1]."""
+    device = q.device if device is None else device
+    T, H, dk, dv = _inputs(q, k, v, g, beta, gate_preactivation, device)
+    _need(isinstance(cu_host, torch.Tensor) and cu_host.device.type == "cpu" and cu_host.dtype == torch.int32
+          and cu_host.dim() == 1 and cu_host.numel() >= 1 and cu_host.is_contiguous(),
+          "cu_seqlens (host copy) must be a contiguous int32 CPU tensor [N+1]")
+    N = cu_host.numel() - 1
+    _tensor("cu_seqlens", cu_dev, device, (N + 1,), (torch.int32,), optional=True)
+    st = (torch.float32,)
+    if initial_state_indices is not None:
+        _tensor("initial_state_indices", initial_state_indices, device, (N,), (torch.int32,))
+        _tensor("state_pool", initial_state, device, (state_pool_slots, H, dk, dv), st)
+    else:
+        _tensor("initial_state", initial_state, device, (N, H, dk, dv), st, optional=True)
+    _tensor("final_state", final_state, device, (N, H, dk, dv), st, optional=True)
+    lens = cu_host[1:] - cu_host[:-1]
+    M = int((lens // checkpoint_every).sum()) if checkpoint_every > 0 and N > 0 else 0
+    if checkpoint_indices is not None:
+        _tensor("checkpoint_indices", checkpoint_indices, device, (M,), (torch.int32,))
+        _tensor("state_pool", checkpoints, device, (state_pool_slots, H, dk, dv), st)
+    elif checkpoints is not None:
+        _tensor("checkpoints", checkpoints, device, (M, H, dk, dv), st)
+    _tensor("o", o, device, (T, H, dv), st, optional=True)
+
+
+def validate_bwd(q, k, v, g, beta, d_o, cu_host, cu_dev=None, initial_state=None, d_final_state=None,
+                 states=None, outs=(), gate_preactivation=False, device=None):
+    """Check the tensors of a backward; raises ValueError.  outs: (dq, dk, dv, dg, dbeta, dS0)."""
+    device = q.device if device is None else device
+    T, H, dk, dv = _inputs(q, k, v, g, beta, gate_preactivation, device)
+    _need(isinstance(cu_host, torch.Tensor) and cu_host.device.type == "cpu" and cu_host.dtype == torch.int32
+          and cu_host.dim() == 1 and cu_host.numel() >= 1 and cu_host.is_contiguous(),
+          "cu_seqlens (host copy) must be a contiguous int32 CPU tensor [N+1]")
+    N = cu_host.numel() - 1
+    f32 = (torch.float32,)
+    _tensor("cu_seqlens", cu_dev, device, (N + 1,), (torch.int32,), optional=True)
+    _tensor("d_o", d_o, device, (T, H, dv), f32)
+    _tensor("initial_state", initial_state, device, (N, H, dk, dv), f32, optional=True)
+    _tensor("d_final_state", d_final_state, device, (N, H, dk, dv), f32, optional=True)
+    M32 = int(((cu_host[1:] - cu_host[:-1]) // 32).sum()) if N > 0 else 0
+    _tensor("states", states, device, (M32, H, dk, dv), f32, optional=True)
+    shapes = ((T, H, dk), (T, H, dk), (T, H, dv), (T, H, dk), (T, H), (N, H, dk, dv))
+    for name, t, shp in zip(("dq", "dk", "dv", "dg", "dbeta", "d_initial_state"), outs, shapes):
+        _tensor(name, t, device, shp, f32, optional=name == "d_initial_state")
+
+
+def validate_decode(q, k, v, g, beta, state, o=None, state_indices=None, gate_preactivation=False, device=None):
+    """Check the tensors of a decode step; raises ValueError."""
+    device = q.device if device is None else device
+    N, H, dk, dv = _inputs(q, k, v, g, beta, gate_preactivation, device)
+    f32 = (torch.float32,)
+    _need(isinstance(state, torch.Tensor) and state.dim() == 4, "state must be [N or slots, H, dk, dv]")
+    if state_indices is not None:
+        _tensor("state_indices", state_indices, device, (N,), (torch.int32,))
+        _need(state.shape[0] >= 1, "the state pool needs at least one slot")
+        _tensor("state", state, device, (state.shape[0], H, dk, dv), f32)
+    else:
+        _tensor("state", state, device, (N, H, dk, dv), f32)
+    _tensor("o", o, device, (N, H, dv), f32, optional=True)
+
+
+def _require_device(q):
+    _need(isinstance(q, torch.Tensor) and q.device.type == "cuda",
+          "inputs must be CUDA (HIP) tensors: the operator runs only in libkda's GPU kernels")
+
 DEFAULT_CHUNK = 32
 
 
 def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final_state, checkpoint_every,
                   checkpoints, o, chunk_size=DEFAULT_CHUNK, initial_state_indices=None, checkpoint_indices=None,
                   num_slots=0, gate_preactivation=False, normalize_qk=False):
+    validate_fwd(q, k, v, g, beta, cu_host, cu_dev, initial_state, final_state, checkpoints, o,
+                 initial_state_indices, checkpoint_indices, num_slots, checkpoint_every, gate_preactivation)
     T, H, dk = q.shape
     a = KdaFwdArgs()
     a.struct_size = ctypes.sizeof(KdaFwdArgs)
@@ -194,6 +302,7 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
     q and k per (token, head) inside the operator.
     Returns (o [T,H,dv] fp32, final_state [N,H,dk,dv] fp32 or None, checkpoints or None).
     """
+    _require_device(q)
     T, H, dk = q.shape
     dv = v.shape[2]
     dev = q.device
@@ -238,6 +347,8 @@ def _cu_host(cu_seqlens, T):
 
 def make_bwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, d_o, d_final_state, dq, dk, dv, dg,
                   dbeta, d_initial_state, gate_preactivation=False, normalize_qk=False, states=None):
+    validate_bwd(q, k, v, g, beta, d_o, cu_host, cu_dev, initial_state, d_final_state, states,
+                 (dq, dk, dv, dg, dbeta, d_initial_state), gate_preactivation)
     T, H, dk_ = q.shape
     a = KdaBwdArgs()
     a.struct_size = ctypes.sizeof(KdaBwdArgs)
@@ -274,6 +385,7 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_sta
     callers that run the backward repeatedly).  states: the forward's checkpoints with
     checkpoint_every=32 (fp32 [sum floor(L/32), H, dk, dv]) to read instead of recomputing them, or
     None.  Returns (dq, dk, dv, dg, dbeta, d_initial_state or None), all fp32."""
+    _require_device(q)
     T, H, dk = q.shape
     dv = v.shape[2]
     dev = q.device
@@ -291,6 +403,8 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_sta
     ws_bytes = int(L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a)))
     if ws_bytes == 0 and N > 0:
         _check(L.kda_chunk_bwd(ctypes.byref(a), None, 0, _stream(stream)))
+    if workspace is not None:
+        _tensor("workspace", workspace, dev, None, (torch.uint8,))
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     _check(L.kda_chunk_bwd(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
@@ -300,6 +414,7 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_sta
 
 def make_decode_args(q, k, v, g, beta, state, o, scale, state_indices=None, gate_preactivation=False,
                      normalize_qk=False):
+    validate_decode(q, k, v, g, beta, state, o, state_indices, gate_preactivation)
     N, H, dk = q.shape
     a = KdaDecodeArgs()
     a.struct_size = ctypes.sizeof(KdaDecodeArgs)
@@ -325,6 +440,7 @@ def kda_decode_step(q, k, v, g, beta, state, scale=1.0, out=None, stream=None, s
     state_indices (int32 [N], CUDA), `state` is a pool [P,H,dk,dv] and sequence n uses slot
     state_indices[n] (-1: inactive, o = 0).  gate_preactivation / normalize_qk: the prologue,
     as in kda_chunk_fwd (bf16 inputs).  Returns o [N, H, dv] fp32."""
+    _require_device(q)
     N, H, dk = q.shape
     o = out if out is not None else torch.empty((N, H, v.shape[2]), dtype=torch.float32, device=q.device)
     a = make_decode_args(q, k, v, g, beta, state, o, scale, state_indices, gate_preactivation, normalize_qk)

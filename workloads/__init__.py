@@ -280,13 +280,51 @@ def make_cotangents(w: Workload, seed=0, d_final=True, wid=120):
 
 def rel_max_err(x, ref) -> float:
     """max |x - ref| / RMS(ref) over the whole tensor, in fp64; inf if x has a
-    non-finite value."""
+    non-finite value.  The two arrays must have the same shape (no broadcasting).
+    An empty ref gives 0; an all-zero ref gives 0 if x is all zero, else inf."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    if x.shape != ref.shape:
+        raise ValueError(f"shape mismatch: {x.shape} vs {ref.shape}")
     if not np.all(np.isfinite(x)):
         return float("inf")
-    rms = math.sqrt(float(np.mean(ref * ref))) if ref.size else 0.0
     if ref.size == 0:
         return 0.0
+    rms = math.sqrt(float(np.mean(ref * ref)))
     d = float(np.max(np.abs(x - ref)))
     return d / rms if rms > 0 else (0.0 if d == 0 else float("inf"))
+
+
+class ErrAccum:
+    """rel_max_err over a tensor seen in pieces (for tensors too large to hold, or to
+    recompute, at once): the global max |x - ref| and the global sum of ref^2 and element
+    count are accumulated, so value() equals rel_max_err of the concatenated pieces."""
+
+    def __init__(self):
+        self.maxdiff = 0.0
+        self.sumsq = 0.0
+        self.count = 0
+        self.finite = True
+
+    def add(self, x, ref):
+        x = np.asarray(x, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        if x.shape != ref.shape:
+            raise ValueError(f"shape mismatch: {x.shape} vs {ref.shape}")
+        if ref.size == 0:
+            return self
+        if not np.all(np.isfinite(x)):
+            self.finite = False
+            return self
+        self.maxdiff = max(self.maxdiff, float(np.max(np.abs(x - ref))))
+        self.sumsq += float(np.sum(ref * ref))
+        self.count += ref.size
+        return self
+
+    def value(self) -> float:
+        if not self.finite:
+            return float("inf")
+        if self.count == 0:
+            return 0.0
+        rms = math.sqrt(self.sumsq / self.count)
+        return self.maxdiff / rms if rms > 0 else (0.0 if self.maxdiff == 0 else float("inf"))
