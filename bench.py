@@ -40,7 +40,22 @@ def decode_bytes(N, H, dk, dv, in_bytes=2):
     return N * H * (2 * dk * dv * 4 + in_bytes * (2 * dk + dv) + 4 * dk + 4 + 4 * dv)
 
 
-PREFILL_ALG_FLOP_PER_TOKHEAD = lambda C, dk, dv: 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
+def prefill_flop_per_tokhead(C, dk, dv):
+    """Algorithmic flops per token-head of the chunked form at chunk size C: the in-chunk Gram
+    tiles, the triangular transform and the output assembly 2C(3 d_k + 2 d_v), plus the state
+    read-outs and update 6 d_k d_v.  At C = 64 and d = 128 this is 180,224 (the count the
+    roofline uses); at the kernel's C = 32 it is 139,264."""
+    return 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
+
+
+ROOFLINE_CHUNK = 64   # the flop count of the roofline is the C = 64 one, whatever chunk the kernel runs
+
+
+def roofline_bound(flop, nbytes):
+    """The roofline that binds an algorithm of `flop` flops and `nbytes` HBM bytes on MI355X: HBM
+    when its intensity is below the ridge point (peak bf16 flop/s over peak HBM bytes/s)."""
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    return ("hbm" if flop / nbytes < ridge else "mfma"), flop / nbytes, ridge
 
 
 def main():
@@ -51,6 +66,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (profiling runs)")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip the T=4096 H=32 and varlen timings that the default line carries")
     ap.add_argument("--chunk", type=int, default=32, choices=(32, 64), help="token block of the chunked form")
     ap.add_argument("--prologue", action="store_true",
                     help="with --workload 2 or --backward: fused gate/normalisation prologue (raw q, k, bf16 "
@@ -141,7 +158,6 @@ def main():
     state = up(wd.s0, torch.float32)
     od = torch.empty((N, Hd, wd.v.shape[2]), dtype=torch.float32, device=dev)
     D = kda.make_decode_args(dq, dk_, dvv, dg, db, state, od, 1.0)
-    del wd
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -185,8 +201,11 @@ def main():
     tokens = T
     value = tokens / (pre_avg * 1e-3)
     pbytes = prefill_bytes(T, H, dk, dv)
-    pflop = PREFILL_ALG_FLOP_PER_TOKHEAD(args.chunk, dk, dv) * T * H
+    pflop = prefill_flop_per_tokhead(ROOFLINE_CHUNK, dk, dv) * T * H
+    pflop_k = prefill_flop_per_tokhead(args.chunk, dk, dv) * T * H
     achieved_gbps = pbytes / (pre_avg * 1e-3) / 1e9
+    bound, intensity, ridge = roofline_bound(pflop, pbytes)
+    achieved_tflops = pflop / (pre_avg * 1e-3) / 1e12
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -205,11 +224,25 @@ def main():
                    "chunk": args.chunk, "tokens_per_step": T, "heads": H},
         "prefill": {"ms": round(pre_avg, 4), "ms_p10": round(float(np.percentile(pre_ms, 10)), 4),
                     "ms_p90": round(float(np.percentile(pre_ms, 90)), 4), "tokens_per_s": round(value, 1),
-                    "alg_GBps": round(achieved_gbps, 1), "alg_TFLOPs": round(pflop / (pre_avg * 1e-3) / 1e12, 2),
-                    "alg_bytes": pbytes, "alg_flop": pflop},
-        "roofline": {"kernel": KERNEL_NAME[args.chunk], "bound": "hbm", "achieved": round(achieved_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+                    "alg_GBps": round(achieved_gbps, 1), "alg_bytes": pbytes,
+                    "alg_flop_C64": pflop, "alg_TFLOPs_C64": round(achieved_tflops, 2),
+                    f"alg_flop_C{args.chunk}": pflop_k,
+                    f"alg_TFLOPs_C{args.chunk}": round(pflop_k / (pre_avg * 1e-3) / 1e12, 2),
+                    "flop_note": "C64 = 180,224 flop per token-head (2C(3dk+2dv)+6dkdv at C=64, the roofline's "
+                                 f"count); C{args.chunk} = the same formula at the chunk the kernel runs"},
+        "roofline": {"kernel": KERNEL_NAME[args.chunk], "bound": bound,
+                     "achieved": round(achieved_gbps if bound == "hbm" else achieved_tflops, 1),
+                     "peak": HBM_PEAK_GBPS if bound == "hbm" else BF16_PEAK_TFLOPS,
+                     "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+                     "frac": round(achieved_gbps / HBM_PEAK_GBPS if bound == "hbm" else
+                                   achieved_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1)},
+        "mfma": {"peak_TFLOPs": BF16_PEAK_TFLOPS, "alg_TFLOPs_C64": round(achieved_tflops, 2),
+                 "alg_frac_of_peak": round(achieved_tflops / BF16_PEAK_TFLOPS, 4),
+                 "busy_pct_executed": None, "executed_bf16_TFLOPs": None,
+                 "note": "busy_pct_executed: rocprof SQ_VALU_MFMA_BUSY_CYCLES over all 1024 SIMDs (counts the "
+                         "hi+lo split passes), from the committed counter summary while the kernel is unchanged"},
         "precision": "MFMA bf16 operands (hi+lo split pairs on all output-facing products), fp32 accumulate, "
                      "fp32 o and state",
         "gen_s": round(gen_s, 1),
@@ -276,12 +309,23 @@ def main():
         res["roofline"]["traffic"] = prof["hbm_bytes_per_launch"]
         res["prefill"]["traffic_over_alg"] = round(prof["hbm_bytes_per_launch"] / pbytes, 3)
         if "mfma_util_pct" in prof:
-            res["prefill"]["mfma_util_pct"] = prof["mfma_util_pct"]
-            res["prefill"]["mfma_bf16_TFLOPs"] = round(prof["mfma_bf16_flop_per_launch"] / (pre_avg * 1e-3) / 1e12, 1)
+            res["mfma"]["busy_pct_executed"] = prof["mfma_util_pct"]
+            res["mfma"]["executed_bf16_TFLOPs"] = round(prof["mfma_bf16_flop_per_launch"] / (pre_avg * 1e-3) / 1e12, 1)
         res["prefill"]["counters"] = prof["file"]
 
+    if not args.prefill_only and not args.no_extra_workloads:
+        # the other measured prefill workloads, each timed on its own after the step timing
+        del q, k, v, g, beta, o, A, ws
+        torch.cuda.empty_cache()
+        for cid in (1, 4):
+            r = other_workload(cid, args.chunk, max(5, min(K, 20)), 2, emit=False)
+            res[f"workload_{cid}"] = {key: r[key] for key in ("workload", "tokens", "heads", "value", "unit", "ms",
+                                                              "ms_p10", "ms_p90", "alg_GBps", "frac_of_hbm_peak",
+                                                              "alg_bytes", "cache")}
+            torch.cuda.empty_cache()
+
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wp, args.cpu_seconds, H)
+        res["cpu_baseline"] = cpu_baseline(wp, args.cpu_seconds, H, wd)
     print(json.dumps(res), flush=True)
 
 
@@ -545,7 +589,7 @@ def summarize_backward_trace(trace_dir, bench_log):
     print("wrote profiles/" + name)
 
 
-def other_workload(cid, chunk, steps, warmup, prologue=False):
+def other_workload(cid, chunk, steps, warmup, prologue=False, emit=True):
     """Prefill tokens/s of workload 1 or 4 (one JSON line).  Workload 1 uses the seeded host
     generator; workload 4 (about 1.85M tokens x 32 heads, ~110 GB with o and checkpoints) is drawn
     on the device with torch's seeded generator from the same distributions (lengths from the
@@ -655,14 +699,18 @@ def other_workload(cid, chunk, steps, warmup, prologue=False):
     med = float(np.median(ms))
     nbytes = prefill_bytes(T, H, dk, dv, with_states=False) + len(seqlens) * H * dk * dv * 4 * (2 if s0 is not None else 1) \
         + n_ck * H * dk * dv * 4 - (T * H * dk * 2 if pro else 0)   # a bf16 gate stream: 2 B per channel less
-    print(json.dumps({
+    out = {
         "metric": "KDA prefill tokens/s", "workload": desc, "tokens": T, "heads": H, "chunk": chunk,
         "cache": "cold (512 MB written between calls)" if flush is not None else "inputs larger than the caches",
         "value": round(T / (med * 1e-3), 1), "unit": "tokens/s", "ms": round(med, 4),
         "ms_p10": round(float(np.percentile(ms, 10)), 4), "ms_p90": round(float(np.percentile(ms, 90)), 4),
         "alg_bytes": int(nbytes), "alg_GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "data": "synthetic (seeded)"}), flush=True)
+        "data": "synthetic (seeded)"}
+    del q, k, v, g, beta, o, sf, ck, ws, A, flush
+    if emit:
+        print(json.dumps(out), flush=True)
+    return out
 
 
 def bwd_alg_bytes(T, H, dk, dv, N, fused=False, in_bytes=2):
@@ -785,16 +833,20 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "calls": 3}), flush=True)
 
 
-def cpu_baseline(wp, target_s, H_full):
+def cpu_baseline(wp, target_s, H_full, wd=None):
     """fp64 oracle on a bounded sample of the prefill workload: the first `Ts` tokens of `Hs`
     heads (one chain per thread), sized from a short calibration run to take about target_s
     seconds; when all tokens of `cores` heads are quicker than that, more heads (up to all of
     them), and when the whole workload is, whole-workload runs repeated.  Reported as
-    equivalent tokens/s for all H_full heads."""
+    equivalent tokens/s for all H_full heads.  With wd (the decode workload), also the oracle's
+    decode step over all of its states, as algorithmic GB/s.  The oracle runs on
+    oracle.default_threads() threads: the host CPUs this process may use, at most 16 (the CPU
+    share of one GPU on a shared host); both counts are reported."""
     import numpy as np
 
     import oracle
     cores = oracle.default_threads()
+    host_cpus = len(os.sched_getaffinity(0))
     T, H = wp.q.shape[0], wp.q.shape[1]
 
     def run(Ts, Hs, threads=cores):
@@ -824,12 +876,25 @@ def cpu_baseline(wp, target_s, H_full):
             reps = max(1, int(target_s / max(per_head_round * -(-H // cores), 1e-3)))
     el = sum(run(Ts, Hs) for _ in range(reps))
     tokhead_per_s = reps * Ts * Hs / el
-    return {"value": round(tokhead_per_s / H_full, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "single_thread_token_heads_per_s": round(single, 1),
-            "sample": f"first {Ts} tokens x {Hs} heads of the T=65536 H=96 prefill (fp64 C recurrence, "
-                      f"{Hs} chains on {cores} threads), {reps} run(s), {el:.1f} s; "
-                      f"value = token-heads/s / 96; single thread: the first {one} tokens of head 0",
-            "seconds": round(el, 2)}
+    out = {"value": round(tokhead_per_s / H_full, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "host_cpus_available": host_cpus,
+           "threads_note": f"{cores} threads: the host CPUs available to this process ({host_cpus}), capped at 16, "
+                           "the CPU share of one GPU",
+           "single_thread_token_heads_per_s": round(single, 1),
+           "sample": f"first {Ts} tokens x {Hs} heads of the T=65536 H=96 prefill (fp64 C recurrence, "
+                     f"{Hs} chains on {cores} threads), {reps} run(s), {el:.1f} s; "
+                     f"value = token-heads/s / 96; single thread: the first {one} tokens of head 0",
+           "seconds": round(el, 2)}
+    if wd is not None:
+        N, Hd, dkd = wd.q.shape
+        t = time.perf_counter()
+        oracle.decode(wd.q, wd.k, wd.v, wd.g, wd.beta, wd.s0, 1.0, n_threads=cores)
+        dt = time.perf_counter() - t
+        nb = decode_bytes(N, Hd, dkd, wd.v.shape[2])
+        out["decode"] = {"GBps": round(nb / dt / 1e9, 2), "seconds": round(dt, 2), "alg_bytes": nb,
+                         "sample": f"one decode step of all {N} x {Hd} states (fp64 C, {cores} threads; the "
+                                   "time includes the oracle's conversion of the fp32 inputs)"}
+    return out
 
 
 if __name__ == "__main__":

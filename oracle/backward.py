@@ -39,11 +39,16 @@ def forward_states(q, k, v, g, beta, S0, scale):
     return states, o
 
 
-def backward(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, do=None, dS_final=None):
+def backward(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, do=None, dS_final=None,
+             amplification=False):
     """Gradients of L = sum(do * o) + sum(dS_final * S_final) for packed varlen inputs.
 
     q, k, g: [T, H, dk]; v, do: [T, H, dv]; beta: [T, H]; initial_state, dS_final:
-    [N, H, dk, dv] or None (zeros).  Returns (dq, dk, dv, dg, dbeta, dS0), fp64."""
+    [N, H, dk, dv] or None (zeros).  Returns (dq, dk, dv, dg, dbeta, dS0), fp64.
+
+    amplification=True also returns amp [T, H, dk]: the sum of the magnitudes of the terms whose
+    signed sum is dg, amp_t = alpha_t * rowsum(|dSt~ * S_{t-1}|) (a diagnostic: it sizes how much
+    an error in the states reaches dg through the cancellation in that sum)."""
     q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
     T, H, dk = q.shape
     dv_ = v.shape[2]
@@ -53,6 +58,7 @@ def backward(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, d
     out = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(g), np.zeros_like(beta)]
     dq_, dk_, dvv, dg_, db_ = out
     dS0 = np.zeros((N, H, dk, dv_))
+    amp = np.zeros_like(g) if amplification else None
     for n in range(N):
         a, b = int(cu[n]), int(cu[n + 1])
         for h in range(H):
@@ -76,8 +82,12 @@ def backward(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, d
                 dk_[tt, h] = dS @ u + St @ dp
                 dSt = dS + np.outer(kt, dp)
                 dg_[tt, h] = al * np.sum(dSt * S_prev, axis=1)
+                if amp is not None:
+                    amp[tt, h] = al * np.sum(np.abs(dSt * S_prev), axis=1)
                 dS = al[:, None] * dSt
             dS0[n, h] = dS
+    if amp is not None:
+        return dq_, dk_, dvv, dg_, db_, dS0, amp
     return dq_, dk_, dvv, dg_, db_, dS0
 
 

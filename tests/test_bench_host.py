@@ -44,3 +44,13 @@ def test_backward_bytes():
     assert bench.bwd_alg_bytes(65536, 96, 128, 128, 1) == 65536 * 96 * per + 3 * 96 * 128 * 128 * 4
     # a bf16 gate stream (pre-activations) is 2 bytes per channel cheaper
     assert bench.bwd_alg_bytes(1, 1, 128, 128, 0, fused=True) == per - 2 * 128
+
+
+def test_flop_counts_and_roofline_bound():
+    # 2C(3 dk + 2 dv) + 6 dk dv: 180,224 at C = 64, d = 128 (the roofline's count); 139,264 at C = 32
+    assert bench.prefill_flop_per_tokhead(64, 128, 128) == 180224
+    assert bench.prefill_flop_per_tokhead(32, 128, 128) == 139264
+    # the prefill's intensity (about 100 flop/B) is below MI355X's ridge (2.5e15 / 8e12 = 312.5): HBM
+    bound, inten, ridge = bench.roofline_bound(180224, 1796)
+    assert bound == "hbm" and ridge == pytest.approx(312.5) and inten == pytest.approx(100.35, abs=0.01)
+    assert bench.roofline_bound(400.0, 1.0)[0] == "mfma"

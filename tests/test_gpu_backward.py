@@ -1,9 +1,12 @@
 """GPU parity of the backward (kda_chunk_bwd through the C ABI) against the fp64 oracle adjoint
 (oracle.backward.backward), per gradient: max|gpu - oracle| / RMS(oracle) over the whole tensor.
 Bars as for the forward, 1e-4 with fp32 inputs and 2e-2 with bf16 inputs, except dg on the fp32
-path: dg_t = alpha_t * rowsum(dS~ * S_{t-1}) sums d_v products that are much larger than the
-result, so the fp32 rounding of the recomputed states (about 2e-6 of RMS(S)) reaches dg amplified
-by sum|dS~ S| / RMS(dg) (50-150 on these workloads); its bar is 1e-3."""
+path, whose bar is derived per case: dg_t = alpha_t * rowsum(dS~ * S_{t-1}) sums d_v terms that
+are much larger than the result, so a relative error eps in the fp32 states and state gradients
+reaches dg as eps * amp, amp_t = alpha_t * rowsum(|dS~ * S_{t-1}|) (the oracle's amplification
+output).  The bar is max(1e-4, 4 * EPS_STATE_F32 * max(amp) / RMS(dg)) with EPS_STATE_F32 =
+2e-6, the fp32 forward's measured state error (max|diff| / RMS of the final states, <= 2e-6 in
+the fp32 parity cases)."""
 import json
 import os
 
@@ -12,13 +15,15 @@ import pytest
 import torch
 
 import gated_delta_rule_49_amd as kda
+import oracle
 import workloads as W
 from oracle import backward as OB
+from parity_helpers import identity_bar
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
-DG_TOL = {"f32": 1e-3, "bf16": 2e-2}
+EPS_STATE_F32 = 2e-6
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
 
 
@@ -36,19 +41,32 @@ def run_bwd(w, do, dsf, scale=1.0, s0=True):
     return [x.cpu().numpy() for x in outs]
 
 
+def dg_bar(dtype, dg_ref, amp):
+    """dg's bar for one case: the path's bar, or on the fp32 path the state error carried through
+    the measured cancellation amplification max(amp) / RMS(dg) (see the module docstring)."""
+    if dtype != "f32" or dg_ref.size == 0:
+        return TOL[dtype], 0.0
+    rms = float(np.sqrt(np.mean(np.asarray(dg_ref, dtype=np.float64) ** 2)))
+    a = float(np.max(amp)) / rms if rms > 0 else 0.0
+    return max(TOL["f32"], 4.0 * EPS_STATE_F32 * a), a
+
+
 def check(w, do, dsf, scale=1.0, s0=True, label=""):
-    tol, dg_tol = TOL[w.dtype], DG_TOL[w.dtype]
+    tol = TOL[w.dtype]
     got = run_bwd(w, do, dsf, scale, s0)
-    ref = OB.backward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, scale, w.s0 if s0 else None, do, dsf)
-    errs = {n: W.rel_max_err(a, b) for n, a, b in zip(NAMES, got, ref) if b.size}
+    *ref, amp = OB.backward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, scale, w.s0 if s0 else None, do, dsf,
+                            amplification=True)
+    dg_tol, a = dg_bar(w.dtype, ref[3], amp)
+    errs = {n: W.rel_max_err(a_, b) for n, a_, b in zip(NAMES, got, ref) if b.size}
     label = label or w.name
     print(f"[bwd parity] {label} seqlens={w.seqlens[:8]} H={w.H} d={w.dk} {w.dtype}: "
-          + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+          + " ".join(f"{k}={v:.2e}" for k, v in errs.items())
+          + (f"  (dg bar {dg_tol:.2e} from amplification {a:.1f})" if w.dtype == "f32" else ""), flush=True)
     log = os.environ.get("KDA_PARITY_LOG")
     if log:
         with open(log, "a") as f:
             f.write(json.dumps({"case": "bwd " + label, "H": w.H, "d": w.dk, "dtype": w.dtype,
-                                "tokens": w.total_tokens, "tol": tol, "dg_tol": dg_tol, **errs}) + "\n")
+                                "tokens": w.total_tokens, "tol": tol, "dg_tol": dg_tol, "dg_amp": a, **errs}) + "\n")
     for k_, v_ in errs.items():
         assert v_ <= (dg_tol if k_ == "dg" else tol), (k_, v_)
     return got
@@ -165,8 +183,7 @@ def test_backward_T4096_H32_sampled_heads_and_linearity():
     heads = [0, 17]
     ref = OB.backward(w.q[:, heads], w.k[:, heads], w.v[:, heads], w.g[:, heads], w.beta[:, heads],
                       w.cu_seqlens, 1.0, None, do[:, heads], dsf[:, heads])
-    errs = {n: W.rel_max_err(a[:, heads] if n != "dS0" else a[:, heads], b)
-            for n, a, b in zip(NAMES, (dq, dk, dv, dg, db, ds0), ref)}
+    errs = {n: W.rel_max_err(a[:, heads], b) for n, a, b in zip(NAMES, (dq, dk, dv, dg, db, ds0), ref)}
     print("[bwd parity] T=4096 H=32 heads", heads, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     for k_, v_ in errs.items():
         assert v_ <= TOL["bf16"], (k_, v_)
@@ -174,11 +191,16 @@ def test_backward_T4096_H32_sampled_heads_and_linearity():
                                  to_dev(w.v, torch.bfloat16), to_dev(w.g, torch.float32),
                                  to_dev(w.beta, torch.float32), list(w.cu_seqlens), 1.0, None)
     torch.cuda.synchronize()
+    o_h, sf_h = o.cpu().numpy(), sf.cpu().numpy()
+    o_r, s_r, _ = oracle.forward(w.q[:, heads], w.k[:, heads], w.v[:, heads], w.g[:, heads], w.beta[:, heads],
+                                 w.cu_seqlens, 1.0, None, 0)
+    errs_f = {"o": W.rel_max_err(o_h[:, heads], o_r), "S": W.rel_max_err(sf_h[:, heads], s_r)}
     lhs = float(np.sum(dv.astype(np.float64) * w.v))
-    rhs = float(np.sum(do.astype(np.float64) * o.cpu().numpy()) + np.sum(dsf.astype(np.float64) * sf.cpu().numpy()))
-    scale_ = float(np.sqrt(np.sum(dv.astype(np.float64) ** 2) * np.sum(w.v.astype(np.float64) ** 2)))
-    print(f"[bwd identity] sum(dv v) = {lhs:.6e}  sum(do o) + sum(dST ST) = {rhs:.6e}", flush=True)
-    assert abs(lhs - rhs) <= 1e-3 * scale_, (lhs, rhs, scale_)
+    rhs = float(np.sum(do.astype(np.float64) * o_h) + np.sum(dsf.astype(np.float64) * sf_h))
+    bar = identity_bar([(dv, w.v, errs["dv"]), (o_h, do, errs_f["o"]), (sf_h, dsf, errs_f["S"])])
+    print(f"[bwd identity] sum(dv v) = {lhs:.9e}  sum(do o) + sum(dST ST) = {rhs:.9e}  |diff| {abs(lhs - rhs):.3e}"
+          f" <= bar {bar:.3e}", flush=True)
+    assert abs(lhs - rhs) <= bar, (lhs, rhs, bar)
 
 
 @pytest.mark.parametrize("gate,norm,d", [(True, True, 128), (True, False, 128), (False, True, 128), (True, True, 64)])

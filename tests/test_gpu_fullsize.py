@@ -1,13 +1,14 @@
-"""GPU parity at the full sizes of the measured workloads, in the launch
-configuration the benchmark times (bf16 q/k/v, chunk 32, the library's default).
+"""GPU parity at the full sizes of the measured workloads, in the launch configuration the
+benchmark times (bf16 q/k/v, the library's default chunk of 32; the T = 4096 workload also at
+chunk 64).
 
-The whole GPU problem runs at once; the fp64 oracle then recomputes a sample of
-independent (sequence, head) chains -- whole chains, every token -- and the
-sampled outputs, final states and checkpoints are compared element by element
-with the bf16-path bar (max|diff| / RMS <= 2e-2).  Everything the oracle does not
-recompute is checked for finiteness.  The decode workload (256 x 96 states) is
-small enough for the oracle to cover completely.
-"""
+The whole GPU problem runs at once; the fp64 oracle then recomputes it piece by piece (groups of
+heads, or one sequence at a time, regenerated from the seeded generator), and the parity metric
+is accumulated over the pieces, so the figure asserted is max|diff| / RMS(ref) over the WHOLE
+output tensor, the whole final-state tensor and the whole checkpoint tensor (bf16-path bar
+2e-2).  The backward's oracle keeps every state of a chain in memory, so at the benchmark's
+size it covers four whole heads, and all heads are tied together by the linearity identity with
+a bar derived from the measured errors (tests/parity_helpers.identity_bar)."""
 import numpy as np
 import pytest
 import torch
@@ -15,6 +16,7 @@ import torch
 import gated_delta_rule_49_amd as kda
 import oracle
 import workloads as W
+from parity_helpers import identity_bar, oracle_backward_heads
 
 pytestmark = pytest.mark.gpu
 
@@ -48,35 +50,40 @@ def _sub(w, heads):
             None if w.s0 is None else np.ascontiguousarray(w.s0[:, h]))
 
 
-def _run_whole(w):
+def _run_whole(w, chunk=CHUNK):
     d = dev()
     return kda.kda_chunk_fwd(_bf16(w.q).to(d), _bf16(w.k).to(d), _bf16(w.v).to(d), _f32(w.g).to(d),
                              _f32(w.beta).to(d), list(w.cu_seqlens), 1.0,
                              None if w.s0 is None else _f32(w.s0).to(d), True, w.checkpoint_every,
-                             chunk_size=CHUNK)
+                             chunk_size=chunk)
 
 
-def test_prefill_T4096_H32_every_head():
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_prefill_T4096_H32_every_head(chunk):
     w = W.make_workload(1)
-    o, sf, _ = _run_whole(w)
+    o, sf, _ = _run_whole(w, chunk)
     torch.cuda.synchronize()
     o_r, s_r, _ = oracle.forward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, 1.0, w.s0, 0)
-    _report("T=4096 H=32", {"o": W.rel_max_err(o.cpu().numpy(), o_r),
-                                     "S": W.rel_max_err(sf.cpu().numpy(), s_r)})
+    _report(f"T=4096 H=32 chunk={chunk} (whole tensors)", {"o": W.rel_max_err(o.cpu().numpy(), o_r),
+                                                          "S": W.rel_max_err(sf.cpu().numpy(), s_r)})
 
 
-def test_prefill_T65536_H96_sampled_heads():
+@pytest.mark.timeout(600)
+def test_prefill_T65536_H96_every_head():
+    """The benchmark's prefill (T = 65536, H = 96, S0): o and the final states of all 96 heads
+    against the oracle, in groups of 16 heads."""
     w = W.make_workload(2)
     o, sf, _ = _run_whole(w)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(sf).all())
-    heads = [0, 41, 95]
-    q, k, v, g, b, s0 = _sub(w, heads)
-    o_r, s_r, _ = oracle.forward(q, k, v, g, b, w.cu_seqlens, 1.0, s0, 0)
-    idx = torch.tensor(heads, device=o.device)
-    o_s = o.index_select(1, idx).cpu().numpy()
-    s_s = sf.index_select(1, idx).cpu().numpy()
-    _report(f"T=65536 H=96 heads={heads}", {"o": W.rel_max_err(o_s, o_r), "S": W.rel_max_err(s_s, s_r)})
+    eo, es = W.ErrAccum(), W.ErrAccum()
+    for h0 in range(0, w.H, 16):
+        heads = list(range(h0, min(w.H, h0 + 16)))
+        q, k, v, g, b, s0 = _sub(w, heads)
+        o_r, s_r, _ = oracle.forward(q, k, v, g, b, w.cu_seqlens, 1.0, s0, 0)
+        eo.add(o[:, h0:h0 + len(heads)].cpu().numpy(), o_r)
+        es.add(sf[:, h0:h0 + len(heads)].cpu().numpy(), s_r)
+        print(f"[fullsize] T=65536 H=96 heads {h0}..{heads[-1]} done: o so far {eo.value():.2e}", flush=True)
+    _report("T=65536 H=96 (whole tensors, all 96 heads)", {"o": eo.value(), "S": es.value()})
 
 
 @pytest.mark.timeout(900)
@@ -93,46 +100,61 @@ def test_prefill_one_million_tokens_two_heads():
                               "ckpt": W.rel_max_err(ck.cpu().numpy(), ck_r)})
 
 
+def _backward_identity(label, grads, fwd, v, s0, do, dsf, errs_b, errs_f):
+    """sum(dv v) + sum(dS0 S0) = sum(d_o o) + sum(dS_T S_T) over every head (o and S_T are linear
+    in (S0, v) jointly), against identity_bar with the errors measured on the sampled heads."""
+    dv, ds0 = grads[2], grads[5]
+    o, sf = fwd
+    lhs = float((dv.double() * v.double()).sum() + (ds0.double() * s0.double()).sum())
+    rhs = float((do.double() * o.double()).sum() + (dsf.double() * sf.double()).sum())
+    bar = identity_bar([(dv, v, errs_b["dv"]), (ds0, s0, errs_b["dS0"]), (o, do, errs_f["o"]),
+                        (sf, dsf, errs_f["S"])])
+    print(f"[fullsize] {label} identity: {lhs:.9e} vs {rhs:.9e}, |diff| {abs(lhs - rhs):.3e} <= bar {bar:.3e}",
+          flush=True)
+    assert abs(lhs - rhs) <= bar, (lhs, rhs, bar)
+
+
 @pytest.mark.timeout(900)
-def test_backward_T65536_H96_sampled_head_and_identity():
-    """The backward at the benchmark's shape: every gradient finite; one whole head (65,536 tokens)
-    against the fp64 oracle adjoint; and over all 96 heads the identity that holds because o and S_T
-    are linear in (S_0, V) jointly: sum(dv v) + sum(dS0 S0) = sum(d_o o) + sum(dS_T S_T), with o and
-    S_T from the forward."""
-    from oracle import backward as OB
+def test_backward_T65536_H96_four_heads_and_identity():
+    """The backward at the benchmark's shape: every gradient finite; four whole heads (65,536
+    tokens each) against the fp64 oracle adjoint; over all 96 heads the linearity identity."""
     w = W.make_workload(2)
     do, dsf = W.make_cotangents(w, seed=31)
     d = dev()
     q, k, v = _bf16(w.q).to(d), _bf16(w.k).to(d), _bf16(w.v).to(d)
     g, b, s0 = _f32(w.g).to(d), _f32(w.beta).to(d), _f32(w.s0).to(d)
     do_d, dsf_d = _f32(do).to(d), _f32(dsf).to(d)
-    dq, dk, dv, dg, db, ds0 = kda.kda_chunk_bwd(q, k, v, g, b, do_d, list(w.cu_seqlens), 1.0, s0, dsf_d)
+    grads = kda.kda_chunk_bwd(q, k, v, g, b, do_d, list(w.cu_seqlens), 1.0, s0, dsf_d)
     o, sf, _ = kda.kda_chunk_fwd(q, k, v, g, b, list(w.cu_seqlens), 1.0, s0, True, 0, chunk_size=CHUNK)
     torch.cuda.synchronize()
-    for x in (dq, dk, dv, dg, db, ds0):
+    for x in grads:
         assert bool(torch.isfinite(x).all())
-    lhs = float((dv.double() * v.double()).sum() + (ds0.double() * s0.double()).sum())
-    rhs = float((do_d.double() * o.double()).sum() + (dsf_d.double() * sf.double()).sum())
-    norm = float(torch.sqrt((dv.double() ** 2).sum() * (v.double() ** 2).sum()))
-    print(f"[fullsize] T=65536 H=96 backward identity: {lhs:.6e} vs {rhs:.6e} (scale {norm:.3e})", flush=True)
-    assert abs(lhs - rhs) <= 1e-3 * norm, (lhs, rhs, norm)
-    del o, sf
-    h = [41]
-    qh, kh, vh, gh, bh, s0h = _sub(w, h)
-    ref = OB.backward(qh, kh, vh, gh, bh, w.cu_seqlens, 1.0, s0h, np.ascontiguousarray(do[:, h]),
-                      np.ascontiguousarray(dsf[:, h]))
-    got = [x[:, h[0]:h[0] + 1].cpu().numpy() for x in (dq, dk, dv, dg, db, ds0)]
-    _report(f"T=65536 H=96 backward head {h[0]}", {n: W.rel_max_err(a, r) for n, a, r in
-                                              zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got, ref)})
+    heads = [0, 41, 70, 95]
+    print(f"[fullsize] backward oracle on heads {heads} (spawned workers)", flush=True)
+    ref = oracle_backward_heads(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, 1.0, w.s0, do, dsf, heads)
+    names = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
+    acc = {n: W.ErrAccum() for n in names}
+    for hh in heads:
+        for n, x, r in zip(names, grads, ref[hh]):
+            acc[n].add(x[:, hh:hh + 1].cpu().numpy(), r)
+    errs_b = {n: a.value() for n, a in acc.items()}
+    _report(f"T=65536 H=96 backward heads {heads}", errs_b)
+    qs, ks, vs, gs, bs, s0s = _sub(w, heads)
+    o_r, s_r, _ = oracle.forward(qs, ks, vs, gs, bs, w.cu_seqlens, 1.0, s0s, 0)
+    idx = torch.tensor(heads, device=d)
+    errs_f = {"o": W.rel_max_err(o.index_select(1, idx).cpu().numpy(), o_r),
+              "S": W.rel_max_err(sf.index_select(1, idx).cpu().numpy(), s_r)}
+    _backward_identity("T=65536 H=96 backward", grads, (o, sf), v, s0, do_d, dsf_d, errs_b, errs_f)
 
 
 @pytest.mark.timeout(900)
-def test_backward_prologue_T65536_H96_sampled_head_and_identity():
+def test_backward_prologue_T65536_H96_two_heads_and_identity():
     """The backward through the fused gate / normalisation prologue at the benchmark's shape and in
     its launch configuration (`bench.py --backward --prologue`): raw bf16 q, k ~ N(0,1), bf16 gate
     pre-activations a ~ N(0,1), fp32 b ~ N(0,1), scale d^-1/2, drawn on the device with a seeded
-    generator.  Every gradient finite; one whole head against the oracle's adjoint through the
-    same prologue; over all 96 heads the linearity identity (the prologue touches neither v nor S_0)."""
+    generator.  Every gradient finite; two whole heads against the oracle's adjoint through the
+    same prologue; over all 96 heads the linearity identity (the prologue touches neither v nor
+    S_0)."""
     from oracle import backward as OB
     d = dev()
     T, H, D = 65536, 96, 128
@@ -153,24 +175,24 @@ def test_backward_prologue_T65536_H96_sampled_head_and_identity():
     torch.cuda.synchronize()
     for x in grads:
         assert bool(torch.isfinite(x).all())
-    dv, ds0 = grads[2], grads[5]
-    lhs = float((dv.double() * v.double()).sum() + (ds0.double() * s0.double()).sum())
-    rhs = float((do.double() * o.double()).sum() + (dsf.double() * sf.double()).sum())
-    norm = float(torch.sqrt((dv.double() ** 2).sum() * (v.double() ** 2).sum()))
-    print(f"[fullsize] T=65536 H=96 prologue backward identity: {lhs:.6e} vs {rhs:.6e} (scale {norm:.3e})",
-          flush=True)
-    assert abs(lhs - rhs) <= 1e-3 * norm, (lhs, rhs, norm)
-    del o, sf
-    h = 57
-
-    def host(x):
-        return x[:, h:h + 1].float().cpu().numpy().astype(np.float64)
-
-    ref = OB.backward_fused(host(q), host(k), host(v), host(a), host(b), [0, T], scale, host(s0), host(do),
-                            host(dsf), normalize=True, gate=True)
-    got = [host(x) for x in grads]
-    _report(f"T=65536 H=96 prologue backward head {h}",
-            {n: W.rel_max_err(x, r) for n, x, r in zip(("dq", "dk", "dv", "da", "db", "dS0"), got, ref)})
+    names = ("dq", "dk", "dv", "da", "db", "dS0")
+    acc = {n: W.ErrAccum() for n in names}
+    fo, fs = W.ErrAccum(), W.ErrAccum()
+    for h in (57, 3):
+        def host(x):
+            return x[:, h:h + 1].float().cpu().numpy().astype(np.float64)
+        ref = OB.backward_fused(host(q), host(k), host(v), host(a), host(b), [0, T], scale, host(s0), host(do),
+                                host(dsf), normalize=True, gate=True)
+        for n, x, r in zip(names, grads, ref):
+            acc[n].add(host(x), r)
+        o_r, s_r, _ = oracle.forward_fused(host(q), host(k), host(v), host(a), host(b), [0, T], scale, host(s0))
+        fo.add(host(o), o_r)
+        fs.add(host(sf), s_r)
+        print(f"[fullsize] prologue backward head {h} compared", flush=True)
+    errs_b = {n: a_.value() for n, a_ in acc.items()}
+    _report("T=65536 H=96 prologue backward heads [57, 3]", errs_b)
+    _backward_identity("T=65536 H=96 prologue backward", grads, (o, sf), v, s0, do, dsf, errs_b,
+                       {"o": fo.value(), "S": fs.value()})
 
 
 def test_decode_N256_H96_every_state():
@@ -182,11 +204,14 @@ def test_decode_N256_H96_every_state():
     torch.cuda.synchronize()
     o_r, s_r = oracle.decode(w.q, w.k, w.v, w.g, w.beta, w.s0, 1.0)
     _report("decode N=256 H=96", {"o": W.rel_max_err(o.cpu().numpy(), o_r),
-                                          "S": W.rel_max_err(state.cpu().numpy(), s_r)})
+                                  "S": W.rel_max_err(state.cpu().numpy(), s_r)})
 
 
-@pytest.mark.timeout(600)
-def test_varlen_64seq_1p85M_tokens_checkpoints_sampled():
+@pytest.mark.timeout(900)
+def test_varlen_64seq_1p85M_tokens_every_sequence():
+    """The varlen workload (64 packed sequences, 1,853,952 tokens, H = 32, per-sequence S0,
+    checkpoints every 512): every output, every final state and every checkpoint against the
+    oracle, sequence by sequence (inputs regenerated per sequence from the seeded generator)."""
     seqlens = W.varlen_lengths()
     c = W.WORKLOADS[4]
     H, dk, dv, every = c["H"], c["dk"], c["dv"], c["checkpoint_every"]
@@ -214,19 +239,19 @@ def test_varlen_64seq_1p85M_tokens_checkpoints_sampled():
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(sf).all()) and bool(torch.isfinite(ck).all())
     del q, k, v, g, beta
 
-    order = np.argsort(seqlens, kind="stable")
-    sample = sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0]), 7})
-    heads = [0, 13, 31]
     ck_first = np.concatenate([[0], np.cumsum([L // every for L in seqlens])])
-    idx = torch.tensor(heads, device=d)
-    for s in sample:
+    eo, es, ec = W.ErrAccum(), W.ErrAccum(), W.ErrAccum()
+    for s in range(N):
         L = seqlens[s]
         w = W.make_prefill([L], H, dk, dv, c["dtype"], 0, c["s0_std"], "default", every, wid=4, seq_ids=[s])
-        qs, ks, vs, gs, bs, s0s = _sub(w, heads)
-        o_r, s_r, ck_r = oracle.forward(qs, ks, vs, gs, bs, w.cu_seqlens, 1.0, s0s, every)
+        o_r, s_r, ck_r = oracle.forward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, 1.0, w.s0, every)
+        del w
         a = int(cu[s])
-        errs = {"o": W.rel_max_err(o[a:a + L].index_select(1, idx).cpu().numpy(), o_r),
-                "S": W.rel_max_err(sf[s:s + 1].index_select(1, idx).cpu().numpy(), s_r)}
+        eo.add(o[a:a + L].cpu().numpy(), o_r)
+        del o_r
+        es.add(sf[s:s + 1].cpu().numpy(), s_r)
         if L // every:
-            errs["ckpt"] = W.rel_max_err(ck[ck_first[s]:ck_first[s + 1]].index_select(1, idx).cpu().numpy(), ck_r)
-        _report(f"varlen seq {s} L={L} heads={heads}", errs)
+            ec.add(ck[ck_first[s]:ck_first[s + 1]].cpu().numpy(), ck_r)
+        print(f"[fullsize] varlen seq {s} L={L} compared: o so far {eo.value():.2e}", flush=True)
+    _report("varlen 64 seqs 1,853,952 tokens H=32 (whole tensors)",
+            {"o": eo.value(), "S": es.value(), "ckpt": ec.value()})

@@ -58,3 +58,29 @@ def test_streamed_equals_whole():
     acc.add(np.array([np.nan]), np.array([1.0]))
     assert acc.value() == math.inf
     assert W.ErrAccum().value() == 0.0
+
+
+def test_identity_bar_closed_form():
+    from parity_helpers import identity_bar
+    n = 400
+    a, b = np.ones(n), np.full(n, 2.0)                  # RMS(a) = 1, |b| = 2 sqrt(n) = 40
+    assert identity_bar([(a, b, 0.1)]) == pytest.approx(6 * 0.1 * 40.0, rel=1e-12)
+    assert identity_bar([(a, b, 0.1), (np.zeros(0), np.zeros(0), 1.0)], sigmas=1) == pytest.approx(4.0)
+    torch = pytest.importorskip("torch")
+    assert identity_bar([(torch.ones(n), torch.full((n,), 2.0), 0.1)]) == pytest.approx(24.0, rel=1e-12)
+
+
+def test_identity_bar_covers_independent_errors_and_not_a_wrong_block():
+    """Independent errors of the stated size stay far inside the bar; replacing one block of a
+    by a vector of the same norm and random direction lands far outside it."""
+    from parity_helpers import identity_bar
+    rng = np.random.default_rng(5)
+    n = 200_000
+    a, b = rng.standard_normal(n), rng.standard_normal(n)
+    e = 1e-3
+    a_err = a + e * rng.uniform(-1, 1, n)
+    bar = identity_bar([(a, b, e)])
+    assert abs(a_err @ b - a @ b) < bar / 2
+    a_bad = a.copy()
+    a_bad[:n // 96] = rng.standard_normal(n // 96)      # one "head" of 96 wrong
+    assert abs(a_bad @ b - a @ b) > 3 * bar

@@ -480,3 +480,26 @@ def test_backward_pure_decay_closed_form():
     ref = 0.5 * sum(np.outer(np.exp(G[t]) * q[t, 0], do[t, 0]) for t in range(T)) + np.exp(G[-1])[:, None] * dSf[0, 0]
     np.testing.assert_allclose(dS0[0, 0], ref, rtol=1e-12)
     assert not dk_.any() or np.allclose(dk_, 0.0)       # k enters only through u, which is 0
+
+
+def test_backward_amplification_bounds_dg():
+    """The amplification diagnostic sums the magnitudes of the terms of dg: amp >= |dg| always, with
+    equality when the state has one value column (d_v = 1: a single term)."""
+    from oracle import backward as OB
+    for dv in (1, 3):
+        rng = np.random.default_rng(11 + dv)
+        T, H, dk = 9, 2, 3
+        q, k = rng.standard_normal((T, H, dk)), rng.standard_normal((T, H, dk))
+        v, do = rng.standard_normal((T, H, dv)), rng.standard_normal((T, H, dv))
+        g, beta = -rng.uniform(0, 2, (T, H, dk)), rng.uniform(0, 1, (T, H))
+        s0, dsf = rng.standard_normal((1, H, dk, dv)), rng.standard_normal((1, H, dk, dv))
+        *grads, amp = OB.backward(q, k, v, g, beta, [0, T], 0.7, s0, do, dsf, amplification=True)
+        plain = OB.backward(q, k, v, g, beta, [0, T], 0.7, s0, do, dsf)
+        for x, y in zip(grads, plain):
+            np.testing.assert_array_equal(x, y)
+        dg = grads[3]
+        assert np.all(amp >= np.abs(dg) - 1e-15)
+        if dv == 1:
+            np.testing.assert_allclose(amp, np.abs(dg), rtol=1e-13, atol=1e-15)
+        else:
+            assert np.any(amp > np.abs(dg) * (1 + 1e-6))
