@@ -80,11 +80,11 @@ struct Lds32 {
     static constexpr int VPITCH = DK * 4 + 16 * JT;
     static constexpr int VB = GC + 2 * DK * 4;            // [32][VPITCH] fp32: -V of a chunk
     // prep-wave scratch
-    static constexpr int KN = VB + 32 * VPITCH;           // [48][DK] hl: K e^{G_ref - G} for tiles (0,0), (1,0), (1,1)
-    static constexpr int KN_PLANE = 48 * DK * ES;
+    static constexpr int KN = VB + 32 * VPITCH;           // [32][DK] hl: K e^{G_ref(a) - G}, sub-chunk a's rows
+    static constexpr int KN_PLANE = 32 * DK * ES;
     // the strictly lower, beta-scaled diagonal A_kk blocks, from the Gram tiles to the inverses:
     // block a as Z (ZR + a TSZ) and as Z^T (ZT + a TSZ), fp32 [16][TP]
-    static constexpr int ZR = KN + 48 * DK * 4;
+    static constexpr int ZR = KN + 32 * DK * 4;
     static constexpr int ZT = ZR + 2 * TSZ * 4;
     static constexpr int XCHG = ZT + 2 * TSZ * 4;         // [8][DK] fp32: decay over each 4-row group
     static constexpr int BETA = XCHG + 8 * DK * 4;        // 2 x [32] fp32
@@ -263,46 +263,38 @@ chunk32_kernel(const ChunkParams p) {
         if (a == 1) M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 + lr, 4 * lq), nm);
     };
 
-    // Gram product of Kn block knb (16 rows) with rows 16 a .. 16 a + 15 of KS (or QS): lane holds
-    // element (row 16 a + lr, Kn row 4 lq + e) of the tile
-    // (one accumulator per K-step: the MFMA chains stay short)
-    auto gram_prod = [&](char *sm, int knb, int a, bool use_q, int lane) {
-        f32x4_t acc[KB];
+    // Gram product of Kn block knb (16 rows) with rows 16 a .. 16 a + 15 of KS (or QS), or with
+    // GAMMA of Gamma*K (or Gamma*Q; a = 1 only): lane holds element (row 16 a + lr, Kn row 4 lq + e)
+    // of the tile.  Two accumulator chains (even and odd K-steps) keep two products in flight for
+    // one final 4-element add.
+    auto gram_prod = [&](char *sm, int knb, int a, bool use_q, int lane, bool gamma = false) {
+        f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int s = 0; s < KB; ++s) {
             const F fn = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(knb, s, lane));
-            acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (use_q) mma<true, true>(acc[s], fn, M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(a, s, lane)));
-            else mma<true, false>(acc[s], fn, M::template get<false>(sm + L::KS, 0, fbase<KB>(a, s, lane)));
+            if (use_q)
+                mma<true, true>(acc[s & 1], fn, gamma ? M::template get<true>(sm + L::QT_AT, L::QT_PLANE, fbase<KB>(a, s, lane))
+                                                      : M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(a, s, lane)));
+            else
+                mma<true, false>(acc[s & 1], fn, M::template get<false>(sm + (gamma ? L::KG_AT : L::KS), 0, fbase<KB>(a, s, lane)));
         }
 #pragma unroll
-        for (int s = 1; s < KB; ++s)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[0][e] += acc[s][e];
+        for (int e = 0; e < 4; ++e) acc[0][e] += acc[1][e];
         return acc[0];
     };
     // The same product of Kn block knb with KS rows 16 a .. 16 a + 15 in both orientations: gA as
-    // gram_prod, gB[e] = element (row 16 a + 4 lq + e, Kn row lr) (operands swapped)
+    // gram_prod, gB[e] = element (row 16 a + 4 lq + e, Kn row lr) (operands swapped); one
+    // accumulator chain per orientation, the two chains interleaved
     auto gram_prod_ab = [&](char *sm, int knb, int a, int lane, f32x4_t &gA, f32x4_t &gB) {
-        f32x4_t accA[KB], accB[KB];
+        gA = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        gB = gA;
 #pragma unroll
         for (int s = 0; s < KB; ++s) {
             const F fn = M::template get<true>(sm + L::KN, L::KN_PLANE, fbase<KB>(knb, s, lane));
             const F fx = M::template get<false>(sm + L::KS, 0, fbase<KB>(a, s, lane));
-            accA[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            accB[s] = accA[s];
-            mma<true, false>(accA[s], fn, fx);
-            mma<false, true>(accB[s], fx, fn);
+            mma<true, false>(gA, fn, fx);
+            mma<false, true>(gB, fx, fn);
         }
-#pragma unroll
-        for (int s = 1; s < KB; ++s)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                accA[0][e] += accA[s][e];
-                accB[0][e] += accB[s][e];
-            }
-        gA = accA[0];
-        gB = accB[0];
     };
     // A_qk tile (a, b) (lower incl. diagonal on the diagonal tiles) -> AQK
     auto store_aqk = [&](char *sm, int a, int b, const f32x4_t &gq, int lane) {
@@ -328,13 +320,14 @@ chunk32_kernel(const ChunkParams p) {
     // (the waves that invert the diagonal blocks run in a later segment and read ZR / ZT):
     //   t 0: tile (0,0)  A_kk -> ZR/ZT block 0   and A_qk(0,0)
     //   t 1: tile (1,1)  A_kk -> ZR/ZT block 1   and A_qk(1,1)
-    //   t 2: tile (1,0)  A10 -> AW               and A_qk(1,0)
+    //   t 2: tile (1,0)  A10 -> AW               and A_qk(1,0): Gamma*K (Gamma*Q) rows 16..31 against
+    //        K e^{-G} rows 0..15 (Kn block 0), since k_r e^{G_r} k_i e^{-G_i} = k_r k_i e^{G_r - G_i}
     auto gram_tile = [&](char *sm, int t, int ch, int lane) {
         const int lr = lane & 15, lq = lane >> 4;
-        const int knb = t == 0 ? 0 : (t == 1 ? 2 : 1);
+        const int knb = t == 1 ? 1 : 0;
         const int a = t == 0 ? 0 : 1, b = t == 1 ? 1 : 0;
-        const f32x4_t gk = gram_prod(sm, knb, a, false, lane);
-        if constexpr (!SO) store_aqk(sm, a, b, gram_prod(sm, knb, a, true, lane), lane);
+        const f32x4_t gk = gram_prod(sm, knb, a, false, lane, t == 2);
+        if constexpr (!SO) store_aqk(sm, a, b, gram_prod(sm, knb, a, true, lane, t == 2), lane);
         const float br = beta_row(sm, a, ch, lane);
         if (t == 2) {
             float w[4];
@@ -377,7 +370,7 @@ chunk32_kernel(const ChunkParams p) {
                 if (rw < 2) {
                     // A_kk(rw, rw) with beta-scaled rows, strictly lower, in both forms
                     f32x4_t gA, gB, z, zb;
-                    gram_prod_ab(sm, rw == 0 ? 0 : 2, rw, lane, gA, gB);
+                    gram_prod_ab(sm, rw, rw, lane, gA, gB);
                     const float *bt = reinterpret_cast<const float *>(sm + L::BETA) + (ch & 1) * 32 + 16 * rw;
                     const float br = bt[lr];
                     const float4 bc = *reinterpret_cast<const float4 *>(bt + 4 * lq);
@@ -391,16 +384,16 @@ chunk32_kernel(const ChunkParams p) {
                 } else if (rw == 2) {
                     if constexpr (!SO) {
                         store_aqk(sm, 0, 0, gram_prod(sm, 0, 0, true, lane), lane);
-                        store_aqk(sm, 1, 1, gram_prod(sm, 2, 1, true, lane), lane);
+                        store_aqk(sm, 1, 1, gram_prod(sm, 1, 1, true, lane), lane);
                     }
                 } else {
-                    const f32x4_t gk = gram_prod(sm, 1, 1, false, lane);
+                    const f32x4_t gk = gram_prod(sm, 0, 1, false, lane, true);
                     const float br = beta_row(sm, 1, ch, lane);
                     float w[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = br * gk[e];
                     M::template put_hl<4>(sm + L::AW, L::AW_PLANE, fofs<1>(lr, 4 * lq), w);
-                    if constexpr (!SO) store_aqk(sm, 1, 0, gram_prod(sm, 1, 1, true, lane), lane);
+                    if constexpr (!SO) store_aqk(sm, 1, 0, gram_prod(sm, 0, 1, true, lane, true), lane);
                 }
             }
             lds_barrier();
@@ -509,6 +502,10 @@ chunk32_kernel(const ChunkParams p) {
                     }
                     UF[jt] = M::template from_tiles<true>(u0, u1);
                 }
+                // Output rows 16 rt + 4 lq + e: the part that varies by (rt, e) is uniform and goes into
+                // a scalar row base; the lane's own part (its 4-row group and columns) is one 32-bit
+                // offset, so each store needs no address arithmetic of its own.
+                const unsigned o_lane = (unsigned)(4 * lq * H * DV + SWC * sw + JT * lr);
 #pragma unroll
                 for (int rt = 0; rt < 2 && !SO; ++rt) {
                     const F fa = M::template get<true>(sm + L::AQK, L::TRI_PLANE, fbase<1>(rt, 0, lane));
@@ -518,18 +515,20 @@ chunk32_kernel(const ChunkParams p) {
                         acc[jt] = *reinterpret_cast<const f32x4_t *>(sm + L::OST + ((JT * rt + jt) * 64 * NSW + 64 * sw + lane) * 16);
 #pragma unroll
                     for (int jt = 0; jt < JT; ++jt) mma<true, true>(acc[jt], fa, UF[jt]);
-                    // chunk base in scalar registers, 32-bit per-lane offsets
-                    float *const obase = p.o + ((size_t)t0 * H + h) * DV + col0;
-                    const bool full = nv == C32;   // (uniform) no row past the end
+                    float x[4][JT];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * rt + 4 * lq + e;
-                        if (full || r < nv) {
-                            float x[JT];
+                    for (int e = 0; e < 4; ++e)
 #pragma unroll
-                            for (int jt = 0; jt < JT; ++jt) x[jt] = p.scale * acc[jt][e];
-                            store_cols<JT>(obase + (unsigned)(r * H * DV + SWC * sw + JT * lr), x);
-                        }
+                        for (int jt = 0; jt < JT; ++jt) x[e][jt] = p.scale * acc[jt][e];
+                    if (nv == C32) {   // (uniform) a full chunk: no row past the end
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            store_cols<JT>(p.o + ((size_t)(t0 + 16 * rt + e) * H + h) * DV + col0 + o_lane, x[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (16 * rt + 4 * lq + e < nv)
+                                store_cols<JT>(p.o + ((size_t)(t0 + 16 * rt + e) * H + h) * DV + col0 + o_lane, x[e]);
                     }
                 }
             }
@@ -600,15 +599,18 @@ chunk32_kernel(const ChunkParams p) {
         const int rgp = NCP >= 64 ? __builtin_amdgcn_readfirstlane(pt / NCP) : pt / NCP;
         // the sub-chunk is wave-uniform either way (with DK = 64 a wave holds groups 2 pw, 2 pw + 1)
         const int sa = __builtin_amdgcn_readfirstlane(rgp >> 2), gi = rgp & 3;
+        // The waves of the second sub-chunk carry its extra operands (Gamma*K and Gamma*Q of rows
+        // 16..31) and are the longest path of every segment: they issue ahead of the other prep and
+        // scan waves (the role waves, at 3, still go first).
+        if (NRW > 0 && sa) __builtin_amdgcn_s_setprio(2);
         const int lane = pt & 63, lr = lane & 15, lq = lane >> 4;
         // per-thread LDS element offsets and input row offsets, fixed for the whole sequence
-        int ks_off[4], kn_off[4], kn2_off[4], vb_off[4];
+        int ks_off[4], kn_off[4], vb_off[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * rgp + i, rl = r - 16 * sa;
             ks_off[i] = fofs<KB>(r, c0);                 // KS and QS share the layout
-            kn_off[i] = fofs<KB>(32 * sa + rl, c0);
-            kn2_off[i] = fofs<KB>(16 + rl, c0);
+            kn_off[i] = fofs<KB>(16 * sa + rl, c0);
             vb_off[i] = r * L::VPITCH + c0 * 4;
         }
         const int kht_off0 = fofs<1>(c0, 4 * rgp), kht_off1 = fofs<1>(c0 + 1, 4 * rgp);
@@ -661,7 +663,6 @@ chunk32_kernel(const ChunkParams p) {
         typename PR::raw kr[4], qr[4];   // this chunk's k, q pairs from P1 to P2
         float Fw[4][2], Bw[4][2];        // decay products within the 4-row group: through row i / after row i
         float kh[2][4], gl[2];           // (e^{G_last-G} K)^T entries and Gamma_last, from P2 to P3
-        float qtv[4][2];                 // Gamma * q of this thread's rows, from P2 to P3
 
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
@@ -801,14 +802,20 @@ chunk32_kernel(const ChunkParams p) {
                         kd[c] = ke[c] * dgf[c];
                         // (e^{G_last-G} K)^T entry: sub-chunk 0 decays on through sub-chunk 1
                         kh[c][i] = SA ? ke[c] : ke[c] * P1[c];
-                        if (SA) qtv[i][c] = qs[c] * P0[c];    // Gamma * q (decay from the chunk start)
                     }
                     M::put_h2(sm + L::KS, ks_off[i], ks[0], ks[1]);
                     if constexpr (!SO) M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, ks_off[i], qs);
-                    // Kn rows: sub-chunk 0 feeds tiles (0,0) [x 1/P0] and (1,0) [x 1]; sub-chunk 1 feeds (1,1) [x 1/P1]
+                    // Kn rows (K e^{G_ref(a) - G}): sub-chunk 0 feeds tiles (0,0) and (1,0), sub-chunk 1 (1,1)
                     M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn_off[i], kd);
-                    if (SA == 0) M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn2_off[i], ke);
-                    else M::put_h2(sm + L::KG_AT, ks_off[i], ks[0] * P0[0], ks[1] * P0[1]);   // Gamma * K
+                    if (SA) {
+                        // Gamma * K and Gamma * Q of rows 16..31 (decay from the chunk start): read by
+                        // the (1,0) Gram tiles in segment 3 and by stage a in segment 1 of the next iteration
+                        M::put_h2(sm + L::KG_AT, ks_off[i], ks[0] * P0[0], ks[1] * P0[1]);
+                        if constexpr (!SO) {
+                            const float qt[2] = {qs[0] * P0[0], qs[1] * P0[1]};
+                            M::template put_hl<2>(sm + L::QT_AT, L::QT_PLANE, ks_off[i], qt);
+                        }
+                    }
                 }
             };
             if (have) {
@@ -843,10 +850,6 @@ chunk32_kernel(const ChunkParams p) {
                 M::template put_hl<4>(sm + L::KHT + buf * L::KHT_BUF, L::KHT_PLANE, kht_off1, kh[1]);
                 if (rgp == 0)
                     *reinterpret_cast<float2 *>(sm + L::GC + (buf * DK + c0) * 4) = make_float2(gl[0], gl[1]);
-                // Gamma * Q of chunk nxt (rows 16..31), read by stage a in segment 1 of the next iteration
-                if (!SO && sa)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) M::template put_hl<2>(sm + L::QT_AT, L::QT_PLANE, ks_off[i], qtv[i]);
                 // -V of chunk nxt in fp32, read by stage a in segment 1 of the next iteration (stage a
                 // of chunk it has finished with the buffer); then fetch chunk nxt + 1's
                 const int nv = min(C32, seq_len - nxt * C32);

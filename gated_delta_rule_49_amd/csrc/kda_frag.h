@@ -56,8 +56,10 @@ template <bool F32P> struct Mat;
 template <> struct Mat<false> {
     static constexpr int ES = 2;  // element bytes per plane
     template <int N> __device__ static void put_hl(char *base, int plane_bytes, int off, const float (&x)[N]) {
+        // the lo plane's address is taken from the hi one, so that a constant plane distance
+        // folds into the LDS instruction's offset field instead of costing an address add
         __bf16 *hi = reinterpret_cast<__bf16 *>(base) + off;
-        __bf16 *lo = reinterpret_cast<__bf16 *>(base + plane_bytes) + off;
+        __bf16 *lo = reinterpret_cast<__bf16 *>(reinterpret_cast<char *>(hi) + plane_bytes);
         if constexpr (N == 2) {
             uint32_t H, Lw;
             split_hl2(x[0], x[1], H, Lw);
@@ -85,8 +87,9 @@ template <> struct Mat<false> {
     }
     template <bool LO> __device__ static Frag<false> get(const char *base, int plane_bytes, int off) {
         Frag<false> f;
-        f.hi = *reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(base) + off);
-        if constexpr (LO) f.lo = *reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(base + plane_bytes) + off);
+        const __bf16 *hp = reinterpret_cast<const __bf16 *>(base) + off;
+        f.hi = *reinterpret_cast<const bf16x8_t *>(hp);
+        if constexpr (LO) f.lo = *reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const char *>(hp) + plane_bytes);
         return f;
     }
     // Operand fragment from two 16x16 output tiles covering contraction rows
