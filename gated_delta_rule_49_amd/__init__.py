@@ -66,10 +66,11 @@ class KdaBwdArgs(ctypes.Structure):
     ]
 
 
-EXPORTED = ["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
-            "kda_decode_step", "kda_status_str", "kda_abi_version"]
+EXPORTED = ["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_noalloc", "kda_chunk_bwd",
+            "kda_chunk_bwd_workspace_bytes", "kda_decode_step", "kda_status_str", "kda_abi_version"]
+NOALLOC_MAX_SEQS = 65536   # KDA_NOALLOC_MAX_SEQS of include/kda.h
 
-ABI_VERSION = 4   # KDA_ABI_VERSION of include/kda.h, whose struct layouts the ctypes classes above mirror
+ABI_VERSION = 5   # KDA_ABI_VERSION of include/kda.h, whose struct layouts the ctypes classes above mirror
 _lib = None
 _lock = threading.Lock()
 
@@ -86,6 +87,8 @@ def lib():
             L.kda_chunk_fwd.argtypes = [ctypes.POINTER(KdaFwdArgs), ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]
             L.kda_chunk_fwd.restype = ctypes.c_int
+            L.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(KdaFwdArgs), ctypes.c_void_p]
+            L.kda_chunk_fwd_noalloc.restype = ctypes.c_int
             L.kda_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(KdaFwdArgs)]
             L.kda_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
             L.kda_chunk_bwd.argtypes = [ctypes.POINTER(KdaBwdArgs), ctypes.c_void_p, ctypes.c_size_t,
@@ -285,7 +288,8 @@ def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final
 
 def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, output_final_state=True,
                   checkpoint_every=0, stream=None, chunk_size=DEFAULT_CHUNK, initial_state_indices=None,
-                  state_pool=None, checkpoint_indices=None, gate_preactivation=False, normalize_qk=False):
+                  state_pool=None, checkpoint_indices=None, gate_preactivation=False, normalize_qk=False,
+                  noalloc=False):
     """Chunked KDA prefill (packed varlen).
 
     q, k: [T, H, dk]; v: [T, H, dv] (bf16 or fp32, CUDA, contiguous); g: [T, H, dk] fp32;
@@ -300,6 +304,8 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
     otherwise): gate_preactivation=True takes g as bf16 pre-activations a and beta as fp32
     pre-activations b (g = -5 sigmoid(a), beta = sigmoid(b)); normalize_qk=True L2-normalises
     q and k per (token, head) inside the operator.
+    noalloc=True calls kda_chunk_fwd_noalloc instead: no workspace (the library's static launch-plan
+    array, at most NOALLOC_MAX_SEQS sequences); the outputs are still allocated here.
     Returns (o [T,H,dv] fp32, final_state [N,H,dk,dv] fp32 or None, checkpoints or None).
     """
     _require_device(q)
@@ -327,6 +333,9 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
                       chunk_size, initial_state_indices, checkpoint_indices, nslots, gate_preactivation,
                       normalize_qk)
     L = lib()
+    if noalloc:
+        _check(L.kda_chunk_fwd_noalloc(ctypes.byref(a), _stream(stream)))
+        return o, sf, ck
     ws_bytes = L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a))
     if ws_bytes == 0 and N > 0:
         # invalid arguments: let the entry point report the precise status

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "kda.h"
 
 extern "C" hipError_t kda_launch_decode(int dk, int in_bf16, int N, int H, const void *q, const void *k,
@@ -165,6 +167,37 @@ int bwd_flags(const kda_bwd_args *a) {
     return (a->gate_mode == KDA_GATE_PREACTIVATION ? 1 : 0) | (a->normalize_qk ? 2 : 0) | (a->states ? 8 : 0);
 }
 
+// ---- scratch of the allocation-free forward ------------------------------------------------
+// kda_chunk_fwd_noalloc keeps its launch plan (sequence order, int32 [N] padded to 256 B, then
+// per-sequence checkpoint bases, int64 [N] padded to 256 B, then 256 B) in this file-scope
+// device array instead of a caller workspace.  Each GPU holds its own copy until the process
+// ends.  In host code the name `scratch` is not a device address: the address on the current
+// device is looked up once per device with hipGetSymbolAddress and only that pointer is used.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)KDA_NOALLOC_MAX_SEQS * 4 + (size_t)KDA_NOALLOC_MAX_SEQS * 8 + 256;
+static_assert(KDA_NOALLOC_MAX_SEQS % 64 == 0, "both plan arrays stay multiples of 256 bytes");
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];   // per device, resolved on the first call with that device current
+
+hipError_t scratch_on_current_device(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -218,6 +251,25 @@ kda_status kda_chunk_fwd(const kda_fwd_args *a, void *workspace, size_t workspac
                                           a->cu_seqlens, a->initial_state, a->final_state, a->checkpoint_every,
                                           a->checkpoints, a->o, a->scale, a->initial_state_indices,
                                           a->checkpoint_indices, a->num_slots, flags, workspace, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+kda_status kda_chunk_fwd_noalloc(const kda_fwd_args *a, void *stream) {
+    const kda_status st = validate_fwd(a);
+    if (st != KDA_OK) return st;
+    if (a->num_seqs > KDA_NOALLOC_MAX_SEQS) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    // the launch plan is the only scratch: the prologue's outputs (not fused at this shape) would
+    // need caller memory
+    if (fwd_flags(a) != 0 && !(a->chunk_size == 32 && a->dk == 128)) return KDA_ERR_UNSUPPORTED;
+    if (a->num_seqs == 0) return KDA_OK;
+    if (kda_chunk_workspace_layout(a->num_seqs, nullptr, nullptr) > NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    void *ws = nullptr;
+    if (scratch_on_current_device(&ws) != hipSuccess) return KDA_ERR_DEVICE;
+    const hipError_t e = kda_launch_chunk(a->chunk_size, a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->q,
+                                          a->k, a->v, a->g, a->beta, a->cu_seqlens, a->initial_state, a->final_state,
+                                          a->checkpoint_every, a->checkpoints, a->o, a->scale,
+                                          a->initial_state_indices, a->checkpoint_indices, a->num_slots, fwd_flags(a),
+                                          ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
 

@@ -32,8 +32,9 @@
  *     range of -5*sigmoid(x)); values below -5 may overflow the in-chunk
  *     factorisation.  Inputs must be finite.  Neither is checked.
  *   - The caller owns every buffer, including the workspace; the library never
- *     allocates device memory.  All work is enqueued asynchronously on
- *     `stream` (a hipStream_t passed as void*; NULL = the default stream).
+ *     allocates device memory (kda_chunk_fwd_noalloc uses a static device array
+ *     of the library instead of a workspace).  All work is enqueued asynchronously
+ *     on `stream` (a hipStream_t passed as void*; NULL = the default stream).
  *   - Errors are returned synchronously as kda_status.  Argument validation is
  *     pure host code and runs before any launch; a failed launch returns
  *     KDA_ERR_DEVICE.  Faults during execution surface at the caller's next
@@ -41,8 +42,9 @@
  *   - A call only enqueues kernels (no allocation, copy or memset), so calls
  *     may be captured into a HIP graph.  Calls from several host threads are
  *     safe; the library's only global state is a per-device compute-unit
- *     count read once.  Calls that share a workspace or an output must be
- *     ordered by the caller (same stream, or events).
+ *     count read once, and the per-device address of kda_chunk_fwd_noalloc's
+ *     array.  Calls that share a workspace or an output must be ordered by the
+ *     caller (same stream, or events).
  *   - Supported: d_k == d_v in {64, 128}; chunk_size 32 or 64; in_dtype
  *     KDA_F32 or KDA_BF16.  Other values -> KDA_ERR_UNSUPPORTED.
  *   - Paged state pool (ABI v2; the digest's inference paragraph: a pool of
@@ -63,7 +65,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4u
+#define KDA_ABI_VERSION 5u
 
 typedef enum {
     KDA_OK = 0,
@@ -174,6 +176,23 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_fwd_args *args);
  * kda_chunk_fwd_workspace_bytes(args) bytes of device memory, 256-byte aligned;
  * it is scratch for the launch plan and is overwritten. */
 kda_status kda_chunk_fwd(const kda_fwd_args *args, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_chunk_fwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same operator, arguments and
+ * results as kda_chunk_fwd, with no workspace.  Its launch plan lives in a static device
+ * array inside the library (768 KiB per GPU, held until the process ends); the call allocates
+ * nothing and enqueues the same kernels on `stream`.
+ *   - At most KDA_NOALLOC_MAX_SEQS sequences, else KDA_ERR_WORKSPACE_TOO_SMALL.
+ *   - A prologue (gate_mode / normalize_qk) only where it is fused into the kernel (chunk_size
+ *     32 and dk 128), else KDA_ERR_UNSUPPORTED: elsewhere its outputs would need a workspace.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (different
+ *     streams, no ordering between them) race.  Order them on one stream or with events.
+ *   - The first call on a device looks the array's address up (no allocation); make that first
+ *     call outside a graph capture.
+ */
+#define KDA_NOALLOC_MAX_SEQS 65536
+kda_status kda_chunk_fwd_noalloc(const kda_fwd_args *args, void *stream);
 
 /*
  * One decode step: for each of N independent sequences and each head, consume

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert kda.kda_abi_version() == 4 == kda.ABI_VERSION
+    assert kda.kda_abi_version() == 5 == kda.ABI_VERSION
     for code, name in enumerate(["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
                                  "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_DEVICE"]):
         assert kda.kda_status_str(code) == name
@@ -328,3 +328,36 @@ def test_bwd_workspace(L):
     b, keep2 = bwd_args(cu=[0])
     b.num_seqs, b.total_tokens = 0, 0
     assert bwd_status(L, b, ws=0, ws_bytes=0) == kda.KDA_OK
+
+
+# ---- the allocation-free forward (host-side refusals; no launch) ----------------------------
+@pytest.mark.parametrize("field,value,expect", [
+    ("struct_size", 8, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("dk", 96, kda.KDA_ERR_UNSUPPORTED),
+    ("q", None, kda.KDA_ERR_INVALID_ARGUMENT),
+    ("total_tokens", 227, kda.KDA_ERR_INVALID_ARGUMENT),
+])
+def test_noalloc_validates_like_the_workspace_entry_point(L, field, value, expect):
+    a, keep = fwd_args(**{field: value})
+    assert L.kda_chunk_fwd_noalloc(ctypes.byref(a), None) == expect == status(L, a)
+
+
+def test_noalloc_refuses_more_sequences_than_its_array_holds(L):
+    # an empty batch of NOALLOC_MAX_SEQS + 1 sequences: valid for kda_chunk_fwd, too many here
+    cu = [0] * (kda.NOALLOC_MAX_SEQS + 2)
+    a, keep = fwd_args(cu=cu)
+    assert L.kda_chunk_fwd_noalloc(ctypes.byref(a), None) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) > 0
+
+
+def test_noalloc_refuses_a_prologue_that_needs_a_workspace(L):
+    # outside chunk 32 / d_k 128 the prologue runs as a pass whose outputs need caller memory
+    for over in (dict(gate_mode=kda.KDA_GATE_PREACTIVATION), dict(normalize_qk=1),
+                 dict(gate_mode=kda.KDA_GATE_PREACTIVATION, dk=64, dv=64, chunk_size=32)):
+        a, keep = fwd_args(**over)
+        assert L.kda_chunk_fwd_noalloc(ctypes.byref(a), None) == kda.KDA_ERR_UNSUPPORTED
+
+
+def test_noalloc_empty_batch_is_a_no_op(L):
+    a, keep = fwd_args(cu=[0])
+    assert L.kda_chunk_fwd_noalloc(ctypes.byref(a), None) == kda.KDA_OK
