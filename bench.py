@@ -90,12 +90,14 @@ def main():
                                                                        "MFMA"),
                     help="only write profiles/backward_T65536_H96_d128_counters.md from five rocprofv3 --pmc "
                          "output folders of bench.py --backward (and the copy calibration)")
-    ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "MFMA"),
-                    help="only write the counter summary of the prefill kernel under profiles/ from five "
-                         "rocprofv3 --pmc output folders (csv)")
+    ap.add_argument("--summarize-counters", nargs=7, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "MFMA",
+                                                              "ISSUE", "STALL"),
+                    help="only write the counter summaries of the prefill kernel and of the decode kernel under "
+                         "profiles/ from seven rocprofv3 --pmc output folders (csv)")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.chunk, *args.summarize_counters)
+        summarize_decode_counters(*args.summarize_counters[:4])
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
@@ -308,6 +310,9 @@ def main():
         # only reported while the kernel sources still hash to what was profiled.
         res["roofline"]["traffic"] = prof["hbm_bytes_per_launch"]
         res["prefill"]["traffic_over_alg"] = round(prof["hbm_bytes_per_launch"] / pbytes, 3)
+        for key in ("valu_busy_pct", "lds_busy_pct", "wait_any_over_wave_cycles"):
+            if key in prof:
+                res["prefill"][key] = prof[key]
         if "mfma_util_pct" in prof:
             res["mfma"]["busy_pct_executed"] = prof["mfma_util_pct"]
             res["mfma"]["executed_bf16_TFLOPs"] = round(prof["mfma_bf16_flop_per_launch"] / (pre_avg * 1e-3) / 1e12, 1)
@@ -381,23 +386,47 @@ def _mean(rows, key):
     return sum(r[key] for r in rows) / len(rows)
 
 
-def summarize_counters(chunk, fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma_dir):
-    """Write profiles/<kernel>_counters.json and .md: HBM bytes per launch of the prefill kernel from
+COUNTER_STEP = "bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-extra-workloads"
+ISSUE_COUNTERS = ("SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_LDS SQ_ACTIVE_INST_LDS SQ_INSTS_SALU SQ_WAVES "
+                  "SQ_WAVE_CYCLES GRBM_GUI_ACTIVE")
+STALL_COUNTERS = ("SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+                  "SQ_ACTIVE_INST_ANY SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE")
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA "
+                 "SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
+
+
+def _copy_scales(cfetch_dir, cwrite_dir):
+    """Bytes per counted byte of FETCH_SIZE and WRITE_SIZE (KiB per dispatch), from a plain copy that reads
+    and writes `copy_bytes` per call (bench.py --copy-calibration 2048; its last three calls)."""
+    copy_bytes = 2048 * (1 << 20)
+    cf = _mean(_counter_rows(cfetch_dir, "elementwise_kernel")[-3:], "FETCH_SIZE")
+    cw = _mean(_counter_rows(cwrite_dir, "elementwise_kernel")[-3:], "WRITE_SIZE")
+    return copy_bytes, cf, cw, copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+
+
+def summarize_counters(chunk, fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma_dir, issue_dir, stall_dir):
+    """Write profiles/<kernel>_counters.json and .md for the prefill kernel: HBM bytes per launch from
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for a plain
-    copy of known size, and MFMA busy / bf16 MOPS from a third pass."""
-    kname = {32: "chunk32_kernel<128, 2, false", 64: "chunk_fwd_kernel<128, false"}[chunk]
-    copy_name = "elementwise_kernel"
+    copy of known size; MFMA busy and bf16 MOPS; VALU and LDS instruction counts and issue cycles; wait
+    and LDS-conflict counters.  Busy fractions divide a per-SIMD cycle count by GRBM_GUI_ACTIVE (summed
+    over the 8 XCDs, so / 8) times the 1024 SIMDs."""
+    kname = {32: "chunk32_kernel<128, 2, false, unsigned short, 0>", 64: "chunk_fwd_kernel<128, false"}[chunk]
     fetch = _mean(_counter_rows(fetch_dir, kname), "FETCH_SIZE")
     write = _mean(_counter_rows(write_dir, kname), "WRITE_SIZE")
-    # the copy reads and writes `copy_bytes` each call (bench.py --copy-calibration 2048)
-    copy_bytes = 2048 * (1 << 20)
-    cf = _mean(_counter_rows(cfetch_dir, copy_name)[-3:], "FETCH_SIZE")
-    cw = _mean(_counter_rows(cwrite_dir, copy_name)[-3:], "WRITE_SIZE")
-    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
-    m = _counter_rows(mfma_dir, kname)
-    busy, gui = _mean(m, "SQ_VALU_MFMA_BUSY_CYCLES"), _mean(m, "GRBM_GUI_ACTIVE")
-    mops = _mean(m, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    copy_bytes, cf, cw, fs, ws = _copy_scales(cfetch_dir, cwrite_dir)
     xcd, simds = 8, 1024          # GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs
+    m = _counter_rows(mfma_dir, kname)
+    gui = _mean(m, "GRBM_GUI_ACTIVE") / xcd
+    busy, mops = _mean(m, "SQ_VALU_MFMA_BUSY_CYCLES"), _mean(m, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    iss = _counter_rows(issue_dir, kname)
+    st = _counter_rows(stall_dir, kname)
+    gi, gs = _mean(iss, "GRBM_GUI_ACTIVE") / xcd, _mean(st, "GRBM_GUI_ACTIVE") / xcd
+    T, H = 65536, 96
+    wg_chunks = T // 32 * H * 2 if chunk == 32 else T // 64 * H   # workgroup-chunks per launch (2 per chain)
+    raw = {k: _mean(iss, k) for k in ISSUE_COUNTERS.split() if k != "GRBM_GUI_ACTIVE"}
+    raw.update({k: _mean(st, k) for k in STALL_COUNTERS.split() if k != "GRBM_GUI_ACTIVE"})
+    raw.update({"SQ_INSTS_MFMA": _mean(m, "SQ_INSTS_MFMA"), "SQ_VALU_MFMA_BUSY_CYCLES": busy,
+                "SQ_INSTS_VALU_MFMA_MOPS_BF16": mops, "SQ_BUSY_CYCLES": _mean(m, "SQ_BUSY_CYCLES")})
     d = {
         "kernel": KERNEL_NAME[chunk],
         "workload": "prefill T=65536 H=96 d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state, initial state "
@@ -412,22 +441,37 @@ def summarize_counters(chunk, fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma
         "hbm_bytes_per_launch": round(fetch * 1024 * fs + write * 1024 * ws),
         "mfma_bf16_flop_per_launch": round(mops * 512),
         "mfma_busy_cycles": busy,
-        "gui_active_cycles_per_xcd": gui / xcd,
-        "mfma_util_pct": round(100.0 * busy / (gui / xcd * simds), 2),
+        "gui_active_cycles_per_xcd": gui,
+        "mfma_util_pct": round(100.0 * busy / (gui * simds), 2),
+        # SQ_ACTIVE_INST_* and SQ_WAVE_CYCLES / SQ_WAIT_* count 4-cycle units (one wave64 VALU
+        # instruction issues in 4 cycles: ACTIVE_INST_VALU ~ INSTS_VALU); SQ_VALU_MFMA_BUSY_CYCLES counts cycles
+        "valu_busy_pct": round(100.0 * 4 * raw["SQ_ACTIVE_INST_VALU"] / (gi * simds), 2),
+        "lds_busy_pct": round(100.0 * 4 * raw["SQ_ACTIVE_INST_LDS"] / (gi * simds), 2),
+        "issue_fraction_of_wave_time": round(raw["SQ_ACTIVE_INST_ANY"] / max(raw["SQ_WAVE_CYCLES"], 1), 4),
+        "workgroup_chunks_per_launch": wg_chunks,
+        "per_workgroup_chunk": {"valu_insts": round(raw["SQ_INSTS_VALU"] / wg_chunks, 1),
+                                "lds_insts": round(raw["SQ_INSTS_LDS"] / wg_chunks, 1),
+                                "salu_insts": round(raw["SQ_INSTS_SALU"] / wg_chunks, 1),
+                                "mfma_insts": round(raw["SQ_INSTS_MFMA"] / wg_chunks, 1)},
+        "lds_bank_conflict_per_lds_active": round(raw["SQ_LDS_BANK_CONFLICT"] / max(raw["SQ_LDS_IDX_ACTIVE"], 1), 4),
+        "wait_inst_any_over_wave_cycles": round(raw["SQ_WAIT_INST_ANY"] / max(raw["SQ_WAVE_CYCLES"], 1), 4),
+        "wait_any_over_wave_cycles": round(raw["SQ_WAIT_ANY"] / max(raw["SQ_WAVE_CYCLES"], 1), 4),
+        "raw_counters_per_launch": {k: round(v) for k, v in raw.items()},
         "commands": [
-            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 bench.py --steps 2 "
-            f"--warmup 0 --no-cpu-baseline --prefill-only --chunk {chunk}",
-            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 bench.py --steps 2 "
-            f"--warmup 0 --no-cpu-baseline --prefill-only --chunk {chunk}",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 {COUNTER_STEP}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 {COUNTER_STEP}",
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cfetch_dir} -o run -- python3 bench.py "
             "--copy-calibration 2048",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cwrite_dir} -o run -- python3 bench.py "
             "--copy-calibration 2048",
-            "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES "
-            f"SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d {mfma_dir} -o run -- python3 bench.py --steps 2 "
-            f"--warmup 0 --no-cpu-baseline --prefill-only --chunk {chunk}",
+            f"rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d {mfma_dir} -o run -- python3 {COUNTER_STEP} "
+            "--prefill-only",
+            f"rocprofv3 --pmc {ISSUE_COUNTERS} --output-format csv -d {issue_dir} -o run -- python3 {COUNTER_STEP} "
+            "--prefill-only",
+            f"rocprofv3 --pmc {STALL_COUNTERS} --output-format csv -d {stall_dir} -o run -- python3 {COUNTER_STEP} "
+            "--prefill-only",
             f"python3 bench.py --chunk {chunk} --summarize-counters {fetch_dir} {write_dir} {cfetch_dir} "
-            f"{cwrite_dir} {mfma_dir}",
+            f"{cwrite_dir} {mfma_dir} {issue_dir} {stall_dir}",
         ],
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
@@ -435,12 +479,12 @@ def summarize_counters(chunk, fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma
     with open(base, "w") as f:
         json.dump(d, f, indent=1)
     alg = prefill_bytes(65536, 96, 128, 128)
+    pw = d["per_workgroup_chunk"]
     with open(base[:-5] + ".md", "w") as f:
-        f.write(f"# {d['kernel']}: HBM traffic and MFMA counters\n\n")
+        f.write(f"# {d['kernel']}: HBM traffic, issue and MFMA counters\n\n")
         f.write(f"Workload: {d['workload']}.  Kernel source digest {d['source_digest']}.\n\n")
         f.write("| quantity | value |\n|---|---|\n")
-        f.write(f"| FETCH_SIZE per launch | {d['fetch_kib_per_launch']} KiB |\n")
-        f.write(f"| WRITE_SIZE per launch | {d['write_kib_per_launch']} KiB |\n")
+        f.write(f"| FETCH_SIZE / WRITE_SIZE per launch | {d['fetch_kib_per_launch']} / {d['write_kib_per_launch']} KiB |\n")
         f.write(f"| copy calibration: FETCH_SIZE / WRITE_SIZE for {copy_bytes} B read + written | "
                 f"{d['copy_calibration']['fetch_kib']} / {d['copy_calibration']['write_kib']} KiB |\n")
         f.write(f"| scale factors (bytes per counted byte) | fetch {fs:.4f}, write {ws:.4f} |\n")
@@ -449,11 +493,57 @@ def summarize_counters(chunk, fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma
         f.write(f"| algorithmic bytes per launch | {alg} |\n")
         f.write(f"| measured / algorithmic | {d['hbm_bytes_per_launch'] / alg:.3f} |\n")
         f.write(f"| MFMA bf16 flop per launch (MOPS x 512) | {d['mfma_bf16_flop_per_launch']:.4g} |\n")
-        f.write(f"| MFMA busy (all 1024 SIMDs) | {d['mfma_util_pct']} % |\n\n")
-        f.write("Commands (each counter group in its own run):\n\n")
+        f.write(f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GUI_ACTIVE/8 x 1024 SIMDs)) | {d['mfma_util_pct']} % |\n")
+        f.write(f"| VALU busy (4 x SQ_ACTIVE_INST_VALU, 4-cycle units, same normalisation) | {d['valu_busy_pct']} % |\n")
+        f.write(f"| LDS busy (4 x SQ_ACTIVE_INST_LDS, same normalisation) | {d['lds_busy_pct']} % |\n")
+        f.write(f"| share of wave time issuing any instruction (SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES) | "
+                f"{d['issue_fraction_of_wave_time']} |\n")
+        f.write(f"| per workgroup-chunk ({wg_chunks} per launch): VALU / LDS / SALU / MFMA instructions | "
+                f"{pw['valu_insts']} / {pw['lds_insts']} / {pw['salu_insts']} / {pw['mfma_insts']} |\n")
+        f.write(f"| LDS bank conflicts per LDS-active cycle | {d['lds_bank_conflict_per_lds_active']} |\n")
+        f.write(f"| SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (waves waiting on a dependency) | "
+                f"{d['wait_inst_any_over_wave_cycles']} |\n")
+        f.write(f"| SQ_WAIT_ANY / SQ_WAVE_CYCLES (waves waiting on anything, barriers included) | "
+                f"{d['wait_any_over_wave_cycles']} |\n\n")
+        f.write("Raw counters per launch (sums over the chip, averaged over the profiled launches):\n\n")
+        for k, v in d["raw_counters_per_launch"].items():
+            f.write(f"    {k} = {v}\n")
+        f.write("\nCommands (each counter group in its own run):\n\n")
         for c in d["commands"]:
             f.write(f"    {c}\n")
     print(json.dumps(d, indent=1))
+
+
+def summarize_decode_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """Write profiles/decode_N256_H96_d128_counters.md: HBM bytes of the decode step (the timed launch of
+    the plain path) from the same FETCH_SIZE / WRITE_SIZE passes as the prefill, calibrated as there."""
+    kname = "decode_kernel<128, 128, unsigned short, 0>"
+    fr, wr = _counter_rows(fetch_dir, kname), _counter_rows(write_dir, kname)
+    fetch, write = _mean(fr, "FETCH_SIZE"), _mean(wr, "WRITE_SIZE")
+    copy_bytes, cf, cw, fs, ws = _copy_scales(cfetch_dir, cwrite_dir)
+    rd, wt = fetch * 1024 * fs, write * 1024 * ws
+    alg = decode_bytes(256, 96, 128, 128)
+    with open(os.path.join(ROOT, "profiles", "decode_N256_H96_d128_counters.md"), "w") as f:
+        f.write(f"# {kname}: HBM traffic\n\n")
+        f.write("Workload: decode step N=256 H=96 d_k=d_v=128 (bf16 q/k/v, fp32 g/beta, fp32 state [256,96,128,128] "
+                f"in place).  Averaged over its {len(fr)} dispatches in the profiled run.\n\n")
+        f.write("| quantity | value |\n|---|---|\n")
+        f.write(f"| FETCH_SIZE / WRITE_SIZE per launch | {fetch:.1f} / {write:.1f} KiB |\n")
+        f.write(f"| scale factors from a plain copy of {copy_bytes} B read + written | fetch {fs:.4f}, write {ws:.4f} |\n")
+        f.write(f"| HBM bytes read / written per launch | {rd:.0f} / {wt:.0f} |\n")
+        f.write(f"| algorithmic bytes per launch (state read + written once, token inputs, o) | {alg} |\n")
+        f.write(f"| measured / algorithmic | {(rd + wt) / alg:.3f} |\n\n")
+        f.write("Commands (the first two are the prefill summary's FETCH / WRITE passes; the step runs one prefill "
+                "and one decode step per iteration):\n\n")
+        for c in (f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 {COUNTER_STEP}",
+                  f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 {COUNTER_STEP}",
+                  f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cfetch_dir} -o run -- python3 bench.py "
+                  "--copy-calibration 2048",
+                  f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cwrite_dir} -o run -- python3 bench.py "
+                  "--copy-calibration 2048",
+                  f"python3 bench.py --summarize-counters {fetch_dir} {write_dir} {cfetch_dir} {cwrite_dir} ..."):
+            f.write(f"    {c}\n")
+    print(f"decode: read {rd:.4g} B, written {wt:.4g} B, measured/alg {(rd + wt) / alg:.3f}")
 
 
 def summarize_backward_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma_dir):
@@ -515,7 +605,8 @@ def summarize_trace(trace_dir, bench_json):
     with open(bench_json) as f:
         b = json.loads(f.read().strip().splitlines()[-1])
     cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o run -- python3 bench.py "
-           f"--steps {b['steps']} --warmup {b['warmup']} --no-cpu-baseline --chunk {b['config']['chunk']}")
+           f"--steps {b['steps']} --warmup {b['warmup']} --no-cpu-baseline --no-extra-workloads "
+           f"--chunk {b['config']['chunk']}")
     table = "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |\n|---|---|---|---|---|---|\n"
     for r in rows:
         table += (f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
