@@ -37,6 +37,7 @@ class KdaFwdArgs(ctypes.Structure):
         ("checkpoint_every", ctypes.c_int32), ("checkpoints", ctypes.c_void_p), ("o", ctypes.c_void_p),
         ("initial_state_indices", ctypes.c_void_p), ("checkpoint_indices", ctypes.c_void_p),
         ("num_slots", ctypes.c_int32), ("gate_mode", ctypes.c_int32), ("normalize_qk", ctypes.c_int32),
+        ("segment_tokens", ctypes.c_int32),
     ]
 
 
@@ -70,7 +71,7 @@ EXPORTED = ["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_noa
             "kda_chunk_bwd_workspace_bytes", "kda_decode_step", "kda_status_str", "kda_abi_version"]
 NOALLOC_MAX_SEQS = 65536   # KDA_NOALLOC_MAX_SEQS of include/kda.h
 
-ABI_VERSION = 5   # KDA_ABI_VERSION of include/kda.h, whose struct layouts the ctypes classes above mirror
+ABI_VERSION = 6   # KDA_ABI_VERSION of include/kda.h, whose struct layouts the ctypes classes above mirror
 _lib = None
 _lock = threading.Lock()
 
@@ -256,7 +257,7 @@ DEFAULT_CHUNK = 32
 
 def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final_state, checkpoint_every,
                   checkpoints, o, chunk_size=DEFAULT_CHUNK, initial_state_indices=None, checkpoint_indices=None,
-                  num_slots=0, gate_preactivation=False, normalize_qk=False):
+                  num_slots=0, gate_preactivation=False, normalize_qk=False, segment_tokens=0):
     validate_fwd(q, k, v, g, beta, cu_host, cu_dev, initial_state, final_state, checkpoints, o,
                  initial_state_indices, checkpoint_indices, num_slots, checkpoint_every, gate_preactivation)
     T, H, dk = q.shape
@@ -283,13 +284,14 @@ def make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, final
     a.num_slots = int(num_slots)
     a.gate_mode = KDA_GATE_PREACTIVATION if gate_preactivation else KDA_GATE_LOG_DECAY
     a.normalize_qk = 1 if normalize_qk else 0
+    a.segment_tokens = int(segment_tokens)
     return a
 
 
 def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None, output_final_state=True,
                   checkpoint_every=0, stream=None, chunk_size=DEFAULT_CHUNK, initial_state_indices=None,
                   state_pool=None, checkpoint_indices=None, gate_preactivation=False, normalize_qk=False,
-                  noalloc=False):
+                  noalloc=False, segment_tokens=0):
     """Chunked KDA prefill (packed varlen).
 
     q, k: [T, H, dk]; v: [T, H, dv] (bf16 or fp32, CUDA, contiguous); g: [T, H, dk] fp32;
@@ -306,6 +308,9 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
     q and k per (token, head) inside the operator.
     noalloc=True calls kda_chunk_fwd_noalloc instead: no workspace (the library's static launch-plan
     array, at most NOALLOC_MAX_SEQS sequences); the outputs are still allocated here.
+    segment_tokens: context parallelism inside the GPU (chunk_size 32): 0 lets the library cut
+    few, long sequences into segments that run side by side, -1 never cuts, > 0 cuts every that
+    many tokens (a multiple of 32 and of checkpoint_every).
     Returns (o [T,H,dv] fp32, final_state [N,H,dk,dv] fp32 or None, checkpoints or None).
     """
     _require_device(q)
@@ -331,7 +336,7 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=No
     nslots = int(state_pool.shape[0]) if state_pool is not None else 0
     a = make_fwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, s0, sf, checkpoint_every, ck_arg, o,
                       chunk_size, initial_state_indices, checkpoint_indices, nslots, gate_preactivation,
-                      normalize_qk)
+                      normalize_qk, segment_tokens)
     L = lib()
     if noalloc:
         _check(L.kda_chunk_fwd_noalloc(ctypes.byref(a), _stream(stream)))

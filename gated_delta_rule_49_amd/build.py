@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunk.hip", "kda_chunk32.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunk.hip", "kda_chunk32.hip", "kda_segments.hip", "kda_bwd.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "kda.h"
+#include "kda_common.h"
 
 extern "C" hipError_t kda_launch_decode(int dk, int in_bf16, int N, int H, const void *q, const void *k,
                                         const void *v, const float *g, const float *beta, float *state,
@@ -20,6 +21,13 @@ extern "C" hipError_t kda_launch_chunk(int chunk, int dk, int in_bf16, int N, in
                                        const float *s0, float *sf, int every, float *ckpt, float *o,
                                        float scale, const int32_t *s0_idx, const int32_t *ck_idx,
                                        int nslots, int flags, void *workspace, hipStream_t stream);
+extern "C" size_t kda_segments_workspace_layout(int N, int NB, int H, int d, int T, int64_t nck, size_t *off);
+extern "C" hipError_t kda_launch_chunk_segmented(int dk, int in_bf16, int N, int H, int T, int seg, int NB,
+                                                 int64_t nck, const void *q, const void *k, const void *v,
+                                                 const float *g, const float *beta, const int32_t *cu, const float *s0,
+                                                 float *sf, int every, float *ckpt, float *o, float scale,
+                                                 const int32_t *s0_idx, const int32_t *ck_idx, int nslots, int flags,
+                                                 void *workspace, hipStream_t stream);
 extern "C" hipError_t kda_launch_prologue(int dk, long long rows, int flags, const void *q, const void *k,
                                           const void *v, const float *a, const float *b, float *qn, float *kn,
                                           float *vf, float *g, float *beta, hipStream_t stream);
@@ -85,7 +93,59 @@ kda_status validate_fwd(const kda_fwd_args *a) {
         (a->normalize_qk != 0 && a->normalize_qk != 1))
         return KDA_ERR_INVALID_ARGUMENT;
     if ((a->gate_mode != KDA_GATE_LOG_DECAY || a->normalize_qk) && a->in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    // segments
+    if (a->segment_tokens < -1) return KDA_ERR_INVALID_ARGUMENT;
+    if (a->segment_tokens > 0) {
+        if (a->segment_tokens % 32 != 0) return KDA_ERR_INVALID_ARGUMENT;
+        if (a->checkpoint_every > 0 && a->segment_tokens % a->checkpoint_every != 0) return KDA_ERR_INVALID_ARGUMENT;
+        if (a->chunk_size != 32) return KDA_ERR_UNSUPPORTED;
+        // the segment launches' grids (2 workgroups per segment and head) stay within int range
+        int64_t nb = 0;
+        for (int n = 0; n < a->num_seqs; ++n) {
+            const int32_t L = cu[n + 1] - cu[n];
+            nb += L > 0 ? (L + (int64_t)a->segment_tokens - 1) / a->segment_tokens : 1;
+        }
+        if (nb * a->num_heads * 2 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    }
     return KDA_OK;
+}
+
+// Where the forward cuts its sequences into segments (see segment_tokens): returns the segment
+// length, 0 for no cut, the number of segments in *nb and of checkpoints in *nck.  The library's own
+// choice (segment_tokens 0) cuts only when the uncut launch leaves most of the chip idle --
+// (sequence, head) pairs at most half the compute units, each pair then running on two workgroups
+// -- into about CUs / 2 (segment, head) pairs, whose two runs then fill the chip; and only when the
+// longest sequence spans at least 3 segments (the cut runs most segments twice, so the critical
+// path must shrink by more).  Validated arguments only.
+int segment_plan(const kda_fwd_args *a, int *nb, int64_t *nck) {
+    *nb = 0;
+    *nck = 0;
+    if (a->segment_tokens < 0 || a->chunk_size != 32 || a->num_seqs == 0) return 0;
+    const int32_t *cu = a->cu_seqlens_host;
+    const int N = a->num_seqs, H = a->num_heads;
+    int64_t seg = a->segment_tokens;
+    if (seg == 0) {
+        const int cus = kda_cu_count();
+        if ((int64_t)N * H * 2 > cus) return 0;
+        const int target = cus / (2 * H);
+        if (target < 2) return 0;
+        const int64_t unit = a->checkpoint_every > 0 ? a->checkpoint_every : 32;   // a multiple of 32
+        seg = ((int64_t)a->total_tokens + target - 1) / target;
+        seg = seg < 512 ? 512 : seg;   // shorter segments: launches and the chain of maps dominate
+        seg = (seg + unit - 1) / unit * unit;
+        int32_t lmax = 0;
+        for (int n = 0; n < N; ++n) lmax = cu[n + 1] - cu[n] > lmax ? cu[n + 1] - cu[n] : lmax;
+        if (lmax < 3 * seg || seg > INT32_MAX) return 0;
+    }
+    int64_t count = 0, ck = 0;
+    for (int n = 0; n < N; ++n) {
+        const int32_t L = cu[n + 1] - cu[n];
+        count += L > 0 ? (L + seg - 1) / seg : 1;
+        ck += a->checkpoint_every > 0 ? L / a->checkpoint_every : 0;
+    }
+    *nb = (int)count;
+    *nck = ck;
+    return (int)seg;
 }
 
 int fwd_flags(const kda_fwd_args *a) {
@@ -94,13 +154,14 @@ int fwd_flags(const kda_fwd_args *a) {
 
 // The forward's workspace: the launch plan, then, when the prologue cannot be fused (it is fused
 // for chunk 32 at dk = 128), its outputs: fp32 q / |q|, k / |k|, v (normalisation) and g, beta
-// (gate).  off[0..5]: qn, kn, vf, g, beta, end.
+// (gate); then, when the sequences are cut into segments, the segments' plan and states.
+// off[0..6]: qn, kn, vf, g, beta, segments, end.
 size_t fwd_workspace(const kda_fwd_args *a, size_t *off) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     const int flags = fwd_flags(a);
     const bool mat = flags != 0 && !(a->chunk_size == 32 && a->dk == 128);
     const size_t rows = (size_t)a->total_tokens * a->num_heads;
-    size_t o[6];
+    size_t o[7];
     o[0] = up(kda_chunk_workspace_layout(a->num_seqs, nullptr, nullptr));
     const bool nrm = mat && (flags & 2), gate = mat && (flags & 1);
     o[1] = o[0] + (nrm ? up(rows * a->dk * 4) : 0);
@@ -108,9 +169,15 @@ size_t fwd_workspace(const kda_fwd_args *a, size_t *off) {
     o[3] = o[2] + (nrm ? up(rows * a->dv * 4) : 0);
     o[4] = o[3] + (gate ? up(rows * a->dk * 4) : 0);
     o[5] = o[4] + (gate ? up(rows * 4) : 0);
+    int nb = 0;
+    int64_t nck = 0;
+    const int seg = segment_plan(a, &nb, &nck);
+    o[6] = o[5] + (seg > 0 ? kda_segments_workspace_layout(a->num_seqs, nb, a->num_heads, a->dk, a->total_tokens,
+                                                           nck, nullptr)
+                           : 0);
     if (off)
-        for (int i = 0; i < 6; ++i) off[i] = o[i];
-    return mat ? o[5] : kda_chunk_workspace_layout(a->num_seqs, nullptr, nullptr);
+        for (int i = 0; i < 7; ++i) off[i] = o[i];
+    return mat || seg > 0 ? o[6] : kda_chunk_workspace_layout(a->num_seqs, nullptr, nullptr);
 }
 
 // Validation of kda_chunk_bwd (and its workspace query); also counts the 32-token checkpoints
@@ -223,7 +290,7 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_fwd_args *a) {
 kda_status kda_chunk_fwd(const kda_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
     const kda_status st = validate_fwd(a);
     if (st != KDA_OK) return st;
-    size_t off[6];
+    size_t off[7];
     const size_t need = fwd_workspace(a, off);
     if (a->num_seqs > 0) {
         if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
@@ -247,6 +314,17 @@ kda_status kda_chunk_fwd(const kda_fwd_args *a, void *workspace, size_t workspac
         if (flags & 1) { g = gm; beta = bm; }
         flags = 0;
     }
+    int nb = 0;
+    int64_t nck = 0;
+    const int seg = segment_plan(a, &nb, &nck);
+    if (seg > 0) {
+        const hipError_t e = kda_launch_chunk_segmented(
+            a->dk, in_bf16, a->num_seqs, a->num_heads, a->total_tokens, seg, nb, nck, q, k, v, g, beta,
+            a->cu_seqlens, a->initial_state,
+            a->final_state, a->checkpoint_every, a->checkpoints, a->o, a->scale, a->initial_state_indices,
+            a->checkpoint_indices, a->num_slots, flags, static_cast<char *>(workspace) + off[5], s);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
+    }
     const hipError_t e = kda_launch_chunk(a->chunk_size, a->dk, in_bf16, a->num_seqs, a->num_heads, q, k, v, g, beta,
                                           a->cu_seqlens, a->initial_state, a->final_state, a->checkpoint_every,
                                           a->checkpoints, a->o, a->scale, a->initial_state_indices,
@@ -261,6 +339,7 @@ kda_status kda_chunk_fwd_noalloc(const kda_fwd_args *a, void *stream) {
     // the launch plan is the only scratch: the prologue's outputs (not fused at this shape) would
     // need caller memory
     if (fwd_flags(a) != 0 && !(a->chunk_size == 32 && a->dk == 128)) return KDA_ERR_UNSUPPORTED;
+    if (a->segment_tokens > 0) return KDA_ERR_UNSUPPORTED;   // the segments' states need a workspace
     if (a->num_seqs == 0) return KDA_OK;
     if (kda_chunk_workspace_layout(a->num_seqs, nullptr, nullptr) > NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE_TOO_SMALL;
     void *ws = nullptr;

@@ -567,7 +567,8 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(int
     kda::ChunkParams p;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu_seqlens = cu; p.order = order;
     p.ckpt_base = base; p.s0 = s0; p.sf = sf; p.ckpt = ckpt; p.o = o; p.H = H; p.every = every;
-    p.scale = scale; p.s0_idx = s0_idx; p.ck_idx = ck_idx; p.nslots = nslots; p.flags = flags;
+    p.scale = scale; p.s0_idx = s0_idx; p.ck_idx = ck_idx; p.nslots = nslots; p.s0_slots = nslots; p.flags = flags; p.nseq = N;
+    p.o_tr = nullptr; p.ckpt_tr = nullptr;
     const dim3 grid((unsigned)N * (unsigned)H);
     if (chunk == 32) return kda_launch_chunk32(dk, in_bf16, grid.x, p, stream);
 #define KDA_CHUNK(DKV, F32P, T) \

@@ -163,6 +163,8 @@ chunk32_kernel(const ChunkParams p) {
     using F = Frag<F32P>;
     using PR = Pair<IN_T>;
     constexpr bool SO = (PRO & KDA_STATES_ONLY) != 0;   // states only: q, Gamma*Q, A_qk and o skipped
+    constexpr bool TR = (PRO & KDA_TRANSITION) != 0;    // the paired segment pass (see KDA_TRANSITION)
+    static_assert(!TR || (!SO && SPLIT == 1), "the paired pass: outputs and states, one workgroup per run");
 
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
 
@@ -171,11 +173,13 @@ chunk32_kernel(const ChunkParams p) {
     // workgroups that split one chain read the same k, q, g and beta, so they take indices 8 apart
     // (same XCD, one L2 fetch serves both): within each group of 16, index 8 r + x (r = 0, 1) is
     // part r of chain 8 j + x.  A tail of fewer than 16 falls back to adjacent indices.
+    // The paired segment pass places the two runs of a chain (kind 0 and 1) the same way.
     int part, hn;
     {
         const int b = (int)blockIdx.x;
-        const int full = SPLIT == 1 ? 0 : ((int)gridDim.x & ~15);
-        if (SPLIT == 1) {
+        constexpr bool PAIRED = SPLIT == 2 || TR;
+        const int full = PAIRED ? ((int)gridDim.x & ~15) : 0;
+        if (!PAIRED) {
             part = 0; hn = b;
         } else if (b < full) {
             part = (b >> 3) & 1; hn = ((b >> 4) << 3) + (b & 7);
@@ -183,8 +187,11 @@ chunk32_kernel(const ChunkParams p) {
             part = (b - full) & 1; hn = (full >> 1) + ((b - full) >> 1);
         }
     }
+    const int kind = TR ? part : 0;           // paired segment pass: 1 = the transition run
+    if (TR) part = 0;
     const int h = hn % H;
     const int n = p.order[hn / H];
+    if (TR && kind && p.s0_idx[n] != -2) return;   // a sequence's first segment needs no transition run
     const int col0 = (DV / SPLIT) * part;     // first value column of this workgroup
     const int seq_start = p.cu_seqlens[n];
     const int seq_len = p.cu_seqlens[n + 1] - seq_start;
@@ -403,7 +410,7 @@ chunk32_kernel(const ChunkParams p) {
         // Lane (lq, lr) of scan wave w owns value columns c(jt) = SWC w + JT lr + jt (jt < JT),
         // adjacent in memory, so V, o and S move as JT-element groups.
         // Sr[jt][ct][e] = S[16 ct + 4 lq + e][col0 + c(jt)]
-        const size_t st_off = ((size_t)n * H + h) * DK * DV;
+        const size_t st_off = ((size_t)(kind * p.nseq + n) * H + h) * DK * DV;
         f32x4_t Sr[JT][KT];
         {
             const long long s0o = s0_offset(p, n, h, DK * DV);
@@ -414,8 +421,9 @@ chunk32_kernel(const ChunkParams p) {
                 for (int e = 0; e < 4; ++e) {
                     float x[JT];
 #pragma unroll
-                    for (int jt = 0; jt < JT; ++jt) x[jt] = 0.f;
-                    if (s0o >= 0)
+                    for (int jt = 0; jt < JT; ++jt)
+                        x[jt] = kind && 16 * ct + 4 * lq + e == col0 + SWC * sw + JT * lr + jt ? 1.f : 0.f;
+                    if (!kind && s0o >= 0)
                         load_cols<JT>(p.s0 + s0o + (16 * ct + 4 * lq + e) * DV + col0 + SWC * sw + JT * lr, x);
 #pragma unroll
                     for (int jt = 0; jt < JT; ++jt) Sr[jt][ct][e] = x[jt];
@@ -506,6 +514,7 @@ chunk32_kernel(const ChunkParams p) {
                 // a scalar row base; the lane's own part (its 4-row group and columns) is one 32-bit
                 // offset, so each store needs no address arithmetic of its own.
                 const unsigned o_lane = (unsigned)(4 * lq * H * DV + SWC * sw + JT * lr);
+                float *const obase = TR && kind ? p.o_tr : p.o;
 #pragma unroll
                 for (int rt = 0; rt < 2 && !SO; ++rt) {
                     const F fa = M::template get<true>(sm + L::AQK, L::TRI_PLANE, fbase<1>(rt, 0, lane));
@@ -523,12 +532,12 @@ chunk32_kernel(const ChunkParams p) {
                     if (nv == C32) {   // (uniform) a full chunk: no row past the end
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            store_cols<JT>(p.o + ((size_t)(t0 + 16 * rt + e) * H + h) * DV + col0 + o_lane, x[e]);
+                            store_cols<JT>(obase + ((size_t)(t0 + 16 * rt + e) * H + h) * DV + col0 + o_lane, x[e]);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (16 * rt + 4 * lq + e < nv)
-                                store_cols<JT>(p.o + ((size_t)(t0 + 16 * rt + e) * H + h) * DV + col0 + o_lane, x[e]);
+                                store_cols<JT>(obase + ((size_t)(t0 + 16 * rt + e) * H + h) * DV + col0 + o_lane, x[e]);
                     }
                 }
             }
@@ -557,7 +566,8 @@ chunk32_kernel(const ChunkParams p) {
                     // state after in-sequence position (it + 1) * 32, a multiple of checkpoint_every
                     ck_left = every_chunks;
                     const int64_t m = p.ckpt_base[n] + ck_idx++;
-                    float *const dbase = ckpt_dst(p, m, h, DK * DV);   // NULL: not kept
+                    float *const dbase = TR && kind ? p.ckpt_tr + ((size_t)m * H + h) * DK * DV
+                                                    : ckpt_dst(p, m, h, DK * DV);   // NULL: not kept
                     if (dbase) {
                         float *const dst = dbase + col0;
 #pragma unroll
@@ -647,6 +657,11 @@ chunk32_kernel(const ChunkParams p) {
             bn_ = p.beta[(size_t)t0 * H + (unsigned)(min(4 * rgp + (cp & 3), nv - 1) * H + h)];
         };
         auto vfetch = [&](int ch) {   // value rows: staged to LDS in segment 3, so fetched separately
+            if (kind) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vn_[i] = PR::zero();
+                return;
+            }
             const int t0 = seq_start + ch * C32, nv = min(C32, seq_len - ch * C32);
             const IN_T *vb = vg + (size_t)t0 * H * DV;
 #pragma unroll
@@ -873,10 +888,13 @@ kda_launch_chunk32(int dk, int in_bf16, unsigned chains, const kda::ChunkParams 
     // compute units idle, split each chain's value columns over two workgroups.
     const int split = (long long)chains * 2 <= kda_cu_count() ? 2 : 1;
 #define KDA_C32(DKV, SP, F32P, T, PRO)                                                                   \
-    hipLaunchKernelGGL((kda::chunk32_kernel<DKV, SP, F32P, T, PRO>), dim3(chains * SP),                 \
+    hipLaunchKernelGGL((kda::chunk32_kernel<DKV, SP, F32P, T, PRO>),                                    \
+                       dim3(chains * SP * (((PRO) & kda::KDA_TRANSITION) ? 2 : 1)),                     \
                        dim3(kda::chunk32_threads<DKV, SP>()), 0, stream, p)
     const int pro = p.flags & (kda::KDA_PRO_GATE | kda::KDA_PRO_NORM);
-    if (p.flags & ~(kda::KDA_PRO_GATE | kda::KDA_PRO_NORM | kda::KDA_STATES_ONLY)) return hipErrorInvalidValue;
+    if (p.flags & ~(kda::KDA_PRO_GATE | kda::KDA_PRO_NORM | kda::KDA_STATES_ONLY | kda::KDA_TRANSITION))
+        return hipErrorInvalidValue;
+    if ((p.flags & kda::KDA_TRANSITION) && (p.flags & kda::KDA_STATES_ONLY)) return hipErrorInvalidValue;
     if (pro != 0 && (dk != 128 || !in_bf16)) return hipErrorInvalidValue;   // fused prologue: bf16, d_k = 128
     // (S: SPLIT, F: the flags, both compile-time)
 #define KDA_C32_DT(S, F)                                                                                    \
@@ -897,11 +915,24 @@ kda_launch_chunk32(int dk, int in_bf16, unsigned chains, const kda::ChunkParams 
             case 4: KDA_C32_DT(S, 4); break;                                                               \
             case 5: KDA_C32(128, S, false, uint16_t, 5); break;                                            \
             case 6: KDA_C32(128, S, false, uint16_t, 6); break;                                            \
-            default: KDA_C32(128, S, false, uint16_t, 7); break;                                           \
+            case 7: KDA_C32(128, S, false, uint16_t, 7); break;                                            \
+            default: return hipErrorInvalidValue;                                                          \
         }                                                                                                  \
     } while (0)
-    if (split == 2) KDA_C32_FLAGS(2);
-    else KDA_C32_FLAGS(1);
+    if (p.flags & kda::KDA_TRANSITION) {
+        // the paired segment pass: one workgroup per chain and kind
+        switch (p.flags) {
+            case 16: KDA_C32_DT(1, 16); break;
+            case 17: KDA_C32(128, 1, false, uint16_t, 17); break;
+            case 18: KDA_C32(128, 1, false, uint16_t, 18); break;
+            case 19: KDA_C32(128, 1, false, uint16_t, 19); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else if (split == 2) {
+        KDA_C32_FLAGS(2);
+    } else {
+        KDA_C32_FLAGS(1);
+    }
 #undef KDA_C32_FLAGS
 #undef KDA_C32_DT
 #undef KDA_C32

@@ -80,6 +80,15 @@ constexpr int KDA_STATES_ONLY = 4;
 // Internal (the backward's workspace and launch): the caller passes the states at every
 // 32-token boundary, so they are neither recomputed nor held in the workspace.
 constexpr int KDA_BWD_STATES_GIVEN = 8;
+// Internal (the forward cut into segments; one workgroup per run): the grid covers twice the
+// launch's (segment, head) chains, and each chain runs twice, on one XCD.  "Kind 0" runs with its
+// v from the initial state that s0_idx names (a sequence's first segment: its slot, -1 zeros;
+// later segments: -2, zeros): outputs to o, checkpoints as usual, final state N.  "Kind 1" runs
+// with v taken as zero from the identity (d_k = d_v), for later segments only (s0_idx -2): its
+// final state is the segment's transition matrix M = prod_t (I - beta_t k_t k_t^T) Diag(alpha_t),
+// its outputs scale M_t^T q_t go to o_tr and its checkpoints (the partial products) to ckpt_tr.
+// Final states go to sf[(kind * nseq + n) * H + h].  s0_idx is always set.
+constexpr int KDA_TRANSITION = 16;
 
 // ---- MFMA ------------------------------------------------------------------
 // 16x16 output tiles: lane l holds D[4*(l/16) + e][l % 16], e = 0..3.

@@ -208,11 +208,15 @@ struct ChunkParams {
     float *o;
     const int32_t *s0_idx;         // NULL, or the pool slot of each sequence's initial state (-1: zeros)
     const int32_t *ck_idx;         // NULL, or the pool slot of each checkpoint (-1: not written)
-    int nslots;                    // slots of the pool(s) when an index array is set
+    int nslots;                    // slots of the checkpoint pool (ck_idx set)
+    int s0_slots;                  // slots of the initial-state pool (s0_idx set)
     int flags;                     // KDA_PRO_GATE: g, beta are pre-activations; KDA_PRO_NORM: normalise q, k
     int H;
     int every;
     float scale;
+    int nseq;                      // sequences of this launch (the paired segment pass indexes its states by it)
+    float *o_tr;                   // the paired segment pass: outputs of the transition runs, [T, H, dk]
+    float *ckpt_tr;                // the paired segment pass: their checkpoints, dense [M, H, dk, dk]
 };
 
 // Element offset of the initial state of (n, h) in p.s0, or -1 for a zero state (no initial
@@ -222,7 +226,7 @@ __device__ __forceinline__ long long s0_offset(const ChunkParams &p, int n, int 
     long long slot = n;
     if (p.s0_idx) {
         const int s = p.s0_idx[n];
-        if (s < 0 || s >= p.nslots) return -1;
+        if (s < 0 || s >= p.s0_slots) return -1;
         slot = s;
     }
     return (slot * p.H + h) * dkdv;

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5u
+#define KDA_ABI_VERSION 6u
 
 typedef enum {
     KDA_OK = 0,
@@ -138,6 +138,27 @@ typedef enum {
  *                    holds (fp32 q / |q|, k / |k| and v with the normalisation, the rest
  *                    of the forward then computing on fp32 inputs; fp32 g and beta with
  *                    the gate), and kda_chunk_fwd_workspace_bytes includes them.
+ *   segment_tokens   Context parallelism inside the GPU (chunk_size 32 only).  Over a stretch
+ *                    of tokens the state is an affine function of the state it starts from,
+ *                    S_t = M_t S_in + N_t, and so o_t = o0_t + S_in^T (scale M_t^T q_t) (the
+ *                    t.iss.one DNSPODT digest of the K3 report, infrastructure paragraph: KDA's
+ *                    context parallelism exchanges only the fixed-size state).  Each sequence
+ *                    is cut into segments of segment_tokens tokens (from its start; the last
+ *                    may be shorter) that run side by side: every segment from zero and, but a
+ *                    sequence's first (which starts from its initial state), also from the
+ *                    identity with v = 0; a short pass along each sequence then chains the
+ *                    maps into every segment's initial state (and the final state, and
+ *                    corrects the checkpoints), and a last pass adds S_in^T (scale M_t^T q_t)
+ *                    to the later segments' outputs.  About twice the arithmetic, spread over
+ *                    many more compute units: it pays for few, long sequences on few heads.
+ *                    Results equal the uncut forward up to rounding.
+ *                    0: the library decides (it cuts only when the (sequence, head) pairs
+ *                    leave most compute units idle and the longest sequence spans at least
+ *                    three segments).  -1: never cut.  > 0: cut at this length, a multiple
+ *                    of 32 and of checkpoint_every (else KDA_ERR_INVALID_ARGUMENT); chunk_size
+ *                    64 then gives KDA_ERR_UNSUPPORTED.  When cut, the workspace grows by
+ *                    12 d_k d_v bytes per (segment, head), 4 d_k bytes per (token, head) and
+ *                    4 d_k d_v bytes per (checkpoint, head).
  */
 typedef struct {
     uint32_t struct_size;
@@ -166,6 +187,7 @@ typedef struct {
     int32_t num_slots;
     int32_t gate_mode;
     int32_t normalize_qk;
+    int32_t segment_tokens;
 } kda_fwd_args;
 
 /* Device workspace (bytes) that kda_chunk_fwd needs for `args` (host only; no
@@ -186,6 +208,8 @@ kda_status kda_chunk_fwd(const kda_fwd_args *args, void *workspace, size_t works
  *   - At most KDA_NOALLOC_MAX_SEQS sequences, else KDA_ERR_WORKSPACE_TOO_SMALL.
  *   - A prologue (gate_mode / normalize_qk) only where it is fused into the kernel (chunk_size
  *     32 and dk 128), else KDA_ERR_UNSUPPORTED: elsewhere its outputs would need a workspace.
+ *   - Sequences are never cut into segments (segment_tokens 0 and -1 both run uncut; > 0
+ *     gives KDA_ERR_UNSUPPORTED): the segments' states would need a workspace.
  *   - Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (different
  *     streams, no ordering between them) race.  Order them on one stream or with events.
  *   - The first call on a device looks the array's address up (no allocation); make that first

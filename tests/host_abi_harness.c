@@ -112,6 +112,33 @@ int main(void) {
                 expect("fwd noalloc", kda_chunk_fwd_noalloc(&a, NULL),
                        dt != KDA_BF16 ? KDA_ERR_UNSUPPORTED
                                       : (chunk == 32 && dk == 128 ? KDA_ERR_DEVICE : KDA_ERR_UNSUPPORTED));
+                /* sequences cut into segments: plain, with checkpoints and a pool, auto on 3000 */
+                a = fwd(cu, nl, dk, chunk, (kda_dtype)dt);
+                a.segment_tokens = 64;
+                fwd_case("fwd segments", a, chunk == 32 ? KDA_ERR_DEVICE : KDA_ERR_UNSUPPORTED);
+                expect("fwd noalloc segments", kda_chunk_fwd_noalloc(&a, NULL), KDA_ERR_UNSUPPORTED);
+                a.checkpoint_every = 32;
+                a.checkpoints = (float *)FAKE(20);
+                a.initial_state = (const float *)FAKE(21);
+                a.final_state = (float *)FAKE(21);
+                a.initial_state_indices = (const int32_t *)FAKE(22);
+                a.checkpoint_indices = (const int32_t *)FAKE(23);
+                a.num_slots = 9;
+                fwd_case("fwd segments, checkpoints, pool", a,
+                         chunk == 32 ? KDA_ERR_DEVICE : KDA_ERR_INVALID_ARGUMENT);
+                a.segment_tokens = 96;
+                a.checkpoint_every = 64;
+                fwd_case("fwd segment not a checkpoint multiple", a, KDA_ERR_INVALID_ARGUMENT);
+                a = fwd(cu, nl, dk, chunk, (kda_dtype)dt);
+                a.segment_tokens = 48;
+                fwd_case("fwd segment not a chunk multiple", a, KDA_ERR_INVALID_ARGUMENT);
+                a.segment_tokens = -2;
+                fwd_case("fwd segment -2", a, KDA_ERR_INVALID_ARGUMENT);
+                a.segment_tokens = -1;
+                fwd_case("fwd segments off", a, KDA_ERR_DEVICE);
+                a = fwd(cu_many, 3000, dk, chunk, (kda_dtype)dt);
+                a.segment_tokens = 32;
+                fwd_case("fwd 3000 sequences in segments", a, chunk == 32 ? KDA_ERR_DEVICE : KDA_ERR_UNSUPPORTED);
             }
     kda_fwd_args a = fwd(cu, nl, 128, 32, KDA_BF16);
     fwd_case("fwd empty batch", fwd(cu_empty, 0, 128, 32, KDA_BF16), KDA_OK);

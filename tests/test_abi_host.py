@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert kda.kda_abi_version() == 5 == kda.ABI_VERSION
+    assert kda.kda_abi_version() == 6 == kda.ABI_VERSION
     for code, name in enumerate(["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
                                  "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_DEVICE"]):
         assert kda.kda_status_str(code) == name
@@ -361,3 +361,38 @@ def test_noalloc_refuses_a_prologue_that_needs_a_workspace(L):
 def test_noalloc_empty_batch_is_a_no_op(L):
     a, keep = fwd_args(cu=[0])
     assert L.kda_chunk_fwd_noalloc(ctypes.byref(a), None) == kda.KDA_OK
+
+
+def test_segment_choice(L):
+    """The library cuts sequences into segments (segment_tokens 0) only when the (sequence, head)
+    pairs leave most of the chip idle and the longest sequence spans at least 3 segments; the
+    workspace then holds 3 states per (segment, head) (the two runs' final states, the entry state)
+    and the transition runs' outputs (4 dk bytes per token and head) on top of the segments' plan.
+    Without a GPU the library assumes 256 compute units."""
+    state = 128 * 128 * 4
+
+    def ws(cu, H, **over):
+        a, keep = fwd_args(cu=cu, num_heads=H, chunk_size=32, **over)
+        return L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a))
+
+    one = [0, 4096]
+    # 4,096 tokens on 32 heads: 256 / (2 * 32) = 4 segments of 1,024 tokens
+    assert ws(one, 32) >= ws(one, 32, segment_tokens=-1) + 4 * 32 * 3 * state + 4096 * 32 * 128 * 4
+    assert ws(one, 32) == ws(one, 32, segment_tokens=1024)
+    # 96 heads fill the chip with two workgroups per pair: no cut; nor for 64 sequences x 32 heads
+    assert ws(one, 96) == ws(one, 96, segment_tokens=-1)
+    many = list(range(0, 65 * 512, 512))
+    assert ws(many, 32) == ws(many, 32, segment_tokens=-1)
+    # too short to gain: 1,024 tokens would give 512-token segments, only 2 of them
+    assert ws([0, 1024], 32) == ws([0, 1024], 32, segment_tokens=-1)
+    # 1M tokens on 2 heads: 64 segments of 16,384 tokens
+    big = [0, 1 << 20]
+    assert ws(big, 2) == ws(big, 2, segment_tokens=16384) > ws(big, 2, segment_tokens=-1) + 64 * 2 * 3 * state
+    # explicit cuts: the workspace grows with the number of segments
+    assert ws(one, 32, segment_tokens=512) > ws(one, 32, segment_tokens=1024)
+    # chunk 64 does not cut by itself, and refuses an explicit cut
+    a, keep = fwd_args(cu=one, num_heads=32)
+    b, keep2 = fwd_args(cu=one, num_heads=32, segment_tokens=-1)
+    assert L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == L.kda_chunk_fwd_workspace_bytes(ctypes.byref(b))
+    a, keep = fwd_args(cu=one, num_heads=32, segment_tokens=1024)
+    assert status(L, a) == kda.KDA_ERR_UNSUPPORTED

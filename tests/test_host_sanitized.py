@@ -15,7 +15,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "gated_delta_rule_49_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["kda_api.hip", "kda_chunk.hip", "kda_chunk32.hip", "kda_decode.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.hip", "kda_chunk.hip", "kda_chunk32.hip", "kda_segments.hip", "kda_decode.hip", "kda_bwd.hip"]
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=all"]
 
