@@ -4,7 +4,8 @@ implementation of the Kimi Delta Attention (KDA) operator.
 This module only marshals arguments: it takes torch tensors for device memory
 and the current HIP stream, and calls the C ABI declared in ``include/kda.h``
 (same names: ``kda_chunk_fwd``, ``kda_chunk_bwd``, ``kda_decode_step``,
-``kda_chunk_fwd_workspace_bytes``, ``kda_chunk_bwd_workspace_bytes``, ``kda_status_str``,
+``kda_chunk_fwd_workspace_bytes``, ``kda_chunk_bwd_workspace_bytes``,
+``kda_chunk_bwd_workspace_min_bytes``, ``kda_status_str``,
 ``kda_abi_version``).
 Every step of the computation runs in the library's HIP kernels; there is no
 fallback of any kind -- if ``libkda.so`` is missing or fails to load, every
@@ -68,10 +69,11 @@ class KdaBwdArgs(ctypes.Structure):
 
 
 EXPORTED = ["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_noalloc", "kda_chunk_bwd",
-            "kda_chunk_bwd_workspace_bytes", "kda_decode_step", "kda_status_str", "kda_abi_version"]
+            "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd_workspace_min_bytes", "kda_decode_step",
+            "kda_status_str", "kda_abi_version"]
 NOALLOC_MAX_SEQS = 65536   # KDA_NOALLOC_MAX_SEQS of include/kda.h
 
-ABI_VERSION = 6   # KDA_ABI_VERSION of include/kda.h, whose struct layouts the ctypes classes above mirror
+ABI_VERSION = 7   # KDA_ABI_VERSION of include/kda.h, whose struct layouts the ctypes classes above mirror
 _lib = None
 _lock = threading.Lock()
 
@@ -97,6 +99,8 @@ def lib():
             L.kda_chunk_bwd.restype = ctypes.c_int
             L.kda_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(KdaBwdArgs)]
             L.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+            L.kda_chunk_bwd_workspace_min_bytes.argtypes = [ctypes.POINTER(KdaBwdArgs)]
+            L.kda_chunk_bwd_workspace_min_bytes.restype = ctypes.c_size_t
             L.kda_decode_step.argtypes = [ctypes.POINTER(KdaDecodeArgs), ctypes.c_void_p]
             L.kda_decode_step.restype = ctypes.c_int
             L.kda_status_str.argtypes = [ctypes.c_int]
@@ -389,7 +393,7 @@ def make_bwd_args(q, k, v, g, beta, cu_dev, cu_host, scale, initial_state, d_o, 
 
 def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_state=None, d_final_state=None,
                   output_d_initial_state=True, stream=None, workspace=None, gate_preactivation=False,
-                  normalize_qk=False, states=None):
+                  normalize_qk=False, states=None, workspace_cap=None):
     """Backward of kda_chunk_fwd: gradients of L = sum(d_o * o) + sum(d_final_state * final_state).
 
     Inputs as for kda_chunk_fwd (with gate_preactivation / normalize_qk as there: g, beta are then
@@ -398,7 +402,9 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_sta
     None (zeros).  workspace: optional uint8 CUDA tensor of at least the queried size (reused by
     callers that run the backward repeatedly).  states: the forward's checkpoints with
     checkpoint_every=32 (fp32 [sum floor(L/32), H, dk, dv]) to read instead of recomputing them, or
-    None.  Returns (dq, dk, dv, dg, dbeta, d_initial_state or None), all fp32."""
+    None.  workspace_cap: when the workspace is allocated here, at most this many bytes (never less
+    than the library's minimum, the longest sequence's): the library then runs the batch in groups
+    of sequences that fit.  Returns (dq, dk, dv, dg, dbeta, d_initial_state or None), all fp32."""
     _require_device(q)
     T, H, dk = q.shape
     dv = v.shape[2]
@@ -419,7 +425,9 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_sta
         _check(L.kda_chunk_bwd(ctypes.byref(a), None, 0, _stream(stream)))
     if workspace is not None:
         _tensor("workspace", workspace, dev, None, (torch.uint8,))
-    if workspace is None or workspace.numel() < ws_bytes:
+    if workspace is None:
+        if workspace_cap is not None:
+            ws_bytes = min(ws_bytes, max(int(workspace_cap), int(L.kda_chunk_bwd_workspace_min_bytes(ctypes.byref(a)))))
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     _check(L.kda_chunk_bwd(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                            ctypes.c_size_t(workspace.numel()), _stream(stream)))

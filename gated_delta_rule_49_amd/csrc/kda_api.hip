@@ -33,6 +33,7 @@ extern "C" hipError_t kda_launch_prologue(int dk, long long rows, int flags, con
                                           float *vf, float *g, float *beta, hipStream_t stream);
 extern "C" size_t kda_bwd_workspace_layout(int N, int H, int T, int dk, int dv, int64_t n_ck, int64_t n_chunks,
                                            int flags, size_t *off);
+extern "C" hipError_t kda_launch_cu_rebase(const int32_t *cu, int first, int n, int32_t *out, hipStream_t stream);
 extern "C" hipError_t kda_launch_bwd(int dk, int in_bf16, int N, int H, int T, int64_t n_ck, int64_t n_chunks,
                                      const void *q, const void *k, const void *v, const float *g, const float *beta,
                                      const int32_t *cu, const float *s0, const float *dO, const float *dSf, float *dq,
@@ -234,6 +235,20 @@ int bwd_flags(const kda_bwd_args *a) {
     return (a->gate_mode == KDA_GATE_PREACTIVATION ? 1 : 0) | (a->normalize_qk ? 2 : 0) | (a->states ? 8 : 0);
 }
 
+// Workspace of the backward of sequences [first, last) run as a group of their own: its layout
+// plus their offsets rebased to the group's first token.  Validated arguments only.
+size_t bwd_group_bytes(const kda_bwd_args *a, int first, int last) {
+    const int32_t *cu = a->cu_seqlens_host;
+    int64_t ck = 0, ch = 0;
+    for (int n = first; n < last; ++n) {
+        ck += (cu[n + 1] - cu[n]) / 32;
+        ch += (cu[n + 1] - cu[n] + 31) / 32;
+    }
+    const size_t body = kda_bwd_workspace_layout(last - first, a->num_heads, cu[last] - cu[first], a->dk, a->dv, ck,
+                                                 ch, bwd_flags(a), nullptr);
+    return (body + 255) / 256 * 256 + ((size_t)(last - first + 1) * 4 + 255) / 256 * 256;
+}
+
 // ---- scratch of the allocation-free forward ------------------------------------------------
 // kda_chunk_fwd_noalloc keeps its launch plan (sequence order, int32 [N] padded to 256 B, then
 // per-sequence checkpoint bases, int64 [N] padded to 256 B, then 256 B) in this file-scope
@@ -359,6 +374,19 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_bwd_args *a) {
                                     nullptr);
 }
 
+size_t kda_chunk_bwd_workspace_min_bytes(const kda_bwd_args *a) {
+    int64_t ck, ch;
+    if (validate_bwd(a, &ck, &ch) != KDA_OK) return 0;
+    const size_t full = kda_bwd_workspace_layout(a->num_seqs, a->num_heads, a->total_tokens, a->dk, a->dv, ck, ch,
+                                                 bwd_flags(a), nullptr);
+    size_t least = 0;
+    for (int n = 0; n < a->num_seqs; ++n) {
+        const size_t need = bwd_group_bytes(a, n, n + 1);
+        least = need > least ? need : least;
+    }
+    return least < full ? least : full;
+}
+
 kda_status kda_chunk_bwd(const kda_bwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
     int64_t ck = 0, ch = 0;
     const kda_status st = validate_bwd(a, &ck, &ch);
@@ -366,14 +394,64 @@ kda_status kda_chunk_bwd(const kda_bwd_args *a, void *workspace, size_t workspac
     if (a->num_seqs == 0) return KDA_OK;
     const size_t need = kda_bwd_workspace_layout(a->num_seqs, a->num_heads, a->total_tokens, a->dk, a->dv, ck, ch,
                                                  bwd_flags(a), nullptr);
-    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace) return KDA_ERR_WORKSPACE_TOO_SMALL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_INVALID_ARGUMENT;
-    const hipError_t e = kda_launch_bwd(a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads, a->total_tokens,
-                                        ck, ch, a->q, a->k, a->v, a->g, a->beta, a->cu_seqlens, a->initial_state,
-                                        a->d_o, a->d_final_state, a->dq, a->dk_out, a->dv_out, a->dg, a->dbeta,
-                                        a->d_initial_state, a->scale, a->states, bwd_flags(a) & 3, workspace,
-                                        static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
+    const hipStream_t sm = static_cast<hipStream_t>(stream);
+    if (workspace_bytes >= need) {
+        const hipError_t e = kda_launch_bwd(a->dk, a->in_dtype == KDA_BF16, a->num_seqs, a->num_heads,
+                                            a->total_tokens, ck, ch, a->q, a->k, a->v, a->g, a->beta, a->cu_seqlens,
+                                            a->initial_state, a->d_o, a->d_final_state, a->dq, a->dk_out, a->dv_out,
+                                            a->dg, a->dbeta, a->d_initial_state, a->scale, a->states,
+                                            bwd_flags(a) & 3, workspace, sm);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
+    }
+    // A smaller workspace: consecutive groups of whole sequences, each within it, one after the
+    // other on the stream (the sequences are independent; each group is the same computation).
+    const int N = a->num_seqs;
+    for (int n = 0; n < N; ++n)
+        if (bwd_group_bytes(a, n, n + 1) > workspace_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    const int32_t *cu = a->cu_seqlens_host;
+    const int H = a->num_heads, dk = a->dk, dv = a->dv;
+    const size_t in_es = a->in_dtype == KDA_BF16 ? 2 : 4;
+    const size_t g_es = a->gate_mode == KDA_GATE_PREACTIVATION ? 2 : 4;   // bf16 pre-activations a
+    const size_t state = (size_t)H * dk * dv;
+    auto shift = [](const void *p, size_t bytes) -> const void * {
+        return p ? static_cast<const char *>(p) + bytes : nullptr;
+    };
+    auto shiftf = [](float *p, size_t elems) { return p ? p + elems : nullptr; };
+    int64_t ck_before = 0;
+    for (int first = 0; first < N;) {
+        int last = first + 1;
+        while (last < N && bwd_group_bytes(a, first, last + 1) <= workspace_bytes) ++last;
+        const int Ng = last - first;
+        const size_t t0 = (size_t)cu[first];
+        const int Tg = cu[last] - cu[first];
+        int64_t ckg = 0, chg = 0;
+        for (int n = first; n < last; ++n) {
+            ckg += (cu[n + 1] - cu[n]) / 32;
+            chg += (cu[n + 1] - cu[n] + 31) / 32;
+        }
+        const size_t body = kda_bwd_workspace_layout(Ng, H, Tg, dk, dv, ckg, chg, bwd_flags(a), nullptr);
+        int32_t *cu_g = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + (body + 255) / 256 * 256);
+        hipError_t e = kda_launch_cu_rebase(a->cu_seqlens, first, Ng, cu_g, sm);
+        if (e == hipSuccess)
+            e = kda_launch_bwd(dk, a->in_dtype == KDA_BF16, Ng, H, Tg, ckg, chg, shift(a->q, t0 * H * dk * in_es),
+                               shift(a->k, t0 * H * dk * in_es), shift(a->v, t0 * H * dv * in_es),
+                               static_cast<const float *>(shift(a->g, t0 * H * dk * g_es)),
+                               static_cast<const float *>(shift(a->beta, t0 * H * 4)), cu_g,
+                               static_cast<const float *>(shift(a->initial_state, first * state * 4)),
+                               static_cast<const float *>(shift(a->d_o, t0 * H * dv * 4)),
+                               static_cast<const float *>(shift(a->d_final_state, first * state * 4)),
+                               shiftf(a->dq, t0 * H * dk), shiftf(a->dk_out, t0 * H * dk), shiftf(a->dv_out, t0 * H * dv),
+                               shiftf(a->dg, t0 * H * dk), shiftf(a->dbeta, t0 * H),
+                               shiftf(a->d_initial_state, first * state), a->scale,
+                               static_cast<const float *>(shift(a->states, (size_t)ck_before * state * 4)),
+                               bwd_flags(a) & 3, workspace, sm);
+        if (e != hipSuccess) return KDA_ERR_DEVICE;
+        ck_before += ckg;
+        first = last;
+    }
+    return KDA_OK;
 }
 
 kda_status kda_decode_step(const kda_decode_args *a, void *stream) {

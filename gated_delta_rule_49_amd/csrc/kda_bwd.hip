@@ -1046,6 +1046,19 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_prologue(
     return hipGetLastError();
 }
 
+// out[i] = cu[first + i] - cu[first], i = 0 .. n: a group's sequence offsets from its first token.
+__global__ void __launch_bounds__(256) cu_rebase_kernel(const int32_t *__restrict__ cu, int first, int n,
+                                                        int32_t *__restrict__ out) {
+    const int32_t base = cu[first];
+    for (int i = (int)threadIdx.x; i <= n; i += blockDim.x) out[i] = cu[first + i] - base;
+}
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_cu_rebase(const int32_t *cu, int first, int n,
+                                                                                int32_t *out, hipStream_t stream) {
+    hipLaunchKernelGGL(cu_rebase_kernel, dim3(1), dim3(256), 0, stream, cu, first, n, out);
+    return hipGetLastError();
+}
+
 extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     int dk, int in_bf16, int N, int H, int T, int64_t n_ck, int64_t n_chunks, const void *q, const void *k,
     const void *v, const float *g, const float *beta, const int32_t *cu, const float *s0, const float *dO,

@@ -125,6 +125,11 @@ __device__ __forceinline__ f32x4_t chain_mma(const float (&a)[D / 4], const floa
     for (int e = 0; e < 4; ++e) c[e] += d[e];
     return c;
 }
+// S_in as the correction reads it: S^T split into bf16 hi and lo planes, [column][k] with rows
+// padded to D + 8 (per segment and head: [2][D][D + 8] bf16, as many bytes as fp32 S plus the pad).
+template <int D> constexpr int sin_pitch() { return D + 8; }
+template <int D> constexpr size_t sin_elems() { return (size_t)2 * D * sin_pitch<D>(); }
+
 template <int D>
 __device__ __forceinline__ int chain_lds_row(int r) {
     return 4 * (r % (D / 4)) + r / (D / 4);
@@ -132,14 +137,14 @@ __device__ __forceinline__ int chain_lds_row(int r) {
 
 // The chain along each sequence's segments, for one (sequence, head) and 16 value columns per
 // workgroup (D / 16 waves, one 16-row tile each).  st: [2][NB][H][D][D] (kind 0: N, kind 1: M).
-// Writes S_in of every later segment to sin_ ([NB][H][D][D]), corrects its checkpoints
+// Writes S_in of every later segment to sin_ ([NB][H] x sin_elems, the correction's layout), corrects its checkpoints
 // (ckpt[m] += M_m S_in, M_m from ckI, dense [M][H][D][D]) and writes the final state.  The next
 // step's M and N are loaded while the current step's products run.
 template <int D>
 __global__ void __launch_bounds__(512)
 segment_chain_kernel(const int32_t *__restrict__ info, const int32_t *__restrict__ cuB,
                      const int64_t *__restrict__ ckb, int H, int NB, int every, const float *__restrict__ st,
-                     float *__restrict__ sin_, float *sf, float *ckpt, const int32_t *__restrict__ ck_idx,
+                     __bf16 *__restrict__ sin_, float *sf, float *ckpt, const int32_t *__restrict__ ck_idx,
                      int nslots, const float *__restrict__ ckI) {
     __shared__ __attribute__((aligned(16))) float S[D * 16];
     constexpr int CB = D / 16;
@@ -171,9 +176,18 @@ segment_chain_kernel(const int32_t *__restrict__ info, const int32_t *__restrict
         const int sg = b + p;
         f32x4_t next = s;
         if (act) {
-            float *si = sin_ + ((size_t)sg * H + h) * per + tile;
+            {   // rows 16 w + 4 lq .. + 3 of column c0 + lr: 4 adjacent k of S^T, hi and lo
+                __bf16 *si = sin_ + ((size_t)sg * H + h) * sin_elems<D>() + (size_t)(c0 + lr) * sin_pitch<D>() +
+                             16 * w + 4 * lq;
+                __attribute__((ext_vector_type(4))) __bf16 hi, lo;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) si[e * D] = s[e];
+                for (int e = 0; e < 4; ++e) {
+                    hi[e] = (__bf16)s[e];
+                    lo[e] = (__bf16)(s[e] - (float)hi[e]);
+                }
+                *reinterpret_cast<decltype(hi) *>(si) = hi;
+                *reinterpret_cast<decltype(lo) *>(si + (size_t)D * sin_pitch<D>()) = lo;
+            }
             if (every > 0) {
                 const int nck = (cuB[sg + 1] - cuB[sg]) / every;
                 for (int j = 0; j < nck; ++j) {
@@ -226,26 +240,29 @@ segment_chain_kernel(const int32_t *__restrict__ info, const int32_t *__restrict
 }
 
 // Output correction of the later segments: o_t += S_in^T r_t, r_t = scale M_t^T q_t (the transition
-// runs' outputs, oI [T][H][D]).  Workgroup (segment s, token tile j, head h): tokens cuB[s] + 128 j
-// .. + 127, wave w of 8 taking 16 of them; two workgroups fit a compute unit, so one's loads overlap
-// the other's products.  Each wave loads its rows of oI and o first, so that their latency
-// overlaps the staging of S_in.  The product is formed transposed, out[c][t] = sum_k S[k][c]
+// runs' outputs, oI [T][H][D]).  Workgroup (segment s, token tile j, head h): tokens cuB[s] + 16 NW j
+// .. + 16 NW - 1, wave w of NW taking 16 of them.  Each wave loads its rows of oI and o first, and
+// every thread issues all its loads of S_in before converting any, so that one round trip covers
+// the workgroup's loads.  The product is formed transposed, out[c][t] = sum_k S[k][c]
 // r_t[k] (S_in^T from LDS as the A operand, r_t as the B operand), so that each lane ends up with
 // 4 adjacent columns of one token: o moves as 16-byte vectors.  bf16 MFMA 16x16x32 in three terms
 // (hi hi + hi lo + lo hi, each operand split as x = hi + lo): about 16 significant bits, the fp32
 // bar's precision.  S_in sits in LDS transposed, [column][k], hi and lo planes, rows padded to
 // D + 8 (the 16 lanes of an operand read then start 4 banks apart).
-constexpr int CORR_TOKENS = 128;
-template <int D>
-__global__ void __launch_bounds__(512)
+constexpr int CORR_WAVES = 8;   // waves (16 tokens each) of a correction workgroup
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW)
 segment_correct_kernel(const int32_t *__restrict__ cuB, const int32_t *__restrict__ s0map, int H, int tiles,
-                       const float *__restrict__ sin_, const float *__restrict__ oI, float *__restrict__ o) {
-    constexpr int KP = D + 8, KS = D / 32, CT = D / 16;
-    __shared__ __attribute__((aligned(16))) __bf16 SH[D * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 SL[D * KP];
+                       const __bf16 *__restrict__ sin_, const float *__restrict__ oI, float *__restrict__ o) {
+    constexpr int KP = D + 8, KS = D / 32, CT = D / 16, TT = 16 * NW;
+    static_assert(KP == sin_pitch<D>(), "LDS rows as stored");
+    constexpr int NV = (int)(sin_elems<D>() * 2 / 16);   // 16-byte vectors of S_in
+    constexpr int VEC = (NV + 64 * NW - 1) / (64 * NW);
+    __shared__ __attribute__((aligned(16))) __bf16 SH[2 * D * KP];   // hi plane, then lo plane
+    __bf16 *const SL = SH + D * KP;
     const int s = (int)blockIdx.x / tiles, j = (int)blockIdx.x % tiles, h = (int)blockIdx.y;
     if (s0map[s] != -2) return;   // a first segment: its outputs are final
-    const int t_beg = cuB[s] + CORR_TOKENS * j, t_end = min(cuB[s + 1], t_beg + CORR_TOKENS);
+    const int t_beg = cuB[s] + TT * j, t_end = min(cuB[s + 1], t_beg + TT);
     if (t_beg >= t_end) return;
     const int w = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
     const int t = t_beg + 16 * w + lr;   // this lane's token
@@ -272,18 +289,20 @@ segment_correct_kernel(const int32_t *__restrict__ cuB, const int32_t *__restric
         acc[ct][0] = y.x; acc[ct][1] = y.y; acc[ct][2] = y.z; acc[ct][3] = y.w;
     }
     // S_in -> LDS
-    const float *Sg = sin_ + ((size_t)s * H + h) * D * D;
-    for (int it = (int)threadIdx.x; it < D * (D / 8); it += blockDim.x) {
-        const int c = it % D, kg = it / D;   // column c, k = 8 kg .. 8 kg + 7
-        bf16x8_t hi, lo;
+    {   // S_in (already split and transposed) -> LDS: a straight copy of 16-byte vectors
+        const uint4 *src = reinterpret_cast<const uint4 *>(sin_ + ((size_t)s * H + h) * sin_elems<D>());
+        uint4 *dst = reinterpret_cast<uint4 *>(SH);
+        uint4 y[VEC];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float y = Sg[(size_t)(8 * kg + i) * D + c];
-            hi[i] = (__bf16)y;
-            lo[i] = (__bf16)(y - (float)hi[i]);
+        for (int q = 0; q < VEC; ++q) {
+            const int i = (int)threadIdx.x + 64 * NW * q;
+            y[q] = i < NV ? src[i] : make_uint4(0u, 0u, 0u, 0u);
         }
-        *reinterpret_cast<bf16x8_t *>(&SH[c * KP + 8 * kg]) = hi;
-        *reinterpret_cast<bf16x8_t *>(&SL[c * KP + 8 * kg]) = lo;
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) {
+            const int i = (int)threadIdx.x + 64 * NW * q;
+            if (i < NV) dst[i] = y[q];
+        }
     }
     __syncthreads();
     if (t_beg + 16 * w >= t_end) return;
@@ -323,7 +342,7 @@ extern "C" hipError_t kda_launch_chunk32(int dk, int in_bf16, unsigned grid, con
 // Workspace of the segmented forward: N sequences cut into NB segments, H heads, d = dk = dv, T
 // tokens, nck checkpoints.  off[0] order int32 [NB]; off[1] checkpoint bases int64 [NB]; off[2]
 // initial-state map int32 [NB]; off[3] cuB int32 [NB + 1]; off[4] info int32 [2 N]; off[5] the runs'
-// final states fp32 [2][NB][H][d][d]; off[6] S_in fp32 [NB][H][d][d]; off[7] the transition runs'
+// final states fp32 [2][NB][H][d][d]; off[6] S_in bf16 [NB][H][2][d][d + 8]; off[7] the transition runs'
 // outputs fp32 [T][H][d]; off[8] their checkpoints fp32 [nck][H][d][d]; off[9] the end.
 extern "C" __attribute__((visibility("hidden"))) size_t
 kda_segments_workspace_layout(int N, int NB, int H, int d, int T, int64_t nck, size_t *off) {
@@ -337,7 +356,7 @@ kda_segments_workspace_layout(int N, int NB, int H, int d, int T, int64_t nck, s
     o[4] = o[3] + up((size_t)(NB + 1) * 4);
     o[5] = o[4] + up((size_t)N * 2 * 4);
     o[6] = o[5] + up(2 * (size_t)NB * H * state);
-    o[7] = o[6] + up((size_t)NB * H * state);
+    o[7] = o[6] + up((size_t)NB * H * (size_t)2 * d * (d + 8) * 2);   // S_in, split and transposed
     o[8] = o[7] + up((size_t)T * H * d * 4);
     o[9] = o[8] + up((size_t)nck * H * state);
     if (off)
@@ -362,7 +381,7 @@ kda_launch_chunk_segmented(int dk, int in_bf16, int N, int H, int T, int seg, in
     int32_t *cuB = reinterpret_cast<int32_t *>(ws + off[3]);
     int32_t *info = reinterpret_cast<int32_t *>(ws + off[4]);
     float *st = reinterpret_cast<float *>(ws + off[5]);
-    float *sin_ = reinterpret_cast<float *>(ws + off[6]);
+    __bf16 *sin_ = reinterpret_cast<__bf16 *>(ws + off[6]);
     float *oI = reinterpret_cast<float *>(ws + off[7]);
     float *ckI = reinterpret_cast<float *>(ws + off[8]);
     const int s0_slots = s0_idx ? nslots : N;
@@ -389,13 +408,14 @@ kda_launch_chunk_segmented(int dk, int in_bf16, int N, int H, int T, int seg, in
     e = hipGetLastError();
     if (e != hipSuccess || NB == N) return e;   // NB == N: every segment is a first one
     // 4. the outputs of the later segments
-    const int tiles = (seg + kda::CORR_TOKENS - 1) / kda::CORR_TOKENS;
+    constexpr int NW = kda::CORR_WAVES;
+    const int tiles = (seg + 16 * NW - 1) / (16 * NW);
     const dim3 grid((unsigned)NB * tiles, (unsigned)H);
     if (dk == 128)
-        hipLaunchKernelGGL(kda::segment_correct_kernel<128>, grid, dim3(512), 0, stream, cuB, s0map, H, tiles, sin_,
-                           oI, o);
+        hipLaunchKernelGGL((kda::segment_correct_kernel<128, NW>), grid, dim3(64 * NW), 0, stream, cuB, s0map, H, tiles,
+                           sin_, oI, o);
     else
-        hipLaunchKernelGGL(kda::segment_correct_kernel<64>, grid, dim3(512), 0, stream, cuB, s0map, H, tiles, sin_,
-                           oI, o);
+        hipLaunchKernelGGL((kda::segment_correct_kernel<64, NW>), grid, dim3(64 * NW), 0, stream, cuB, s0map, H, tiles,
+                           sin_, oI, o);
     return hipGetLastError();
 }

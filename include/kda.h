@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6u
+#define KDA_ABI_VERSION 7u
 
 typedef enum {
     KDA_OK = 0,
@@ -339,12 +339,22 @@ typedef struct {
     const float *states;
 } kda_bwd_args;
 
-/* Device workspace (bytes) that kda_chunk_bwd needs for `args` (host only).
+/* Device workspace (bytes) with which kda_chunk_bwd runs the whole batch at once (host only).
  * Returns 0 when args are invalid. */
 size_t kda_chunk_bwd_workspace_bytes(const kda_bwd_args *args);
 
-/* Enqueue the backward.  `workspace`: at least kda_chunk_bwd_workspace_bytes(args)
- * bytes of device memory, 256-byte aligned, overwritten. */
+/* The least workspace kda_chunk_bwd accepts (host only): that of the batch's longest single
+ * sequence run alone (at most kda_chunk_bwd_workspace_bytes).  Returns 0 when args are invalid. */
+size_t kda_chunk_bwd_workspace_min_bytes(const kda_bwd_args *args);
+
+/* Enqueue the backward.  `workspace`: device memory, 256-byte aligned, overwritten, of
+ * workspace_bytes >= kda_chunk_bwd_workspace_min_bytes(args) (else
+ * KDA_ERR_WORKSPACE_TOO_SMALL).  With less than kda_chunk_bwd_workspace_bytes(args) the batch
+ * runs as consecutive groups of whole sequences, each group the most that fits, one after
+ * the other on `stream` (the sequences are independent; each group performs the same
+ * computation, so results differ from the one-pass run only where the forward recompute
+ * chooses another split of its work: by rounding).  This bounds the memory of a large batch
+ * (the workspace of a whole batch grows with its tokens times heads). */
 kda_status kda_chunk_bwd(const kda_bwd_args *args, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static string for a status code. */

@@ -199,6 +199,21 @@ int main(void) {
             expect("bwd aliased outputs", kda_chunk_bwd(&b, FAKE(64), 1 << 20, NULL), KDA_ERR_INVALID_ARGUMENT);
             b = bwd(cu, nl, dk, (kda_dtype)dt);
             expect("bwd small workspace", kda_chunk_bwd(&b, FAKE(64), 64, NULL), KDA_ERR_WORKSPACE_TOO_SMALL);
+            {   /* groups of sequences within a smaller workspace, with and without given states */
+                b = bwd(cu, nl, dk, (kda_dtype)dt);
+                const size_t full = kda_chunk_bwd_workspace_bytes(&b), least = kda_chunk_bwd_workspace_min_bytes(&b);
+                expect("bwd min <= full", least <= full && least > 0, 1);
+                expect("bwd groups", kda_chunk_bwd(&b, FAKE(64), least, NULL), KDA_ERR_DEVICE);
+                expect("bwd below min", kda_chunk_bwd(&b, FAKE(64), least - 256, NULL), KDA_ERR_WORKSPACE_TOO_SMALL);
+                b = bwd(cu_many, 3000, dk, (kda_dtype)dt);
+                b.initial_state = (const float *)FAKE(21);
+                b.d_final_state = (const float *)FAKE(24);
+                b.d_initial_state = (float *)FAKE(25);
+                b.states = (const float *)FAKE(26);
+                b.gate_mode = dt == KDA_BF16 ? KDA_GATE_PREACTIVATION : KDA_GATE_LOG_DECAY;
+                expect("bwd 3000 sequences in groups",
+                       kda_chunk_bwd(&b, FAKE(64), kda_chunk_bwd_workspace_min_bytes(&b) * 7, NULL), KDA_ERR_DEVICE);
+            }
         }
     {
         kda_bwd_args b = bwd(cu_empty, 0, 128, KDA_BF16);

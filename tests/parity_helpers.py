@@ -5,6 +5,18 @@ import multiprocessing as mp
 import numpy as np
 
 
+def sum_sq(x, rows=1 << 16):
+    """sum(x^2) of a torch tensor in fp64, a slice of the first axis at a time (the whole tensor
+    in fp64 may not fit the device)."""
+    return sum(float((x[i:i + rows].double() ** 2).sum()) for i in range(0, x.shape[0], rows)) if x.numel() else 0.0
+
+
+def dot(a, b, rows=1 << 16):
+    """sum(a * b) of two torch tensors of one shape in fp64, a slice of the first axis at a time."""
+    assert a.shape == b.shape
+    return sum(float((a[i:i + rows].double() * b[i:i + rows].double()).sum()) for i in range(0, a.shape[0], rows))
+
+
 def identity_bar(terms, sigmas=6.0):
     """Bar for |sum_i <a_i, b_i> - sum_j <c_j, d_j>| when each GPU-computed tensor a carries an
     elementwise error of size at most e_a * RMS(a) (e_a: its measured max|diff| / RMS against the
@@ -20,8 +32,8 @@ def identity_bar(terms, sigmas=6.0):
             a64, b64 = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
             rms_a, l2_b = math.sqrt(float(np.mean(a64 * a64))), math.sqrt(float(np.sum(b64 * b64)))
         else:
-            rms_a = math.sqrt(float((a.double() ** 2).mean()))
-            l2_b = math.sqrt(float((b.double() ** 2).sum()))
+            rms_a = math.sqrt(sum_sq(a) / a.numel())
+            l2_b = math.sqrt(sum_sq(b))
         tot += e * rms_a * l2_b
     return sigmas * tot
 

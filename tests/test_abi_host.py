@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert kda.kda_abi_version() == 6 == kda.ABI_VERSION
+    assert kda.kda_abi_version() == 7 == kda.ABI_VERSION
     for code, name in enumerate(["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
                                  "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_DEVICE"]):
         assert kda.kda_status_str(code) == name
@@ -298,7 +298,9 @@ def test_bwd_prologue_workspace(L):
     need = L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a))
     rows = 228 * 4
     assert need >= base + rows * (3 * 128 * 4 + 128 * 4 + 4)
-    assert bwd_status(L, a, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd_status(L, a, ws_bytes=need - 1) == kda.KDA_ERR_DEVICE   # groups of sequences
+    assert bwd_status(L, a, ws_bytes=L.kda_chunk_bwd_workspace_min_bytes(ctypes.byref(a)) - 1) == \
+        kda.KDA_ERR_WORKSPACE_TOO_SMALL
     g, keep2 = bwd_args(gate_mode=kda.KDA_GATE_PREACTIVATION)
     n, keep3 = bwd_args(normalize_qk=1)
     assert base < L.kda_chunk_bwd_workspace_bytes(ctypes.byref(g)) < need
@@ -312,7 +314,8 @@ def test_bwd_given_states_workspace(L):
     need = L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a))
     n_ck = 100 // 32 + 128 // 32
     assert need <= base - n_ck * 4 * 128 * 128 * 4
-    assert bwd_status(L, a, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd_status(L, a, ws_bytes=L.kda_chunk_bwd_workspace_min_bytes(ctypes.byref(a)) - 1) == \
+        kda.KDA_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_bwd_workspace(L):
@@ -322,7 +325,8 @@ def test_bwd_workspace(L):
     # checkpoints (7) and per chunk (8): D, W, E, A and T
     expect = (7 * 4 * 128 * 128 + 8 * 4 * (128 * 128 + 2 * 32 * 128 + 2 * 32 * 32)) * 4
     assert need % 256 == 0 and need >= expect
-    assert bwd_status(L, a, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd_status(L, a, ws_bytes=L.kda_chunk_bwd_workspace_min_bytes(ctypes.byref(a)) - 1) == \
+        kda.KDA_ERR_WORKSPACE_TOO_SMALL
     assert bwd_status(L, a, ws=0, ws_bytes=need) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
     assert bwd_status(L, a, ws=FAKE * 64 + 128, ws_bytes=need) == kda.KDA_ERR_INVALID_ARGUMENT
     b, keep2 = bwd_args(cu=[0])
@@ -396,3 +400,26 @@ def test_segment_choice(L):
     assert L.kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) == L.kda_chunk_fwd_workspace_bytes(ctypes.byref(b))
     a, keep = fwd_args(cu=one, num_heads=32, segment_tokens=1024)
     assert status(L, a) == kda.KDA_ERR_UNSUPPORTED
+
+
+def test_bwd_workspace_groups(L):
+    """A workspace below the whole batch's need, but at least the longest sequence's, is accepted:
+    the batch then runs in groups of whole sequences (here the launch itself fails: no GPU).  The
+    minimum is the longest sequence's own need, so it grows with that sequence, not the batch."""
+    cu = [0, 100, 4196, 4228, 4228, 4356]   # lengths 100, 4096, 32, 0, 128
+    a, keep = bwd_args(cu=cu)
+    full = L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a))
+    least = L.kda_chunk_bwd_workspace_min_bytes(ctypes.byref(a))
+    b, keep2 = bwd_args(cu=[0, 4096])
+    alone = L.kda_chunk_bwd_workspace_bytes(ctypes.byref(b))
+    assert 0 < least < full
+    assert alone <= least <= alone + 1024          # the 4096-token sequence alone (+ its offsets)
+    assert bwd_status(L, a, ws_bytes=full) == kda.KDA_ERR_DEVICE
+    assert bwd_status(L, a, ws_bytes=least) == kda.KDA_ERR_DEVICE
+    assert bwd_status(L, a, ws_bytes=least - 256) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    # states given: the groups read their slices of them
+    c, keep3 = bwd_args(cu=cu, states=FAKE * 40)
+    assert bwd_status(L, c, ws_bytes=L.kda_chunk_bwd_workspace_min_bytes(ctypes.byref(c))) == kda.KDA_ERR_DEVICE
+    # a single sequence: the minimum is the whole need
+    assert L.kda_chunk_bwd_workspace_min_bytes(ctypes.byref(b)) == alone
+    assert L.kda_chunk_bwd_workspace_min_bytes(ctypes.byref(bwd_args(num_heads=0)[0])) == 0   # invalid

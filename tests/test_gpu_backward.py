@@ -31,12 +31,12 @@ def to_dev(x, dt):
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.device("cuda:0"), dt)
 
 
-def run_bwd(w, do, dsf, scale=1.0, s0=True):
+def run_bwd(w, do, dsf, scale=1.0, s0=True, **kw):
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     outs = kda.kda_chunk_bwd(to_dev(w.q, dt), to_dev(w.k, dt), to_dev(w.v, dt), to_dev(w.g, torch.float32),
                              to_dev(w.beta, torch.float32), to_dev(do, torch.float32), list(w.cu_seqlens), scale,
                              to_dev(w.s0, torch.float32) if (s0 and w.s0 is not None) else None,
-                             None if dsf is None else to_dev(dsf, torch.float32))
+                             None if dsf is None else to_dev(dsf, torch.float32), **kw)
     torch.cuda.synchronize()
     return [x.cpu().numpy() for x in outs]
 
@@ -51,9 +51,9 @@ def dg_bar(dtype, dg_ref, amp):
     return max(TOL["f32"], 4.0 * EPS_STATE_F32 * a), a
 
 
-def check(w, do, dsf, scale=1.0, s0=True, label=""):
+def check(w, do, dsf, scale=1.0, s0=True, label="", **kw):
     tol = TOL[w.dtype]
-    got = run_bwd(w, do, dsf, scale, s0)
+    got = run_bwd(w, do, dsf, scale, s0, **kw)
     *ref, amp = OB.backward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, scale, w.s0 if s0 else None, do, dsf,
                             amplification=True)
     dg_tol, a = dg_bar(w.dtype, ref[3], amp)
@@ -111,6 +111,29 @@ def test_backward_more_sequences_than_one_plan_tile():
     w = W.make_prefill(lens, H=1, dk=64, dv=64, dtype="bf16", seed=62, s0_std=0.1)
     do, dsf = W.make_cotangents(w, seed=62)
     check(w, do, dsf, label="1500 sequences")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("given", [False, True])
+def test_backward_in_groups_of_sequences(dtype, given):
+    """With the least workspace the library accepts (the longest sequence's own), the batch runs as
+    groups of whole sequences one after another: against the oracle at the usual bars, and
+    bit-identical to the one-pass run (every chunk and chain takes the same arithmetic; both runs'
+    forward recomputes split each chain over two workgroups, having fewer chains than half the
+    compute units).  With given states, each group reads its own slice of them."""
+    w = W.make_prefill([300, 0, 1000, 64, 33, 700], H=2, dk=128, dv=128, dtype=dtype, seed=29, s0_std=0.1)
+    do, dsf = W.make_cotangents(w, seed=29)
+    kw = {}
+    if given:
+        dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        _, _, ck = kda.kda_chunk_fwd(to_dev(w.q, dt), to_dev(w.k, dt), to_dev(w.v, dt), to_dev(w.g, torch.float32),
+                                     to_dev(w.beta, torch.float32), list(w.cu_seqlens), 1.0,
+                                     to_dev(w.s0, torch.float32), False, 32, chunk_size=32, segment_tokens=-1)
+        kw["states"] = ck
+    got = check(w, do, dsf, label=f"groups {dtype} given={given}", workspace_cap=1, **kw)
+    one = run_bwd(w, do, dsf, **kw)
+    for n, a_, b_ in zip(NAMES, got, one):
+        np.testing.assert_array_equal(a_, b_, err_msg=n)
 
 
 @pytest.mark.parametrize("gate", ["min", "zero", "slow"])

@@ -16,7 +16,7 @@ import torch
 import gated_delta_rule_49_amd as kda
 import oracle
 import workloads as W
-from parity_helpers import identity_bar, oracle_backward_heads
+from parity_helpers import dot, identity_bar, oracle_backward_heads
 
 pytestmark = pytest.mark.gpu
 
@@ -193,6 +193,86 @@ def test_backward_prologue_T65536_H96_two_heads_and_identity():
     _report("T=65536 H=96 prologue backward heads [57, 3]", errs_b)
     _backward_identity("T=65536 H=96 prologue backward", grads, (o, sf), v, s0, do, dsf, errs_b,
                        {"o": fo.value(), "S": fs.value()})
+
+
+@pytest.mark.timeout(1200)
+def test_backward_varlen_64seq_in_one_call_bounded_workspace():
+    """The backward at the varlen workload's shape (64 sequences, 1,853,952 tokens, H = 32, d = 128,
+    bf16, per-sequence S0) in ONE call, within a workspace of 36 GiB (the whole batch's would be
+    about ten times that): the library runs it in groups of whole sequences.  Every gradient
+    finite; the shortest sequence on all 32 heads and a 4,096-token one on 4 heads against the
+    fp64 oracle adjoint; over the whole batch the linearity identity, with d_o and dS_T seeded
+    draws on the device."""
+    from oracle import backward as OB
+    seqlens = W.varlen_lengths()
+    c = W.WORKLOADS[4]
+    H, dk, dv = c["H"], c["dk"], c["dv"]
+    T, N = sum(seqlens), len(seqlens)
+    d = dev()
+    q = torch.empty((T, H, dk), dtype=torch.bfloat16, device=d)
+    k = torch.empty_like(q)
+    v = torch.empty((T, H, dv), dtype=torch.bfloat16, device=d)
+    g = torch.empty((T, H, dk), dtype=torch.float32, device=d)
+    beta = torch.empty((T, H), dtype=torch.float32, device=d)
+    s0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=d)
+    for first, off, part in W.workload_parts(4):
+        n = part.total_tokens
+        q[off:off + n] = _bf16(part.q).to(d)
+        k[off:off + n] = _bf16(part.k).to(d)
+        v[off:off + n] = _bf16(part.v).to(d)
+        g[off:off + n] = _f32(part.g).to(d)
+        beta[off:off + n] = _f32(part.beta).to(d)
+        s0[first:first + len(part.seqlens)] = _f32(part.s0).to(d)
+    gen = torch.Generator(device=d)
+    gen.manual_seed(41)
+    do = torch.randn((T, H, dv), generator=gen, device=d)
+    dsf = torch.randn((N, H, dk, dv), generator=gen, device=d)
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int64)
+    cap = 36 << 30
+    print(f"[fullsize] varlen backward: {T} tokens, workspace cap {cap >> 30} GiB", flush=True)
+    grads = kda.kda_chunk_bwd(q, k, v, g, beta, do, list(cu), 1.0, s0, dsf, workspace_cap=cap)
+    torch.cuda.synchronize()
+    for x in grads:
+        assert bool(torch.isfinite(x).all())
+    names = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
+    acc = {n: W.ErrAccum() for n in names}
+    fo, fs = W.ErrAccum(), W.ErrAccum()
+    short = int(np.argmin(seqlens))
+    mid = int(np.argmin([abs(L - 4096) for L in seqlens]))
+    samples = [(short, list(range(H))), (mid, [0, 11, 22, 31])]
+    for sq, heads in samples:
+        L, a0 = seqlens[sq], int(cu[sq])
+        w = W.make_prefill([L], H, dk, dv, c["dtype"], 0, c["s0_std"], "default", 0, wid=4, seq_ids=[sq])
+        do_h = do[a0:a0 + L].cpu().numpy()
+        dsf_h = dsf[sq:sq + 1].cpu().numpy()
+        ref = oracle_backward_heads(w.q, w.k, w.v, w.g, w.beta, [0, L], 1.0, w.s0, do_h, dsf_h, heads)
+        for hh in heads:
+            sl = (slice(a0, a0 + L), slice(hh, hh + 1))
+            got = [grads[0][sl], grads[1][sl], grads[2][sl], grads[3][sl], grads[4][sl], grads[5][sq:sq + 1, hh:hh + 1]]
+            for n, x, r in zip(names, got, ref[hh]):
+                acc[n].add(x.cpu().numpy(), r)
+        qs, ks, vs, gs, bs, s0s = _sub(w, heads)
+        o_r, s_r, _ = oracle.forward(qs, ks, vs, gs, bs, [0, L], 1.0, s0s, 0)
+        o_g, s_g, _ = kda.kda_chunk_fwd(q[a0:a0 + L], k[a0:a0 + L], v[a0:a0 + L], g[a0:a0 + L], beta[a0:a0 + L],
+                                        [0, L], 1.0, s0[sq:sq + 1], True, 0, chunk_size=CHUNK)
+        idx = torch.tensor(heads, device=d)
+        fo.add(o_g.index_select(1, idx).cpu().numpy(), o_r)
+        fs.add(s_g.index_select(1, idx).cpu().numpy(), s_r)
+        print(f"[fullsize] varlen backward: sequence {sq} (L={L}) heads {heads[:4]}... compared", flush=True)
+    errs_b = {n: a_.value() for n, a_ in acc.items()}
+    _report("varlen 64 seqs backward (sampled sequences and heads)", errs_b)
+    # linearity identity over the whole batch: the gradients first, then the forward's o and S_T
+    dv_, ds0 = grads[2], grads[5]
+    lhs = dot(dv_, v) + dot(ds0, s0)
+    bar_b = identity_bar([(dv_, v, errs_b["dv"]), (ds0, s0, errs_b["dS0"])])
+    del grads, dv_
+    torch.cuda.empty_cache()
+    o, sf, _ = kda.kda_chunk_fwd(q, k, v, g, beta, list(cu), 1.0, s0, True, 0, chunk_size=CHUNK)
+    rhs = dot(do, o) + dot(dsf, sf)
+    bar = bar_b + identity_bar([(o, do, fo.value()), (sf, dsf, fs.value())])
+    print(f"[fullsize] varlen backward identity: {lhs:.9e} vs {rhs:.9e}, |diff| {abs(lhs - rhs):.3e} <= bar "
+          f"{bar:.3e}", flush=True)
+    assert abs(lhs - rhs) <= bar, (lhs, rhs, bar)
 
 
 def test_decode_N256_H96_every_state():
