@@ -74,7 +74,8 @@ def main():
                          "gate pre-activations)")
     ap.add_argument("--workload", type=int, default=0, choices=(0, 1, 2, 4),
                     help="instead of the benchmark step, time the prefill of workload 1 (T=4096, H=32) or 4 "
-                         "(64 packed sequences, H=32, checkpoints every 512) and print its own JSON line")
+                         "(64 packed sequences, H=32, checkpoints every 512) and print its own JSON line; with "
+                         "--backward 4, the backward of workload 4 within a bounded workspace")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the benchmark step, time the backward (kda_chunk_bwd) on workload 2's shape "
                          "and print its own JSON line")
@@ -119,6 +120,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.backward and args.workload == 4:
+        backward_varlen_workload(args.steps, args.warmup)
         return
     if args.backward:
         backward_workload(args.steps, args.warmup, args.prologue)
@@ -902,6 +906,83 @@ def backward_workload(steps, warmup, fused=False):
         "with_forward_states": {"ms": round(med_s, 4), "tokens_per_s": round(T / (med_s * 1e-3), 1),
                                 "note": "the forward's checkpoints every 32 tokens passed in, not recomputed"},
         "data": "synthetic (seeded)"}), flush=True)
+
+
+BWD_VARLEN_CAP = 36 << 30   # workspace of the varlen backward: the library runs it in groups of sequences
+
+
+def backward_varlen_workload(steps, warmup):
+    """Backward tokens/s on workload 4's shape (64 packed sequences, 1,853,952 tokens, H=32, d=128,
+    bf16 q/k/v, per-sequence initial states, d_o and dS_T) in one call within a 36 GiB workspace
+    (the whole batch at once would need about ten times that): the library runs it in groups of
+    whole sequences.  Inputs drawn on the device with torch's seeded generator (timing only)."""
+    import numpy as np
+    import torch
+    import gated_delta_rule_49_amd as kda
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    lens = W.varlen_lengths()
+    T, N, H, dk, dv = sum(lens), len(lens), 32, 128, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261204)
+    rn = lambda *shape: torch.randn(shape, generator=gen, device=dev)
+    q = torch.empty((T, H, dk), dtype=bf, device=dev)
+    k = torch.empty_like(q)
+    for dst, sc in ((q, dk ** -0.5), (k, 1.0)):
+        for i in range(0, T, 1 << 17):   # in slices: the fp32 draw of the whole tensor is 30 GB
+            x = rn(min(T - i, 1 << 17), H, dk)
+            dst[i:i + x.shape[0]] = (x / x.norm(dim=-1, keepdim=True) * sc).to(bf)
+    del x
+    v = torch.empty((T, H, dv), dtype=bf, device=dev)
+    for i in range(0, T, 1 << 17):
+        v[i:i + (1 << 17)] = rn(min(T - i, 1 << 17), H, dv).to(bf)
+    g = rn(T, H, dk)
+    g.sigmoid_().mul_(-5.0)
+    beta = torch.sigmoid(rn(T, H))
+    s0 = 0.1 * rn(N, H, dk, dv)
+    do = rn(T, H, dv)
+    dsf = rn(N, H, dk, dv)
+    cu = [0] + list(np.cumsum(lens))
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dkk, dg = (torch.empty((T, H, dk), **f32) for _ in range(3))
+    dvv, db, ds0 = torch.empty((T, H, dv), **f32), torch.empty((T, H), **f32), torch.empty((N, H, dk, dv), **f32)
+    cu_h = torch.tensor(cu, dtype=torch.int32)
+    cu_d = cu_h.to(dev)
+    a = kda.make_bwd_args(q, k, v, g, beta, cu_d, cu_h, 1.0, s0, do, dsf, dq, dkk, dvv, dg, db, ds0)
+    L = kda.lib()
+    full = int(L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a)))
+    least = int(L.kda_chunk_bwd_workspace_min_bytes(ctypes.byref(a)))
+    ws = torch.empty(max(least, min(full, BWD_VARLEN_CAP)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        kda._check(L.kda_chunk_bwd(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                                   ctypes.c_void_p(stream.cuda_stream)))
+
+    for _ in range(max(1, warmup)):
+        run()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = float(np.median(ms))
+    nbytes = bwd_alg_bytes(T, H, dk, dv, N)
+    print(json.dumps({
+        "metric": "KDA backward tokens/s", "workload": "backward of the varlen prefill: 64 sequences, "
+                                                      f"{T} tokens, H=32 d_k=d_v=128 bf16 q/k/v, fp32 g/beta, "
+                                                      "per-sequence initial states, d_o and dS_T",
+        "tokens": T, "heads": H, "value": round(T / (med * 1e-3), 1), "unit": "tokens/s", "ms": round(med, 4),
+        "ms_min": round(min(ms), 4), "alg_bytes": int(nbytes), "alg_GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "workspace_GB": round(ws.numel() / 1e9, 2), "workspace_whole_batch_GB": round(full / 1e9, 2),
+        "workspace_min_GB": round(least / 1e9, 2), "data": "synthetic (seeded)"}), flush=True)
 
 
 def _bwd_ws_bytes(kda, q, k, v, g, beta, do, cu, s0, dsf, out, fused=False):

@@ -402,9 +402,10 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_sta
     None (zeros).  workspace: optional uint8 CUDA tensor of at least the queried size (reused by
     callers that run the backward repeatedly).  states: the forward's checkpoints with
     checkpoint_every=32 (fp32 [sum floor(L/32), H, dk, dv]) to read instead of recomputing them, or
-    None.  workspace_cap: when the workspace is allocated here, at most this many bytes (never less
-    than the library's minimum, the longest sequence's): the library then runs the batch in groups
-    of sequences that fit.  Returns (dq, dk, dv, dg, dbeta, d_initial_state or None), all fp32."""
+    None.  A given workspace smaller than the library's minimum (the longest sequence's need) is
+    replaced by one allocated here.  workspace_cap: when the workspace is allocated here, at most
+    this many bytes (never less than that minimum): the library then runs the batch in groups of
+    sequences that fit.  Returns (dq, dk, dv, dg, dbeta, d_initial_state or None), all fp32."""
     _require_device(q)
     T, H, dk = q.shape
     dv = v.shape[2]
@@ -425,9 +426,12 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, scale=1.0, initial_sta
         _check(L.kda_chunk_bwd(ctypes.byref(a), None, 0, _stream(stream)))
     if workspace is not None:
         _tensor("workspace", workspace, dev, None, (torch.uint8,))
-    if workspace is None:
+    least = int(L.kda_chunk_bwd_workspace_min_bytes(ctypes.byref(a)))
+    if workspace is None or workspace.numel() < least:
+        # (a given workspace of at least the minimum is used as it is: the library then runs the
+        # batch in groups of sequences if it is below the whole batch's need)
         if workspace_cap is not None:
-            ws_bytes = min(ws_bytes, max(int(workspace_cap), int(L.kda_chunk_bwd_workspace_min_bytes(ctypes.byref(a)))))
+            ws_bytes = min(ws_bytes, max(int(workspace_cap), least))
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     _check(L.kda_chunk_bwd(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                            ctypes.c_size_t(workspace.numel()), _stream(stream)))
