@@ -367,9 +367,69 @@ chunk32_kernel(const ChunkParams p) {
         const int rw = wave - (NSW + DK / 16);
         // their work is a chain of dependent MFMA products: issue it ahead of the other waves
         __builtin_amdgcn_s_setprio(3);
+        // With the fused normalisation they also form 1/|k| and 1/|q| of every row of chunk it + 1 in
+        // segment 1 (where they are otherwise idle), for the prep waves' segment 2: wave rw takes rows
+        // 8 rw + 4 u + (lane / 16), u = 0, 1, each row's 128 values as 16 lanes x 8; the raw rows
+        // load one iteration ahead.
+        constexpr bool RNORM = (PRO & KDA_PRO_NORM) != 0;
+        uint4 nk_[2], nq_[2];
+        auto nload = [&](int ch) {
+            const int t0 = seq_start + ch * C32, nv = min(C32, seq_len - ch * C32), lane = lane_id();
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r = min(8 * rw + 4 * u + (lane >> 4), nv - 1);
+                const size_t off = ((size_t)(t0 + r) * H + h) * DK + 8 * (lane & 15);
+                nk_[u] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.k) + off);
+                nq_[u] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + off);
+            }
+        };
+        if constexpr (RNORM) {
+            static_assert(DK == 128 && sizeof(IN_T) == 2, "the normalisation reads bf16 rows of 16 x 8 values");
+            if (nchunks > 0) nload(0);
+        }
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
             const int lane = lane_id(), lr = lane & 15, lq = lane >> 4;
+            if constexpr (RNORM) {
+                if (it + 1 < nchunks) {
+                    __builtin_amdgcn_s_setprio(0);   // behind the prep waves' segment 1
+                    float ss[4];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const uint32_t wk[4] = {nk_[u].x, nk_[u].y, nk_[u].z, nk_[u].w};
+                        const uint32_t wq[4] = {nq_[u].x, nq_[u].y, nq_[u].z, nq_[u].w};
+                        float sk = 0.f, sq = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float k0 = lo_bf16_of(wk[i]), k1 = hi_bf16_of(wk[i]);
+                            const float q0 = lo_bf16_of(wq[i]), q1 = hi_bf16_of(wq[i]);
+                            sk += k0 * k0 + k1 * k1;
+                            sq += q0 * q0 + q1 * q1;
+                        }
+                        ss[2 * u] = sk;
+                        ss[2 * u + 1] = sq;
+                    }
+                    // sums over the 16 lanes of each row (DPP rotations within a row of 16)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        ss[j] += dpp_f32<0x128>(ss[j]);   // row_ror:8
+                        ss[j] += dpp_f32<0x124>(ss[j]);   // row_ror:4
+                        ss[j] += dpp_f32<0x122>(ss[j]);   // row_ror:2
+                        ss[j] += dpp_f32<0x121>(ss[j]);   // row_ror:1
+                    }
+                    if (lr == 0) {
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int r = 8 * rw + 4 * u + lq;
+                            *reinterpret_cast<float2 *>(sm + L::NRM + r * 8) =
+                                make_float2(ss[2 * u] > 0.f ? rsqrtf(ss[2 * u]) : 0.f,
+                                            ss[2 * u + 1] > 0.f ? rsqrtf(ss[2 * u + 1]) : 0.f);
+                        }
+                    }
+                    nload(min(it + 2, nchunks - 1));
+                    __builtin_amdgcn_s_setprio(3);
+                }
+            }
             lds_barrier();
             lds_barrier();
             const int ch = it + 1;
@@ -711,7 +771,8 @@ chunk32_kernel(const ChunkParams p) {
                     if constexpr (pre) bv = __builtin_amdgcn_rcpf(1.f + __expf(-bn_));   // sigmoid(b)
                     s_beta[4 * rgp + cp] = 4 * rgp + cp < nv ? bv : 0.f;
                 }
-                if constexpr ((PRO & KDA_PRO_NORM) != 0) {
+                if constexpr ((PRO & KDA_PRO_NORM) != 0 && NRW == 0) {
+                    // (with role waves, they form these in this segment instead)
                     // 1/|k|, 1/|q| of each row (0 for a zero row): sums of squares over the NCP lanes
                     // holding the row, then one lane per group -> LDS for P2
                     float ss[8];
