@@ -240,19 +240,19 @@ segment_chain_kernel(const int32_t *__restrict__ info, const int32_t *__restrict
 }
 
 // Output correction of the later segments: o_t += S_in^T r_t, r_t = scale M_t^T q_t (the transition
-// runs' outputs, oI [T][H][D]).  Workgroup (segment s, token tile j, head h): tokens cuB[s] + 16 NW j
-// .. + 16 NW - 1, wave w of NW taking 16 of them.  Each wave loads its rows of oI and o first, and
-// every thread issues all its loads of S_in before converting any, so that one round trip covers
-// the workgroup's loads.  The product is formed transposed, out[c][t] = sum_k S[k][c]
-// r_t[k] (S_in^T from LDS as the A operand, r_t as the B operand), so that each lane ends up with
-// 4 adjacent columns of one token: o moves as 16-byte vectors.  bf16 MFMA 16x16x32 in three terms
+// runs' outputs, oI [T][H][D]).  Workgroup (segment s, tile group jg, head h): TPW consecutive tiles
+// of 16 NW tokens from cuB[s] + 16 NW TPW jg, wave w of NW taking 16 tokens of each tile.  S_in is
+// staged once per workgroup; each tile's rows of oI (and, with PO, of o) load while the previous
+// tile's products run.  The product is formed transposed, out[c][t] = sum_k S[k][c] r_t[k]
+// (S_in^T from LDS as the A operand, r_t as the B operand), so that each lane ends up with 4
+// adjacent columns of one token: o moves as 16-byte vectors.  bf16 MFMA 16x16x32 in three terms
 // (hi hi + hi lo + lo hi, each operand split as x = hi + lo): about 16 significant bits, the fp32
 // bar's precision.  S_in sits in LDS transposed, [column][k], hi and lo planes, rows padded to
 // D + 8 (the 16 lanes of an operand read then start 4 banks apart).
 constexpr int CORR_WAVES = 8;   // waves (16 tokens each) of a correction workgroup
-template <int D, int NW>
+template <int D, int NW, int TPW, bool PO>
 __global__ void __launch_bounds__(64 * NW)
-segment_correct_kernel(const int32_t *__restrict__ cuB, const int32_t *__restrict__ s0map, int H, int tiles,
+segment_correct_kernel(const int32_t *__restrict__ cuB, const int32_t *__restrict__ s0map, int H, int groups,
                        const __bf16 *__restrict__ sin_, const float *__restrict__ oI, float *__restrict__ o) {
     constexpr int KP = D + 8, KS = D / 32, CT = D / 16, TT = 16 * NW;
     static_assert(KP == sin_pitch<D>(), "LDS rows as stored");
@@ -260,35 +260,43 @@ segment_correct_kernel(const int32_t *__restrict__ cuB, const int32_t *__restric
     constexpr int VEC = (NV + 64 * NW - 1) / (64 * NW);
     __shared__ __attribute__((aligned(16))) __bf16 SH[2 * D * KP];   // hi plane, then lo plane
     __bf16 *const SL = SH + D * KP;
-    const int s = (int)blockIdx.x / tiles, j = (int)blockIdx.x % tiles, h = (int)blockIdx.y;
+    const int s = (int)blockIdx.x / groups, jg = (int)blockIdx.x % groups, h = (int)blockIdx.y;
     if (s0map[s] != -2) return;   // a first segment: its outputs are final
-    const int t_beg = cuB[s] + TT * j, t_end = min(cuB[s + 1], t_beg + TT);
-    if (t_beg >= t_end) return;
+    const int seg_end = cuB[s + 1], t_first = cuB[s] + TT * TPW * jg;
+    if (t_first >= seg_end) return;
     const int w = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
-    const int t = t_beg + 16 * w + lr;   // this lane's token
-    const bool live = t < t_end;
-    const size_t row = ((size_t)t * H + h) * D;
-    // r_t as B operands (k = 32 ks + 8 lq .. + 7) and o_t[16 ct + 4 lq .. + 3] as the addends
-    float x[KS][8];
-    f32x4_t acc[CT];
+    // this lane's token of tile i, and its rows: r_t as B operands (k = 32 ks + 8 lq .. + 7),
+    // o_t[16 ct + 4 lq .. + 3] as the addends
+    auto token = [&](int i) { return t_first + TT * i + 16 * w + lr; };
+    auto load_r = [&](int i, float (&x)[KS][8]) {
+        const int t = token(i);
+        const size_t row = ((size_t)t * H + h) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        float4 u = make_float4(0.f, 0.f, 0.f, 0.f), v = u;
-        if (live) {
-            const float4 *src = reinterpret_cast<const float4 *>(oI + row + 32 * ks + 8 * lq);
-            u = src[0];
-            v = src[1];
+        for (int ks = 0; ks < KS; ++ks) {
+            float4 u = make_float4(0.f, 0.f, 0.f, 0.f), v = u;
+            if (t < seg_end) {
+                const float4 *src = reinterpret_cast<const float4 *>(oI + row + 32 * ks + 8 * lq);
+                u = src[0];
+                v = src[1];
+            }
+            x[ks][0] = u.x; x[ks][1] = u.y; x[ks][2] = u.z; x[ks][3] = u.w;
+            x[ks][4] = v.x; x[ks][5] = v.y; x[ks][6] = v.z; x[ks][7] = v.w;
         }
-        x[ks][0] = u.x; x[ks][1] = u.y; x[ks][2] = u.z; x[ks][3] = u.w;
-        x[ks][4] = v.x; x[ks][5] = v.y; x[ks][6] = v.z; x[ks][7] = v.w;
-    }
+    };
+    auto load_o = [&](int i, f32x4_t (&a)[CT]) {
+        const int t = token(i);
+        const size_t row = ((size_t)t * H + h) * D;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-        float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (live) y = *reinterpret_cast<const float4 *>(o + row + 16 * ct + 4 * lq);
-        acc[ct][0] = y.x; acc[ct][1] = y.y; acc[ct][2] = y.z; acc[ct][3] = y.w;
-    }
-    // S_in -> LDS
+        for (int ct = 0; ct < CT; ++ct) {
+            float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t < seg_end) y = *reinterpret_cast<const float4 *>(o + row + 16 * ct + 4 * lq);
+            a[ct][0] = y.x; a[ct][1] = y.y; a[ct][2] = y.z; a[ct][3] = y.w;
+        }
+    };
+    float x[KS][8], xn[KS][8];
+    f32x4_t acc[CT], accn[CT];
+    load_r(0, x);
+    load_o(0, acc);
     {   // S_in (already split and transposed) -> LDS: a straight copy of 16-byte vectors
         const uint4 *src = reinterpret_cast<const uint4 *>(sin_ + ((size_t)s * H + h) * sin_elems<D>());
         uint4 *dst = reinterpret_cast<uint4 *>(SH);
@@ -305,32 +313,54 @@ segment_correct_kernel(const int32_t *__restrict__ cuB, const int32_t *__restric
         }
     }
     __syncthreads();
-    if (t_beg + 16 * w >= t_end) return;
-    bf16x8_t bh[KS], bl[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            bh[ks][i] = (__bf16)x[ks][i];
-            bl[ks][i] = (__bf16)(x[ks][i] - (float)bh[ks][i]);
+    for (int i = 0; i < TPW; ++i) {
+        if (t_first + TT * i >= seg_end) break;   // (uniform)
+        const bool more = i + 1 < TPW && t_first + TT * (i + 1) < seg_end;
+        if (more) {
+            load_r(i + 1, xn);
+            if constexpr (PO) load_o(i + 1, accn);
         }
+        bf16x8_t bh[KS], bl[KS];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int off = (16 * ct + lr) * KP + 32 * ks + 8 * lq;
-            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(&SH[off]);
-            const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(&SL[off]);
-            acc[ct] = mfma_bf16(al, bh[ks], acc[ct]);
-            acc[ct] = mfma_bf16(ah, bl[ks], acc[ct]);
-            acc[ct] = mfma_bf16(ah, bh[ks], acc[ct]);
+            for (int e = 0; e < 8; ++e) {
+                bh[ks][e] = (__bf16)x[ks][e];
+                bl[ks][e] = (__bf16)(x[ks][e] - (float)bh[ks][e]);
+            }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int off = (16 * ct + lr) * KP + 32 * ks + 8 * lq;
+                const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(&SH[off]);
+                const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(&SL[off]);
+                acc[ct] = mfma_bf16(al, bh[ks], acc[ct]);
+                acc[ct] = mfma_bf16(ah, bl[ks], acc[ct]);
+                acc[ct] = mfma_bf16(ah, bh[ks], acc[ct]);
+            }
         }
-    }
-    // lane (lr, lq) holds out[16 ct + 4 lq + e][t] in acc[ct][e]: its token's 4 adjacent columns
-    if (live) {
+        // lane (lr, lq) holds out[16 ct + 4 lq + e][t] in acc[ct][e]: its token's 4 adjacent columns
+        const int t = token(i);
+        if (t < seg_end) {
+            const size_t row = ((size_t)t * H + h) * D;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-            *reinterpret_cast<float4 *>(o + row + 16 * ct + 4 * lq) = make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
+            for (int ct = 0; ct < CT; ++ct)
+                *reinterpret_cast<float4 *>(o + row + 16 * ct + 4 * lq) =
+                    make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
+        }
+        if (more) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[ks][e] = xn[ks][e];
+            if constexpr (PO) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[ct] = accn[ct];
+            } else {
+                load_o(i + 1, acc);
+            }
+        }
     }
 }
 
@@ -407,15 +437,30 @@ kda_launch_chunk_segmented(int dk, int in_bf16, int N, int H, int T, int seg, in
                            ckb, H, NB, every, st, sin_, sf, ckpt, ck_idx, nslots, ckI);
     e = hipGetLastError();
     if (e != hipSuccess || NB == N) return e;   // NB == N: every segment is a first one
-    // 4. the outputs of the later segments
-    constexpr int NW = kda::CORR_WAVES;
-    const int tiles = (seg + 16 * NW - 1) / (16 * NW);
-    const dim3 grid((unsigned)NB * tiles, (unsigned)H);
-    if (dk == 128)
-        hipLaunchKernelGGL((kda::segment_correct_kernel<128, NW>), grid, dim3(64 * NW), 0, stream, cuB, s0map, H, tiles,
-                           sin_, oI, o);
-    else
-        hipLaunchKernelGGL((kda::segment_correct_kernel<64, NW>), grid, dim3(64 * NW), 0, stream, cuB, s0map, H, tiles,
-                           sin_, oI, o);
+    // 4. the outputs of the later segments: tiles of 128 tokens, several per workgroup when there
+    // are many (each workgroup stages its S_in once, and its next tile loads during this one)
+    constexpr int NW = kda::CORR_WAVES, TT = 16 * NW;
+    const int tiles = (seg + TT - 1) / TT;
+    const long long busy = (long long)(NB - N) * tiles * H / kda_cu_count();   // tiles per compute unit
+    const int tpw = busy < 2 ? 1 : busy < 6 ? 4 : 8;   // (measured best of 1, 2, 4, 8 at 1, 3 and 7 per CU)
+    const int groups = (tiles + tpw - 1) / tpw;
+    const dim3 grid((unsigned)NB * groups, (unsigned)H);
+#define KDA_CORR(DKV, TPW, PO)                                                                                  \
+    hipLaunchKernelGGL((kda::segment_correct_kernel<DKV, NW, TPW, PO>), grid, dim3(64 * NW), 0, stream, cuB, s0map, \
+                       H, groups, sin_, oI, o)
+    if (dk == 128) {
+        switch (tpw) {
+            case 1: KDA_CORR(128, 1, false); break;
+            case 4: KDA_CORR(128, 4, true); break;
+            default: KDA_CORR(128, 8, true); break;
+        }
+    } else {
+        switch (tpw) {
+            case 1: KDA_CORR(64, 1, false); break;
+            case 4: KDA_CORR(64, 4, true); break;
+            default: KDA_CORR(64, 8, true); break;
+        }
+    }
+#undef KDA_CORR
     return hipGetLastError();
 }
