@@ -90,8 +90,9 @@ struct Lds32 {
     static constexpr int BETA = XCHG + 8 * DK * 4;        // 2 x [32] fp32
     // scan-wave stash: each scan lane parks its 8 JT (Gamma*Q) S partial outputs here between
     // segments 1 and 2 (register pressure), tile j of lane l at OST + (j * 64 NSW + l) * 16 bytes
-    static constexpr int NRM = BETA + 2 * 32 * 4;         // [32][2] fp32: 1/|k|, 1/|q| per row (fused prologue)
-    static constexpr int OST = NRM + 32 * 2 * 4;
+    static constexpr int NRM = BETA + 2 * 32 * 4;         // 2 x [32][2] fp32: 1/|k|, 1/|q| per row (fused prologue)
+    static constexpr int NRM_BUF = 32 * 2 * 4;
+    static constexpr int OST = NRM + 2 * NRM_BUF;
     static constexpr int TOTAL = OST + 2 * JT * 64 * NSW * 16;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -367,10 +368,11 @@ chunk32_kernel(const ChunkParams p) {
         const int rw = wave - (NSW + DK / 16);
         // their work is a chain of dependent MFMA products: issue it ahead of the other waves
         __builtin_amdgcn_s_setprio(3);
-        // With the fused normalisation they also form 1/|k| and 1/|q| of every row of chunk it + 1 in
-        // segment 1 (where they are otherwise idle), for the prep waves' segment 2: wave rw takes rows
-        // 8 rw + 4 u + (lane / 16), u = 0, 1, each row's 128 values as 16 lanes x 8; the raw rows
-        // load one iteration ahead.
+        // With the fused normalisation they also form 1/|k| and 1/|q| of every row of chunk it + 2 in
+        // segment 1 (where they are otherwise idle; chunk 0's before the loop), into the buffer of
+        // that chunk's parity, which the prep waves read in segment 1 of the next iteration, off
+        // their segment-2 path: wave rw takes rows 8 rw + 4 u + (lane / 16), u = 0, 1, each row's
+        // 128 values as 16 lanes x 8; the raw rows load one iteration ahead.
         constexpr bool RNORM = (PRO & KDA_PRO_NORM) != 0;
         uint4 nk_[2], nq_[2];
         auto nload = [&](int ch) {
@@ -383,50 +385,59 @@ chunk32_kernel(const ChunkParams p) {
                 nq_[u] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + off);
             }
         };
+        auto nstore = [&](char *sm, int ch) {   // 1/|k|, 1/|q| of chunk ch's rows from the loaded rows
+            const int lane = lane_id(), lr = lane & 15, lq = lane >> 4;
+            float ss[4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint32_t wk[4] = {nk_[u].x, nk_[u].y, nk_[u].z, nk_[u].w};
+                const uint32_t wq[4] = {nq_[u].x, nq_[u].y, nq_[u].z, nq_[u].w};
+                float sk = 0.f, sq = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float k0 = lo_bf16_of(wk[i]), k1 = hi_bf16_of(wk[i]);
+                    const float q0 = lo_bf16_of(wq[i]), q1 = hi_bf16_of(wq[i]);
+                    sk += k0 * k0 + k1 * k1;
+                    sq += q0 * q0 + q1 * q1;
+                }
+                ss[2 * u] = sk;
+                ss[2 * u + 1] = sq;
+            }
+            // sums over the 16 lanes of each row (DPP rotations within a row of 16)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                ss[j] += dpp_f32<0x128>(ss[j]);   // row_ror:8
+                ss[j] += dpp_f32<0x124>(ss[j]);   // row_ror:4
+                ss[j] += dpp_f32<0x122>(ss[j]);   // row_ror:2
+                ss[j] += dpp_f32<0x121>(ss[j]);   // row_ror:1
+            }
+            if (lr == 0) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int r = 8 * rw + 4 * u + lq;
+                    *reinterpret_cast<float2 *>(sm + L::NRM + (ch & 1) * L::NRM_BUF + r * 8) =
+                        make_float2(ss[2 * u] > 0.f ? rsqrtf(ss[2 * u]) : 0.f,
+                                    ss[2 * u + 1] > 0.f ? rsqrtf(ss[2 * u + 1]) : 0.f);
+                }
+            }
+        };
         if constexpr (RNORM) {
             static_assert(DK == 128 && sizeof(IN_T) == 2, "the normalisation reads bf16 rows of 16 x 8 values");
-            if (nchunks > 0) nload(0);
+            if (nchunks > 0) {
+                nload(0);
+                nstore(smem + opaque_s(0), 0);
+                nload(min(1, nchunks - 1));
+            }
+            lds_barrier();   // chunk 0's norms before the prep waves' first segment 1 (all roles pass one)
         }
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
             const int lane = lane_id(), lr = lane & 15, lq = lane >> 4;
             if constexpr (RNORM) {
-                if (it + 1 < nchunks) {
+                if (it + 2 < nchunks) {
                     __builtin_amdgcn_s_setprio(0);   // behind the prep waves' segment 1
-                    float ss[4];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const uint32_t wk[4] = {nk_[u].x, nk_[u].y, nk_[u].z, nk_[u].w};
-                        const uint32_t wq[4] = {nq_[u].x, nq_[u].y, nq_[u].z, nq_[u].w};
-                        float sk = 0.f, sq = 0.f;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float k0 = lo_bf16_of(wk[i]), k1 = hi_bf16_of(wk[i]);
-                            const float q0 = lo_bf16_of(wq[i]), q1 = hi_bf16_of(wq[i]);
-                            sk += k0 * k0 + k1 * k1;
-                            sq += q0 * q0 + q1 * q1;
-                        }
-                        ss[2 * u] = sk;
-                        ss[2 * u + 1] = sq;
-                    }
-                    // sums over the 16 lanes of each row (DPP rotations within a row of 16)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        ss[j] += dpp_f32<0x128>(ss[j]);   // row_ror:8
-                        ss[j] += dpp_f32<0x124>(ss[j]);   // row_ror:4
-                        ss[j] += dpp_f32<0x122>(ss[j]);   // row_ror:2
-                        ss[j] += dpp_f32<0x121>(ss[j]);   // row_ror:1
-                    }
-                    if (lr == 0) {
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            const int r = 8 * rw + 4 * u + lq;
-                            *reinterpret_cast<float2 *>(sm + L::NRM + r * 8) =
-                                make_float2(ss[2 * u] > 0.f ? rsqrtf(ss[2 * u]) : 0.f,
-                                            ss[2 * u + 1] > 0.f ? rsqrtf(ss[2 * u + 1]) : 0.f);
-                        }
-                    }
-                    nload(min(it + 2, nchunks - 1));
+                    nstore(sm, it + 2);
+                    nload(min(it + 3, nchunks - 1));
                     __builtin_amdgcn_s_setprio(3);
                 }
             }
@@ -491,6 +502,7 @@ chunk32_kernel(const ChunkParams p) {
         }
         const int every_chunks = p.every / C32;   // checkpoint_every is a multiple of the chunk size
         int ck_left = every_chunks, ck_idx = 0;
+        if constexpr (NRW > 0 && (PRO & KDA_PRO_NORM) != 0) lds_barrier();   // the role waves' first norms
 
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
@@ -738,6 +750,8 @@ chunk32_kernel(const ChunkParams p) {
         typename PR::raw kr[4], qr[4];   // this chunk's k, q pairs from P1 to P2
         float Fw[4][2], Bw[4][2];        // decay products within the 4-row group: through row i / after row i
         float kh[2][4], gl[2];           // (e^{G_last-G} K)^T entries and Gamma_last, from P2 to P3
+        float2 nrm[4];                   // 1/|k|, 1/|q| of this thread's rows, from P1 to P2 (fused normalisation)
+        if constexpr (NRW > 0 && (PRO & KDA_PRO_NORM) != 0) lds_barrier();   // the role waves' first norms
 
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
@@ -771,8 +785,13 @@ chunk32_kernel(const ChunkParams p) {
                     if constexpr (pre) bv = __builtin_amdgcn_rcpf(1.f + __expf(-bn_));   // sigmoid(b)
                     s_beta[4 * rgp + cp] = 4 * rgp + cp < nv ? bv : 0.f;
                 }
+                if constexpr ((PRO & KDA_PRO_NORM) != 0 && NRW > 0) {
+                    // formed by the role waves one iteration ahead: read here, off segment 2's path
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        nrm[i] = *reinterpret_cast<const float2 *>(sm + L::NRM + (nxt & 1) * L::NRM_BUF + (4 * rgp + i) * 8);
+                }
                 if constexpr ((PRO & KDA_PRO_NORM) != 0 && NRW == 0) {
-                    // (with role waves, they form these in this segment instead)
                     // 1/|k|, 1/|q| of each row (0 for a zero row): sums of squares over the NCP lanes
                     // holding the row, then one lane per group -> LDS for P2
                     float ss[8];
@@ -864,7 +883,8 @@ chunk32_kernel(const ChunkParams p) {
                     float ks[2], qs[2], ke[2], kd[2];
                     float kv[2] = {PR::lo(kr[i]), PR::hi(kr[i])}, qv[2] = {PR::lo(qr[i]), PR::hi(qr[i])};
                     if constexpr ((PRO & KDA_PRO_NORM) != 0) {   // fused normalisation: row factors from P1
-                        const float2 nr = *reinterpret_cast<const float2 *>(sm + L::NRM + (4 * rgp + i) * 8);
+                        const float2 nr = NRW > 0 ? nrm[i]
+                                                  : *reinterpret_cast<const float2 *>(sm + L::NRM + (4 * rgp + i) * 8);
                         kv[0] *= nr.x; kv[1] *= nr.x;
                         qv[0] *= nr.y; qv[1] *= nr.y;
                     }
