@@ -332,6 +332,12 @@ def main():
                                                               "ms_p10", "ms_p90", "alg_GBps", "frac_of_hbm_peak",
                                                               "alg_bytes", "cache")}
             torch.cuda.empty_cache()
+        if args.chunk == 32:
+            # the prefill's shape through the fused prologue (raw q and k, bf16 gate pre-activations)
+            r = other_workload(2, args.chunk, max(5, min(K, 20)), 2, prologue=True, emit=False)
+            res["prefill"]["prologue"] = {"ms": r["ms"], "tokens_per_s": r["value"],
+                                          "over_plain": round(r["ms"] / pre_avg, 4), "workload": r["workload"]}
+            torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wp, args.cpu_seconds, H, wd)
