@@ -369,61 +369,44 @@ chunk32_kernel(const ChunkParams p) {
         // their work is a chain of dependent MFMA products: issue it ahead of the other waves
         __builtin_amdgcn_s_setprio(3);
         // With the fused normalisation they also form 1/|k| and 1/|q| of every row of chunk it + 2 in
-        // segment 1 (where they are otherwise idle; chunk 0's before the loop), into the buffer of
-        // that chunk's parity, which the prep waves read in segment 1 of the next iteration, off
-        // their segment-2 path: wave rw takes rows 8 rw + 4 u + (lane / 16), u = 0, 1, each row's
-        // 128 values as 16 lanes x 8; the raw rows load one iteration ahead.
+        // segment 2 (where they are otherwise idle and the scan waves' products are few; chunk 0's
+        // before the loop), at the lowest priority, into the buffer of that chunk's parity, which
+        // the prep waves read in segment 1 of the next iteration, off their segment-2 path.  A row's sum of squares is the diagonal entry of the Gram product of
+        // the raw rows with themselves, formed on the matrix cores (bf16 products are exact in fp32,
+        // fp32 accumulation): wave rw takes the 16 rows 16 (rw & 1) .. of k (rw < 2) or q (rw >= 2),
+        // and lane (lr, lq) holds values 32 s + 8 lq .. + 7 of row lr for K-step s, which is both the
+        // A and the B fragment of the 16x16x32 product.  The raw rows load one iteration ahead.
         constexpr bool RNORM = (PRO & KDA_PRO_NORM) != 0;
-        uint4 nk_[2], nq_[2];
+        const bool nwave = !SO || rw < 2;   // states only: q and its norms are not used
+        uint4 xr_[KB];
         auto nload = [&](int ch) {
             const int t0 = seq_start + ch * C32, nv = min(C32, seq_len - ch * C32), lane = lane_id();
+            const int r = min(16 * (rw & 1) + (lane & 15), nv - 1);
+            const uint16_t *src = reinterpret_cast<const uint16_t *>(rw < 2 ? p.k : p.q) +
+                                  ((size_t)(t0 + r) * H + h) * DK + 8 * (lane >> 4);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int r = min(8 * rw + 4 * u + (lane >> 4), nv - 1);
-                const size_t off = ((size_t)(t0 + r) * H + h) * DK + 8 * (lane & 15);
-                nk_[u] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.k) + off);
-                nq_[u] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + off);
-            }
+            for (int s = 0; s < KB; ++s) xr_[s] = *reinterpret_cast<const uint4 *>(src + 32 * s);
         };
-        auto nstore = [&](char *sm, int ch) {   // 1/|k|, 1/|q| of chunk ch's rows from the loaded rows
+        auto nstore = [&](char *sm, int ch) {   // 1/|x| of the wave's 16 rows of chunk ch (0 for a zero row)
             const int lane = lane_id(), lr = lane & 15, lq = lane >> 4;
-            float ss[4];
+            f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const uint32_t wk[4] = {nk_[u].x, nk_[u].y, nk_[u].z, nk_[u].w};
-                const uint32_t wq[4] = {nq_[u].x, nq_[u].y, nq_[u].z, nq_[u].w};
-                float sk = 0.f, sq = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float k0 = lo_bf16_of(wk[i]), k1 = hi_bf16_of(wk[i]);
-                    const float q0 = lo_bf16_of(wq[i]), q1 = hi_bf16_of(wq[i]);
-                    sk += k0 * k0 + k1 * k1;
-                    sq += q0 * q0 + q1 * q1;
-                }
-                ss[2 * u] = sk;
-                ss[2 * u + 1] = sq;
+            for (int s = 0; s < KB; ++s) {
+                const bf16x8_t x = __builtin_bit_cast(bf16x8_t, xr_[s]);
+                acc[s & 1] = mfma_bf16(x, x, acc[s & 1]);
             }
-            // sums over the 16 lanes of each row (DPP rotations within a row of 16)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                ss[j] += dpp_f32<0x128>(ss[j]);   // row_ror:8
-                ss[j] += dpp_f32<0x124>(ss[j]);   // row_ror:4
-                ss[j] += dpp_f32<0x122>(ss[j]);   // row_ror:2
-                ss[j] += dpp_f32<0x121>(ss[j]);   // row_ror:1
-            }
-            if (lr == 0) {
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int r = 8 * rw + 4 * u + lq;
-                    *reinterpret_cast<float2 *>(sm + L::NRM + (ch & 1) * L::NRM_BUF + r * 8) =
-                        make_float2(ss[2 * u] > 0.f ? rsqrtf(ss[2 * u]) : 0.f,
-                                    ss[2 * u + 1] > 0.f ? rsqrtf(ss[2 * u + 1]) : 0.f);
-                }
+            // lane (lr, lq) holds entries (4 lq + e, lr): the diagonal entry of row lr where lr / 4 == lq
+            if ((lr >> 2) == lq) {
+                const int e = lr & 3;
+                const float ss = (e == 0 ? acc[0][0] + acc[1][0] : e == 1 ? acc[0][1] + acc[1][1]
+                                  : e == 2 ? acc[0][2] + acc[1][2] : acc[0][3] + acc[1][3]);
+                reinterpret_cast<float *>(sm + L::NRM + (ch & 1) * L::NRM_BUF + (16 * (rw & 1) + lr) * 8)[rw >> 1] =
+                    ss > 0.f ? rsqrtf(ss) : 0.f;
             }
         };
         if constexpr (RNORM) {
-            static_assert(DK == 128 && sizeof(IN_T) == 2, "the normalisation reads bf16 rows of 16 x 8 values");
-            if (nchunks > 0) {
+            static_assert(DK == 128 && sizeof(IN_T) == 2, "the normalisation reads bf16 rows, four K-steps of 32");
+            if (nwave && nchunks > 0) {
                 nload(0);
                 nstore(smem + opaque_s(0), 0);
                 nload(min(1, nchunks - 1));
@@ -433,15 +416,15 @@ chunk32_kernel(const ChunkParams p) {
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
             const int lane = lane_id(), lr = lane & 15, lq = lane >> 4;
+            lds_barrier();
             if constexpr (RNORM) {
-                if (it + 2 < nchunks) {
-                    __builtin_amdgcn_s_setprio(0);   // behind the prep waves' segment 1
+                if (nwave && it + 2 < nchunks) {
+                    __builtin_amdgcn_s_setprio(0);   // behind the prep waves' segment 2
                     nstore(sm, it + 2);
                     nload(min(it + 3, nchunks - 1));
                     __builtin_amdgcn_s_setprio(3);
                 }
             }
-            lds_barrier();
             lds_barrier();
             const int ch = it + 1;
             if (ch < nchunks) {
