@@ -403,6 +403,35 @@ def test_prefill_fused_prologue(gate, norm, d, chunk):
           "ckpt": W.rel_max_err(ck.cpu().numpy(), ck_r)}, TOL["bf16"])
 
 
+@pytest.mark.parametrize("segment_tokens", [-1, 64])
+def test_prefill_fused_normalisation_edge_rows(segment_tokens):
+    """The fused normalisation (role waves: the rows' sums of squares from the diagonal of their Gram
+    product) on edge rows: a zero q row and a zero k row (they stay zero), rows scaled by 2^-40 and
+    2^40 (exact in bf16; their squares stay normal in fp32), in chunks 0, 1 and the ragged last one,
+    uncut and cut into segments."""
+    w = W.make_prefill_raw([150, 70], H=2, dk=128, dv=128, seed=57, s0_std=0.1)
+    q, k = w.q.copy(), w.k.copy()
+    q[3, 1] = 0.0
+    k[40, 0] = 0.0
+    q[33, 0] *= np.float32(2.0 ** -40)
+    k[34, 1] *= np.float32(2.0 ** 40)
+    k[149, 0] *= np.float32(2.0 ** -40)
+    q[160, 1] *= np.float32(2.0 ** 40)
+    k[219, 1] = 0.0
+    scale = 128 ** -0.5
+    qn, kn, g64, b64 = oracle.prologue(q, k, w.g, w.beta, normalize=True)
+    o, sf, _ = kda.kda_chunk_fwd(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(w.v, torch.bfloat16),
+                                 to_dev(w.g, torch.bfloat16), to_dev(w.beta, torch.float32), list(w.cu_seqlens),
+                                 scale, to_dev(w.s0, torch.float32), True, chunk_size=32, gate_preactivation=True,
+                                 normalize_qk=True, segment_tokens=segment_tokens)
+    torch.cuda.synchronize()
+    o_r, sf_r, _ = oracle.forward(qn, kn, w.v, g64, b64, w.cu_seqlens, scale, w.s0)
+    o_g = o.cpu().numpy()
+    assert np.all(o_g[3, 1] == 0.0)   # a zero query row reads nothing
+    _log(f"fused normalisation edge rows seg={segment_tokens}",
+         {"o": W.rel_max_err(o_g, o_r), "S": W.rel_max_err(sf.cpu().numpy(), sf_r)}, TOL["bf16"])
+
+
 # ---- context parallelism: one GPU's share and the combine ----------------------------------------
 def test_context_parallel_segments_combine():
     """One 512-token sequence cut into 4 segments, as 4 GPUs would hold it: each segment runs from
