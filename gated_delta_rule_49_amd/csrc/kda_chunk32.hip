@@ -371,11 +371,12 @@ chunk32_kernel(const ChunkParams p) {
         // With the fused normalisation they also form 1/|k| and 1/|q| of every row of chunk it + 2 in
         // segment 2 (where they are otherwise idle and the scan waves' products are few; chunk 0's
         // before the loop), at the lowest priority, into the buffer of that chunk's parity, which
-        // the prep waves read in segment 1 of the next iteration, off their segment-2 path.  A row's sum of squares is the diagonal entry of the Gram product of
-        // the raw rows with themselves, formed on the matrix cores (bf16 products are exact in fp32,
-        // fp32 accumulation): wave rw takes the 16 rows 16 (rw & 1) .. of k (rw < 2) or q (rw >= 2),
-        // and lane (lr, lq) holds values 32 s + 8 lq .. + 7 of row lr for K-step s, which is both the
-        // A and the B fragment of the 16x16x32 product.  The raw rows load one iteration ahead.
+        // the prep waves read in segment 1 of the next iteration, off their segment-2 path.  A row's
+        // sum of squares is the diagonal entry of the Gram product of the raw rows with themselves,
+        // formed on the matrix cores (bf16 products are exact in fp32, fp32 accumulation): wave rw
+        // takes the 16 rows 16 (rw & 1) .. of k (rw < 2) or q (rw >= 2), and lane (lr, lq) holds
+        // values 32 s + 8 lq .. + 7 of row lr for K-step s, which is both the A and the B fragment
+        // of the 16x16x32 product.  The raw rows load one iteration ahead.
         constexpr bool RNORM = (PRO & KDA_PRO_NORM) != 0;
         const bool nwave = !SO || rw < 2;   // states only: q and its norms are not used
         uint4 xr_[KB];
