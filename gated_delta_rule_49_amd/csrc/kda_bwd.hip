@@ -62,7 +62,8 @@ struct BwdParams {
 //   ET [dv][32]   E^T                          GL [dk]      Gam_C = e^{B_last}
 //   RC [dk][dv]   R = scale (Gam Q - Aq W)^T dO = scale (Gam Q)^T dO - W^T E, the part of the
 //                 update that does not depend on D, in 16x16 tiles (tile (i/16, j/16), then lane
-//                 4 (i % 16 / 4) ... as an MFMA output tile: 64 lanes x 4 values)
+//                 4 (i % 16 / 4) ... as an MFMA output tile: 64 lanes x 4 values); for the
+//                 one-workgroup-per-chain scan, P^T [dk][32] (P = scale (Gam Q - Aq W)) instead
 template <int DK> struct ScanRec {
     static constexpr int DV = DK;
     static constexpr int KB = 0, WT = 32 * DK, ET = 64 * DK, GL = 64 * DK + 32 * DV, RC = GL + DK;
@@ -131,7 +132,9 @@ __global__ void __launch_bounds__(1024) bwd_plan_kernel(const int32_t *__restric
 
 // ---- per-chunk prep: A, T, W = T Diag(beta) (Gam K), E = scale Aq^T dO, R -------------------
 // One workgroup of dk/16 waves per (chunk, head).
-template <int DK, typename IN_T>
+// PT: the scan forms R = P^T dO itself (P = scale (Gam Q - Aq W)): the record's RC region holds
+// P^T [dk][32] instead of R.
+template <int DK, typename IN_T, bool PT = false>
 __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
     constexpr int NW = DK / 16, NT = DK * 4, P = DK + 4, DV = DK;
     __shared__ __attribute__((aligned(16))) float sk[BC][P], sq[BC][P], sb[BC][P], sdo[BC][P];
@@ -313,14 +316,21 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
                 Qp[rt][e] = p.scale * (sq[r][i] * __expf(sb[r][i]) - aw[e]);
             }
         }
-        float *Rt = rec + SR::RC + (size_t)w * (DV / 16) * 256 + 4 * lane;
-        for (int jt = 0; jt < DV / 16; ++jt) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (PT) {
 #pragma unroll
-            for (int rg = 0; rg < 2; ++rg)
+            for (int rt = 0; rt < 2; ++rt)
+                *reinterpret_cast<float4 *>(rec + SR::RC + i * BC + 16 * rt + 4 * q4) =
+                    make_float4(Qp[rt][0], Qp[rt][1], Qp[rt][2], Qp[rt][3]);
+        } else {
+            float *Rt = rec + SR::RC + (size_t)w * (DV / 16) * 256 + 4 * lane;
+            for (int jt = 0; jt < DV / 16; ++jt) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(Qp[rg][kk], sdo[16 * rg + 4 * q4 + kk][16 * jt + c], acc);
-            *reinterpret_cast<float4 *>(Rt + jt * 256) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(Qp[rg][kk], sdo[16 * rg + 4 * q4 + kk][16 * jt + c], acc);
+                *reinterpret_cast<float4 *>(Rt + jt * 256) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            }
         }
     }
     // E = scale Aq^T dO, stored transposed: wave w writes value columns 16 w .. 16 w + 15
@@ -468,6 +478,186 @@ __global__ void __launch_bounds__(256) bwd_dstate_kernel(const BwdParams p) {
         for (int kt = 0; kt < RT; ++kt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) p.dS0[st_off + (size_t)(kr0 + 16 * kt + 4 * q4 + e) * DV + j0 + c] = Dr[kt][e];
+}
+
+// ---- state-gradient scan, one workgroup per chain (d = 128, hi/lo bf16 products) -------------
+// Wave w of 8 holds value columns 16 w .. 16 w + 15 of D for every d_k row, as 8 output tiles (the
+// forward's layout of the state), so no partial product crosses waves.  Per chunk, last to first:
+//     D (the gradient at the chunk's end) -> Dck,   Y = Kbar D,   D <- Gam_C D + P^T dO - W^T Y,
+// with P^T from the record (R = P^T dO is formed here, not stored) and dO of the wave's columns.
+// Kbar, W^T and P^T are staged in LDS as hi/lo bf16 planes in the MFMA fragment layout, in two
+// buffers: after chunk r (counted from the last) has run, chunk r + 1's records go from registers
+// (loaded one step earlier) into the other buffer and chunk r + 2's are loaded, with dO of chunk
+// r + 2.  Products: hi/lo bf16 pairs (three MFMAs), fp32 accumulation.
+template <int DK> struct DScanLds {
+    static constexpr int KB = DK / 32;
+    static constexpr int KBAR = 0;                          // [32][DK] hl, fofs<KB>
+    static constexpr int KBAR_PLANE = 32 * DK * 2;
+    static constexpr int WT = KBAR + 2 * KBAR_PLANE;        // [DK][32] hl, fofs<1>
+    static constexpr int T_PLANE = DK * 32 * 2;
+    static constexpr int PT = WT + 2 * T_PLANE;             // [DK][32] hl, fofs<1>
+    static constexpr int GL = PT + 2 * T_PLANE;             // [DK] fp32
+    static constexpr int BUF = GL + DK * 4;
+    static constexpr int TOTAL = 2 * BUF;
+};
+
+template <int DK>
+__global__ void __launch_bounds__(512) bwd_dscan_hl_kernel(const BwdParams p) {
+    static_assert(DK == 128, "8 waves of 16 value columns");
+    constexpr int DV = DK, KB = DK / 32, KT = DK / 16, NT = 512;
+    using L = DScanLds<DK>;
+    using M = Mat<false>;
+    using SR = ScanRec<DK>;
+    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+
+    const int H = p.H;
+    const int ci = (int)blockIdx.x, n = p.order[ci / H], h = ci % H;
+    const int seq0 = p.cu[n], Lq = p.cu[n + 1] - seq0, nch = (Lq + BC - 1) / BC;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, q4 = lane >> 4;
+    const int j0 = 16 * w;
+    const size_t st_off = ((size_t)n * H + h) * DK * DV;
+    const int cb0 = p.cbase[n];
+
+    f32x4_t Dt[KT];   // D[16 ct + 4 q4 + e][j0 + c]
+#pragma unroll
+    for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            Dt[ct][e] = p.dSf ? p.dSf[st_off + (size_t)(16 * ct + 4 * q4 + e) * DV + j0 + c] : 0.f;
+    if (nch == 0) {
+        if (p.dS0)
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p.dS0[st_off + (size_t)(16 * ct + 4 * q4 + e) * DV + j0 + c] = Dt[ct][e];
+        return;
+    }
+
+    // chunk of relative index r (0: the last), clamped for the loads past the first
+    auto chunk_of = [&](int r) { return max(nch - 1 - r, 0); };
+    // Addresses: a uniform (scalar) base per row or record plus one 32-bit lane offset, so that
+    // no load or store keeps a 64-bit address of its own in registers.
+    const unsigned d_lane = (unsigned)(4 * q4 * DV + j0 + c);        // D[4 q4][j0 + c] in a [DK][DV] state
+    const unsigned o_lane = (unsigned)(4 * q4 * H * DV + j0 + c);    // dO[row 4 q4][h][j0 + c], relative
+    // the records of a chunk: thread tid holds float4 tid + 512 u of [Kbar | W^T | P^T] and float4
+    // tid % (DK / 4) of Gam_C (written by threads tid < DK / 4)
+    struct Stage { float4 x[6]; float4 gl; };
+    auto sload = [&](Stage &st, int r) {
+        const float *rec = p.SCk + ((size_t)(cb0 + chunk_of(r)) * H + h) * SR::SIZE;
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+            const unsigned f = (unsigned)tid + NT * u;
+            const float *src = u < 2 ? rec + SR::KB : u < 4 ? rec + SR::WT - 4096 : rec + SR::RC - 8192;
+            st.x[u] = *reinterpret_cast<const float4 *>(src + 4 * f);
+        }
+        st.gl = *reinterpret_cast<const float4 *>(rec + SR::GL + 4 * (unsigned)(tid & (DK / 4 - 1)));
+    };
+    auto swrite = [&](const Stage &st, char *buf) {
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+            const int f = tid + NT * u;
+            const float x[4] = {st.x[u].x, st.x[u].y, st.x[u].z, st.x[u].w};
+            if (u < 2) {
+                M::template put_hl<4>(buf + L::KBAR, L::KBAR_PLANE, fofs<KB>(f / (DK / 4), 4 * (f % (DK / 4))), x);
+            } else {
+                const int g = f - (u < 4 ? 1024 : 2048);
+                M::template put_hl<4>(buf + (u < 4 ? L::WT : L::PT), L::T_PLANE, fofs<1>(g / 8, 4 * (g % 8)), x);
+            }
+        }
+        if (tid < DK / 4) *reinterpret_cast<float4 *>(buf + L::GL + 16 * tid) = st.gl;
+    };
+    // dO of a chunk for this wave's columns, as two output tiles (rows past the chunk: zeros)
+    auto dload = [&](f32x4_t (&d)[2], int r) {
+        const int jc = chunk_of(r), t0 = seq0 + BC * jc, nv = min(BC, Lq - BC * jc);
+        if (nv == BC) {   // (uniform) a full chunk
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d[rt][e] = p.dO[((size_t)(t0 + 16 * rt + e) * H + h) * DV + o_lane];
+        } else {          // the last chunk of a sequence: rows past it read its last row, then zero
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * rt + 4 * q4 + e;
+                    const float x = p.dO[((size_t)(t0 + min(t, nv - 1)) * H + h) * DV + j0 + c];
+                    d[rt][e] = t < nv ? x : 0.f;
+                }
+        }
+    };
+    // one chunk (relative index r) with its records in LDS buffer `buf` and its dO in `dcur`
+    auto step = [&](int r, const char *buf, const f32x4_t (&dcur)[2]) {
+        const int jc = nch - 1 - r;
+        float *const dd = p.Dck + ((size_t)(cb0 + jc) * H + h) * DK * DV;
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dd[(size_t)(16 * ct + e) * DV + d_lane] = Dt[ct][e];
+        // Y = Kbar D, then -Y
+        f32x4_t Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < KB; ++s) {
+            const Frag<false> df = M::template from_tiles<true>(Dt[2 * s], Dt[2 * s + 1]);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+                mma<true, true>(Y[rt], M::template get<true>(buf + L::KBAR, L::KBAR_PLANE, fbase<KB>(rt, s, lane)), df);
+            __builtin_amdgcn_sched_barrier(0);   // one K-step's fragments live at a time (registers)
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Y[rt][e] = -Y[rt][e];
+        const Frag<false> yf = M::template from_tiles<true>(Y[0], Y[1]);
+        const Frag<false> of = M::template from_tiles<true>(dcur[0], dcur[1]);
+        const float *gl = reinterpret_cast<const float *>(buf + L::GL);
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+            const float4 g4 = *reinterpret_cast<const float4 *>(gl + 16 * ct + 4 * q4);
+            f32x4_t acc = {g4.x * Dt[ct][0], g4.y * Dt[ct][1], g4.z * Dt[ct][2], g4.w * Dt[ct][3]};
+            mma<true, true>(acc, M::template get<true>(buf + L::PT, L::T_PLANE, fbase<1>(ct, 0, lane)), of);
+            mma<true, true>(acc, M::template get<true>(buf + L::WT, L::T_PLANE, fbase<1>(ct, 0, lane)), yf);
+            Dt[ct] = acc;
+            __builtin_amdgcn_sched_barrier(0);   // one tile's fragments live at a time (registers)
+        }
+    };
+
+    Stage sa;              // register stage: the records of the next chunk
+    f32x4_t da[2], db[2];  // dO: da for even relative chunks, db for odd
+    sload(sa, 0);
+    swrite(sa, smem);      // chunk 0 (relative) into buffer 0
+    sload(sa, 1);
+    dload(da, 0);
+    dload(db, 1);
+    // even r: buffer 0 and da, then chunk r + 1 from the stage into buffer 1; odd r: buffer 1 and db,
+    // then chunk r + 1 into buffer 0.  Step 0 and a last odd step are peeled so that the loop runs
+    // over whole pairs (no exit between its two steps, where the registers carried around the loop
+    // would need copies, and those copies waits for their loads).
+    auto even = [&](int r) {
+        lds_barrier();
+        step(r, smem, da);
+        if (r + 1 < nch) swrite(sa, smem + L::BUF);
+        sload(sa, r + 2);
+        dload(da, r + 2);
+    };
+    auto odd = [&](int r) {
+        lds_barrier();
+        step(r, smem + L::BUF, db);
+        if (r + 1 < nch) swrite(sa, smem);
+        sload(sa, r + 2);
+        dload(db, r + 2);
+    };
+    even(0);
+    int r = 1;
+    for (; r + 1 < nch; r += 2) {
+        odd(r);
+        even(r + 1);
+    }
+    if (r < nch) odd(r);
+    if (p.dS0)
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.dS0[st_off + (size_t)(16 * ct + 4 * q4 + e) * DV + j0 + c] = Dt[ct][e];
 }
 
 // ---- per-chunk gradients --------------------------------------------------------------------
@@ -1123,11 +1313,18 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     const unsigned chunk_blocks = (unsigned)(n_chunks * H);
     const unsigned scan_blocks = (unsigned)N * (unsigned)H * (unsigned)(dk / 16);
     // (with the normalising prologue the inputs are fp32 unit vectors, the error budget bf16's)
+    // (d = 128 with bf16 error budgets: the scan takes one workgroup per chain and forms R itself)
 #define KDA_BWD(DKV, T_, HL_)                                                                                      \
     do {                                                                                                           \
+        constexpr bool ONE = DKV == 128 && HL_;                                                                    \
         if (chunk_blocks)                                                                                          \
-            hipLaunchKernelGGL((kda::bwd_prep_kernel<DKV, T_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, p); \
-        hipLaunchKernelGGL((kda::bwd_dstate_kernel<DKV>), dim3(scan_blocks), dim3(256), 0, stream, p);             \
+            hipLaunchKernelGGL((kda::bwd_prep_kernel<DKV, T_, ONE>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, \
+                               p);                                                                                 \
+        if constexpr (ONE)                                                                                         \
+            hipLaunchKernelGGL((kda::bwd_dscan_hl_kernel<128>), dim3((unsigned)N * (unsigned)H), dim3(512), 0,     \
+                               stream, p);                                                                         \
+        else                                                                                                       \
+            hipLaunchKernelGGL((kda::bwd_dstate_kernel<DKV>), dim3(scan_blocks), dim3(256), 0, stream, p);         \
         if (chunk_blocks)                                                                                          \
             hipLaunchKernelGGL((kda::bwd_grad_kernel<DKV, T_, HL_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, \
                                p);                                                                                 \
