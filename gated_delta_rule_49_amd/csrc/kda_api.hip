@@ -235,6 +235,20 @@ int bwd_flags(const kda_bwd_args *a) {
     return (a->gate_mode == KDA_GATE_PREACTIVATION ? 1 : 0) | (a->normalize_qk ? 2 : 0) | (a->states ? 8 : 0);
 }
 
+// The state-gradient scan with one workgroup per chain serves batches whose chains all run the whole
+// scan at full load: at least 3 x 8 column-block workgroups per compute unit's worth of chains for
+// the scan split over column blocks (which that one runs at contention), and sequences of nearly
+// equal length (the longest at most 5/4 of the mean), since a long chain's tail runs faster split.
+int bwd_scan_choice(const int32_t *cu, int first, int last, int H) {
+    const int n = last - first;
+    int longest = 0;
+    for (int i = first; i < last; ++i) longest = cu[i + 1] - cu[i] > longest ? cu[i + 1] - cu[i] : longest;
+    const long long total = (long long)cu[last] - cu[first];
+    const bool full = (long long)n * H * 8 >= 3LL * kda_cu_count();
+    const bool even = total > 0 && 4LL * longest * n <= 5LL * total;
+    return full && even ? kda::KDA_BWD_ONE_WG_SCAN : 0;
+}
+
 // Workspace of the backward of sequences [first, last) run as a group of their own: its layout
 // plus their offsets rebased to the group's first token.  Validated arguments only.
 size_t bwd_group_bytes(const kda_bwd_args *a, int first, int last) {
@@ -402,7 +416,9 @@ kda_status kda_chunk_bwd(const kda_bwd_args *a, void *workspace, size_t workspac
                                             a->total_tokens, ck, ch, a->q, a->k, a->v, a->g, a->beta, a->cu_seqlens,
                                             a->initial_state, a->d_o, a->d_final_state, a->dq, a->dk_out, a->dv_out,
                                             a->dg, a->dbeta, a->d_initial_state, a->scale, a->states,
-                                            bwd_flags(a) & 3, workspace, sm);
+                                            (bwd_flags(a) & 3) | bwd_scan_choice(a->cu_seqlens_host, 0, a->num_seqs,
+                                                                                 a->num_heads),
+                                            workspace, sm);
         return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
     }
     // A smaller workspace: consecutive groups of whole sequences, each within it, one after the
@@ -446,7 +462,7 @@ kda_status kda_chunk_bwd(const kda_bwd_args *a, void *workspace, size_t workspac
                                shiftf(a->dg, t0 * H * dk), shiftf(a->dbeta, t0 * H),
                                shiftf(a->d_initial_state, first * state), a->scale,
                                static_cast<const float *>(shift(a->states, (size_t)ck_before * state * 4)),
-                               bwd_flags(a) & 3, workspace, sm);
+                               (bwd_flags(a) & 3) | bwd_scan_choice(cu, first, last, H), workspace, sm);
         if (e != hipSuccess) return KDA_ERR_DEVICE;
         ck_before += ckg;
         first = last;

@@ -54,6 +54,7 @@ struct BwdParams {
     float *dq, *dk, *dv, *dg, *dbeta, *dS0;
     int N, H;
     float scale;
+    int pt;                        // the record's RC region holds P^T (the one-workgroup scan), not R
 };
 
 // Per (chunk, head): the operands of the state-gradient scan (and E for the gradient kernel),
@@ -132,9 +133,9 @@ __global__ void __launch_bounds__(1024) bwd_plan_kernel(const int32_t *__restric
 
 // ---- per-chunk prep: A, T, W = T Diag(beta) (Gam K), E = scale Aq^T dO, R -------------------
 // One workgroup of dk/16 waves per (chunk, head).
-// PT: the scan forms R = P^T dO itself (P = scale (Gam Q - Aq W)): the record's RC region holds
-// P^T [dk][32] instead of R.
-template <int DK, typename IN_T, bool PT = false>
+// With p.pt the scan forms R = P^T dO itself (P = scale (Gam Q - Aq W)): the record's RC region
+// holds P^T [dk][32] instead of R.
+template <int DK, typename IN_T>
 __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
     constexpr int NW = DK / 16, NT = DK * 4, P = DK + 4, DV = DK;
     __shared__ __attribute__((aligned(16))) float sk[BC][P], sq[BC][P], sb[BC][P], sdo[BC][P];
@@ -316,7 +317,7 @@ __global__ void __launch_bounds__(DK * 4) bwd_prep_kernel(const BwdParams p) {
                 Qp[rt][e] = p.scale * (sq[r][i] * __expf(sb[r][i]) - aw[e]);
             }
         }
-        if constexpr (PT) {
+        if (p.pt) {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
                 *reinterpret_cast<float4 *>(rec + SR::RC + i * BC + 16 * rt + 4 * q4) =
@@ -487,7 +488,7 @@ __global__ void __launch_bounds__(256) bwd_dstate_kernel(const BwdParams p) {
 // with P^T from the record (R = P^T dO is formed here, not stored) and dO of the wave's columns.
 // Kbar, W^T and P^T are staged in LDS as hi/lo bf16 planes in the MFMA fragment layout, in two
 // buffers: after chunk r (counted from the last) has run, chunk r + 1's records go from registers
-// (loaded one step earlier) into the other buffer and chunk r + 2's are loaded, with dO of chunk
+// (loaded two steps earlier) into the other buffer and chunk r + 3's are loaded, with dO of chunk
 // r + 2.  Products: hi/lo bf16 pairs (three MFMAs), fp32 accumulation.
 template <int DK> struct DScanLds {
     static constexpr int KB = DK / 32;
@@ -505,6 +506,7 @@ template <int DK>
 __global__ void __launch_bounds__(512) bwd_dscan_hl_kernel(const BwdParams p) {
     static_assert(DK == 128, "8 waves of 16 value columns");
     constexpr int DV = DK, KB = DK / 32, KT = DK / 16, NT = 512;
+    constexpr int RPM = 1024 / NT;   // float4 rounds per staged matrix ([32][DK] or [DK][32])
     using L = DScanLds<DK>;
     using M = Mat<false>;
     using SR = ScanRec<DK>;
@@ -537,52 +539,53 @@ __global__ void __launch_bounds__(512) bwd_dscan_hl_kernel(const BwdParams p) {
     auto chunk_of = [&](int r) { return max(nch - 1 - r, 0); };
     // Addresses: a uniform (scalar) base per row or record plus one 32-bit lane offset, so that
     // no load or store keeps a 64-bit address of its own in registers.
-    const unsigned d_lane = (unsigned)(4 * q4 * DV + j0 + c);        // D[4 q4][j0 + c] in a [DK][DV] state
-    const unsigned o_lane = (unsigned)(4 * q4 * H * DV + j0 + c);    // dO[row 4 q4][h][j0 + c], relative
+    // (byte offsets: a 32-bit offset register with a scalar base)
+    const unsigned d_lane = 4u * (unsigned)(4 * q4 * DV + j0 + c);        // D[4 q4][j0 + c] of a [DK][DV] state
+    const unsigned o_lane = 4u * (unsigned)(4 * q4 * H * DV + j0 + c);    // dO[row 4 q4][h][j0 + c], relative
+    auto at = [](const float *base, unsigned byte_off) {
+        return reinterpret_cast<const float *>(reinterpret_cast<const char *>(base) + byte_off);
+    };
     // the records of a chunk: thread tid holds float4 tid + 512 u of [Kbar | W^T | P^T] and float4
     // tid % (DK / 4) of Gam_C (written by threads tid < DK / 4)
-    struct Stage { float4 x[6]; float4 gl; };
+    struct Stage { float4 x[3 * RPM]; float4 gl; };
     auto sload = [&](Stage &st, int r) {
         const float *rec = p.SCk + ((size_t)(cb0 + chunk_of(r)) * H + h) * SR::SIZE;
 #pragma unroll
-        for (int u = 0; u < 6; ++u) {
-            const unsigned f = (unsigned)tid + NT * u;
-            const float *src = u < 2 ? rec + SR::KB : u < 4 ? rec + SR::WT - 4096 : rec + SR::RC - 8192;
+        for (int u = 0; u < 3 * RPM; ++u) {
+            const unsigned f = (unsigned)tid + NT * (u % RPM);   // float4 index within its matrix
+            const float *src = u < RPM ? rec + SR::KB : u < 2 * RPM ? rec + SR::WT : rec + SR::RC;
             st.x[u] = *reinterpret_cast<const float4 *>(src + 4 * f);
         }
         st.gl = *reinterpret_cast<const float4 *>(rec + SR::GL + 4 * (unsigned)(tid & (DK / 4 - 1)));
     };
     auto swrite = [&](const Stage &st, char *buf) {
 #pragma unroll
-        for (int u = 0; u < 6; ++u) {
-            const int f = tid + NT * u;
+        for (int u = 0; u < 3 * RPM; ++u) {
+            const int f = tid + NT * (u % RPM);
             const float x[4] = {st.x[u].x, st.x[u].y, st.x[u].z, st.x[u].w};
-            if (u < 2) {
+            if (u < RPM)
                 M::template put_hl<4>(buf + L::KBAR, L::KBAR_PLANE, fofs<KB>(f / (DK / 4), 4 * (f % (DK / 4))), x);
-            } else {
-                const int g = f - (u < 4 ? 1024 : 2048);
-                M::template put_hl<4>(buf + (u < 4 ? L::WT : L::PT), L::T_PLANE, fofs<1>(g / 8, 4 * (g % 8)), x);
-            }
+            else
+                M::template put_hl<4>(buf + (u < 2 * RPM ? L::WT : L::PT), L::T_PLANE, fofs<1>(f / 8, 4 * (f % 8)), x);
         }
         if (tid < DK / 4) *reinterpret_cast<float4 *>(buf + L::GL + 16 * tid) = st.gl;
     };
     // dO of a chunk for this wave's columns, as two output tiles (rows past the chunk: zeros)
+    // (rows past the chunk's end read its last row; the step zeroes them, so that no load is
+    // waited for here)
     auto dload = [&](f32x4_t (&d)[2], int r) {
         const int jc = chunk_of(r), t0 = seq0 + BC * jc, nv = min(BC, Lq - BC * jc);
         if (nv == BC) {   // (uniform) a full chunk
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) d[rt][e] = p.dO[((size_t)(t0 + 16 * rt + e) * H + h) * DV + o_lane];
-        } else {          // the last chunk of a sequence: rows past it read its last row, then zero
+                for (int e = 0; e < 4; ++e) d[rt][e] = *at(p.dO + ((size_t)(t0 + 16 * rt + e) * H + h) * DV, o_lane);
+        } else {          // the last chunk of a sequence
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * rt + 4 * q4 + e;
-                    const float x = p.dO[((size_t)(t0 + min(t, nv - 1)) * H + h) * DV + j0 + c];
-                    d[rt][e] = t < nv ? x : 0.f;
-                }
+                for (int e = 0; e < 4; ++e)
+                    d[rt][e] = p.dO[((size_t)(t0 + min(16 * rt + 4 * q4 + e, nv - 1)) * H + h) * DV + j0 + c];
         }
     };
     // one chunk (relative index r) with its records in LDS buffer `buf` and its dO in `dcur`
@@ -592,7 +595,7 @@ __global__ void __launch_bounds__(512) bwd_dscan_hl_kernel(const BwdParams p) {
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dd[(size_t)(16 * ct + e) * DV + d_lane] = Dt[ct][e];
+            for (int e = 0; e < 4; ++e) *const_cast<float *>(at(dd + (size_t)(16 * ct + e) * DV, d_lane)) = Dt[ct][e];
         // Y = Kbar D, then -Y
         f32x4_t Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -608,7 +611,15 @@ __global__ void __launch_bounds__(512) bwd_dscan_hl_kernel(const BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) Y[rt][e] = -Y[rt][e];
         const Frag<false> yf = M::template from_tiles<true>(Y[0], Y[1]);
-        const Frag<false> of = M::template from_tiles<true>(dcur[0], dcur[1]);
+        f32x4_t dm[2];   // dO, zero past the chunk's end
+        {
+            const int nv = min(BC, Lq - BC * jc);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dm[rt][e] = 16 * rt + 4 * q4 + e < nv ? dcur[rt][e] : 0.f;
+        }
+        const Frag<false> of = M::template from_tiles<true>(dm[0], dm[1]);
         const float *gl = reinterpret_cast<const float *>(buf + L::GL);
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
@@ -621,29 +632,31 @@ __global__ void __launch_bounds__(512) bwd_dscan_hl_kernel(const BwdParams p) {
         }
     };
 
-    Stage sa;              // register stage: the records of the next chunk
+    Stage sa, sb;          // register stages: sa for even relative chunks, sb for odd
     f32x4_t da[2], db[2];  // dO: da for even relative chunks, db for odd
     sload(sa, 0);
     swrite(sa, smem);      // chunk 0 (relative) into buffer 0
-    sload(sa, 1);
+    sload(sb, 1);
+    sload(sa, 2);
     dload(da, 0);
     dload(db, 1);
-    // even r: buffer 0 and da, then chunk r + 1 from the stage into buffer 1; odd r: buffer 1 and db,
-    // then chunk r + 1 into buffer 0.  Step 0 and a last odd step are peeled so that the loop runs
-    // over whole pairs (no exit between its two steps, where the registers carried around the loop
-    // would need copies, and those copies waits for their loads).
+    // even r: buffer 0 and da, then chunk r + 1 from sb into buffer 1 and chunk r + 3 into sb; odd r:
+    // buffer 1 and db, then chunk r + 1 from sa into buffer 0 and chunk r + 3 into sa.  Step 0 and a
+    // last odd step are peeled so that the loop runs over whole pairs (no exit between its two
+    // steps, where the registers carried around the loop would need copies, and the copies waits
+    // for their loads).
     auto even = [&](int r) {
         lds_barrier();
         step(r, smem, da);
-        if (r + 1 < nch) swrite(sa, smem + L::BUF);
-        sload(sa, r + 2);
+        if (r + 1 < nch) swrite(sb, smem + L::BUF);
+        sload(sb, r + 3);
         dload(da, r + 2);
     };
     auto odd = [&](int r) {
         lds_barrier();
         step(r, smem + L::BUF, db);
         if (r + 1 < nch) swrite(sa, smem);
-        sload(sa, r + 2);
+        sload(sa, r + 3);
         dload(db, r + 2);
     };
     even(0);
@@ -1257,6 +1270,7 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     if (N == 0) return hipSuccess;
     if (states) flags |= kda::KDA_BWD_STATES_GIVEN;
     const int given = flags & kda::KDA_BWD_STATES_GIVEN;
+    const bool one_wg = flags & kda::KDA_BWD_ONE_WG_SCAN;
     flags &= kda::KDA_PRO_GATE | kda::KDA_PRO_NORM;   // the prologue bits from here on
     size_t off[12];
     kda_bwd_workspace_layout(N, H, T, dk, dk, n_ck, n_chunks, flags | given, off);
@@ -1313,14 +1327,15 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     const unsigned chunk_blocks = (unsigned)(n_chunks * H);
     const unsigned scan_blocks = (unsigned)N * (unsigned)H * (unsigned)(dk / 16);
     // (with the normalising prologue the inputs are fp32 unit vectors, the error budget bf16's)
-    // (d = 128 with bf16 error budgets: the scan takes one workgroup per chain and forms R itself)
+    // (d = 128 with bf16 error budgets, on batches that suit it: the scan takes one workgroup per
+    // chain and forms R itself)
 #define KDA_BWD(DKV, T_, HL_)                                                                                      \
     do {                                                                                                           \
-        constexpr bool ONE = DKV == 128 && HL_;                                                                    \
+        const bool one = DKV == 128 && HL_ && one_wg;                                                              \
+        p.pt = one;                                                                                                \
         if (chunk_blocks)                                                                                          \
-            hipLaunchKernelGGL((kda::bwd_prep_kernel<DKV, T_, ONE>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, \
-                               p);                                                                                 \
-        if constexpr (ONE)                                                                                         \
+            hipLaunchKernelGGL((kda::bwd_prep_kernel<DKV, T_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, p); \
+        if (one)                                                                                                   \
             hipLaunchKernelGGL((kda::bwd_dscan_hl_kernel<128>), dim3((unsigned)N * (unsigned)H), dim3(512), 0,     \
                                stream, p);                                                                         \
         else                                                                                                       \

@@ -185,6 +185,49 @@ def test_backward_from_the_forwards_states(pro):
         assert v_ <= 1e-6, (k_, v_)
 
 
+@pytest.mark.parametrize("given", [False, True])
+def test_backward_one_workgroup_scan(given):
+    """A batch of equal-length sequences with enough chains to fill the chip (4 x 150 tokens, 24
+    heads: 96 chains on 256 compute units, d = 128, bf16) takes the state-gradient scan with one
+    workgroup per chain, which forms R = P^T dO itself (ragged last chunks, S0 and dS_T): against
+    the oracle, and with the forward's states given, identical to the recomputing run."""
+    w = W.make_prefill([150] * 4, H=24, dk=128, dv=128, dtype="bf16", seed=31, s0_std=0.1)
+    do, dsf = W.make_cotangents(w, seed=31)
+    kw = {}
+    if given:
+        _, _, ck = kda.kda_chunk_fwd(to_dev(w.q, torch.bfloat16), to_dev(w.k, torch.bfloat16),
+                                     to_dev(w.v, torch.bfloat16), to_dev(w.g, torch.float32),
+                                     to_dev(w.beta, torch.float32), list(w.cu_seqlens), 1.0,
+                                     to_dev(w.s0, torch.float32), False, 32, chunk_size=32)
+        kw["states"] = ck
+    got = check(w, do, dsf, label=f"one-workgroup scan given={given}", **kw)
+    if given:
+        ref = run_bwd(w, do, dsf)
+        for n, a_, b_ in zip(NAMES, got, ref):
+            np.testing.assert_array_equal(a_, b_, err_msg=n)
+
+
+def test_backward_one_workgroup_scan_fused_prologue():
+    """The one-workgroup scan through the fused gate and normalisation (fp32 unit vectors, the
+    bf16 error budget): 4 x 150 tokens, 24 heads, d = 128, against the oracle's backward through
+    the same prologue."""
+    w = W.make_prefill_raw([150] * 4, H=24, dk=128, dv=128, seed=53, s0_std=0.1)
+    scale = 128 ** -0.5
+    do, dsf = W.make_cotangents(w, seed=53)
+    outs = kda.kda_chunk_bwd(to_dev(w.q, torch.bfloat16), to_dev(w.k, torch.bfloat16), to_dev(w.v, torch.bfloat16),
+                             to_dev(w.g, torch.bfloat16), to_dev(w.beta, torch.float32), to_dev(do, torch.float32),
+                             list(w.cu_seqlens), scale, to_dev(w.s0, torch.float32), to_dev(dsf, torch.float32),
+                             gate_preactivation=True, normalize_qk=True)
+    torch.cuda.synchronize()
+    got = [x.cpu().numpy() for x in outs]
+    ref = OB.backward_fused(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, scale, w.s0, do, dsf, normalize=True, gate=True)
+    errs = {n: W.rel_max_err(x, y) for n, x, y in zip(NAMES, got, ref)}
+    print("[bwd parity] one-workgroup scan, fused prologue: " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()),
+          flush=True)
+    for k_, v_ in errs.items():
+        assert v_ <= TOL["bf16"], (k_, v_)
+
+
 def test_backward_deterministic():
     w = W.make_prefill([150, 77], H=4, dk=128, dv=128, dtype="bf16", seed=26, s0_std=0.1)
     do, dsf = W.make_cotangents(w, seed=26)
