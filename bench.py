@@ -374,8 +374,9 @@ def measured_counters(chunk):
     return d
 
 
-def _counter_rows(folder, name_part):
-    """Per-dispatch sums (over the whole chip) of each counter for kernels whose name contains name_part."""
+def _counter_rows(folder, name_part, must=True):
+    """Per-dispatch sums (over the whole chip) of each counter for kernels whose name contains
+    name_part (none: an error, or with must=False an empty list)."""
     import csv
     import glob
     path = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
@@ -387,7 +388,7 @@ def _counter_rows(folder, name_part):
             if name_part in r["Kernel_Name"]:
                 d = per.setdefault(int(r["Dispatch_Id"]), {})
                 d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    if not per:
+    if not per and must:
         raise ValueError(f"no dispatch of a kernel matching {name_part!r} in {path[0]}")
     return list(per.values())
 
@@ -565,8 +566,11 @@ def summarize_backward_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, mf
     fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
     # (the recompute is the states-only variant of the chunk kernel, flag 4; the run's other
     # chunk32 launch is the forward that provides the states for the second timing)
+    # (the state-gradient scan is whichever of its two forms the library chose for this batch)
+    scan = "bwd_dscan_hl_kernel<128" if _counter_rows(fetch_dir, "bwd_dscan_hl_kernel<128", must=False) \
+        else "bwd_dstate_kernel<128"
     kernels = [("chunk32_kernel<128, 2, false, unsigned short, 4", "forward recompute (checkpoint every 32)"),
-               ("bwd_prep_kernel<128", "prep"), ("bwd_dstate_kernel<128", "state-gradient scan"),
+               ("bwd_prep_kernel<128", "prep"), (scan, "state-gradient scan"),
                ("bwd_grad_kernel<128", "gradients")]
     xcd, simds = 8, 1024
     lines = []
