@@ -10,6 +10,7 @@
 
 #include "kda.h"
 #include "kda_common.h"
+#include "kda_bwd_flags.h"
 
 extern "C" hipError_t kda_launch_decode(int dk, int in_bf16, int N, int H, const void *q, const void *k,
                                         const void *v, const float *g, const float *beta, float *state,

@@ -34,6 +34,7 @@
 // below them): e^{B_r - B_s} = e^{B_r - B_m} e^{B_m - B_s} with both factors within e^{40}
 // for decays g >= -5.
 #include "kda_frag.h"
+#include "kda_bwd_flags.h"
 
 namespace kda {
 

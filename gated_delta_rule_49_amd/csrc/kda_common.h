@@ -77,13 +77,8 @@ constexpr int KDA_PRO_NORM = 2;   // q and k are L2-normalised per (token, head)
 // Internal (the backward's recompute of the chunk-start states): o is neither formed nor written,
 // and q is not read.
 constexpr int KDA_STATES_ONLY = 4;
-// Internal (the backward's workspace and launch): the caller passes the states at every
-// 32-token boundary, so they are neither recomputed nor held in the workspace.
-constexpr int KDA_BWD_STATES_GIVEN = 8;
-// Internal (the backward's launch): the batch suits the state-gradient scan with one workgroup per
-// chain (sequences of nearly equal length, enough chains to fill the chip), used where the error
-// budget is bf16's at d = 128.
-constexpr int KDA_BWD_ONE_WG_SCAN = 32;
+// (KDA_BWD_STATES_GIVEN = 8 and KDA_BWD_ONE_WG_SCAN = 32, the backward's own launch flags, are in
+// kda_bwd_flags.h.)
 // Internal (the forward cut into segments; one workgroup per run): the grid covers twice the
 // launch's (segment, head) chains, and each chain runs twice, on one XCD.  "Kind 0" runs with its
 // v from the initial state that s0_idx names (a sequence's first segment: its slot, -1 zeros;
