@@ -185,13 +185,15 @@ def test_backward_from_the_forwards_states(pro):
         assert v_ <= 1e-6, (k_, v_)
 
 
-@pytest.mark.parametrize("given", [False, True])
-def test_backward_one_workgroup_scan(given):
+@pytest.mark.parametrize("given,lens", [(False, [150] * 4), (True, [150] * 4), (False, [150] * 4 + [0])])
+def test_backward_one_workgroup_scan(given, lens):
     """A batch of equal-length sequences with enough chains to fill the chip (4 x 150 tokens, 24
     heads: 96 chains on 256 compute units, d = 128, bf16) takes the state-gradient scan with one
     workgroup per chain, which forms R = P^T dO itself (ragged last chunks, S0 and dS_T): against
-    the oracle, and with the forward's states given, identical to the recomputing run."""
-    w = W.make_prefill([150] * 4, H=24, dk=128, dv=128, dtype="bf16", seed=31, s0_std=0.1)
+    the oracle, and with the forward's states given, identical to the recomputing run.  With one
+    more, empty sequence the batch still takes it (the longest is 5/4 of the mean): that chain's
+    dS0 is its dS_T."""
+    w = W.make_prefill(lens, H=24, dk=128, dv=128, dtype="bf16", seed=31, s0_std=0.1)
     do, dsf = W.make_cotangents(w, seed=31)
     kw = {}
     if given:
@@ -200,7 +202,10 @@ def test_backward_one_workgroup_scan(given):
                                      to_dev(w.beta, torch.float32), list(w.cu_seqlens), 1.0,
                                      to_dev(w.s0, torch.float32), False, 32, chunk_size=32)
         kw["states"] = ck
-    got = check(w, do, dsf, label=f"one-workgroup scan given={given}", **kw)
+    got = check(w, do, dsf, label=f"one-workgroup scan given={given} seqs={len(lens)}", **kw)
+    for n, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(got[5][n], dsf[n])
     if given:
         ref = run_bwd(w, do, dsf)
         for n, a_, b_ in zip(NAMES, got, ref):
