@@ -36,6 +36,8 @@
 #include "kda_frag.h"
 #include "kda_bwd_flags.h"
 
+#include <type_traits>
+
 namespace kda {
 
 constexpr int BC = 32;   // chunk of the backward
@@ -55,7 +57,8 @@ struct BwdParams {
     float *dq, *dk, *dv, *dg, *dbeta, *dS0;
     int N, H;
     float scale;
-    int pt;                        // the record's RC region holds P^T (the one-workgroup scan), not R
+    int pt;                        // the one-workgroup scan: the record's RC region holds P^T, not R,
+                                   // and the scan leaves Y = Kbar D in its KB region
 };
 
 // Per (chunk, head): the operands of the state-gradient scan (and E for the gradient kernel),
@@ -66,6 +69,8 @@ struct BwdParams {
 //                 update that does not depend on D, in 16x16 tiles (tile (i/16, j/16), then lane
 //                 4 (i % 16 / 4) ... as an MFMA output tile: 64 lanes x 4 values); for the
 //                 one-workgroup-per-chain scan, P^T [dk][32] (P = scale (Gam Q - Aq W)) instead
+// That scan also overwrites KB, once it has read it, with Y = Kbar D [32][dv] (D the gradient at
+// the chunk's end), which the gradient kernel then reads instead of forming it.
 template <int DK> struct ScanRec {
     static constexpr int DV = DK;
     static constexpr int KB = 0, WT = 32 * DK, ET = 64 * DK, GL = 64 * DK + 32 * DV, RC = GL + DK;
@@ -607,6 +612,14 @@ __global__ void __launch_bounds__(512) bwd_dscan_hl_kernel(const BwdParams p) {
                 mma<true, true>(Y[rt], M::template get<true>(buf + L::KBAR, L::KBAR_PLANE, fbase<KB>(rt, s, lane)), df);
             __builtin_amdgcn_sched_barrier(0);   // one K-step's fragments live at a time (registers)
         }
+        // Y into the record's KB region (read into LDS two steps ago) for the gradient kernel
+        {
+            float *const yd = p.SCk + ((size_t)(cb0 + jc) * H + h) * SR::SIZE + SR::KB;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) *const_cast<float *>(at(yd + (16 * rt + e) * DV, d_lane)) = Y[rt][e];
+        }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -795,34 +808,48 @@ bwd_grad_kernel(const BwdParams p) {
         f32x4_t X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4_t Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         // S and D tiles of column block jj, rows 16 kt + 4 q4 + e; the pair for k-tile kt + 1 loads
-        // while the pair for kt is used
+        // while the pair for kt is used.  YREC: Y = Kbar D comes from the one-workgroup scan's
+        // record, so only S is read here.
         const float *Sc = (S ? S : D) + jj, *Dc = D + jj;
-        auto ld = [&](float (&sv)[4], float (&dv4)[4], int kt) {
+        auto products = [&](auto yrec_c) {
+            constexpr bool YREC = decltype(yrec_c)::value;
+            auto ld = [&](float (&sv)[4], float (&dv4)[4], int kt) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * kt + 4 * q4 + e;
-                sv[e] = S ? Sc[(size_t)i * DV] : 0.f;
-                dv4[e] = Dc[(size_t)i * DV];
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * kt + 4 * q4 + e;
+                    sv[e] = S ? Sc[(size_t)i * DV] : 0.f;
+                    dv4[e] = YREC ? 0.f : Dc[(size_t)i * DV];
+                }
+            };
+            auto use = [&](const float (&sv)[4], const float (&dv4)[4], int kt) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const int i = 16 * kt + 4 * q4 + kk, r = 16 * rt + c;
+                        const float kv = widen(sk[r][i]), bi = sb[r][i];
+                        X[rt] = mfma_f32(kv * __expf(bi), sv[kk], X[rt]);
+                        if constexpr (!YREC) Y[rt] = mfma_f32(kv * __expf(sb[BC - 1][i] - bi), dv4[kk], Y[rt]);
+                    }
+            };
+            float sa4[4], da4[4], sb4[4], db4[4];
+            ld(sa4, da4, 0);
+            for (int kt = 0; kt < DK / 16; kt += 2) {
+                ld(sb4, db4, kt + 1);
+                use(sa4, da4, kt);
+                if (kt + 2 < DK / 16) ld(sa4, da4, kt + 2);
+                use(sb4, db4, kt + 1);
             }
         };
-        auto use = [&](const float (&sv)[4], const float (&dv4)[4], int kt) {
+        if (p.pt) {
+            const float *yr = p.SCk + cb * ScanRec<DK>::SIZE + ScanRec<DK>::KB + jj;
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int i = 16 * kt + 4 * q4 + kk, r = 16 * rt + c;
-                    const float kv = widen(sk[r][i]), bi = sb[r][i];
-                    X[rt] = mfma_f32(kv * __expf(bi), sv[kk], X[rt]);
-                    Y[rt] = mfma_f32(kv * __expf(sb[BC - 1][i] - bi), dv4[kk], Y[rt]);
-                }
-        };
-        float sa4[4], da4[4], sb4[4], db4[4];
-        ld(sa4, da4, 0);
-        for (int kt = 0; kt < DK / 16; kt += 2) {
-            ld(sb4, db4, kt + 1);
-            use(sa4, da4, kt);
-            if (kt + 2 < DK / 16) ld(sa4, da4, kt + 2);
-            use(sb4, db4, kt + 1);
+                for (int e = 0; e < 4; ++e) Y[rt][e] = yr[(16 * rt + 4 * q4 + e) * DV];
+            products(std::true_type{});
+        } else {
+            products(std::false_type{});
         }
         // dU = E + Kbar D, then dZ = T^T dU
         const float *ET = p.SCk + cb * ScanRec<DK>::SIZE + ScanRec<DK>::ET + jj * BC;
