@@ -36,6 +36,7 @@
 #include "kda_frag.h"
 #include "kda_bwd_flags.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace kda {
@@ -1255,6 +1256,42 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk(
     const int32_t *s0_idx, const int32_t *ck_idx, int nslots, int flags, void *workspace, hipStream_t stream);
 extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_plan(int N, const int32_t *cu, int every,
                                                                            void *workspace, hipStream_t stream);
+extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk32_split(int dk, int in_bf16, unsigned chains,
+                                                                                    const kda::ChunkParams &p,
+                                                                                    int max_split, hipStream_t stream);
+
+namespace {
+// A second stream per device, on which the forward recompute runs beside the one-workgroup
+// state-gradient scan (neither needs the other's results), with the events that fork it from the
+// caller's stream and join it back.  Created on first use (default priority) and kept until the
+// process ends; g_side_mu orders the record / wait pairs of concurrent callers.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+// (with g_side_mu held) the current device's side stream; null when it cannot be had
+SideStream *side_stream() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    SideStream &ss = g_side[dev];
+    if (!ss.s) {
+        hipStream_t st = nullptr;
+        hipEvent_t a = nullptr, b = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+            if (a) (void)hipEventDestroy(a);
+            (void)hipStreamDestroy(st);
+            return nullptr;
+        }
+        ss.s = st; ss.fork = a; ss.join = b;
+    }
+    return &ss;
+}
+}  // namespace
 
 // The fused prologue's outputs, materialised (one wave per (token, head) row; see prologue_kernel):
 // with KDA_PRO_NORM fp32 q / |q|, k / |k| and v into qn, kn, vf; with KDA_PRO_GATE fp32 g, beta.
@@ -1326,7 +1363,12 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     // reads the materialised inputs
     // (given by the caller instead: the launch plan alone)
     const bool fused_fwd = flags && dk == 128;
-    if (given)
+    // With the one-workgroup scan on few chains (two workgroups per chain fit the chip), the
+    // recompute runs on the side stream, one workgroup per chain, at the same time as the scan;
+    // the plan is made here first for both.  Otherwise it runs before everything else.
+    const bool side = !given && one_wg && dk == 128 && (in_bf16 || raw_bf16) &&
+                      2LL * N * H <= (long long)kda_cu_count();
+    if (given || side)
         e = kda_launch_plan(N, cu, kda::BC, ws, stream);
     else
         e = kda_launch_chunk(32, dk, fused_fwd ? raw_bf16 : in_bf16, N, H, fused_fwd ? q_raw : q,
@@ -1337,6 +1379,40 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     if (e != hipSuccess) return e;
     size_t order_off, base_off;
     kda_chunk_workspace_layout(N, &order_off, &base_off);
+    // the side stream's recompute: forked after the prep kernel (so that it shares the chip with
+    // the scan, not with the prep), joined before the gradient kernel
+    auto fork_recompute = [&]() -> hipError_t {
+        kda::ChunkParams cp;
+        cp.q = fused_fwd ? q_raw : q; cp.k = fused_fwd ? k_raw : k; cp.v = fused_fwd ? v_raw : v;
+        cp.g = fused_fwd ? a_raw : g; cp.beta = fused_fwd ? b_raw : beta;
+        cp.cu_seqlens = cu;
+        cp.order = reinterpret_cast<const int32_t *>(ws + order_off);
+        cp.ckpt_base = reinterpret_cast<const int64_t *>(ws + base_off);
+        cp.s0 = s0; cp.sf = nullptr; cp.ckpt = reinterpret_cast<float *>(ws + off[1]); cp.o = nullptr;
+        cp.s0_idx = nullptr; cp.ck_idx = nullptr; cp.nslots = 0; cp.s0_slots = 0;
+        cp.flags = (fused_fwd ? flags : 0) | kda::KDA_STATES_ONLY;
+        cp.H = H; cp.every = kda::BC; cp.scale = scale; cp.nseq = N;
+        cp.o_tr = nullptr; cp.ckpt_tr = nullptr;
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        SideStream *ss = side_stream();
+        if (!ss)   // no side stream: the recompute goes first on the caller's stream instead
+            return kda_launch_chunk32_split(dk, fused_fwd ? raw_bf16 : in_bf16, (unsigned)N * (unsigned)H, cp, 2,
+                                            stream);
+        hipError_t r;
+        if ((r = hipEventRecord(ss->fork, stream)) != hipSuccess) return r;
+        if ((r = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return r;
+        if ((r = kda_launch_chunk32_split(dk, fused_fwd ? raw_bf16 : in_bf16, (unsigned)N * (unsigned)H, cp, 1,
+                                          ss->s)) != hipSuccess)
+            return r;
+        return hipEventRecord(ss->join, ss->s);
+    };
+    // (a later caller may have recorded the join event again since: its recompute was queued on the
+    // side stream after this one, so waiting for it also covers this one)
+    auto join_recompute = [&]() -> hipError_t {
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        SideStream *ss = side_stream();
+        return ss ? hipStreamWaitEvent(stream, ss->join, 0) : hipSuccess;
+    };
     kda::BwdParams p;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu = cu;
     p.order = reinterpret_cast<const int32_t *>(ws + order_off);
@@ -1363,11 +1439,13 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
         p.pt = one;                                                                                                \
         if (chunk_blocks)                                                                                          \
             hipLaunchKernelGGL((kda::bwd_prep_kernel<DKV, T_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, p); \
+        if (side && (e = fork_recompute()) != hipSuccess) return e;                                                \
         if (one)                                                                                                   \
             hipLaunchKernelGGL((kda::bwd_dscan_hl_kernel<128>), dim3((unsigned)N * (unsigned)H), dim3(512), 0,     \
                                stream, p);                                                                         \
         else                                                                                                       \
             hipLaunchKernelGGL((kda::bwd_dstate_kernel<DKV>), dim3(scan_blocks), dim3(256), 0, stream, p);         \
+        if (side && (e = join_recompute()) != hipSuccess) return e;                                                \
         if (chunk_blocks)                                                                                          \
             hipLaunchKernelGGL((kda::bwd_grad_kernel<DKV, T_, HL_>), dim3(chunk_blocks), dim3(DKV * 4), 0, stream, \
                                p);                                                                                 \

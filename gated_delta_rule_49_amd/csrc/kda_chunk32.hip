@@ -947,11 +947,13 @@ chunk32_kernel(const ChunkParams p) {
 
 }  // namespace kda
 
+// max_split 1 keeps one workgroup per chain, for a launch that shares the chip with another kernel.
 extern "C" __attribute__((visibility("hidden"))) hipError_t
-kda_launch_chunk32(int dk, int in_bf16, unsigned chains, const kda::ChunkParams &p, hipStream_t stream) {
+kda_launch_chunk32_split(int dk, int in_bf16, unsigned chains, const kda::ChunkParams &p, int max_split,
+                         hipStream_t stream) {
     // One workgroup per (sequence, head) chain; when the chains would leave more than half the
     // compute units idle, split each chain's value columns over two workgroups.
-    const int split = (long long)chains * 2 <= kda_cu_count() ? 2 : 1;
+    const int split = max_split >= 2 && (long long)chains * 2 <= kda_cu_count() ? 2 : 1;
 #define KDA_C32(DKV, SP, F32P, T, PRO)                                                                   \
     hipLaunchKernelGGL((kda::chunk32_kernel<DKV, SP, F32P, T, PRO>),                                    \
                        dim3(chains * SP * (((PRO) & kda::KDA_TRANSITION) ? 2 : 1)),                     \
@@ -1002,4 +1004,9 @@ kda_launch_chunk32(int dk, int in_bf16, unsigned chains, const kda::ChunkParams 
 #undef KDA_C32_DT
 #undef KDA_C32
     return hipGetLastError();
+}
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t
+kda_launch_chunk32(int dk, int in_bf16, unsigned chains, const kda::ChunkParams &p, hipStream_t stream) {
+    return kda_launch_chunk32_split(dk, in_bf16, chains, p, 2, stream);
 }

@@ -190,9 +190,12 @@ def test_backward_one_workgroup_scan(given, lens):
     """A batch of equal-length sequences with enough chains to fill the chip (4 x 150 tokens, 24
     heads: 96 chains on 256 compute units, d = 128, bf16) takes the state-gradient scan with one
     workgroup per chain, which forms R = P^T dO itself (ragged last chunks, S0 and dS_T): against
-    the oracle, and with the forward's states given, identical to the recomputing run.  With one
-    more, empty sequence the batch still takes it (the longest is 5/4 of the mean): that chain's
-    dS0 is its dS_T."""
+    the oracle, and with the forward's states given, against the recomputing run.  That run
+    recomputes the states beside the scan with one workgroup per chain, where the forward took two,
+    so the two agree to the states' fp32 rounding, not bit for bit: the bar, 1e-4 of each
+    gradient's RMS, is 200 times below the bf16 bar (wrong states would miss it by orders of
+    magnitude).  With one more, empty sequence the batch still takes it (the longest is 5/4 of
+    the mean): that chain's dS0 is its dS_T."""
     w = W.make_prefill(lens, H=24, dk=128, dv=128, dtype="bf16", seed=31, s0_std=0.1)
     do, dsf = W.make_cotangents(w, seed=31)
     kw = {}
@@ -208,8 +211,11 @@ def test_backward_one_workgroup_scan(given, lens):
             assert np.array_equal(got[5][n], dsf[n])
     if given:
         ref = run_bwd(w, do, dsf)
-        for n, a_, b_ in zip(NAMES, got, ref):
-            np.testing.assert_array_equal(a_, b_, err_msg=n)
+        errs = {n: W.rel_max_err(a_, b_) for n, a_, b_ in zip(NAMES, got, ref)}
+        print("[bwd parity] given states vs recomputed beside the scan: "
+              + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+        for k_, v_ in errs.items():
+            assert v_ <= 1e-4, (k_, v_)
 
 
 def test_backward_one_workgroup_scan_fused_prologue():
