@@ -569,7 +569,11 @@ def summarize_backward_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, mf
     # (the state-gradient scan is whichever of its two forms the library chose for this batch)
     scan = "bwd_dscan_hl_kernel<128" if _counter_rows(fetch_dir, "bwd_dscan_hl_kernel<128", must=False) \
         else "bwd_dstate_kernel<128"
-    kernels = [("chunk32_kernel<128, 2, false, unsigned short, 4", "forward recompute (checkpoint every 32)"),
+    # (the recompute takes one workgroup per chain when it runs beside the one-workgroup scan)
+    rec = "chunk32_kernel<128, 1, false, unsigned short, 4" \
+        if _counter_rows(fetch_dir, "chunk32_kernel<128, 1, false, unsigned short, 4", must=False) \
+        else "chunk32_kernel<128, 2, false, unsigned short, 4"
+    kernels = [(rec, "forward recompute (checkpoint every 32)"),
                ("bwd_prep_kernel<128", "prep"), (scan, "state-gradient scan"),
                ("bwd_grad_kernel<128", "gradients")]
     xcd, simds = 8, 1024
@@ -684,7 +688,10 @@ def summarize_backward_trace(trace_dir, bench_log):
         f.write(f"Workload: {b['workload']}.\n\n")
         f.write(f"bench.py HIP-event median of one backward (same process): {b['ms']} ms "
                 f"({b['value']:.0f} tokens/s); sum of the per-kernel rocprof averages below: {total:.3f} ms (prep, scan and gradient kernels "
-                "averaged over both timings, recomputing and reading the forward's states: the same work).\n\n")
+                "averaged over both timings, recomputing and reading the forward's states: the same work).  "
+                "When the scan takes one workgroup per chain on few chains, the states-only recompute "
+                "(`chunk32_kernel<..., 4>`) runs on a second stream beside the scan, so their times overlap "
+                "and the sum exceeds the wall time.\n\n")
         f.write("Command:\n\n    rocprofv3 --kernel-trace --stats -d " + trace_dir + " -o run --output-format csv "
                 "-- python -u bench.py --backward " + ("--prologue " if fused else "") + "--steps 5 --warmup 1\n\n")
         f.write("| kernel | calls | average (ms) | min (ms) | max (ms) |\n|---|---|---|---|---|\n")

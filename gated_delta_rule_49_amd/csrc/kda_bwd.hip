@@ -60,6 +60,7 @@ struct BwdParams {
     float scale;
     int pt;                        // the one-workgroup scan: the record's RC region holds P^T, not R,
                                    // and the scan leaves Y = Kbar D in its KB region
+    int rrec;                      // (with pt) the recompute left R = V - (Gam K) S in the record (RR)
 };
 
 // Per (chunk, head): the operands of the state-gradient scan (and E for the gradient kernel),
@@ -71,10 +72,12 @@ struct BwdParams {
 //                 4 (i % 16 / 4) ... as an MFMA output tile: 64 lanes x 4 values); for the
 //                 one-workgroup-per-chain scan, P^T [dk][32] (P = scale (Gam Q - Aq W)) instead
 // That scan also overwrites KB, once it has read it, with Y = Kbar D [32][dv] (D the gradient at
-// the chunk's end), which the gradient kernel then reads instead of forming it.
+// the chunk's end), and the states-only recompute that runs with it leaves R = V - (Gam K) S
+// [32][dv] in RC after P^T (RR): the gradient kernel reads both instead of forming them.
 template <int DK> struct ScanRec {
     static constexpr int DV = DK;
     static constexpr int KB = 0, WT = 32 * DK, ET = 64 * DK, GL = 64 * DK + 32 * DV, RC = GL + DK;
+    static constexpr int RR = RC + DK * 32;
     static constexpr int SIZE = RC + DK * DV;
 };
 
@@ -842,13 +845,23 @@ bwd_grad_kernel(const BwdParams p) {
                 use(sb4, db4, kt + 1);
             }
         };
+        // (with rrec, X holds -R, read from the record: R = V - X below then takes no V)
+        const bool rrec = p.pt && p.rrec;
         if (p.pt) {
             const float *yr = p.SCk + cb * ScanRec<DK>::SIZE + ScanRec<DK>::KB + jj;
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Y[rt][e] = yr[(16 * rt + 4 * q4 + e) * DV];
-            products(std::true_type{});
+            if (rrec) {
+                const float *rr = p.SCk + cb * ScanRec<DK>::SIZE + ScanRec<DK>::RR + jj;
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) X[rt][e] = -rr[(16 * rt + 4 * q4 + e) * DV];
+            } else {
+                products(std::true_type{});
+            }
         } else {
             products(std::false_type{});
         }
@@ -881,7 +894,7 @@ bwd_grad_kernel(const BwdParams p) {
                 const int s = 16 * st + 4 * q4 + e;
                 const bool ok = s < nv;
                 const size_t off = ((size_t)(t0 + s) * H + h) * DV + jj;
-                const float R = (ok ? load_in(vg + off) : 0.f) - X[st][e];
+                const float R = ok ? (rrec ? 0.f : load_in(vg + off)) - X[st][e] : 0.f;
                 const float bs = sbeta[s];
                 Zv[st][e] = bs * R;
                 if (ok) p.dv[off] = bs * dZ[st][e];
@@ -1366,9 +1379,17 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     // With the one-workgroup scan on few chains (two workgroups per chain fit the chip), the
     // recompute runs on the side stream, one workgroup per chain, at the same time as the scan;
     // the plan is made here first for both.  Otherwise it runs before everything else.
-    const bool side = !given && one_wg && dk == 128 && (in_bf16 || raw_bf16) &&
-                      2LL * N * H <= (long long)kda_cu_count();
-    if (given || side)
+    // With the one-workgroup scan (d = 128, bf16 error budget) the recompute is launched here (own):
+    // it also leaves R = V - (Gam K) S in each chunk's record for the gradient kernel.  On few
+    // chains (two workgroups per chain fit the chip) it runs on the side stream, one workgroup per
+    // chain, at the same time as the scan; otherwise first, on the caller's stream.
+    const bool own = !given && one_wg && dk == 128 && (in_bf16 || raw_bf16);
+    const bool side = own && 2LL * N * H <= (long long)kda_cu_count();
+    // chunk bases first: the recompute's R records are indexed by them
+    hipLaunchKernelGGL(kda::bwd_plan_kernel, dim3(1), dim3(1024), 0, stream, cu, N,
+                       reinterpret_cast<int32_t *>(ws + off[0]));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (given || own)
         e = kda_launch_plan(N, cu, kda::BC, ws, stream);
     else
         e = kda_launch_chunk(32, dk, fused_fwd ? raw_bf16 : in_bf16, N, H, fused_fwd ? q_raw : q,
@@ -1379,31 +1400,36 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     if (e != hipSuccess) return e;
     size_t order_off, base_off;
     kda_chunk_workspace_layout(N, &order_off, &base_off);
+    kda::ChunkParams cp;
+    cp.q = fused_fwd ? q_raw : q; cp.k = fused_fwd ? k_raw : k; cp.v = fused_fwd ? v_raw : v;
+    cp.g = fused_fwd ? a_raw : g; cp.beta = fused_fwd ? b_raw : beta;
+    cp.cu_seqlens = cu;
+    cp.order = reinterpret_cast<const int32_t *>(ws + order_off);
+    cp.ckpt_base = reinterpret_cast<const int64_t *>(ws + base_off);
+    cp.s0 = s0; cp.sf = nullptr; cp.ckpt = reinterpret_cast<float *>(ws + off[1]); cp.o = nullptr;
+    cp.s0_idx = nullptr; cp.ck_idx = nullptr; cp.nslots = 0; cp.s0_slots = 0;
+    cp.flags = (fused_fwd ? flags : 0) | kda::KDA_STATES_ONLY;
+    cp.H = H; cp.every = kda::BC; cp.scale = scale; cp.nseq = N;
+    cp.o_tr = nullptr; cp.ckpt_tr = nullptr;
+    cp.rres = own ? reinterpret_cast<float *>(ws + off[4]) + kda::ScanRec<128>::RR : nullptr;
+    cp.rbase = reinterpret_cast<const int32_t *>(ws + off[0]);
+    cp.rstride = kda::ScanRec<128>::SIZE;
+    const int rec_bf16 = fused_fwd ? raw_bf16 : in_bf16;
+    const unsigned chains = (unsigned)N * (unsigned)H;
+    if (own && !side &&
+        (e = kda_launch_chunk32_split(dk, rec_bf16, chains, cp, 2, stream)) != hipSuccess)
+        return e;
     // the side stream's recompute: forked after the prep kernel (so that it shares the chip with
     // the scan, not with the prep), joined before the gradient kernel
     auto fork_recompute = [&]() -> hipError_t {
-        kda::ChunkParams cp;
-        cp.q = fused_fwd ? q_raw : q; cp.k = fused_fwd ? k_raw : k; cp.v = fused_fwd ? v_raw : v;
-        cp.g = fused_fwd ? a_raw : g; cp.beta = fused_fwd ? b_raw : beta;
-        cp.cu_seqlens = cu;
-        cp.order = reinterpret_cast<const int32_t *>(ws + order_off);
-        cp.ckpt_base = reinterpret_cast<const int64_t *>(ws + base_off);
-        cp.s0 = s0; cp.sf = nullptr; cp.ckpt = reinterpret_cast<float *>(ws + off[1]); cp.o = nullptr;
-        cp.s0_idx = nullptr; cp.ck_idx = nullptr; cp.nslots = 0; cp.s0_slots = 0;
-        cp.flags = (fused_fwd ? flags : 0) | kda::KDA_STATES_ONLY;
-        cp.H = H; cp.every = kda::BC; cp.scale = scale; cp.nseq = N;
-        cp.o_tr = nullptr; cp.ckpt_tr = nullptr;
         std::lock_guard<std::mutex> lock(g_side_mu);
         SideStream *ss = side_stream();
-        if (!ss)   // no side stream: the recompute goes first on the caller's stream instead
-            return kda_launch_chunk32_split(dk, fused_fwd ? raw_bf16 : in_bf16, (unsigned)N * (unsigned)H, cp, 2,
-                                            stream);
+        if (!ss)   // no side stream: the recompute goes on the caller's stream, before the scan
+            return kda_launch_chunk32_split(dk, rec_bf16, chains, cp, 2, stream);
         hipError_t r;
         if ((r = hipEventRecord(ss->fork, stream)) != hipSuccess) return r;
         if ((r = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return r;
-        if ((r = kda_launch_chunk32_split(dk, fused_fwd ? raw_bf16 : in_bf16, (unsigned)N * (unsigned)H, cp, 1,
-                                          ss->s)) != hipSuccess)
-            return r;
+        if ((r = kda_launch_chunk32_split(dk, rec_bf16, chains, cp, 1, ss->s)) != hipSuccess) return r;
         return hipEventRecord(ss->join, ss->s);
     };
     // (a later caller may have recorded the join event again since: its recompute was queued on the
@@ -1425,9 +1451,7 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
     p.TAk = reinterpret_cast<float *>(ws + off[5]);
     p.dq = dq; p.dk = dkk; p.dv = dv; p.dg = dg; p.dbeta = dbeta; p.dS0 = dS0;
     p.N = N; p.H = H; p.scale = scale;
-    hipLaunchKernelGGL(kda::bwd_plan_kernel, dim3(1), dim3(1024), 0, stream, cu, N,
-                       reinterpret_cast<int32_t *>(ws + off[0]));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    p.rrec = own;
     const unsigned chunk_blocks = (unsigned)(n_chunks * H);
     const unsigned scan_blocks = (unsigned)N * (unsigned)H * (unsigned)(dk / 16);
     // (with the normalising prologue the inputs are fp32 unit vectors, the error budget bf16's)

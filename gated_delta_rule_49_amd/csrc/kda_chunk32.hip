@@ -66,6 +66,8 @@ struct Lds32 {
     static constexpr int QT_AT = QT - 16 * DK * ES;
     static constexpr int KG = QT + 16 * DK * 4;           // [16][DK] single: Gamma * K, rows 16..31
     static constexpr int KG_AT = KG - 16 * DK * ES;
+    // states-only runs keep KS and KG as hl, their lo planes in the unused QS and QT
+    static constexpr int KG_LO = QT - KG;                 // (a negative plane distance)
     static constexpr int KHT = KG + 16 * DK * ES;         // 2 x [DK][32] hl: (e^{G_last-G} K)^T
     static constexpr int KHT_PLANE = DK * 32 * ES;
     static constexpr int KHT_BUF = DK * 32 * 4;
@@ -515,16 +517,19 @@ chunk32_kernel(const ChunkParams p) {
                     for (int jt = 0; jt < JT; ++jt) Oacc[rt][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < KB; ++s) {
-                    const F fk0 = M::template get<false>(sm + L::KS, 0, fbase<KB>(0, s, lane));
-                    const F fk1 = M::template get<false>(sm + L::KG_AT, 0, fbase<KB>(1, s, lane));
                     if constexpr (SO) {
+                        // hi/lo products: R = -Yacc is handed to the backward's gradient kernel
+                        const F fk0 = M::template get<true>(sm + L::KS, L::SQ_PLANE, fbase<KB>(0, s, lane));
+                        const F fk1 = M::template get<true>(sm + L::KG_AT, L::KG_LO, fbase<KB>(1, s, lane));
 #pragma unroll
                         for (int jt = 0; jt < JT; ++jt) {
-                            const F sf = M::template from_tiles<false>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
-                            mma<false, false>(Yacc[0][jt], fk0, sf);
-                            mma<false, false>(Yacc[1][jt], fk1, sf);
+                            const F sf = M::template from_tiles<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
+                            mma<true, true>(Yacc[0][jt], fk0, sf);
+                            mma<true, true>(Yacc[1][jt], fk1, sf);
                         }
                     } else {
+                        const F fk0 = M::template get<false>(sm + L::KS, 0, fbase<KB>(0, s, lane));
+                        const F fk1 = M::template get<false>(sm + L::KG_AT, 0, fbase<KB>(1, s, lane));
                         const F fq0 = M::template get<true>(sm + L::QS, L::SQ_PLANE, fbase<KB>(0, s, lane));
                         const F fq1 = M::template get<true>(sm + L::QT_AT, L::QT_PLANE, fbase<KB>(1, s, lane));
 #pragma unroll
@@ -535,6 +540,21 @@ chunk32_kernel(const ChunkParams p) {
                             mma<true, true>(Oacc[1][jt], fq1, sf);
                             mma<false, false>(Yacc[1][jt], fk1, sf);
                         }
+                    }
+                }
+                if constexpr (SO) {
+                    if (p.rres) {   // R = V - (Gamma K) S of chunk it
+                        float *const rb = p.rres + ((long long)(p.rbase[n] + it) * H + h) * p.rstride + col0 +
+                                          SWC * sw + JT * lr;
+#pragma unroll
+                        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float x[JT];
+#pragma unroll
+                                for (int jt = 0; jt < JT; ++jt) x[jt] = -Yacc[rt][jt][e];
+                                store_cols<JT>(rb + (unsigned)((16 * rt + 4 * lq + e) * DV), x);
+                            }
                     }
                 }
                 // park the output partials in LDS until stage o (this lane's private slots)
@@ -883,14 +903,20 @@ chunk32_kernel(const ChunkParams p) {
                         // (e^{G_last-G} K)^T entry: sub-chunk 0 decays on through sub-chunk 1
                         kh[c][i] = SA ? ke[c] : ke[c] * P1[c];
                     }
-                    M::put_h2(sm + L::KS, ks_off[i], ks[0], ks[1]);
+                    if constexpr (SO) M::template put_hl<2>(sm + L::KS, L::SQ_PLANE, ks_off[i], ks);
+                    else M::put_h2(sm + L::KS, ks_off[i], ks[0], ks[1]);
                     if constexpr (!SO) M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, ks_off[i], qs);
                     // Kn rows (K e^{G_ref(a) - G}): sub-chunk 0 feeds tiles (0,0) and (1,0), sub-chunk 1 (1,1)
                     M::template put_hl<2>(sm + L::KN, L::KN_PLANE, kn_off[i], kd);
                     if (SA) {
                         // Gamma * K and Gamma * Q of rows 16..31 (decay from the chunk start): read by
                         // the (1,0) Gram tiles in segment 3 and by stage a in segment 1 of the next iteration
-                        M::put_h2(sm + L::KG_AT, ks_off[i], ks[0] * P0[0], ks[1] * P0[1]);
+                        if constexpr (SO) {
+                            const float kg2[2] = {ks[0] * P0[0], ks[1] * P0[1]};
+                            M::template put_hl<2>(sm + L::KG_AT, L::KG_LO, ks_off[i], kg2);
+                        } else {
+                            M::put_h2(sm + L::KG_AT, ks_off[i], ks[0] * P0[0], ks[1] * P0[1]);
+                        }
                         if constexpr (!SO) {
                             const float qt[2] = {qs[0] * P0[0], qs[1] * P0[1]};
                             M::template put_hl<2>(sm + L::QT_AT, L::QT_PLANE, ks_off[i], qt);

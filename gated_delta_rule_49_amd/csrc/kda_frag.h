@@ -217,6 +217,11 @@ struct ChunkParams {
     int nseq;                      // sequences of this launch (the paired segment pass indexes its states by it)
     float *o_tr;                   // the paired segment pass: outputs of the transition runs, [T, H, dk]
     float *ckpt_tr;                // the paired segment pass: their checkpoints, dense [M, H, dk, dk]
+    // states-only runs: when set, R = V - (Gamma K) S of every chunk, [32][dv] fp32 (zero rows past
+    // a sequence's end), at rres + ((rbase[n] + chunk) H + h) rstride
+    float *rres = nullptr;
+    const int32_t *rbase = nullptr;
+    long long rstride = 0;
 };
 
 // Element offset of the initial state of (n, h) in p.s0, or -1 for a zero state (no initial

@@ -191,10 +191,10 @@ def test_backward_one_workgroup_scan(given, lens):
     heads: 96 chains on 256 compute units, d = 128, bf16) takes the state-gradient scan with one
     workgroup per chain, which forms R = P^T dO itself (ragged last chunks, S0 and dS_T): against
     the oracle, and with the forward's states given, against the recomputing run.  That run
-    recomputes the states beside the scan with one workgroup per chain, where the forward took two,
-    so the two agree to the states' fp32 rounding, not bit for bit: the bar, 1e-4 of each
-    gradient's RMS, is 200 times below the bf16 bar (wrong states would miss it by orders of
-    magnitude).  With one more, empty sequence the batch still takes it (the longest is 5/4 of
+    recomputes the states beside the scan with one workgroup per chain (the forward took two) and
+    hi/lo products for (Gamma K) S, whose R = V - (Gamma K) S it hands to the gradient kernel, so
+    the two agree to the states' rounding, not bit for bit: the bar, 1e-4 of each gradient's RMS,
+    is 200 times below the bf16 bar (wrong states would miss it by orders of magnitude).  With one more, empty sequence the batch still takes it (the longest is 5/4 of
     the mean): that chain's dS0 is its dS_T."""
     w = W.make_prefill(lens, H=24, dk=128, dv=128, dtype="bf16", seed=31, s0_std=0.1)
     do, dsf = W.make_cotangents(w, seed=31)
