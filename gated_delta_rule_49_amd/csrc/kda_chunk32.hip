@@ -66,7 +66,7 @@ struct Lds32 {
     static constexpr int QT_AT = QT - 16 * DK * ES;
     static constexpr int KG = QT + 16 * DK * 4;           // [16][DK] single: Gamma * K, rows 16..31
     static constexpr int KG_AT = KG - 16 * DK * ES;
-    // states-only runs keep KS and KG as hl, their lo planes in the unused QS and QT
+    // states-only runs that hand R on keep KS and KG as hl, their lo planes in the unused QS and QT
     static constexpr int KG_LO = QT - KG;                 // (a negative plane distance)
     static constexpr int KHT = KG + 16 * DK * ES;         // 2 x [DK][32] hl: (e^{G_last-G} K)^T
     static constexpr int KHT_PLANE = DK * 32 * ES;
@@ -518,14 +518,25 @@ chunk32_kernel(const ChunkParams p) {
 #pragma unroll
                 for (int s = 0; s < KB; ++s) {
                     if constexpr (SO) {
-                        // hi/lo products: R = -Yacc is handed to the backward's gradient kernel
-                        const F fk0 = M::template get<true>(sm + L::KS, L::SQ_PLANE, fbase<KB>(0, s, lane));
-                        const F fk1 = M::template get<true>(sm + L::KG_AT, L::KG_LO, fbase<KB>(1, s, lane));
+                        if (p.rres) {
+                            // hi/lo products: R = -Yacc is handed to the backward's gradient kernel
+                            const F fk0 = M::template get<true>(sm + L::KS, L::SQ_PLANE, fbase<KB>(0, s, lane));
+                            const F fk1 = M::template get<true>(sm + L::KG_AT, L::KG_LO, fbase<KB>(1, s, lane));
 #pragma unroll
-                        for (int jt = 0; jt < JT; ++jt) {
-                            const F sf = M::template from_tiles<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
-                            mma<true, true>(Yacc[0][jt], fk0, sf);
-                            mma<true, true>(Yacc[1][jt], fk1, sf);
+                            for (int jt = 0; jt < JT; ++jt) {
+                                const F sf = M::template from_tiles<true>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
+                                mma<true, true>(Yacc[0][jt], fk0, sf);
+                                mma<true, true>(Yacc[1][jt], fk1, sf);
+                            }
+                        } else {
+                            const F fk0 = M::template get<false>(sm + L::KS, 0, fbase<KB>(0, s, lane));
+                            const F fk1 = M::template get<false>(sm + L::KG_AT, 0, fbase<KB>(1, s, lane));
+#pragma unroll
+                            for (int jt = 0; jt < JT; ++jt) {
+                                const F sf = M::template from_tiles<false>(Sr[jt][2 * s], Sr[jt][2 * s + 1]);
+                                mma<false, false>(Yacc[0][jt], fk0, sf);
+                                mma<false, false>(Yacc[1][jt], fk1, sf);
+                            }
                         }
                     } else {
                         const F fk0 = M::template get<false>(sm + L::KS, 0, fbase<KB>(0, s, lane));
@@ -903,7 +914,7 @@ chunk32_kernel(const ChunkParams p) {
                         // (e^{G_last-G} K)^T entry: sub-chunk 0 decays on through sub-chunk 1
                         kh[c][i] = SA ? ke[c] : ke[c] * P1[c];
                     }
-                    if constexpr (SO) M::template put_hl<2>(sm + L::KS, L::SQ_PLANE, ks_off[i], ks);
+                    if (SO && p.rres) M::template put_hl<2>(sm + L::KS, L::SQ_PLANE, ks_off[i], ks);
                     else M::put_h2(sm + L::KS, ks_off[i], ks[0], ks[1]);
                     if constexpr (!SO) M::template put_hl<2>(sm + L::QS, L::SQ_PLANE, ks_off[i], qs);
                     // Kn rows (K e^{G_ref(a) - G}): sub-chunk 0 feeds tiles (0,0) and (1,0), sub-chunk 1 (1,1)
@@ -911,7 +922,7 @@ chunk32_kernel(const ChunkParams p) {
                     if (SA) {
                         // Gamma * K and Gamma * Q of rows 16..31 (decay from the chunk start): read by
                         // the (1,0) Gram tiles in segment 3 and by stage a in segment 1 of the next iteration
-                        if constexpr (SO) {
+                        if (SO && p.rres) {
                             const float kg2[2] = {ks[0] * P0[0], ks[1] * P0[1]};
                             M::template put_hl<2>(sm + L::KG_AT, L::KG_LO, ks_off[i], kg2);
                         } else {
