@@ -8,8 +8,10 @@ decode step of the decode workload (256 sequences x 96 heads, fp32 state
 (workloads.make_workload) resident in HBM before the timed region.
 
 Prints ONE JSON line: value = prefill tokens/s; decode GB/s and the roofline
-of the dominant kernel are reported beside it; cpu_baseline times the fp64 CPU
-oracle on a bounded sample of the prefill workload on the host cores.
+of the dominant kernel are reported beside it, and (each timed on its own after
+the step) the prefill of the T=4096 and varlen workloads, the prefill through
+the fused prologue and the backward on the prefill's shape; cpu_baseline times
+the fp64 CPU oracle on a bounded sample of the prefill workload on the host cores.
 """
 from __future__ import annotations
 
@@ -337,6 +339,12 @@ def main():
             r = other_workload(2, args.chunk, max(5, min(K, 20)), 2, prologue=True, emit=False)
             res["prefill"]["prologue"] = {"ms": r["ms"], "tokens_per_s": r["value"],
                                           "over_plain": round(r["ms"] / pre_avg, 4), "workload": r["workload"]}
+            torch.cuda.empty_cache()
+            # the backward (kda_chunk_bwd) on the prefill's shape, timed on its own
+            r = backward_workload(max(3, min(K, 10)), 1, emit=False)
+            res["backward"] = {key: r[key] for key in ("workload", "ms", "value", "unit", "alg_GBps",
+                                                        "frac_of_hbm_peak", "workspace_GB")}
+            res["backward"]["with_forward_states_ms"] = r["with_forward_states"]["ms"]
             torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
@@ -833,7 +841,7 @@ def bwd_alg_bytes(T, H, dk, dv, N, fused=False, in_bytes=2):
     return T * H * per_tok_head + 3 * N * H * dk * dv * 4
 
 
-def backward_workload(steps, warmup, fused=False):
+def backward_workload(steps, warmup, fused=False, emit=True):
     """Backward tokens/s on workload 2's shape (one sequence, T=65536, H=96, d=128, bf16 q/k/v,
     initial state, d_o and dS_T upstream gradients), inputs drawn on the device with torch's seeded
     generator from the workload distributions (timing only).  With fused, the inputs are the raw
@@ -912,7 +920,7 @@ def backward_workload(steps, warmup, fused=False):
     nbytes = bwd_alg_bytes(T, H, dk, dv, 1, fused)
     what = ("raw bf16 q/k/v, bf16 gate pre-activations a, fp32 b, gradients through the fused gate and "
             "q/k normalisation" if fused else "bf16 q/k/v, fp32 g/beta")
-    print(json.dumps({
+    r = {
         "metric": "KDA backward tokens/s", "workload": "backward of the prefill T=65536 H=96 d_k=d_v=128 "
                                                       + what + ", initial state, d_o and dS_T",
         "tokens": T, "heads": H, "value": round(T / (med * 1e-3), 1), "unit": "tokens/s", "ms": round(med, 4),
@@ -922,7 +930,10 @@ def backward_workload(steps, warmup, fused=False):
         "workspace_GB": round(ws.numel() / 1e9, 2),
         "with_forward_states": {"ms": round(med_s, 4), "tokens_per_s": round(T / (med_s * 1e-3), 1),
                                 "note": "the forward's checkpoints every 32 tokens passed in, not recomputed"},
-        "data": "synthetic (seeded)"}), flush=True)
+        "data": "synthetic (seeded)"}
+    if emit:
+        print(json.dumps(r), flush=True)
+    return r
 
 
 BWD_VARLEN_CAP = 36 << 30   # workspace of the varlen backward: the library runs it in groups of sequences
