@@ -553,21 +553,6 @@ chunk32_kernel(const ChunkParams p) {
                         }
                     }
                 }
-                if constexpr (SO) {
-                    if (p.rres) {   // R = V - (Gamma K) S of chunk it
-                        float *const rb = p.rres + ((long long)(p.rbase[n] + it) * H + h) * p.rstride + col0 +
-                                          SWC * sw + JT * lr;
-#pragma unroll
-                        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                float x[JT];
-#pragma unroll
-                                for (int jt = 0; jt < JT; ++jt) x[jt] = -Yacc[rt][jt][e];
-                                store_cols<JT>(rb + (unsigned)((16 * rt + 4 * lq + e) * DV), x);
-                            }
-                    }
-                }
                 // park the output partials in LDS until stage o (this lane's private slots)
                 if constexpr (!SO)
 #pragma unroll
@@ -596,6 +581,22 @@ chunk32_kernel(const ChunkParams p) {
                         mma<true, true>(u1, t1f, M::template from_tiles<true>(w, Y[1][jt]));
                     }
                     UF[jt] = M::template from_tiles<true>(u0, u1);
+                }
+                if constexpr (SO) {
+                    // R = V - (Gamma K) S of chunk it (here, where its products have long completed)
+                    if (p.rres) {
+                        float *const rb = p.rres + ((long long)(p.rbase[n] + it) * H + h) * p.rstride + col0 +
+                                          SWC * sw + JT * lr;
+#pragma unroll
+                        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float x[JT];
+#pragma unroll
+                                for (int jt = 0; jt < JT; ++jt) x[jt] = -Y[rt][jt][e];
+                                store_cols<JT>(rb + (unsigned)((16 * rt + 4 * lq + e) * DV), x);
+                            }
+                    }
                 }
                 // Output rows 16 rt + 4 lq + e: the part that varies by (rt, e) is uniform and goes into
                 // a scalar row base; the lane's own part (its 4-row group and columns) is one 32-bit
