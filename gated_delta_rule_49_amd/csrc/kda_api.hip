@@ -11,6 +11,7 @@
 #include "kda.h"
 #include "kda_common.h"
 #include "kda_bwd_flags.h"
+#include "kda_side.h"
 
 extern "C" hipError_t kda_launch_decode(int dk, int in_bf16, int N, int H, const void *q, const void *k,
                                         const void *v, const float *g, const float *beta, float *state,
@@ -497,3 +498,59 @@ kda_status kda_decode_step(const kda_decode_args *a, void *stream) {
 }
 
 }  // extern "C"
+
+// ---- the side stream (kda_side.h) ----------------------------------------------------------
+namespace {
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+SideStream *g_side_cur = nullptr;   // between kda_side_fork and kda_side_forked (lock held)
+
+// (with g_side_mu held) the current device's side stream; null when it cannot be had
+SideStream *side_stream() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    SideStream &ss = g_side[dev];
+    if (!ss.s) {
+        hipStream_t st = nullptr;
+        hipEvent_t a = nullptr, b = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+            if (a) (void)hipEventDestroy(a);
+            (void)hipStreamDestroy(st);
+            return nullptr;
+        }
+        ss.s = st; ss.fork = a; ss.join = b;
+    }
+    return &ss;
+}
+}  // namespace
+
+extern "C" __attribute__((visibility("hidden"))) hipStream_t kda_side_fork(hipStream_t s) {
+    g_side_mu.lock();
+    SideStream *ss = side_stream();
+    if (!ss || hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) {
+        g_side_mu.unlock();
+        return nullptr;
+    }
+    g_side_cur = ss;
+    return ss->s;
+}
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t kda_side_forked(void) {
+    SideStream *ss = g_side_cur;
+    g_side_cur = nullptr;
+    const hipError_t e = ss ? hipEventRecord(ss->join, ss->s) : hipErrorInvalidValue;
+    g_side_mu.unlock();
+    return e;
+}
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t kda_side_join(hipStream_t s) {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream *ss = side_stream();
+    return ss ? hipStreamWaitEvent(s, ss->join, 0) : hipErrorInvalidValue;
+}

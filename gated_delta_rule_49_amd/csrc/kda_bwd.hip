@@ -35,8 +35,8 @@
 // for decays g >= -5.
 #include "kda_frag.h"
 #include "kda_bwd_flags.h"
+#include "kda_side.h"
 
-#include <mutex>
 #include <type_traits>
 
 namespace kda {
@@ -1273,38 +1273,6 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_chunk32_s
                                                                                     const kda::ChunkParams &p,
                                                                                     int max_split, hipStream_t stream);
 
-namespace {
-// A second stream per device, on which the forward recompute runs beside the one-workgroup
-// state-gradient scan (neither needs the other's results), with the events that fork it from the
-// caller's stream and join it back.  Created on first use (default priority) and kept until the
-// process ends; g_side_mu orders the record / wait pairs of concurrent callers.
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-std::mutex g_side_mu;
-SideStream g_side[64];
-
-// (with g_side_mu held) the current device's side stream; null when it cannot be had
-SideStream *side_stream() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    SideStream &ss = g_side[dev];
-    if (!ss.s) {
-        hipStream_t st = nullptr;
-        hipEvent_t a = nullptr, b = nullptr;
-        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-        if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
-            if (a) (void)hipEventDestroy(a);
-            (void)hipStreamDestroy(st);
-            return nullptr;
-        }
-        ss.s = st; ss.fork = a; ss.join = b;
-    }
-    return &ss;
-}
-}  // namespace
 
 // The fused prologue's outputs, materialised (one wave per (token, head) row; see prologue_kernel):
 // with KDA_PRO_NORM fp32 q / |q|, k / |k| and v into qn, kn, vf; with KDA_PRO_GATE fp32 g, beta.
@@ -1421,24 +1389,17 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t kda_launch_bwd(
         return e;
     // the side stream's recompute: forked after the prep kernel (so that it shares the chip with
     // the scan, not with the prep), joined before the gradient kernel
+    bool forked = false;
     auto fork_recompute = [&]() -> hipError_t {
-        std::lock_guard<std::mutex> lock(g_side_mu);
-        SideStream *ss = side_stream();
-        if (!ss)   // no side stream: the recompute goes on the caller's stream, before the scan
+        const hipStream_t side_s = kda_side_fork(stream);
+        if (!side_s)   // no side stream: the recompute goes on the caller's stream, before the scan
             return kda_launch_chunk32_split(dk, rec_bf16, chains, cp, 2, stream);
-        hipError_t r;
-        if ((r = hipEventRecord(ss->fork, stream)) != hipSuccess) return r;
-        if ((r = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return r;
-        if ((r = kda_launch_chunk32_split(dk, rec_bf16, chains, cp, 1, ss->s)) != hipSuccess) return r;
-        return hipEventRecord(ss->join, ss->s);
+        forked = true;
+        const hipError_t r = kda_launch_chunk32_split(dk, rec_bf16, chains, cp, 1, side_s);
+        const hipError_t j = kda_side_forked();
+        return r != hipSuccess ? r : j;
     };
-    // (a later caller may have recorded the join event again since: its recompute was queued on the
-    // side stream after this one, so waiting for it also covers this one)
-    auto join_recompute = [&]() -> hipError_t {
-        std::lock_guard<std::mutex> lock(g_side_mu);
-        SideStream *ss = side_stream();
-        return ss ? hipStreamWaitEvent(stream, ss->join, 0) : hipSuccess;
-    };
+    auto join_recompute = [&]() -> hipError_t { return forked ? kda_side_join(stream) : hipSuccess; };
     kda::BwdParams p;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu = cu;
     p.order = reinterpret_cast<const int32_t *>(ws + order_off);
