@@ -41,7 +41,8 @@
 // are masked where used).
 //
 // Precision: hi+lo bf16 operand pairs on every product feeding the outputs
-// except (Gamma*K) S and the KS side of A_kk (single bf16 there), fp32
+// except (Gamma*K) S and the KS side of A_kk (single bf16 there; hi+lo in the
+// states-only runs that hand R = V - (Gamma*K) S to the backward), fp32
 // accumulation, fp32 o and S.  The fp32-input instantiation uses fp32 MFMA
 // throughout.
 #include <type_traits>
@@ -218,49 +219,53 @@ chunk32_kernel(const ChunkParams p) {
     //     M = (I + X)(I + X^2)(I + X^4)(I + X^8),  X = -N,  N^16 = 0,
     // with 16x16 MFMA products held in registers (four dependent levels instead of a 16-step
     // substitution; hi/lo bf16 operands, or fp32 MFMA for fp32 inputs).  -T_aa = -M Diag(beta_a)
-    // (and -M11) -> TM, read by stage b in segment 2.
-    auto diag_inverse = [&](char *sm, int a, int ch, int lane, const f32x4_t &NA, const f32x4_t &NB) {
-        const int lr = lane & 15, lq = lane >> 4;
-        const float *beta_ch = reinterpret_cast<const float *>(sm + L::BETA) + (ch & 1) * 32;
-        const f32x4_t XA = {-NA[0], -NA[1], -NA[2], -NA[3]}, XB = {-NB[0], -NB[1], -NB[2], -NB[3]};
-        // (Z W) in B form = mm(Z_A, W_B); in A form = mm(W_B, Z_A)
-        auto mm = [](const f32x4_t &za, const f32x4_t &wb) {
-            f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (F32P) {
+    // (and -M11) -> TM, read by stage b in segment 2.  In two parts: the first three levels
+    // (inv_front: X8 and A3 = (I + X)(I + X^2)(I + X^4)), then M = A3 + A3 X^8 and the stores
+    // (inv_back), which the role waves run in the next iteration's segment 1.
+    // (Z W) in B form = inv_mm(Z_A, W_B); in A form = inv_mm(W_B, Z_A)
+    auto inv_mm = [](const f32x4_t &za, const f32x4_t &wb) {
+        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (F32P) {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) d = mfma_f32(za[kk], wb[kk], d);
-            } else {
-                // hi/lo bf16 split in two 16x16x32 MFMAs: K-slots 0..15 carry the hi parts and
-                // 16..31 the lo parts of Z, so [Zh Zl][Wh; Wh] + [Zh Zh][Wl; 0] = Zh Wh + Zl Wh + Zh Wl
-                uint32_t zh[2], zl[2], wh[2], wl[2];
-                split_hl2(za[0], za[1], zh[0], zl[0]);
-                split_hl2(za[2], za[3], zh[1], zl[1]);
-                split_hl2(wb[0], wb[1], wh[0], wl[0]);
-                split_hl2(wb[2], wb[3], wh[1], wl[1]);
-                const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, (uint4){zh[0], zh[1], zl[0], zl[1]});
-                const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, (uint4){wh[0], wh[1], wh[0], wh[1]});
-                const bf16x8_t a2 = __builtin_bit_cast(bf16x8_t, (uint4){zh[0], zh[1], zh[0], zh[1]});
-                const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, (uint4){wl[0], wl[1], 0u, 0u});
-                d = mfma_bf16(a1, b1, d);
-                d = mfma_bf16(a2, b2, d);
-            }
-            return d;
-        };
-        // M = A1 (I + X^2)(I + X^4)(I + X^8) with A1 = I + X, each factor applied as A += A X^(2^k):
-        // four dependent levels of products
+            for (int kk = 0; kk < 4; ++kk) d = mfma_f32(za[kk], wb[kk], d);
+        } else {
+            // hi/lo bf16 split in two 16x16x32 MFMAs: K-slots 0..15 carry the hi parts and
+            // 16..31 the lo parts of Z, so [Zh Zl][Wh; Wh] + [Zh Zh][Wl; 0] = Zh Wh + Zl Wh + Zh Wl
+            uint32_t zh[2], zl[2], wh[2], wl[2];
+            split_hl2(za[0], za[1], zh[0], zl[0]);
+            split_hl2(za[2], za[3], zh[1], zl[1]);
+            split_hl2(wb[0], wb[1], wh[0], wl[0]);
+            split_hl2(wb[2], wb[3], wh[1], wl[1]);
+            const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, (uint4){zh[0], zh[1], zl[0], zl[1]});
+            const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, (uint4){wh[0], wh[1], wh[0], wh[1]});
+            const bf16x8_t a2 = __builtin_bit_cast(bf16x8_t, (uint4){zh[0], zh[1], zh[0], zh[1]});
+            const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, (uint4){wl[0], wl[1], 0u, 0u});
+            d = mfma_bf16(a1, b1, d);
+            d = mfma_bf16(a2, b2, d);
+        }
+        return d;
+    };
+    // M = A1 (I + X^2)(I + X^4)(I + X^8) with A1 = I + X, each factor applied as A += A X^(2^k)
+    auto inv_front = [&](int lane, const f32x4_t &NA, const f32x4_t &NB, f32x4_t &X8B, f32x4_t &A3A) {
+        const int lr = lane & 15, lq = lane >> 4;
+        const f32x4_t XA = {-NA[0], -NA[1], -NA[2], -NA[3]}, XB = {-NB[0], -NB[1], -NB[2], -NB[3]};
         f32x4_t A1A;
 #pragma unroll
         for (int e = 0; e < 4; ++e) A1A[e] = ((4 * lq + e == lr) ? 1.f : 0.f) + XA[e];
-        const f32x4_t X2B = mm(XA, XB), X2A = mm(XB, XA);
-        const f32x4_t X4B = mm(X2A, X2B), X4A = mm(X2B, X2A), Y2A = mm(X2B, A1A);
+        const f32x4_t X2B = inv_mm(XA, XB), X2A = inv_mm(XB, XA);
+        const f32x4_t X4B = inv_mm(X2A, X2B), X4A = inv_mm(X2B, X2A), Y2A = inv_mm(X2B, A1A);
         f32x4_t A2A;
 #pragma unroll
         for (int e = 0; e < 4; ++e) A2A[e] = A1A[e] + Y2A[e];
-        const f32x4_t X8B = mm(X4A, X4B), Y3A = mm(X4B, A2A);
-        f32x4_t A3A;
+        X8B = inv_mm(X4A, X4B);
+        const f32x4_t Y3A = inv_mm(X4B, A2A);
 #pragma unroll
         for (int e = 0; e < 4; ++e) A3A[e] = A2A[e] + Y3A[e];
-        const f32x4_t Y4A = mm(X8B, A3A);
+    };
+    auto inv_back = [&](char *sm, int a, int ch, int lane, const f32x4_t &X8B, const f32x4_t &A3A) {
+        const int lr = lane & 15, lq = lane >> 4;
+        const float *beta_ch = reinterpret_cast<const float *>(sm + L::BETA) + (ch & 1) * 32;
+        const f32x4_t Y4A = inv_mm(X8B, A3A);
         f32x4_t MA;                                      // A form: M[lr][4 lq + e]
 #pragma unroll
         for (int e = 0; e < 4; ++e) MA[e] = A3A[e] + Y4A[e];
@@ -271,6 +276,11 @@ chunk32_kernel(const ChunkParams p) {
         for (int e = 0; e < 4; ++e) { tv[e] = -(MA[e] * bv[e]); nm[e] = -MA[e]; }
         M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 * a + lr, 16 * a + 4 * lq), tv);
         if (a == 1) M::template put_hl<4>(sm + L::TM, L::TRI_PLANE, fofs<1>(16 + lr, 4 * lq), nm);
+    };
+    auto diag_inverse = [&](char *sm, int a, int ch, int lane, const f32x4_t &NA, const f32x4_t &NB) {
+        f32x4_t X8B, A3A;
+        inv_front(lane, NA, NB, X8B, A3A);
+        inv_back(sm, a, ch, lane, X8B, A3A);
     };
 
     // Gram product of Kn block knb (16 rows) with rows 16 a .. 16 a + 15 of KS (or QS), or with
@@ -416,9 +426,13 @@ chunk32_kernel(const ChunkParams p) {
             }
             lds_barrier();   // chunk 0's norms before the prep waves' first segment 1 (all roles pass one)
         }
+        // role waves 0, 1: the last level of the pending chunk's inverse, in segment 1 where the
+        // chunk's T is not yet read (stage b reads it in segment 2); the other levels in segment 3
+        f32x4_t x8b = {0.f, 0.f, 0.f, 0.f}, a3a = x8b;
         for (int it = -1; it < nchunks; ++it) {
             char *const sm = smem + opaque_s(0);
             const int lane = lane_id(), lr = lane & 15, lq = lane >> 4;
+            if (rw < 2 && it >= 0) inv_back(sm, rw, it, lane, x8b, a3a);
             lds_barrier();
             if constexpr (RNORM) {
                 if (nwave && it + 2 < nchunks) {
@@ -444,7 +458,7 @@ chunk32_kernel(const ChunkParams p) {
                         z[e] = 4 * lq + e < lr ? br * gA[e] : 0.f;          // (lr, 4 lq + e)
                         zb[e] = lr < 4 * lq + e ? bcv[e] * gB[e] : 0.f;     // (4 lq + e, lr)
                     }
-                    diag_inverse(sm, rw, ch, lane, z, zb);
+                    inv_front(lane, z, zb, x8b, a3a);
                 } else if (rw == 2) {
                     if constexpr (!SO) {
                         store_aqk(sm, 0, 0, gram_prod(sm, 0, 0, true, lane), lane);
