@@ -132,6 +132,28 @@ template <int DK, int SPLIT> constexpr int chunk32_threads() {
     return 64 * (chunk32_scan_waves<DK, SPLIT>() + DK / 16 + chunk32_role_waves<DK, SPLIT>());
 }
 
+// Decay table of the fused gate, alpha = exp(-5 sigmoid(a)) for every bf16 pre-activation a that
+// changes it in fp32: per sign, entry 0 stands for |a| < 2^-24 (where 1 + e^-a rounds as at a = 0),
+// entries 1 .. 29 * 128 for the binades 2^-24 <= |a| < 32 (bf16 exponents 103 .. 131, 128 mantissas
+// each), and the last entry for |a| >= 32 (alpha is then exactly e^-5 for a > 0, 1 for a < 0; the
+// same rounding already holds from |a| > 17).  The entries are formed with the instructions of the
+// arithmetic path, so a lookup returns that path's value.  Only the two-workgroup kernels take it:
+// their LDS has room for its 29,712 bytes.
+constexpr int GT_U0 = 103 * 128 - 1;          // magnitude bits (exponent, mantissa) of entry 0
+constexpr int GT_ROW = 1 + 29 * 128 + 1;      // entries per sign
+__device__ __forceinline__ float gate_decay(float a) {
+    return __expf(-5.f * __builtin_amdgcn_rcpf(1.f + __expf(-a)));
+}
+__device__ __forceinline__ int gate_index(uint32_t b) {   // b: the 16 bits of a in its low half
+    const int j = min(max((int)(b & 0x7FFFu) - GT_U0, 0), GT_ROW - 1);
+    return (int)((b >> 15) & 1u) * GT_ROW + j;
+}
+__device__ __forceinline__ float gate_entry(int i) {
+    const int sgn = i >= GT_ROW, j = i - sgn * GT_ROW;
+    const uint32_t mag = j == 0 ? 0u : j == GT_ROW - 1 ? (132u << 7) : (uint32_t)(j + GT_U0);
+    return gate_decay(__uint_as_float(((uint32_t)sgn << 31) | (mag << 16)));
+}
+
 // JT adjacent fp32 values (the columns one scan lane owns in a row) from / to memory
 template <int JT> __device__ __forceinline__ void load_cols(const float *ptr, float (&x)[JT]) {
     if constexpr (JT == 2) {
@@ -170,7 +192,11 @@ chunk32_kernel(const ChunkParams p) {
     constexpr bool TR = (PRO & KDA_TRANSITION) != 0;    // the paired segment pass (see KDA_TRANSITION)
     static_assert(!TR || (!SO && SPLIT == 1), "the paired pass: outputs and states, one workgroup per run");
 
-    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+    // the fused gate's decay table after the operands (two workgroups per chain, d_k = 128)
+    constexpr bool GTAB = (PRO & KDA_PRO_GATE) != 0 && NRW > 0;
+    constexpr int GT_BYTES = GTAB ? 2 * GT_ROW * 4 : 0;
+    static_assert(L::TOTAL % 16 == 0 && L::TOTAL + GT_BYTES <= 160 * 1024, "LDS budget with the gate table");
+    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL + GT_BYTES];
 
     const int H = p.H;
     // Workgroups are handed to the 8 XCDs round-robin by index, and each XCD has its own L2.  The
@@ -209,6 +235,12 @@ chunk32_kernel(const ChunkParams p) {
     const bool is_scan = wave >= SCAN0 && wave < SCAN0 + NSW;
     const bool is_role = wave >= NSW + DK / 16;      // role waves come last
     const int sw = wave - SCAN0;                     // scan wave index (scan waves only)
+
+    if constexpr (GTAB) {
+        float *tab = reinterpret_cast<float *>(smem + L::TOTAL);
+        for (int i = (int)threadIdx.x; i < 2 * GT_ROW; i += 64 * NWAVES) tab[i] = gate_entry(i);
+        __syncthreads();
+    }
 
     const IN_T *qg = reinterpret_cast<const IN_T *>(p.q);
     const IN_T *kg = reinterpret_cast<const IN_T *>(p.k);
@@ -800,15 +832,22 @@ chunk32_kernel(const ChunkParams p) {
                     const bool valid = 4 * rgp + i < nv;   // padded rows: k = q = 0, alpha = 1, beta = 0
                     kr[i] = valid ? kn_[i] : PR::zero();
                     qr[i] = valid ? qn_[i] : PR::zero();
-                    float gx[2] = {gn_[i].x, gn_[i].y};
-                    if constexpr (pre) {
-                        // fused gate: g = -5 sigmoid(a), a a bf16 pair
+                    if constexpr (pre && GTAB) {
+                        // fused gate from the table: alpha of a bf16 pair a in one LDS read each
                         const uint32_t ab = __float_as_uint(gn_[i].x);
-                        gx[0] = -5.f * __builtin_amdgcn_rcpf(1.f + __expf(-lo_bf16_of(ab)));
-                        gx[1] = -5.f * __builtin_amdgcn_rcpf(1.f + __expf(-hi_bf16_of(ab)));
+                        const float *tab = reinterpret_cast<const float *>(sm + L::TOTAL);
+                        const float t0 = tab[gate_index(ab)], t1 = tab[gate_index(ab >> 16)];
+                        al[i][0] = valid ? t0 : 1.f;
+                        al[i][1] = valid ? t1 : 1.f;
+                    } else if constexpr (pre) {
+                        // fused gate: alpha = exp(-5 sigmoid(a)), a a bf16 pair
+                        const uint32_t ab = __float_as_uint(gn_[i].x);
+                        al[i][0] = valid ? gate_decay(lo_bf16_of(ab)) : 1.f;
+                        al[i][1] = valid ? gate_decay(hi_bf16_of(ab)) : 1.f;
+                    } else {
+                        al[i][0] = valid ? __expf(gn_[i].x) : 1.f;
+                        al[i][1] = valid ? __expf(gn_[i].y) : 1.f;
                     }
-                    al[i][0] = valid ? __expf(gx[0]) : 1.f;
-                    al[i][1] = valid ? __expf(gx[1]) : 1.f;
                 }
                 if (cp < 4) {
                     float bv = bn_;

@@ -403,6 +403,44 @@ def test_prefill_fused_prologue(gate, norm, d, chunk):
           "ckpt": W.rel_max_err(ck.cpu().numpy(), ck_r)}, TOL["bf16"])
 
 
+def test_gate_decay_of_every_bf16_value():
+    """The fused gate's decay alpha = exp(-5 sigmoid(a)) for every bf16 pre-activation a (NaNs aside):
+    one token per chain with k = q = v = 0, beta = sigmoid(-1e30) = 0 and S0 = 1 leaves
+    S_1 = Diag(alpha) S0, so the final state reads alpha out exactly.  With 128 chains the kernel
+    runs two workgroups per chain, which look alpha up in a table in LDS; a second token per head in
+    a second sequence makes 256 chains, one workgroup each, which form alpha arithmetically.  The two
+    must agree bit for bit, and both lie within 1e-6 (8 ulp: three approximate fp32 transcendentals)
+    of exp(-5 sigmoid(a)) in fp64 (the gate of the
+    skill card's quick facts: scaled sigmoid, g >= -5)."""
+    if torch.cuda.get_device_properties(0).multi_processor_count < 256:
+        pytest.skip("the one- and two-workgroup kernels are chosen for a 256-CU device")
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    e, m = (bits >> 7) & 0xFF, bits & 0x7F
+    bits = bits[~((e == 0xFF) & (m != 0))].astype(np.uint16)
+    H, D, blk = 128, 128, 128 * 128
+    bits = np.concatenate([bits, bits[: (-len(bits)) % blk]])
+    ref_all = -5.0 / (1.0 + np.exp(-(bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)))
+    ref_all = np.exp(ref_all)
+    z = torch.zeros((2, H, D), dtype=torch.bfloat16, device="cuda")
+    b = torch.full((2, H), -1e30, dtype=torch.float32, device="cuda")
+    s0 = torch.ones((2, H, D, D), dtype=torch.float32, device="cuda")
+    worst = 0.0
+    for i in range(0, len(bits), blk):
+        a1 = torch.from_numpy(bits[i:i + blk].view(np.int16).copy()).view(torch.bfloat16).reshape(1, H, D).cuda()
+        a2 = torch.cat([a1, a1])
+        _, sf1, _ = kda.kda_chunk_fwd(z[:1], z[:1], z[:1], a1, b[:1], [0, 1], 1.0, s0[:1], gate_preactivation=True)
+        _, sf2, _ = kda.kda_chunk_fwd(z, z, z, a2, b, [0, 1, 2], 1.0, s0, gate_preactivation=True)
+        torch.cuda.synchronize()
+        t1, t2 = sf1[0].cpu().numpy(), sf2[0].cpu().numpy()
+        assert np.all(t1 == t1[..., :1]) and np.all(t2 == t2[..., :1]), "S_1 rows are alpha times ones"
+        np.testing.assert_array_equal(t1[..., 0].ravel().view(np.uint32), t2[..., 0].ravel().view(np.uint32))
+        ref = ref_all[i:i + blk]
+        worst = max(worst, float(np.max(np.abs(t1[..., 0].ravel() - ref) / ref)))
+    print(f"gate decay over {len(bits)} bf16 values: table == arithmetic, worst relative error {worst:.2e}",
+          flush=True)
+    assert worst <= 1e-6
+
+
 @pytest.mark.parametrize("segment_tokens", [-1, 64])
 def test_prefill_fused_normalisation_edge_rows(segment_tokens):
     """The fused normalisation (role waves: the rows' sums of squares from the diagonal of their Gram
