@@ -824,6 +824,14 @@ chunk32_kernel(const ChunkParams p) {
 
             // ---- seg 1, P1(nxt): alpha = exp(g), running products over the 4-row group
             if (have) {
+                if constexpr ((PRO & KDA_PRO_NORM) != 0 && NRW > 0) {
+                    // formed by the role waves one iteration ahead: read first thing here (off segment
+                    // 2's path), so that the reads' latency passes under this segment's work
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        nrm[i] = *reinterpret_cast<const float2 *>(sm + L::NRM + (nxt & 1) * L::NRM_BUF + (4 * rgp + i) * 8);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 const int nv = min(C32, seq_len - nxt * C32);
                 constexpr bool pre = PRO & KDA_PRO_GATE;
                 float al[4][2];
@@ -853,12 +861,6 @@ chunk32_kernel(const ChunkParams p) {
                     float bv = bn_;
                     if constexpr (pre) bv = __builtin_amdgcn_rcpf(1.f + __expf(-bn_));   // sigmoid(b)
                     s_beta[4 * rgp + cp] = 4 * rgp + cp < nv ? bv : 0.f;
-                }
-                if constexpr ((PRO & KDA_PRO_NORM) != 0 && NRW > 0) {
-                    // formed by the role waves one iteration ahead: read here, off segment 2's path
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        nrm[i] = *reinterpret_cast<const float2 *>(sm + L::NRM + (nxt & 1) * L::NRM_BUF + (4 * rgp + i) * 8);
                 }
                 if constexpr ((PRO & KDA_PRO_NORM) != 0 && NRW == 0) {
                     // 1/|k|, 1/|q| of each row (0 for a zero row): sums of squares over the NCP lanes
