@@ -1088,7 +1088,12 @@ bwd_grad_kernel(const BwdParams p) {
             for (int e = 0; e < 4; ++e) G24[st][e] += __expf(bm - sb[16 * st + 4 * q4 + e][i]) * t2[e];
         }
 
-        // assemble dq, dk and dB (into sb: this wave's columns only, after its last read of them)
+        // assemble dq, dk and dB (into sb: this wave's columns only, after its last read of them).
+        // Output addresses: a scalar base per row (from a chunk start the compiler cannot hoist,
+        // which would keep 64-bit row offsets live through stages 1-3 and spill them) plus a 32-bit
+        // lane offset.
+        const size_t rowb = ((size_t)opaque_s(t0) * H + h) * DK;
+        const unsigned lo_ = (unsigned)(4 * q4 * H * DK + i);
         const float bl = sb[BC - 1][i];
         float cs = 0.f, dBv[2][4];
 #pragma unroll
@@ -1105,9 +1110,9 @@ bwd_grad_kernel(const BwdParams p) {
                 cs += kr * kbg;
                 dBv[rt][e] = widen(sq[r][i]) * dqv + kr * (dkp - dkm);
                 if (r < nv) {
-                    const size_t off = ((size_t)(t0 + r) * H + h) * DK + i;
-                    p.dq[off] = dqv;
-                    p.dk[off] = dkp + dkm;
+                    const size_t rs = rowb + (size_t)(16 * rt + e) * H * DK;   // (scalar)
+                    (p.dq + rs)[lo_] = dqv;
+                    (p.dk + rs)[lo_] = dkp + dkm;
                 }
             }
         cs += shfl_xor(cs, 16);
