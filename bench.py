@@ -360,11 +360,14 @@ COUNTER_FILE = {32: "chunk32_prefill_T65536_H96_d128_counters.json",
 
 
 def kernel_digest(chunk):
+    """Digest of the kernel's sources and of the compile flags they are built with."""
     import hashlib
+    from gated_delta_rule_49_amd.build import SOURCE_FLAGS
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[chunk]:
         with open(os.path.join(ROOT, "gated_delta_rule_49_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+        h.update(repr(SOURCE_FLAGS.get(f, [])).encode())
     return h.hexdigest()[:16]
 
 
